@@ -1,0 +1,474 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each test checks an oracle function against a closed form, an invariant, a
+brute-force computation or an independent library routine (numpy / torch in
+float64), chosen so that a dropped term, a wrong sign or index or a
+transposed operand in the oracle fails at least one of them.  None of these
+tests touches the GPU.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle_util import bf16, bf16_val, f32_bits, rec, run
+
+RNG = np.random.default_rng(12345)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding (round to nearest, ties to even) -- pinned to torch's own
+# fp32 -> bf16 conversion on fp32-representable inputs, over every exponent.
+# ---------------------------------------------------------------------------
+def test_bf16_round_matches_torch_on_fp32_values():
+    bits = RNG.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)
+    # add exact ties and neighbours of ties for many exponents
+    hi = (RNG.integers(0, 2 ** 16, 20_000, dtype=np.uint64).astype(np.uint32) << 16)
+    bits = np.concatenate([bits, hi | 0x8000, hi | 0x7FFF, hi | 0x8001, hi])
+    vals = bits.view(np.float32)
+    vals = vals[~np.isnan(vals)]
+    ref = bf16(vals)
+    got = np.array([oracle.round_bf16(float(v)) for v in vals[:60_000]], np.uint16)
+    assert np.array_equal(got, ref[:60_000])
+
+
+def test_bf16_round_special_cases():
+    assert oracle.round_bf16(0.0) == 0x0000
+    assert oracle.round_bf16(-0.0) == 0x8000
+    assert oracle.round_bf16(float("inf")) == 0x7F80
+    assert oracle.round_bf16(float("-inf")) == 0xFF80
+    assert (oracle.round_bf16(float("nan")) & 0x7FC0) == 0x7FC0
+    # 1 + 2^-8 is exactly half way between 1 and 1 + 2^-7: ties to even -> 1
+    assert oracle.round_bf16(1.0 + 2 ** -8) == 0x3F80
+    # 1 + 3*2^-8 is half way between 1+2^-7 (odd) and 1+2^-6 (even) -> up
+    assert oracle.round_bf16(1.0 + 3 * 2 ** -8) == 0x3F82
+    # just above a tie rounds up (a double that fp32 could not hold)
+    assert oracle.round_bf16(1.0 + 2 ** -8 + 2 ** -40) == 0x3F81
+    # largest finite bf16 and the overflow threshold
+    maxf = (2 - 2 ** -7) * 2.0 ** 127
+    assert oracle.round_bf16(maxf) == 0x7F7F
+    assert oracle.round_bf16((2 - 2 ** -8) * 2.0 ** 127) == 0x7F80
+    # smallest subnormal 2^-133, and half of it rounds to zero (even)
+    assert oracle.round_bf16(2.0 ** -133) == 0x0001
+    assert oracle.round_bf16(2.0 ** -134) == 0x0000
+    assert oracle.round_bf16(3 * 2.0 ** -134) == 0x0002
+
+
+def test_bf16_decode_is_exact_widening():
+    h = np.arange(0, 65536, 97, dtype=np.uint16)
+    got = np.array([oracle.bf16_to_float(int(x)) for x in h])
+    ref = bf16_val(h).astype(np.float64)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+# ---------------------------------------------------------------------------
+# add / mul: bit-exact IEEE results
+# ---------------------------------------------------------------------------
+def _specials_f32():
+    return np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, 1e-45, -1e-45,
+                     1.1754942e-38, 3.4028235e38, -3.4028235e38, 0.5, 2.0], np.float32)
+
+
+@pytest.mark.parametrize("op", [W.OP_ADD, W.OP_MUL])
+def test_f32_binary_matches_numpy(op):
+    n = 4096
+    a = RNG.standard_normal(n).astype(np.float32) * np.float32(2.0) ** RNG.integers(-140, 120, n)
+    b = RNG.standard_normal(n).astype(np.float32) * np.float32(2.0) ** RNG.integers(-140, 120, n)
+    sp = _specials_f32()
+    a[:len(sp) ** 2] = np.repeat(sp, len(sp))
+    b[:len(sp) ** 2] = np.tile(sp, len(sp))
+    a, b = a.astype(np.float32), b.astype(np.float32)
+    o = np.zeros(n, np.float32)
+    _, _, out = run(rec(op, size=n, a=0, b=1, out=2), [a, b, o])
+    with np.errstate(all="ignore"):
+        ref = a + b if op == W.OP_ADD else a * b
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(out), nan)
+    assert np.array_equal(f32_bits(out)[~nan], f32_bits(ref)[~nan])
+
+
+def test_f32_identities():
+    x = RNG.standard_normal(1000).astype(np.float32)
+    z, one, m1 = np.zeros_like(x), np.ones_like(x), -np.ones_like(x)
+    o = np.zeros_like(x)
+    r = run([rec(W.OP_ADD, size=1000, a=0, b=1, out=4)], [x, z, one, m1, o])[4]
+    assert np.array_equal(f32_bits(r), f32_bits(x))
+    r = run([rec(W.OP_MUL, size=1000, a=0, b=2, out=4)], [x, z, one, m1, o])[4]
+    assert np.array_equal(f32_bits(r), f32_bits(x))
+    r = run([rec(W.OP_MUL, size=1000, a=0, b=3, out=4)], [x, z, one, m1, o])[4]
+    assert np.array_equal(f32_bits(r), f32_bits(-x))
+    y = RNG.standard_normal(1000).astype(np.float32)
+    r1 = run([rec(W.OP_ADD, size=1000, a=0, b=1, out=2)], [x, y, o])[2]
+    r2 = run([rec(W.OP_ADD, size=1000, a=1, b=0, out=2)], [x, y, o])[2]
+    assert np.array_equal(f32_bits(r1), f32_bits(r2))
+
+
+@pytest.mark.parametrize("op", [W.OP_ADD, W.OP_MUL])
+def test_bf16_binary_matches_torch_bf16(op):
+    """Every bf16 value against 512 random bf16 partners: torch computes the
+    bf16 op in fp32 and rounds once to bf16; since fp32 holds 2*8+2 bits this
+    is the correctly rounded result, the same definition the oracle follows."""
+    allv = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    partners = RNG.integers(0, 65536, 512).astype(np.uint16)
+    a = np.repeat(allv, len(partners))
+    b = np.tile(partners, len(allv))
+    o = np.zeros_like(a)
+    _, _, out = run(rec(op, dtype=W.BF16, size=len(a), a=0, b=1, out=2), [a, b, o])
+    ta = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    tb = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+    ref = (ta + tb if op == W.OP_ADD else ta * tb).view(torch.int16).numpy().view(np.uint16)
+    nan_ref = (ref & 0x7F80) == 0x7F80
+    nan_ref &= (ref & 0x007F) != 0
+    nan_out = ((out & 0x7F80) == 0x7F80) & ((out & 0x007F) != 0)
+    assert np.array_equal(nan_ref, nan_out)
+    assert np.array_equal(out[~nan_ref], ref[~nan_ref])
+
+
+# ---------------------------------------------------------------------------
+# ReLU
+# ---------------------------------------------------------------------------
+def test_relu_identities_and_specials():
+    x = np.concatenate([RNG.standard_normal(2000), _specials_f32()]).astype(np.float32)
+    n = len(x)
+    o = np.zeros(n, np.float32)
+    r = run(rec(W.OP_RELU, size=n, a=0, out=1), [x, o])[1]
+    rr = run(rec(W.OP_RELU, size=n, a=0, out=1), [r, o])[1]
+    assert np.array_equal(f32_bits(rr), f32_bits(r))           # idempotent
+    rn = run(rec(W.OP_RELU, size=n, a=0, out=1), [-x, o])[1]
+    fin = np.isfinite(x)
+    assert np.array_equal((r - rn)[fin], x[fin])                  # relu(x)-relu(-x) = x
+    assert f32_bits(r[x == 0]).max() == 0                          # +0 for both zeros
+    assert np.isnan(r[np.isnan(x)]).all()
+    assert np.all(r[x > 0] == x[x > 0])
+
+
+# ---------------------------------------------------------------------------
+# GELU (tanh approximation)
+# ---------------------------------------------------------------------------
+def test_gelu_matches_torch_tanh_gelu_in_double():
+    x = np.concatenate([np.linspace(-12, 12, 4001), RNG.standard_normal(2000) * 3])
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    got = np.array([oracle.gelu(v) for v in x])
+    assert np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-300)) < 1e-12 or \
+        np.max(np.abs(got - ref)) < 1e-15
+
+
+def test_gelu_odd_identity_and_limits():
+    for x in list(np.linspace(-8, 8, 321)) + [1e-6, 0.3, 17.0]:
+        assert abs(oracle.gelu(x) - oracle.gelu(-x) - x) <= 1e-15 * max(1.0, abs(x))
+    assert oracle.gelu(0.0) == 0.0
+    assert abs(oracle.gelu(30.0) - 30.0) < 1e-12
+    assert abs(oracle.gelu(-30.0)) < 1e-12
+    # the sigmoid form x / (1 + exp(-2u)) is algebraically identical
+    for x in np.linspace(-6, 6, 121):
+        u = math.sqrt(2 / math.pi) * (x + 0.044715 * x ** 3)
+        assert abs(oracle.gelu(x) - x / (1 + math.exp(-2 * u))) <= 1e-15 * max(1.0, abs(x))
+
+
+def test_gelu_record_rounds_once():
+    x = RNG.standard_normal(3000).astype(np.float32)
+    o = np.zeros_like(x)
+    r = run(rec(W.OP_GELU, size=len(x), a=0, out=1), [x, o])[1]
+    ref = torch.nn.functional.gelu(torch.from_numpy(x.astype(np.float64)), approximate="tanh")
+    ref32 = ref.numpy().astype(np.float32)
+    assert np.max(np.abs(r.astype(np.float64) - ref32.astype(np.float64))
+                  / np.maximum(np.abs(ref32), 1e-30)) <= 2 ** -23
+
+
+# ---------------------------------------------------------------------------
+# sum / max / min along the last dimension
+# ---------------------------------------------------------------------------
+def test_sum_exact_on_integers_and_constants():
+    rows, h = 8, 1024
+    x = RNG.integers(-1000, 1000, (rows, h)).astype(np.float32)
+    o = np.zeros(rows, np.float32)
+    r = run(rec(W.OP_SUM, size=rows, dim=(h,), a=0, out=1), [x, o])[1]
+    assert np.array_equal(r, x.sum(axis=1, dtype=np.int64).astype(np.float32))
+    c = np.full((4, 4096), 0.75, np.float32)
+    r = run(rec(W.OP_SUM, size=4, dim=(4096,), a=0, out=1), [c, np.zeros(4, np.float32)])[1]
+    assert np.all(r == 3072.0)
+
+
+def test_max_min_match_numpy_and_order_zeros():
+    rows, h = 16, 768
+    x = RNG.standard_normal((rows, h)).astype(np.float32) * 2
+    o = np.zeros(rows, np.float32)
+    mx = run(rec(W.OP_MAX, size=rows, dim=(h,), a=0, out=1), [x, o])[1]
+    mn = run(rec(W.OP_MIN, size=rows, dim=(h,), a=0, out=1), [x, o])[1]
+    assert np.array_equal(mx, x.max(axis=1)) and np.array_equal(mn, x.min(axis=1))
+    z = np.array([[0.0, -0.0, -0.0], [-0.0, 0.0, -0.0], [-1.0, np.nan, 5.0]], np.float32)
+    o = np.zeros(3, np.float32)
+    mx = run(rec(W.OP_MAX, size=3, dim=(3,), a=0, out=1), [z, o])[1]
+    mn = run(rec(W.OP_MIN, size=3, dim=(3,), a=0, out=1), [z, o])[1]
+    assert f32_bits(mx[:2]).tolist() == [0, 0]                   # +0 is the max
+    assert f32_bits(mn[:2]).tolist() == [0x80000000] * 2          # -0 is the min
+    assert np.isnan(mx[2]) and np.isnan(mn[2])
+    assert oracle.max2(1.0, float("nan")) != oracle.max2(1.0, float("nan"))
+
+
+# ---------------------------------------------------------------------------
+# softmax
+# ---------------------------------------------------------------------------
+def test_softmax_against_torch_and_closed_forms():
+    rows, h = 4, 2048
+    x = (RNG.standard_normal((rows, h)) * 2).astype(np.float32)
+    o = np.zeros_like(x)
+    y = run(rec(W.OP_SOFTMAX, size=rows, dim=(h,), a=0, out=1), [x, o])[1]
+    ref = torch.softmax(torch.from_numpy(x.astype(np.float64)), dim=1).numpy()
+    assert np.max(np.abs(y - ref) / ref) <= 2 ** -24 * 1.01
+    assert np.all(np.abs(y.astype(np.float64).sum(axis=1) - 1) <= h * 2 ** -24)
+    y2 = run(rec(W.OP_SOFTMAX, size=rows, dim=(h,), a=0, out=1), [x + np.float32(3.0), o])[1]
+    assert np.max(np.abs(y2 - y) / y) < 1e-6                         # shift invariance
+    for n in (1024, 2048, 4096):
+        c = np.full((1, n), -0.3, np.float32)
+        yc = run(rec(W.OP_SOFTMAX, size=1, dim=(n,), a=0, out=1), [c, np.zeros_like(c)])[1]
+        assert np.all(yc == np.float32(1.0 / n))
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm
+# ---------------------------------------------------------------------------
+def test_layernorm_closed_form_and_torch():
+    rows, h, eps = 3, 1024, np.float32(1e-5)
+    x = (RNG.standard_normal((rows, h)) * 2 + 0.5).astype(np.float32)
+    g1, b0 = np.ones(h, np.float32), np.zeros(h, np.float32)
+    o = np.zeros_like(x)
+    y = run(rec(W.OP_LAYERNORM, size=rows, dim=(h,), fparam=(eps,), a=0, out=3, aux0=1, aux1=2),
+            [x, g1, b0, o])[3].astype(np.float64)
+    xd = x.astype(np.float64)
+    var = xd.var(axis=1)
+    assert np.all(np.abs(y.mean(axis=1)) < 1e-6)
+    assert np.allclose(y.var(axis=1), var / (var + float(eps)), rtol=1e-6)
+    g = (1 + 0.1 * RNG.standard_normal(h)).astype(np.float32)
+    b = (0.1 * RNG.standard_normal(h)).astype(np.float32)
+    y = run(rec(W.OP_LAYERNORM, size=rows, dim=(h,), fparam=(eps,), a=0, out=3, aux0=1, aux1=2),
+            [x, g, b, o])[3]
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(xd), (h,), torch.from_numpy(g.astype(np.float64)),
+                                         torch.from_numpy(b.astype(np.float64)), eps=float(eps)).numpy()
+    assert np.max(np.abs(y - ref) / np.maximum(np.abs(ref), 1)) < 2 ** -23
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+def _rope_complex(x, pos, theta, half=False):
+    """Independent formulation: pairs as complex numbers times e^{i angle}."""
+    B, H, D = x.shape
+    i = np.arange(D // 2)
+    freq = np.power(theta, -2.0 * i / D)
+    if half:
+        z = x[..., : D // 2] + 1j * x[..., D // 2:]
+    else:
+        z = x[..., 0::2] + 1j * x[..., 1::2]
+    rot = z * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    out = np.empty_like(x)
+    if half:
+        out[..., : D // 2], out[..., D // 2:] = rot.real, rot.imag
+    else:
+        out[..., 0::2], out[..., 1::2] = rot.real, rot.imag
+    return out
+
+
+@pytest.mark.parametrize("half", [False, True])
+def test_rope_matches_complex_rotation_f32(half):
+    B, H, D = 3, 4, 128
+    q = RNG.standard_normal((B, H, D)).astype(np.float32)
+    k = RNG.standard_normal((B, H, D)).astype(np.float32)
+    lens = [1, 77, 4096]
+    out = run(rec(W.OP_ROPE, size=B, dim=(H, D), fparam=(10000.0,), lens=lens,
+                  flags=W.FLAG_ROPE_HALF if half else 0, a=0, b=1), [q, k])
+    pos = np.array(lens, np.float64) - 1
+    for got, x in zip(out, (q, k)):
+        ref = _rope_complex(x.astype(np.float64), pos, 10000.0, half)
+        assert np.max(np.abs(got - ref)) <= 2 ** -23 * np.max(np.abs(ref)) + 1e-12
+        # position 0 (L = 1) is the identity, bit-exact
+        assert np.array_equal(f32_bits(got[0]), f32_bits(x[0]))
+
+
+def test_rope_relative_position_and_norm():
+    H, D = 2, 128
+    q = RNG.standard_normal((1, H, D))
+    k = RNG.standard_normal((1, H, D))
+
+    def rot(x, L):
+        xx = x.astype(np.float32)
+        out = run(rec(W.OP_ROPE, size=1, dim=(H, D), fparam=(10000.0,), lens=[L], a=0, b=1), [xx, xx.copy()])
+        return out[0].astype(np.float64)
+    for (m, n, t) in [(5, 9, 11), (100, 3, 40)]:
+        d1 = np.sum(rot(q, m + 1) * rot(k, n + 1))
+        d2 = np.sum(rot(q, m + t + 1) * rot(k, n + t + 1))
+        assert abs(d1 - d2) < 1e-4
+    r = rot(q, 300)
+    qq = q.astype(np.float32).astype(np.float64)
+    n0 = qq[..., 0::2] ** 2 + qq[..., 1::2] ** 2
+    n1 = r[..., 0::2] ** 2 + r[..., 1::2] ** 2
+    assert np.allclose(n0, n1, rtol=1e-6)
+
+
+def test_rope_bf16_is_single_rounding_of_double():
+    B, H, D = 2, 3, 128
+    q = bf16(RNG.standard_normal((B, H, D)))
+    k = bf16(RNG.standard_normal((B, H, D)))
+    lens = [10, 3000]
+    oq, ok = run(rec(W.OP_ROPE, dtype=W.BF16, size=B, dim=(H, D), fparam=(10000.0,), lens=lens, a=0, b=1),
+                 [q, k])
+    pos = np.array(lens, np.float64) - 1
+    for got, x in ((oq, q), (ok, k)):
+        ref = _rope_complex(bf16_val(x).astype(np.float64), pos, 10000.0)
+        expect = np.array([oracle.round_bf16(v) for v in ref.reshape(-1)], np.uint16).reshape(ref.shape)
+        # complex-exponential vs cos/sin evaluation differ by ~1e-16; a bf16
+        # tie flip is possible only at exact midpoints
+        mism = np.sum(got != expect)
+        assert mism <= 2
+
+
+# ---------------------------------------------------------------------------
+# KV append
+# ---------------------------------------------------------------------------
+def test_kv_append_is_bit_copy_and_touches_one_row():
+    B, H, D, C = 2, 3, 8, 16
+    k = bf16(RNG.standard_normal((B, H, D)))
+    v = bf16(RNG.standard_normal((B, H, D)))
+    K0 = bf16(RNG.standard_normal((B, H, C, D)))
+    V0 = bf16(RNG.standard_normal((B, H, C, D)))
+    lens = [5, 16]
+    _, _, K, V = run(rec(W.OP_KV_APPEND, dtype=W.BF16, size=B, dim=(H, D, C), lens=lens,
+                         a=0, b=1, aux0=2, aux1=3), [k, v, K0, V0])
+    for b, L in enumerate(lens):
+        assert np.array_equal(K[b, :, L - 1], k[b]) and np.array_equal(V[b, :, L - 1], v[b])
+        mask = np.ones(C, bool)
+        mask[L - 1] = False
+        assert np.array_equal(K[b][:, mask], K0[b][:, mask])
+        assert np.array_equal(V[b][:, mask], V0[b][:, mask])
+
+
+# ---------------------------------------------------------------------------
+# decode SDPA
+# ---------------------------------------------------------------------------
+def _sdpa_torch(q, K, V, lens):
+    B, H, D = q.shape
+    out = np.zeros((B, H, D))
+    for b, L in enumerate(lens):
+        qq = torch.from_numpy(q[b][:, None, :])
+        kk = torch.from_numpy(K[b][:, :L, :])
+        vv = torch.from_numpy(V[b][:, :L, :])
+        out[b] = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[:, 0, :].numpy()
+    return out
+
+
+def test_sdpa_matches_torch_brute_force():
+    for (B, H, D, C) in [(1, 1, 4, 8), (2, 3, 8, 8), (3, 2, 128, 64)]:
+        q = bf16(RNG.standard_normal((B, H, D)))
+        K = bf16(RNG.standard_normal((B, H, C, D)))
+        V = bf16(RNG.standard_normal((B, H, C, D)))
+        lens = list(RNG.integers(1, C + 1, B))
+        o = np.zeros((B, H, D), np.float32)
+        got = run(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=B, dim=(H, D, C), lens=lens,
+                      a=0, aux0=1, aux1=2, out=3), [q, K, V, o])[3]
+        ref = _sdpa_torch(*(bf16_val(t).astype(np.float64) for t in (q, K, V)), lens)
+        assert np.max(np.abs(got - ref)) <= 2 ** -23 * np.max(np.abs(ref)) + 1e-12
+
+
+def test_sdpa_special_cases():
+    B, H, D, C = 1, 2, 16, 32
+    q = bf16(RNG.standard_normal((B, H, D)))
+    K = bf16(RNG.standard_normal((B, H, C, D)))
+    V = bf16(RNG.standard_normal((B, H, C, D)))
+    o = np.zeros((B, H, D), np.float32)
+
+    def sdpa(qq, KK, VV, L):
+        return run(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=B, dim=(H, D, C), lens=[L],
+                       a=0, aux0=1, aux1=2, out=3), [qq, KK, VV, o])[3]
+    # L = 1: o = V_0
+    assert np.array_equal(sdpa(q, K, V, 1), bf16_val(V[:, :, 0, :]))
+    # q = 0: uniform weights -> mean of V over [0, L)
+    L = 20
+    got = sdpa(np.zeros_like(q), K, V, L)
+    ref = bf16_val(V[:, :, :L, :]).astype(np.float64).mean(axis=2)
+    assert np.max(np.abs(got - ref)) < 1e-6
+    # identical keys: mean of V as well
+    Ks = np.repeat(K[:, :, :1, :], C, axis=2)
+    got = sdpa(q, Ks, V, L)
+    assert np.max(np.abs(got - ref)) < 1e-6
+    # permuting keys together with their values changes nothing
+    perm = np.concatenate([RNG.permutation(L), np.arange(L, C)])
+    a = sdpa(q, K, V, L)
+    b = sdpa(q, K[:, :, perm, :], V[:, :, perm, :], L)
+    assert np.max(np.abs(a - b)) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------
+def test_gemv_exact_on_small_integers_and_against_numpy():
+    K, N = 64, 48
+    x = RNG.integers(-4, 5, K).astype(np.float32)
+    Wm = RNG.integers(-4, 5, (K, N)).astype(np.float32)
+    y = run(rec(W.OP_GEMV, dim=(K, N), a=0, b=1, out=2), [x, Wm, np.zeros(N, np.float32)])[2]
+    assert np.array_equal(y, (x.astype(np.int64) @ Wm.astype(np.int64)).astype(np.float32))
+    K, N = 1024, 96
+    x = bf16(RNG.standard_normal(K))
+    Wb = bf16(RNG.standard_normal((K, N)) * 0.02)
+    y = run(rec(W.OP_GEMV, dtype=W.BF16, dim=(K, N), a=0, b=1, out=2), [x, Wb, np.zeros(N, np.uint16)])[2]
+    ref = bf16_val(x).astype(np.float64) @ bf16_val(Wb).astype(np.float64)
+    expect = np.array([oracle.round_bf16(v) for v in ref], np.uint16)
+    assert np.sum(y != expect) == 0
+    # transposed operand would fail this: a non-square W with distinct rows
+    x = np.zeros(K, np.float32)
+    x[3] = 1
+    Wm = RNG.standard_normal((K, N)).astype(np.float32)
+    y = run(rec(W.OP_GEMV, dim=(K, N), a=0, b=1, out=2), [x, Wm, np.zeros(N, np.float32)])[2]
+    assert np.array_equal(y, Wm[3])
+
+
+# ---------------------------------------------------------------------------
+# copy, errors, stream semantics
+# ---------------------------------------------------------------------------
+def test_copy_and_bounds_errors():
+    a = RNG.integers(0, 255, 1000).astype(np.uint8)
+    o = np.zeros(1000, np.uint8)
+    r = run(rec(W.OP_COPY, size=1000, a=0, out=1), [a, o])[1]
+    assert np.array_equal(r, a)
+    with pytest.raises(oracle.OracleError):
+        run(rec(W.OP_COPY, size=1001, a=0, out=1), [a, o])
+    with pytest.raises(oracle.OracleError):
+        run(rec(99, size=1, a=0, out=1), [a, o])
+
+
+def test_stream_is_sequential_with_aliasing():
+    """A stream equals running its records one after another: y = (x + x) * x
+    written in place, then relu, matches the hand-computed composition."""
+    x = RNG.standard_normal(500).astype(np.float32)
+    recs = [rec(W.OP_ADD, size=500, a=0, b=0, out=0),
+            rec(W.OP_MUL, size=500, a=0, b=1, out=0),
+            rec(W.OP_RELU, size=500, a=0, out=0)]
+    y = run(recs, [x, x.copy()])[0]
+    ref = np.maximum((x + x) * x, np.float32(0))
+    ref[ref == 0] = 0.0
+    assert np.array_equal(f32_bits(y), f32_bits(ref))
+
+
+def test_pr1_prefix_matches_numpy_replay():
+    """PR1 (add/mul/relu only) replayed independently with numpy fp32."""
+    s = W.make_pr1()
+    pool = oracle.Pool.from_stream(s)
+    pool.run(s.recs)
+    vals = [b.host_values().copy() for b in s.buffers]
+    with np.errstate(all="ignore"):
+        for r in s.recs:
+            a = vals[r["buf"][W.A]]
+            if r["op"] == W.OP_RELU:
+                out = np.where(np.isnan(a), a, np.where(a > 0, a, np.float32(0)))
+            else:
+                b = vals[r["buf"][W.B]]
+                out = a + b if r["op"] == W.OP_ADD else a * b
+            vals[r["buf"][W.OUT]] = out.astype(np.float32)
+    for i, v in enumerate(vals):
+        got = pool.view(i, np.float32)
+        nan = np.isnan(v)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(f32_bits(got)[~nan], f32_bits(v)[~nan])
