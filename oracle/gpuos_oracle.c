@@ -30,7 +30,9 @@
  * Readings where the pages are silent (each is listed in the design notes):
  *  - relu(-0) = +0 and relu(NaN) = NaN.
  *  - max/min propagate NaN and order -0 below +0.
- *  - GELU is the tanh approximation with sqrt(2/pi) and 0.044715.
+ *  - GELU is the tanh approximation with sqrt(2/pi) and 0.044715; where
+ *    1 + tanh(u) would cancel (u < -1/2) the exact identity
+ *    1 + tanh(u) = 2 / (1 + e^(-2u)) is used instead.
  *  - LayerNorm uses the biased variance and adds eps inside the root.
  *  - RoPE rotates adjacent pairs (x_2i, x_2i+1) by pos * theta^(-2i/D)
  *    (rotate-half pairing with flag 1); pos = L_b - 1.
@@ -125,10 +127,15 @@ double orc_relu(double x) {
     return x > 0.0 ? x : 0.0;                  /* -0 and negatives give +0 */
 }
 
-/* GELU, tanh approximation: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+/* GELU, tanh approximation: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+ * For u < -1/2 the sum 1 + tanh(u) cancels in double (at x = -7 it keeps
+ * only a few digits, below about x = -8.5 none), so there it is evaluated
+ * with the exact identity 1 + tanh(u) = 2 / (1 + e^(-2u)). */
 double orc_gelu(double x) {
     const double k = sqrt(2.0 / M_PI);
-    return 0.5 * x * (1.0 + tanh(k * (x + 0.044715 * x * x * x)));
+    const double u = k * (x + 0.044715 * x * x * x);
+    const double t = u >= -0.5 ? 1.0 + tanh(u) : 2.0 / (1.0 + exp(-2.0 * u));
+    return 0.5 * x * t;
 }
 
 /* max/min under a total order on non-NaN values with -0 < +0; NaN wins */
