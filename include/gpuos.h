@@ -1,0 +1,281 @@
+/*
+ * gpuos.h -- C ABI of the MI355X persistent micro-op dispatcher.
+ *
+ * The operation (GPUOS digest page, sections 2 and 3 Q2): a host thread
+ * writes small task descriptors into a lock-free ring in device-visible
+ * memory (prepare -> acquire slot -> write -> commit with store-release);
+ * a persistent executor kernel, launched once with one workgroup per
+ * compute unit, polls the ring with load-acquire, claims work atomically,
+ * looks the op up in a dual-slot, version-flipped operator table and runs
+ * the micro-op as a device function instead of a kernel launch; then it
+ * releases the slot.  Results equal running every micro-op in submission
+ * order (the pages keep eager semantics).
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device pointer" are HIP device addresses (for example
+ *    a torch tensor's data_ptr()); the library never allocates, frees or
+ *    copies them.  Other pointers are host pointers.
+ *  - Every function returns GPUOS_OK (0) or a negative GPUOS_E_* code and
+ *    never throws or aborts.
+ *  - A context is driven by one producer thread at a time (calls into one
+ *    context are serialised internally; producers on different threads are
+ *    ordered only by that serialisation).
+ *  - While a context is alive, do not call hipDeviceSynchronize (or
+ *    torch.cuda.synchronize()) on its device: the executor kernel does not
+ *    exit until gpuos_pause or gpuos_shutdown.  Use gpuos_sync instead.
+ */
+#ifndef GPUOS_H
+#define GPUOS_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GPUOS_ABI_VERSION 1
+
+/* ---------------------------------------------------------------- errors */
+#define GPUOS_OK 0
+#define GPUOS_E_INVAL (-1)    /* bad argument, descriptor layout or shape */
+#define GPUOS_E_FULL (-2)     /* not enough free ring slots (no BLOCK flag) */
+#define GPUOS_E_NOOP (-3)     /* register_op: unknown kind or op_id out of range */
+#define GPUOS_E_TIMEOUT (-4)  /* gpuos_sync / shutdown deadline passed */
+#define GPUOS_E_DEVICE (-5)   /* a descriptor completed with a non-zero status */
+#define GPUOS_E_HIP (-6)      /* a HIP runtime call failed */
+#define GPUOS_E_STATE (-7)    /* call not valid in the context's state */
+
+/* per-descriptor device status codes (see gpuos_sync's err_seq/err_status) */
+#define GPUOS_ST_OK 0
+#define GPUOS_ST_BAD_OP 1     /* op_id out of range or table entry empty */
+#define GPUOS_ST_BAD_SHAPE 2  /* shape the op body does not support */
+#define GPUOS_ST_SPIN 3       /* a dependency wait exceeded the spin limit */
+
+/* -------------------------------------------------------- operator kinds */
+/* Built-in operator bodies (digest page, section 3 Q2 "Operator library").
+ * At init op_id k is bound to kind k for every built-in kind; op ids from
+ * GPUOS_OP_USER upward start empty and can be bound with gpuos_register_op. */
+enum gpuos_kind {
+    GPUOS_OP_NOP = 0,        /* nothing; the analogue of a null kernel */
+    GPUOS_OP_ADD = 1,        /* out[i] = a[i] + b[i], i < size */
+    GPUOS_OP_MUL = 2,        /* out[i] = a[i] * b[i] */
+    GPUOS_OP_RELU = 3,       /* out[i] = max(a[i], +0); NaN stays NaN */
+    GPUOS_OP_GELU = 4,       /* tanh-approximation GELU */
+    GPUOS_OP_SUM = 5,        /* [rows, h] -> [rows], along the last dim */
+    GPUOS_OP_MAX = 6,
+    GPUOS_OP_MIN = 7,
+    GPUOS_OP_SOFTMAX = 8,    /* [rows, h] -> [rows, h] */
+    GPUOS_OP_LAYERNORM = 9,  /* [rows, h] -> [rows, h], gamma/beta [h] */
+    GPUOS_OP_ROPE = 10,      /* in place on q and k, [B, H, D] */
+    GPUOS_OP_KV_APPEND = 11, /* K/V cache [B, H, C, D] row L_b-1 <- k/v [B, H, D] */
+    GPUOS_OP_SDPA = 12,      /* single-query attention over keys [0, L_b) */
+    GPUOS_OP_GEMV = 13,      /* y[N] = x[K] . W[K, N] (W row-major) */
+    GPUOS_OP_COPY = 14,      /* byte copy of `size` bytes */
+    GPUOS_KIND_COUNT = 15,
+    GPUOS_KIND_EMPTY = 0xFFFFFFFFu /* register_op: unbind an op id */
+};
+#define GPUOS_MAX_OPS 256
+#define GPUOS_OP_USER 64
+
+/* element types */
+#define GPUOS_F32 0u
+#define GPUOS_BF16 1u
+
+/* descriptor flags: bits 0-3 input dtype, bits 4-7 output dtype */
+#define GPUOS_FLAGS(in_dtype, out_dtype) ((uint32_t)(in_dtype) | ((uint32_t)(out_dtype) << 4))
+#define GPUOS_F_ROPE_HALF (1u << 8)  /* RoPE pairs (x_i, x_{i+D/2}) instead of (x_2i, x_2i+1) */
+
+/* ------------------------------------------------------------ descriptor */
+/* One ring entry, 128 bytes (the pages give 64-128 B holding op_id,
+ * input_a, input_b, output, size, flags plus dims).  The caller fills the
+ * first 88 bytes and `param`; gpuos_submit fills seq, dep_delta, dep_range
+ * and table_version.
+ *
+ * Operand meaning by kind (all pointers are device pointers):
+ *   ADD, MUL        a, b, output: `size` elements of the input dtype.
+ *   RELU, GELU      a, output: `size` elements.
+ *   SUM/MAX/MIN     a = x [size rows, dim[0]]; output [size].
+ *   SOFTMAX         a = x [size, dim[0]]; output [size, dim[0]].
+ *   LAYERNORM       as SOFTMAX; aux[0] = gamma [dim[0]], aux[1] = beta;
+ *                   param.f[0] = eps (0 -> the table entry's default).
+ *   ROPE            a = q, b = k, both [size=B, dim[0]=H, dim[1]=D], rotated
+ *                   in place at position lens[b]-1; param.f[4] = theta
+ *                   (0 -> table default, 10000).
+ *   KV_APPEND       a = k, b = v [B, H, D]; aux[0] = K cache, aux[1] = V cache
+ *                   [B, H, dim[2]=C, D]; writes row lens[b]-1.
+ *   SDPA            a = q [B, H, D]; aux[0] = K, aux[1] = V [B, H, C, D];
+ *                   output [B, H, D] in the output dtype; keys [0, lens[b]);
+ *                   param.f[4] = scale (0 -> 1/sqrt(D)).  D must be 64 or 128.
+ *   GEMV            a = x [dim[0]=K], b = W [K, dim[1]=N] row-major, output [N].
+ *   COPY            a -> output, `size` bytes.
+ * Within one descriptor an output must coincide exactly with an input or
+ * not overlap it.  B must be at most 8 (lens are inline). */
+typedef struct gpuos_desc {
+    uint32_t op_id;          /*   0 */
+    uint32_t flags;          /*   4 */
+    uint64_t seq;            /*   8  set by gpuos_submit */
+    uint64_t input_a;        /*  16 */
+    uint64_t input_b;        /*  24 */
+    uint64_t output;         /*  32 */
+    uint64_t size;           /*  40 */
+    uint32_t dim[4];         /*  48 */
+    uint64_t aux[3];         /*  64 */
+    uint16_t dep_delta[6];   /*  88  set by gpuos_submit: wait for seq - delta (0 = none) */
+    uint16_t dep_range;      /* 100  set by gpuos_submit: wait for all of [seq - range, seq) */
+    uint16_t table_version;  /* 102  set by gpuos_submit */
+    union {
+        float f[6];
+        uint32_t u[6];
+        uint16_t lens[12];   /* lens[0..7] per batch row for ROPE/KV_APPEND/SDPA */
+    } param;                 /* 104 */
+} gpuos_desc;
+
+#ifdef __cplusplus
+static_assert(sizeof(gpuos_desc) == 128, "gpuos_desc must be 128 bytes");
+#endif
+
+/* ---------------------------------------------------------------- init */
+#define GPUOS_INIT_LOOPBACK (1u << 0) /* test only: no GPU; a host thread plays the
+                                         consumer, completes descriptors in a random
+                                         dependency-respecting order and computes nothing */
+
+typedef struct gpuos_init_params {
+    int32_t device;             /* HIP device ordinal */
+    uint32_t ring_entries;      /* power of two in [8, 32768]; 0 -> 4096 */
+    uint32_t num_wgs;           /* executor workgroups; 0 -> one per CU */
+    uint32_t waves_per_wg;      /* wave64s per workgroup, 1..4; 0 -> 4 */
+    uint32_t backoff_max;       /* s_sleep cap, 1..127; 0 -> 64 */
+    uint32_t flags;             /* GPUOS_INIT_* */
+    void* hip_stream;           /* optional hipStream_t for the executor (must be
+                                   non-blocking); NULL -> the library creates one */
+    uint64_t scratch_bytes;     /* device scratch for split ops; 0 -> 256 MiB */
+    uint32_t unit_queue_log2;   /* log2 of unit-queue entries, 12..24; 0 -> 20 */
+    uint32_t spin_limit_ms;     /* dependency-wait limit before ST_SPIN; 0 -> 20000 */
+} gpuos_init_params;
+
+/* Allocate the ring (fine-grained coherent host memory), the device tables
+ * and counters, bind the built-in op ids and launch the executor once.
+ * params may be NULL for defaults.  *out receives the context.
+ * Errors: E_INVAL (bad params), E_HIP (allocation or launch failed). */
+int gpuos_init(const gpuos_init_params* params, void** out);
+
+/* ------------------------------------------------------------- register */
+/* Bind op_id to a built-in kind with constants (the pages' operator
+ * injection: write the inactive table slot, then flip the version counter;
+ * digest page, section 3 Q2 "Dynamic Operator Table").  consts (may be NULL)
+ * points to `len` bytes: up to two floats, the kind's default parameter
+ * (LAYERNORM eps, ROPE theta, SDPA scale).  Descriptors submitted after this
+ * call returns use the new entry; earlier ones keep the old one.
+ * Errors: E_NOOP (op_id >= GPUOS_MAX_OPS or unknown kind), E_INVAL, E_HIP. */
+int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* consts, uint32_t len);
+
+/* --------------------------------------------------------------- submit */
+#define GPUOS_SUBMIT_BLOCK (1u << 0)     /* wait for free slots instead of E_FULL */
+#define GPUOS_SUBMIT_NOHAZARD (1u << 1)  /* caller guarantees no overlap with work in flight */
+#define GPUOS_SUBMIT_SERIAL (1u << 2)    /* each descriptor waits for its predecessor */
+
+/* Copy `count` descriptors into consecutive ring slots and commit them in
+ * order (store-release of each slot's stamp).  Before writing, every
+ * descriptor is checked and annotated with dependencies on earlier
+ * descriptors whose byte ranges it reads or writes (read-after-write,
+ * write-after-read, write-after-write), so results equal sequential
+ * execution.  The caller's array may be reused on return.  *first_seq
+ * (may be NULL) receives the sequence number of descriptor 0; the others
+ * follow consecutively.  All or nothing: on error no descriptor is
+ * submitted.  Errors: E_INVAL (a descriptor fails validation),
+ * E_FULL (fewer than count free slots and no BLOCK), E_STATE. */
+int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t flags,
+                 uint64_t* first_seq);
+
+/* Producer loop in native code: submit descs[0..sum(bursts)) as n_bursts
+ * consecutive gpuos_submit calls of burst_sizes[i] descriptors each (each
+ * burst is committed as a group).  Stops at the first error and returns it;
+ * *n_done (may be NULL) receives the number of descriptors submitted. */
+int gpuos_submit_bursts(void* ctx, const gpuos_desc* descs, const uint32_t* burst_sizes, uint32_t n_bursts,
+                        uint32_t flags, uint64_t* first_seq, uint64_t* n_done);
+
+/* ----------------------------------------------------------------- sync */
+#define GPUOS_SEQ_ALL 0xFFFFFFFFFFFFFFFFull
+
+/* Wait until every descriptor with seq <= upto_seq (GPUOS_SEQ_ALL: every
+ * submitted one) has completed.  timeout_ns < 0 waits forever.  Returns
+ * E_DEVICE if any of them completed with a non-zero status (the first one's
+ * seq and status go to *err_seq and *err_status, either may be NULL),
+ * E_TIMEOUT if the deadline passed. */
+int gpuos_sync(void* ctx, uint64_t upto_seq, int64_t timeout_ns, uint64_t* err_seq,
+               uint32_t* err_status);
+
+/* Non-blocking: 1 if seq has completed, 0 if not, negative on error. */
+int gpuos_query(void* ctx, uint64_t seq);
+
+/* ----------------------------------------------------- pause / shutdown */
+/* Wait for all submitted work, then stop the executor kernel (it exits and
+ * frees the compute units) while keeping the ring, tables and sequence
+ * numbers.  The next gpuos_submit or gpuos_resume relaunches it. */
+int gpuos_pause(void* ctx, int64_t timeout_ns);
+int gpuos_resume(void* ctx);
+
+/* Stop the executor (work already submitted is finished first) and free
+ * every resource.  The context pointer is invalid afterwards.  If the
+ * executor does not exit within the timeout the device is told to abort
+ * and E_TIMEOUT is returned after the context is freed as far as safe. */
+int gpuos_shutdown(void* ctx);
+
+/* ---------------------------------------------------------------- stats */
+typedef struct gpuos_stats {
+    uint64_t submitted;          /* descriptors submitted */
+    uint64_t completed;          /* descriptors observed complete by the host */
+    uint64_t full_rejections;    /* submits that returned E_FULL */
+    uint64_t launches;           /* executor launches (init + resumes) */
+    float last_launch_ms;        /* duration of the last finished executor launch
+                                    (HIP events on the executor stream) */
+    float total_launch_ms;       /* sum over finished launches */
+    uint64_t units;              /* work units executed (device counter) */
+    uint64_t fetch_batches;      /* ring batches the fetcher read (device counter) */
+    uint64_t fetched;            /* descriptors fetched (device counter) */
+    uint64_t dep_waits;          /* units that found a dependency not yet done */
+    uint32_t num_wgs, waves_per_wg, ring_entries, cu_count;
+    uint64_t next_seq;           /* sequence number the next submit will get */
+} gpuos_stats;
+
+/* Snapshot of the counters.  Device counters are added up when a launch
+ * ends (gpuos_pause / gpuos_shutdown); while the executor runs, units and
+ * dependency waits of still-running waves are not yet included. */
+int gpuos_stats_get(void* ctx, gpuos_stats* out);
+
+/* Test only (GPUOS_INIT_LOOPBACK contexts): copy up to max sequence
+ * numbers in the order the loopback consumer completed them. */
+int gpuos_loopback_order(void* ctx, uint64_t* out, uint64_t max, uint64_t* n_out);
+
+/* ------------------------------------------------- baselines (measurement) */
+/* Eager baseline: run each descriptor as its own hipLaunchKernel (one or
+ * more kernels per descriptor, same op bodies as the executor) on
+ * hip_stream, in order, with no dependency tracking beyond stream order.
+ * No persistent context is needed; scratch (device pointer, scratch_bytes)
+ * is caller-provided working memory for split ops (>= gpuos_eager_scratch_bytes).
+ * Asynchronous: returns after enqueueing.  Errors: E_INVAL, E_HIP. */
+int gpuos_eager_submit(const gpuos_desc* descs, uint32_t count, void* hip_stream,
+                       void* scratch, uint64_t scratch_bytes);
+/* Scratch bytes gpuos_eager_submit needs for these descriptors. */
+uint64_t gpuos_eager_scratch_bytes(const gpuos_desc* descs, uint32_t count);
+
+/* hipGraph baseline: capture the eager launches of `descs` into a graph
+ * and instantiate it; *graph_exec receives an opaque handle. */
+int gpuos_graph_build(const gpuos_desc* descs, uint32_t count, void* hip_stream, void* scratch,
+                      uint64_t scratch_bytes, void** graph_exec);
+int gpuos_graph_launch(void* graph_exec, void* hip_stream);
+int gpuos_graph_destroy(void* graph_exec);
+
+/* Null-kernel launch cost: launch an empty kernel n times on hip_stream;
+ * *ns_per_launch_async = host time per back-to-back launch call,
+ * *ns_launch_sync = mean time of launch + hipStreamSynchronize. */
+int gpuos_null_launch_bench(void* hip_stream, uint32_t n, double* ns_per_launch_async,
+                            double* ns_launch_sync);
+
+/* ABI version of the loaded library. */
+int gpuos_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPUOS_H */

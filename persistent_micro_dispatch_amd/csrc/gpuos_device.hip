@@ -1,0 +1,414 @@
+// Persistent executor for gfx950 (GPUOS digest page, section 3 Q2,
+// "Persistent Kernel Executor" and "Ring Buffer Communication Channel").
+//
+// Launched once; one workgroup per CU; every wave64 is independent.
+//  - Wave 0 of workgroup 0 is the fetcher.  It polls the host ring (fine-
+//    grained host memory, system-scope loads) 64 slots at a time, reads the
+//    committed descriptors over PCIe in one batch, resolves op_id through
+//    the dual-slot operator table at the descriptor's table version, splits
+//    each descriptor into work units, and publishes them to a unit queue in
+//    HBM with a release store of the queue tail.
+//  - Every other wave is a worker.  It claims the next unit with one atomic
+//    fetch-add, waits until the unit is published, waits for the
+//    descriptor's dependencies (done[] counters), runs the op body, and
+//    completes: the last unit of a descriptor writes done[slot] (agent
+//    scope) and the slot's stamp in host memory (system scope), which
+//    releases the ring slot.
+// Idle waits back off exponentially with s_sleep.  Every wait loop checks
+// the stop flag, so the grid drains when the host asks it to.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gpuos_internal.h"
+#include "gpuos_ops.h"
+
+namespace gpuos {
+
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_sys(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_agent(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_sys(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint64_t rl64(uint64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void nap(uint32_t n) {
+    for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
+}
+
+constexpr uint64_t STOP_DRAIN = 1, STOP_ABORT = 2;
+constexpr uint64_t NO_SCRATCH = ~0ull;
+
+// ------------------------------------------------------------------ worker
+__device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
+    DevCtl* C = A.dctl;
+    uint64_t n_units = 0, n_depw = 0;
+    const uint64_t N = (uint64_t)A.mask + 1;
+    for (;;) {
+        uint64_t u = 0;
+        if (lane == 0) u = __hip_atomic_fetch_add(&C->q_head, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        u = rl64(u, 0);
+        // wait until unit u is published
+        bool stop = false;
+        uint32_t bo = 1, polls = 0;
+        for (;;) {
+            const uint64_t tail = ld_agent(&C->q_tail);
+            if (tail > u) break;
+            if ((++polls & 3u) == 0 && ld_agent(&C->stop)) { stop = true; break; }
+            const uint64_t dist = u - tail;
+            bo = dist > 512 ? A.backoff_max : (bo * 2 < A.backoff_max ? bo * 2 : A.backoff_max);
+            nap(bo);
+        }
+        if (stop) break;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const uint64_t ent = A.queue[u & A.qmask];
+        const uint64_t seq = ent >> 24;
+        const uint32_t tile = (uint32_t)(ent & 0xFFFFFFu);
+        const uint64_t slot = seq & A.mask;
+        uint64_t w = 0;
+        if (lane < 16) w = ((const uint64_t*)&A.mirror[slot])[lane];
+        else if (lane < 20) w = ((const uint64_t*)&A.meta[slot])[lane - 16];
+        Unit U;
+        const uint64_t w0 = rl64(w, 0), w6 = rl64(w, 6), w7 = rl64(w, 7);
+        const uint64_t w11 = rl64(w, 11), w12 = rl64(w, 12);
+        const uint64_t w13 = rl64(w, 13), w14 = rl64(w, 14), w15 = rl64(w, 15);
+        const uint64_t m0 = rl64(w, 16), m1 = rl64(w, 17), m3 = rl64(w, 19);
+        U.seq = seq;
+        U.flags = (uint32_t)(w0 >> 32);
+        U.tile = tile;
+        U.a = rl64(w, 2); U.b = rl64(w, 3); U.out = rl64(w, 4); U.size = rl64(w, 5);
+        U.dim[0] = (uint32_t)w6; U.dim[1] = (uint32_t)(w6 >> 32);
+        U.dim[2] = (uint32_t)w7; U.dim[3] = (uint32_t)(w7 >> 32);
+        U.aux0 = rl64(w, 8); U.aux1 = rl64(w, 9); U.aux2 = rl64(w, 10);
+        U.pf[0] = __uint_as_float((uint32_t)w13); U.pf[1] = __uint_as_float((uint32_t)(w13 >> 32));
+        U.pf[2] = __uint_as_float((uint32_t)w14); U.pf[3] = __uint_as_float((uint32_t)(w14 >> 32));
+        U.pf[4] = __uint_as_float((uint32_t)w15); U.pf[5] = __uint_as_float((uint32_t)(w15 >> 32));
+        U.lensw[0] = w13;
+        U.lensw[1] = w14;
+        U.kind = (uint32_t)m0;
+        uint32_t status = (uint32_t)(m0 >> 32);
+        U.ntiles = (uint32_t)m1;
+        U.p0 = __uint_as_float((uint32_t)(m1 >> 32));
+        U.scratch = m3 == NO_SCRATCH ? nullptr : A.scratch + (m3 % A.scratch_bytes);
+        // dependencies: explicit seq deltas (lanes 0..5) and a contiguous range
+        const uint32_t delta = lane < 4 ? (uint32_t)((w11 >> (16 * lane)) & 0xFFFFu)
+                             : lane < 6 ? (uint32_t)((w12 >> (16 * (lane - 4))) & 0xFFFFu) : 0u;
+        uint64_t rlo = seq - ((w12 >> 32) & 0xFFFFu);
+        if (w11 != 0 || (w12 & 0xFFFFFFFFFFFFull) != 0) {
+            bool counted = false;
+            uint64_t t0 = 0;
+            uint32_t dbo = 1;
+            for (;;) {
+                bool ok = true;
+                if (delta) {
+                    const uint64_t d = seq - delta;
+                    ok = ld_agent(&A.done[d & A.mask]) >= d;
+                }
+                while (rlo < seq) {
+                    const uint64_t x = rlo + lane;
+                    const bool okr = x >= seq || ld_agent(&A.done[x & A.mask]) >= x;
+                    const uint64_t bal = __ballot(okr);
+                    if (bal == ~0ull) { rlo += 64; continue; }
+                    rlo += (uint64_t)(__ffsll((long long)~bal) - 1);
+                    break;
+                }
+                if (__all(ok) && rlo >= seq) break;
+                if (!counted) { counted = true; ++n_depw; t0 = wall_clock64(); }
+                if (ld_agent(&C->stop) == STOP_ABORT) { stop = true; break; }
+                if (wall_clock64() - t0 > A.spin_limit_ticks) {
+                    status = GPUOS_ST_SPIN;
+                    if (lane == 0) {
+                        __hip_atomic_store(&C->error, (uint64_t)GPUOS_ST_SPIN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        st_sys(&A.hctl->dev_error, GPUOS_ST_SPIN);
+                    }
+                    break;
+                }
+                nap(dbo);
+                dbo = dbo * 2 < A.backoff_max ? dbo * 2 : A.backoff_max;
+            }
+            if (stop) break;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        if (status == GPUOS_ST_OK && U.kind != KIND_BAD) run_unit(U, lane);
+        ++n_units;
+        // completion: the last unit of the descriptor releases the slot
+        bool last = true;
+        if (U.ntiles > 1) {
+            uint32_t prev = 0;
+            if (lane == 0)
+                prev = __hip_atomic_fetch_add(&A.tiles_done[slot], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
+            last = prev == U.ntiles - 1;
+        }
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // system scope: outputs visible to all
+            if (lane == 0) {
+                st_agent(&A.done[slot], seq);
+                if (status != GPUOS_ST_OK)
+                    __hip_atomic_store(&A.status[slot], status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                st_sys(&A.stamp[slot], seq + N);
+            }
+        }
+    }
+    if (lane == 0) {
+        __hip_atomic_fetch_add(&C->stat_units, n_units, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&C->stat_dep_waits, n_depw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ----------------------------------------------------------------- fetcher
+__device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, uint64_t* lds, uint64_t* pref) {
+    DevCtl* C = A.dctl;
+    const uint64_t mask = A.mask;
+    const uint64_t Q = (uint64_t)A.qmask + 1;
+    const uint64_t S = A.scratch_bytes;
+    const uint64_t* ringw = (const uint64_t*)A.ring;
+    uint64_t* mirw = (uint64_t*)A.mirror;
+    uint64_t f = A.start_seq, u_next = 0, sv_next = 0, cw = A.start_seq;
+    uint32_t cur_ver = 0xFFFFFFFFu, bo = 1;
+    uint64_t batches = 0, fetched = 0;
+    uint64_t stop_code = STOP_DRAIN;
+    for (;;) {
+        const uint64_t sl = f + lane;
+        const uint64_t st = ld_sys(&A.stamp[sl & mask]);
+        const uint64_t rb = __ballot(st == sl + 1);
+        uint32_t count = rb == ~0ull ? 64u : (uint32_t)(__ffsll((long long)~rb) - 1);
+        if (count == 0) {
+            const uint64_t abt = ld_sys(&A.hctl->abort);
+            if (abt) { stop_code = STOP_ABORT; break; }
+            const uint64_t stp = ld_sys(&A.hctl->stop);
+            if (stp) {
+                // the host commits before it sets stop: look once more
+                if (ld_sys(&A.stamp[f & mask]) == f + 1) continue;
+                break;
+            }
+            nap(bo);
+            bo = bo * 2 < A.backoff_max ? bo * 2 : A.backoff_max;
+            continue;
+        }
+        bo = 1;
+        // read the committed bodies (count x 16 words) in one go
+        const uint32_t nw = count * 16u;
+        uint64_t v[16];
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k) {
+            const uint32_t wi = lane + 64u * k;
+            if (wi < nw) v[k] = ld_sys(&ringw[((f + (wi >> 4)) & mask) * 16u + (wi & 15u)]);
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k) {
+            const uint32_t wi = lane + 64u * k;
+            if (wi < nw) lds[wi] = v[k];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        // lane i parses descriptor i
+        const bool act = lane < count;
+        const uint64_t* dw = lds + (act ? lane : 0) * 16u;
+        const uint64_t d0 = dw[0], d12 = dw[12];
+        const uint32_t op_id = (uint32_t)d0;
+        const uint32_t ver = (uint32_t)(d12 >> 48);
+        const uint32_t maxver = (uint32_t)__shfl((int)ver, (int)count - 1, 64);
+        if (maxver != cur_ver) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");  // the host rewrote a table slot
+            cur_ver = maxver;
+        }
+        PlanIn pin;
+        pin.flags = (uint32_t)(d0 >> 32);
+        pin.size = dw[5];
+        pin.dim[0] = (uint32_t)dw[6]; pin.dim[1] = (uint32_t)(dw[6] >> 32);
+        pin.dim[2] = (uint32_t)dw[7]; pin.dim[3] = (uint32_t)(dw[7] >> 32);
+        pin.a = dw[2]; pin.b = dw[3]; pin.out = dw[4]; pin.aux0 = dw[8]; pin.aux1 = dw[9];
+        pin.lensw[0] = dw[13];
+        pin.lensw[1] = dw[14];
+        uint32_t kind = KIND_BAD;
+        float p0 = 0.0f;
+        if (op_id < GPUOS_MAX_OPS) {
+            const TableEntry* te = &A.table[(ver & 1u) * GPUOS_MAX_OPS + op_id];
+            kind = te->kind;
+            p0 = te->p0;
+        }
+        Plan pl;
+        if (kind < GPUOS_KIND_COUNT) {
+            pin.kind = kind;
+            pl = make_plan(pin);
+        } else {
+            pl.status = GPUOS_ST_BAD_OP;
+            pl.ntiles = 1;
+            pl.scratch = 0;
+        }
+        if (pl.status != GPUOS_ST_OK) { kind = KIND_BAD; pl.ntiles = 1; pl.scratch = 0; }
+        uint32_t nt = act ? pl.ntiles : 0u;
+        // inclusive prefix of units over lanes
+        uint64_t inc = nt;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const uint64_t o = __shfl_up(inc, (unsigned)m, 64);
+            if ((int)lane >= m) inc += o;
+        }
+        // scratch allocation in lane order (few descriptors need any); my_mark
+        // is the watermark before descriptor i, my_end the one after it
+        const uint64_t need = act ? ((pl.scratch + 255u) & ~255ull) : 0ull;
+        uint64_t my_sv = NO_SCRATCH, my_mark = sv_next, sv = sv_next;
+        uint64_t nm = __ballot(need > 0);
+        while (nm) {
+            const int j = __ffsll((long long)nm) - 1;
+            nm &= nm - 1;
+            const uint64_t nj = rl64(need, j);
+            const uint64_t phys = sv % S;
+            if (phys + nj > S) sv += S - phys;  // an allocation never wraps
+            if ((int)lane == j) my_sv = sv;
+            sv += nj;
+            if ((int)lane > j) my_mark = sv;
+        }
+        const uint64_t sv_end_i = my_sv != NO_SCRATCH ? my_sv + need : my_mark;
+        // capacity: units and scratch still held by incomplete descriptors
+        uint32_t fit;
+        for (;;) {
+            // advance the completion watermark cw
+            for (;;) {
+                if (cw >= f) break;
+                const uint64_t x = cw + lane;
+                const bool ok = x >= f || ld_agent(&A.done[x & mask]) >= x;
+                const uint64_t bal = __ballot(ok);
+                if (bal == ~0ull) { cw = cw + 64 < f ? cw + 64 : f; continue; }
+                cw += (uint64_t)(__ffsll((long long)~bal) - 1);
+                break;
+            }
+            const uint64_t cw_units = cw < f ? A.meta[cw & mask].ubegin : u_next;
+            const uint64_t cw_scr = cw < f ? A.meta[cw & mask].scratch_mark : sv_next;
+            const bool ok = !act || ((u_next + inc - cw_units <= Q) && (sv_end_i - cw_scr <= S));
+            const uint64_t fb = __ballot(ok);
+            fit = fb == ~0ull ? 64u : (uint32_t)(__ffsll((long long)~fb) - 1);
+            if (fit > count) fit = count;
+            if (fit > 0) break;
+            if (ld_sys(&A.hctl->abort)) { stop_code = STOP_ABORT; break; }
+            nap(A.backoff_max);
+        }
+        if (fit == 0) break;  // abort while waiting for space
+        count = fit;
+        const bool keep = lane < count;
+        const uint64_t T = rl64(inc, (int)count - 1);
+        const uint64_t ubegin = u_next + inc - nt;
+        // mirror bodies, meta, per-slot unit counters
+#pragma unroll
+        for (uint32_t k = 0; k < 16; ++k) {
+            const uint32_t wi = lane + 64u * k;
+            if (wi < count * 16u) mirw[((f + (wi >> 4)) & mask) * 16u + (wi & 15u)] = v[k];
+        }
+        if (keep) {
+            const uint64_t slot = (f + lane) & mask;
+            MirrorMeta* mm = &A.meta[slot];
+            mm->kind = kind;
+            mm->status = pl.status;
+            mm->ntiles = nt;
+            mm->p0 = p0;
+            mm->ubegin = ubegin;
+            mm->scratch_v = my_sv;
+            mm->scratch_mark = my_mark;
+            A.tiles_done[slot] = 0;
+            pref[lane] = inc - nt;
+        }
+        // zero the group counters of descriptors that use scratch
+        uint64_t zm = __ballot(keep && my_sv != NO_SCRATCH);
+        while (zm) {
+            const int j = __ffsll((long long)zm) - 1;
+            zm &= zm - 1;
+            const uint64_t svj = rl64(my_sv, j);
+            uint8_t* base = A.scratch + (svj % S);
+#pragma unroll
+            for (uint32_t k = 0; k < COUNTER_AREA / 16u / 64u; ++k)
+                st16(base + (uint64_t)(lane + 64u * k) * 16u, u32x4{0, 0, 0, 0});
+        }
+        if (lane == 0) pref[count] = T;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        // one queue entry per unit: (seq << 24) | tile
+        for (uint64_t wi = lane; wi < T; wi += 64u) {
+            uint32_t lo = 0, hi = count;  // find j with pref[j] <= wi < pref[j+1]
+            while (hi - lo > 1) {
+                const uint32_t mid = (lo + hi) >> 1;
+                if (pref[mid] <= wi) lo = mid; else hi = mid;
+            }
+            A.queue[(u_next + wi) & A.qmask] = ((f + lo) << 24) | (wi - pref[lo]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        if (lane == 0) st_agent(&C->q_tail, u_next + T);
+        f += count;
+        u_next += T;
+        sv_next = rl64(sv_end_i, (int)count - 1);
+        ++batches;
+        fetched += count;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (lane == 0) {
+        st_agent(&C->stop, stop_code);
+        __hip_atomic_fetch_add(&C->stat_batches, batches, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(&C->stat_fetched, fetched, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) gpuos_executor(ExecArgs A) {
+    __shared__ uint64_t lds[64 * 16 + 72];
+    const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    if (blockIdx.x == 0 && wave == 0) fetcher_loop(A, lane, lds, lds + 64 * 16);
+    else worker_loop(A, lane);
+    if (lane == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+        __hip_atomic_fetch_add(&A.hctl->exited, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+}
+
+// ------------------------------------------------------------ eager kernels
+// One launch per descriptor; wave w of block x runs tile 4x + w.
+extern "C" __global__ void __launch_bounds__(256) gpuos_eager_kernel(gpuos_desc d, uint32_t kind, uint32_t ntiles,
+                                                                      uint8_t* scratch) {
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t tile = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (tile >= ntiles) return;
+    Unit U;
+    U.seq = 0;
+    U.kind = kind;
+    U.flags = d.flags;
+    U.tile = tile;
+    U.ntiles = ntiles;
+    U.a = d.input_a; U.b = d.input_b; U.out = d.output; U.size = d.size;
+    for (int i = 0; i < 4; ++i) U.dim[i] = d.dim[i];
+    U.aux0 = d.aux[0]; U.aux1 = d.aux[1]; U.aux2 = d.aux[2];
+    for (int i = 0; i < 6; ++i) U.pf[i] = d.param.f[i];
+    U.lensw[0] = (uint64_t)d.param.u[0] | ((uint64_t)d.param.u[1] << 32);
+    U.lensw[1] = (uint64_t)d.param.u[2] | ((uint64_t)d.param.u[3] << 32);
+    U.p0 = 0.0f;
+    U.scratch = scratch;
+    run_unit(U, lane);
+}
+
+extern "C" __global__ void gpuos_null_kernel() {}
+
+// ------------------------------------------------------ host-side launchers
+hipError_t launch_executor(const ExecArgs& a, uint32_t grid, uint32_t block, hipStream_t s) {
+    hipLaunchKernelGGL(gpuos_executor, dim3(grid), dim3(block), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_eager(const gpuos_desc& d, uint32_t kind, uint32_t ntiles, uint8_t* scratch, hipStream_t s) {
+    const uint32_t grid = (ntiles + 3u) / 4u;
+    hipLaunchKernelGGL(gpuos_eager_kernel, dim3(grid), dim3(256), 0, s, d, kind, ntiles, scratch);
+    return hipGetLastError();
+}
+
+hipError_t launch_null(hipStream_t s) {
+    hipLaunchKernelGGL(gpuos_null_kernel, dim3(1), dim3(64), 0, s);
+    return hipGetLastError();
+}
+
+}  // namespace gpuos

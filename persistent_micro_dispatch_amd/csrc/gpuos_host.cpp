@@ -1,0 +1,849 @@
+// Host runtime of the persistent micro-op dispatcher (C ABI in gpuos.h).
+//
+// Submission follows the pages' producer protocol (GPUOS digest page,
+// section 3 Q2 "Ring Buffer Communication Channel"): prepare descriptor ->
+// acquire slot -> write -> commit with store-release.  Slot p of a ring of
+// N entries is free for sequence number p when stamp[p % N] == p; the host
+// writes the body and stores stamp = p + 1 (commit); the executor stores
+// stamp = p + N when descriptor p has completed, which frees the slot for
+// p + N (the slot is released after the op finishes).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include <time.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <mutex>
+#include <random>
+#include <thread>
+#include <vector>
+
+#include "gpuos.h"
+#include "gpuos_internal.h"
+#include "hazard.h"
+
+#if defined(__x86_64__)
+#include <immintrin.h>
+#define GPUOS_PAUSE() _mm_pause()
+#else
+#define GPUOS_PAUSE() std::this_thread::yield()
+#endif
+
+namespace gpuos {
+hipError_t launch_executor(const ExecArgs& a, uint32_t grid, uint32_t block, hipStream_t s);
+hipError_t launch_eager(const gpuos_desc& d, uint32_t kind, uint32_t ntiles, uint8_t* scratch, hipStream_t s);
+hipError_t launch_null(hipStream_t s);
+}  // namespace gpuos
+
+using namespace gpuos;
+
+namespace {
+
+inline uint64_t now_ns() {
+    return (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(
+               std::chrono::steady_clock::now().time_since_epoch())
+        .count();
+}
+
+template <typename T>
+inline T ld_acq(const T* p) { return __atomic_load_n(p, __ATOMIC_ACQUIRE); }
+template <typename T>
+inline void st_rel(T* p, T v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
+
+// --------------------------------------------------------------------------
+// Operand byte ranges of a descriptor for hazard tracking (conservative
+// bounding boxes for the strided KV-cache rows).
+// --------------------------------------------------------------------------
+int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
+    int n = 0;
+    auto add = [&](uint64_t p, uint64_t bytes, bool w) {
+        if (p && bytes) out[n++] = Access{p, p + bytes, w};
+    };
+    const uint32_t di = dt_in(d.flags), dout = dt_out(d.flags);
+    const uint64_t es = esz(di), eo = esz(dout);
+    const uint64_t sz = d.size;
+    const uint64_t lensw[2] = {(uint64_t)d.param.u[0] | ((uint64_t)d.param.u[1] << 32),
+                               (uint64_t)d.param.u[2] | ((uint64_t)d.param.u[3] << 32)};
+    switch (kind) {
+        case GPUOS_OP_ADD:
+        case GPUOS_OP_MUL:
+            add(d.input_a, sz * es, false);
+            add(d.input_b, sz * es, false);
+            add(d.output, sz * eo, true);
+            break;
+        case GPUOS_OP_RELU:
+        case GPUOS_OP_GELU:
+            add(d.input_a, sz * es, false);
+            add(d.output, sz * eo, true);
+            break;
+        case GPUOS_OP_SUM:
+        case GPUOS_OP_MAX:
+        case GPUOS_OP_MIN:
+            add(d.input_a, sz * d.dim[0] * es, false);
+            add(d.output, sz * eo, true);
+            break;
+        case GPUOS_OP_SOFTMAX:
+            add(d.input_a, sz * d.dim[0] * es, false);
+            add(d.output, sz * d.dim[0] * eo, true);
+            break;
+        case GPUOS_OP_LAYERNORM:
+            add(d.input_a, sz * d.dim[0] * es, false);
+            add(d.aux[0], (uint64_t)d.dim[0] * es, false);
+            add(d.aux[1], (uint64_t)d.dim[0] * es, false);
+            add(d.output, sz * d.dim[0] * eo, true);
+            break;
+        case GPUOS_OP_ROPE: {
+            const uint64_t bytes = sz * d.dim[0] * d.dim[1] * es;
+            add(d.input_a, bytes, false);
+            add(d.input_b, bytes, false);
+            add(d.input_a, bytes, true);
+            add(d.input_b, bytes, true);
+            break;
+        }
+        case GPUOS_OP_KV_APPEND: {
+            const uint64_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            add(d.input_a, sz * H * D * es, false);
+            add(d.input_b, sz * H * D * es, false);
+            for (uint32_t b = 0; b < sz && b < MAX_B; ++b) {
+                const uint64_t pos = lens_at(lensw, b) - 1;
+                const uint64_t lo = ((b * H) * C + pos) * D * es;
+                const uint64_t hi = ((b * H + H - 1) * C + pos) * D * es + D * es;
+                add(d.aux[0] + lo, hi - lo, true);
+                add(d.aux[1] + lo, hi - lo, true);
+            }
+            break;
+        }
+        case GPUOS_OP_SDPA: {
+            const uint64_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            add(d.input_a, sz * H * D * es, false);
+            for (uint32_t b = 0; b < sz && b < MAX_B; ++b) {
+                const uint64_t L = lens_at(lensw, b);
+                const uint64_t lo = (b * H) * C * D * es;
+                const uint64_t hi = ((b * H + H - 1) * C + L) * D * es;
+                add(d.aux[0] + lo, hi - lo, false);
+                add(d.aux[1] + lo, hi - lo, false);
+            }
+            add(d.output, sz * H * D * eo, true);
+            break;
+        }
+        case GPUOS_OP_GEMV:
+            add(d.input_a, (uint64_t)d.dim[0] * es, false);
+            add(d.input_b, (uint64_t)d.dim[0] * d.dim[1] * es, false);
+            add(d.output, (uint64_t)d.dim[1] * eo, true);
+            break;
+        case GPUOS_OP_COPY:
+            add(d.input_a, sz, false);
+            add(d.output, sz, true);
+            break;
+        default:
+            break;
+    }
+    return n;
+}
+
+PlanIn plan_in(uint32_t kind, const gpuos_desc& d) {
+    PlanIn p;
+    p.kind = kind;
+    p.flags = d.flags;
+    p.size = d.size;
+    for (int i = 0; i < 4; ++i) p.dim[i] = d.dim[i];
+    p.lensw[0] = (uint64_t)d.param.u[0] | ((uint64_t)d.param.u[1] << 32);
+    p.lensw[1] = (uint64_t)d.param.u[2] | ((uint64_t)d.param.u[3] << 32);
+    p.a = d.input_a;
+    p.b = d.input_b;
+    p.out = d.output;
+    p.aux0 = d.aux[0];
+    p.aux1 = d.aux[1];
+    return p;
+}
+
+void* aligned_zalloc(size_t bytes) {
+    void* p = nullptr;
+    if (posix_memalign(&p, 4096, (bytes + 4095) & ~(size_t)4095) != 0) return nullptr;
+    memset(p, 0, bytes);
+    return p;
+}
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+// Context
+// --------------------------------------------------------------------------
+struct gpuos_ctx {
+    gpuos_init_params P{};
+    bool loopback = false;
+    uint32_t N = 0, mask = 0, Q = 0, cu_count = 0;
+    // host-coherent ring memory
+    gpuos_desc* ring = nullptr;
+    uint64_t* stamp = nullptr;
+    uint32_t* status = nullptr;
+    HostCtl* hctl = nullptr;
+    // device memory
+    DevCtl* dctl = nullptr;
+    gpuos_desc* mirror = nullptr;
+    MirrorMeta* meta = nullptr;
+    uint64_t* done = nullptr;
+    uint32_t* tiles_done = nullptr;
+    uint64_t* queue = nullptr;
+    TableEntry* table = nullptr;
+    uint8_t* scratch = nullptr;
+    hipStream_t exec = nullptr, aux = nullptr;
+    bool own_exec = false;
+    hipEvent_t ev_start = nullptr, ev_stop = nullptr;
+    uint64_t spin_ticks = 0;
+    // producer state
+    std::mutex mu;
+    uint64_t next_seq = 0;
+    uint64_t wm = 0;  // every seq < wm observed complete
+    HazardTracker hz;
+    std::vector<uint64_t> deps;
+    TableEntry shadow[2][GPUOS_MAX_OPS];
+    uint32_t version = 0;
+    uint64_t flip_seq = 0;  // first seq submitted under the current version
+    // errors
+    struct Err { uint64_t seq; uint32_t st; };
+    std::vector<Err> errors;
+    // executor state
+    bool running = false;
+    uint64_t launches = 0;
+    float last_ms = 0.f, total_ms = 0.f;
+    // stats (device counters are accumulated here when a launch ends)
+    uint64_t submitted = 0, completed = 0, full_rej = 0;
+    uint64_t acc_units = 0, acc_depw = 0, acc_batches = 0, acc_fetched = 0;
+    // loopback consumer
+    std::thread lb_thread;
+    std::atomic<bool> lb_stop{false};
+    std::vector<uint64_t> lb_done;
+    std::vector<uint64_t> lb_order;
+    std::mutex lb_mu;
+};
+
+namespace {
+
+void refresh_wm(gpuos_ctx* c) {
+    const uint64_t N = c->N;
+    while (c->wm < c->next_seq) {
+        const uint64_t s = c->wm;
+        const uint64_t st = ld_acq(&c->stamp[s & c->mask]);
+        if (st < s + N) break;
+        const uint32_t code = ld_acq(&c->status[s & c->mask]);
+        if (code) c->errors.push_back({s, code});
+        ++c->completed;
+        ++c->wm;
+    }
+}
+
+int executor_launch(gpuos_ctx* c) {
+    if (c->loopback || c->running) return GPUOS_OK;
+    hipError_t e = hipMemsetAsync(c->dctl, 0, sizeof(DevCtl), c->exec);
+    if (e != hipSuccess) return GPUOS_E_HIP;
+    st_rel(&c->hctl->stop, (uint64_t)0);
+    st_rel(&c->hctl->abort, (uint64_t)0);
+    st_rel(&c->hctl->exited, (uint64_t)0);
+    ExecArgs a{};
+    a.ring = c->ring;
+    a.stamp = c->stamp;
+    a.status = c->status;
+    a.hctl = c->hctl;
+    a.dctl = c->dctl;
+    a.mirror = c->mirror;
+    a.meta = c->meta;
+    a.done = c->done;
+    a.tiles_done = c->tiles_done;
+    a.queue = c->queue;
+    a.table = c->table;
+    a.scratch = c->scratch;
+    a.scratch_bytes = c->P.scratch_bytes;
+    a.start_seq = c->next_seq;
+    a.spin_limit_ticks = c->spin_ticks;
+    a.mask = c->mask;
+    a.qmask = c->Q - 1;
+    a.backoff_max = c->P.backoff_max;
+    if (hipEventRecord(c->ev_start, c->exec) != hipSuccess) return GPUOS_E_HIP;
+    if (launch_executor(a, c->P.num_wgs, 64u * c->P.waves_per_wg, c->exec) != hipSuccess) return GPUOS_E_HIP;
+    if (hipEventRecord(c->ev_stop, c->exec) != hipSuccess) return GPUOS_E_HIP;
+    c->running = true;
+    ++c->launches;
+    return GPUOS_OK;
+}
+
+// Ask the executor to drain and exit; wait for its completion event.
+int executor_stop(gpuos_ctx* c, int64_t timeout_ns) {
+    if (c->loopback || !c->running) return GPUOS_OK;
+    st_rel(&c->hctl->stop, (uint64_t)1);
+    const uint64_t t0 = now_ns();
+    bool aborted = false;
+    for (;;) {
+        hipError_t q = hipEventQuery(c->ev_stop);
+        if (q == hipSuccess) break;
+        if (q != hipErrorNotReady) return GPUOS_E_HIP;
+        const uint64_t el = now_ns() - t0;
+        if (!aborted && timeout_ns >= 0 && el > (uint64_t)timeout_ns) {
+            st_rel(&c->hctl->abort, (uint64_t)1);
+            aborted = true;
+        }
+        if (aborted && el > (uint64_t)timeout_ns + 5000000000ull) return GPUOS_E_TIMEOUT;
+        std::this_thread::sleep_for(std::chrono::microseconds(20));
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->ev_start, c->ev_stop) == hipSuccess) {
+        c->last_ms = ms;
+        c->total_ms += ms;
+    }
+    c->running = false;
+    DevCtl d;
+    if (hipMemcpyAsync(&d, c->dctl, sizeof(DevCtl), hipMemcpyDeviceToHost, c->aux) == hipSuccess &&
+        hipStreamSynchronize(c->aux) == hipSuccess) {
+        c->acc_units += d.stat_units;
+        c->acc_depw += d.stat_dep_waits;
+        c->acc_batches += d.stat_batches;
+        c->acc_fetched += d.stat_fetched;
+    }
+    return aborted ? GPUOS_E_TIMEOUT : GPUOS_OK;
+}
+
+// ---- loopback consumer (test only): completes descriptors in a random order
+// that respects their dependency annotations, computing nothing.
+void loopback_main(gpuos_ctx* c) {
+    std::mt19937_64 rng(12345);
+    const uint64_t N = c->N;
+    uint64_t f = c->N;  // next seq to fetch
+    struct Pend { uint64_t seq; gpuos_desc d; };
+    std::vector<Pend> pend;
+    auto is_done = [&](uint64_t s) { return c->lb_done[s & c->mask] >= s; };
+    while (!c->lb_stop.load()) {
+        bool progress = false;
+        while (ld_acq(&c->stamp[f & c->mask]) == f + 1 && pend.size() < 256) {
+            pend.push_back({f, c->ring[f & c->mask]});
+            ++f;
+            progress = true;
+        }
+        // runnable candidates
+        std::vector<size_t> ready;
+        for (size_t i = 0; i < pend.size(); ++i) {
+            const gpuos_desc& d = pend[i].d;
+            const uint64_t s = pend[i].seq;
+            bool ok = true;
+            for (int k = 0; k < 6 && ok; ++k)
+                if (d.dep_delta[k]) ok = is_done(s - d.dep_delta[k]);
+            for (uint64_t x = s - d.dep_range; x < s && ok; ++x) ok = is_done(x);
+            if (ok) ready.push_back(i);
+        }
+        if (!ready.empty()) {
+            const size_t pick = ready[rng() % ready.size()];
+            const Pend p = pend[pick];
+            pend.erase(pend.begin() + (long)pick);
+            const uint32_t slot = (uint32_t)(p.seq & c->mask);
+            // mirror the device's table lookup and shape check for the status
+            uint32_t st = GPUOS_ST_OK;
+            const uint32_t op = p.d.op_id;
+            if (op >= GPUOS_MAX_OPS) st = GPUOS_ST_BAD_OP;
+            else {
+                std::lock_guard<std::mutex> g(c->lb_mu);
+                const uint32_t kind = c->shadow[p.d.table_version & 1u][op].kind;
+                if (kind >= GPUOS_KIND_COUNT) st = GPUOS_ST_BAD_OP;
+                else st = make_plan(plan_in(kind, p.d)).status;
+            }
+            {
+                std::lock_guard<std::mutex> g(c->lb_mu);
+                c->lb_order.push_back(p.seq);
+            }
+            c->lb_done[slot] = p.seq;
+            if (st) st_rel(&c->status[slot], st);
+            st_rel(&c->stamp[slot], p.seq + N);
+            progress = true;
+        }
+        if (!progress) std::this_thread::sleep_for(std::chrono::microseconds(5));
+    }
+}
+
+int validate_params(gpuos_init_params& P) {
+    if (P.ring_entries == 0) P.ring_entries = 4096;
+    if (P.ring_entries < 8 || P.ring_entries > 32768 || (P.ring_entries & (P.ring_entries - 1))) return GPUOS_E_INVAL;
+    if (P.waves_per_wg == 0) P.waves_per_wg = 4;
+    if (P.waves_per_wg > 4) return GPUOS_E_INVAL;
+    if (P.backoff_max == 0) P.backoff_max = 64;
+    if (P.backoff_max > 127) return GPUOS_E_INVAL;
+    if (P.scratch_bytes == 0) P.scratch_bytes = 256ull << 20;
+    if (P.scratch_bytes < (1u << 20)) return GPUOS_E_INVAL;
+    P.scratch_bytes = (P.scratch_bytes + 255) & ~255ull;
+    if (P.unit_queue_log2 == 0) P.unit_queue_log2 = 20;
+    if (P.unit_queue_log2 < 12 || P.unit_queue_log2 > 24) return GPUOS_E_INVAL;
+    if (P.spin_limit_ms == 0) P.spin_limit_ms = 20000;
+    return GPUOS_OK;
+}
+
+void free_ctx(gpuos_ctx* c) {
+    if (c->loopback) {
+        c->lb_stop = true;
+        if (c->lb_thread.joinable()) c->lb_thread.join();
+        free(c->ring);
+        free(c->stamp);
+        free(c->status);
+        free(c->hctl);
+        delete c;
+        return;
+    }
+    if (c->ring) (void)hipHostFree(c->ring);
+    if (c->stamp) (void)hipHostFree(c->stamp);
+    if (c->status) (void)hipHostFree(c->status);
+    if (c->hctl) (void)hipHostFree(c->hctl);
+    void* dev[] = {c->dctl, c->mirror, c->meta, c->done, c->tiles_done, c->queue, c->table, c->scratch};
+    for (void* p : dev)
+        if (p) (void)hipFree(p);
+    if (c->ev_start) (void)hipEventDestroy(c->ev_start);
+    if (c->ev_stop) (void)hipEventDestroy(c->ev_stop);
+    if (c->aux) (void)hipStreamDestroy(c->aux);
+    if (c->own_exec && c->exec) (void)hipStreamDestroy(c->exec);
+    delete c;
+}
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+// C ABI
+// --------------------------------------------------------------------------
+extern "C" {
+
+int gpuos_abi_version(void) { return GPUOS_ABI_VERSION; }
+
+int gpuos_init(const gpuos_init_params* params, void** out) {
+    if (!out) return GPUOS_E_INVAL;
+    *out = nullptr;
+    gpuos_init_params P{};
+    if (params) P = *params;
+    int rc = validate_params(P);
+    if (rc) return rc;
+    gpuos_ctx* c = new gpuos_ctx();
+    c->P = P;
+    c->N = P.ring_entries;
+    c->mask = c->N - 1;
+    c->Q = 1u << P.unit_queue_log2;
+    c->loopback = (P.flags & GPUOS_INIT_LOOPBACK) != 0;
+    c->next_seq = c->N;  // seqs start at N so that done[i] = i means "nothing done"
+    c->wm = c->N;
+    c->flip_seq = c->N;
+    for (int v = 0; v < 2; ++v)
+        for (uint32_t i = 0; i < GPUOS_MAX_OPS; ++i)
+            c->shadow[v][i] = TableEntry{i < GPUOS_KIND_COUNT ? i : (uint32_t)GPUOS_KIND_EMPTY, 0, 0.f, 0.f, 0, 0};
+    const size_t N = c->N;
+    if (c->loopback) {
+        c->ring = (gpuos_desc*)aligned_zalloc(N * sizeof(gpuos_desc));
+        c->stamp = (uint64_t*)aligned_zalloc(N * 8);
+        c->status = (uint32_t*)aligned_zalloc(N * 4);
+        c->hctl = (HostCtl*)aligned_zalloc(sizeof(HostCtl));
+        if (!c->ring || !c->stamp || !c->status || !c->hctl) { free_ctx(c); return GPUOS_E_INVAL; }
+        for (size_t i = 0; i < N; ++i) c->stamp[i] = N + i;
+        c->lb_done.assign(N, 0);
+        for (size_t i = 0; i < N; ++i) c->lb_done[i] = i;
+        c->P.num_wgs = 1;
+        c->lb_thread = std::thread(loopback_main, c);
+        *out = c;
+        return GPUOS_OK;
+    }
+    hipError_t e;
+#define HIPCHK(x)                                      \
+    do {                                               \
+        e = (x);                                       \
+        if (e != hipSuccess) { free_ctx(c); return GPUOS_E_HIP; } \
+    } while (0)
+    HIPCHK(hipSetDevice(P.device));
+    hipDeviceProp_t prop;
+    HIPCHK(hipGetDeviceProperties(&prop, P.device));
+    c->cu_count = (uint32_t)prop.multiProcessorCount;
+    if (c->P.num_wgs == 0) c->P.num_wgs = c->cu_count;
+    int wclk = 0;
+    if (hipDeviceGetAttribute(&wclk, hipDeviceAttributeWallClockRate, P.device) != hipSuccess || wclk <= 0)
+        wclk = 100000;  // kHz
+    c->spin_ticks = (uint64_t)P.spin_limit_ms * (uint64_t)wclk;
+    const unsigned hflags = hipHostMallocCoherent | hipHostMallocMapped;
+    HIPCHK(hipHostMalloc((void**)&c->ring, N * sizeof(gpuos_desc), hflags));
+    HIPCHK(hipHostMalloc((void**)&c->stamp, N * 8, hflags));
+    HIPCHK(hipHostMalloc((void**)&c->status, N * 4, hflags));
+    HIPCHK(hipHostMalloc((void**)&c->hctl, sizeof(HostCtl), hflags));
+    memset(c->ring, 0, N * sizeof(gpuos_desc));
+    memset(c->status, 0, N * 4);
+    memset(c->hctl, 0, sizeof(HostCtl));
+    for (size_t i = 0; i < N; ++i) c->stamp[i] = N + i;
+    HIPCHK(hipMalloc((void**)&c->dctl, sizeof(DevCtl)));
+    HIPCHK(hipMalloc((void**)&c->mirror, N * sizeof(gpuos_desc)));
+    HIPCHK(hipMalloc((void**)&c->meta, N * sizeof(MirrorMeta)));
+    HIPCHK(hipMalloc((void**)&c->done, N * 8));
+    HIPCHK(hipMalloc((void**)&c->tiles_done, N * 4));
+    HIPCHK(hipMalloc((void**)&c->queue, (size_t)c->Q * 8));
+    HIPCHK(hipMalloc((void**)&c->table, 2 * GPUOS_MAX_OPS * sizeof(TableEntry)));
+    HIPCHK(hipMalloc((void**)&c->scratch, P.scratch_bytes));
+    HIPCHK(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
+    if (P.hip_stream) {
+        c->exec = (hipStream_t)P.hip_stream;
+        unsigned int fl = 0;
+        HIPCHK(hipStreamGetFlags(c->exec, &fl));
+        if (!(fl & hipStreamNonBlocking)) { free_ctx(c); return GPUOS_E_INVAL; }
+    } else {
+        HIPCHK(hipStreamCreateWithFlags(&c->exec, hipStreamNonBlocking));
+        c->own_exec = true;
+    }
+    HIPCHK(hipEventCreate(&c->ev_start));
+    HIPCHK(hipEventCreate(&c->ev_stop));
+    {
+        std::vector<uint64_t> d(N);
+        for (size_t i = 0; i < N; ++i) d[i] = i;
+        HIPCHK(hipMemcpyAsync(c->done, d.data(), N * 8, hipMemcpyHostToDevice, c->aux));
+        HIPCHK(hipMemsetAsync(c->tiles_done, 0, N * 4, c->aux));
+        HIPCHK(hipMemsetAsync(c->meta, 0, N * sizeof(MirrorMeta), c->aux));
+        HIPCHK(hipMemsetAsync(c->scratch, 0, P.scratch_bytes, c->aux));
+        HIPCHK(hipMemcpyAsync(c->table, c->shadow, sizeof(c->shadow), hipMemcpyHostToDevice, c->aux));
+        HIPCHK(hipStreamSynchronize(c->aux));
+    }
+#undef HIPCHK
+    rc = executor_launch(c);
+    if (rc) { free_ctx(c); return rc; }
+    *out = c;
+    return GPUOS_OK;
+}
+
+int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* consts, uint32_t len) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    if (op_id >= GPUOS_MAX_OPS || (kind >= GPUOS_KIND_COUNT && kind != GPUOS_KIND_EMPTY)) return GPUOS_E_NOOP;
+    if (len > 8 || (len && !consts)) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    // Grace period: the slot about to be rewritten was last used by version
+    // (version - 1); every descriptor submitted before the current version's
+    // flip must have completed (and so been resolved) first.
+    const uint64_t t0 = now_ns();
+    for (;;) {
+        refresh_wm(c);
+        if (c->wm >= c->flip_seq) break;
+        if (now_ns() - t0 > 60000000000ull) return GPUOS_E_TIMEOUT;
+        GPUOS_PAUSE();
+    }
+    const uint32_t nv = c->version + 1, slot = nv & 1u;
+    TableEntry te{kind, 0, 0.f, 0.f, 0, 0};
+    if (len >= 4) memcpy(&te.p0, consts, 4);
+    if (len >= 8) memcpy(&te.p1, (const char*)consts + 4, 4);
+    {
+        std::lock_guard<std::mutex> lg(c->lb_mu);
+        memcpy(c->shadow[slot], c->shadow[c->version & 1u], sizeof(c->shadow[0]));
+        c->shadow[slot][op_id] = te;
+    }
+    if (!c->loopback) {
+        if (hipMemcpyAsync(c->table + (size_t)slot * GPUOS_MAX_OPS, c->shadow[slot], sizeof(c->shadow[0]),
+                           hipMemcpyHostToDevice, c->aux) != hipSuccess)
+            return GPUOS_E_HIP;
+        if (hipStreamSynchronize(c->aux) != hipSuccess) return GPUOS_E_HIP;
+    }
+    // the flip: descriptors committed from now on carry the new version
+    c->version = nv;
+    c->flip_seq = c->next_seq;
+    if (getenv("GPUOS_AUDIT"))
+        fprintf(stderr, "gpuos: op %u -> kind %u (version %u, from seq %llu)\n", op_id, kind, nv,
+                (unsigned long long)c->next_seq);
+    return GPUOS_OK;
+}
+
+int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t flags, uint64_t* first_seq) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c || (count && !descs)) return GPUOS_E_INVAL;
+    if (count > c->N) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    if (first_seq) *first_seq = c->next_seq;
+    if (count == 0) return GPUOS_OK;
+    // resolve kinds and validate shapes before touching the ring
+    uint32_t kinds_small[64];
+    std::vector<uint32_t> kinds_big;
+    uint32_t* kinds = kinds_small;
+    if (count > 64) { kinds_big.resize(count); kinds = kinds_big.data(); }
+    const TableEntry* tab = c->shadow[c->version & 1u];
+    for (uint32_t i = 0; i < count; ++i) {
+        const gpuos_desc& d = descs[i];
+        uint32_t kind = d.op_id < GPUOS_MAX_OPS ? tab[d.op_id].kind : (uint32_t)GPUOS_KIND_EMPTY;
+        if (kind < GPUOS_KIND_COUNT) {
+            const Plan pl = make_plan(plan_in(kind, d));
+            if (pl.status != GPUOS_ST_OK) return GPUOS_E_INVAL;
+            if (pl.ntiles > c->Q / 2 || pl.scratch > c->P.scratch_bytes / 2) return GPUOS_E_INVAL;
+        } else {
+            kind = GPUOS_KIND_EMPTY;  // the device reports BAD_OP; nothing to order
+        }
+        kinds[i] = kind;
+    }
+    if (!c->running && !c->loopback) {
+        int rc = executor_launch(c);
+        if (rc) return rc;
+    }
+    // acquire slots: seq s needs seq s - N complete
+    const uint64_t need_wm = c->next_seq + count - c->N;
+    refresh_wm(c);
+    if (c->wm < need_wm) {
+        if (!(flags & GPUOS_SUBMIT_BLOCK)) { ++c->full_rej; return GPUOS_E_FULL; }
+        uint32_t spins = 0;
+        while (c->wm < need_wm) {
+            if (c->hctl && ld_acq(&c->hctl->dev_error)) return GPUOS_E_DEVICE;
+            if (++spins > 1000) std::this_thread::yield();
+            else GPUOS_PAUSE();
+            refresh_wm(c);
+        }
+    }
+    const uint64_t s0 = c->next_seq;
+    Access acc[2 * MAX_B + 4];
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint64_t s = s0 + i;
+        const uint32_t slot = (uint32_t)(s & c->mask);
+        gpuos_desc d = descs[i];
+        d.seq = s;
+        d.table_version = (uint16_t)c->version;
+        memset(d.dep_delta, 0, sizeof(d.dep_delta));
+        d.dep_range = 0;
+        c->deps.clear();
+        if (!(flags & GPUOS_SUBMIT_NOHAZARD) && kinds[i] < GPUOS_KIND_COUNT) {
+            const int n = accesses(kinds[i], d, acc);
+            c->hz.analyze(s, acc, n, c->wm, c->deps);
+        }
+        if ((flags & GPUOS_SUBMIT_SERIAL) && s - 1 >= c->wm) c->deps.push_back(s - 1);
+        if (!c->deps.empty()) {
+            std::sort(c->deps.begin(), c->deps.end());
+            c->deps.erase(std::unique(c->deps.begin(), c->deps.end()), c->deps.end());
+            if (c->deps.size() <= 6) {
+                for (size_t k = 0; k < c->deps.size(); ++k) d.dep_delta[k] = (uint16_t)(s - c->deps[k]);
+            } else {
+                d.dep_range = (uint16_t)(s - c->deps.front());
+            }
+        }
+        c->status[slot] = 0;
+        memcpy(&c->ring[slot], &d, sizeof(gpuos_desc));
+    }
+    // commit in order (store-release of each stamp)
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint64_t s = s0 + i;
+        st_rel(&c->stamp[s & c->mask], s + 1);
+    }
+    c->next_seq += count;
+    c->submitted += count;
+    return GPUOS_OK;
+}
+
+int gpuos_submit_bursts(void* ctx, const gpuos_desc* descs, const uint32_t* burst_sizes, uint32_t n_bursts,
+                        uint32_t flags, uint64_t* first_seq, uint64_t* n_done) {
+    if (!ctx || (n_bursts && (!descs || !burst_sizes))) return GPUOS_E_INVAL;
+    uint64_t off = 0;
+    int rc = GPUOS_OK;
+    for (uint32_t i = 0; i < n_bursts; ++i) {
+        uint64_t f = 0;
+        rc = gpuos_submit(ctx, descs + off, burst_sizes[i], flags, &f);
+        if (rc != GPUOS_OK) break;
+        if (i == 0 && first_seq) *first_seq = f;
+        off += burst_sizes[i];
+    }
+    if (n_done) *n_done = off;
+    return rc;
+}
+
+int gpuos_query(void* ctx, uint64_t seq) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    refresh_wm(c);
+    return seq < c->wm ? 1 : 0;
+}
+
+int gpuos_sync(void* ctx, uint64_t upto, int64_t timeout_ns, uint64_t* err_seq, uint32_t* err_status) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    const uint64_t t0 = now_ns();
+    uint32_t spins = 0;
+    for (;;) {
+        {
+            std::lock_guard<std::mutex> g(c->mu);
+            const uint64_t target = (upto == GPUOS_SEQ_ALL || upto >= c->next_seq) ? c->next_seq : upto + 1;
+            refresh_wm(c);
+            if (c->wm >= target) {
+                for (size_t i = 0; i < c->errors.size(); ++i) {
+                    if (c->errors[i].seq < target) {
+                        if (err_seq) *err_seq = c->errors[i].seq;
+                        if (err_status) *err_status = c->errors[i].st;
+                        c->errors.erase(c->errors.begin() + (long)i);
+                        return GPUOS_E_DEVICE;
+                    }
+                }
+                return GPUOS_OK;
+            }
+            if (!c->loopback && c->running && hipEventQuery(c->ev_stop) == hipSuccess) {
+                // the executor exited with work outstanding
+                return GPUOS_E_DEVICE;
+            }
+        }
+        if (timeout_ns >= 0 && now_ns() - t0 > (uint64_t)timeout_ns) return GPUOS_E_TIMEOUT;
+        if (++spins > 20000) std::this_thread::yield();
+        else GPUOS_PAUSE();
+    }
+}
+
+int gpuos_pause(void* ctx, int64_t timeout_ns) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    int rc = gpuos_sync(ctx, GPUOS_SEQ_ALL, timeout_ns, nullptr, nullptr);
+    if (rc != GPUOS_OK && rc != GPUOS_E_DEVICE) return rc;
+    std::lock_guard<std::mutex> g(c->mu);
+    int rs = executor_stop(c, timeout_ns < 0 ? 10000000000ll : timeout_ns);
+    return rs ? rs : rc;
+}
+
+int gpuos_resume(void* ctx) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    return executor_launch(c);
+}
+
+int gpuos_shutdown(void* ctx) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    int rc = GPUOS_OK;
+    {
+        std::lock_guard<std::mutex> g(c->mu);
+        rc = executor_stop(c, 10000000000ll);
+    }
+    if (rc == GPUOS_E_TIMEOUT && c->running) {
+        // the kernel is still resident: freeing its memory would fault it
+        return rc;
+    }
+    free_ctx(c);
+    return rc;
+}
+
+int gpuos_stats_get(void* ctx, gpuos_stats* out) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c || !out) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    refresh_wm(c);
+    memset(out, 0, sizeof(*out));
+    out->submitted = c->submitted;
+    out->completed = c->completed;
+    out->full_rejections = c->full_rej;
+    out->launches = c->launches;
+    out->last_launch_ms = c->last_ms;
+    out->total_launch_ms = c->total_ms;
+    out->num_wgs = c->P.num_wgs;
+    out->waves_per_wg = c->P.waves_per_wg;
+    out->ring_entries = c->N;
+    out->cu_count = c->cu_count;
+    out->next_seq = c->next_seq;
+    if (!c->loopback) {
+        out->units = c->acc_units;
+        out->dep_waits = c->acc_depw;
+        out->fetch_batches = c->acc_batches;
+        out->fetched = c->acc_fetched;
+        if (c->running) {  // add the live launch's counters (workers add theirs when they exit)
+            DevCtl d;
+            if (hipMemcpyAsync(&d, c->dctl, sizeof(DevCtl), hipMemcpyDeviceToHost, c->aux) != hipSuccess)
+                return GPUOS_E_HIP;
+            if (hipStreamSynchronize(c->aux) != hipSuccess) return GPUOS_E_HIP;
+            out->units += d.stat_units;
+            out->dep_waits += d.stat_dep_waits;
+            out->fetch_batches += d.stat_batches;
+            out->fetched += d.stat_fetched;
+        }
+    } else {
+        std::lock_guard<std::mutex> lg(c->lb_mu);
+        out->units = c->lb_order.size();
+        out->fetched = c->lb_order.size();
+    }
+    return GPUOS_OK;
+}
+
+int gpuos_loopback_order(void* ctx, uint64_t* out, uint64_t max, uint64_t* n_out) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c || !c->loopback) return GPUOS_E_STATE;
+    std::lock_guard<std::mutex> g(c->lb_mu);
+    const uint64_t n = std::min<uint64_t>(max, c->lb_order.size());
+    if (out) memcpy(out, c->lb_order.data(), n * 8);
+    if (n_out) *n_out = c->lb_order.size();
+    return GPUOS_OK;
+}
+
+// ------------------------------------------------------------ baselines
+uint64_t gpuos_eager_scratch_bytes(const gpuos_desc* descs, uint32_t count) {
+    uint64_t m = COUNTER_AREA;
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint32_t kind = descs[i].op_id;
+        if (kind >= GPUOS_KIND_COUNT) continue;
+        const Plan p = make_plan(plan_in(kind, descs[i]));
+        m = std::max<uint64_t>(m, p.scratch);
+    }
+    return m;
+}
+
+int gpuos_eager_submit(const gpuos_desc* descs, uint32_t count, void* hip_stream, void* scratch,
+                       uint64_t scratch_bytes) {
+    if (count && !descs) return GPUOS_E_INVAL;
+    hipStream_t s = (hipStream_t)hip_stream;
+    for (uint32_t i = 0; i < count; ++i) {
+        const gpuos_desc& d = descs[i];
+        if (d.op_id >= GPUOS_KIND_COUNT) return GPUOS_E_INVAL;
+        const Plan p = make_plan(plan_in(d.op_id, d));
+        if (p.status != GPUOS_ST_OK) return GPUOS_E_INVAL;
+        if (p.scratch > 0 && (!scratch || p.scratch > scratch_bytes)) return GPUOS_E_INVAL;
+        if (d.op_id == GPUOS_OP_NOP) {
+            if (launch_null(s) != hipSuccess) return GPUOS_E_HIP;
+            continue;
+        }
+        if (launch_eager(d, d.op_id, p.ntiles, (uint8_t*)scratch, s) != hipSuccess) return GPUOS_E_HIP;
+    }
+    return GPUOS_OK;
+}
+
+int gpuos_graph_build(const gpuos_desc* descs, uint32_t count, void* hip_stream, void* scratch,
+                      uint64_t scratch_bytes, void** graph_exec) {
+    if (!graph_exec) return GPUOS_E_INVAL;
+    *graph_exec = nullptr;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) return GPUOS_E_HIP;
+    int rc = gpuos_eager_submit(descs, count, hip_stream, scratch, scratch_bytes);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &g);
+    if (rc) { if (g) (void)hipGraphDestroy(g); return rc; }
+    if (e != hipSuccess) return GPUOS_E_HIP;
+    hipGraphExec_t ge = nullptr;
+    e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) return GPUOS_E_HIP;
+    *graph_exec = ge;
+    return GPUOS_OK;
+}
+
+int gpuos_graph_launch(void* graph_exec, void* hip_stream) {
+    if (!graph_exec) return GPUOS_E_INVAL;
+    return hipGraphLaunch((hipGraphExec_t)graph_exec, (hipStream_t)hip_stream) == hipSuccess ? GPUOS_OK : GPUOS_E_HIP;
+}
+
+int gpuos_graph_destroy(void* graph_exec) {
+    if (!graph_exec) return GPUOS_E_INVAL;
+    return hipGraphExecDestroy((hipGraphExec_t)graph_exec) == hipSuccess ? GPUOS_OK : GPUOS_E_HIP;
+}
+
+int gpuos_null_launch_bench(void* hip_stream, uint32_t n, double* ns_async, double* ns_sync) {
+    if (n == 0) return GPUOS_E_INVAL;
+    hipStream_t s = (hipStream_t)hip_stream;
+    if (launch_null(s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess) return GPUOS_E_HIP;
+    uint64_t t0 = now_ns();
+    for (uint32_t i = 0; i < n; ++i)
+        if (launch_null(s) != hipSuccess) return GPUOS_E_HIP;
+    uint64_t t1 = now_ns();
+    if (hipStreamSynchronize(s) != hipSuccess) return GPUOS_E_HIP;
+    if (ns_async) *ns_async = (double)(t1 - t0) / n;
+    const uint32_t m = n < 2000 ? n : 2000;
+    t0 = now_ns();
+    for (uint32_t i = 0; i < m; ++i) {
+        if (launch_null(s) != hipSuccess) return GPUOS_E_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return GPUOS_E_HIP;
+    }
+    t1 = now_ns();
+    if (ns_sync) *ns_sync = (double)(t1 - t0) / m;
+    return GPUOS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,221 @@
+// Internal layouts shared by the host runtime and the device executor.
+// Not part of the public ABI (include/gpuos.h is).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gpuos.h"
+
+namespace gpuos {
+
+// ---------------------------------------------------------------------------
+// Device-side operator table: two slots of GPUOS_MAX_OPS entries.  A
+// descriptor carries the table version it was submitted under and is
+// resolved against slot (version & 1) (the pages' dual-slot table with a
+// version counter flip; digest page, section 3 Q2 "Dynamic Operator Table").
+// ---------------------------------------------------------------------------
+struct alignas(32) TableEntry {
+    uint32_t kind;     // gpuos_kind, or GPUOS_KIND_EMPTY
+    uint32_t flags;    // reserved
+    float p0;          // kind's default parameter (eps / theta / scale), 0 = built-in
+    float p1;          // reserved
+    uint64_t fn;       // reserved for injected code objects (not used by built-ins)
+    uint64_t reserved;
+};
+static_assert(sizeof(TableEntry) == 32, "TableEntry is 32 bytes");
+
+constexpr uint32_t KIND_BAD = 0xFEu;  // internal: descriptor rejected on the device
+
+// Per-slot metadata the fetcher writes next to the mirrored descriptor.
+struct alignas(64) MirrorMeta {
+    uint32_t kind;          // resolved body
+    uint32_t status;        // GPUOS_ST_* decided at fetch time
+    uint32_t ntiles;        // work units
+    float p0;               // default parameter from the table entry
+    uint64_t ubegin;        // first unit number (this launch's numbering)
+    uint64_t scratch_v;     // virtual scratch offset (physical = v % scratch_bytes), or ~0
+    uint64_t scratch_mark;  // scratch watermark before this descriptor's allocation
+    uint64_t pad[3];
+};
+static_assert(sizeof(MirrorMeta) == 64, "MirrorMeta is 64 bytes");
+
+// Control words in fine-grained host memory (host writes, device polls).
+struct HostCtl {
+    alignas(64) uint64_t stop;       // host -> device: finish and exit when idle
+    alignas(64) uint64_t abort;      // host -> device: exit at once
+    alignas(64) uint64_t dev_error;  // device -> host: sticky error code
+    alignas(64) uint64_t exited;     // device -> host: number of waves that left
+};
+
+// Control words in device memory (one 128-byte line each).
+struct DevCtl {
+    alignas(128) uint64_t q_head;    // next unit ticket (workers fetch_add)
+    alignas(128) uint64_t q_tail;    // units published by the fetcher
+    alignas(128) uint64_t stop;      // fetcher -> workers
+    alignas(128) uint64_t error;     // sticky device error
+    alignas(128) uint64_t stat_units;
+    uint64_t stat_dep_waits;
+    uint64_t stat_batches;
+    uint64_t stat_fetched;
+};
+
+// Kernel arguments of the executor.
+struct ExecArgs {
+    const gpuos_desc* ring;   // host-mapped
+    uint64_t* stamp;          // host-mapped
+    uint32_t* status;         // host-mapped
+    HostCtl* hctl;            // host-mapped
+    DevCtl* dctl;
+    gpuos_desc* mirror;
+    MirrorMeta* meta;
+    uint64_t* done;
+    uint32_t* tiles_done;
+    uint64_t* queue;
+    const TableEntry* table;  // [2][GPUOS_MAX_OPS]
+    uint8_t* scratch;
+    uint64_t scratch_bytes;
+    uint64_t start_seq;
+    uint64_t spin_limit_ticks;  // in wall-clock ticks
+    uint32_t mask;              // ring_entries - 1
+    uint32_t qmask;             // unit-queue entries - 1
+    uint32_t backoff_max;
+    uint32_t pad;
+};
+
+// ---------------------------------------------------------------------------
+// Work plan of a descriptor: how many work units (tiles) it splits into and
+// how much scratch it needs.  Shared by the fetcher (device), the eager
+// launcher and host-side validation so that all three agree.
+// ---------------------------------------------------------------------------
+constexpr uint32_t EW_TILE_BYTES = 8192;   // per operand per element-wise tile
+constexpr uint32_t COPY_TILE_BYTES = 16384;
+constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
+constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit
+constexpr uint32_t GEMV_KC = 64;           // rows of W per GEMV unit
+constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
+constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
+constexpr uint32_t MAX_TILES = 1u << 22;   // hard cap of units per descriptor
+
+__host__ __device__ inline uint32_t dt_in(uint32_t flags) { return flags & 15u; }
+__host__ __device__ inline uint32_t dt_out(uint32_t flags) { return (flags >> 4) & 15u; }
+__host__ __device__ inline uint32_t esz(uint32_t dt) { return dt == GPUOS_F32 ? 4u : 2u; }
+__host__ __device__ inline bool dt_ok(uint32_t dt) { return dt == GPUOS_F32 || dt == GPUOS_BF16; }
+__host__ __device__ inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+// The fields of a descriptor the plan depends on.
+struct PlanIn {
+    uint32_t kind, flags;
+    uint64_t size;
+    uint32_t dim[4];
+    uint64_t lensw[2];  // lens[0..7] as packed 16-bit fields (descriptor bytes 104..120)
+    uint64_t a, b, out, aux0, aux1;
+};
+
+// lens[i] from the two packed words (kept packed: a dynamically indexed
+// array would live in private memory on the GPU)
+__host__ __device__ inline uint32_t lens_at(const uint64_t* w, uint32_t i) {
+    const uint64_t word = i < 4u ? w[0] : w[1];
+    return (uint32_t)((word >> (16u * (i & 3u))) & 0xFFFFu);
+}
+
+struct Plan {
+    uint32_t status;      // GPUOS_ST_OK or GPUOS_ST_BAD_SHAPE
+    uint32_t ntiles;
+    uint64_t scratch;     // bytes (0 = none); counters occupy the first COUNTER_AREA
+};
+
+__host__ __device__ inline uint32_t gemv_cols_per_block(uint32_t dt) { return 64u * (16u / esz(dt)); }
+
+__host__ __device__ inline Plan make_plan(const PlanIn& d) {
+    Plan p{GPUOS_ST_OK, 1u, 0u};
+    const uint32_t di = dt_in(d.flags), dout = dt_out(d.flags);
+    auto bad = [&]() { p.status = GPUOS_ST_BAD_SHAPE; p.ntiles = 1; p.scratch = 0; return p; };
+    if (d.kind != GPUOS_OP_NOP && d.kind != GPUOS_OP_COPY && (!dt_ok(di) || !dt_ok(dout))) return bad();
+    switch (d.kind) {
+        case GPUOS_OP_NOP:
+            return p;
+        case GPUOS_OP_ADD:
+        case GPUOS_OP_MUL:
+        case GPUOS_OP_RELU:
+        case GPUOS_OP_GELU: {
+            if (di != dout) return bad();
+            if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
+            if ((d.kind == GPUOS_OP_ADD || d.kind == GPUOS_OP_MUL) && d.size > 0 && d.b == 0) return bad();
+            uint64_t t = cdiv(d.size, EW_TILE_BYTES / esz(di));
+            if (t > MAX_TILES) return bad();
+            p.ntiles = t ? (uint32_t)t : 1u;
+            return p;
+        }
+        case GPUOS_OP_SUM:
+        case GPUOS_OP_MAX:
+        case GPUOS_OP_MIN:
+        case GPUOS_OP_SOFTMAX:
+        case GPUOS_OP_LAYERNORM: {
+            if (di != dout || d.dim[0] == 0) return bad();
+            if (d.size > MAX_TILES) return bad();
+            if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
+            if (d.kind == GPUOS_OP_LAYERNORM && d.size > 0 && (d.aux0 == 0 || d.aux1 == 0)) return bad();
+            p.ntiles = d.size ? (uint32_t)d.size : 1u;
+            return p;
+        }
+        case GPUOS_OP_ROPE:
+        case GPUOS_OP_KV_APPEND: {
+            const uint64_t B = d.size;
+            const uint32_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            if (B == 0 || B > MAX_B || H == 0 || D == 0 || di != dout) return bad();
+            if (d.kind == GPUOS_OP_ROPE) {
+                if ((D & 1u) || D > 256u || d.a == 0 || d.b == 0) return bad();
+            } else {
+                if (C == 0 || d.a == 0 || d.b == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
+            }
+            for (uint32_t i = 0; i < B; ++i) {
+                if (lens_at(d.lensw, i) == 0) return bad();
+                if (d.kind == GPUOS_OP_KV_APPEND && lens_at(d.lensw, i) > C) return bad();
+            }
+            p.ntiles = (uint32_t)B;
+            return p;
+        }
+        case GPUOS_OP_SDPA: {
+            const uint64_t B = d.size;
+            const uint32_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            if (B == 0 || B > MAX_B || H == 0 || C == 0 || (D != 64u && D != 128u)) return bad();
+            if (di != GPUOS_BF16) return bad();
+            if (d.a == 0 || d.out == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
+            uint64_t units = 0;
+            bool split = false;
+            for (uint32_t i = 0; i < B; ++i) {
+                const uint32_t L = lens_at(d.lensw, i);
+                if (L == 0 || L > C) return bad();
+                uint64_t ns = cdiv(L, SDPA_KT);
+                if (ns > 1) split = true;
+                units += ns * H;
+            }
+            if (units > MAX_TILES || (uint64_t)B * H * 4 > COUNTER_AREA) return bad();
+            p.ntiles = (uint32_t)units;
+            if (split) p.scratch = COUNTER_AREA + units * (uint64_t)(D + 4) * 4u;
+            return p;
+        }
+        case GPUOS_OP_GEMV: {
+            const uint32_t K = d.dim[0], N = d.dim[1];
+            if (K == 0 || N == 0 || d.a == 0 || d.b == 0 || d.out == 0) return bad();
+            const uint64_t ncb = cdiv(N, gemv_cols_per_block(di));
+            const uint64_t nks = cdiv(K, GEMV_KC);
+            if (ncb * nks > MAX_TILES || ncb * 4 > COUNTER_AREA) return bad();
+            p.ntiles = (uint32_t)(ncb * nks);
+            if (nks > 1) p.scratch = COUNTER_AREA + nks * (uint64_t)N * 4u;
+            return p;
+        }
+        case GPUOS_OP_COPY: {
+            if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
+            uint64_t t = cdiv(d.size, COPY_TILE_BYTES);
+            if (t > MAX_TILES) return bad();
+            p.ntiles = t ? (uint32_t)t : 1u;
+            return p;
+        }
+        default:
+            p.status = GPUOS_ST_BAD_OP;
+            return p;
+    }
+}
+
+}  // namespace gpuos

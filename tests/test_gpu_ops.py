@@ -1,0 +1,177 @@
+"""GPU parity, one micro-op at a time, through the C ABI: every op body at
+small shapes (several tiles, ragged tails, misaligned operands, special
+values) against the oracle.  Bytes no record writes must stay identical."""
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_harness import check_record, run_gpu, run_oracle, say, untouched_equal
+from oracle_util import bf16, rec
+
+pytestmark = pytest.mark.gpu
+RNG = np.random.default_rng(2024)
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    from persistent_micro_dispatch_amd import gpuos as G
+    c = G.gpuos_init()
+    yield c
+    assert G.gpuos_shutdown(c) == 0
+
+
+def _special_f32(n):
+    x = (RNG.standard_normal(n) * 3).astype(np.float32)
+    sp = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -1e-40, 3e38, -3e38, 1.0, -1.0], np.float32)
+    k = min(len(sp), n)
+    x[:k] = sp[:k]
+    return x
+
+
+def _vals(n, dt):
+    x = _special_f32(n)
+    return x if dt == W.F32 else bf16(x)
+
+
+def _run_and_check(ctx, arrays, recs):
+    gpu = run_gpu(arrays, recs, ctx=ctx)
+    orc = run_oracle(arrays, recs)
+    inputs = [np.ascontiguousarray(a).view(np.uint8).reshape(-1) for a in arrays]
+    results = [check_record(r, inputs, gpu, orc) for r in recs]
+    bad = [x for x in results if not x["ok"]]
+    assert not bad, bad[:5]
+    assert untouched_equal(recs, gpu, orc)
+    return results
+
+
+@pytest.mark.parametrize("dt", [W.F32, W.BF16])
+@pytest.mark.parametrize("op", [W.OP_ADD, W.OP_MUL, W.OP_RELU, W.OP_GELU])
+def test_elementwise(ctx, op, dt):
+    say(f"elementwise op={W.OP_NAMES[op]} dt={dt}")
+    sizes = [1, 7, 255, 256, 2047, 2048, 2049, 4095, 4097, 8192, 12345, 65536]
+    recs, arrays = [], []
+    for i, n in enumerate(sizes):
+        cap = n + 16
+        a, b, o = _vals(cap, dt), _vals(cap, dt), np.zeros_like(_vals(cap, dt))
+        base = len(arrays)
+        arrays += [a, b, o]
+        es = W.DTYPE_BYTES[dt]
+        sh = es if i % 3 == 2 else 0      # every third case misaligned by one element
+        recs.append(rec(op, dtype=dt, size=n, a=(base, sh), b=(base + 1, sh), out=(base + 2, sh)))
+    # in place: out = a
+    a = _vals(5000, dt)
+    arrays.append(a)
+    recs.append(rec(op, dtype=dt, size=5000, a=len(arrays) - 1, b=len(arrays) - 1, out=len(arrays) - 1))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))
+
+
+@pytest.mark.parametrize("op", [W.OP_SUM, W.OP_MAX, W.OP_MIN, W.OP_SOFTMAX, W.OP_LAYERNORM])
+@pytest.mark.parametrize("dt", [W.F32, W.BF16])
+def test_rows(ctx, op, dt):
+    say(f"rows op={W.OP_NAMES[op]} dt={dt}")
+    recs, arrays = [], []
+    for rows, h in [(1, 768), (3, 1024), (64, 2048), (5, 4096), (2, 100), (3, 5000), (1, 1)]:
+        x = (RNG.standard_normal(rows * h) * 2).astype(np.float32)
+        if op in (W.OP_MAX, W.OP_MIN) and rows * h > 10:
+            x[3] = -0.0
+            x[4] = 0.0
+        xs = x if dt == W.F32 else bf16(x)
+        g = (1 + 0.1 * RNG.standard_normal(h)).astype(np.float32)
+        b = (0.1 * RNG.standard_normal(h)).astype(np.float32)
+        gs, bs = (g, b) if dt == W.F32 else (bf16(g), bf16(b))
+        red = op in (W.OP_SUM, W.OP_MAX, W.OP_MIN)
+        o = np.zeros(rows if red else rows * h, xs.dtype)
+        base = len(arrays)
+        arrays += [xs, gs, bs, o]
+        recs.append(rec(op, dtype=dt, size=rows, dim=(h,), fparam=(1e-5,), a=base, aux0=base + 1,
+                        aux1=base + 2, out=base + 3))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))
+
+
+def test_rows_special_values(ctx):
+    x = np.array([[1.0, np.nan, -2.0, 3.0] * 256, [-0.0] * 1024, [0.0, -0.0] * 512], np.float32).reshape(-1)
+    arrays = [x, np.zeros(3, np.float32), np.zeros(3, np.float32)]
+    recs = np.concatenate([rec(W.OP_MAX, size=3, dim=(1024,), a=0, out=1),
+                           rec(W.OP_MIN, size=3, dim=(1024,), a=0, out=2)])
+    _run_and_check(ctx, arrays, recs)
+
+
+@pytest.mark.parametrize("dt,half", [(W.BF16, False), (W.BF16, True), (W.F32, False)])
+def test_rope(ctx, dt, half):
+    say(f"rope dt={dt} half={half}")
+    recs, arrays = [], []
+    for B, H, D, lens in [(1, 32, 128, [1]), (3, 8, 128, [2, 100, 4096]), (8, 32, 128, list(RNG.integers(1, 4097, 8))),
+                          (2, 4, 64, [7, 3000]), (1, 2, 256, [1234])]:
+        q = _vals(B * H * D, dt)
+        k = _vals(B * H * D, dt)
+        if dt == W.F32:
+            q = (RNG.standard_normal(B * H * D)).astype(np.float32)
+            k = (RNG.standard_normal(B * H * D)).astype(np.float32)
+        else:
+            q, k = bf16(RNG.standard_normal(B * H * D)), bf16(RNG.standard_normal(B * H * D))
+        base = len(arrays)
+        arrays += [q, k]
+        recs.append(rec(W.OP_ROPE, dtype=dt, size=B, dim=(H, D), fparam=(10000.0,), lens=lens,
+                        flags=W.FLAG_ROPE_HALF if half else 0, a=base, b=base + 1))
+    _run_and_check(ctx, arrays, np.concatenate(recs))
+
+
+def test_kv_append(ctx):
+    recs, arrays = [], []
+    for B, H, D, C, lens in [(1, 32, 128, 4096, [4096]), (8, 32, 128, 512, list(RNG.integers(1, 513, 8))),
+                             (3, 4, 64, 100, [1, 50, 100])]:
+        k, v = bf16(RNG.standard_normal(B * H * D)), bf16(RNG.standard_normal(B * H * D))
+        K, V = bf16(RNG.standard_normal(B * H * C * D)), bf16(RNG.standard_normal(B * H * C * D))
+        base = len(arrays)
+        arrays += [k, v, K, V]
+        recs.append(rec(W.OP_KV_APPEND, dtype=W.BF16, size=B, dim=(H, D, C), lens=lens, a=base, b=base + 1,
+                        aux0=base + 2, aux1=base + 3))
+    _run_and_check(ctx, arrays, np.concatenate(recs))
+
+
+@pytest.mark.parametrize("out_dt", [W.F32, W.BF16])
+def test_sdpa(ctx, out_dt):
+    say(f"sdpa out={out_dt}")
+    recs, arrays = [], []
+    for B, H, D, C, lens in [(1, 4, 128, 4096, [1]), (2, 4, 128, 4096, [255, 257]), (1, 2, 128, 4096, [4096]),
+                             (8, 2, 128, 2048, list(RNG.integers(1, 2049, 8))), (2, 3, 64, 600, [256, 513]),
+                             (3, 1, 128, 300, [300, 1, 129])]:
+        q = bf16(RNG.standard_normal(B * H * D))
+        K, V = bf16(RNG.standard_normal(B * H * C * D)), bf16(RNG.standard_normal(B * H * C * D))
+        o = np.zeros(B * H * D, np.float32 if out_dt == W.F32 else np.uint16)
+        base = len(arrays)
+        arrays += [q, K, V, o]
+        recs.append(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=out_dt, size=B, dim=(H, D, C), lens=lens,
+                        a=base, aux0=base + 1, aux1=base + 2, out=base + 3))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))
+
+
+@pytest.mark.parametrize("dt,out_dt", [(W.BF16, W.BF16), (W.F32, W.F32), (W.BF16, W.F32)])
+def test_gemv(ctx, dt, out_dt):
+    say(f"gemv dt={dt} out={out_dt}")
+    recs, arrays = [], []
+    for K, N in [(1024, 3072), (3072, 1024), (100, 77), (64, 512), (65, 513), (1, 8)]:
+        x = RNG.standard_normal(K).astype(np.float32)
+        Wm = (RNG.standard_normal(K * N) * 0.02).astype(np.float32)
+        if dt == W.BF16:
+            x, Wm = bf16(x), bf16(Wm)
+        o = np.zeros(N, np.float32 if out_dt == W.F32 else np.uint16)
+        base = len(arrays)
+        arrays += [x, Wm, o]
+        recs.append(rec(W.OP_GEMV, dtype=dt, out_dtype=out_dt, dim=(K, N), a=base, b=base + 1, out=base + 2))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))
+
+
+def test_copy_and_nop(ctx):
+    recs, arrays = [], []
+    for n, sh in [(1, 0), (15, 1), (16384, 0), (100000, 3), (0, 0)]:
+        a = RNG.integers(0, 255, n + 8).astype(np.uint8)
+        base = len(arrays)
+        arrays += [a, np.zeros(n + 8, np.uint8)]
+        recs.append(rec(W.OP_COPY, size=n, a=(base, sh), out=(base + 1, sh)))
+    recs.append(rec(W.OP_NOP))
+    _run_and_check(ctx, arrays, np.concatenate(recs))

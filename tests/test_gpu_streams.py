@@ -1,0 +1,90 @@
+"""GPU parity on whole descriptor streams through the C ABI.
+
+PR1 and the element-wise stream restricted to {add, mul, relu} run free
+(no intervention) and the final pool must be bit-identical to the oracle's:
+this also checks that concurrent claiming keeps sequential semantics under
+heavy aliasing."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_harness import run_gpu, say
+from parity import bits_equal
+from persistent_micro_dispatch_amd import gpuos as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _final_pools(stream, n, **init):
+    arrays = [b.host_bytes() for b in stream.buffers]
+    recs = stream.recs[:n]
+    gpu = run_gpu(arrays, recs, bursts=stream.bursts, **init)
+    p = oracle.Pool([a.copy() for a in arrays])
+    p.run(recs)
+    return gpu, p.arrays
+
+
+@pytest.mark.parametrize("n", [1, 100, 1000])
+def test_pr1_bit_exact(n):
+    s = W.make_pr1()
+    say(f"pr1 prefix {n}")
+    gpu, orc = _final_pools(s, n)
+    for i, b in enumerate(s.buffers):
+        eq = bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype)
+        assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
+
+
+@pytest.mark.parametrize("ring,waves", [(8, 4), (4096, 1)])
+def test_pr1_bit_exact_small_ring_and_one_wave(ring, waves):
+    s = W.make_pr1()
+    s.bursts = np.full(125, 8)
+    say(f"pr1 ring={ring} waves={waves}")
+    gpu, orc = _final_pools(s, 1000, ring_entries=ring, waves_per_wg=waves)
+    for i, b in enumerate(s.buffers):
+        assert bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype).all()
+
+
+def test_elementwise_exact_ops_bit_exact():
+    s = W.make_elementwise(n_desc=5000, ops=(W.OP_ADD, W.OP_MUL, W.OP_RELU))
+    say("elementwise exact 5000")
+    gpu, orc = _final_pools(s, len(s))
+    for i, b in enumerate(s.buffers):
+        eq = bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype)
+        assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
+
+
+# --------------------------------------------------------------------------
+# Verify mode (every output logged on the GPU, teacher-forced oracle replay)
+# --------------------------------------------------------------------------
+from gpu_harness import verify_stream  # noqa: E402
+
+
+def _report(name, res):
+    say(f"{name}: logged {res['n_logged']} outputs; worst ratio per op {res['worst']}")
+    assert not res["fails"], res["fails"][:3]
+    assert res["kv_ok"]
+
+
+def test_elementwise_stream_verify():
+    s = W.make_elementwise(n_desc=3000)
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs)
+    _report("elementwise", res)
+
+
+def test_rows_stream_verify():
+    s = W.make_rows(n_desc=600, n_pool=8, arena_bytes=32 << 20)
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs)
+    _report("rows", res)
+
+
+def test_decode_stream_verify():
+    s = W.make_decode(steps=4, layers=2, heads=8, capacity=512, l_min=100, n_triples=4, n_out=16)
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs)
+    _report("decode", res)
+
+
+def test_mixed_stream_verify():
+    s = W.make_mixed(tokens=2, layers=2, capacity=256, l0_range=(32, 200))
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs)
+    _report("mixed", res)

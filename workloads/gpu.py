@@ -1,0 +1,87 @@
+"""GPU-side harness: put a symbolic stream's pool in device memory and turn
+its records into gpuos descriptors (device pointers).  Marshalling only."""
+from __future__ import annotations
+
+from typing import List, Sequence
+
+import numpy as np
+
+import workloads as W
+from persistent_micro_dispatch_amd import gpuos as G
+
+
+class DevicePool:
+    """One torch uint8 tensor per buffer of a stream (or given arrays)."""
+
+    def __init__(self, host_arrays: Sequence[np.ndarray], device: str = "cuda:0"):
+        import torch
+        self.tensors = []
+        for a in host_arrays:
+            b = np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+            t = torch.empty(max(b.nbytes, 1), dtype=torch.uint8, device=device)
+            if b.nbytes:
+                t[: b.nbytes].copy_(torch.from_numpy(b))
+            self.tensors.append(t)
+        self.nbytes = [np.ascontiguousarray(a).nbytes for a in host_arrays]
+        # only torch's stream: a device-wide synchronize would wait for a
+        # resident executor kernel forever
+        torch.cuda.current_stream().synchronize()
+
+    @classmethod
+    def from_stream(cls, stream: W.Stream, device: str = "cuda:0") -> "DevicePool":
+        return cls([b.host_bytes() for b in stream.buffers], device)
+
+    @property
+    def ptrs(self) -> List[int]:
+        return [t.data_ptr() for t in self.tensors]
+
+    def download(self, i: int) -> np.ndarray:
+        return self.tensors[i][: self.nbytes[i]].cpu().numpy()
+
+
+def to_descs(recs: np.ndarray, ptrs: Sequence[int]) -> np.ndarray:
+    """Records (workloads.REC_DTYPE) -> descriptors (gpuos DESC_DTYPE)."""
+    n = len(recs)
+    d = G.new_descs(n)
+    P = np.asarray(list(ptrs) + [0], dtype=np.uint64)  # index -1 -> 0
+
+    def addr(role):
+        b = recs["buf"][:, role].astype(np.int64)
+        base = P[np.where(b < 0, len(P) - 1, b)]
+        return np.where(b < 0, np.uint64(0), base + recs["off"][:, role].astype(np.uint64))
+
+    d["op_id"] = recs["op"].astype(np.uint32)
+    d["flags"] = (recs["dtype"].astype(np.uint32) | (recs["out_dtype"].astype(np.uint32) << 4)
+                  | np.where(recs["flags"] & W.FLAG_ROPE_HALF, G.GPUOS_F_ROPE_HALF, 0).astype(np.uint32))
+    d["input_a"] = addr(W.A)
+    d["input_b"] = addr(W.B)
+    d["output"] = addr(W.OUT)
+    d["aux"][:, 0] = addr(W.AUX0)
+    d["aux"][:, 1] = addr(W.AUX1)
+    d["aux"][:, 2] = addr(W.AUX2)
+    d["size"] = recs["size"].astype(np.uint64)
+    d["dim"] = recs["dim"].astype(np.uint32)
+    op = recs["op"]
+    attn = (op == W.OP_ROPE) | (op == W.OP_KV_APPEND) | (op == W.OP_SDPA)
+    # generic float params in words 0..1
+    fp = recs["fparam"].astype(np.float32).view(np.uint32)
+    d["param"][:, 0:2] = np.where(attn[:, None], 0, fp)
+    # attention ops: lens in words 0..3, theta / scale in word 4
+    if attn.any():
+        L = np.zeros((n, 8), np.uint16)
+        L[:] = recs["lens"].astype(np.uint16)
+        words = L.view(np.uint32).reshape(n, 4)
+        d["param"][attn, 0:4] = words[attn]
+        f4 = np.where(op == W.OP_ROPE, recs["fparam"][:, 0], np.where(op == W.OP_SDPA, recs["fparam"][:, 1], 0))
+        d["param"][attn, 4] = f4.astype(np.float32).view(np.uint32)[attn]
+    return d
+
+
+def split_bursts(n: int, bursts: np.ndarray) -> List[slice]:
+    out, s = [], 0
+    for b in bursts:
+        out.append(slice(s, s + int(b)))
+        s += int(b)
+    if s < n:
+        out.append(slice(s, n))
+    return out
