@@ -138,6 +138,7 @@ static_assert(sizeof(gpuos_desc) == 128, "gpuos_desc must be 128 bytes");
 #define GPUOS_INIT_LOOPBACK (1u << 0) /* test only: no GPU; a host thread plays the
                                          consumer, completes descriptors in a random
                                          dependency-respecting order and computes nothing */
+#define GPUOS_INIT_TRACE (1u << 1)    /* record one gpuos_trace_rec per work unit */
 
 typedef struct gpuos_init_params {
     int32_t device;             /* HIP device ordinal */
@@ -236,6 +237,8 @@ typedef struct gpuos_stats {
     uint64_t dep_waits;          /* units that found a dependency not yet done */
     uint32_t num_wgs, waves_per_wg, ring_entries, cu_count;
     uint64_t next_seq;           /* sequence number the next submit will get */
+    uint64_t deps_explicit;      /* explicit dependencies written (host) */
+    uint64_t deps_range;         /* descriptors that fell back to a range dependency */
 } gpuos_stats;
 
 /* Snapshot of the counters.  Device counters are added up when a launch
@@ -246,6 +249,26 @@ int gpuos_stats_get(void* ctx, gpuos_stats* out);
 /* Test only (GPUOS_INIT_LOOPBACK contexts): copy up to max sequence
  * numbers in the order the loopback consumer completed them. */
 int gpuos_loopback_order(void* ctx, uint64_t* out, uint64_t max, uint64_t* n_out);
+
+/* ---------------------------------------------------------------- trace */
+/* One record per executed work unit (GPUOS_INIT_TRACE contexts).  Times are
+ * the device's constant-rate wall clock (hipDeviceAttributeWallClockRate,
+ * kHz); unit numbers restart at 0 with every executor launch. */
+typedef struct gpuos_trace_rec {
+    uint64_t seq;          /* descriptor */
+    uint32_t tile;         /* unit within the descriptor */
+    uint32_t hw;           /* XCC id << 16 | workgroup id */
+    uint64_t t_claim;      /* unit claimed and published */
+    uint64_t t_ready;      /* dependencies satisfied */
+    uint64_t t_body;       /* op body finished */
+    uint64_t t_done;       /* completion written (last unit: slot released) */
+    uint64_t unit;         /* unit number within the launch */
+    uint64_t pad;
+} gpuos_trace_rec;
+
+/* Copy the trace of the last finished launch (call after gpuos_pause):
+ * up to max records into out (host memory); *n_out = records available. */
+int gpuos_trace_read(void* ctx, gpuos_trace_rec* out, uint64_t max, uint64_t* n_out);
 
 /* ------------------------------------------------- baselines (measurement) */
 /* Eager baseline: run each descriptor as its own hipLaunchKernel (one or

@@ -69,6 +69,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             nap(bo);
         }
         if (stop) break;
+        const uint64_t t_claim = A.trace ? wall_clock64() : 0;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         const uint64_t ent = A.queue[u & A.qmask];
         const uint64_t seq = ent >> 24;
@@ -76,12 +77,13 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         const uint64_t slot = seq & A.mask;
         uint64_t w = 0;
         if (lane < 16) w = ((const uint64_t*)&A.mirror[slot])[lane];
-        else if (lane < 20) w = ((const uint64_t*)&A.meta[slot])[lane - 16];
+        else if (lane < 24) w = ((const uint64_t*)&A.meta[slot])[lane - 16];
         Unit U;
         const uint64_t w0 = rl64(w, 0), w6 = rl64(w, 6), w7 = rl64(w, 7);
         const uint64_t w11 = rl64(w, 11), w12 = rl64(w, 12);
         const uint64_t w13 = rl64(w, 13), w14 = rl64(w, 14), w15 = rl64(w, 15);
         const uint64_t m0 = rl64(w, 16), m1 = rl64(w, 17), m3 = rl64(w, 19);
+        const uint64_t x0 = rl64(w, 21), x1 = rl64(w, 22);
         U.seq = seq;
         U.flags = (uint32_t)(w0 >> 32);
         U.tile = tile;
@@ -99,11 +101,14 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         U.ntiles = (uint32_t)m1;
         U.p0 = __uint_as_float((uint32_t)(m1 >> 32));
         U.scratch = m3 == NO_SCRATCH ? nullptr : A.scratch + (m3 % A.scratch_bytes);
-        // dependencies: explicit seq deltas (lanes 0..5) and a contiguous range
+        // dependencies: explicit deltas in lanes 0..13 (6 in the descriptor,
+        // 8 copied beside it) and a contiguous range
         const uint32_t delta = lane < 4 ? (uint32_t)((w11 >> (16 * lane)) & 0xFFFFu)
-                             : lane < 6 ? (uint32_t)((w12 >> (16 * (lane - 4))) & 0xFFFFu) : 0u;
+                             : lane < 6 ? (uint32_t)((w12 >> (16 * (lane - 4))) & 0xFFFFu)
+                             : lane < 10 ? (uint32_t)((x0 >> (16 * (lane - 6))) & 0xFFFFu)
+                             : lane < 14 ? (uint32_t)((x1 >> (16 * (lane - 10))) & 0xFFFFu) : 0u;
         uint64_t rlo = seq - ((w12 >> 32) & 0xFFFFu);
-        if (w11 != 0 || (w12 & 0xFFFFFFFFFFFFull) != 0) {
+        if (w11 != 0 || (w12 & 0xFFFFFFFFFFFFull) != 0 || x0 != 0) {
             bool counted = false;
             uint64_t t0 = 0;
             uint32_t dbo = 1;
@@ -138,8 +143,10 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             if (stop) break;
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
+        const uint64_t t_ready = A.trace ? wall_clock64() : 0;
         if (status == GPUOS_ST_OK && U.kind != KIND_BAD) run_unit(U, lane);
         ++n_units;
+        const uint64_t t_body = A.trace ? wall_clock64() : 0;
         // completion: the last unit of the descriptor releases the slot
         bool last = true;
         if (U.ntiles > 1) {
@@ -157,6 +164,19 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
                     __hip_atomic_store(&A.status[slot], status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                 st_sys(&A.stamp[slot], seq + N);
             }
+        }
+        if (A.trace && lane == 0) {
+            uint32_t xcc = 0;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+            gpuos_trace_rec* tr = &A.trace[u & (A.trace_cap - 1)];
+            tr->seq = seq;
+            tr->tile = tile;
+            tr->hw = (xcc << 16) | (uint32_t)blockIdx.x;
+            tr->t_claim = t_claim;
+            tr->t_ready = t_ready;
+            tr->t_body = t_body;
+            tr->t_done = wall_clock64();
+            tr->unit = u;
         }
     }
     if (lane == 0) {
@@ -203,6 +223,12 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         for (uint32_t k = 0; k < 16; ++k) {
             const uint32_t wi = lane + 64u * k;
             if (wi < nw) v[k] = ld_sys(&ringw[((f + (wi >> 4)) & mask) * 16u + (wi & 15u)]);
+        }
+        // extra dependency deltas: 2 words per descriptor, lane i < count
+        uint64_t xd0 = 0, xd1 = 0;
+        if (lane < count) {
+            xd0 = ld_sys(&A.depx[2 * ((f + lane) & mask)]);
+            xd1 = ld_sys(&A.depx[2 * ((f + lane) & mask) + 1]);
         }
 #pragma unroll
         for (uint32_t k = 0; k < 16; ++k) {
@@ -303,19 +329,19 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
 #pragma unroll
         for (uint32_t k = 0; k < 16; ++k) {
             const uint32_t wi = lane + 64u * k;
-            if (wi < count * 16u) mirw[((f + (wi >> 4)) & mask) * 16u + (wi & 15u)] = v[k];
+            if (wi < count * 16u) wst64(&mirw[((f + (wi >> 4)) & mask) * 16u + (wi & 15u)], lds[wi]);
         }
         if (keep) {
             const uint64_t slot = (f + lane) & mask;
-            MirrorMeta* mm = &A.meta[slot];
-            mm->kind = kind;
-            mm->status = pl.status;
-            mm->ntiles = nt;
-            mm->p0 = p0;
-            mm->ubegin = ubegin;
-            mm->scratch_v = my_sv;
-            mm->scratch_mark = my_mark;
-            A.tiles_done[slot] = 0;
+            uint64_t* mm = (uint64_t*)&A.meta[slot];  // MirrorMeta as 64-bit words
+            wst64(mm + 0, (uint64_t)kind | ((uint64_t)pl.status << 32));
+            wst64(mm + 1, (uint64_t)nt | ((uint64_t)__float_as_uint(p0) << 32));
+            wst64(mm + 2, ubegin);
+            wst64(mm + 3, my_sv);
+            wst64(mm + 4, my_mark);
+            wst64(mm + 5, xd0);
+            wst64(mm + 6, xd1);
+            wst32(&A.tiles_done[slot], 0u);
             pref[lane] = inc - nt;
         }
         // zero the group counters of descriptors that use scratch
@@ -324,10 +350,10 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             const int j = __ffsll((long long)zm) - 1;
             zm &= zm - 1;
             const uint64_t svj = rl64(my_sv, j);
-            uint8_t* base = A.scratch + (svj % S);
+            const WBuf zb = wbuf(A.scratch + (svj % S));
 #pragma unroll
             for (uint32_t k = 0; k < COUNTER_AREA / 16u / 64u; ++k)
-                st16(base + (uint64_t)(lane + 64u * k) * 16u, u32x4{0, 0, 0, 0});
+                wst16(zb, (lane + 64u * k) * 16u, u32x4{0, 0, 0, 0});
         }
         if (lane == 0) pref[count] = T;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -339,7 +365,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
                 const uint32_t mid = (lo + hi) >> 1;
                 if (pref[mid] <= wi) lo = mid; else hi = mid;
             }
-            A.queue[(u_next + wi) & A.qmask] = ((f + lo) << 24) | (wi - pref[lo]);
+            wst64(&A.queue[(u_next + wi) & A.qmask], ((f + lo) << 24) | (wi - pref[lo]));
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         if (lane == 0) st_agent(&C->q_tail, u_next + T);
@@ -357,7 +383,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     }
 }
 
-extern "C" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) gpuos_executor(ExecArgs A) {
+extern "C" __global__ void __launch_bounds__(256) gpuos_executor(ExecArgs A) {
     __shared__ uint64_t lds[64 * 16 + 72];
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     if (blockIdx.x == 0 && wave == 0) fetcher_loop(A, lane, lds, lds + 64 * 16);

@@ -179,6 +179,7 @@ struct gpuos_ctx {
     uint32_t N = 0, mask = 0, Q = 0, cu_count = 0;
     // host-coherent ring memory
     gpuos_desc* ring = nullptr;
+    uint64_t* depx = nullptr;  // [N][2]: dependency deltas 6..13
     uint64_t* stamp = nullptr;
     uint32_t* status = nullptr;
     HostCtl* hctl = nullptr;
@@ -191,6 +192,8 @@ struct gpuos_ctx {
     uint64_t* queue = nullptr;
     TableEntry* table = nullptr;
     uint8_t* scratch = nullptr;
+    gpuos_trace_rec* trace = nullptr;
+    uint64_t trace_cap = 0;
     hipStream_t exec = nullptr, aux = nullptr;
     bool own_exec = false;
     hipEvent_t ev_start = nullptr, ev_stop = nullptr;
@@ -214,6 +217,7 @@ struct gpuos_ctx {
     // stats (device counters are accumulated here when a launch ends)
     uint64_t submitted = 0, completed = 0, full_rej = 0;
     uint64_t acc_units = 0, acc_depw = 0, acc_batches = 0, acc_fetched = 0;
+    uint64_t deps_explicit = 0, deps_range = 0;
     // loopback consumer
     std::thread lb_thread;
     std::atomic<bool> lb_stop{false};
@@ -246,6 +250,7 @@ int executor_launch(gpuos_ctx* c) {
     st_rel(&c->hctl->exited, (uint64_t)0);
     ExecArgs a{};
     a.ring = c->ring;
+    a.depx = c->depx;
     a.stamp = c->stamp;
     a.status = c->status;
     a.hctl = c->hctl;
@@ -258,11 +263,15 @@ int executor_launch(gpuos_ctx* c) {
     a.table = c->table;
     a.scratch = c->scratch;
     a.scratch_bytes = c->P.scratch_bytes;
+    a.trace = c->trace;
+    a.trace_cap = c->trace_cap;
     a.start_seq = c->next_seq;
     a.spin_limit_ticks = c->spin_ticks;
     a.mask = c->mask;
     a.qmask = c->Q - 1;
     a.backoff_max = c->P.backoff_max;
+    if (c->trace && hipMemsetAsync(c->trace, 0, c->trace_cap * sizeof(gpuos_trace_rec), c->exec) != hipSuccess)
+        return GPUOS_E_HIP;
     if (hipEventRecord(c->ev_start, c->exec) != hipSuccess) return GPUOS_E_HIP;
     if (launch_executor(a, c->P.num_wgs, 64u * c->P.waves_per_wg, c->exec) != hipSuccess) return GPUOS_E_HIP;
     if (hipEventRecord(c->ev_stop, c->exec) != hipSuccess) return GPUOS_E_HIP;
@@ -312,13 +321,17 @@ void loopback_main(gpuos_ctx* c) {
     std::mt19937_64 rng(12345);
     const uint64_t N = c->N;
     uint64_t f = c->N;  // next seq to fetch
-    struct Pend { uint64_t seq; gpuos_desc d; };
+    struct Pend { uint64_t seq; gpuos_desc d; uint16_t ex[8]; };
     std::vector<Pend> pend;
     auto is_done = [&](uint64_t s) { return c->lb_done[s & c->mask] >= s; };
     while (!c->lb_stop.load()) {
         bool progress = false;
         while (ld_acq(&c->stamp[f & c->mask]) == f + 1 && pend.size() < 256) {
-            pend.push_back({f, c->ring[f & c->mask]});
+            Pend pe;
+            pe.seq = f;
+            pe.d = c->ring[f & c->mask];
+            memcpy(pe.ex, &c->depx[2 * (f & c->mask)], 16);
+            pend.push_back(pe);
             ++f;
             progress = true;
         }
@@ -330,6 +343,9 @@ void loopback_main(gpuos_ctx* c) {
             bool ok = true;
             for (int k = 0; k < 6 && ok; ++k)
                 if (d.dep_delta[k]) ok = is_done(s - d.dep_delta[k]);
+            const uint16_t* ex = pend[i].ex;
+            for (int k = 0; k < 8 && ok; ++k)
+                if (ex[k]) ok = is_done(s - ex[k]);
             for (uint64_t x = s - d.dep_range; x < s && ok; ++x) ok = is_done(x);
             if (ok) ready.push_back(i);
         }
@@ -382,6 +398,7 @@ void free_ctx(gpuos_ctx* c) {
         c->lb_stop = true;
         if (c->lb_thread.joinable()) c->lb_thread.join();
         free(c->ring);
+        free(c->depx);
         free(c->stamp);
         free(c->status);
         free(c->hctl);
@@ -389,10 +406,11 @@ void free_ctx(gpuos_ctx* c) {
         return;
     }
     if (c->ring) (void)hipHostFree(c->ring);
+    if (c->depx) (void)hipHostFree(c->depx);
     if (c->stamp) (void)hipHostFree(c->stamp);
     if (c->status) (void)hipHostFree(c->status);
     if (c->hctl) (void)hipHostFree(c->hctl);
-    void* dev[] = {c->dctl, c->mirror, c->meta, c->done, c->tiles_done, c->queue, c->table, c->scratch};
+    void* dev[] = {c->dctl, c->mirror, c->meta, c->done, c->tiles_done, c->queue, c->table, c->scratch, c->trace};
     for (void* p : dev)
         if (p) (void)hipFree(p);
     if (c->ev_start) (void)hipEventDestroy(c->ev_start);
@@ -433,10 +451,11 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     const size_t N = c->N;
     if (c->loopback) {
         c->ring = (gpuos_desc*)aligned_zalloc(N * sizeof(gpuos_desc));
+        c->depx = (uint64_t*)aligned_zalloc(N * 16);
         c->stamp = (uint64_t*)aligned_zalloc(N * 8);
         c->status = (uint32_t*)aligned_zalloc(N * 4);
         c->hctl = (HostCtl*)aligned_zalloc(sizeof(HostCtl));
-        if (!c->ring || !c->stamp || !c->status || !c->hctl) { free_ctx(c); return GPUOS_E_INVAL; }
+        if (!c->ring || !c->depx || !c->stamp || !c->status || !c->hctl) { free_ctx(c); return GPUOS_E_INVAL; }
         for (size_t i = 0; i < N; ++i) c->stamp[i] = N + i;
         c->lb_done.assign(N, 0);
         for (size_t i = 0; i < N; ++i) c->lb_done[i] = i;
@@ -462,10 +481,12 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     c->spin_ticks = (uint64_t)P.spin_limit_ms * (uint64_t)wclk;
     const unsigned hflags = hipHostMallocCoherent | hipHostMallocMapped;
     HIPCHK(hipHostMalloc((void**)&c->ring, N * sizeof(gpuos_desc), hflags));
+    HIPCHK(hipHostMalloc((void**)&c->depx, N * 16, hflags));
     HIPCHK(hipHostMalloc((void**)&c->stamp, N * 8, hflags));
     HIPCHK(hipHostMalloc((void**)&c->status, N * 4, hflags));
     HIPCHK(hipHostMalloc((void**)&c->hctl, sizeof(HostCtl), hflags));
     memset(c->ring, 0, N * sizeof(gpuos_desc));
+    memset(c->depx, 0, N * 16);
     memset(c->status, 0, N * 4);
     memset(c->hctl, 0, sizeof(HostCtl));
     for (size_t i = 0; i < N; ++i) c->stamp[i] = N + i;
@@ -477,6 +498,10 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     HIPCHK(hipMalloc((void**)&c->queue, (size_t)c->Q * 8));
     HIPCHK(hipMalloc((void**)&c->table, 2 * GPUOS_MAX_OPS * sizeof(TableEntry)));
     HIPCHK(hipMalloc((void**)&c->scratch, P.scratch_bytes));
+    if (P.flags & GPUOS_INIT_TRACE) {
+        c->trace_cap = 1u << 20;
+        HIPCHK(hipMalloc((void**)&c->trace, c->trace_cap * sizeof(gpuos_trace_rec)));
+    }
     HIPCHK(hipStreamCreateWithFlags(&c->aux, hipStreamNonBlocking));
     if (P.hip_stream) {
         c->exec = (hipStream_t)P.hip_stream;
@@ -599,20 +624,35 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
         memset(d.dep_delta, 0, sizeof(d.dep_delta));
         d.dep_range = 0;
         c->deps.clear();
+        uint64_t range_from = UINT64_MAX;
         if (!(flags & GPUOS_SUBMIT_NOHAZARD) && kinds[i] < GPUOS_KIND_COUNT) {
             const int n = accesses(kinds[i], d, acc);
-            c->hz.analyze(s, acc, n, c->wm, c->deps);
+            c->hz.analyze(s, acc, n, c->wm, c->deps, &range_from);
         }
         if ((flags & GPUOS_SUBMIT_SERIAL) && s - 1 >= c->wm) c->deps.push_back(s - 1);
-        if (!c->deps.empty()) {
+        uint16_t ex[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (!c->deps.empty() || range_from != UINT64_MAX) {
             std::sort(c->deps.begin(), c->deps.end());
             c->deps.erase(std::unique(c->deps.begin(), c->deps.end()), c->deps.end());
-            if (c->deps.size() <= 6) {
-                for (size_t k = 0; k < c->deps.size(); ++k) d.dep_delta[k] = (uint16_t)(s - c->deps[k]);
-            } else {
-                d.dep_range = (uint16_t)(s - c->deps.front());
+            if (range_from != UINT64_MAX && range_from < c->wm) range_from = c->wm;
+            if (range_from != UINT64_MAX)  // the range covers every dep at or after it
+                c->deps.erase(std::lower_bound(c->deps.begin(), c->deps.end(), range_from), c->deps.end());
+            if (c->deps.size() > MAX_DEPS) {
+                range_from = std::min<uint64_t>(range_from, c->deps.front());
+                c->deps.clear();
+            }
+            for (size_t k = 0; k < c->deps.size(); ++k) {
+                const uint16_t dl = (uint16_t)(s - c->deps[k]);
+                if (k < 6) d.dep_delta[k] = dl;
+                else ex[k - 6] = dl;
+            }
+            c->deps_explicit += c->deps.size();
+            if (range_from != UINT64_MAX && range_from < s) {
+                d.dep_range = (uint16_t)(s - range_from);
+                ++c->deps_range;
             }
         }
+        memcpy(&c->depx[2 * slot], ex, 16);
         c->status[slot] = 0;
         memcpy(&c->ring[slot], &d, sizeof(gpuos_desc));
     }
@@ -732,6 +772,8 @@ int gpuos_stats_get(void* ctx, gpuos_stats* out) {
     out->ring_entries = c->N;
     out->cu_count = c->cu_count;
     out->next_seq = c->next_seq;
+    out->deps_explicit = c->deps_explicit;
+    out->deps_range = c->deps_range;
     if (!c->loopback) {
         out->units = c->acc_units;
         out->dep_waits = c->acc_depw;
@@ -762,6 +804,21 @@ int gpuos_loopback_order(void* ctx, uint64_t* out, uint64_t max, uint64_t* n_out
     const uint64_t n = std::min<uint64_t>(max, c->lb_order.size());
     if (out) memcpy(out, c->lb_order.data(), n * 8);
     if (n_out) *n_out = c->lb_order.size();
+    return GPUOS_OK;
+}
+
+int gpuos_trace_read(void* ctx, gpuos_trace_rec* out, uint64_t max, uint64_t* n_out) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    if (!c->trace || c->running) return GPUOS_E_STATE;
+    const uint64_t n = std::min<uint64_t>(max, c->trace_cap);
+    if (n_out) *n_out = c->trace_cap;
+    if (n && out) {
+        if (hipMemcpyAsync(out, c->trace, n * sizeof(gpuos_trace_rec), hipMemcpyDeviceToHost, c->aux) != hipSuccess)
+            return GPUOS_E_HIP;
+        if (hipStreamSynchronize(c->aux) != hipSuccess) return GPUOS_E_HIP;
+    }
     return GPUOS_OK;
 }
 

@@ -35,7 +35,8 @@ struct alignas(64) MirrorMeta {
     uint64_t ubegin;        // first unit number (this launch's numbering)
     uint64_t scratch_v;     // virtual scratch offset (physical = v % scratch_bytes), or ~0
     uint64_t scratch_mark;  // scratch watermark before this descriptor's allocation
-    uint64_t pad[3];
+    uint64_t dep_extra[2];  // dependency deltas 6..13 (16-bit each), copied from the host side array
+    uint64_t pad;
 };
 static_assert(sizeof(MirrorMeta) == 64, "MirrorMeta is 64 bytes");
 
@@ -62,6 +63,7 @@ struct DevCtl {
 // Kernel arguments of the executor.
 struct ExecArgs {
     const gpuos_desc* ring;   // host-mapped
+    const uint64_t* depx;     // host-mapped: 2 words of extra dependency deltas per slot
     uint64_t* stamp;          // host-mapped
     uint32_t* status;         // host-mapped
     HostCtl* hctl;            // host-mapped
@@ -74,6 +76,8 @@ struct ExecArgs {
     const TableEntry* table;  // [2][GPUOS_MAX_OPS]
     uint8_t* scratch;
     uint64_t scratch_bytes;
+    gpuos_trace_rec* trace;     // null unless tracing
+    uint64_t trace_cap;         // records (power of two)
     uint64_t start_seq;
     uint64_t spin_limit_ticks;  // in wall-clock ticks
     uint32_t mask;              // ring_entries - 1
@@ -95,6 +99,7 @@ constexpr uint32_t GEMV_KC = 64;           // rows of W per GEMV unit
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
 constexpr uint32_t MAX_TILES = 1u << 22;   // hard cap of units per descriptor
+constexpr uint32_t MAX_DEPS = 14;          // explicit dependencies: 6 in the descriptor + 8 beside it
 
 __host__ __device__ inline uint32_t dt_in(uint32_t flags) { return flags & 15u; }
 __host__ __device__ inline uint32_t dt_out(uint32_t flags) { return (flags >> 4) & 15u; }

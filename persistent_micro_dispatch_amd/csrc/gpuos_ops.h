@@ -59,28 +59,30 @@ __device__ __forceinline__ float ld_elem(const uint8_t* p, uint64_t i) {
     else return bf2f(((const uint16_t*)p)[i]);
 }
 template <uint32_t DT>
-__device__ __forceinline__ void st_elem(uint8_t* p, uint64_t i, float v) {
-    if constexpr (DT == GPUOS_F32) ((float*)p)[i] = v;
-    else ((uint16_t*)p)[i] = (uint16_t)f2bf(v);
-}
+__device__ __forceinline__ void st_elem(uint8_t* p, uint64_t i, float v);
 
 __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : (x != x ? x : 0.0f); }
 
 // GELU, tanh approximation, evaluated as x / (1 + exp(-2u)) with
 // u = sqrt(2/pi) (x + 0.044715 x^3) (the same function; no cancellation).
-// The exponent is formed in double and split as k ln2 + r so that only
-// |r| <= ln2/2 goes through the fp32 exp: relative error stays ~3 ulp even
-// where |2u| is large (x near -10).
+// The exponent a = -2u is formed in double and split as k ln2 + r with
+// |r| <= ln2/2, so only r goes through the fp32 exp.  For a > 0 (x < 0) the
+// result x e^{-a} / (1 + e^{-a}) is formed as a normal float and scaled by
+// 2^-k last, so results down in the denormal range are rounded only once.
 __device__ __forceinline__ float gelu_f(float x) {
     const double xd = (double)x;
     const double a = -2.0 * 0.7978845608028654 * (xd + 0.044715 * xd * xd * xd);
     if (a != a) return x;                    // NaN input
-    if (a > 300.0) return x / INFINITY;      // exp(-2u) = inf: -0 for finite x, NaN for -inf
+    if (a > 300.0) return x * 0.0f;          // below every denormal: -0 (NaN for -inf)
     if (a < -300.0) return x;                // exp(-2u) = 0
     const double k = rint(a * 1.4426950408889634);
     const float r = (float)(a - k * 0.6931471805599453);
-    const float e = ldexpf(expf(r), (int)k);
-    return x / (1.0f + e);
+    if (a > 0.0) {
+        const float er = expf(-r);                 // e^{-r} in [0.7, 1.42]
+        const float t = ldexpf(er, -(int)k);       // e^{-a}
+        return ldexpf(x * er / (1.0f + t), -(int)k);
+    }
+    return x / (1.0f + ldexpf(expf(r), (int)k));
 }
 
 // max / min under a total order: NaN wins, -0 < +0.
@@ -119,8 +121,44 @@ __device__ __forceinline__ float wtmin(float v) {
     return v;
 }
 
+// Stores of op outputs are device-scope write-through (cache policy SC1): the
+// eight XCD L2s are not coherent, and a release fence on gfx950 has to write
+// back every dirty line of the issuing XCD's L2.  Writing results through
+// keeps that fence cheap and leaves nothing stale for readers on other XCDs.
+// 128-bit stores go through a raw buffer resource built on the unit's base
+// pointer (the per-lane offset stays below 2 GiB); narrower stores use
+// relaxed agent-scope atomic stores, which compile to the same SC1 stores.
+constexpr int CPOL_SC1 = 16;
+struct WBuf {
+    __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ WBuf wbuf(const void* base) {
+    return WBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000)};
+}
+__device__ __forceinline__ void wst16(WBuf b, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.r, (int)off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ void wst32(void* p, uint32_t v) {
+    __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wst16b(void* p, uint16_t v) {
+    __hip_atomic_store((uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wst8(void* p, uint8_t v) {
+    __hip_atomic_store((uint8_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wst64(void* p, uint64_t v) {
+    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wstf(void* p, float v) { wst32(p, __float_as_uint(v)); }
+
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(const u32x4*)p; }
-__device__ __forceinline__ void st16(uint8_t* p, u32x4 v) { *(u32x4*)p = v; }
+
+template <uint32_t DT>
+__device__ __forceinline__ void st_elem(uint8_t* p, uint64_t i, float v) {
+    if constexpr (DT == GPUOS_F32) wstf(p + 4 * i, v);
+    else wst16b(p + 2 * i, (uint16_t)f2bf(v));
+}
 
 // 16 bytes -> VE floats
 template <uint32_t DT>
@@ -175,6 +213,7 @@ __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
     uint8_t* O = (uint8_t*)u.out;
     const bool aligned = (((u.a | u.out | (BIN ? u.b : 0ull)) & 15ull) == 0);
     if (aligned) {
+        const WBuf ob = wbuf(O + start * ES);
         u32x4 va[CH], vb[CH];
 #pragma unroll
         for (uint32_t c = 0; c < CH; ++c) {
@@ -193,7 +232,7 @@ __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
                 if constexpr (BIN) unpack<DT>(vb[c], y);
 #pragma unroll
                 for (uint32_t e = 0; e < VE; ++e) o[e] = ew_op<K>(x[e], BIN ? y[e] : 0.0f);
-                st16(O + idx * ES, pack<DT>(o));
+                wst16(ob, (uint32_t)((idx - start) * ES), pack<DT>(o));
             }
         }
         const uint64_t rem = start + ((end - start) / VE) * VE;
@@ -221,6 +260,7 @@ __device__ __forceinline__ void ew_tile<GPUOS_OP_RELU, GPUOS_BF16>(const Unit& u
         return (h & 0x8000u) ? 0u : h;          // negatives and -0 -> +0
     };
     if (((u.a | u.out) & 15ull) == 0) {
+        const WBuf ob = wbuf(O + start);
         u32x4 va[8];
 #pragma unroll
         for (uint32_t c = 0; c < 8; ++c) {
@@ -236,13 +276,13 @@ __device__ __forceinline__ void ew_tile<GPUOS_OP_RELU, GPUOS_BF16>(const Unit& u
                 o.y = r16(v.y & 0xFFFFu) | (r16(v.y >> 16) << 16);
                 o.z = r16(v.z & 0xFFFFu) | (r16(v.z >> 16) << 16);
                 o.w = r16(v.w & 0xFFFFu) | (r16(v.w >> 16) << 16);
-                st16((uint8_t*)(O + idx), o);
+                wst16(ob, (uint32_t)((idx - start) * 2u), o);
             }
         }
         const uint64_t rem = start + ((end - start) / 8u) * 8u;
-        if (rem + lane < end) O[rem + lane] = (uint16_t)r16(A[rem + lane]);
+        if (rem + lane < end) wst16b(O + rem + lane, (uint16_t)r16(A[rem + lane]));
     } else {
-        for (uint64_t i = start + lane; i < end; i += 64u) O[i] = (uint16_t)r16(A[i]);
+        for (uint64_t i = start + lane; i < end; i += 64u) wst16b(O + i, (uint16_t)r16(A[i]));
     }
 }
 
@@ -270,6 +310,7 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
     if constexpr (K == GPUOS_OP_LAYERNORM) amask |= u.aux0 | u.aux1;
     const bool cached = h <= ROW_MAX_CACHED && (h % VE) == 0 && (amask & 15ull) == 0;
     if (cached) {
+        const WBuf ob = wbuf(O);
         const uint32_t nch = h / VE;
         float v[KMAX][VE];
         u32x4 raw[KMAX];
@@ -326,7 +367,7 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
                     float o[VE];
 #pragma unroll
                     for (uint32_t e = 0; e < VE; ++e) o[e] = v[k][e] / s;
-                    st16(O + (uint64_t)c * 16u, pack<DT>(o));
+                    wst16(ob, c * 16u, pack<DT>(o));
                 }
             }
         } else {  // LAYERNORM
@@ -351,7 +392,7 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
                     unpack<DT>(ld16(Bt + (uint64_t)c * 16u), bb);
 #pragma unroll
                     for (uint32_t e = 0; e < VE; ++e) o[e] = (v[k][e] - mean) * rstd * g[e] + bb[e];
-                    st16(O + (uint64_t)c * 16u, pack<DT>(o));
+                    wst16(ob, c * 16u, pack<DT>(o));
                 }
             }
         }
@@ -421,11 +462,11 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
                 const double y0 = x0 * c - x1 * s;
                 const double y1 = x0 * s + x1 * c;
                 if constexpr (DT == GPUOS_F32) {
-                    ((float*)P)[base + i0] = (float)y0;
-                    ((float*)P)[base + i1] = (float)y1;
+                    wstf(P + 4 * (base + i0), (float)y0);
+                    wstf(P + 4 * (base + i1), (float)y1);
                 } else {
-                    ((uint16_t*)P)[base + i0] = (uint16_t)d2bf(y0);
-                    ((uint16_t*)P)[base + i1] = (uint16_t)d2bf(y1);
+                    wst16b(P + 2 * (base + i0), (uint16_t)d2bf(y0));
+                    wst16b(P + 2 * (base + i1), (uint16_t)d2bf(y1));
                 }
             }
         }
@@ -447,14 +488,16 @@ __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
             const uint64_t cpr = RB / 16u, total = cpr * H;
             for (uint64_t j = lane; j < total; j += 64u) {
                 const uint64_t hh = j / cpr, off = (j % cpr) * 16u;
-                st16(dst + (((uint64_t)b * H + hh) * C + pos) * RB + off, ld16(src + hh * RB + off));
+                const u32x4 v = ld16(src + hh * RB + off);
+                uint8_t* d = dst + (((uint64_t)b * H + hh) * C + pos) * RB + off;
+                wst64(d, (uint64_t)v.x | ((uint64_t)v.y << 32));
+                wst64(d + 8, (uint64_t)v.z | ((uint64_t)v.w << 32));
             }
         } else {
             const uint64_t total = RB * H / 2u;  // 2-byte words (ES is 2 or 4)
             for (uint64_t j = lane; j < total; j += 64u) {
                 const uint64_t byte = j * 2u, hh = byte / RB, off = byte % RB;
-                *(uint16_t*)(dst + (((uint64_t)b * H + hh) * C + pos) * RB + off) =
-                    *(const uint16_t*)(src + hh * RB + off);
+                wst16b(dst + (((uint64_t)b * H + hh) * C + pos) * RB + off, *(const uint16_t*)(src + hh * RB + off));
             }
         }
     }
@@ -562,11 +605,12 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
             const float inv = 1.0f / lsum;
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[e] = acc[e] * inv;
+            const WBuf ob = wbuf(O);
             if constexpr (DTO == GPUOS_F32) {
-                st16(O + c * 32u, pack<GPUOS_F32>(o));
-                st16(O + c * 32u + 16u, pack<GPUOS_F32>(o + 4));
+                wst16(ob, c * 32u, pack<GPUOS_F32>(o));
+                wst16(ob, c * 32u + 16u, pack<GPUOS_F32>(o + 4));
             } else {
-                st16(O + c * 16u, pack<GPUOS_BF16>(o));
+                wst16(ob, c * 16u, pack<GPUOS_BF16>(o));
             }
         }
         return;
@@ -574,10 +618,11 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     // several splits: publish this partial, the last arriver merges
     float* part = (float*)(u.scratch + COUNTER_AREA) + (uint64_t)t * PSTRIDE;
     if (g == 0) {
-        st16((uint8_t*)(part + 4 + 8 * c), pack<GPUOS_F32>(acc));
-        st16((uint8_t*)(part + 4 + 8 * c + 4), pack<GPUOS_F32>(acc + 4));
+        const WBuf pb = wbuf(part);
+        wst16(pb, (4u + 8u * c) * 4u, pack<GPUOS_F32>(acc));
+        wst16(pb, (8u + 8u * c) * 4u, pack<GPUOS_F32>(acc + 4));
     }
-    if (lane == 0) { part[0] = m; part[1] = lsum; }
+    if (lane == 0) { wstf(part, m); wstf(part + 1, lsum); }
     uint32_t* ctr = (uint32_t*)u.scratch + bh;
     uint32_t prev = 0;
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -603,8 +648,7 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
 #pragma unroll
     for (uint32_t e = 0; e < DPL; ++e) {
         const uint32_t d = lane * DPL + e;
-        if constexpr (DTO == GPUOS_F32) ((float*)O)[d] = o[e] * inv;
-        else ((uint16_t*)O)[d] = (uint16_t)f2bf(o[e] * inv);
+        st_elem<DTO>(O, d, o[e] * inv);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -686,7 +730,7 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
 #pragma unroll
     for (uint32_t e = 0; e < VE; ++e) {
         const uint32_t col = col_of(e);
-        if (col < N) part[(uint64_t)ks * N + col] = acc[e];
+        if (col < N) wstf(part + (uint64_t)ks * N + col, acc[e]);
     }
     uint32_t* ctr = (uint32_t*)u.scratch + cb;
     uint32_t prev = 0;
@@ -713,6 +757,7 @@ __device__ __forceinline__ void copy_tile(const Unit& u, uint32_t lane) {
     const uint8_t* A = (const uint8_t*)u.a;
     uint8_t* O = (uint8_t*)u.out;
     if (((u.a | u.out) & 15ull) == 0) {
+        const WBuf ob = wbuf(O + start);
         u32x4 v[16];
 #pragma unroll
         for (uint32_t k = 0; k < 16; ++k) {
@@ -722,12 +767,12 @@ __device__ __forceinline__ void copy_tile(const Unit& u, uint32_t lane) {
 #pragma unroll
         for (uint32_t k = 0; k < 16; ++k) {
             const uint64_t off = start + (uint64_t)(lane + 64u * k) * 16u;
-            if (off + 16 <= end) st16(O + off, v[k]);
+            if (off + 16 <= end) wst16(ob, (uint32_t)(off - start), v[k]);
         }
         const uint64_t rem = start + ((end - start) / 16u) * 16u;
-        for (uint64_t i = rem + lane; i < end; i += 64u) O[i] = A[i];
+        for (uint64_t i = rem + lane; i < end; i += 64u) wst8(O + i, A[i]);
     } else {
-        for (uint64_t i = start + lane; i < end; i += 64u) O[i] = A[i];
+        for (uint64_t i = start + lane; i < end; i += 64u) wst8(O + i, A[i]);
     }
 }
 

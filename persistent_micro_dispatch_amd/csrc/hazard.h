@@ -8,9 +8,24 @@
 // complete before running it.  Descriptors without conflicts run
 // concurrently.
 //
-// The tracker keeps a map of disjoint byte intervals, each with its last
-// writer and the readers since that write.  Sequence numbers below the
-// host's completion watermark are known complete and are never returned.
+// Data structure.  Byte intervals are kept in clusters: a cluster covers a
+// contiguous span that accesses have touched (in practice one tensor) and
+// holds a small sorted vector of disjoint intervals, each with its last
+// writer and the readers since that write.  An access costs one map lookup
+// to find its cluster plus a few edits of a short vector; clusters are
+// created or merged only when an access reaches memory not seen before.
+//  - A read never splits an interval: the reader is recorded on every
+//    interval it overlaps, whole, so intervals are created only by writes
+//    (which coalesce what they cover) and by reads of untouched bytes.  A
+//    later write to the part that was not read then waits for that reader
+//    too: an extra wait, never a missing one.
+//  - A writer's dependency on the interval's previous writer is dropped when
+//    the interval has a live reader: every reader waited for that writer.
+//  - An interval keeps up to MAXR readers; beyond that it keeps the oldest
+//    overflowed reader, and a writer then depends on the whole range from it
+//    (reported through `range_from`).
+// Sequence numbers below the host's completion watermark are known complete
+// and are never returned.
 #pragma once
 #include <stdint.h>
 
@@ -28,110 +43,195 @@ struct Access {
 
 class HazardTracker {
 public:
-    // Appends to `deps` every live seq (>= floor) that `seq` must wait for,
-    // then records the accesses of `seq`.  Reads are recorded before writes,
-    // so an operand that is both read and written ends with `seq` as writer.
-    void analyze(uint64_t seq, const Access* acc, int n, uint64_t floor, std::vector<uint64_t>& deps) {
+    static constexpr int MAXR = 14;
+
+    // Appends to `deps` every live seq (>= floor) that `seq` must wait for
+    // and lowers *range_from to the first seq of a range that must be waited
+    // for entirely (left untouched if none); then records the accesses.
+    void analyze(uint64_t seq, const Access* acc, int n, uint64_t floor, std::vector<uint64_t>& deps,
+                 uint64_t* range_from) {
         for (int i = 0; i < n; ++i) {
             if (acc[i].hi <= acc[i].lo) continue;
-            collect(acc[i], floor, deps);
+            Cluster& c = cluster_for(acc[i].lo, acc[i].hi);
+            collect(c, acc[i], floor, deps, range_from);
         }
-        std::sort(deps.begin(), deps.end());
-        deps.erase(std::unique(deps.begin(), deps.end()), deps.end());
         for (int pass = 0; pass < 2; ++pass) {
             for (int i = 0; i < n; ++i) {
                 if (acc[i].hi <= acc[i].lo || acc[i].write != (pass == 1)) continue;
-                if (acc[i].write) record_write(acc[i].lo, acc[i].hi, seq);
-                else record_read(acc[i].lo, acc[i].hi, seq, floor);
+                Cluster& c = cluster_for(acc[i].lo, acc[i].hi);
+                if (acc[i].write) record_write(c, acc[i].lo, acc[i].hi, seq);
+                else record_read(c, acc[i].lo, acc[i].hi, seq, floor);
+                if (c.regs.size() > c.prune_at) prune(c, floor);
             }
         }
-        if (m_.size() > prune_at_) prune(floor);
     }
 
-    void clear() { m_.clear(); }
-    size_t size() const { return m_.size(); }
+    void clear() { cl_.clear(); }
+    size_t size() const {
+        size_t n = 0;
+        for (auto& kv : cl_) n += kv.second.regs.size();
+        return n;
+    }
+    size_t clusters() const { return cl_.size(); }
 
 private:
     struct Region {
-        uint64_t hi;
-        uint64_t writer;                // 0 = none
-        std::vector<uint64_t> readers;  // since the last write
+        uint64_t lo, hi;
+        uint64_t writer;    // 0 = none
+        uint64_t overflow;  // 0 = none; else the oldest reader not kept inline
+        uint32_t nr;
+        uint64_t readers[MAXR];
     };
-    using Map = std::map<uint64_t, Region>;
-    Map m_;
-    size_t prune_at_ = 1u << 16;
+    struct Cluster {
+        uint64_t hi;
+        std::vector<Region> regs;  // sorted by lo, disjoint, inside [key, hi)
+        size_t prune_at = 64;
+    };
+    std::map<uint64_t, Cluster> cl_;
 
-    Map::iterator first_overlap(uint64_t lo) {
-        auto it = m_.upper_bound(lo);
-        if (it != m_.begin()) {
+    static Region make(uint64_t lo, uint64_t hi, uint64_t writer) {
+        Region r;
+        r.lo = lo;
+        r.hi = hi;
+        r.writer = writer;
+        r.overflow = 0;
+        r.nr = 0;
+        return r;
+    }
+
+    // The cluster containing [lo, hi), created, extended or merged as needed.
+    Cluster& cluster_for(uint64_t lo, uint64_t hi) {
+        auto it = cl_.upper_bound(lo);
+        if (it != cl_.begin()) {
             auto p = std::prev(it);
-            if (p->second.hi > lo) return p;
+            if (p->second.hi > lo) it = p;
         }
-        return it;
+        if (it != cl_.end() && it->first <= lo && it->second.hi >= hi) return it->second;  // common case
+        // collect every cluster overlapping [lo, hi)
+        auto first = it;
+        uint64_t nlo = lo, nhi = hi;
+        size_t k = 0;
+        for (auto j = it; j != cl_.end() && j->first < hi; ++j, ++k) {
+            nlo = std::min(nlo, j->first);
+            nhi = std::max(nhi, j->second.hi);
+        }
+        Cluster merged;
+        merged.hi = nhi;
+        auto j = first;
+        for (size_t q = 0; q < k; ++q) {
+            merged.regs.insert(merged.regs.end(), j->second.regs.begin(), j->second.regs.end());
+            j = cl_.erase(j);
+        }
+        merged.prune_at = std::max<size_t>(64, 2 * merged.regs.size());
+        return cl_.emplace_hint(j, nlo, std::move(merged))->second;
     }
 
-    void collect(const Access& a, uint64_t floor, std::vector<uint64_t>& deps) {
-        for (auto it = first_overlap(a.lo); it != m_.end() && it->first < a.hi; ++it) {
-            const Region& r = it->second;
-            if (r.writer >= floor && r.writer != 0) deps.push_back(r.writer);
-            if (a.write)
-                for (uint64_t s : r.readers)
-                    if (s >= floor) deps.push_back(s);
+    // index of the first region with hi > x
+    static size_t first_after(const std::vector<Region>& v, uint64_t x) {
+        size_t a = 0, b = v.size();
+        while (a < b) {
+            const size_t m = (a + b) >> 1;
+            if (v[m].hi > x) b = m; else a = m + 1;
+        }
+        return a;
+    }
+
+    // readers are appended in sequence order, so the array is sorted and the
+    // completed ones form a prefix
+    static void prune_readers(Region& r, uint64_t floor) {
+        if (r.overflow && r.overflow < floor) r.overflow = 0;
+        if (r.nr == 0 || r.readers[0] >= floor) return;
+        uint32_t k = 1;
+        while (k < r.nr && r.readers[k] < floor) ++k;
+        std::copy(r.readers + k, r.readers + r.nr, r.readers);
+        r.nr -= k;
+    }
+
+    void collect(Cluster& c, const Access& a, uint64_t floor, std::vector<uint64_t>& deps, uint64_t* range_from) {
+        for (size_t i = first_after(c.regs, a.lo); i < c.regs.size() && c.regs[i].lo < a.hi; ++i) {
+            Region& r = c.regs[i];
+            prune_readers(r, floor);
+            const bool live_w = r.writer >= floor && r.writer != 0;
+            if (!a.write || (r.nr == 0 && !r.overflow)) {
+                if (live_w) deps.push_back(r.writer);
+                continue;
+            }
+            for (uint32_t k = 0; k < r.nr; ++k) deps.push_back(r.readers[k]);
+            if (r.overflow && r.overflow < *range_from) *range_from = r.overflow;
         }
     }
 
-    // make x a region boundary
-    void split_at(uint64_t x) {
-        auto it = m_.upper_bound(x);
-        if (it == m_.begin()) return;
-        auto p = std::prev(it);
-        if (p->first < x && x < p->second.hi) {
-            Region tail = p->second;
-            p->second.hi = x;
-            m_.emplace_hint(it, x, std::move(tail));
+    static void record_write(Cluster& c, uint64_t lo, uint64_t hi, uint64_t seq) {
+        auto& v = c.regs;
+        const size_t i0 = first_after(v, lo);
+        size_t i1 = i0;
+        while (i1 < v.size() && v[i1].lo < hi) ++i1;
+        if (i1 == i0 + 1 && v[i0].lo == lo && v[i0].hi == hi) {  // exact match: reuse
+            v[i0].writer = seq;
+            v[i0].nr = 0;
+            v[i0].overflow = 0;
+            return;
+        }
+        Region parts[3];
+        int np = 0;
+        if (i1 > i0 && v[i0].lo < lo) { parts[np] = v[i0]; parts[np].hi = lo; ++np; }
+        parts[np++] = make(lo, hi, seq);
+        if (i1 > i0 && v[i1 - 1].hi > hi) { parts[np] = v[i1 - 1]; parts[np].lo = hi; ++np; }
+        const size_t old = i1 - i0;
+        if ((size_t)np <= old) {
+            std::copy(parts, parts + np, v.begin() + (long)i0);
+            v.erase(v.begin() + (long)(i0 + np), v.begin() + (long)i1);
+        } else {
+            std::copy(parts, parts + old, v.begin() + (long)i0);
+            v.insert(v.begin() + (long)(i0 + old), parts + old, parts + np);
         }
     }
 
-    void record_write(uint64_t lo, uint64_t hi, uint64_t seq) {
-        split_at(lo);
-        split_at(hi);
-        auto it = m_.lower_bound(lo);
-        while (it != m_.end() && it->first < hi) it = m_.erase(it);
-        m_.emplace_hint(it, lo, Region{hi, seq, {}});
+    static void add_reader(Region& r, uint64_t seq) {
+        if (r.nr < MAXR) {
+            r.readers[r.nr++] = seq;
+            return;
+        }
+        const uint64_t oldest = r.readers[0];
+        if (!r.overflow || oldest < r.overflow) r.overflow = oldest;
+        std::copy(r.readers + 1, r.readers + MAXR, r.readers);
+        r.readers[MAXR - 1] = seq;
     }
 
-    void record_read(uint64_t lo, uint64_t hi, uint64_t seq, uint64_t floor) {
-        split_at(lo);
-        split_at(hi);
+    static void record_read(Cluster& c, uint64_t lo, uint64_t hi, uint64_t seq, uint64_t floor) {
+        auto& v = c.regs;
+        size_t i = first_after(v, lo);
         uint64_t cur = lo;
-        auto it = m_.lower_bound(lo);
         while (cur < hi) {
-            if (it == m_.end() || it->first > cur) {
-                // gap [cur, next start or hi): a region with no writer
-                const uint64_t end = (it == m_.end() || it->first > hi) ? hi : it->first;
-                it = m_.emplace_hint(it, cur, Region{end, 0, {seq}});
-                ++it;
+            if (i == v.size() || v[i].lo > cur) {
+                // gap [cur, next start or hi): an interval with no writer
+                const uint64_t end = (i == v.size() || v[i].lo > hi) ? hi : v[i].lo;
+                Region g = make(cur, end, 0);
+                g.nr = 1;
+                g.readers[0] = seq;
+                v.insert(v.begin() + (long)i, g);
+                ++i;
                 cur = end;
                 continue;
             }
-            Region& r = it->second;
-            auto& rd = r.readers;
-            rd.erase(std::remove_if(rd.begin(), rd.end(), [&](uint64_t s) { return s < floor; }), rd.end());
-            rd.push_back(seq);
-            cur = r.hi;
-            ++it;
+            prune_readers(v[i], floor);
+            add_reader(v[i], seq);
+            cur = v[i].hi;
+            ++i;
         }
     }
 
     // drop intervals that carry no live information
-    void prune(uint64_t floor) {
-        for (auto it = m_.begin(); it != m_.end();) {
-            Region& r = it->second;
-            bool live = r.writer >= floor && r.writer != 0;
-            for (uint64_t s : r.readers) live |= s >= floor;
-            it = live ? std::next(it) : m_.erase(it);
+    static void prune(Cluster& c, uint64_t floor) {
+        auto& v = c.regs;
+        size_t k = 0;
+        for (size_t i = 0; i < v.size(); ++i) {
+            prune_readers(v[i], floor);
+            const bool live = (v[i].writer >= floor && v[i].writer != 0) || v[i].nr || v[i].overflow;
+            if (live) v[k++] = v[i];
         }
-        prune_at_ = std::max<size_t>(1u << 16, 2 * m_.size());
+        v.resize(k);
+        c.prune_at = std::max<size_t>(64, 2 * v.size());
     }
 };
 

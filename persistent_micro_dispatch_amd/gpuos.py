@@ -13,7 +13,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgpuos.so")
+LIB_PATH = os.environ.get("GPUOS_LIB") or os.path.join(_PKG, "libgpuos.so")
 
 # ---- constants (mirror include/gpuos.h) ----
 GPUOS_OK, GPUOS_E_INVAL, GPUOS_E_FULL, GPUOS_E_NOOP = 0, -1, -2, -3
@@ -29,6 +29,7 @@ GPUOS_OP_USER = 64
 GPUOS_F32, GPUOS_BF16 = 0, 1
 GPUOS_F_ROPE_HALF = 1 << 8
 GPUOS_INIT_LOOPBACK = 1
+GPUOS_INIT_TRACE = 2
 GPUOS_SUBMIT_BLOCK, GPUOS_SUBMIT_NOHAZARD, GPUOS_SUBMIT_SERIAL = 1, 2, 4
 GPUOS_SEQ_ALL = 0xFFFFFFFFFFFFFFFF
 
@@ -89,7 +90,8 @@ class Stats(ctypes.Structure):
                 ("fetched", ctypes.c_uint64), ("dep_waits", ctypes.c_uint64),
                 ("num_wgs", ctypes.c_uint32), ("waves_per_wg", ctypes.c_uint32),
                 ("ring_entries", ctypes.c_uint32), ("cu_count", ctypes.c_uint32),
-                ("next_seq", ctypes.c_uint64)]
+                ("next_seq", ctypes.c_uint64), ("deps_explicit", ctypes.c_uint64),
+                ("deps_range", ctypes.c_uint64)]
 
 
 _lib = None
@@ -97,8 +99,11 @@ EXPORTS = [
     "gpuos_abi_version", "gpuos_init", "gpuos_register_op", "gpuos_submit", "gpuos_submit_bursts", "gpuos_sync",
     "gpuos_query", "gpuos_pause", "gpuos_resume", "gpuos_shutdown", "gpuos_stats_get",
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
-    "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench",
+    "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_trace_read",
 ]
+
+TRACE_DTYPE = np.dtype([("seq", "<u8"), ("tile", "<u4"), ("hw", "<u4"), ("t_claim", "<u8"), ("t_ready", "<u8"),
+                        ("t_body", "<u8"), ("t_done", "<u8"), ("unit", "<u8"), ("pad", "<u8")])
 
 
 def lib():
@@ -128,6 +133,7 @@ def lib():
         "gpuos_graph_build": ([vp, u32, vp, vp, u64, ctypes.POINTER(vp)], ctypes.c_int),
         "gpuos_graph_launch": ([vp, vp], ctypes.c_int),
         "gpuos_graph_destroy": ([vp], ctypes.c_int),
+        "gpuos_trace_read": ([vp, vp, u64, ctypes.POINTER(u64)], ctypes.c_int),
         "gpuos_null_launch_bench": ([vp, u32, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     }
@@ -256,3 +262,11 @@ def gpuos_null_launch_bench(hip_stream: int, n: int) -> Tuple[float, float]:
     _check("gpuos_null_launch_bench",
            lib().gpuos_null_launch_bench(hip_stream or None, n, ctypes.byref(a), ctypes.byref(s)))
     return a.value, s.value
+
+
+def gpuos_trace_read(ctx: int, max_records: int = 1 << 20) -> np.ndarray:
+    """Trace of the last finished launch (records with t_done == 0 are unused)."""
+    out = np.zeros(max_records, TRACE_DTYPE)
+    n = ctypes.c_uint64(0)
+    _check("gpuos_trace_read", lib().gpuos_trace_read(ctx, out.ctypes.data, max_records, ctypes.byref(n)))
+    return out[out["t_done"] != 0]
