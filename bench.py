@@ -71,7 +71,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="elementwise")
-    ap.add_argument("--waves", type=int, default=4)
+    ap.add_argument("--waves", type=int, default=1, help="wave64s per workgroup (one workgroup per CU)")
+    ap.add_argument("--ring", type=int, default=1024, help="ring entries")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
@@ -97,7 +98,7 @@ def main():
     bursts = np.asarray(stream.bursts, np.uint32)
     step_bytes = int(algorithmic_bytes(recs).sum())
 
-    ctx = G.gpuos_init(waves_per_wg=args.waves)
+    ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring)
     st0 = G.gpuos_stats_get(ctx)
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
 
@@ -259,6 +260,9 @@ def main():
         "units_per_step": (st["units"] - st0["units"]) / max(1, args.steps + args.warmup),
         "dep_waits_per_step": (st["dep_waits"] - st0["dep_waits"]) / max(1, args.steps + args.warmup),
         "fetch_batches_per_step": (st["fetch_batches"] - st0["fetch_batches"]) / max(1, args.steps + args.warmup),
+        "host_submit_ns_per_desc": st["ns_submit"] / max(1, st["submitted"]),
+        "host_blocked_ns_per_desc": st["ns_blocked"] / max(1, st["submitted"]),
+        "host_annotate_ns_per_desc": st["ns_annotate"] / max(1, st["submitted"]),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

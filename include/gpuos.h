@@ -239,6 +239,9 @@ typedef struct gpuos_stats {
     uint64_t next_seq;           /* sequence number the next submit will get */
     uint64_t deps_explicit;      /* explicit dependencies written (host) */
     uint64_t deps_range;         /* descriptors that fell back to a range dependency */
+    uint64_t ns_submit;          /* host time spent inside gpuos_submit */
+    uint64_t ns_blocked;         /*   of which waiting for free ring slots (BLOCK) */
+    uint64_t ns_annotate;        /*   of which annotating and writing descriptors */
 } gpuos_stats;
 
 /* Snapshot of the counters.  Device counters are added up when a launch

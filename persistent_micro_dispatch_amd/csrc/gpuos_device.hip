@@ -46,6 +46,7 @@ __device__ __forceinline__ void nap(uint32_t n) {
 }
 
 constexpr uint64_t STOP_DRAIN = 1, STOP_ABORT = 2;
+constexpr uint32_t DEP_BACKOFF_MAX = 16;
 constexpr uint64_t NO_SCRATCH = ~0ull;
 
 // ------------------------------------------------------------------ worker
@@ -137,8 +138,10 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
                     }
                     break;
                 }
+                // dependency waits back off to at most 16 x 64 clocks: the
+                // awaited op is in flight, so a long sleep only adds latency
                 nap(dbo);
-                dbo = dbo * 2 < A.backoff_max ? dbo * 2 : A.backoff_max;
+                dbo = dbo * 2 < DEP_BACKOFF_MAX ? dbo * 2 : DEP_BACKOFF_MAX;
             }
             if (stop) break;
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -150,11 +153,14 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         // completion: the last unit of the descriptor releases the slot
         bool last = true;
         if (U.ntiles > 1) {
+            // release this unit's writes; only the last unit needs to acquire
+            // the others' before it signals the descriptor complete
             uint32_t prev = 0;
             if (lane == 0)
-                prev = __hip_atomic_fetch_add(&A.tiles_done[slot], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                prev = __hip_atomic_fetch_add(&A.tiles_done[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
             last = prev == U.ntiles - 1;
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         if (last) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // system scope: outputs visible to all

@@ -218,6 +218,7 @@ struct gpuos_ctx {
     uint64_t submitted = 0, completed = 0, full_rej = 0;
     uint64_t acc_units = 0, acc_depw = 0, acc_batches = 0, acc_fetched = 0;
     uint64_t deps_explicit = 0, deps_range = 0;
+    uint64_t ns_submit = 0, ns_blocked = 0, ns_hazard = 0;  // host time inside gpuos_submit
     // loopback consumer
     std::thread lb_thread;
     std::atomic<bool> lb_stop{false};
@@ -578,6 +579,7 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
     std::lock_guard<std::mutex> g(c->mu);
     if (first_seq) *first_seq = c->next_seq;
     if (count == 0) return GPUOS_OK;
+    const uint64_t t_enter = now_ns();
     // resolve kinds and validate shapes before touching the ring
     uint32_t kinds_small[64];
     std::vector<uint32_t> kinds_big;
@@ -606,13 +608,16 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
     if (c->wm < need_wm) {
         if (!(flags & GPUOS_SUBMIT_BLOCK)) { ++c->full_rej; return GPUOS_E_FULL; }
         uint32_t spins = 0;
+        const uint64_t tb = now_ns();
         while (c->wm < need_wm) {
             if (c->hctl && ld_acq(&c->hctl->dev_error)) return GPUOS_E_DEVICE;
             if (++spins > 1000) std::this_thread::yield();
             else GPUOS_PAUSE();
             refresh_wm(c);
         }
+        c->ns_blocked += now_ns() - tb;
     }
+    const uint64_t t_hz0 = now_ns();
     const uint64_t s0 = c->next_seq;
     Access acc[2 * MAX_B + 4];
     for (uint32_t i = 0; i < count; ++i) {
@@ -656,6 +661,7 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
         c->status[slot] = 0;
         memcpy(&c->ring[slot], &d, sizeof(gpuos_desc));
     }
+    const uint64_t t_hz1 = now_ns();
     // commit in order (store-release of each stamp)
     for (uint32_t i = 0; i < count; ++i) {
         const uint64_t s = s0 + i;
@@ -663,6 +669,8 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
     }
     c->next_seq += count;
     c->submitted += count;
+    c->ns_hazard += t_hz1 - t_hz0;
+    c->ns_submit += now_ns() - t_enter;
     return GPUOS_OK;
 }
 
@@ -774,6 +782,9 @@ int gpuos_stats_get(void* ctx, gpuos_stats* out) {
     out->next_seq = c->next_seq;
     out->deps_explicit = c->deps_explicit;
     out->deps_range = c->deps_range;
+    out->ns_submit = c->ns_submit;
+    out->ns_blocked = c->ns_blocked;
+    out->ns_annotate = c->ns_hazard;
     if (!c->loopback) {
         out->units = c->acc_units;
         out->dep_waits = c->acc_depw;

@@ -92,6 +92,11 @@ struct ExecArgs {
 // launcher and host-side validation so that all three agree.
 // ---------------------------------------------------------------------------
 constexpr uint32_t EW_TILE_BYTES = 8192;   // per operand per element-wise tile
+constexpr uint32_t EW_TILE_BYTES_GELU = 2048;  // GELU costs ~40 instructions per element: smaller units
+
+__host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind) {
+    return kind == GPUOS_OP_GELU ? EW_TILE_BYTES_GELU : EW_TILE_BYTES;
+}
 constexpr uint32_t COPY_TILE_BYTES = 16384;
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
 constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit
@@ -146,7 +151,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (di != dout) return bad();
             if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
             if ((d.kind == GPUOS_OP_ADD || d.kind == GPUOS_OP_MUL) && d.size > 0 && d.b == 0) return bad();
-            uint64_t t = cdiv(d.size, EW_TILE_BYTES / esz(di));
+            uint64_t t = cdiv(d.size, ew_tile_bytes(d.kind) / esz(di));
             if (t > MAX_TILES) return bad();
             p.ntiles = t ? (uint32_t)t : 1u;
             return p;

@@ -65,11 +65,13 @@ __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : (x != x
 
 // GELU, tanh approximation, evaluated as x / (1 + exp(-2u)) with
 // u = sqrt(2/pi) (x + 0.044715 x^3) (the same function; no cancellation).
-// The exponent a = -2u is formed in double and split as k ln2 + r with
-// |r| <= ln2/2, so only r goes through the fp32 exp.  For a > 0 (x < 0) the
-// result x e^{-a} / (1 + e^{-a}) is formed as a normal float and scaled by
-// 2^-k last, so results down in the denormal range are rounded only once.
-__device__ __forceinline__ float gelu_f(float x) {
+// For |x| < 3 (|2u| < 7) fp32 arithmetic keeps the relative error near
+// 1e-6.  Beyond that the exponent a = -2u is formed in double and split as
+// k ln2 + r with |r| <= ln2/2, so only r goes through the fp32 exp; for
+// a > 0 (x < 0) the result x e^{-a} / (1 + e^{-a}) is formed as a normal
+// float and scaled by 2^-k last, so results in the denormal range are
+// rounded only once.
+__device__ __forceinline__ float gelu_wide(float x) {
     const double xd = (double)x;
     const double a = -2.0 * 0.7978845608028654 * (xd + 0.044715 * xd * xd * xd);
     if (a != a) return x;                    // NaN input
@@ -83,6 +85,11 @@ __device__ __forceinline__ float gelu_f(float x) {
         return ldexpf(x * er / (1.0f + t), -(int)k);
     }
     return x / (1.0f + ldexpf(expf(r), (int)k));
+}
+__device__ __forceinline__ float gelu_f(float x) {
+    if (!(fabsf(x) < 3.0f)) return gelu_wide(x);   // also NaN and infinities
+    const float a = -1.5957691216057308f * (x + 0.044715f * x * x * x);
+    return x / (1.0f + expf(a));
 }
 
 // max / min under a total order: NaN wins, -0 < +0.
@@ -195,13 +202,13 @@ __device__ __forceinline__ float ew_op(float x, float y) {
     else return gelu_f(x);
 }
 
-// One tile of EW_TILE_BYTES per operand: 8 chunks of 16 bytes per lane,
-// all loads issued before any compute.  The ragged tail (fewer than one
+// One tile of ew_tile_bytes(K) per operand (8 chunks of 16 bytes per lane,
+// 2 for GELU), all loads issued before any compute.  The ragged tail (fewer than one
 // chunk) and misaligned operands take an element loop.
 template <uint32_t K, uint32_t DT>
 __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
-    constexpr uint32_t TILE = EW_TILE_BYTES / ES;
+    constexpr uint32_t TILE = ew_tile_bytes(K) / ES;
     constexpr uint32_t VE = 16u / ES;
     constexpr uint32_t CH = TILE / VE / 64u;
     constexpr bool BIN = (K == GPUOS_OP_ADD || K == GPUOS_OP_MUL);

@@ -50,18 +50,39 @@ public:
     // for entirely (left untouched if none); then records the accesses.
     void analyze(uint64_t seq, const Access* acc, int n, uint64_t floor, std::vector<uint64_t>& deps,
                  uint64_t* range_from) {
-        for (int i = 0; i < n; ++i) {
-            if (acc[i].hi <= acc[i].lo) continue;
-            Cluster& c = cluster_for(acc[i].lo, acc[i].hi);
-            collect(c, acc[i], floor, deps, range_from);
+        // resolve each access's cluster once (a merge invalidates earlier
+        // ones: resolve again until no merge happens)
+        Cluster* cp[24];
+        if (n > 24) n = 24;
+        for (int round = 0; round < 4; ++round) {
+            const uint64_t m0 = merges_;
+            for (int i = 0; i < n; ++i) cp[i] = acc[i].hi > acc[i].lo ? &cluster_for(acc[i].lo, acc[i].hi) : nullptr;
+            if (merges_ == m0) break;
         }
+        bool distinct = true;
+        for (int i = 0; i < n && distinct; ++i)
+            for (int j = 0; j < i; ++j)
+                if (cp[i] && cp[i] == cp[j]) { distinct = false; break; }
+        if (distinct) {
+            // no two accesses share a cluster: each can be collected and
+            // recorded in one pass without seeing the others
+            for (int i = 0; i < n; ++i) {
+                if (!cp[i]) continue;
+                collect(*cp[i], acc[i], floor, deps, range_from);
+                if (acc[i].write) record_write(*cp[i], acc[i].lo, acc[i].hi, seq);
+                else record_read(*cp[i], acc[i].lo, acc[i].hi, seq, floor);
+                if (cp[i]->regs.size() > cp[i]->prune_at) prune(*cp[i], floor);
+            }
+            return;
+        }
+        for (int i = 0; i < n; ++i)
+            if (cp[i]) collect(*cp[i], acc[i], floor, deps, range_from);
         for (int pass = 0; pass < 2; ++pass) {
             for (int i = 0; i < n; ++i) {
-                if (acc[i].hi <= acc[i].lo || acc[i].write != (pass == 1)) continue;
-                Cluster& c = cluster_for(acc[i].lo, acc[i].hi);
-                if (acc[i].write) record_write(c, acc[i].lo, acc[i].hi, seq);
-                else record_read(c, acc[i].lo, acc[i].hi, seq, floor);
-                if (c.regs.size() > c.prune_at) prune(c, floor);
+                if (!cp[i] || acc[i].write != (pass == 1)) continue;
+                if (acc[i].write) record_write(*cp[i], acc[i].lo, acc[i].hi, seq);
+                else record_read(*cp[i], acc[i].lo, acc[i].hi, seq, floor);
+                if (cp[i]->regs.size() > cp[i]->prune_at) prune(*cp[i], floor);
             }
         }
     }
@@ -88,6 +109,7 @@ private:
         size_t prune_at = 64;
     };
     std::map<uint64_t, Cluster> cl_;
+    uint64_t merges_ = 0;
 
     static Region make(uint64_t lo, uint64_t hi, uint64_t writer) {
         Region r;
@@ -108,6 +130,7 @@ private:
         }
         if (it != cl_.end() && it->first <= lo && it->second.hi >= hi) return it->second;  // common case
         // collect every cluster overlapping [lo, hi)
+        ++merges_;
         auto first = it;
         uint64_t nlo = lo, nhi = hi;
         size_t k = 0;

@@ -91,7 +91,8 @@ class Stats(ctypes.Structure):
                 ("num_wgs", ctypes.c_uint32), ("waves_per_wg", ctypes.c_uint32),
                 ("ring_entries", ctypes.c_uint32), ("cu_count", ctypes.c_uint32),
                 ("next_seq", ctypes.c_uint64), ("deps_explicit", ctypes.c_uint64),
-                ("deps_range", ctypes.c_uint64)]
+                ("deps_range", ctypes.c_uint64), ("ns_submit", ctypes.c_uint64),
+                ("ns_blocked", ctypes.c_uint64), ("ns_annotate", ctypes.c_uint64)]
 
 
 _lib = None
