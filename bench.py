@@ -8,14 +8,27 @@ op body, completion) over one seeded synthetic descriptor stream:
                          of 65536 values; n log-uniform in [256, 65536];
                          {add, mul, relu, gelu}; 10% in place; bursts 1-64
   pr1                    1,000 fp32 add/mul/relu descriptors over 16 x 4096
+  rows                   50,000 row ops (sum/max/min/softmax/LayerNorm) on
+                         [r in 1..64, h in {768,1024,2048,4096}] fp32 slices
+                         of a 2 GiB pool
+  decode                 25 decode steps x 32 layers x {RoPE, KV append,
+                         SDPA}: B in {1,2,4,8}, 32 heads x 128, bf16 KV cache
+                         of 4096 per sequence (16 GiB), L in [128, 4096]
+  mixed                  10 tokens x 32 layers x 11 ops at hidden 1024 (LN,
+                         GEMV 1024x3072, RoPE, KV append, SDPA, add, LN, GEMV
+                         1024x3072, GELU, GEMV 3072x1024, add); with --gemm a
+                         bf16 8192^3 GEMM loop co-runs on a second stream
+Pools larger than the host generator fills quickly (rows, decode, mixed) are
+drawn on the GPU with torch's seeded generator.
+
 The executor is launched at the start of each step and paused (it drains and
-exits) at its end, so each launch covers exactly one step; its duration comes
+exits) at its end, so one launch covers exactly one step; its duration comes
 from HIP events recorded on the executor's own stream.
 
 Printed: one JSON line with micro-ops/s (the headline value), p50/p99
 closed-loop per-op latency, the eager hipLaunchKernel-per-op and hipGraph
-baselines, null-launch cost, the roofline of the executor kernel and the CPU
-oracle timed on a bounded sample of the same stream.
+baselines, null-launch cost, host submission cost, the roofline of the
+executor kernel and the CPU oracle timed on a bounded sample of the stream.
 """
 from __future__ import annotations
 
@@ -37,19 +50,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(recs) -> np.ndarray:
-    """Bytes each element-wise descriptor must move: every operand read once,
-    the output written once (3 n s for add/mul, 2 n s for relu/gelu)."""
-    import workloads as W
-    es = np.where(recs["dtype"] == W.BF16, 2, 4).astype(np.int64)
-    n = recs["size"].astype(np.int64)
-    binary = (recs["op"] == W.OP_ADD) | (recs["op"] == W.OP_MUL)
-    unary = (recs["op"] == W.OP_RELU) | (recs["op"] == W.OP_GELU)
-    return np.where(binary, 3 * n * es, np.where(unary, 2 * n * es, 0))
-
-
 def make_stream(name):
     import workloads as W
+    fill = "host"
     if name == "elementwise":
         s = W.make_elementwise()
         desc = ("element-wise micro-op stream: 100,000 descriptors over 32 fp32 + 32 bf16 tensors of 65536 "
@@ -59,10 +62,23 @@ def make_stream(name):
         s = W.make_pr1()
         s.bursts = np.full(len(s) // 8, 8)
         desc = ("PR1: 1,000 fp32 descriptors over 16 vectors of 4096 values U[-1,1]; op uniform over "
-                "{add, mul, relu}; operands and outputs uniform over the pool; ring of 4096")
+                "{add, mul, relu}; operands and outputs uniform over the pool")
+    elif name == "rows":
+        s, fill = W.make_rows(), "device"
+        desc = ("row ops: 50,000 descriptors of [r, h] fp32, r in {1,2,...,64}, h in {768,1024,2048,4096}, "
+                "x ~ N(0,2) from a 2 GiB pool; op uniform over {sum, max, min, softmax, LayerNorm}")
+    elif name == "decode":
+        s, fill = W.make_decode(steps=25), "device"
+        desc = ("attention decoding: 25 decode steps x 32 layers x {RoPE(theta 1e4), KV append, SDPA}; "
+                "B in {1,2,4,8}, 32 heads x 128, bf16 KV cache 4096/sequence, L in [128, 4096] +1 per step")
+    elif name == "mixed":
+        s, fill = W.make_mixed(tokens=10), "device"
+        desc = ("mixed decode pipeline: 10 tokens x 32 layers x 11 ops at hidden 1024, 8 heads x 128, bf16: "
+                "LN, GEMV 1x1024.1024x3072, RoPE, KV append, SDPA (L in [64, 2048]), add, LN, GEMV 1024x3072, "
+                "GELU, GEMV 3072x1024, add")
     else:
         raise SystemExit(f"unknown workload {name}")
-    return s, desc
+    return s, desc, fill
 
 
 def main():
@@ -73,12 +89,13 @@ def main():
     ap.add_argument("--workload", default="elementwise")
     ap.add_argument("--waves", type=int, default=1, help="wave64s per workgroup (one workgroup per CU)")
     ap.add_argument("--ring", type=int, default=1024, help="ring entries")
+    ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop (mixed workload)")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the dispatcher is a "
-              "single-device path; see the design notes for how it would shard.", file=sys.stderr)
+              "single-device path; the design notes describe how it would shard.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -88,15 +105,15 @@ def main():
     from workloads.gpu import DevicePool, to_descs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    stream, wdesc = make_stream(args.workload)
+    stream, wdesc, fill = make_stream(args.workload)
     recs = stream.recs
     nd = len(recs)
-    log(f"workload {args.workload}: {nd} descriptors, {len(stream.bursts)} bursts")
-    arrays = [b.host_bytes() for b in stream.buffers]
-    pool = DevicePool(arrays)
+    log(f"workload {args.workload}: {nd} descriptors, {len(stream.bursts)} bursts, fill={fill}")
+    arrays = [b.host_bytes() for b in stream.buffers] if fill == "host" else None
+    pool = DevicePool(arrays) if fill == "host" else DevicePool.from_stream(stream, fill="device")
     descs = to_descs(recs, pool.ptrs)
     bursts = np.asarray(stream.bursts, np.uint32)
-    step_bytes = int(algorithmic_bytes(recs).sum())
+    step_bytes = int(W.algorithmic_bytes(recs).sum())
 
     ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring)
     st0 = G.gpuos_stats_get(ctx)
@@ -106,7 +123,7 @@ def main():
         assert G.gpuos_resume(ctx) == 0
         rc, first, n = G.gpuos_submit_bursts(ctx, descs, bursts, G.GPUOS_SUBMIT_BLOCK)
         assert rc == 0 and n == nd, (rc, n)
-        rc, es, stc = G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 120_000_000_000)
+        rc, es, stc = G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 300_000_000_000)
         assert rc == 0, (rc, es, stc)
         assert G.gpuos_pause(ctx, 30_000_000_000) == 0
         return G.gpuos_stats_get(ctx)["last_launch_ms"]
@@ -118,11 +135,53 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         launch_ms.append(one_step())
+        log(f"step {i}: executor launch {launch_ms[-1]:.2f} ms")
     t1 = time.perf_counter()
-    log(f"timed {args.steps} steps in {t1 - t0:.3f} s; executor launches {launch_ms} ms")
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ops_per_s = nd * args.steps / (t1 - t0)
     st = G.gpuos_stats_get(ctx)
+    extra = {}
+
+    # ---- co-running GEMM (mixed workload): bf16 8192^3 loop on its own stream
+    if args.gemm:
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+            b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+            c = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+            torch.matmul(a, b, out=c)
+        gs.synchronize()
+        n_gemm = 40
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(gs):
+            e0.record(gs)
+            for _ in range(n_gemm):
+                torch.matmul(a, b, out=c)
+            e1.record(gs)
+        gs.synchronize()
+        gemm_alone_ms = e0.elapsed_time(e1) / n_gemm
+        # GEMMs and the micro-op stream together
+        with torch.cuda.stream(gs):
+            e0.record(gs)
+            for _ in range(n_gemm):
+                torch.matmul(a, b, out=c)
+            e1.record(gs)
+        tc0 = time.perf_counter()
+        k_co = 0
+        while not e1.query():
+            one_step()
+            k_co += 1
+        tc1 = time.perf_counter()
+        gs.synchronize()
+        gemm_co_ms = e0.elapsed_time(e1) / n_gemm
+        flop = 2.0 * 8192 ** 3
+        extra.update({
+            "gemm_tflops_alone": flop / (gemm_alone_ms * 1e-3) / 1e12,
+            "gemm_tflops_corun": flop / (gemm_co_ms * 1e-3) / 1e12,
+            "corun_steps": k_co,
+            "ops_per_s_with_gemm": nd * k_co / (tc1 - tc0) if k_co else None,
+        })
+        log(f"gemm alone {gemm_alone_ms:.3f} ms, co-run {gemm_co_ms:.3f} ms; {k_co} steps during the GEMMs")
 
     # ---- closed-loop latency: one descriptor at a time, waited for
     assert G.gpuos_resume(ctx) == 0
@@ -156,8 +215,8 @@ def main():
     chain_s = time.perf_counter() - ta
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     chain_ok = float(chain_buf.cpu()[0]) == 5000.0
+    st_end = G.gpuos_stats_get(ctx)
 
-    extra = {}
     if not args.no_baselines:
         # ---- eager: one hipLaunchKernel per descriptor on a torch stream
         s_eager = torch.cuda.Stream()
@@ -175,7 +234,7 @@ def main():
         eager_lat = np.zeros(500)
         for i in range(500):
             ta = time.perf_counter_ns()
-            assert G.gpuos_eager_submit(descs[i:i + 1], sp, scratch.data_ptr(), scratch_b) == 0
+            assert G.gpuos_eager_submit(descs[i % nd:i % nd + 1], sp, scratch.data_ptr(), scratch_b) == 0
             s_eager.synchronize()
             eager_lat[i] = (time.perf_counter_ns() - ta) / 1e3
         # ---- hipGraph: captured per burst; stable = replay prebuilt graphs,
@@ -205,6 +264,7 @@ def main():
             "speedup_vs_eager": ops_per_s / (nb_e / eager_s),
             "graph_stable_ops_per_s": gdesc / stable_s,
             "graph_variable_ops_per_s": gdesc / var_s,
+            "speedup_vs_graph_stable": ops_per_s / (gdesc / stable_s),
             "null_launch_us": null_async / 1e3,
             "null_launch_sync_us": null_sync / 1e3,
         })
@@ -218,17 +278,15 @@ def main():
             "kernel": "gpuos_executor", "launch_ms": mean_launch_ms, "bytes_per_launch": step_bytes}
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and fill == "host":
         import oracle
-        p = oracle.Pool([a.copy() for a in arrays])
         n_cpu = min(nd, 1000)
-        p.run(recs[:min(nd, 100)])  # warm
         p = oracle.Pool([a.copy() for a in arrays])
         ta = time.perf_counter()
         while True:
             p.run(recs[:n_cpu])
             el = time.perf_counter() - ta
-            if el > 2.0 or n_cpu >= nd:
+            if el > 3.0 or n_cpu >= nd:
                 break
             n_cpu = min(nd, n_cpu * 4)
             p = oracle.Pool([a.copy() for a in arrays])
@@ -236,6 +294,7 @@ def main():
         cpu = {"value": n_cpu / el, "unit": "micro-ops/s", "cores": 1, "kind": "oracle",
                "sample": f"first {n_cpu} descriptors of the same stream, sequential C oracle (fp64), one thread"}
 
+    steps_total = max(1, args.steps + args.warmup)
     out = {
         "metric": "micro-ops/sec (+ p50 per-op latency us, vs per-op hipLaunch; HBM GB/s frac)",
         "value": ops_per_s,
@@ -250,19 +309,19 @@ def main():
         "dtype": "f32 (bf16 operands computed in f32)",
         "data": "synthetic",
         "config": {"workload": wdesc, "descriptors_per_step": nd, "waves_per_wg": args.waves,
-                   "num_wgs": st["num_wgs"], "ring_entries": st["ring_entries"]},
+                   "num_wgs": st["num_wgs"], "ring_entries": st["ring_entries"], "fill": fill},
         "p50_us": float(np.percentile(lat, 50)),
         "p99_us": float(np.percentile(lat, 99)),
         "dispatch_interval_us_nop": nop_s / len(nop) * 1e6,
         "dependent_chain_us_per_op": chain_s / len(chain) * 1e6,
         "dependent_chain_ok": chain_ok,
         "stream_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "units_per_step": (st["units"] - st0["units"]) / max(1, args.steps + args.warmup),
-        "dep_waits_per_step": (st["dep_waits"] - st0["dep_waits"]) / max(1, args.steps + args.warmup),
-        "fetch_batches_per_step": (st["fetch_batches"] - st0["fetch_batches"]) / max(1, args.steps + args.warmup),
-        "host_submit_ns_per_desc": st["ns_submit"] / max(1, st["submitted"]),
-        "host_blocked_ns_per_desc": st["ns_blocked"] / max(1, st["submitted"]),
-        "host_annotate_ns_per_desc": st["ns_annotate"] / max(1, st["submitted"]),
+        "units_per_step": (st["units"] - st0["units"]) / steps_total,
+        "dep_waits_per_step": (st["dep_waits"] - st0["dep_waits"]) / steps_total,
+        "fetch_batches_per_step": (st["fetch_batches"] - st0["fetch_batches"]) / steps_total,
+        "host_submit_ns_per_desc": st_end["ns_submit"] / max(1, st_end["submitted"]),
+        "host_blocked_ns_per_desc": st_end["ns_blocked"] / max(1, st_end["submitted"]),
+        "host_annotate_ns_per_desc": st_end["ns_annotate"] / max(1, st_end["submitted"]),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

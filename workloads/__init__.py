@@ -524,3 +524,37 @@ def output_ranges(r) -> list:
     if op == OP_COPY:
         return [(int(buf[OUT]), int(off[OUT]), size)]
     return []
+
+
+def algorithmic_bytes(recs: np.ndarray) -> np.ndarray:
+    """Bytes each record must move at minimum: every operand read once and
+    every output written once (per-op formulas of the measurement plan)."""
+    op = recs["op"]
+    es = np.where(recs["dtype"] == BF16, 2, 4).astype(np.int64)
+    eo = np.where(recs["out_dtype"] == BF16, 2, 4).astype(np.int64)
+    n = recs["size"].astype(np.int64)
+    d0, d1 = recs["dim"][:, 0].astype(np.int64), recs["dim"][:, 1].astype(np.int64)
+    out = np.zeros(len(recs), np.int64)
+    m = (op == OP_ADD) | (op == OP_MUL)
+    out[m] = (2 * es[m] + eo[m]) * n[m]
+    m = (op == OP_RELU) | (op == OP_GELU)
+    out[m] = (es[m] + eo[m]) * n[m]
+    m = (op == OP_SUM) | (op == OP_MAX) | (op == OP_MIN)
+    out[m] = es[m] * n[m] * d0[m] + eo[m] * n[m]
+    m = op == OP_SOFTMAX
+    out[m] = (es[m] + eo[m]) * n[m] * d0[m]
+    m = op == OP_LAYERNORM
+    out[m] = (es[m] + eo[m]) * n[m] * d0[m] + 2 * es[m] * d0[m]
+    m = (op == OP_ROPE) | (op == OP_KV_APPEND)
+    out[m] = 4 * n[m] * d0[m] * d1[m] * es[m]
+    m = op == OP_SDPA
+    if m.any():
+        L = recs["lens"][m].astype(np.int64)
+        bmask = np.arange(8)[None, :] < n[m][:, None]
+        keys = (L * bmask).sum(axis=1)
+        out[m] = (n[m] * d0[m] * d1[m] * (es[m] + eo[m])) + 2 * keys * d0[m] * d1[m] * es[m]
+    m = op == OP_GEMV
+    out[m] = es[m] * d0[m] + es[m] * d0[m] * d1[m] + eo[m] * d1[m]
+    m = op == OP_COPY
+    out[m] = 2 * n[m]
+    return out

@@ -28,8 +28,32 @@ class DevicePool:
         torch.cuda.current_stream().synchronize()
 
     @classmethod
-    def from_stream(cls, stream: W.Stream, device: str = "cuda:0") -> "DevicePool":
-        return cls([b.host_bytes() for b in stream.buffers], device)
+    def from_stream(cls, stream: W.Stream, device: str = "cuda:0", fill: str = "host") -> "DevicePool":
+        """fill="host": values from the seeded host generator (identical to the
+        oracle's inputs); fill="device": same distributions drawn on the GPU by
+        torch's seeded generator (for large benchmark pools; not for parity)."""
+        if fill == "host":
+            return cls([b.host_bytes() for b in stream.buffers], device)
+        import torch
+        self = cls.__new__(cls)
+        self.tensors, self.nbytes = [], []
+        for b in stream.buffers:
+            dt = torch.float32 if b.dtype == W.F32 else torch.bfloat16
+            g = torch.Generator(device=device)
+            g.manual_seed(int(b.seed) & 0x7FFFFFFFFFFFFFFF)
+            kind = b.init[0]
+            if kind == "zeros":
+                v = torch.zeros(b.nelem, dtype=dt, device=device)
+            elif kind == "normal":
+                std, mean = b.init[1], (b.init[2] if len(b.init) > 2 else 0.0)
+                v = (torch.randn(b.nelem, generator=g, device=device) * std + mean).to(dt)
+            else:
+                lo, hi = b.init[1], b.init[2]
+                v = (torch.rand(b.nelem, generator=g, device=device) * (hi - lo) + lo).to(dt)
+            self.tensors.append(v.view(torch.uint8))
+            self.nbytes.append(b.nbytes)
+        torch.cuda.current_stream().synchronize()
+        return self
 
     @property
     def ptrs(self) -> List[int]:
