@@ -97,10 +97,10 @@ constexpr uint32_t EW_TILE_BYTES_GELU = 2048;  // GELU costs ~40 instructions pe
 __host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind) {
     return kind == GPUOS_OP_GELU ? EW_TILE_BYTES_GELU : EW_TILE_BYTES;
 }
-constexpr uint32_t COPY_TILE_BYTES = 16384;
+constexpr uint32_t COPY_TILE_BYTES = 32768;
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
 constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit
-constexpr uint32_t GEMV_KC = 64;           // rows of W per GEMV unit
+constexpr uint32_t GEMV_KC = 256;          // rows of W per GEMV unit
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
 constexpr uint32_t MAX_TILES = 1u << 22;   // hard cap of units per descriptor
@@ -134,7 +134,8 @@ struct Plan {
     uint64_t scratch;     // bytes (0 = none); counters occupy the first COUNTER_AREA
 };
 
-__host__ __device__ inline uint32_t gemv_cols_per_block(uint32_t dt) { return 64u * (16u / esz(dt)); }
+// a GEMV unit covers 16 lanes x 16 bytes of columns (four rows per load)
+__host__ __device__ inline uint32_t gemv_cols_per_block(uint32_t dt) { return 16u * (16u / esz(dt)); }
 
 __host__ __device__ inline Plan make_plan(const PlanIn& d) {
     Plan p{GPUOS_ST_OK, 1u, 0u};

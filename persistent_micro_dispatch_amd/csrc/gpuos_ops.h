@@ -5,6 +5,21 @@
 // Operator list: GPUOS digest page, section 3 Q2 ("Operator library"):
 // element-wise add/mul/ReLU/GELU, softmax, LayerNorm, vector-matrix
 // products, SDPA, rotary embeddings, KV-cache update, sum/max/min.
+//
+// Memory access rules that every body follows:
+//  - Operand pointers arrive in descriptors, so the compiler cannot see that
+//    they are global; left generic they become flat instructions, which also
+//    count on the LDS/scalar counter: every shuffle or scalar load would then
+//    wait for all outstanding loads, and a guarded flat load is preceded by a
+//    full wait.  All loads and stores of op data name the global address
+//    space, or go through a buffer resource.
+//  - A body issues all loads of a batch before it uses any of them, so one
+//    wave keeps 8-32 KiB in flight; stores come after.
+//  - Ragged ends use buffer resources bounded to the valid bytes: 16-byte
+//    loads beyond the bound return zero and stores beyond it are dropped,
+//    without a divergent branch around the access.
+//  - Reductions inside 8- or 16-lane groups use DPP lane moves; across the
+//    four 16-lane rows of the wave, readlane.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -15,6 +30,15 @@
 namespace gpuos {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x4 gc_u32x4;
+typedef __attribute__((address_space(1))) const uint32_t gc_u32;
+typedef __attribute__((address_space(1))) const uint16_t gc_u16;
+typedef __attribute__((address_space(1))) const uint8_t gc_u8;
+typedef __attribute__((address_space(1))) uint64_t g_u64;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+typedef __attribute__((address_space(1))) uint8_t g_u8;
 
 // Wave-uniform view of one work unit.
 struct Unit {
@@ -53,13 +77,99 @@ __device__ __forceinline__ uint32_t d2bf(double x) {
     return f2bf(f);
 }
 
+// ------------------------------------------------------------ global memory
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(gc_u32x4*)p; }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *(gc_u32*)p; }
+__device__ __forceinline__ uint32_t ld2(const uint8_t* p) { return *(gc_u16*)p; }
+__device__ __forceinline__ uint32_t ld1(const uint8_t* p) { return *(gc_u8*)p; }
+
 template <uint32_t DT>
 __device__ __forceinline__ float ld_elem(const uint8_t* p, uint64_t i) {
-    if constexpr (DT == GPUOS_F32) return ((const float*)p)[i];
-    else return bf2f(((const uint16_t*)p)[i]);
+    if constexpr (DT == GPUOS_F32) return __uint_as_float(ld4(p + 4 * i));
+    else return bf2f(ld2(p + 2 * i));
+}
+
+// Stores of op outputs are device-scope write-through (cache policy SC1): the
+// eight XCD L2s are not coherent, and a release fence on gfx950 has to write
+// back every dirty line of the issuing XCD's L2.  Writing results through
+// keeps that fence cheap and leaves nothing stale for readers on other XCDs.
+// Narrow stores are relaxed agent-scope atomic stores, which compile to the
+// same SC1 global stores.
+__device__ __forceinline__ void wst32(void* p, uint32_t v) {
+    __hip_atomic_store((g_u32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wst16b(void* p, uint16_t v) {
+    __hip_atomic_store((g_u16*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wst8(void* p, uint8_t v) {
+    __hip_atomic_store((g_u8*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wst64(void* p, uint64_t v) {
+    __hip_atomic_store((g_u64*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wstf(void* p, float v) { wst32(p, __float_as_uint(v)); }
+
+template <uint32_t DT>
+__device__ __forceinline__ void st_elem(uint8_t* p, uint64_t i, float v) {
+    if constexpr (DT == GPUOS_F32) wstf(p + 4 * i, v);
+    else wst16b(p + 2 * i, (uint16_t)f2bf(v));
+}
+
+// ------------------------------------------------------- buffer resources
+// A window of `nbytes` at `base` (raw buffer, stride 0).  Word 3 selects the
+// 32-bit data format that raw buffer instructions require on gfx9-family
+// parts.  Offsets are 32-bit: callers keep windows below 2 GiB.
+constexpr int CPOL_SC1 = 16;
+struct RBuf {
+    __amdgpu_buffer_rsrc_t r;
+};
+struct WBuf {
+    __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mkrsrc(const void* base, uint32_t nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
+}
+__device__ __forceinline__ RBuf rbuf(const void* base, uint32_t nbytes) { return RBuf{mkrsrc(base, nbytes)}; }
+__device__ __forceinline__ WBuf wbuf(const void* base, uint32_t nbytes = 0x7FFFFFFFu) {
+    return WBuf{mkrsrc(base, nbytes)};
+}
+__device__ __forceinline__ u32x4 rld16(RBuf b, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void wst16(WBuf b, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.r, (int)off, 0, CPOL_SC1);
+}
+
+// Two bf16 in one dword.  The argument is taken by value: a bit cast applied
+// directly to a vector component expression (v.y) reads component 0 with
+// this compiler.
+__device__ __forceinline__ bf16x2 as_bf2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// 16 bytes -> VE floats
+template <uint32_t DT>
+__device__ __forceinline__ void unpack(u32x4 v, float* f) {
+    if constexpr (DT == GPUOS_F32) {
+        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+    } else {
+        f[0] = bf2f(v.x & 0xFFFFu); f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+        f[2] = bf2f(v.y & 0xFFFFu); f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+        f[4] = bf2f(v.z & 0xFFFFu); f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+        f[6] = bf2f(v.w & 0xFFFFu); f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+    }
 }
 template <uint32_t DT>
-__device__ __forceinline__ void st_elem(uint8_t* p, uint64_t i, float v);
+__device__ __forceinline__ u32x4 pack(const float* f) {
+    u32x4 v;
+    if constexpr (DT == GPUOS_F32) {
+        v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
+        v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
+    } else {
+        v.x = f2bf(f[0]) | (f2bf(f[1]) << 16); v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
+        v.z = f2bf(f[4]) | (f2bf(f[5]) << 16); v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
+    }
+    return v;
+}
 
 __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : (x != x ? x : 0.0f); }
 
@@ -107,91 +217,44 @@ __device__ __forceinline__ float tmin(float a, float b) {
 }
 
 // ------------------------------------------------------------ wave helpers
-__device__ __forceinline__ float wsum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
+// DPP lane moves (gfx9 encodings): quad_perm [1,0,3,2] and [2,3,0,1] swap
+// neighbours and pairs; half-mirror reverses each 8 lanes, mirror each 16.
+// After xor1, xor2 every lane holds its quad's value; half-mirror then pairs
+// quad 0 with quad 1 of each 8, mirror pairs the two 8s of each 16.  Each
+// step combines a lane with a partner that holds the mirror-image partial,
+// so every lane of the group ends with the same, bit-identical result.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wmaxf(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+__device__ __forceinline__ float rlf(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
-__device__ __forceinline__ float wtmax(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = tmax(v, __shfl_xor(v, m, 64));
-    return v;
-}
-__device__ __forceinline__ float wtmin(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = tmin(v, __shfl_xor(v, m, 64));
-    return v;
-}
+struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpTMax { __device__ float operator()(float a, float b) const { return tmax(a, b); } };
+struct OpTMin { __device__ float operator()(float a, float b) const { return tmin(a, b); } };
 
-// Stores of op outputs are device-scope write-through (cache policy SC1): the
-// eight XCD L2s are not coherent, and a release fence on gfx950 has to write
-// back every dirty line of the issuing XCD's L2.  Writing results through
-// keeps that fence cheap and leaves nothing stale for readers on other XCDs.
-// 128-bit stores go through a raw buffer resource built on the unit's base
-// pointer (the per-lane offset stays below 2 GiB); narrower stores use
-// relaxed agent-scope atomic stores, which compile to the same SC1 stores.
-constexpr int CPOL_SC1 = 16;
-struct WBuf {
-    __amdgpu_buffer_rsrc_t r;
-};
-__device__ __forceinline__ WBuf wbuf(const void* base) {
-    return WBuf{__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000)};
-}
-__device__ __forceinline__ void wst16(WBuf b, uint32_t off, u32x4 v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, b.r, (int)off, 0, CPOL_SC1);
-}
-__device__ __forceinline__ void wst32(void* p, uint32_t v) {
-    __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wst16b(void* p, uint16_t v) {
-    __hip_atomic_store((uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wst8(void* p, uint8_t v) {
-    __hip_atomic_store((uint8_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wst64(void* p, uint64_t v) {
-    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wstf(void* p, float v) { wst32(p, __float_as_uint(v)); }
-
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(const u32x4*)p; }
-
-template <uint32_t DT>
-__device__ __forceinline__ void st_elem(uint8_t* p, uint64_t i, float v) {
-    if constexpr (DT == GPUOS_F32) wstf(p + 4 * i, v);
-    else wst16b(p + 2 * i, (uint16_t)f2bf(v));
-}
-
-// 16 bytes -> VE floats
-template <uint32_t DT>
-__device__ __forceinline__ void unpack(u32x4 v, float* f) {
-    if constexpr (DT == GPUOS_F32) {
-        f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
-        f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
-    } else {
-        f[0] = bf2f(v.x & 0xFFFFu); f[1] = bf2f(v.x >> 16);
-        f[2] = bf2f(v.y & 0xFFFFu); f[3] = bf2f(v.y >> 16);
-        f[4] = bf2f(v.z & 0xFFFFu); f[5] = bf2f(v.z >> 16);
-        f[6] = bf2f(v.w & 0xFFFFu); f[7] = bf2f(v.w >> 16);
-    }
-}
-template <uint32_t DT>
-__device__ __forceinline__ u32x4 pack(const float* f) {
-    u32x4 v;
-    if constexpr (DT == GPUOS_F32) {
-        v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
-        v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
-    } else {
-        v.x = f2bf(f[0]) | (f2bf(f[1]) << 16); v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
-        v.z = f2bf(f[4]) | (f2bf(f[5]) << 16); v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
-    }
+// combine over groups of G (8 or 16) consecutive lanes; all lanes active
+template <int G, class F>
+__device__ __forceinline__ float gred(float v, F f) {
+    v = f(v, dpp<DPP_XOR1>(v));
+    v = f(v, dpp<DPP_XOR2>(v));
+    v = f(v, dpp<DPP_HALF_MIRROR>(v));
+    if constexpr (G == 16) v = f(v, dpp<DPP_MIRROR>(v));
     return v;
 }
+// combine over the wave: 16-lane groups, then the four rows in a fixed order
+template <class F>
+__device__ __forceinline__ float wred(float v, F f) {
+    v = gred<16>(v, f);
+    return f(f(rlf(v, 0), rlf(v, 16)), f(rlf(v, 32), rlf(v, 48)));
+}
+__device__ __forceinline__ float wsum(float v) { return wred(v, OpAdd{}); }
+__device__ __forceinline__ float wmaxf(float v) { return wred(v, OpMax{}); }
+__device__ __forceinline__ float wtmax(float v) { return wred(v, OpTMax{}); }
+__device__ __forceinline__ float wtmin(float v) { return wred(v, OpTMin{}); }
 
 // ------------------------------------------------------------ element-wise
 template <uint32_t K>
@@ -202,9 +265,24 @@ __device__ __forceinline__ float ew_op(float x, float y) {
     else return gelu_f(x);
 }
 
-// One tile of ew_tile_bytes(K) per operand (8 chunks of 16 bytes per lane,
-// 2 for GELU), all loads issued before any compute.  The ragged tail (fewer than one
-// chunk) and misaligned operands take an element loop.
+// bf16 ReLU acts on the bit pattern (no rounding involved)
+__device__ __forceinline__ uint32_t relu_bf16(uint32_t h) {
+    if ((h & 0x7FFFu) > 0x7F80u) return h;  // NaN
+    return (h & 0x8000u) ? 0u : h;          // negatives and -0 -> +0
+}
+__device__ __forceinline__ u32x4 relu_bf16x8(u32x4 v) {
+    u32x4 o;
+    o.x = relu_bf16(v.x & 0xFFFFu) | (relu_bf16(v.x >> 16) << 16);
+    o.y = relu_bf16(v.y & 0xFFFFu) | (relu_bf16(v.y >> 16) << 16);
+    o.z = relu_bf16(v.z & 0xFFFFu) | (relu_bf16(v.z >> 16) << 16);
+    o.w = relu_bf16(v.w & 0xFFFFu) | (relu_bf16(v.w >> 16) << 16);
+    return o;
+}
+
+// One tile of ew_tile_bytes(K) per operand: CH chunks of 16 bytes per lane
+// (8 for add/mul/ReLU, 2 for GELU), all loads issued first.  The elements
+// after the last whole chunk (fewer than one chunk) are one per lane.
+// Misaligned operands take an element loop.
 template <uint32_t K, uint32_t DT>
 __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
@@ -212,97 +290,71 @@ __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t VE = 16u / ES;
     constexpr uint32_t CH = TILE / VE / 64u;
     constexpr bool BIN = (K == GPUOS_OP_ADD || K == GPUOS_OP_MUL);
+    constexpr bool RELU16 = (K == GPUOS_OP_RELU && DT == GPUOS_BF16);
     const uint64_t start = (uint64_t)u.tile * TILE;
     if (start >= u.size) return;
-    const uint64_t end = u.size - start < TILE ? u.size : start + TILE;
-    const uint8_t* A = (const uint8_t*)u.a;
-    const uint8_t* B = (const uint8_t*)u.b;
-    uint8_t* O = (uint8_t*)u.out;
+    const uint32_t cnt = (uint32_t)(u.size - start < TILE ? u.size - start : TILE);
+    const uint8_t* A = (const uint8_t*)u.a + start * ES;
+    const uint8_t* B = (const uint8_t*)u.b + start * ES;
+    uint8_t* O = (uint8_t*)u.out + start * ES;
     const bool aligned = (((u.a | u.out | (BIN ? u.b : 0ull)) & 15ull) == 0);
     if (aligned) {
-        const WBuf ob = wbuf(O + start * ES);
+        const uint32_t full = cnt / VE;  // whole 16-byte chunks
+        const RBuf ra = rbuf(A, full * 16u);
+        const RBuf rb = rbuf(BIN ? B : A, full * 16u);
+        const WBuf ob = wbuf(O, full * 16u);
         u32x4 va[CH], vb[CH];
 #pragma unroll
         for (uint32_t c = 0; c < CH; ++c) {
-            const uint64_t idx = start + (uint64_t)(lane + 64u * c) * VE;
-            if (idx + VE <= end) {
-                va[c] = ld16(A + idx * ES);
-                if constexpr (BIN) vb[c] = ld16(B + idx * ES);
-            }
+            va[c] = rld16(ra, (lane + 64u * c) * 16u);
+            if constexpr (BIN) vb[c] = rld16(rb, (lane + 64u * c) * 16u);
+        }
+        const uint32_t rem = full * VE;
+        const bool tl = rem + lane < cnt;
+        float xt = 0.0f, yt = 0.0f;
+        if (tl) {
+            xt = ld_elem<DT>(A, rem + lane);
+            if constexpr (BIN) yt = ld_elem<DT>(B, rem + lane);
         }
 #pragma unroll
         for (uint32_t c = 0; c < CH; ++c) {
-            const uint64_t idx = start + (uint64_t)(lane + 64u * c) * VE;
-            if (idx + VE <= end) {
-                float x[VE], y[VE], o[VE];
+            u32x4 o;
+            if constexpr (RELU16) {
+                o = relu_bf16x8(va[c]);
+            } else {
+                float x[VE], y[VE], r[VE];
                 unpack<DT>(va[c], x);
                 if constexpr (BIN) unpack<DT>(vb[c], y);
 #pragma unroll
-                for (uint32_t e = 0; e < VE; ++e) o[e] = ew_op<K>(x[e], BIN ? y[e] : 0.0f);
-                wst16(ob, (uint32_t)((idx - start) * ES), pack<DT>(o));
+                for (uint32_t e = 0; e < VE; ++e) r[e] = ew_op<K>(x[e], BIN ? y[e] : 0.0f);
+                o = pack<DT>(r);
             }
+            wst16(ob, (lane + 64u * c) * 16u, o);  // chunks past `full` are dropped
         }
-        const uint64_t rem = start + ((end - start) / VE) * VE;
-        if (rem + lane < end) {
-            const uint64_t i = rem + lane;
-            st_elem<DT>(O, i, ew_op<K>(ld_elem<DT>(A, i), BIN ? ld_elem<DT>(B, i) : 0.0f));
+        if (tl) {
+            if constexpr (RELU16) wst16b(O + 2u * (rem + lane), (uint16_t)relu_bf16(ld2(A + 2u * (rem + lane))));
+            else st_elem<DT>(O, rem + lane, ew_op<K>(xt, yt));
         }
     } else {
-        for (uint64_t i = start + lane; i < end; i += 64u)
-            st_elem<DT>(O, i, ew_op<K>(ld_elem<DT>(A, i), BIN ? ld_elem<DT>(B, i) : 0.0f));
-    }
-}
-
-// bf16 ReLU acts on the bit pattern (no rounding involved); fp32 uses relu_f.
-template <>
-__device__ __forceinline__ void ew_tile<GPUOS_OP_RELU, GPUOS_BF16>(const Unit& u, uint32_t lane) {
-    constexpr uint32_t TILE = EW_TILE_BYTES / 2u;
-    const uint64_t start = (uint64_t)u.tile * TILE;
-    if (start >= u.size) return;
-    const uint64_t end = u.size - start < TILE ? u.size : start + TILE;
-    const uint16_t* A = (const uint16_t*)u.a;
-    uint16_t* O = (uint16_t*)u.out;
-    auto r16 = [](uint32_t h) -> uint32_t {
-        if ((h & 0x7FFFu) > 0x7F80u) return h;  // NaN
-        return (h & 0x8000u) ? 0u : h;          // negatives and -0 -> +0
-    };
-    if (((u.a | u.out) & 15ull) == 0) {
-        const WBuf ob = wbuf(O + start);
-        u32x4 va[8];
-#pragma unroll
-        for (uint32_t c = 0; c < 8; ++c) {
-            const uint64_t idx = start + (uint64_t)(lane + 64u * c) * 8u;
-            if (idx + 8 <= end) va[c] = ld16((const uint8_t*)(A + idx));
+        for (uint32_t i = lane; i < cnt; i += 64u) {
+            if constexpr (RELU16) wst16b(O + 2u * i, (uint16_t)relu_bf16(ld2(A + 2u * i)));
+            else st_elem<DT>(O, i, ew_op<K>(ld_elem<DT>(A, i), BIN ? ld_elem<DT>(B, i) : 0.0f));
         }
-#pragma unroll
-        for (uint32_t c = 0; c < 8; ++c) {
-            const uint64_t idx = start + (uint64_t)(lane + 64u * c) * 8u;
-            if (idx + 8 <= end) {
-                u32x4 v = va[c], o;
-                o.x = r16(v.x & 0xFFFFu) | (r16(v.x >> 16) << 16);
-                o.y = r16(v.y & 0xFFFFu) | (r16(v.y >> 16) << 16);
-                o.z = r16(v.z & 0xFFFFu) | (r16(v.z >> 16) << 16);
-                o.w = r16(v.w & 0xFFFFu) | (r16(v.w >> 16) << 16);
-                wst16(ob, (uint32_t)((idx - start) * 2u), o);
-            }
-        }
-        const uint64_t rem = start + ((end - start) / 8u) * 8u;
-        if (rem + lane < end) wst16b(O + rem + lane, (uint16_t)r16(A[rem + lane]));
-    } else {
-        for (uint64_t i = start + lane; i < end; i += 64u) wst16b(O + i, (uint16_t)r16(A[i]));
     }
 }
 
 // ------------------------------------------------------------------ rows
 // One row of [rows, h] per unit.  Rows up to ROW_MAX_CACHED elements with
-// 16-byte alignment are held in registers (64 values per lane); others
-// stream from memory in several passes.
+// 16-byte alignment are held in registers (up to 16 chunks of 16 bytes per
+// lane, loaded in one batch together with LayerNorm's gamma and beta);
+// others stream from memory in several passes.
 template <uint32_t K, uint32_t DT>
 __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
     constexpr uint32_t VE = 16u / ES;
     constexpr uint32_t KMAX = ROW_MAX_CACHED / VE / 64u;
     constexpr bool RED = (K == GPUOS_OP_SUM || K == GPUOS_OP_MAX || K == GPUOS_OP_MIN);
+    constexpr bool LN = (K == GPUOS_OP_LAYERNORM);
     const uint64_t r = u.tile;
     if (r >= u.size) return;
     const uint32_t h = u.dim[0];
@@ -311,48 +363,59 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
     const uint8_t* G = (const uint8_t*)u.aux0;
     const uint8_t* Bt = (const uint8_t*)u.aux1;
     float eps = 1e-5f;
-    if constexpr (K == GPUOS_OP_LAYERNORM) eps = u.pf[0] != 0.0f ? u.pf[0] : (u.p0 != 0.0f ? u.p0 : 1e-5f);
+    if constexpr (LN) eps = u.pf[0] != 0.0f ? u.pf[0] : (u.p0 != 0.0f ? u.p0 : 1e-5f);
     const float inv_h = 1.0f / (float)h;
     uint64_t amask = (uint64_t)X | (RED ? 0ull : (uint64_t)O);
-    if constexpr (K == GPUOS_OP_LAYERNORM) amask |= u.aux0 | u.aux1;
+    if constexpr (LN) amask |= u.aux0 | u.aux1;
     const bool cached = h <= ROW_MAX_CACHED && (h % VE) == 0 && (amask & 15ull) == 0;
     if (cached) {
-        const WBuf ob = wbuf(O);
         const uint32_t nch = h / VE;
-        float v[KMAX][VE];
-        u32x4 raw[KMAX];
+        const uint32_t kn = (nch + 63u) / 64u;  // chunk rounds in use (wave-uniform)
+        const RBuf rx = rbuf(X, h * ES);
+        u32x4 raw[KMAX], rg[LN ? KMAX : 1], rbb[LN ? KMAX : 1];
 #pragma unroll
-        for (uint32_t k = 0; k < KMAX; ++k) {
-            const uint32_t c = lane + 64u * k;
-            if (c < nch) raw[k] = ld16(X + (uint64_t)c * 16u);
+        for (uint32_t k = 0; k < KMAX; ++k)
+            if (k < kn) raw[k] = rld16(rx, (lane + 64u * k) * 16u);
+        if constexpr (LN) {
+            const RBuf rgm = rbuf(G, h * ES), rbt = rbuf(Bt, h * ES);
+#pragma unroll
+            for (uint32_t k = 0; k < KMAX; ++k)
+                if (k < kn) {
+                    rg[k] = rld16(rgm, (lane + 64u * k) * 16u);
+                    rbb[k] = rld16(rbt, (lane + 64u * k) * 16u);
+                }
         }
-        float acc = RED && K != GPUOS_OP_SUM ? __uint_as_float(0x7FC00000u) : 0.0f;
-        bool first = true;
-        float mx = -INFINITY;
+        float v[KMAX][VE];
+        float acc = 0.0f, mx = -INFINITY;
+        bool has = false;
 #pragma unroll
         for (uint32_t k = 0; k < KMAX; ++k) {
-            const uint32_t c = lane + 64u * k;
-            if (c < nch) {
+            if (k < kn) {
+                const bool valid = lane + 64u * k < nch;  // chunks past the row read as zero
                 unpack<DT>(raw[k], v[k]);
 #pragma unroll
                 for (uint32_t e = 0; e < VE; ++e) {
                     const float x = v[k][e];
-                    if constexpr (K == GPUOS_OP_SUM || K == GPUOS_OP_LAYERNORM) acc += x;
-                    else if constexpr (K == GPUOS_OP_MAX) acc = first ? x : tmax(acc, x);
-                    else if constexpr (K == GPUOS_OP_MIN) acc = first ? x : tmin(acc, x);
-                    else mx = fmaxf(mx, x);
-                    first = false;
+                    if constexpr (K == GPUOS_OP_SUM || LN) {
+                        acc += x;
+                    } else if constexpr (K == GPUOS_OP_MAX || K == GPUOS_OP_MIN) {
+                        const float c = has ? (K == GPUOS_OP_MAX ? tmax(acc, x) : tmin(acc, x)) : x;
+                        acc = valid ? c : acc;
+                        has = has || valid;
+                    } else {
+                        mx = valid ? fmaxf(mx, x) : mx;
+                    }
                 }
             }
         }
+        const WBuf ob = wbuf(O, RED ? ES : h * ES);
         if constexpr (K == GPUOS_OP_SUM) {
             acc = wsum(acc);
             if (lane == 0) st_elem<DT>(O, 0, acc);
         } else if constexpr (K == GPUOS_OP_MAX || K == GPUOS_OP_MIN) {
-            // lanes that saw no element hold a placeholder: replace it by an
-            // element of the row so it never wins
-            const float ref = __shfl(acc, 0, 64);  // lane 0 always has an element (h >= VE)
-            if (first) acc = ref;
+            // lanes that saw no element take lane 0's value (lane 0 always has one)
+            const float ref = rlf(acc, 0);
+            acc = has ? acc : ref;
             acc = K == GPUOS_OP_MAX ? wtmax(acc) : wtmin(acc);
             if (lane == 0) st_elem<DT>(O, 0, acc);
         } else if constexpr (K == GPUOS_OP_SOFTMAX) {
@@ -360,46 +423,50 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
             float s = 0.0f;
 #pragma unroll
             for (uint32_t k = 0; k < KMAX; ++k) {
-                const uint32_t c = lane + 64u * k;
-                if (c < nch) {
+                if (k < kn) {
+                    const bool valid = lane + 64u * k < nch;
 #pragma unroll
-                    for (uint32_t e = 0; e < VE; ++e) { v[k][e] = expf(v[k][e] - mx); s += v[k][e]; }
+                    for (uint32_t e = 0; e < VE; ++e) {
+                        v[k][e] = valid ? expf(v[k][e] - mx) : 0.0f;
+                        s += v[k][e];
+                    }
                 }
             }
             s = wsum(s);
 #pragma unroll
             for (uint32_t k = 0; k < KMAX; ++k) {
-                const uint32_t c = lane + 64u * k;
-                if (c < nch) {
+                if (k < kn) {
                     float o[VE];
 #pragma unroll
                     for (uint32_t e = 0; e < VE; ++e) o[e] = v[k][e] / s;
-                    wst16(ob, c * 16u, pack<DT>(o));
+                    wst16(ob, (lane + 64u * k) * 16u, pack<DT>(o));
                 }
             }
-        } else {  // LAYERNORM
+        } else {  // LAYERNORM: two-pass variance from the registers
             const float mean = wsum(acc) * inv_h;
             float q = 0.0f;
 #pragma unroll
             for (uint32_t k = 0; k < KMAX; ++k) {
-                const uint32_t c = lane + 64u * k;
-                if (c < nch) {
+                if (k < kn) {
+                    const bool valid = lane + 64u * k < nch;
 #pragma unroll
-                    for (uint32_t e = 0; e < VE; ++e) { const float d = v[k][e] - mean; q += d * d; }
+                    for (uint32_t e = 0; e < VE; ++e) {
+                        const float d = v[k][e] - mean;
+                        q += valid ? d * d : 0.0f;
+                    }
                 }
             }
             const float var = wsum(q) * inv_h;
             const float rstd = 1.0f / sqrtf(var + eps);
 #pragma unroll
             for (uint32_t k = 0; k < KMAX; ++k) {
-                const uint32_t c = lane + 64u * k;
-                if (c < nch) {
+                if (k < kn) {
                     float g[VE], bb[VE], o[VE];
-                    unpack<DT>(ld16(G + (uint64_t)c * 16u), g);
-                    unpack<DT>(ld16(Bt + (uint64_t)c * 16u), bb);
+                    unpack<DT>(rg[k], g);
+                    unpack<DT>(rbb[k], bb);
 #pragma unroll
                     for (uint32_t e = 0; e < VE; ++e) o[e] = (v[k][e] - mean) * rstd * g[e] + bb[e];
-                    wst16(ob, c * 16u, pack<DT>(o));
+                    wst16(ob, (lane + 64u * k) * 16u, pack<DT>(o));
                 }
             }
         }
@@ -419,7 +486,7 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
         if constexpr (K == GPUOS_OP_SUM) {
             acc = wsum(acc);
         } else {
-            const float ref = __shfl(acc, 0, 64);  // lane 0 has element 0
+            const float ref = rlf(acc, 0);  // lane 0 has element 0
             if (!has) acc = ref;
             acc = K == GPUOS_OP_MAX ? wtmax(acc) : wtmin(acc);
         }
@@ -446,15 +513,86 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
 
 // ------------------------------------------------------------------ RoPE
 // Unit = one batch row b: every head of q and k, rotated at pos = L_b - 1.
-// The angle pos * theta^(-2i/D) and its sine and cosine are evaluated in
-// double, as is the rotation; the result is rounded once to the dtype.
+// The angle pos * theta^(-2i/D), its sine and cosine and the rotation are
+// evaluated in double and rounded once to the dtype, so the result is the
+// correctly rounded rotation up to the last-bit ties of double rounding.
+//
+// Fast path (adjacent pairs, row of D elements = CPR chunks of 16 bytes with
+// CPR dividing 64, 16-byte aligned operands): lane l always holds column
+// chunk l % CPR of some row, so its VE/2 angles are computed once; up to 16
+// rows per instruction group of each tensor are loaded before any store.
 template <uint32_t DT>
 __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
+    constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
+    constexpr uint32_t VE = 16u / ES;
+    constexpr uint32_t NI = 16;  // load instructions per tensor per group
     const uint32_t b = u.tile;
     const uint32_t H = u.dim[0], D = u.dim[1];
     const bool half = (u.flags & GPUOS_F_ROPE_HALF) != 0;
     const double theta = u.pf[4] != 0.0f ? (double)u.pf[4] : (u.p0 != 0.0f ? (double)u.p0 : 10000.0);
     const double pos = (double)((int)lens_at(u.lensw, b) - 1);
+    const uint32_t RB = D * ES;
+    const uint32_t CPR = RB / 16u;
+    const bool fast = !half && (RB % 16u) == 0 && CPR > 0 && CPR <= 64u && (64u % CPR) == 0 &&
+                      ((u.a | u.b) & 15ull) == 0;
+    if (fast) {
+        const uint32_t RPI = 64u / CPR;  // rows per load instruction
+        const uint32_t cc = lane % CPR, sub = lane / CPR;
+        double cs[VE / 2], sn[VE / 2];
+#pragma unroll
+        for (uint32_t j = 0; j < VE / 2; ++j) {
+            const uint32_t pi = cc * (VE / 2) + j;
+            const double fr = pow(theta, -2.0 * (double)pi / (double)D);
+            sincos(pos * fr, &sn[j], &cs[j]);
+        }
+        uint8_t* P0 = (uint8_t*)u.a + (uint64_t)b * H * RB;
+        uint8_t* P1 = (uint8_t*)u.b + (uint64_t)b * H * RB;
+        const WBuf w0 = wbuf(P0, H * RB), w1 = wbuf(P1, H * RB);
+        const RBuf r0 = rbuf(P0, H * RB), r1 = rbuf(P1, H * RB);
+        for (uint32_t h0 = 0; h0 < H; h0 += NI * RPI) {
+            u32x4 v0[NI], v1[NI];
+#pragma unroll
+            for (uint32_t i = 0; i < NI; ++i) {
+                const uint32_t off = ((h0 + i * RPI + sub) * CPR + cc) * 16u;  // rows past H read zero
+                v0[i] = rld16(r0, off);
+                v1[i] = rld16(r1, off);
+            }
+#pragma unroll
+            for (uint32_t t = 0; t < 2; ++t) {
+#pragma unroll
+                for (uint32_t i = 0; i < NI; ++i) {
+                    float x[VE];
+                    unpack<DT>(t == 0 ? v0[i] : v1[i], x);
+                    u32x4 o;
+                    if constexpr (DT == GPUOS_F32) {
+                        float y[VE];
+#pragma unroll
+                        for (uint32_t j = 0; j < VE / 2; ++j) {
+                            const double x0 = x[2 * j], x1 = x[2 * j + 1];
+                            y[2 * j] = (float)(x0 * cs[j] - x1 * sn[j]);
+                            y[2 * j + 1] = (float)(x0 * sn[j] + x1 * cs[j]);
+                        }
+                        o = pack<GPUOS_F32>(y);
+                    } else {
+                        uint32_t hb[VE];
+#pragma unroll
+                        for (uint32_t j = 0; j < VE / 2; ++j) {
+                            const double x0 = x[2 * j], x1 = x[2 * j + 1];
+                            hb[2 * j] = d2bf(x0 * cs[j] - x1 * sn[j]);
+                            hb[2 * j + 1] = d2bf(x0 * sn[j] + x1 * cs[j]);
+                        }
+                        o.x = hb[0] | (hb[1] << 16); o.y = hb[2] | (hb[3] << 16);
+                        o.z = hb[4] | (hb[5] << 16); o.w = hb[6] | (hb[7] << 16);
+                    }
+                    const uint32_t off = ((h0 + i * RPI + sub) * CPR + cc) * 16u;  // past H: dropped
+                    if (t == 0) wst16(w0, off, o);
+                    else wst16(w1, off, o);
+                }
+            }
+        }
+        return;
+    }
+    // general path: one pair per lane per step
     for (uint32_t pi = lane; pi < D / 2; pi += 64u) {
         const double fr = pow(theta, -2.0 * (double)pi / (double)D);
         double s, c;
@@ -482,47 +620,77 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
 
 // -------------------------------------------------------------- KV append
 // Unit = one batch row b: K[b, h, L_b-1, :] = k[b, h, :] and the same for V.
+// Fast path: rows a multiple of 16 bytes, aligned, and the strided window of
+// destination rows below 2 GiB; 8 chunks per lane of each tensor are loaded
+// before any store.
 __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
+    constexpr uint32_t NI = 8;
     const uint32_t b = u.tile;
     const uint32_t H = u.dim[0], D = u.dim[1], C = u.dim[2];
     const uint32_t ES = esz(dt_in(u.flags));
     const uint64_t pos = (uint64_t)lens_at(u.lensw, b) - 1;
     const uint64_t RB = (uint64_t)D * ES;
+    const uint64_t span = ((uint64_t)H - 1) * C * RB + RB;
+    const bool fast = (RB % 16u) == 0 && ((u.a | u.b | u.aux0 | u.aux1) & 15ull) == 0 && span < (1ull << 31) &&
+                      (uint64_t)H * RB < (1ull << 31);
+    if (fast) {
+        const uint32_t cpr = (uint32_t)(RB / 16u), total = cpr * H;
+        const uint8_t* s0 = (const uint8_t*)u.a + (uint64_t)b * H * RB;
+        const uint8_t* s1 = (const uint8_t*)u.b + (uint64_t)b * H * RB;
+        const uint64_t dbase = ((uint64_t)b * H * C + pos) * RB;
+        const RBuf r0 = rbuf(s0, total * 16u), r1 = rbuf(s1, total * 16u);
+        const WBuf w0 = wbuf((const uint8_t*)u.aux0 + dbase, (uint32_t)span);
+        const WBuf w1 = wbuf((const uint8_t*)u.aux1 + dbase, (uint32_t)span);
+        for (uint32_t j0 = 0; j0 < total; j0 += NI * 64u) {
+            u32x4 v0[NI], v1[NI];
+#pragma unroll
+            for (uint32_t i = 0; i < NI; ++i) {
+                const uint32_t j = j0 + i * 64u + lane;
+                v0[i] = rld16(r0, j * 16u);
+                v1[i] = rld16(r1, j * 16u);
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < NI; ++i) {
+                const uint32_t j = j0 + i * 64u + lane;
+                if (j < total) {
+                    const uint32_t hh = j / cpr, off = (uint32_t)((uint64_t)hh * C * RB) + (j % cpr) * 16u;
+                    wst16(w0, off, v0[i]);
+                    wst16(w1, off, v1[i]);
+                }
+            }
+        }
+        return;
+    }
     for (uint32_t t = 0; t < 2; ++t) {
         const uint8_t* src = (const uint8_t*)(t == 0 ? u.a : u.b) + (uint64_t)b * H * RB;
         uint8_t* dst = (uint8_t*)(t == 0 ? u.aux0 : u.aux1);
-        if (((uint64_t)src & 15ull) == 0 && ((uint64_t)dst & 15ull) == 0 && (RB & 15ull) == 0) {
-            const uint64_t cpr = RB / 16u, total = cpr * H;
-            for (uint64_t j = lane; j < total; j += 64u) {
-                const uint64_t hh = j / cpr, off = (j % cpr) * 16u;
-                const u32x4 v = ld16(src + hh * RB + off);
-                uint8_t* d = dst + (((uint64_t)b * H + hh) * C + pos) * RB + off;
-                wst64(d, (uint64_t)v.x | ((uint64_t)v.y << 32));
-                wst64(d + 8, (uint64_t)v.z | ((uint64_t)v.w << 32));
-            }
-        } else {
-            const uint64_t total = RB * H / 2u;  // 2-byte words (ES is 2 or 4)
-            for (uint64_t j = lane; j < total; j += 64u) {
-                const uint64_t byte = j * 2u, hh = byte / RB, off = byte % RB;
-                wst16b(dst + (((uint64_t)b * H + hh) * C + pos) * RB + off, *(const uint16_t*)(src + hh * RB + off));
-            }
+        const uint64_t total = RB * H / 2u;  // 2-byte words (ES is 2 or 4)
+        for (uint64_t j = lane; j < total; j += 64u) {
+            const uint64_t byte = j * 2u, hh = byte / RB, off = byte % RB;
+            wst16b(dst + (((uint64_t)b * H + hh) * C + pos) * RB + off, (uint16_t)ld2(src + hh * RB + off));
         }
     }
 }
 
 // ------------------------------------------------------------ decode SDPA
 // Unit = (b, h, split of SDPA_KT keys).  One key row of D bf16 is DV = D/8
-// lanes x 16 bytes, so one load instruction covers RPI = 64/DV keys.  Keys
-// are consumed in chunks of 8 instructions with a running max (online
-// softmax); each unit produces (max, sum of exp, unnormalised P.V) for its
-// keys, and when a head has several splits the last unit to finish merges
-// them (the split softmax of flash-decoding).  Dense MFMA does not apply:
-// one query per head makes q.K^T and P.V matrix-vector products with no reuse.
+// lanes x 16 bytes, so one load instruction covers RPI = 64/DV keys and the
+// wave reads keys in chunks of 8 instructions (8 RPI keys, 16 KiB of K and V
+// for D = 128).  The next chunk's loads are issued before the current chunk
+// is used, so two chunks are in flight.  Scores are bf16 dot products (exact
+// products, fp32 sums) reduced inside each DV-lane group with DPP, kept in
+// the log2 domain (scale * log2 e folded in), with a running max (online
+// softmax); each unit produces (max, sum of 2^(s - max), unnormalised P.V)
+// for its keys, and when a head has several splits the last unit to finish
+// merges them (the split softmax of flash-decoding).  Keys past L read as
+// zero through the bounded buffer window and get weight 0.  Dense MFMA does
+// not apply: one query per head makes q.K^T and P.V matrix-vector products
+// with no reuse.
 template <uint32_t DV, uint32_t DTO>
 __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t D = DV * 8u;
     constexpr uint32_t RPI = 64u / DV;
-    constexpr uint32_t NIT = SDPA_KT / RPI;
+    constexpr uint32_t CK = 8u * RPI;     // keys per chunk
     constexpr uint32_t PSTRIDE = D + 4u;  // floats per partial record: m, l, pad, pad, acc[D]
     const uint32_t H = u.dim[0], C = u.dim[2];
     const uint32_t Bn = (uint32_t)u.size;
@@ -540,64 +708,76 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     const uint32_t nk = min(L - k0, SDPA_KT);
     const uint64_t bh = (uint64_t)b * H + h;
     const float scale = u.pf[4] != 0.0f ? u.pf[4] : (u.p0 != 0.0f ? u.p0 : 1.0f / sqrtf((float)D));
+    const float sl2 = scale * 1.4426950408889634f;  // scores in the log2 domain
     const uint32_t g = lane / DV, c = lane % DV;
-    const uint8_t* Kp = (const uint8_t*)u.aux0 + (bh * C + k0) * D * 2u + c * 16u;
-    const uint8_t* Vp = (const uint8_t*)u.aux1 + (bh * C + k0) * D * 2u + c * 16u;
-    float q[8];
-    unpack<GPUOS_BF16>(ld16((const uint8_t*)u.a + bh * D * 2u + c * 16u), q);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] *= scale;
+    const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bh * C + k0) * D * 2u, nk * D * 2u);
+    const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bh * C + k0) * D * 2u, nk * D * 2u);
+    const u32x4 qr = ld16((const uint8_t*)u.a + bh * D * 2u + c * 16u);
+    const bf16x2 q0 = as_bf2(qr.x), q1 = as_bf2(qr.y), q2 = as_bf2(qr.z), q3 = as_bf2(qr.w);
     float m = -INFINITY, lsum = 0.0f;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (uint32_t i0 = 0; i0 < NIT && i0 * RPI < nk; i0 += 8) {
-        u32x4 kv[8], vv[8];
+    const uint32_t nch = (nk + CK - 1) / CK;
+    auto load = [&](u32x4* kv, u32x4* vv, uint32_t ci) {
 #pragma unroll
         for (uint32_t j = 0; j < 8; ++j) {
-            const uint32_t key = (i0 + j) * RPI + g;
-            if (key < nk) kv[j] = ld16(Kp + (uint64_t)key * D * 2u);
+            const uint32_t off = ((ci * CK + j * RPI + g) * D) * 2u + c * 16u;
+            kv[j] = rld16(rk, off);
+            vv[j] = rld16(rv, off);
         }
-#pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) {
-            const uint32_t key = (i0 + j) * RPI + g;
-            if (key < nk) vv[j] = ld16(Vp + (uint64_t)key * D * 2u);
-        }
+    };
+    auto consume = [&](const u32x4* kv, const u32x4* vv, uint32_t ci) {
         float s[8];
         float cm = -INFINITY;
 #pragma unroll
         for (uint32_t j = 0; j < 8; ++j) {
-            const uint32_t key = (i0 + j) * RPI + g;
-            float kf[8], d = 0.0f;
-            if (key < nk) {
-                unpack<GPUOS_BF16>(kv[j], kf);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) d += q[e] * kf[e];
-            }
-#pragma unroll
-            for (uint32_t mm = DV / 2; mm >= 1; mm >>= 1) d += __shfl_xor(d, mm, 64);
-            s[j] = key < nk ? d : -INFINITY;
+            float d = 0.0f;
+            d = __builtin_amdgcn_fdot2_f32_bf16(q0, as_bf2(kv[j].x), d, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(q1, as_bf2(kv[j].y), d, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(q2, as_bf2(kv[j].z), d, false);
+            d = __builtin_amdgcn_fdot2_f32_bf16(q3, as_bf2(kv[j].w), d, false);
+            d = gred<DV>(d, OpAdd{}) * sl2;
+            const bool valid = ci * CK + j * RPI + g < nk;
+            s[j] = valid ? d : -INFINITY;
             cm = fmaxf(cm, s[j]);
         }
+        // chunk max over the RPI key groups of the wave
+        if constexpr (DV == 16) {
+            cm = fmaxf(fmaxf(rlf(cm, 0), rlf(cm, 16)), fmaxf(rlf(cm, 32), rlf(cm, 48)));
+        } else {
 #pragma unroll
-        for (uint32_t mm = DV; mm < 64; mm <<= 1) cm = fmaxf(cm, __shfl_xor(cm, mm, 64));
-        const float mn = fmaxf(m, cm);          // finite: the chunk has at least one key
-        const float alpha = expf(m - mn);       // 0 on the first chunk (m = -inf)
+            for (uint32_t mm = DV; mm < 64; mm <<= 1) cm = fmaxf(cm, __shfl_xor(cm, mm, 64));
+        }
+        const float mn = fmaxf(m, cm);          // finite: every chunk has at least one key
+        const float alpha = exp2f(m - mn);      // 0 on the first chunk (m = -inf)
         lsum *= alpha;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] *= alpha;
 #pragma unroll
         for (uint32_t j = 0; j < 8; ++j) {
-            const uint32_t key = (i0 + j) * RPI + g;
-            if (key < nk) {
-                const float p = expf(s[j] - mn);
-                float vf[8];
-                unpack<GPUOS_BF16>(vv[j], vf);
-                lsum += p;
+            const float p = exp2f(s[j] - mn);   // 0 for keys past L
+            float vf[8];
+            unpack<GPUOS_BF16>(vv[j], vf);
+            lsum += p;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += p * vf[e];
-            }
+            for (int e = 0; e < 8; ++e) acc[e] += p * vf[e];
         }
         m = mn;
+    };
+    // The scheduling barriers keep the compiler from sinking the next chunk's
+    // loads below the use of the current one (it would to save registers).
+    u32x4 ka[8], va[8], kb[8], vb[8];
+    load(ka, va, 0);
+    for (uint32_t ci = 0; ci < nch; ci += 2) {
+        load(kb, vb, ci + 1);  // past the last chunk: outside the window, reads nothing
+        __builtin_amdgcn_sched_barrier(0);
+        consume(ka, va, ci);
+        if (ci + 1 < nch) {
+            load(ka, va, ci + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(kb, vb, ci + 1);
+        }
     }
+    // combine the RPI key groups (lanes with equal c)
 #pragma unroll
     for (uint32_t mm = DV; mm < 64; mm <<= 1) {
         lsum += __shfl_xor(lsum, mm, 64);
@@ -635,21 +815,21 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != ns - 1) return;
-    // merge: M = max m_i, Ls = sum l_i e^{m_i - M}, o = sum acc_i e^{m_i - M} / Ls
-    const float* p0 = (const float*)(u.scratch + COUNTER_AREA) + (uint64_t)(t - sp) * PSTRIDE;
-    float M = -INFINITY;
-    for (uint32_t i = 0; i < ns; ++i) M = fmaxf(M, p0[(uint64_t)i * PSTRIDE]);
-    float Ls = 0.0f;
+    // merge (log2 domain): M = max m_i, Ls = sum l_i 2^{m_i - M}, o = sum acc_i 2^{m_i - M} / Ls
+    const uint8_t* p0 = (const uint8_t*)((const float*)(u.scratch + COUNTER_AREA) + (uint64_t)(t - sp) * PSTRIDE);
     constexpr uint32_t DPL = D / 64u;  // dims per lane
+    float M = -INFINITY;
+    for (uint32_t i = 0; i < ns; ++i) M = fmaxf(M, __uint_as_float(ld4(p0 + (uint64_t)i * PSTRIDE * 4u)));
+    float Ls = 0.0f;
     float o[DPL];
 #pragma unroll
     for (uint32_t e = 0; e < DPL; ++e) o[e] = 0.0f;
     for (uint32_t i = 0; i < ns; ++i) {
-        const float* pi = p0 + (uint64_t)i * PSTRIDE;
-        const float w = expf(pi[0] - M);
-        Ls += pi[1] * w;
+        const uint8_t* pi = p0 + (uint64_t)i * PSTRIDE * 4u;
+        const float w = exp2f(__uint_as_float(ld4(pi)) - M);
+        Ls += __uint_as_float(ld4(pi + 4u)) * w;
 #pragma unroll
-        for (uint32_t e = 0; e < DPL; ++e) o[e] += pi[4 + lane * DPL + e] * w;
+        for (uint32_t e = 0; e < DPL; ++e) o[e] += __uint_as_float(ld4(pi + (4u + lane * DPL + e) * 4u)) * w;
     }
     const float inv = 1.0f / Ls;
 #pragma unroll
@@ -661,125 +841,164 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
 }
 
 // ------------------------------------------------------------------ GEMV
-// Unit = (column block of 64 lanes x 16 bytes, k-split of GEMV_KC rows of W).
-// x[k] for the split is loaded once (lane k) and broadcast with readlane.
-// With several k-splits each unit writes fp32 partial sums and the last unit
-// of a column block adds them in split order (a fixed order).
+// y[1,N] = x[1,K] W[K,N], W row-major.  Unit = (column block, k-split):
+// 16 lanes x 16 bytes cover CPB = 16 VE columns of one row, the four 16-lane
+// rows of the wave take four rows of W per load instruction, and a unit
+// walks GEMV_KC rows in batches of 64 (16 instructions, 16 KiB of bf16 W),
+// the next batch loaded before the current one is used.  x[k] comes from a
+// per-batch load of 64 values (one per lane) moved to the using lanes with a
+// lane permute.  The four row groups are summed at the end in a fixed
+// order; with several k-splits each unit writes fp32 partial sums and the
+// last unit of a column block adds them in split order.
 template <uint32_t DT, uint32_t DTO>
 __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
     constexpr uint32_t VE = 16u / ES;
-    constexpr uint32_t CPB = 64u * VE;
+    constexpr uint32_t CPB = 16u * VE;
+    constexpr uint32_t RB = 64u;  // rows per batch
     const uint32_t K = u.dim[0], N = u.dim[1];
     const uint32_t ncb = (N + CPB - 1) / CPB, nks = (K + GEMV_KC - 1) / GEMV_KC;
     const uint32_t cb = u.tile % ncb, ks = u.tile / ncb;
     const uint32_t kb = ks * GEMV_KC, kn = min(K - kb, GEMV_KC);
     const uint8_t* X = (const uint8_t*)u.a;
     const uint8_t* Wm = (const uint8_t*)u.b;
-    const float xv = lane < kn ? ld_elem<DT>(X, kb + lane) : 0.0f;
-    const uint32_t c0 = cb * CPB + lane * VE;
+    const uint32_t g = lane / 16u, cl = lane % 16u;
+    const uint32_t c0 = cb * CPB + cl * VE;  // first column of this lane
     float acc[VE];
 #pragma unroll
     for (uint32_t e = 0; e < VE; ++e) acc[e] = 0.0f;
-    const bool vec = (N % VE) == 0 && ((uint64_t)Wm & 15ull) == 0;
+    const uint64_t rowb = (uint64_t)N * ES;
+    const bool vec = (N % VE) == 0 && ((uint64_t)Wm & 15ull) == 0 && (uint64_t)kn * rowb < (1ull << 31);
     if (vec) {
-        const bool mine = c0 < N;
-        const uint8_t* wp = Wm + ((uint64_t)kb * N + c0) * ES;
-        uint32_t r = 0;
-        for (; r + 8 <= kn; r += 8) {
-            u32x4 w[8];
+        // window: rows kb .. kb+kn-1 of the column block; columns past N in the
+        // last block read neighbouring valid memory (never stored) or zero
+        const uint8_t* wbase = Wm + (uint64_t)kb * rowb + (uint64_t)cb * CPB * ES;
+        const uint32_t wlen = (uint32_t)((uint64_t)(kn - 1) * rowb + (uint64_t)(N - cb * CPB) * ES);
+        const RBuf rw = rbuf(wbase, wlen);
+        const RBuf rx = rbuf(X + (uint64_t)kb * ES, kn * ES);
+        const uint32_t nb = (kn + RB - 1) / RB;
+        auto loadw = [&](u32x4* w, uint32_t bi) {
 #pragma unroll
-            for (uint32_t j = 0; j < 8; ++j)
-                if (mine) w[j] = ld16(wp + (uint64_t)(r + j) * N * ES);
-#pragma unroll
-            for (uint32_t j = 0; j < 8; ++j) {
-                const float xr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(xv), r + j));
-                if (mine) {
-                    float wf[VE];
-                    unpack<DT>(w[j], wf);
-#pragma unroll
-                    for (uint32_t e = 0; e < VE; ++e) acc[e] += xr * wf[e];
-                }
+            for (uint32_t i = 0; i < 16; ++i) {
+                const uint32_t r = bi * RB + i * 4u + g;
+                // rows past kn fall outside the window (zero)
+                w[i] = rld16(rw, r < kn ? r * (uint32_t)rowb + cl * 16u : 0xFFFFFFF0u);
             }
-        }
-        for (; r < kn; ++r) {
-            const float xr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(xv), r));
-            if (mine) {
+        };
+        auto loadx = [&](uint32_t bi) -> float {
+            const uint32_t r = bi * RB + lane;
+            if constexpr (DT == GPUOS_F32) {
+                return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx.r, (int)(r * 4u), 0, 0));
+            } else {
+                return bf2f(__builtin_amdgcn_raw_buffer_load_b16(rx.r, (int)(r * 2u), 0, 0));
+            }
+        };
+        auto consume = [&](const u32x4* w, float xv) {
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) {
+                const float xr = __shfl(xv, (int)(i * 4u + g), 64);
                 float wf[VE];
-                unpack<DT>(ld16(wp + (uint64_t)r * N * ES), wf);
+                unpack<DT>(w[i], wf);
 #pragma unroll
                 for (uint32_t e = 0; e < VE; ++e) acc[e] += xr * wf[e];
             }
+        };
+        u32x4 wa[16], wb[16];
+        float xa = loadx(0), xb = 0.0f;
+        loadw(wa, 0);
+        for (uint32_t bi = 0; bi < nb; bi += 2) {
+            if (bi + 1 < nb) { xb = loadx(bi + 1); loadw(wb, bi + 1); }
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch above the use
+            consume(wa, xa);
+            if (bi + 1 < nb) {
+                if (bi + 2 < nb) { xa = loadx(bi + 2); loadw(wa, bi + 2); }
+                __builtin_amdgcn_sched_barrier(0);
+                consume(wb, xb);
+            }
+        }
+        // sum the four row groups (lanes cl, cl+16, cl+32, cl+48) in a fixed order
+#pragma unroll
+        for (uint32_t e = 0; e < VE; ++e) {
+            const float a1 = __shfl_xor(acc[e], 16, 64);
+            const float s01 = (g & 1u) ? a1 + acc[e] : acc[e] + a1;  // same value in both lanes
+            const float s23 = __shfl_xor(s01, 32, 64);
+            acc[e] = (g & 2u) ? s23 + s01 : s01 + s23;
         }
     } else {
-        // element path: lane handles columns cb*CPB + lane + 64 e
-        for (uint32_t r = 0; r < kn; ++r) {
-            const float xr = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(xv), r));
+        // element path: lane handles columns cb*CPB + cl + 16 e, rows kb + g + 4 i
+        for (uint32_t r = g; r < kn; r += 4u) {
+            const float xr = ld_elem<DT>(X, kb + r);
 #pragma unroll
             for (uint32_t e = 0; e < VE; ++e) {
-                const uint32_t col = cb * CPB + lane + 64u * e;
+                const uint32_t col = cb * CPB + cl + 16u * e;
                 if (col < N) acc[e] += xr * ld_elem<DT>(Wm, (uint64_t)(kb + r) * N + col);
             }
         }
-    }
-    // column of acc[e]
-    auto col_of = [&](uint32_t e) -> uint32_t { return vec ? c0 + e : cb * CPB + lane + 64u * e; };
-    uint8_t* Y = (uint8_t*)u.out;
-    if (nks == 1) {
 #pragma unroll
         for (uint32_t e = 0; e < VE; ++e) {
-            const uint32_t col = col_of(e);
-            if (col < N) st_elem<DTO>(Y, col, acc[e]);
+            const float a1 = __shfl_xor(acc[e], 16, 64);
+            const float s01 = (g & 1u) ? a1 + acc[e] : acc[e] + a1;
+            const float s23 = __shfl_xor(s01, 32, 64);
+            acc[e] = (g & 2u) ? s23 + s01 : s01 + s23;
+        }
+    }
+    // lanes of row group 0 hold the column sums
+    auto col_of = [&](uint32_t e) -> uint32_t { return vec ? c0 + e : cb * CPB + cl + 16u * e; };
+    uint8_t* Y = (uint8_t*)u.out;
+    if (nks == 1) {
+        if (g == 0) {
+#pragma unroll
+            for (uint32_t e = 0; e < VE; ++e) {
+                const uint32_t col = col_of(e);
+                if (col < N) st_elem<DTO>(Y, col, acc[e]);
+            }
         }
         return;
     }
     float* part = (float*)(u.scratch + COUNTER_AREA);
+    if (g == 0) {
 #pragma unroll
-    for (uint32_t e = 0; e < VE; ++e) {
-        const uint32_t col = col_of(e);
-        if (col < N) wstf(part + (uint64_t)ks * N + col, acc[e]);
+        for (uint32_t e = 0; e < VE; ++e) {
+            const uint32_t col = col_of(e);
+            if (col < N) wstf(part + (uint64_t)ks * N + col, acc[e]);
+        }
     }
     uint32_t* ctr = (uint32_t*)u.scratch + cb;
     uint32_t prev = 0;
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != nks - 1) return;
-#pragma unroll
-    for (uint32_t e = 0; e < VE; ++e) {
-        const uint32_t col = col_of(e);
-        if (col < N) {
-            float s = 0.0f;
-            for (uint32_t k = 0; k < nks; ++k) s += part[(uint64_t)k * N + col];
-            st_elem<DTO>(Y, col, s);
-        }
+    // merge: each of the 64 lanes sums CPB/64 columns over the splits in order
+    const uint8_t* pb = (const uint8_t*)part;
+    for (uint32_t col = cb * CPB + lane; col < min(N, (cb + 1u) * CPB); col += 64u) {
+        float s = 0.0f;
+        for (uint32_t k = 0; k < nks; ++k) s += __uint_as_float(ld4(pb + ((uint64_t)k * N + col) * 4u));
+        st_elem<DTO>(Y, col, s);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ COPY
+// COPY_TILE_BYTES per unit: 32 chunks of 16 bytes per lane, all loads first.
 __device__ __forceinline__ void copy_tile(const Unit& u, uint32_t lane) {
+    constexpr uint32_t NC = COPY_TILE_BYTES / 1024u;
     const uint64_t start = (uint64_t)u.tile * COPY_TILE_BYTES;
     if (start >= u.size) return;
-    const uint64_t end = u.size - start < COPY_TILE_BYTES ? u.size : start + COPY_TILE_BYTES;
-    const uint8_t* A = (const uint8_t*)u.a;
-    uint8_t* O = (uint8_t*)u.out;
+    const uint32_t cnt = (uint32_t)(u.size - start < COPY_TILE_BYTES ? u.size - start : COPY_TILE_BYTES);
+    const uint8_t* A = (const uint8_t*)u.a + start;
+    uint8_t* O = (uint8_t*)u.out + start;
     if (((u.a | u.out) & 15ull) == 0) {
-        const WBuf ob = wbuf(O + start);
-        u32x4 v[16];
+        const uint32_t full = cnt & ~15u;
+        const RBuf ra = rbuf(A, full);
+        const WBuf ob = wbuf(O, full);
+        u32x4 v[NC];
 #pragma unroll
-        for (uint32_t k = 0; k < 16; ++k) {
-            const uint64_t off = start + (uint64_t)(lane + 64u * k) * 16u;
-            if (off + 16 <= end) v[k] = ld16(A + off);
-        }
+        for (uint32_t k = 0; k < NC; ++k) v[k] = rld16(ra, (lane + 64u * k) * 16u);
 #pragma unroll
-        for (uint32_t k = 0; k < 16; ++k) {
-            const uint64_t off = start + (uint64_t)(lane + 64u * k) * 16u;
-            if (off + 16 <= end) wst16(ob, (uint32_t)(off - start), v[k]);
-        }
-        const uint64_t rem = start + ((end - start) / 16u) * 16u;
-        for (uint64_t i = rem + lane; i < end; i += 64u) wst8(O + i, A[i]);
+        for (uint32_t k = 0; k < NC; ++k) wst16(ob, (lane + 64u * k) * 16u, v[k]);
+        if (full + lane < cnt) wst8(O + full + lane, (uint8_t)ld1(A + full + lane));
     } else {
-        for (uint64_t i = start + lane; i < end; i += 64u) wst8(O + i, A[i]);
+        for (uint32_t i = lane; i < cnt; i += 64u) wst8(O + i, (uint8_t)ld1(A + i));
     }
 }
 
