@@ -71,14 +71,17 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         }
         if (stop) break;
         const uint64_t t_claim = A.trace ? wall_clock64() : 0;
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const uint64_t ent = A.queue[u & A.qmask];
+        // The entry, the mirror and the meta were made device-visible before
+        // the tail that was just seen; device-coherent loads issued after it
+        // read them without a cache invalidation.
+        asm volatile("" ::: "memory");
+        const uint64_t ent = ld_agent(&A.queue[u & A.qmask]);
         const uint64_t seq = ent >> 24;
         const uint32_t tile = (uint32_t)(ent & 0xFFFFFFu);
         const uint64_t slot = seq & A.mask;
         uint64_t w = 0;
-        if (lane < 16) w = ((const uint64_t*)&A.mirror[slot])[lane];
-        else if (lane < 24) w = ((const uint64_t*)&A.meta[slot])[lane - 16];
+        if (lane < 16) w = ld_agent(&((const uint64_t*)&A.mirror[slot])[lane]);
+        else if (lane < 24) w = ld_agent(&((const uint64_t*)&A.meta[slot])[lane - 16]);
         Unit U;
         const uint64_t w0 = rl64(w, 0), w6 = rl64(w, 6), w7 = rl64(w, 7);
         const uint64_t w11 = rl64(w, 11), w12 = rl64(w, 12);
@@ -144,30 +147,32 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
                 dbo = dbo * 2 < DEP_BACKOFF_MAX ? dbo * 2 : DEP_BACKOFF_MAX;
             }
             if (stop) break;
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            asm volatile("" ::: "memory");  // op loads are device-coherent: no invalidation
         }
         const uint64_t t_ready = A.trace ? wall_clock64() : 0;
         if (status == GPUOS_ST_OK && U.kind != KIND_BAD) run_unit(U, lane);
         ++n_units;
         const uint64_t t_body = A.trace ? wall_clock64() : 0;
-        // completion: the last unit of the descriptor releases the slot
+        // completion: publish this unit's (write-through) outputs, count it;
+        // the last unit of the descriptor marks it done and releases the
+        // slot.  Every unit's outputs were acknowledged before its count, so
+        // once done[] is visible all of them are.
+        stores_done();
         bool last = true;
         if (U.ntiles > 1) {
-            // release this unit's writes; only the last unit needs to acquire
-            // the others' before it signals the descriptor complete
             uint32_t prev = 0;
             if (lane == 0)
-                prev = __hip_atomic_fetch_add(&A.tiles_done[slot], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                prev = __hip_atomic_fetch_add(&A.tiles_done[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
             last = prev == U.ntiles - 1;
-            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
         if (last) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");  // system scope: outputs visible to all
             if (lane == 0) {
                 st_agent(&A.done[slot], seq);
-                if (status != GPUOS_ST_OK)
+                if (status != GPUOS_ST_OK) {
                     __hip_atomic_store(&A.status[slot], status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    stores_done();  // the status reaches the host before the stamp
+                }
                 st_sys(&A.stamp[slot], seq + N);
             }
         }
@@ -373,7 +378,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             }
             wst64(&A.queue[(u_next + wi) & A.qmask], ((f + lo) << 24) | (wi - pref[lo]));
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        stores_done();  // entries, mirror, meta and counters are written through
         if (lane == 0) st_agent(&C->q_tail, u_next + T);
         f += count;
         u_next += T;

@@ -13,6 +13,11 @@
 //    wait for all outstanding loads, and a guarded flat load is preceded by a
 //    full wait.  All loads and stores of op data name the global address
 //    space, or go through a buffer resource.
+//  - Loads and stores of op data are device-scope (cache policy SC1): loads
+//    are coherent across the eight XCDs, whose L2s are not, and stores are
+//    written through.  A unit therefore needs no cache invalidation before
+//    it reads what a unit on another XCD wrote, and no L2 write-back after
+//    it writes: waiting for its own stores (stores_done) publishes them.
 //  - A body issues all loads of a batch before it uses any of them, so one
 //    wave keeps 8-32 KiB in flight; stores come after.
 //  - Ragged ends use buffer resources bounded to the valid bytes: 16-byte
@@ -78,10 +83,17 @@ __device__ __forceinline__ uint32_t d2bf(double x) {
 }
 
 // ------------------------------------------------------------ global memory
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *(gc_u32x4*)p; }
-__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *(gc_u32*)p; }
-__device__ __forceinline__ uint32_t ld2(const uint8_t* p) { return *(gc_u16*)p; }
-__device__ __forceinline__ uint32_t ld1(const uint8_t* p) { return *(gc_u8*)p; }
+// Device-coherent scalar loads (relaxed agent-scope atomic loads compile to
+// SC1 global loads).
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) {
+    return __hip_atomic_load((g_u32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld2(const uint8_t* p) {
+    return __hip_atomic_load((g_u16*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld1(const uint8_t* p) {
+    return __hip_atomic_load((g_u8*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 template <uint32_t DT>
 __device__ __forceinline__ float ld_elem(const uint8_t* p, uint64_t i) {
@@ -115,6 +127,13 @@ __device__ __forceinline__ void st_elem(uint8_t* p, uint64_t i, float v) {
     else wst16b(p + 2 * i, (uint16_t)f2bf(v));
 }
 
+// Wait until every store this wave issued is acknowledged at device scope
+// (gfx9 counts stores in vmcnt).  With write-through stores this makes them
+// visible to every XCD, in place of a release fence, which on gfx950 would
+// also write back the whole L2 of the issuing XCD.  The memory clobber keeps
+// the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ------------------------------------------------------- buffer resources
 // A window of `nbytes` at `base` (raw buffer, stride 0).  Word 3 selects the
 // 32-bit data format that raw buffer instructions require on gfx9-family
@@ -134,7 +153,7 @@ __device__ __forceinline__ WBuf wbuf(const void* base, uint32_t nbytes = 0x7FFFF
     return WBuf{mkrsrc(base, nbytes)};
 }
 __device__ __forceinline__ u32x4 rld16(RBuf b, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)off, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)off, 0, CPOL_SC1);
 }
 __device__ __forceinline__ void wst16(WBuf b, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, b.r, (int)off, 0, CPOL_SC1);
@@ -712,7 +731,7 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     const uint32_t g = lane / DV, c = lane % DV;
     const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bh * C + k0) * D * 2u, nk * D * 2u);
     const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bh * C + k0) * D * 2u, nk * D * 2u);
-    const u32x4 qr = ld16((const uint8_t*)u.a + bh * D * 2u + c * 16u);
+    const u32x4 qr = rld16(rbuf((const uint8_t*)u.a + bh * D * 2u, D * 2u), c * 16u);
     const bf16x2 q0 = as_bf2(qr.x), q1 = as_bf2(qr.y), q2 = as_bf2(qr.z), q3 = as_bf2(qr.w);
     float m = -INFINITY, lsum = 0.0f;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -812,7 +831,8 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     if (lane == 0) { wstf(part, m); wstf(part + 1, lsum); }
     uint32_t* ctr = (uint32_t*)u.scratch + bh;
     uint32_t prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    stores_done();  // this unit's partial is published before it is counted
+    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != ns - 1) return;
     // merge (log2 domain): M = max m_i, Ls = sum l_i 2^{m_i - M}, o = sum acc_i 2^{m_i - M} / Ls
@@ -888,9 +908,9 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
         auto loadx = [&](uint32_t bi) -> float {
             const uint32_t r = bi * RB + lane;
             if constexpr (DT == GPUOS_F32) {
-                return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx.r, (int)(r * 4u), 0, 0));
+                return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx.r, (int)(r * 4u), 0, CPOL_SC1));
             } else {
-                return bf2f(__builtin_amdgcn_raw_buffer_load_b16(rx.r, (int)(r * 2u), 0, 0));
+                return bf2f(__builtin_amdgcn_raw_buffer_load_b16(rx.r, (int)(r * 2u), 0, CPOL_SC1));
             }
         };
         auto consume = [&](const u32x4* w, float xv) {
@@ -965,7 +985,8 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
     }
     uint32_t* ctr = (uint32_t*)u.scratch + cb;
     uint32_t prev = 0;
-    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    stores_done();  // this unit's partial is published before it is counted
+    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != nks - 1) return;
     // merge: each of the 64 lanes sums CPB/64 columns over the splits in order
