@@ -34,6 +34,7 @@ executor kernel and the CPU oracle timed on a bounded sample of the stream.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -45,6 +46,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+# sources of the executor kernel: recorded counter values hold only for these
+KERNEL_SOURCES = ["persistent_micro_dispatch_amd/csrc/gpuos_device.hip",
+                  "persistent_micro_dispatch_amd/csrc/gpuos_ops.h",
+                  "persistent_micro_dispatch_amd/csrc/gpuos_internal.h",
+                  "include/gpuos.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gpuos_executor_hbm_traffic.md")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per executor launch for `workload`, from the rocprofv3
+    FETCH_SIZE/WRITE_SIZE runs summarised under profiles/ (scaled by a copy
+    of known size), or None when none was taken or the kernel changed since."""
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    cur = kernel_source_hash()
+    for line in lines:
+        f = line.split()
+        if len(f) == 4 and f[0] == "traffic" and f[1] == workload and f[2] == cur:
+            return float(f[3])
+    return None
 
 
 def log(*a):
@@ -286,8 +317,11 @@ def main():
     # ---- roofline of the executor kernel (one launch = one step)
     mean_launch_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (mean_launch_ms * 1e-3) / 1e9
+    tb = recorded_traffic(args.workload)
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": tb / (mean_launch_ms * 1e-3) / 1e9 if tb else None,
+            "traffic_bytes_per_launch": tb,
             "kernel": "gpuos_executor", "launch_ms": mean_launch_ms, "bytes_per_launch": step_bytes}
 
     cpu = None
