@@ -143,7 +143,8 @@ static_assert(sizeof(gpuos_desc) == 128, "gpuos_desc must be 128 bytes");
 typedef struct gpuos_init_params {
     int32_t device;             /* HIP device ordinal */
     uint32_t ring_entries;      /* power of two in [8, 32768]; 0 -> 4096 */
-    uint32_t num_wgs;           /* executor workgroups; 0 -> one per CU */
+    uint32_t num_wgs;           /* executor workgroups, at most 4 per CU, and at least
+                                   2 waves in all (one fetches); 0 -> one per CU */
     uint32_t waves_per_wg;      /* wave64s per workgroup, 1..4; 0 -> 4 */
     uint32_t backoff_max;       /* s_sleep cap, 1..127; 0 -> 64 */
     uint32_t flags;             /* GPUOS_INIT_* */

@@ -476,6 +476,12 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     HIPCHK(hipGetDeviceProperties(&prop, P.device));
     c->cu_count = (uint32_t)prop.multiProcessorCount;
     if (c->P.num_wgs == 0) c->P.num_wgs = c->cu_count;
+    // one fetcher wave plus at least one worker; every workgroup must be able
+    // to be resident at once (at most four one-wave workgroups per CU)
+    if ((uint64_t)c->P.num_wgs * c->P.waves_per_wg < 2 || c->P.num_wgs > 4 * c->cu_count) {
+        free_ctx(c);
+        return GPUOS_E_INVAL;
+    }
     int wclk = 0;
     if (hipDeviceGetAttribute(&wclk, hipDeviceAttributeWallClockRate, P.device) != hipSuccess || wclk <= 0)
         wclk = 100000;  // kHz

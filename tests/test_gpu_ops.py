@@ -175,3 +175,19 @@ def test_copy_and_nop(ctx):
         recs.append(rec(W.OP_COPY, size=n, a=(base, sh), out=(base + 1, sh)))
     recs.append(rec(W.OP_NOP))
     _run_and_check(ctx, arrays, np.concatenate(recs))
+
+
+def test_large_descriptors(ctx):
+    """Descriptors of hundreds of units (completion counted in sub-counters)."""
+    say("large descriptors: copy 8 MiB + 37 B, add/mul 1M + 3 elements")
+    recs, arrays = [], []
+    n = (8 << 20) + 37
+    a = RNG.integers(0, 255, n + 8).astype(np.uint8)
+    arrays += [a, np.zeros(n + 8, np.uint8)]
+    recs.append(rec(W.OP_COPY, size=n, a=0, out=1))
+    for op, dt in [(W.OP_ADD, W.F32), (W.OP_MUL, W.BF16), (W.OP_GELU, W.F32)]:
+        m = (1 << 20) + 3
+        base = len(arrays)
+        arrays += [_vals(m, dt), _vals(m, dt), np.zeros_like(_vals(m, dt))]
+        recs.append(rec(op, dtype=dt, size=m, a=base, b=base + 1, out=base + 2))
+    _run_and_check(ctx, arrays, np.concatenate(recs))
