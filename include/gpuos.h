@@ -105,7 +105,8 @@ enum gpuos_kind {
  *                   [B, H, dim[2]=C, D]; writes row lens[b]-1.
  *   SDPA            a = q [B, H, D]; aux[0] = K, aux[1] = V [B, H, C, D];
  *                   output [B, H, D] in the output dtype; keys [0, lens[b]);
- *                   param.f[4] = scale (0 -> 1/sqrt(D)).  D must be 64 or 128.
+ *                   param.f[4] = scale (0 -> 1/sqrt(D)).  D must be 64 or 128;
+ *                   lens[b] at most 16384 (64 splits of 256 keys).
  *   GEMV            a = x [dim[0]=K], b = W [K, dim[1]=N] row-major, output [N].
  *   COPY            a -> output, `size` bytes.
  * Within one descriptor an output must coincide exactly with an input or

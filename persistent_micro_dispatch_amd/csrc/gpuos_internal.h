@@ -198,6 +198,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
                 const uint32_t L = lens_at(d.lensw, i);
                 if (L == 0 || L > C) return bad();
                 uint64_t ns = cdiv(L, SDPA_KT);
+                if (ns > 64) return bad();  // the split merge reads one split per lane
                 if (ns > 1) split = true;
                 units += ns * H;
             }

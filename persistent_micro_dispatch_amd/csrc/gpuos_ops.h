@@ -365,8 +365,9 @@ __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
 // ------------------------------------------------------------------ rows
 // One row of [rows, h] per unit.  Rows up to ROW_MAX_CACHED elements with
 // 16-byte alignment are held in registers (up to 16 chunks of 16 bytes per
-// lane, loaded in one batch together with LayerNorm's gamma and beta);
-// others stream from memory in several passes.
+// lane, loaded in one batch together with LayerNorm's gamma and beta for the
+// first LN_PRE chunks; the rest of gamma and beta is loaded after the
+// statistics); others stream from memory in several passes.
 template <uint32_t K, uint32_t DT>
 __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
@@ -374,6 +375,7 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t KMAX = ROW_MAX_CACHED / VE / 64u;
     constexpr bool RED = (K == GPUOS_OP_SUM || K == GPUOS_OP_MAX || K == GPUOS_OP_MIN);
     constexpr bool LN = (K == GPUOS_OP_LAYERNORM);
+    constexpr uint32_t LN_PRE = KMAX / 2;
     const uint64_t r = u.tile;
     if (r >= u.size) return;
     const uint32_t h = u.dim[0];
@@ -391,14 +393,14 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
         const uint32_t nch = h / VE;
         const uint32_t kn = (nch + 63u) / 64u;  // chunk rounds in use (wave-uniform)
         const RBuf rx = rbuf(X, h * ES);
-        u32x4 raw[KMAX], rg[LN ? KMAX : 1], rbb[LN ? KMAX : 1];
+        u32x4 raw[KMAX], rg[LN ? LN_PRE : 1], rbb[LN ? LN_PRE : 1];
 #pragma unroll
         for (uint32_t k = 0; k < KMAX; ++k)
             if (k < kn) raw[k] = rld16(rx, (lane + 64u * k) * 16u);
+        const RBuf rgm = rbuf(G, LN ? h * ES : 0u), rbt = rbuf(Bt, LN ? h * ES : 0u);
         if constexpr (LN) {
-            const RBuf rgm = rbuf(G, h * ES), rbt = rbuf(Bt, h * ES);
 #pragma unroll
-            for (uint32_t k = 0; k < KMAX; ++k)
+            for (uint32_t k = 0; k < LN_PRE; ++k)
                 if (k < kn) {
                     rg[k] = rld16(rgm, (lane + 64u * k) * 16u);
                     rbb[k] = rld16(rbt, (lane + 64u * k) * 16u);
@@ -477,12 +479,19 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
             }
             const float var = wsum(q) * inv_h;
             const float rstd = 1.0f / sqrtf(var + eps);
+            u32x4 lg[KMAX - LN_PRE], lb[KMAX - LN_PRE];
+#pragma unroll
+            for (uint32_t k = LN_PRE; k < KMAX; ++k)
+                if (k < kn) {
+                    lg[k - LN_PRE] = rld16(rgm, (lane + 64u * k) * 16u);
+                    lb[k - LN_PRE] = rld16(rbt, (lane + 64u * k) * 16u);
+                }
 #pragma unroll
             for (uint32_t k = 0; k < KMAX; ++k) {
                 if (k < kn) {
                     float g[VE], bb[VE], o[VE];
-                    unpack<DT>(rg[k], g);
-                    unpack<DT>(rbb[k], bb);
+                    unpack<DT>(k < LN_PRE ? rg[k < LN_PRE ? k : 0] : lg[k < LN_PRE ? 0 : k - LN_PRE], g);
+                    unpack<DT>(k < LN_PRE ? rbb[k < LN_PRE ? k : 0] : lb[k < LN_PRE ? 0 : k - LN_PRE], bb);
 #pragma unroll
                     for (uint32_t e = 0; e < VE; ++e) o[e] = (v[k][e] - mean) * rstd * g[e] + bb[e];
                     wst16(ob, (lane + 64u * k) * 16u, pack<DT>(o));
@@ -544,7 +553,7 @@ template <uint32_t DT>
 __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
     constexpr uint32_t VE = 16u / ES;
-    constexpr uint32_t NI = 16;  // load instructions per tensor per group
+    constexpr uint32_t NI = 8;  // load instructions per tensor per group
     const uint32_t b = u.tile;
     const uint32_t H = u.dim[0], D = u.dim[1];
     const bool half = (u.flags & GPUOS_F_ROPE_HALF) != 0;
@@ -569,17 +578,21 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
         const WBuf w0 = wbuf(P0, H * RB), w1 = wbuf(P1, H * RB);
         const RBuf r0 = rbuf(P0, H * RB), r1 = rbuf(P1, H * RB);
         for (uint32_t h0 = 0; h0 < H; h0 += NI * RPI) {
+            const uint32_t ni = min(NI, (H - h0 + RPI - 1) / RPI);  // instructions in use (uniform)
             u32x4 v0[NI], v1[NI];
 #pragma unroll
             for (uint32_t i = 0; i < NI; ++i) {
-                const uint32_t off = ((h0 + i * RPI + sub) * CPR + cc) * 16u;  // rows past H read zero
-                v0[i] = rld16(r0, off);
-                v1[i] = rld16(r1, off);
+                if (i < ni) {
+                    const uint32_t off = ((h0 + i * RPI + sub) * CPR + cc) * 16u;  // rows past H read zero
+                    v0[i] = rld16(r0, off);
+                    v1[i] = rld16(r1, off);
+                }
             }
 #pragma unroll
             for (uint32_t t = 0; t < 2; ++t) {
 #pragma unroll
                 for (uint32_t i = 0; i < NI; ++i) {
+                    if (i >= ni) continue;
                     float x[VE];
                     unpack<DT>(t == 0 ? v0[i] : v1[i], x);
                     u32x4 o;
@@ -835,21 +848,42 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != ns - 1) return;
-    // merge (log2 domain): M = max m_i, Ls = sum l_i 2^{m_i - M}, o = sum acc_i 2^{m_i - M} / Ls
+    // merge (log2 domain): M = max m_i, Ls = sum l_i 2^{m_i - M}, o = sum acc_i 2^{m_i - M} / Ls.
+    // Lane i < ns reads split i's (m, l); every lane then reads its DPL dims
+    // of all splits in one batch and adds them in split order.
     const uint8_t* p0 = (const uint8_t*)((const float*)(u.scratch + COUNTER_AREA) + (uint64_t)(t - sp) * PSTRIDE);
     constexpr uint32_t DPL = D / 64u;  // dims per lane
-    float M = -INFINITY;
-    for (uint32_t i = 0; i < ns; ++i) M = fmaxf(M, __uint_as_float(ld4(p0 + (uint64_t)i * PSTRIDE * 4u)));
+    constexpr uint32_t MAXS = 8;       // splits per batch of loads
+    float mi = -INFINITY, li = 0.0f;
+    if (lane < ns) {
+        mi = __uint_as_float(ld4(p0 + (uint64_t)lane * PSTRIDE * 4u));
+        li = __uint_as_float(ld4(p0 + (uint64_t)lane * PSTRIDE * 4u + 4u));
+    }
+    const float M = wmaxf(mi);
+    const float wi = lane < ns ? exp2f(mi - M) : 0.0f;
     float Ls = 0.0f;
     float o[DPL];
 #pragma unroll
     for (uint32_t e = 0; e < DPL; ++e) o[e] = 0.0f;
-    for (uint32_t i = 0; i < ns; ++i) {
-        const uint8_t* pi = p0 + (uint64_t)i * PSTRIDE * 4u;
-        const float w = exp2f(__uint_as_float(ld4(pi)) - M);
-        Ls += __uint_as_float(ld4(pi + 4u)) * w;
+    for (uint32_t i0 = 0; i0 < ns; i0 += MAXS) {
+        float av[MAXS][DPL];
 #pragma unroll
-        for (uint32_t e = 0; e < DPL; ++e) o[e] += __uint_as_float(ld4(pi + (4u + lane * DPL + e) * 4u)) * w;
+        for (uint32_t k = 0; k < MAXS; ++k) {
+            if (i0 + k < ns) {
+#pragma unroll
+                for (uint32_t e = 0; e < DPL; ++e)
+                    av[k][e] = __uint_as_float(ld4(p0 + ((uint64_t)(i0 + k) * PSTRIDE + 4u + lane * DPL + e) * 4u));
+            }
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < MAXS; ++k) {
+            if (i0 + k < ns) {
+                const float w = rlf(wi, (int)(i0 + k));
+                Ls += rlf(li, (int)(i0 + k)) * w;
+#pragma unroll
+                for (uint32_t e = 0; e < DPL; ++e) o[e] += av[k][e] * w;
+            }
+        }
     }
     const float inv = 1.0f / Ls;
 #pragma unroll
@@ -989,11 +1023,21 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != nks - 1) return;
-    // merge: each of the 64 lanes sums CPB/64 columns over the splits in order
+    // merge: each of the 64 lanes sums CPB/64 columns over the splits in
+    // split order, loading up to 8 splits at a time
     const uint8_t* pb = (const uint8_t*)part;
+    constexpr uint32_t MAXS = 8;
     for (uint32_t col = cb * CPB + lane; col < min(N, (cb + 1u) * CPB); col += 64u) {
         float s = 0.0f;
-        for (uint32_t k = 0; k < nks; ++k) s += __uint_as_float(ld4(pb + ((uint64_t)k * N + col) * 4u));
+        for (uint32_t k0 = 0; k0 < nks; k0 += MAXS) {
+            float pv[MAXS];
+#pragma unroll
+            for (uint32_t k = 0; k < MAXS; ++k)
+                if (k0 + k < nks) pv[k] = __uint_as_float(ld4(pb + ((uint64_t)(k0 + k) * N + col) * 4u));
+#pragma unroll
+            for (uint32_t k = 0; k < MAXS; ++k)
+                if (k0 + k < nks) s += pv[k];
+        }
         st_elem<DTO>(Y, col, s);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
