@@ -130,6 +130,8 @@ def main():
     ap.add_argument("--workload", default="elementwise")
     ap.add_argument("--waves", type=int, default=1, help="wave64s per workgroup (one workgroup per CU)")
     ap.add_argument("--ring", type=int, default=1024, help="ring entries")
+    ap.add_argument("--num-wgs", type=int, default=0,
+                    help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
     ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop (mixed workload)")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -162,7 +164,7 @@ def main():
     chain_buf = torch.zeros(256, dtype=torch.float32, device="cuda")
     one_buf = torch.ones(256, dtype=torch.float32, device="cuda")
     torch.cuda.current_stream().synchronize()
-    ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring)
+    ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring, num_wgs=args.num_wgs)
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     st0 = G.gpuos_stats_get(ctx)
 
@@ -225,6 +227,7 @@ def main():
         extra.update({
             "gemm_tflops_alone": flop / (gemm_alone_ms * 1e-3) / 1e12,
             "gemm_tflops_corun": flop / (gemm_co_ms * 1e-3) / 1e12,
+            "gemm_retained": gemm_alone_ms / gemm_co_ms,
             "corun_steps": k_co,
             "ops_per_s_with_gemm": nd * k_co / (tc1 - tc0) if k_co else None,
         })
