@@ -24,6 +24,10 @@
 //  - An interval keeps up to MAXR readers; beyond that it keeps the oldest
 //    overflowed reader, and a writer then depends on the whole range from it
 //    (reported through `range_from`).
+//  - A cluster that holds more than SPLIT_AT live intervals (a long-lived
+//    buffer written piece by piece, such as an output arena) is split in two
+//    at an interval boundary, so that inserting an interval never moves more
+//    than a few dozen of them.
 // Sequence numbers below the host's completion watermark are known complete
 // and are never returned.
 #pragma once
@@ -44,6 +48,7 @@ struct Access {
 class HazardTracker {
 public:
     static constexpr int MAXR = 14;
+    static constexpr size_t SPLIT_AT = 96;
 
     // Appends to `deps` every live seq (>= floor) that `seq` must wait for
     // and lowers *range_from to the first seq of a range that must be waited
@@ -73,18 +78,21 @@ public:
                 else record_read(*cp[i], acc[i].lo, acc[i].hi, seq, floor);
                 if (cp[i]->regs.size() > cp[i]->prune_at) prune(*cp[i], floor);
             }
-            return;
-        }
-        for (int i = 0; i < n; ++i)
-            if (cp[i]) collect(*cp[i], acc[i], floor, deps, range_from);
-        for (int pass = 0; pass < 2; ++pass) {
-            for (int i = 0; i < n; ++i) {
-                if (!cp[i] || acc[i].write != (pass == 1)) continue;
-                if (acc[i].write) record_write(*cp[i], acc[i].lo, acc[i].hi, seq);
-                else record_read(*cp[i], acc[i].lo, acc[i].hi, seq, floor);
-                if (cp[i]->regs.size() > cp[i]->prune_at) prune(*cp[i], floor);
+        } else {
+            for (int i = 0; i < n; ++i)
+                if (cp[i]) collect(*cp[i], acc[i], floor, deps, range_from);
+            for (int pass = 0; pass < 2; ++pass) {
+                for (int i = 0; i < n; ++i) {
+                    if (!cp[i] || acc[i].write != (pass == 1)) continue;
+                    if (acc[i].write) record_write(*cp[i], acc[i].lo, acc[i].hi, seq);
+                    else record_read(*cp[i], acc[i].lo, acc[i].hi, seq, floor);
+                    if (cp[i]->regs.size() > cp[i]->prune_at) prune(*cp[i], floor);
+                }
             }
         }
+        // split large clusters only now: the pointers in cp stay valid above
+        for (int i = 0; i < n; ++i)
+            if (cp[i] && cp[i]->regs.size() > SPLIT_AT) split(*cp[i], floor);
     }
 
     void clear() { cl_.clear(); }
@@ -104,7 +112,7 @@ private:
         uint64_t readers[MAXR];
     };
     struct Cluster {
-        uint64_t hi;
+        uint64_t lo, hi;  // lo is also the map key
         std::vector<Region> regs;  // sorted by lo, disjoint, inside [key, hi)
         size_t prune_at = 64;
     };
@@ -139,6 +147,7 @@ private:
             nhi = std::max(nhi, j->second.hi);
         }
         Cluster merged;
+        merged.lo = nlo;
         merged.hi = nhi;
         auto j = first;
         for (size_t q = 0; q < k; ++q) {
@@ -242,6 +251,24 @@ private:
             cur = v[i].hi;
             ++i;
         }
+    }
+
+    // Prune, and if the cluster is still large move its upper half into a
+    // cluster of its own (map nodes do not move, so other Cluster pointers
+    // stay valid).
+    void split(Cluster& c, uint64_t floor) {
+        prune(c, floor);
+        if (c.regs.size() <= SPLIT_AT) return;
+        const size_t mid = c.regs.size() / 2;
+        Cluster up;
+        up.lo = c.regs[mid].lo;
+        up.hi = c.hi;
+        up.regs.assign(c.regs.begin() + (long)mid, c.regs.end());
+        up.prune_at = std::max<size_t>(64, 2 * up.regs.size());
+        c.regs.resize(mid);
+        c.hi = up.lo;
+        c.prune_at = std::max<size_t>(64, 2 * c.regs.size());
+        cl_.emplace(up.lo, std::move(up));
     }
 
     // drop intervals that carry no live information

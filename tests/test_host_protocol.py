@@ -131,6 +131,31 @@ def test_loopback_respects_hazards_elementwise_partial_overlaps():
     assert _check_order(r, order, first) == 0
 
 
+def test_loopback_respects_hazards_in_a_large_arena():
+    """Thousands of small reads and writes scattered over one buffer: the
+    tracker splits the buffer's interval list into several clusters and an
+    access may straddle two; the order must still respect every conflict."""
+    rng = np.random.default_rng(11)
+    n = 3000
+    r = np.zeros(n, W.REC_DTYPE)
+    r["buf"] = -1
+    r["dtype"] = r["out_dtype"] = W.F32
+    r["op"] = np.where(rng.random(n) < 0.5, W.OP_ADD, W.OP_RELU)
+    r["size"] = rng.integers(64, 1024, n)
+    cap = 1 << 20
+    for role in (W.A, W.B, W.OUT):
+        r["buf"][:, role] = 0
+        r["off"][:, role] = rng.integers(0, (cap - 1024) // 4, n) * 16
+    descs = to_descs(r, _fake_ptrs(1))
+    ctx = _loopback()
+    try:
+        first = _run(ctx, descs, np.full(n // 50, 50))
+        order = G.gpuos_loopback_order(ctx)
+    finally:
+        G.gpuos_shutdown(ctx)
+    assert _check_order(r, order, first) == 0
+
+
 def test_serial_flag_gives_submission_order():
     s = W.make_elementwise(n_desc=500)
     descs = to_descs(s.recs, _fake_ptrs(len(s.buffers)))
@@ -216,6 +241,10 @@ def test_invalid_shapes_rejected_before_submission():
         assert G.gpuos_submit(ctx, d, 0)[0] == 0
         G.set_lens(d, [5000, 5])        # L > C
         assert G.gpuos_submit(ctx, d, 0)[0] == G.GPUOS_E_INVAL
+        d["dim"] = (32, 128, 20000, 0)
+        G.set_lens(d, [16385, 5])       # more than 64 splits of 256 keys
+        assert G.gpuos_submit(ctx, d, 0)[0] == G.GPUOS_E_INVAL
+        d["dim"] = (32, 128, 4096, 0)
         assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 5_000_000_000)[0] == 0
         assert G.gpuos_stats_get(ctx)["submitted"] == 1
     finally:
