@@ -129,7 +129,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="elementwise")
     ap.add_argument("--waves", type=int, default=1, help="wave64s per workgroup (one workgroup per CU)")
-    ap.add_argument("--ring", type=int, default=1024, help="ring entries")
+    ap.add_argument("--ring", type=int, default=256,
+                    help="ring entries: descriptors in flight, which is also the window of hazard tracking")
     ap.add_argument("--num-wgs", type=int, default=0,
                     help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
     ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop (mixed workload)")

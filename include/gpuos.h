@@ -192,8 +192,9 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
 
 /* Producer loop in native code: submit descs[0..sum(bursts)) as n_bursts
  * consecutive gpuos_submit calls of burst_sizes[i] descriptors each (each
- * burst is committed as a group).  Stops at the first error and returns it;
- * *n_done (may be NULL) receives the number of descriptors submitted. */
+ * burst is committed as a group; a burst larger than the ring is committed
+ * in ring-sized groups).  Stops at the first error and returns it; *n_done
+ * (may be NULL) receives the number of descriptors submitted. */
 int gpuos_submit_bursts(void* ctx, const gpuos_desc* descs, const uint32_t* burst_sizes, uint32_t n_bursts,
                         uint32_t flags, uint64_t* first_seq, uint64_t* n_done);
 

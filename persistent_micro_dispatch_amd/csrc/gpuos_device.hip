@@ -50,145 +50,228 @@ constexpr uint32_t DEP_BACKOFF_MAX = 16;
 constexpr uint64_t NO_SCRATCH = ~0ull;
 
 // ------------------------------------------------------------------ worker
+// A worker wave holds up to SLOTS claimed units and runs whichever of them
+// has its dependencies satisfied (the oldest such), so a unit waiting on a
+// long chain does not hold back a ready unit claimed after it.  Claims stay
+// in queue order, so the executor always progresses: if the oldest
+// unfinished unit is unclaimed, every claimed unit is older, hence finished,
+// and a wave with a free slot claims it; if it is claimed, its holder finds
+// it ready.  No wave waits on one unit alone.
+constexpr uint32_t SLOTS = 1;
+constexpr uint32_t SL_FREE = 0, SL_CLAIMED = 1, SL_WAIT = 2;
+
+template <class T>
+__device__ __forceinline__ T pick(const T* v, uint32_t r) {
+    T x = v[0];
+#pragma unroll
+    for (uint32_t k = 1; k < SLOTS; ++k) x = r == k ? v[k] : x;
+    return x;
+}
+
 __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
     DevCtl* C = A.dctl;
     uint64_t n_units = 0, n_depw = 0;
     const uint64_t N = (uint64_t)A.mask + 1;
+    uint32_t state[SLOTS];
+    uint64_t su[SLOTS], sseq[SLOTS], srlo[SLOTS], st0[SLOTS], tclaim[SLOTS];
+    uint64_t sw[SLOTS];   // per lane: mirror words in lanes 0..15, meta words in 16..23
+    uint32_t sdl[SLOTS];  // per lane: dependency delta (lanes 0..13), 0 = none
+    uint32_t stile[SLOTS];
+    bool sdeps[SLOTS], swaited[SLOTS];
+#pragma unroll
+    for (uint32_t k = 0; k < SLOTS; ++k) {
+        state[k] = SL_FREE;
+        su[k] = sseq[k] = srlo[k] = st0[k] = tclaim[k] = 0;
+        sw[k] = 0;
+        sdl[k] = 0;
+        stile[k] = 0;
+        sdeps[k] = swaited[k] = false;
+    }
+    bool stop_seen = false;
+    uint32_t bo = 1;
     for (;;) {
-        uint64_t u = 0;
-        if (lane == 0) u = __hip_atomic_fetch_add(&C->q_head, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        u = rl64(u, 0);
-        // wait until unit u is published
-        bool stop = false;
-        uint32_t bo = 1, polls = 0;
-        for (;;) {
-            const uint64_t tail = ld_agent(&C->q_tail);
-            if (tail > u) break;
-            if ((++polls & 3u) == 0 && ld_agent(&C->stop)) { stop = true; break; }
-            const uint64_t dist = u - tail;
-            bo = dist > 512 ? A.backoff_max : (bo * 2 < A.backoff_max ? bo * 2 : A.backoff_max);
-            nap(bo);
+        // One dependency load per waiting slot and the queue tail, issued
+        // together.  Claims come after the run below, so their atomic round
+        // trip never delays a ready unit.
+        uint64_t dv[SLOTS];
+#pragma unroll
+        for (uint32_t k = 0; k < SLOTS; ++k) {
+            const bool need = state[k] == SL_WAIT && sdl[k] != 0;
+            const uint64_t d = need ? sseq[k] - sdl[k] : 0;
+            dv[k] = ld_agent(&A.done[d & A.mask]);
         }
-        if (stop) break;
-        const uint64_t t_claim = A.trace ? wall_clock64() : 0;
-        // The entry, the mirror and the meta were made device-visible before
-        // the tail that was just seen; device-coherent loads issued after it
-        // read them without a cache invalidation.
-        asm volatile("" ::: "memory");
-        const uint64_t ent = ld_agent(&A.queue[u & A.qmask]);
-        const uint64_t seq = ent >> 24;
-        const uint32_t tile = (uint32_t)(ent & 0xFFFFFFu);
-        const uint64_t slot = seq & A.mask;
-        uint64_t w = 0;
-        if (lane < 16) w = ld_agent(&((const uint64_t*)&A.mirror[slot])[lane]);
-        else if (lane < 24) w = ld_agent(&((const uint64_t*)&A.meta[slot])[lane - 16]);
-        Unit U;
-        const uint64_t w0 = rl64(w, 0), w6 = rl64(w, 6), w7 = rl64(w, 7);
-        const uint64_t w11 = rl64(w, 11), w12 = rl64(w, 12);
-        const uint64_t w13 = rl64(w, 13), w14 = rl64(w, 14), w15 = rl64(w, 15);
-        const uint64_t m0 = rl64(w, 16), m1 = rl64(w, 17), m3 = rl64(w, 19);
-        const uint64_t x0 = rl64(w, 21), x1 = rl64(w, 22);
-        U.seq = seq;
-        U.flags = (uint32_t)(w0 >> 32);
-        U.tile = tile;
-        U.a = rl64(w, 2); U.b = rl64(w, 3); U.out = rl64(w, 4); U.size = rl64(w, 5);
-        U.dim[0] = (uint32_t)w6; U.dim[1] = (uint32_t)(w6 >> 32);
-        U.dim[2] = (uint32_t)w7; U.dim[3] = (uint32_t)(w7 >> 32);
-        U.aux0 = rl64(w, 8); U.aux1 = rl64(w, 9); U.aux2 = rl64(w, 10);
-        U.pf[0] = __uint_as_float((uint32_t)w13); U.pf[1] = __uint_as_float((uint32_t)(w13 >> 32));
-        U.pf[2] = __uint_as_float((uint32_t)w14); U.pf[3] = __uint_as_float((uint32_t)(w14 >> 32));
-        U.pf[4] = __uint_as_float((uint32_t)w15); U.pf[5] = __uint_as_float((uint32_t)(w15 >> 32));
-        U.lensw[0] = w13;
-        U.lensw[1] = w14;
-        U.kind = (uint32_t)m0;
-        uint32_t status = (uint32_t)(m0 >> 32);
-        U.ntiles = (uint32_t)m1;
-        U.p0 = __uint_as_float((uint32_t)(m1 >> 32));
-        U.scratch = m3 == NO_SCRATCH ? nullptr : A.scratch + (m3 % A.scratch_bytes);
-        // dependencies: explicit deltas in lanes 0..13 (6 in the descriptor,
-        // 8 copied beside it) and a contiguous range
-        const uint32_t delta = lane < 4 ? (uint32_t)((w11 >> (16 * lane)) & 0xFFFFu)
-                             : lane < 6 ? (uint32_t)((w12 >> (16 * (lane - 4))) & 0xFFFFu)
-                             : lane < 10 ? (uint32_t)((x0 >> (16 * (lane - 6))) & 0xFFFFu)
-                             : lane < 14 ? (uint32_t)((x1 >> (16 * (lane - 10))) & 0xFFFFu) : 0u;
-        uint64_t rlo = seq - ((w12 >> 32) & 0xFFFFu);
-        if (w11 != 0 || (w12 & 0xFFFFFFFFFFFFull) != 0 || x0 != 0) {
-            bool counted = false;
-            uint64_t t0 = 0;
-            uint32_t dbo = 1;
-            for (;;) {
-                bool ok = true;
-                if (delta) {
-                    const uint64_t d = seq - delta;
-                    ok = ld_agent(&A.done[d & A.mask]) >= d;
-                }
-                while (rlo < seq) {
-                    const uint64_t x = rlo + lane;
-                    const bool okr = x >= seq || ld_agent(&A.done[x & A.mask]) >= x;
+        const uint64_t tail = ld_agent(&C->q_tail);
+        const uint64_t now = wall_clock64();
+        uint32_t r = SLOTS, rstatus = GPUOS_ST_OK;
+        uint64_t rseq = ~0ull;
+#pragma unroll
+        for (uint32_t k = 0; k < SLOTS; ++k) {
+            if (state[k] != SL_WAIT) continue;
+            bool ready = true;
+            if (sdeps[k]) {
+                const uint64_t d = sseq[k] - sdl[k];
+                const bool ok = sdl[k] == 0 || dv[k] >= d;
+                if (srlo[k] < sseq[k]) {
+                    // range dependency: advance over up to 64 completed seqs per check
+                    const uint64_t x = srlo[k] + lane;
+                    const bool okr = x >= sseq[k] || ld_agent(&A.done[x & A.mask]) >= x;
                     const uint64_t bal = __ballot(okr);
-                    if (bal == ~0ull) { rlo += 64; continue; }
-                    rlo += (uint64_t)(__ffsll((long long)~bal) - 1);
-                    break;
+                    srlo[k] += bal == ~0ull ? 64u : (uint64_t)(__ffsll((long long)~bal) - 1);
                 }
-                if (__all(ok) && rlo >= seq) break;
-                if (!counted) { counted = true; ++n_depw; t0 = wall_clock64(); }
-                if (ld_agent(&C->stop) == STOP_ABORT) { stop = true; break; }
-                if (wall_clock64() - t0 > A.spin_limit_ticks) {
-                    status = GPUOS_ST_SPIN;
-                    if (lane == 0) {
-                        __hip_atomic_store(&C->error, (uint64_t)GPUOS_ST_SPIN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        st_sys(&A.hctl->dev_error, GPUOS_ST_SPIN);
-                    }
-                    break;
-                }
-                // dependency waits back off to at most 16 x 64 clocks: the
-                // awaited op is in flight, so a long sleep only adds latency
-                nap(dbo);
-                dbo = dbo * 2 < DEP_BACKOFF_MAX ? dbo * 2 : DEP_BACKOFF_MAX;
+                ready = __all(ok) && srlo[k] >= sseq[k];
             }
-            if (stop) break;
+            uint32_t stat = GPUOS_ST_OK;
+            if (!ready) {
+                if (!swaited[k]) { swaited[k] = true; st0[k] = now; ++n_depw; }
+                if (now - st0[k] > A.spin_limit_ticks) { ready = true; stat = GPUOS_ST_SPIN; }
+            }
+            if (ready && sseq[k] < rseq) { r = k; rseq = sseq[k]; rstatus = stat; }
+        }
+        if (r < SLOTS) {
+            const uint64_t w = pick(sw, r);
+            const uint64_t seq = rseq, u = pick(su, r), t_claim = pick(tclaim, r);
+            const uint32_t tile = pick(stile, r);
+            const uint64_t slot = seq & A.mask;
+            Unit U;
+            const uint64_t w0 = rl64(w, 0), w6 = rl64(w, 6), w7 = rl64(w, 7);
+            const uint64_t w13 = rl64(w, 13), w14 = rl64(w, 14), w15 = rl64(w, 15);
+            const uint64_t m0 = rl64(w, 16), m1 = rl64(w, 17), m3 = rl64(w, 19);
+            U.seq = seq;
+            U.flags = (uint32_t)(w0 >> 32);
+            U.tile = tile;
+            U.a = rl64(w, 2); U.b = rl64(w, 3); U.out = rl64(w, 4); U.size = rl64(w, 5);
+            U.dim[0] = (uint32_t)w6; U.dim[1] = (uint32_t)(w6 >> 32);
+            U.dim[2] = (uint32_t)w7; U.dim[3] = (uint32_t)(w7 >> 32);
+            U.aux0 = rl64(w, 8); U.aux1 = rl64(w, 9); U.aux2 = rl64(w, 10);
+            U.pf[0] = __uint_as_float((uint32_t)w13); U.pf[1] = __uint_as_float((uint32_t)(w13 >> 32));
+            U.pf[2] = __uint_as_float((uint32_t)w14); U.pf[3] = __uint_as_float((uint32_t)(w14 >> 32));
+            U.pf[4] = __uint_as_float((uint32_t)w15); U.pf[5] = __uint_as_float((uint32_t)(w15 >> 32));
+            U.lensw[0] = w13;
+            U.lensw[1] = w14;
+            U.kind = (uint32_t)m0;
+            uint32_t status = (uint32_t)(m0 >> 32);
+            U.ntiles = (uint32_t)m1;
+            U.p0 = __uint_as_float((uint32_t)(m1 >> 32));
+            U.scratch = m3 == NO_SCRATCH ? nullptr : A.scratch + (m3 % A.scratch_bytes);
+            if (rstatus != GPUOS_ST_OK) {
+                status = rstatus;
+                if (lane == 0) {
+                    __hip_atomic_store(&C->error, (uint64_t)rstatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    st_sys(&A.hctl->dev_error, rstatus);
+                }
+            }
             asm volatile("" ::: "memory");  // op loads are device-coherent: no invalidation
-        }
-        const uint64_t t_ready = A.trace ? wall_clock64() : 0;
-        if (status == GPUOS_ST_OK && U.kind != KIND_BAD) run_unit(U, lane);
-        ++n_units;
-        const uint64_t t_body = A.trace ? wall_clock64() : 0;
-        // completion: publish this unit's (write-through) outputs, count it;
-        // the last unit of the descriptor marks it done and releases the
-        // slot.  Every unit's outputs were acknowledged before its count, so
-        // once done[] is visible all of them are.
-        stores_done();
-        bool last = true;
-        if (U.ntiles > 1) {
-            uint32_t prev = 0;
-            if (lane == 0)
-                prev = __hip_atomic_fetch_add(&A.tiles_done[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
-            last = prev == U.ntiles - 1;
-        }
-        if (last) {
-            if (lane == 0) {
-                st_agent(&A.done[slot], seq);
-                if (status != GPUOS_ST_OK) {
-                    __hip_atomic_store(&A.status[slot], status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                    stores_done();  // the status reaches the host before the stamp
-                }
-                st_sys(&A.stamp[slot], seq + N);
+            const uint64_t t_ready = A.trace ? wall_clock64() : 0;
+            // The lane id goes through an empty asm so that the compiler
+            // computes lane-derived addresses inside each body instead of
+            // hoisting hundreds of them out of the persistent loop, where they
+            // would hold registers for the kernel's whole life.
+            uint32_t ln = lane;
+            asm volatile("" : "+v"(ln));
+            if (status == GPUOS_ST_OK && U.kind != KIND_BAD) run_unit(U, ln);
+            ++n_units;
+            const uint64_t t_body = A.trace ? wall_clock64() : 0;
+            // completion: publish this unit's (write-through) outputs, count
+            // it; the last unit of the descriptor marks it done and releases
+            // the slot.  Every unit's outputs were acknowledged before its
+            // count, so once done[] is visible all of them are.
+            stores_done();
+            bool last = true;
+            if (U.ntiles > 1) {
+                uint32_t prev = 0;
+                if (lane == 0)
+                    prev = __hip_atomic_fetch_add(&A.tiles_done[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
+                last = prev == U.ntiles - 1;
             }
+            if (last) {
+                if (lane == 0) {
+                    st_agent(&A.done[slot], seq);
+                    if (status != GPUOS_ST_OK) {
+                        __hip_atomic_store(&A.status[slot], status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                        stores_done();  // the status reaches the host before the stamp
+                    }
+                    st_sys(&A.stamp[slot], seq + N);
+                }
+            }
+            if (A.trace && lane == 0) {
+                uint32_t xcc = 0;
+                asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
+                gpuos_trace_rec* tr = &A.trace[u & (A.trace_cap - 1)];
+                tr->seq = seq;
+                tr->tile = tile;
+                tr->hw = (xcc << 16) | (uint32_t)blockIdx.x;
+                tr->t_claim = t_claim;
+                tr->t_ready = t_ready;
+                tr->t_body = t_body;
+                tr->t_done = wall_clock64();
+                tr->unit = u;
+            }
+#pragma unroll
+            for (uint32_t k = 0; k < SLOTS; ++k)
+                if (k == r) state[k] = SL_FREE;
+            bo = 1;
         }
-        if (A.trace && lane == 0) {
-            uint32_t xcc = 0;
-            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(xcc));
-            gpuos_trace_rec* tr = &A.trace[u & (A.trace_cap - 1)];
-            tr->seq = seq;
-            tr->tile = tile;
-            tr->hw = (xcc << 16) | (uint32_t)blockIdx.x;
-            tr->t_claim = t_claim;
-            tr->t_ready = t_ready;
-            tr->t_body = t_body;
-            tr->t_done = wall_clock64();
-            tr->unit = u;
+        // claim units for the free slots (queue order), then read the units
+        // published by the tail seen above: their entry, mirror and meta
+        // were made device-visible before that tail, so device-coherent
+        // loads issued after it need no cache invalidation.  Claims continue
+        // after the stop: units published before it must all run, and a
+        // ticket past the final tail is simply never used.
+#pragma unroll
+        for (uint32_t k = 0; k < SLOTS; ++k) {
+            if (state[k] != SL_FREE) continue;
+            uint64_t c = 0;
+            if (lane == 0) c = __hip_atomic_fetch_add(&C->q_head, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            su[k] = rl64(c, 0);
+            state[k] = SL_CLAIMED;
         }
+        asm volatile("" ::: "memory");
+        bool any_wait = false, fresh = false;
+#pragma unroll
+        for (uint32_t k = 0; k < SLOTS; ++k) {
+            if (state[k] == SL_CLAIMED && tail > su[k]) {
+                const uint64_t ent = ld_agent(&A.queue[su[k] & A.qmask]);
+                const uint64_t seq = ent >> 24;
+                const uint64_t slot = seq & A.mask;
+                uint64_t w = 0;
+                if (lane < 16) w = ld_agent(&((const uint64_t*)&A.mirror[slot])[lane]);
+                else if (lane < 24) w = ld_agent(&((const uint64_t*)&A.meta[slot])[lane - 16]);
+                const uint64_t w11 = rl64(w, 11), w12 = rl64(w, 12);
+                const uint64_t x0 = rl64(w, 21), x1 = rl64(w, 22);
+                // dependencies: explicit deltas in lanes 0..13 (6 in the
+                // descriptor, 8 copied beside it) and a contiguous range
+                sdl[k] = lane < 4 ? (uint32_t)((w11 >> (16 * lane)) & 0xFFFFu)
+                       : lane < 6 ? (uint32_t)((w12 >> (16 * (lane - 4))) & 0xFFFFu)
+                       : lane < 10 ? (uint32_t)((x0 >> (16 * (lane - 6))) & 0xFFFFu)
+                       : lane < 14 ? (uint32_t)((x1 >> (16 * (lane - 10))) & 0xFFFFu) : 0u;
+                srlo[k] = seq - ((w12 >> 32) & 0xFFFFu);
+                sdeps[k] = w11 != 0 || (w12 & 0xFFFFFFFFFFFFull) != 0 || x0 != 0;
+                swaited[k] = false;
+                sw[k] = w;
+                sseq[k] = seq;
+                stile[k] = (uint32_t)(ent & 0xFFFFFFu);
+                tclaim[k] = A.trace ? wall_clock64() : 0;
+                state[k] = SL_WAIT;
+                fresh = true;
+            }
+            any_wait = any_wait || state[k] == SL_WAIT;
+        }
+        if (r < SLOTS || fresh) continue;  // something ran or was just published: no sleep
+        // nothing ready.  Once the fetcher has stopped, the tail read above
+        // (after the stop flag was seen) is final: every slot not waiting
+        // holds a ticket beyond it, which will never be published, and the
+        // wave leaves when it holds no published unit.
+        if (stop_seen && !any_wait) break;
+        const uint64_t stp = ld_agent(&C->stop);
+        if (stp == STOP_ABORT) break;
+        if (stp) { stop_seen = true; continue; }
+        // dependency waits back off to at most DEP_BACKOFF_MAX x 64 clocks
+        // (the awaited op is in flight); waits for publication up to
+        // backoff_max
+        const uint32_t cap = any_wait ? DEP_BACKOFF_MAX : A.backoff_max;
+        nap(bo);
+        bo = bo * 2 < cap ? bo * 2 : cap;
     }
     if (lane == 0) {
         __hip_atomic_fetch_add(&C->stat_units, n_units, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

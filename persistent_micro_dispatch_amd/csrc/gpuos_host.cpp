@@ -685,12 +685,18 @@ int gpuos_submit_bursts(void* ctx, const gpuos_desc* descs, const uint32_t* burs
     if (!ctx || (n_bursts && (!descs || !burst_sizes))) return GPUOS_E_INVAL;
     uint64_t off = 0;
     int rc = GPUOS_OK;
-    for (uint32_t i = 0; i < n_bursts; ++i) {
-        uint64_t f = 0;
-        rc = gpuos_submit(ctx, descs + off, burst_sizes[i], flags, &f);
-        if (rc != GPUOS_OK) break;
-        if (i == 0 && first_seq) *first_seq = f;
-        off += burst_sizes[i];
+    const uint32_t ring = ((gpuos_ctx*)ctx)->N;
+    for (uint32_t i = 0; i < n_bursts && rc == GPUOS_OK; ++i) {
+        // a burst larger than the ring is committed in ring-sized groups
+        for (uint32_t done = 0; done < burst_sizes[i];) {
+            const uint32_t n = std::min(burst_sizes[i] - done, ring);
+            uint64_t f = 0;
+            rc = gpuos_submit(ctx, descs + off, n, flags, &f);
+            if (rc != GPUOS_OK) break;
+            if (off == 0 && first_seq) *first_seq = f;
+            off += n;
+            done += n;
+        }
     }
     if (n_done) *n_done = off;
     return rc;

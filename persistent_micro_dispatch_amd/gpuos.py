@@ -6,6 +6,7 @@ fallback implementation.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -162,6 +163,21 @@ def gpuos_abi_version() -> int:
     return lib().gpuos_abi_version()
 
 
+# Contexts not yet shut down.  A resident executor kernel never finishes by
+# itself, and the HIP runtime waits for running kernels when the process
+# exits, so contexts left open (an exception, a forgotten shutdown) are shut
+# down at interpreter exit.
+_LIVE = set()
+
+
+def _shutdown_live():
+    for c in list(_LIVE):
+        gpuos_shutdown(c)
+
+
+atexit.register(_shutdown_live)
+
+
 def gpuos_init(device: int = 0, ring_entries: int = 0, num_wgs: int = 0, waves_per_wg: int = 0,
                backoff_max: int = 0, flags: int = 0, hip_stream: int = 0, scratch_bytes: int = 0,
                unit_queue_log2: int = 0, spin_limit_ms: int = 0) -> int:
@@ -169,6 +185,7 @@ def gpuos_init(device: int = 0, ring_entries: int = 0, num_wgs: int = 0, waves_p
                    hip_stream or None, scratch_bytes, unit_queue_log2, spin_limit_ms)
     out = ctypes.c_void_p()
     _check("gpuos_init", lib().gpuos_init(ctypes.byref(p), ctypes.byref(out)))
+    _LIVE.add(out.value)
     return out.value
 
 
@@ -217,6 +234,7 @@ def gpuos_resume(ctx: int) -> int:
 
 
 def gpuos_shutdown(ctx: int) -> int:
+    _LIVE.discard(ctx)
     return lib().gpuos_shutdown(ctx)
 
 
