@@ -182,11 +182,17 @@ int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* cons
  * descriptor is checked and annotated with dependencies on earlier
  * descriptors whose byte ranges it reads or writes (read-after-write,
  * write-after-read, write-after-write), so results equal sequential
- * execution.  The caller's array may be reused on return.  *first_seq
+ * execution.  A descriptor waits for up to 62 earlier descriptors by
+ * number (six in dep_delta, the rest in a side array owned by the library
+ * and copied to device memory with the descriptor); with more it waits for
+ * every descriptor from the oldest on (dep_range).  Annotation runs before
+ * the wait for free slots, so it overlaps the device's work.  The caller's
+ * array may be reused on return.  *first_seq
  * (may be NULL) receives the sequence number of descriptor 0; the others
  * follow consecutively.  All or nothing: on error no descriptor is
  * submitted.  Errors: E_INVAL (a descriptor fails validation),
- * E_FULL (fewer than count free slots and no BLOCK), E_STATE. */
+ * E_FULL (fewer than count free slots and no BLOCK), E_DEVICE (the
+ * executor reported an error while this call waited), E_STATE. */
 int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t flags,
                  uint64_t* first_seq);
 

@@ -238,15 +238,17 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
                 if (lane < 16) w = ld_agent(&((const uint64_t*)&A.mirror[slot])[lane]);
                 else if (lane < 24) w = ld_agent(&((const uint64_t*)&A.meta[slot])[lane - 16]);
                 const uint64_t w11 = rl64(w, 11), w12 = rl64(w, 12);
-                const uint64_t x0 = rl64(w, 21), x1 = rl64(w, 22);
-                // dependencies: explicit deltas in lanes 0..13 (6 in the
-                // descriptor, 8 copied beside it) and a contiguous range
+                // dependencies: one explicit delta per lane (6 in the
+                // descriptor, the rest in the side words copied to HBM when
+                // the sixth is in use) and a contiguous range
+                uint64_t xw = 0;
+                if (((w12 >> 16) & 0xFFFFu) != 0 && lane >= 6 && lane < MAX_DEPS)
+                    xw = ld_agent(&A.depd[slot * DEPX_WORDS + (lane - 6) / 4]);
                 sdl[k] = lane < 4 ? (uint32_t)((w11 >> (16 * lane)) & 0xFFFFu)
                        : lane < 6 ? (uint32_t)((w12 >> (16 * (lane - 4))) & 0xFFFFu)
-                       : lane < 10 ? (uint32_t)((x0 >> (16 * (lane - 6))) & 0xFFFFu)
-                       : lane < 14 ? (uint32_t)((x1 >> (16 * (lane - 10))) & 0xFFFFu) : 0u;
+                       : lane < MAX_DEPS ? (uint32_t)((xw >> (16 * ((lane - 6) & 3u))) & 0xFFFFu) : 0u;
                 srlo[k] = seq - ((w12 >> 32) & 0xFFFFu);
-                sdeps[k] = w11 != 0 || (w12 & 0xFFFFFFFFFFFFull) != 0 || x0 != 0;
+                sdeps[k] = w11 != 0 || (w12 & 0xFFFFFFFFFFFFull) != 0;
                 swaited[k] = false;
                 sw[k] = w;
                 sseq[k] = seq;
@@ -318,12 +320,6 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             const uint32_t wi = lane + 64u * k;
             if (wi < nw) v[k] = ld_sys(&ringw[((f + (wi >> 4)) & mask) * 16u + (wi & 15u)]);
         }
-        // extra dependency deltas: 2 words per descriptor, lane i < count
-        uint64_t xd0 = 0, xd1 = 0;
-        if (lane < count) {
-            xd0 = ld_sys(&A.depx[2 * ((f + lane) & mask)]);
-            xd1 = ld_sys(&A.depx[2 * ((f + lane) & mask) + 1]);
-        }
 #pragma unroll
         for (uint32_t k = 0; k < 16; ++k) {
             const uint32_t wi = lane + 64u * k;
@@ -335,6 +331,18 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         const bool act = lane < count;
         const uint64_t* dw = lds + (act ? lane : 0) * 16u;
         const uint64_t d0 = dw[0], d12 = dw[12];
+        // a descriptor with more than six dependencies keeps the rest in
+        // DEPX_WORDS side words of the host array: copy them to HBM for the
+        // workers (the slot's previous descriptor has completed, so nobody
+        // reads its copy any more)
+        if (act && ((d12 >> 16) & 0xFFFFu) != 0) {
+            const uint64_t sl = (f + lane) & mask;
+            uint64_t xw[DEPX_WORDS];
+#pragma unroll
+            for (uint32_t k = 0; k < DEPX_WORDS; ++k) xw[k] = ld_sys(&A.depx[sl * DEPX_WORDS + k]);
+#pragma unroll
+            for (uint32_t k = 0; k < DEPX_WORDS; ++k) wst64(&A.depd[sl * DEPX_WORDS + k], xw[k]);
+        }
         const uint32_t op_id = (uint32_t)d0;
         const uint32_t ver = (uint32_t)(d12 >> 48);
         const uint32_t maxver = (uint32_t)__shfl((int)ver, (int)count - 1, 64);
@@ -433,8 +441,6 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             wst64(mm + 2, ubegin);
             wst64(mm + 3, my_sv);
             wst64(mm + 4, my_mark);
-            wst64(mm + 5, xd0);
-            wst64(mm + 6, xd1);
             wst32(&A.tiles_done[slot], 0u);
             pref[lane] = inc - nt;
         }

@@ -179,7 +179,11 @@ struct gpuos_ctx {
     uint32_t N = 0, mask = 0, Q = 0, cu_count = 0;
     // host-coherent ring memory
     gpuos_desc* ring = nullptr;
-    uint64_t* depx = nullptr;  // [N][2]: dependency deltas 6..13
+    uint64_t* depx = nullptr;  // [N][DEPX_WORDS]: dependency deltas 6..MAX_DEPS-1
+    uint64_t* depd = nullptr;  // device copy, written by the fetcher
+    std::vector<gpuos_desc> stage;     // annotated descriptors waiting for ring slots
+    std::vector<uint64_t> stage_ex;    // their side dependency words
+    bool hz_reset = false;             // tracker cleared after a failed blocking submit
     uint64_t* stamp = nullptr;
     uint32_t* status = nullptr;
     HostCtl* hctl = nullptr;
@@ -252,6 +256,7 @@ int executor_launch(gpuos_ctx* c) {
     ExecArgs a{};
     a.ring = c->ring;
     a.depx = c->depx;
+    a.depd = c->depd;
     a.stamp = c->stamp;
     a.status = c->status;
     a.hctl = c->hctl;
@@ -322,7 +327,7 @@ void loopback_main(gpuos_ctx* c) {
     std::mt19937_64 rng(12345);
     const uint64_t N = c->N;
     uint64_t f = c->N;  // next seq to fetch
-    struct Pend { uint64_t seq; gpuos_desc d; uint16_t ex[8]; };
+    struct Pend { uint64_t seq; gpuos_desc d; uint16_t ex[4 * DEPX_WORDS]; };
     std::vector<Pend> pend;
     auto is_done = [&](uint64_t s) { return c->lb_done[s & c->mask] >= s; };
     while (!c->lb_stop.load()) {
@@ -331,7 +336,8 @@ void loopback_main(gpuos_ctx* c) {
             Pend pe;
             pe.seq = f;
             pe.d = c->ring[f & c->mask];
-            memcpy(pe.ex, &c->depx[2 * (f & c->mask)], 16);
+            memset(pe.ex, 0, sizeof(pe.ex));
+            if (pe.d.dep_delta[5]) memcpy(pe.ex, &c->depx[DEPX_WORDS * (f & c->mask)], 8 * DEPX_WORDS);
             pend.push_back(pe);
             ++f;
             progress = true;
@@ -345,7 +351,7 @@ void loopback_main(gpuos_ctx* c) {
             for (int k = 0; k < 6 && ok; ++k)
                 if (d.dep_delta[k]) ok = is_done(s - d.dep_delta[k]);
             const uint16_t* ex = pend[i].ex;
-            for (int k = 0; k < 8 && ok; ++k)
+            for (uint32_t k = 0; k < 4 * DEPX_WORDS && ok; ++k)
                 if (ex[k]) ok = is_done(s - ex[k]);
             for (uint64_t x = s - d.dep_range; x < s && ok; ++x) ok = is_done(x);
             if (ok) ready.push_back(i);
@@ -411,7 +417,7 @@ void free_ctx(gpuos_ctx* c) {
     if (c->stamp) (void)hipHostFree(c->stamp);
     if (c->status) (void)hipHostFree(c->status);
     if (c->hctl) (void)hipHostFree(c->hctl);
-    void* dev[] = {c->dctl, c->mirror, c->meta, c->done, c->tiles_done, c->queue, c->table, c->scratch, c->trace};
+    void* dev[] = {c->dctl, c->mirror, c->meta, c->done, c->tiles_done, c->depd, c->queue, c->table, c->scratch, c->trace};
     for (void* p : dev)
         if (p) (void)hipFree(p);
     if (c->ev_start) (void)hipEventDestroy(c->ev_start);
@@ -452,7 +458,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     const size_t N = c->N;
     if (c->loopback) {
         c->ring = (gpuos_desc*)aligned_zalloc(N * sizeof(gpuos_desc));
-        c->depx = (uint64_t*)aligned_zalloc(N * 16);
+        c->depx = (uint64_t*)aligned_zalloc(N * 8 * DEPX_WORDS);
         c->stamp = (uint64_t*)aligned_zalloc(N * 8);
         c->status = (uint32_t*)aligned_zalloc(N * 4);
         c->hctl = (HostCtl*)aligned_zalloc(sizeof(HostCtl));
@@ -488,12 +494,12 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     c->spin_ticks = (uint64_t)P.spin_limit_ms * (uint64_t)wclk;
     const unsigned hflags = hipHostMallocCoherent | hipHostMallocMapped;
     HIPCHK(hipHostMalloc((void**)&c->ring, N * sizeof(gpuos_desc), hflags));
-    HIPCHK(hipHostMalloc((void**)&c->depx, N * 16, hflags));
+    HIPCHK(hipHostMalloc((void**)&c->depx, N * 8 * DEPX_WORDS, hflags));
     HIPCHK(hipHostMalloc((void**)&c->stamp, N * 8, hflags));
     HIPCHK(hipHostMalloc((void**)&c->status, N * 4, hflags));
     HIPCHK(hipHostMalloc((void**)&c->hctl, sizeof(HostCtl), hflags));
     memset(c->ring, 0, N * sizeof(gpuos_desc));
-    memset(c->depx, 0, N * 16);
+    memset(c->depx, 0, N * 8 * DEPX_WORDS);
     memset(c->status, 0, N * 4);
     memset(c->hctl, 0, sizeof(HostCtl));
     for (size_t i = 0; i < N; ++i) c->stamp[i] = N + i;
@@ -502,6 +508,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     HIPCHK(hipMalloc((void**)&c->meta, N * sizeof(MirrorMeta)));
     HIPCHK(hipMalloc((void**)&c->done, N * 8));
     HIPCHK(hipMalloc((void**)&c->tiles_done, N * 4));
+    HIPCHK(hipMalloc((void**)&c->depd, N * 8 * DEPX_WORDS));
     HIPCHK(hipMalloc((void**)&c->queue, (size_t)c->Q * 8));
     HIPCHK(hipMalloc((void**)&c->table, 2 * GPUOS_MAX_OPS * sizeof(TableEntry)));
     HIPCHK(hipMalloc((void**)&c->scratch, P.scratch_bytes));
@@ -608,28 +615,48 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
         int rc = executor_launch(c);
         if (rc) return rc;
     }
-    // acquire slots: seq s needs seq s - N complete
-    const uint64_t need_wm = c->next_seq + count - c->N;
-    refresh_wm(c);
-    if (c->wm < need_wm) {
-        if (!(flags & GPUOS_SUBMIT_BLOCK)) { ++c->full_rej; return GPUOS_E_FULL; }
+    const bool block = (flags & GPUOS_SUBMIT_BLOCK) != 0;
+    // wait until seq `upto` is complete (spinning, then yielding)
+    auto wait_wm = [&](uint64_t upto) -> int {
         uint32_t spins = 0;
         const uint64_t tb = now_ns();
-        while (c->wm < need_wm) {
+        while (c->wm < upto) {
             if (c->hctl && ld_acq(&c->hctl->dev_error)) return GPUOS_E_DEVICE;
             if (++spins > 1000) std::this_thread::yield();
             else GPUOS_PAUSE();
             refresh_wm(c);
         }
         c->ns_blocked += now_ns() - tb;
+        return GPUOS_OK;
+    };
+    refresh_wm(c);
+    if (c->hz_reset) {
+        // an earlier blocking submit failed after annotating and cleared the
+        // tracker: nothing it knew about may still be in flight
+        if (c->wm < c->next_seq) {
+            if (!block) { ++c->full_rej; return GPUOS_E_FULL; }
+            const int rc = wait_wm(c->next_seq);
+            if (rc) return rc;
+        }
+        c->hz_reset = false;
     }
+    // slots: seq s needs seq s - N complete
+    const uint64_t need_wm = c->next_seq + count - c->N;
+    if (c->wm < need_wm && !block) { ++c->full_rej; return GPUOS_E_FULL; }
+    // Annotate before waiting for slots, so that this work overlaps the
+    // device's.  Dependencies are computed against the watermark seen now;
+    // an older watermark only adds waits on descriptors already complete.
     const uint64_t t_hz0 = now_ns();
     const uint64_t s0 = c->next_seq;
+    if (c->stage.size() < count) {
+        c->stage.resize(count);
+        c->stage_ex.resize((size_t)count * DEPX_WORDS);
+    }
     Access acc[2 * MAX_B + 4];
     for (uint32_t i = 0; i < count; ++i) {
         const uint64_t s = s0 + i;
-        const uint32_t slot = (uint32_t)(s & c->mask);
-        gpuos_desc d = descs[i];
+        gpuos_desc& d = c->stage[i];
+        d = descs[i];
         d.seq = s;
         d.table_version = (uint16_t)c->version;
         memset(d.dep_delta, 0, sizeof(d.dep_delta));
@@ -641,7 +668,7 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
             c->hz.analyze(s, acc, n, c->wm, c->deps, &range_from);
         }
         if ((flags & GPUOS_SUBMIT_SERIAL) && s - 1 >= c->wm) c->deps.push_back(s - 1);
-        uint16_t ex[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        uint16_t* ex = (uint16_t*)&c->stage_ex[(size_t)i * DEPX_WORDS];
         if (!c->deps.empty() || range_from != UINT64_MAX) {
             std::sort(c->deps.begin(), c->deps.end());
             c->deps.erase(std::unique(c->deps.begin(), c->deps.end()), c->deps.end());
@@ -663,11 +690,26 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
                 ++c->deps_range;
             }
         }
-        memcpy(&c->depx[2 * slot], ex, 16);
+        if (c->deps.size() > 6)  // the side words are read only when dep_delta[5] is set
+            for (size_t k = c->deps.size() - 6; k < 4 * DEPX_WORDS; ++k) ex[k] = 0;
+    }
+    const uint64_t t_hz1 = now_ns();
+    if (c->wm < need_wm) {
+        const int rc = wait_wm(need_wm);
+        if (rc) {
+            // the tracker already holds accesses that will not be submitted
+            c->hz.clear();
+            c->hz_reset = true;
+            return rc;
+        }
+    }
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint32_t slot = (uint32_t)((s0 + i) & c->mask);
+        const gpuos_desc& d = c->stage[i];
+        if (d.dep_delta[5]) memcpy(&c->depx[DEPX_WORDS * slot], &c->stage_ex[(size_t)i * DEPX_WORDS], 8 * DEPX_WORDS);
         c->status[slot] = 0;
         memcpy(&c->ring[slot], &d, sizeof(gpuos_desc));
     }
-    const uint64_t t_hz1 = now_ns();
     // commit in order (store-release of each stamp)
     for (uint32_t i = 0; i < count; ++i) {
         const uint64_t s = s0 + i;

@@ -35,8 +35,7 @@ struct alignas(64) MirrorMeta {
     uint64_t ubegin;        // first unit number (this launch's numbering)
     uint64_t scratch_v;     // virtual scratch offset (physical = v % scratch_bytes), or ~0
     uint64_t scratch_mark;  // scratch watermark before this descriptor's allocation
-    uint64_t dep_extra[2];  // dependency deltas 6..13 (16-bit each), copied from the host side array
-    uint64_t pad;
+    uint64_t pad[3];
 };
 static_assert(sizeof(MirrorMeta) == 64, "MirrorMeta is 64 bytes");
 
@@ -63,7 +62,8 @@ struct DevCtl {
 // Kernel arguments of the executor.
 struct ExecArgs {
     const gpuos_desc* ring;   // host-mapped
-    const uint64_t* depx;     // host-mapped: 2 words of extra dependency deltas per slot
+    const uint64_t* depx;     // host-mapped: DEPX_WORDS words of extra dependency deltas per slot
+    uint64_t* depd;           // device copy of depx for descriptors that use it
     uint64_t* stamp;          // host-mapped
     uint32_t* status;         // host-mapped
     HostCtl* hctl;            // host-mapped
@@ -104,7 +104,9 @@ constexpr uint32_t GEMV_KC = 256;          // rows of W per GEMV unit
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
 constexpr uint32_t MAX_TILES = 1u << 22;   // hard cap of units per descriptor
-constexpr uint32_t MAX_DEPS = 14;          // explicit dependencies: 6 in the descriptor + 8 beside it
+constexpr uint32_t DEPX_WORDS = 14;        // side words of extra dependency deltas per ring slot
+constexpr uint32_t MAX_DEPS = 6 + 4 * DEPX_WORDS;  // explicit dependencies: 6 in the descriptor + 56 beside it
+static_assert(MAX_DEPS <= 64, "one dependency per lane");
 
 __host__ __device__ inline uint32_t dt_in(uint32_t flags) { return flags & 15u; }
 __host__ __device__ inline uint32_t dt_out(uint32_t flags) { return (flags >> 4) & 15u; }

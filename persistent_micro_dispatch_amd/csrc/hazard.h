@@ -47,7 +47,7 @@ struct Access {
 
 class HazardTracker {
 public:
-    static constexpr int MAXR = 14;
+    static constexpr int MAXR = 30;
     static constexpr size_t SPLIT_AT = 96;
 
     // Appends to `deps` every live seq (>= floor) that `seq` must wait for

@@ -156,6 +156,36 @@ def test_loopback_respects_hazards_in_a_large_arena():
     assert _check_order(r, order, first) == 0
 
 
+@pytest.mark.parametrize("n_read", [25, 40])
+def test_many_readers_give_explicit_dependencies(n_read):
+    """A write after n reads of its output waits on exactly those n
+    descriptors: explicit dependencies up to the tracker's 30 readers per
+    interval, beyond that a range from the oldest reader."""
+    r = np.zeros(n_read + 1, W.REC_DTYPE)
+    r["buf"] = -1
+    r["dtype"] = r["out_dtype"] = W.F32
+    r["op"] = W.OP_RELU
+    r["size"] = 256
+    r["buf"][:n_read, W.A] = 0                          # all read buffer 0
+    r["buf"][:n_read, W.OUT] = np.arange(1, n_read + 1)  # each writes its own buffer
+    r["buf"][n_read, W.A] = n_read + 1                  # then buffer 0 is overwritten
+    r["buf"][n_read, W.OUT] = 0
+    descs = to_descs(r, _fake_ptrs(n_read + 2))
+    ctx = _loopback()
+    try:
+        first = _run(ctx, descs)
+        order = G.gpuos_loopback_order(ctx)
+        st = G.gpuos_stats_get(ctx)
+    finally:
+        G.gpuos_shutdown(ctx)
+    if n_read <= 30:
+        assert st["deps_range"] == 0 and st["deps_explicit"] == n_read
+    else:
+        assert st["deps_range"] == 1
+    assert _check_order(r, order, first) == 0
+    assert order[-1] == first + n_read or list(order).index(first + n_read) == len(order) - 1
+
+
 def test_serial_flag_gives_submission_order():
     s = W.make_elementwise(n_desc=500)
     descs = to_descs(s.recs, _fake_ptrs(len(s.buffers)))
