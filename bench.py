@@ -28,8 +28,10 @@ from HIP events recorded on the executor's own stream.
 
 Printed: one JSON line with micro-ops/s (the headline value), p50/p99
 closed-loop per-op latency, the eager hipLaunchKernel-per-op and hipGraph
-baselines, null-launch cost, host submission cost, the roofline of the
-executor kernel and the CPU oracle timed on a bounded sample of the stream.
+baselines, null-launch cost, host submission cost, element-wise ops/s and
+GB/s per log2-size bucket (in stream order with hazard ordering, and as
+independent ops), the roofline of the executor kernel and the CPU oracle
+timed on a bounded sample of the stream.
 """
 from __future__ import annotations
 
@@ -50,6 +52,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 KERNEL_SOURCES = ["persistent_micro_dispatch_amd/csrc/gpuos_device.hip",
                   "persistent_micro_dispatch_amd/csrc/gpuos_ops.h",
                   "persistent_micro_dispatch_amd/csrc/gpuos_internal.h",
+                  "persistent_micro_dispatch_amd/csrc/rope_math.h",
                   "include/gpuos.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gpuos_executor_hbm_traffic.md")
 
@@ -261,6 +264,33 @@ def main():
     rc, _, _ = G.gpuos_submit_bursts(ctx, chain, np.full(len(chain) // 50, 50, np.uint32), G.GPUOS_SUBMIT_BLOCK)
     assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
     chain_s = time.perf_counter() - ta
+    # ---- element-wise throughput per log2-size bucket: the bucket's
+    # descriptors in stream order, once with hazard ordering and once as
+    # independent ops (NOHAZARD; outputs race, nothing reads them after)
+    buckets = None
+    if args.workload in ("elementwise", "pr1"):
+        buckets = {}
+        lg = np.minimum(np.floor(np.log2(recs["size"])).astype(np.int64), 15)
+        per_op = W.algorithmic_bytes(recs)
+        for b in range(int(lg.min()), int(lg.max()) + 1):
+            idx = np.nonzero(lg == b)[0]
+            if len(idx) < 64:
+                continue
+            sub = descs[idx].copy()
+            nbk = np.full(len(sub) // 64, 64, np.uint32)
+            rem = len(sub) - int(nbk.sum())
+            if rem:
+                nbk = np.append(nbk, np.uint32(rem))
+            row = {"descriptors": int(len(idx)), "bytes_per_op": float(per_op[idx].mean())}
+            for key, fl in (("ordered", G.GPUOS_SUBMIT_BLOCK),
+                            ("independent", G.GPUOS_SUBMIT_BLOCK | G.GPUOS_SUBMIT_NOHAZARD)):
+                ta = time.perf_counter()
+                rc, _, _ = G.gpuos_submit_bursts(ctx, sub, nbk, fl)
+                assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
+                el = time.perf_counter() - ta
+                row[key + "_ops_per_s"] = len(idx) / el
+                row[key + "_gbs"] = float(per_op[idx].sum()) / el / 1e9
+            buckets[f"2^{b}"] = row
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     chain_ok = float(chain_buf.cpu()[0]) == 5000.0
     st_end = G.gpuos_stats_get(ctx)
@@ -373,6 +403,7 @@ def main():
         "host_submit_ns_per_desc": st_end["ns_submit"] / max(1, st_end["submitted"]),
         "host_blocked_ns_per_desc": st_end["ns_blocked"] / max(1, st_end["submitted"]),
         "host_annotate_ns_per_desc": st_end["ns_annotate"] / max(1, st_end["submitted"]),
+        "size_buckets": buckets,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

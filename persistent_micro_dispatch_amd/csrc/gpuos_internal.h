@@ -100,7 +100,7 @@ __host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind) {
 constexpr uint32_t COPY_TILE_BYTES = 32768;
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
 constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit
-constexpr uint32_t GEMV_KC = 256;          // rows of W per GEMV unit
+constexpr uint32_t GEMV_KC = 128;          // rows of W per GEMV unit
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
 constexpr uint32_t MAX_TILES = 1u << 22;   // hard cap of units per descriptor
@@ -135,6 +135,14 @@ struct Plan {
     uint32_t ntiles;
     uint64_t scratch;     // bytes (0 = none); counters occupy the first COUNTER_AREA
 };
+
+// A RoPE unit is one batch row and the heads one wave-wide load of 64 x 16
+// bytes covers, when a head's row of D elements divides 1 KiB; else one head.
+__host__ __device__ inline uint32_t rope_heads_per_unit(uint32_t D, uint32_t dt) {
+    const uint32_t rb = D * esz(dt);
+    if (rb == 0 || rb % 16u != 0 || rb > 1024u || (1024u % rb) != 0) return 1u;
+    return 1024u / rb;
+}
 
 // a GEMV unit covers 16 lanes x 16 bytes of columns (four rows per load)
 __host__ __device__ inline uint32_t gemv_cols_per_block(uint32_t dt) { return 16u * (16u / esz(dt)); }
@@ -185,7 +193,13 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
                 if (lens_at(d.lensw, i) == 0) return bad();
                 if (d.kind == GPUOS_OP_KV_APPEND && lens_at(d.lensw, i) > C) return bad();
             }
-            p.ntiles = (uint32_t)B;
+            if (d.kind == GPUOS_OP_ROPE) {
+                const uint64_t t = B * cdiv(H, rope_heads_per_unit(D, di));
+                if (t > MAX_TILES) return bad();
+                p.ntiles = (uint32_t)t;
+            } else {
+                p.ntiles = (uint32_t)B;
+            }
             return p;
         }
         case GPUOS_OP_SDPA: {

@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include "gpuos_internal.h"
+#include "rope_math.h"
 
 namespace gpuos {
 
@@ -540,99 +541,86 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
 }
 
 // ------------------------------------------------------------------ RoPE
-// Unit = one batch row b: every head of q and k, rotated at pos = L_b - 1.
-// The angle pos * theta^(-2i/D), its sine and cosine and the rotation are
-// evaluated in double and rounded once to the dtype, so the result is the
-// correctly rounded rotation up to the last-bit ties of double rounding.
+// Unit = one batch row b and a group of heads (rope_heads_per_unit), of both
+// q and k, rotated at pos = L_b - 1.  The angle pos * theta^(-2i/D), its sine
+// and cosine (rope_math.h, a few double ulps) and the rotation are evaluated
+// in double and rounded once to the dtype, so the result is the correctly
+// rounded rotation except where the exact value lies within a few double
+// ulps of a rounding boundary.
 //
-// Fast path (adjacent pairs, row of D elements = CPR chunks of 16 bytes with
-// CPR dividing 64, 16-byte aligned operands): lane l always holds column
-// chunk l % CPR of some row, so its VE/2 angles are computed once; up to 16
-// rows per instruction group of each tensor are loaded before any store.
+// Fast path (adjacent pairs, a head's row of D elements = CPR chunks of 16
+// bytes with CPR dividing 64, 16-byte aligned operands): the unit's heads
+// are exactly one load instruction per tensor; lane l holds column chunk
+// l % CPR of head l / CPR, so it computes the angles of its VE/2 pairs once.
 template <uint32_t DT>
 __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
     constexpr uint32_t VE = 16u / ES;
-    constexpr uint32_t NI = 8;  // load instructions per tensor per group
-    const uint32_t b = u.tile;
     const uint32_t H = u.dim[0], D = u.dim[1];
+    const uint32_t RH = rope_heads_per_unit(D, DT);
+    const uint32_t ng = (H + RH - 1) / RH;
+    const uint32_t b = u.tile / ng, h0 = (u.tile - b * ng) * RH;
+    const uint32_t hn = min(RH, H - h0);
     const bool half = (u.flags & GPUOS_F_ROPE_HALF) != 0;
     const double theta = u.pf[4] != 0.0f ? (double)u.pf[4] : (u.p0 != 0.0f ? (double)u.p0 : 10000.0);
     const double pos = (double)((int)lens_at(u.lensw, b) - 1);
+    const double l2t = rmath::log2_d(theta);
     const uint32_t RB = D * ES;
     const uint32_t CPR = RB / 16u;
     const bool fast = !half && (RB % 16u) == 0 && CPR > 0 && CPR <= 64u && (64u % CPR) == 0 &&
-                      ((u.a | u.b) & 15ull) == 0;
+                      ((u.a | u.b) & 15ull) == 0 && (uint64_t)H * RB < 0x80000000ull;
     if (fast) {
-        const uint32_t RPI = 64u / CPR;  // rows per load instruction
+        // here RH = 64 / CPR: one row per (lane / CPR), rows past H read zero
+        // and their stores are dropped by the window
         const uint32_t cc = lane % CPR, sub = lane / CPR;
-        double cs[VE / 2], sn[VE / 2];
-#pragma unroll
-        for (uint32_t j = 0; j < VE / 2; ++j) {
-            const uint32_t pi = cc * (VE / 2) + j;
-            const double fr = pow(theta, -2.0 * (double)pi / (double)D);
-            sincos(pos * fr, &sn[j], &cs[j]);
-        }
         uint8_t* P0 = (uint8_t*)u.a + (uint64_t)b * H * RB;
         uint8_t* P1 = (uint8_t*)u.b + (uint64_t)b * H * RB;
         const WBuf w0 = wbuf(P0, H * RB), w1 = wbuf(P1, H * RB);
         const RBuf r0 = rbuf(P0, H * RB), r1 = rbuf(P1, H * RB);
-        for (uint32_t h0 = 0; h0 < H; h0 += NI * RPI) {
-            const uint32_t ni = min(NI, (H - h0 + RPI - 1) / RPI);  // instructions in use (uniform)
-            u32x4 v0[NI], v1[NI];
+        const uint32_t off = ((h0 + sub) * CPR + cc) * 16u;
+        const u32x4 v0 = rld16(r0, off), v1 = rld16(r1, off);
+        double cs[VE / 2], sn[VE / 2];
 #pragma unroll
-            for (uint32_t i = 0; i < NI; ++i) {
-                if (i < ni) {
-                    const uint32_t off = ((h0 + i * RPI + sub) * CPR + cc) * 16u;  // rows past H read zero
-                    v0[i] = rld16(r0, off);
-                    v1[i] = rld16(r1, off);
+        for (uint32_t j = 0; j < VE / 2; ++j)
+            rmath::sincos_d(rmath::rope_angle(pos, l2t, cc * (VE / 2) + j, D), &sn[j], &cs[j]);
+#pragma unroll
+        for (uint32_t t = 0; t < 2; ++t) {
+            float x[VE];
+            unpack<DT>(t == 0 ? v0 : v1, x);
+            u32x4 o;
+            if constexpr (DT == GPUOS_F32) {
+                float y[VE];
+#pragma unroll
+                for (uint32_t j = 0; j < VE / 2; ++j) {
+                    const double x0 = x[2 * j], x1 = x[2 * j + 1];
+                    y[2 * j] = (float)(x0 * cs[j] - x1 * sn[j]);
+                    y[2 * j + 1] = (float)(x0 * sn[j] + x1 * cs[j]);
                 }
-            }
+                o = pack<GPUOS_F32>(y);
+            } else {
+                uint32_t hb[VE];
 #pragma unroll
-            for (uint32_t t = 0; t < 2; ++t) {
-#pragma unroll
-                for (uint32_t i = 0; i < NI; ++i) {
-                    if (i >= ni) continue;
-                    float x[VE];
-                    unpack<DT>(t == 0 ? v0[i] : v1[i], x);
-                    u32x4 o;
-                    if constexpr (DT == GPUOS_F32) {
-                        float y[VE];
-#pragma unroll
-                        for (uint32_t j = 0; j < VE / 2; ++j) {
-                            const double x0 = x[2 * j], x1 = x[2 * j + 1];
-                            y[2 * j] = (float)(x0 * cs[j] - x1 * sn[j]);
-                            y[2 * j + 1] = (float)(x0 * sn[j] + x1 * cs[j]);
-                        }
-                        o = pack<GPUOS_F32>(y);
-                    } else {
-                        uint32_t hb[VE];
-#pragma unroll
-                        for (uint32_t j = 0; j < VE / 2; ++j) {
-                            const double x0 = x[2 * j], x1 = x[2 * j + 1];
-                            hb[2 * j] = d2bf(x0 * cs[j] - x1 * sn[j]);
-                            hb[2 * j + 1] = d2bf(x0 * sn[j] + x1 * cs[j]);
-                        }
-                        o.x = hb[0] | (hb[1] << 16); o.y = hb[2] | (hb[3] << 16);
-                        o.z = hb[4] | (hb[5] << 16); o.w = hb[6] | (hb[7] << 16);
-                    }
-                    const uint32_t off = ((h0 + i * RPI + sub) * CPR + cc) * 16u;  // past H: dropped
-                    if (t == 0) wst16(w0, off, o);
-                    else wst16(w1, off, o);
+                for (uint32_t j = 0; j < VE / 2; ++j) {
+                    const double x0 = x[2 * j], x1 = x[2 * j + 1];
+                    hb[2 * j] = d2bf(x0 * cs[j] - x1 * sn[j]);
+                    hb[2 * j + 1] = d2bf(x0 * sn[j] + x1 * cs[j]);
                 }
+                o.x = hb[0] | (hb[1] << 16); o.y = hb[2] | (hb[3] << 16);
+                o.z = hb[4] | (hb[5] << 16); o.w = hb[6] | (hb[7] << 16);
             }
+            if (t == 0) wst16(w0, off, o);
+            else wst16(w1, off, o);
         }
         return;
     }
-    // general path: one pair per lane per step
+    // general path: one pair per lane per step, heads [h0, h0 + hn)
     for (uint32_t pi = lane; pi < D / 2; pi += 64u) {
-        const double fr = pow(theta, -2.0 * (double)pi / (double)D);
         double s, c;
-        sincos(pos * fr, &s, &c);
+        rmath::sincos_d(rmath::rope_angle(pos, l2t, pi, D), &s, &c);
         const uint32_t i0 = half ? pi : 2u * pi, i1 = half ? pi + D / 2 : 2u * pi + 1u;
         for (uint32_t t = 0; t < 2; ++t) {
             uint8_t* P = (uint8_t*)(t == 0 ? u.a : u.b);
-            for (uint32_t hh = 0; hh < H; ++hh) {
+            for (uint32_t hh = h0; hh < h0 + hn; ++hh) {
                 const uint64_t base = ((uint64_t)b * H + hh) * D;
                 const double x0 = (double)ld_elem<DT>(P, base + i0);
                 const double x1 = (double)ld_elem<DT>(P, base + i1);
@@ -849,11 +837,15 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != ns - 1) return;
     // merge (log2 domain): M = max m_i, Ls = sum l_i 2^{m_i - M}, o = sum acc_i 2^{m_i - M} / Ls.
-    // Lane i < ns reads split i's (m, l); every lane then reads its DPL dims
-    // of all splits in one batch and adds them in split order.
+    // Lane i < ns reads split i's (m, l).  A record's acc is CH = D/4 chunks
+    // of 16 bytes, so one load instruction covers SPI = 64/CH splits: lane l
+    // reads chunk l % CH of split l / CH (+ SPI per instruction), up to 16
+    // instructions in flight; each lane adds its splits in order, then the
+    // SPI lane groups are added in a fixed tree.
     const uint8_t* p0 = (const uint8_t*)((const float*)(u.scratch + COUNTER_AREA) + (uint64_t)(t - sp) * PSTRIDE);
-    constexpr uint32_t DPL = D / 64u;  // dims per lane
-    constexpr uint32_t MAXS = 8;       // splits per batch of loads
+    constexpr uint32_t CH = D / 4u;
+    constexpr uint32_t SPI = 64u / CH;
+    constexpr uint32_t NB = 16;  // load instructions per batch
     float mi = -INFINITY, li = 0.0f;
     if (lane < ns) {
         mi = __uint_as_float(ld4(p0 + (uint64_t)lane * PSTRIDE * 4u));
@@ -861,35 +853,35 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     }
     const float M = wmaxf(mi);
     const float wi = lane < ns ? exp2f(mi - M) : 0.0f;
-    float Ls = 0.0f;
-    float o[DPL];
+    const float Ls = wsum(li * wi);
+    const uint32_t j = lane / CH, cc = lane % CH;
+    const RBuf rp = rbuf(p0, ns * PSTRIDE * 4u);  // splits past ns read zero
+    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (uint32_t i0 = 0; i0 < ns; i0 += NB * SPI) {
+        u32x4 v[NB];
 #pragma unroll
-    for (uint32_t e = 0; e < DPL; ++e) o[e] = 0.0f;
-    for (uint32_t i0 = 0; i0 < ns; i0 += MAXS) {
-        float av[MAXS][DPL];
+        for (uint32_t k = 0; k < NB; ++k)
+            if (i0 + k * SPI < ns) v[k] = rld16(rp, ((i0 + k * SPI + j) * PSTRIDE + 4u + 4u * cc) * 4u);
 #pragma unroll
-        for (uint32_t k = 0; k < MAXS; ++k) {
-            if (i0 + k < ns) {
-#pragma unroll
-                for (uint32_t e = 0; e < DPL; ++e)
-                    av[k][e] = __uint_as_float(ld4(p0 + ((uint64_t)(i0 + k) * PSTRIDE + 4u + lane * DPL + e) * 4u));
-            }
-        }
-#pragma unroll
-        for (uint32_t k = 0; k < MAXS; ++k) {
-            if (i0 + k < ns) {
-                const float w = rlf(wi, (int)(i0 + k));
-                Ls += rlf(li, (int)(i0 + k)) * w;
-#pragma unroll
-                for (uint32_t e = 0; e < DPL; ++e) o[e] += av[k][e] * w;
+        for (uint32_t k = 0; k < NB; ++k) {
+            if (i0 + k * SPI < ns) {
+                const float w = __shfl(wi, (int)((i0 + k * SPI + j) & 63u), 64);  // 0 past ns
+                o[0] += w * __uint_as_float(v[k].x);
+                o[1] += w * __uint_as_float(v[k].y);
+                o[2] += w * __uint_as_float(v[k].z);
+                o[3] += w * __uint_as_float(v[k].w);
             }
         }
     }
-    const float inv = 1.0f / Ls;
 #pragma unroll
-    for (uint32_t e = 0; e < DPL; ++e) {
-        const uint32_t d = lane * DPL + e;
-        st_elem<DTO>(O, d, o[e] * inv);
+    for (uint32_t mm = CH; mm < 64; mm <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], (int)mm, 64);
+    }
+    if (lane < CH) {
+        const float inv = 1.0f / Ls;
+#pragma unroll
+        for (uint32_t e = 0; e < 4; ++e) st_elem<DTO>(O, 4u * cc + e, o[e] * inv);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -898,7 +890,7 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
 // y[1,N] = x[1,K] W[K,N], W row-major.  Unit = (column block, k-split):
 // 16 lanes x 16 bytes cover CPB = 16 VE columns of one row, the four 16-lane
 // rows of the wave take four rows of W per load instruction, and a unit
-// walks GEMV_KC rows in batches of 64 (16 instructions, 16 KiB of bf16 W),
+// walks GEMV_KC (128) rows in batches of 64 (16 instructions, 16 KiB of bf16 W),
 // the next batch loaded before the current one is used.  x[k] comes from a
 // per-batch load of 64 values (one per lane) moved to the using lanes with a
 // lane permute.  The four row groups are summed at the end in a fixed
@@ -1023,22 +1015,37 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != nks - 1) return;
-    // merge: each of the 64 lanes sums CPB/64 columns over the splits in
-    // split order, loading up to 8 splits at a time
+    // merge: each of the 64 lanes sums its NCL = CPB/64 columns over the
+    // splits in split order, the loads of up to 16 splits of all its columns
+    // in flight together
     const uint8_t* pb = (const uint8_t*)part;
-    constexpr uint32_t MAXS = 8;
-    for (uint32_t col = cb * CPB + lane; col < min(N, (cb + 1u) * CPB); col += 64u) {
-        float s = 0.0f;
-        for (uint32_t k0 = 0; k0 < nks; k0 += MAXS) {
-            float pv[MAXS];
+    constexpr uint32_t MAXS = 16;
+    constexpr uint32_t NCL = CPB / 64u;
+    const uint32_t cend = min(N, (cb + 1u) * CPB);
+    float sm[NCL];
 #pragma unroll
-            for (uint32_t k = 0; k < MAXS; ++k)
-                if (k0 + k < nks) pv[k] = __uint_as_float(ld4(pb + ((uint64_t)(k0 + k) * N + col) * 4u));
+    for (uint32_t q = 0; q < NCL; ++q) sm[q] = 0.0f;
+    for (uint32_t k0 = 0; k0 < nks; k0 += MAXS) {
+        float pv[MAXS][NCL];
 #pragma unroll
-            for (uint32_t k = 0; k < MAXS; ++k)
-                if (k0 + k < nks) s += pv[k];
+        for (uint32_t k = 0; k < MAXS; ++k) {
+#pragma unroll
+            for (uint32_t q = 0; q < NCL; ++q) {
+                const uint32_t col = cb * CPB + lane + 64u * q;
+                pv[k][q] = k0 + k < nks && col < cend ? __uint_as_float(ld4(pb + ((uint64_t)(k0 + k) * N + col) * 4u)) : 0.0f;
+            }
         }
-        st_elem<DTO>(Y, col, s);
+#pragma unroll
+        for (uint32_t k = 0; k < MAXS; ++k) {
+#pragma unroll
+            for (uint32_t q = 0; q < NCL; ++q)
+                if (k0 + k < nks) sm[q] += pv[k][q];
+        }
+    }
+#pragma unroll
+    for (uint32_t q = 0; q < NCL; ++q) {
+        const uint32_t col = cb * CPB + lane + 64u * q;
+        if (col < cend) st_elem<DTO>(Y, col, sm[q]);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -137,7 +137,8 @@ def test_sdpa(ctx, out_dt):
     recs, arrays = [], []
     for B, H, D, C, lens in [(1, 4, 128, 4096, [1]), (2, 4, 128, 4096, [255, 257]), (1, 2, 128, 4096, [4096]),
                              (8, 2, 128, 2048, list(RNG.integers(1, 2049, 8))), (2, 3, 64, 600, [256, 513]),
-                             (3, 1, 128, 300, [300, 1, 129])]:
+                             (3, 1, 128, 300, [300, 1, 129]), (1, 2, 128, 16384, [16384]),
+                             (2, 1, 128, 9000, [8500, 7937]), (1, 3, 64, 10000, [9000])]:
         q = bf16(RNG.standard_normal(B * H * D))
         K, V = bf16(RNG.standard_normal(B * H * C * D)), bf16(RNG.standard_normal(B * H * C * D))
         o = np.zeros(B * H * D, np.float32 if out_dt == W.F32 else np.uint16)
@@ -153,7 +154,8 @@ def test_sdpa(ctx, out_dt):
 def test_gemv(ctx, dt, out_dt):
     say(f"gemv dt={dt} out={out_dt}")
     recs, arrays = [], []
-    for K, N in [(1024, 3072), (3072, 1024), (100, 77), (64, 512), (65, 513), (1, 8)]:
+    for K, N in [(1024, 3072), (3072, 1024), (100, 77), (64, 512), (65, 513), (1, 8), (1000, 200),
+                 (4100, 72)]:
         x = RNG.standard_normal(K).astype(np.float32)
         Wm = (RNG.standard_normal(K * N) * 0.02).astype(np.float32)
         if dt == W.BF16:
