@@ -30,8 +30,10 @@ Printed: one JSON line with micro-ops/s (the headline value), p50/p99
 closed-loop per-op latency, the eager hipLaunchKernel-per-op and hipGraph
 baselines, null-launch cost, host submission cost, element-wise ops/s and
 GB/s per log2-size bucket (in stream order with hazard ordering, and as
-independent ops), the roofline of the executor kernel and the CPU oracle
-timed on a bounded sample of the stream.
+independent ops), the achievable HBM read and copy bandwidth with the op
+bodies' memory instructions (a plain streaming kernel), the roofline of
+the executor kernel and the CPU oracle timed on a bounded sample of the
+stream.
 """
 from __future__ import annotations
 
@@ -134,12 +136,17 @@ def main():
     ap.add_argument("--waves", type=int, default=1, help="wave64s per workgroup (one workgroup per CU)")
     ap.add_argument("--ring", type=int, default=256,
                     help="ring entries: descriptors in flight, which is also the window of hazard tracking")
+    ap.add_argument("--units-per-wave", type=int, default=0, choices=(0, 1, 2),
+                    help="units a worker wave holds at once (2 lets a ready unit overtake a waiting one); "
+                         "0: 2 for decode and rows, else 1")
     ap.add_argument("--num-wgs", type=int, default=0,
                     help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
     ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop (mixed workload)")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
+    if args.units_per_wave == 0:
+        args.units_per_wave = 2 if args.workload in ("decode", "rows") else 1
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the dispatcher is a "
               "single-device path; the design notes describe how it would shard.", file=sys.stderr)
@@ -167,8 +174,21 @@ def main():
     # dispatches would otherwise queue it behind the executor)
     chain_buf = torch.zeros(256, dtype=torch.float32, device="cuda")
     one_buf = torch.ones(256, dtype=torch.float32, device="cuda")
+    # achievable HBM bandwidth with the op bodies' memory instructions (1 GiB
+    # read and copy), measured before the executor is resident
+    pb = 1 << 30
+    p_src = torch.empty(pb, dtype=torch.uint8, device="cuda").fill_(7)
+    p_dst = torch.empty(pb, dtype=torch.uint8, device="cuda")
     torch.cuda.current_stream().synchronize()
-    ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring, num_wgs=args.num_wgs)
+    sp0 = torch.cuda.current_stream().cuda_stream
+    hbm_probe = {"bytes": pb,
+                 "read_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 0, 5, sp0),
+                 "copy_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 1, 5, sp0)}
+    del p_src, p_dst
+    torch.cuda.current_stream().synchronize()
+    log(f"hbm probe: read {hbm_probe['read_gbs']:.0f} GB/s, copy {hbm_probe['copy_gbs']:.0f} GB/s")
+    ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring, num_wgs=args.num_wgs,
+                       units_per_wave=args.units_per_wave)
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     st0 = G.gpuos_stats_get(ctx)
 
@@ -351,12 +371,13 @@ def main():
     # ---- roofline of the executor kernel (one launch = one step)
     mean_launch_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (mean_launch_ms * 1e-3) / 1e9
-    tb = recorded_traffic(args.workload)
+    tb = recorded_traffic(args.workload if args.units_per_wave == 1 else f"{args.workload}/upw2")
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": tb / (mean_launch_ms * 1e-3) / 1e9 if tb else None,
             "traffic_bytes_per_launch": tb,
-            "kernel": "gpuos_executor", "launch_ms": mean_launch_ms, "bytes_per_launch": step_bytes}
+            "kernel": "gpuos_executor_s2" if args.units_per_wave == 2 else "gpuos_executor",
+            "launch_ms": mean_launch_ms, "bytes_per_launch": step_bytes}
 
     cpu = None
     if not args.no_cpu and fill == "host":
@@ -390,7 +411,8 @@ def main():
         "dtype": "f32 (bf16 operands computed in f32)",
         "data": "synthetic",
         "config": {"workload": wdesc, "descriptors_per_step": nd, "waves_per_wg": args.waves,
-                   "num_wgs": st["num_wgs"], "ring_entries": st["ring_entries"], "fill": fill},
+                   "num_wgs": st["num_wgs"], "ring_entries": st["ring_entries"],
+                   "units_per_wave": args.units_per_wave, "fill": fill},
         "p50_us": float(np.percentile(lat, 50)),
         "p99_us": float(np.percentile(lat, 99)),
         "dispatch_interval_us_nop": nop_s / len(nop) * 1e6,
@@ -404,6 +426,7 @@ def main():
         "host_blocked_ns_per_desc": st_end["ns_blocked"] / max(1, st_end["submitted"]),
         "host_annotate_ns_per_desc": st_end["ns_annotate"] / max(1, st_end["submitted"]),
         "size_buckets": buckets,
+        "hbm_probe": hbm_probe,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

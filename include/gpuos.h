@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 1
+#define GPUOS_ABI_VERSION 2
 
 /* ---------------------------------------------------------------- errors */
 #define GPUOS_OK 0
@@ -154,6 +154,11 @@ typedef struct gpuos_init_params {
     uint64_t scratch_bytes;     /* device scratch for split ops; 0 -> 256 MiB */
     uint32_t unit_queue_log2;   /* log2 of unit-queue entries, 12..24; 0 -> 20 */
     uint32_t spin_limit_ms;     /* dependency-wait limit before ST_SPIN; 0 -> 20000 */
+    uint32_t units_per_wave;    /* units a worker wave holds at once, 1 or 2; 0 -> 1.
+                                   With 2 a ready unit overtakes one still waiting for
+                                   its dependencies (helps streams of long bodies, such
+                                   as decode attention), but each wave holds two claims
+                                   (slower on long dependency chains of short ops) */
 } gpuos_init_params;
 
 /* Allocate the ring (fine-grained coherent host memory), the device tables
@@ -306,6 +311,18 @@ int gpuos_graph_destroy(void* graph_exec);
  * *ns_launch_sync = mean time of launch + hipStreamSynchronize. */
 int gpuos_null_launch_bench(void* hip_stream, uint32_t n, double* ns_per_launch_async,
                             double* ns_launch_sync);
+
+/* Achievable HBM bandwidth with the memory instructions the op bodies use
+ * (device-scope 16-byte loads, write-through stores), one workgroup of four
+ * waves per CU: mode 0 reads `bytes` at src (dst: device memory of at least
+ * 4 KiB, written only in the unlikely case that the xor of the data equals a
+ * fixed value), mode 1 copies `bytes` from src to dst (device memory, no
+ * overlap).  bytes: a multiple of 16, 4 KiB to 1 GiB.  One untimed launch,
+ * then `reps` launches between two events on hip_stream; *gbs = bytes moved
+ * (read, or read + written) per second / 1e9.  Blocks until done; run it
+ * while no executor is resident.  Errors: E_INVAL, E_HIP. */
+int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps, void* hip_stream,
+                    double* gbs);
 
 /* ABI version of the loaded library. */
 int gpuos_abi_version(void);

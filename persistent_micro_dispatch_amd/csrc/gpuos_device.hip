@@ -57,10 +57,12 @@ constexpr uint64_t NO_SCRATCH = ~0ull;
 // unfinished unit is unclaimed, every claimed unit is older, hence finished,
 // and a wave with a free slot claims it; if it is claimed, its holder finds
 // it ready.  No wave waits on one unit alone.
-constexpr uint32_t SLOTS = 1;
+// SLOTS is 1 or 2 (gpuos_init_params.units_per_wave): with one, a wave
+// claims its next unit only after running the current one; two let a ready
+// unit overtake one that waits, at the price of holding two claims.
 constexpr uint32_t SL_FREE = 0, SL_CLAIMED = 1, SL_WAIT = 2;
 
-template <class T>
+template <uint32_t SLOTS, class T>
 __device__ __forceinline__ T pick(const T* v, uint32_t r) {
     T x = v[0];
 #pragma unroll
@@ -68,6 +70,7 @@ __device__ __forceinline__ T pick(const T* v, uint32_t r) {
     return x;
 }
 
+template <uint32_t SLOTS>
 __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
     DevCtl* C = A.dctl;
     uint64_t n_units = 0, n_depw = 0;
@@ -128,9 +131,9 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             if (ready && sseq[k] < rseq) { r = k; rseq = sseq[k]; rstatus = stat; }
         }
         if (r < SLOTS) {
-            const uint64_t w = pick(sw, r);
-            const uint64_t seq = rseq, u = pick(su, r), t_claim = pick(tclaim, r);
-            const uint32_t tile = pick(stile, r);
+            const uint64_t w = pick<SLOTS>(sw, r);
+            const uint64_t seq = rseq, u = pick<SLOTS>(su, r), t_claim = pick<SLOTS>(tclaim, r);
+            const uint32_t tile = pick<SLOTS>(stile, r);
             const uint64_t slot = seq & A.mask;
             Unit U;
             const uint64_t w0 = rl64(w, 0), w6 = rl64(w, 6), w7 = rl64(w, 7);
@@ -483,15 +486,27 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     }
 }
 
-extern "C" __global__ void __launch_bounds__(256) gpuos_executor(ExecArgs A) {
-    __shared__ uint64_t lds[64 * 16 + 72];
+template <uint32_t SLOTS>
+__device__ __forceinline__ void executor_body(const ExecArgs& A, uint64_t* lds) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     if (blockIdx.x == 0 && wave == 0) fetcher_loop(A, lane, lds, lds + 64 * 16);
-    else worker_loop(A, lane);
+    else worker_loop<SLOTS>(A, lane);
     if (lane == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
         __hip_atomic_fetch_add(&A.hctl->exited, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
+}
+
+// one unit per worker wave
+extern "C" __global__ void __launch_bounds__(256) gpuos_executor(ExecArgs A) {
+    __shared__ uint64_t lds[64 * 16 + 72];
+    executor_body<1>(A, lds);
+}
+
+// two units per worker wave
+extern "C" __global__ void __launch_bounds__(256) gpuos_executor_s2(ExecArgs A) {
+    __shared__ uint64_t lds[64 * 16 + 72];
+    executor_body<2>(A, lds);
 }
 
 // ------------------------------------------------------------ eager kernels
@@ -520,15 +535,60 @@ extern "C" __global__ void __launch_bounds__(256) gpuos_eager_kernel(gpuos_desc 
 
 extern "C" __global__ void gpuos_null_kernel() {}
 
+// ------------------------------------------------------------- HBM probe
+// Achievable bandwidth with the memory instructions the op bodies use
+// (device-scope 16-byte buffer loads, write-through stores): a grid-stride
+// read (COPY = false; the xor of the data goes to sink only if it equals a
+// magic value, so the loads cannot be dropped) or copy of n bytes, n a
+// multiple of 16.  Each lane keeps PROBE_U loads in flight.
+constexpr uint32_t PROBE_U = 16;
+template <bool COPY>
+__global__ void __launch_bounds__(256) gpuos_hbm_probe_kernel(const uint8_t* src, uint8_t* dst, uint32_t n) {
+    const RBuf rs = rbuf(src, n);
+    const WBuf wd = wbuf(dst, COPY ? n : 4096u);
+    const uint64_t T = (uint64_t)gridDim.x * blockDim.x;
+    const uint64_t tid = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t x = 0;
+    for (uint64_t base = tid * 16u; base < n; base += T * 16u * PROBE_U) {
+        u32x4 v[PROBE_U];
+#pragma unroll
+        for (uint32_t k = 0; k < PROBE_U; ++k) {
+            const uint64_t off = base + (uint64_t)k * T * 16u;
+            v[k] = rld16(rs, off < n ? (uint32_t)off : n);  // at n: outside the window, reads zero
+        }
+#pragma unroll
+        for (uint32_t k = 0; k < PROBE_U; ++k) {
+            const uint64_t off = base + (uint64_t)k * T * 16u;
+            if constexpr (COPY) {
+                if (off < n) wst16(wd, (uint32_t)off, v[k]);
+            } else {
+                x ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+            }
+        }
+    }
+    if constexpr (!COPY) {
+        if (x == 0x9E3779B9u) wst16(wd, (uint32_t)(tid & 255u) * 16u, u32x4{x, x, x, x});
+    }
+}
+
 // ------------------------------------------------------ host-side launchers
-hipError_t launch_executor(const ExecArgs& a, uint32_t grid, uint32_t block, hipStream_t s) {
-    hipLaunchKernelGGL(gpuos_executor, dim3(grid), dim3(block), 0, s, a);
+hipError_t launch_executor(const ExecArgs& a, uint32_t slots, uint32_t grid, uint32_t block, hipStream_t s) {
+    if (slots == 2) hipLaunchKernelGGL(gpuos_executor_s2, dim3(grid), dim3(block), 0, s, a);
+    else hipLaunchKernelGGL(gpuos_executor, dim3(grid), dim3(block), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_eager(const gpuos_desc& d, uint32_t kind, uint32_t ntiles, uint8_t* scratch, hipStream_t s) {
     const uint32_t grid = (ntiles + 3u) / 4u;
     hipLaunchKernelGGL(gpuos_eager_kernel, dim3(grid), dim3(256), 0, s, d, kind, ntiles, scratch);
+    return hipGetLastError();
+}
+
+hipError_t launch_hbm_probe(const void* src, void* dst, uint32_t n, bool copy, uint32_t grid, hipStream_t s) {
+    if (copy)
+        hipLaunchKernelGGL(gpuos_hbm_probe_kernel<true>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst, n);
+    else
+        hipLaunchKernelGGL(gpuos_hbm_probe_kernel<false>, dim3(grid), dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst, n);
     return hipGetLastError();
 }
 

@@ -34,9 +34,10 @@
 #endif
 
 namespace gpuos {
-hipError_t launch_executor(const ExecArgs& a, uint32_t grid, uint32_t block, hipStream_t s);
+hipError_t launch_executor(const ExecArgs& a, uint32_t slots, uint32_t grid, uint32_t block, hipStream_t s);
 hipError_t launch_eager(const gpuos_desc& d, uint32_t kind, uint32_t ntiles, uint8_t* scratch, hipStream_t s);
 hipError_t launch_null(hipStream_t s);
+hipError_t launch_hbm_probe(const void* src, void* dst, uint32_t n, bool copy, uint32_t grid, hipStream_t s);
 }  // namespace gpuos
 
 using namespace gpuos;
@@ -279,7 +280,8 @@ int executor_launch(gpuos_ctx* c) {
     if (c->trace && hipMemsetAsync(c->trace, 0, c->trace_cap * sizeof(gpuos_trace_rec), c->exec) != hipSuccess)
         return GPUOS_E_HIP;
     if (hipEventRecord(c->ev_start, c->exec) != hipSuccess) return GPUOS_E_HIP;
-    if (launch_executor(a, c->P.num_wgs, 64u * c->P.waves_per_wg, c->exec) != hipSuccess) return GPUOS_E_HIP;
+    if (launch_executor(a, c->P.units_per_wave, c->P.num_wgs, 64u * c->P.waves_per_wg, c->exec) != hipSuccess)
+        return GPUOS_E_HIP;
     if (hipEventRecord(c->ev_stop, c->exec) != hipSuccess) return GPUOS_E_HIP;
     c->running = true;
     ++c->launches;
@@ -389,6 +391,8 @@ int validate_params(gpuos_init_params& P) {
     if (P.ring_entries < 8 || P.ring_entries > 32768 || (P.ring_entries & (P.ring_entries - 1))) return GPUOS_E_INVAL;
     if (P.waves_per_wg == 0) P.waves_per_wg = 4;
     if (P.waves_per_wg > 4) return GPUOS_E_INVAL;
+    if (P.units_per_wave == 0) P.units_per_wave = 1;
+    if (P.units_per_wave > 2) return GPUOS_E_INVAL;
     if (P.backoff_max == 0) P.backoff_max = 64;
     if (P.backoff_max > 127) return GPUOS_E_INVAL;
     if (P.scratch_bytes == 0) P.scratch_bytes = 256ull << 20;
@@ -966,6 +970,41 @@ int gpuos_null_launch_bench(void* hip_stream, uint32_t n, double* ns_async, doub
     t1 = now_ns();
     if (ns_sync) *ns_sync = (double)(t1 - t0) / m;
     return GPUOS_OK;
+}
+
+int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps, void* hip_stream,
+                    double* gbs) {
+    if (!src || !dst || bytes == 0 || (bytes & 15u) || bytes > (1ull << 30) || mode > 1 || reps == 0)
+        return GPUOS_E_INVAL;
+    if (mode == 0 && bytes < 4096) return GPUOS_E_INVAL;
+    hipStream_t s = (hipStream_t)hip_stream;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return GPUOS_E_HIP;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess) return GPUOS_E_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return GPUOS_E_HIP;
+    }
+    int rc = GPUOS_OK;
+    const bool copy = mode == 1;
+    float ms = 0.0f;
+    if (launch_hbm_probe(src, dst, (uint32_t)bytes, copy, (uint32_t)cus, s) != hipSuccess ||
+        hipEventRecord(e0, s) != hipSuccess) {
+        rc = GPUOS_E_HIP;
+    } else {
+        for (uint32_t i = 0; i < reps && rc == GPUOS_OK; ++i)
+            if (launch_hbm_probe(src, dst, (uint32_t)bytes, copy, (uint32_t)cus, s) != hipSuccess) rc = GPUOS_E_HIP;
+        if (rc == GPUOS_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                               hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            rc = GPUOS_E_HIP;
+    }
+    if (rc == GPUOS_OK && gbs) *gbs = ms > 0.0f ? (copy ? 2.0 : 1.0) * (double)bytes * reps / (ms * 1e-3) / 1e9 : 0.0;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    return rc;
 }
 
 }  // extern "C"

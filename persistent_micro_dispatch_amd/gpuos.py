@@ -80,7 +80,8 @@ class InitParams(ctypes.Structure):
                 ("num_wgs", ctypes.c_uint32), ("waves_per_wg", ctypes.c_uint32),
                 ("backoff_max", ctypes.c_uint32), ("flags", ctypes.c_uint32),
                 ("hip_stream", ctypes.c_void_p), ("scratch_bytes", ctypes.c_uint64),
-                ("unit_queue_log2", ctypes.c_uint32), ("spin_limit_ms", ctypes.c_uint32)]
+                ("unit_queue_log2", ctypes.c_uint32), ("spin_limit_ms", ctypes.c_uint32),
+                ("units_per_wave", ctypes.c_uint32)]
 
 
 class Stats(ctypes.Structure):
@@ -102,6 +103,7 @@ EXPORTS = [
     "gpuos_query", "gpuos_pause", "gpuos_resume", "gpuos_shutdown", "gpuos_stats_get",
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
     "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_trace_read",
+    "gpuos_hbm_probe",
 ]
 
 TRACE_DTYPE = np.dtype([("seq", "<u8"), ("tile", "<u4"), ("hw", "<u4"), ("t_claim", "<u8"), ("t_ready", "<u8"),
@@ -138,6 +140,7 @@ def lib():
         "gpuos_trace_read": ([vp, vp, u64, ctypes.POINTER(u64)], ctypes.c_int),
         "gpuos_null_launch_bench": ([vp, u32, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "gpuos_hbm_probe": ([vp, vp, u64, u32, u32, vp, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -180,9 +183,9 @@ atexit.register(_shutdown_live)
 
 def gpuos_init(device: int = 0, ring_entries: int = 0, num_wgs: int = 0, waves_per_wg: int = 0,
                backoff_max: int = 0, flags: int = 0, hip_stream: int = 0, scratch_bytes: int = 0,
-               unit_queue_log2: int = 0, spin_limit_ms: int = 0) -> int:
+               unit_queue_log2: int = 0, spin_limit_ms: int = 0, units_per_wave: int = 0) -> int:
     p = InitParams(device, ring_entries, num_wgs, waves_per_wg, backoff_max, flags,
-                   hip_stream or None, scratch_bytes, unit_queue_log2, spin_limit_ms)
+                   hip_stream or None, scratch_bytes, unit_queue_log2, spin_limit_ms, units_per_wave)
     out = ctypes.c_void_p()
     _check("gpuos_init", lib().gpuos_init(ctypes.byref(p), ctypes.byref(out)))
     _LIVE.add(out.value)
@@ -281,6 +284,13 @@ def gpuos_null_launch_bench(hip_stream: int, n: int) -> Tuple[float, float]:
     _check("gpuos_null_launch_bench",
            lib().gpuos_null_launch_bench(hip_stream or None, n, ctypes.byref(a), ctypes.byref(s)))
     return a.value, s.value
+
+
+def gpuos_hbm_probe(src: int, dst: int, nbytes: int, mode: int, reps: int, hip_stream: int) -> float:
+    """Achievable GB/s: mode 0 reads nbytes at src, mode 1 copies src -> dst."""
+    g = ctypes.c_double(0)
+    _check("gpuos_hbm_probe", lib().gpuos_hbm_probe(src, dst, nbytes, mode, reps, hip_stream or None, ctypes.byref(g)))
+    return g.value
 
 
 def gpuos_trace_read(ctx: int, max_records: int = 1 << 20) -> np.ndarray:

@@ -35,20 +35,21 @@ def test_pr1_bit_exact(n):
         assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
 
 
-@pytest.mark.parametrize("ring,waves", [(8, 4), (4096, 1)])
-def test_pr1_bit_exact_small_ring_and_one_wave(ring, waves):
+@pytest.mark.parametrize("ring,waves,upw", [(8, 4, 1), (4096, 1, 1), (8, 4, 2), (64, 1, 2)])
+def test_pr1_bit_exact_small_ring_and_one_wave(ring, waves, upw):
     s = W.make_pr1()
     s.bursts = np.full(125, 8)
-    say(f"pr1 ring={ring} waves={waves}")
-    gpu, orc = _final_pools(s, 1000, ring_entries=ring, waves_per_wg=waves)
+    say(f"pr1 ring={ring} waves={waves} units_per_wave={upw}")
+    gpu, orc = _final_pools(s, 1000, ring_entries=ring, waves_per_wg=waves, units_per_wave=upw)
     for i, b in enumerate(s.buffers):
         assert bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype).all()
 
 
-def test_elementwise_exact_ops_bit_exact():
+@pytest.mark.parametrize("upw", [1, 2])
+def test_elementwise_exact_ops_bit_exact(upw):
     s = W.make_elementwise(n_desc=5000, ops=(W.OP_ADD, W.OP_MUL, W.OP_RELU))
-    say("elementwise exact 5000")
-    gpu, orc = _final_pools(s, len(s))
+    say(f"elementwise exact 5000, units_per_wave={upw}")
+    gpu, orc = _final_pools(s, len(s), units_per_wave=upw)
     for i, b in enumerate(s.buffers):
         eq = bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype)
         assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
@@ -78,13 +79,17 @@ def test_rows_stream_verify():
     _report("rows", res)
 
 
-def test_decode_stream_verify():
+@pytest.mark.parametrize("upw", [1, 2])
+def test_decode_stream_verify(upw):
     s = W.make_decode(steps=4, layers=2, heads=8, capacity=512, l_min=100, n_triples=4, n_out=16)
-    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs)
+    say(f"decode verify, units_per_wave={upw}")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, units_per_wave=upw)
     _report("decode", res)
 
 
-def test_mixed_stream_verify():
+@pytest.mark.parametrize("upw", [1, 2])
+def test_mixed_stream_verify(upw):
     s = W.make_mixed(tokens=2, layers=2, capacity=256, l0_range=(32, 200))
-    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs)
+    say(f"mixed verify, units_per_wave={upw}")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, units_per_wave=upw)
     _report("mixed", res)

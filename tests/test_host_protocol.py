@@ -28,7 +28,7 @@ def test_library_exports_every_declared_entry_point():
     L = G.lib()
     for name in declared:
         assert hasattr(L, name), name
-    assert G.gpuos_abi_version() == 1
+    assert G.gpuos_abi_version() == 2
 
 
 def _ranges(recs):
@@ -314,3 +314,12 @@ def test_bad_init_params():
         G.gpuos_init(flags=G.GPUOS_INIT_LOOPBACK, ring_entries=100)
     with pytest.raises(G.GpuosError):
         G.gpuos_init(flags=G.GPUOS_INIT_LOOPBACK, waves_per_wg=5)
+
+
+def test_hbm_probe_rejects_bad_arguments():
+    # checked before any HIP call
+    lib = G.lib()
+    g = G.ctypes.c_double(0)
+    for src, dst, n, mode, reps in [(0, 64, 4096, 0, 1), (64, 64, 4100, 1, 1), (64, 64, 1024, 0, 1),
+                                    (64, 64, (1 << 30) + 16, 1, 1), (64, 64, 4096, 2, 1), (64, 64, 4096, 1, 0)]:
+        assert lib.gpuos_hbm_probe(src, dst, n, mode, reps, None, G.ctypes.byref(g)) == G.GPUOS_E_INVAL
