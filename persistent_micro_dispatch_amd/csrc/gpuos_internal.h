@@ -136,6 +136,16 @@ struct Plan {
     uint64_t scratch;     // bytes (0 = none); counters occupy the first COUNTER_AREA
 };
 
+// A row-op unit covers as many consecutive rows as fit in 16 KiB of input
+// (at least one, at most 16): claims are the executor's scarcest resource
+// for short rows, so small rows are grouped.
+__host__ __device__ inline uint32_t rows_per_unit(uint32_t h, uint32_t dt) {
+    const uint64_t rb = (uint64_t)h * esz(dt);
+    if (rb == 0 || rb >= 16384u) return 1u;
+    const uint64_t g = 16384u / rb;
+    return g > 16u ? 16u : (uint32_t)g;
+}
+
 // A RoPE unit is one batch row and the heads one wave-wide load of 64 x 16
 // bytes covers, when a head's row of D elements divides 1 KiB; else one head.
 __host__ __device__ inline uint32_t rope_heads_per_unit(uint32_t D, uint32_t dt) {
@@ -176,7 +186,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (d.size > MAX_TILES) return bad();
             if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
             if (d.kind == GPUOS_OP_LAYERNORM && d.size > 0 && (d.aux0 == 0 || d.aux1 == 0)) return bad();
-            p.ntiles = d.size ? (uint32_t)d.size : 1u;
+            p.ntiles = d.size ? (uint32_t)cdiv(d.size, rows_per_unit(d.dim[0], di)) : 1u;
             return p;
         }
         case GPUOS_OP_ROPE:

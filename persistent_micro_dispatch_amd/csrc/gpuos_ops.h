@@ -223,17 +223,21 @@ __device__ __forceinline__ float gelu_f(float x) {
 }
 
 // max / min under a total order: NaN wins, -0 < +0.
+// Written as selects, not early returns: the returns became divergent
+// branches around every element.  Equal operands are identical bit
+// patterns unless they are +0 and -0, so AND of the bits picks +0 for max and
+// OR picks -0 for min.  -inf (max) and +inf (min) are identities.
 __device__ __forceinline__ float tmax(float a, float b) {
-    if (a != a) return a;
-    if (b != b) return b;
-    if (a == b) return (__float_as_uint(a) & 0x80000000u) ? b : a;
-    return a < b ? b : a;
+    const float m = a < b ? b : a;
+    const float z = __uint_as_float(__float_as_uint(a) & __float_as_uint(b));
+    const float r = a == b ? z : m;
+    return a != a ? a : (b != b ? b : r);
 }
 __device__ __forceinline__ float tmin(float a, float b) {
-    if (a != a) return a;
-    if (b != b) return b;
-    if (a == b) return (__float_as_uint(a) & 0x80000000u) ? a : b;
-    return a < b ? a : b;
+    const float m = a < b ? a : b;
+    const float z = __uint_as_float(__float_as_uint(a) | __float_as_uint(b));
+    const float r = a == b ? z : m;
+    return a != a ? a : (b != b ? b : r);
 }
 
 // ------------------------------------------------------------ wave helpers
@@ -364,21 +368,20 @@ __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
 }
 
 // ------------------------------------------------------------------ rows
-// One row of [rows, h] per unit.  Rows up to ROW_MAX_CACHED elements with
-// 16-byte alignment are held in registers (up to 16 chunks of 16 bytes per
-// lane, loaded in one batch together with LayerNorm's gamma and beta for the
-// first LN_PRE chunks; the rest of gamma and beta is loaded after the
-// statistics); others stream from memory in several passes.
+// A unit is rows_per_unit(h) consecutive rows of [rows, h], done one after
+// another.  Rows up to ROW_MAX_CACHED elements with 16-byte alignment are
+// held in registers (up to 16 chunks of 16 bytes per lane, loaded in one
+// batch together with LayerNorm's gamma and beta for the first LN_PRE
+// chunks; the rest of gamma and beta is loaded after the statistics); others
+// stream from memory in several passes.
 template <uint32_t K, uint32_t DT>
-__device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
+__device__ __forceinline__ void row_one(const Unit& u, uint64_t r, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
     constexpr uint32_t VE = 16u / ES;
     constexpr uint32_t KMAX = ROW_MAX_CACHED / VE / 64u;
     constexpr bool RED = (K == GPUOS_OP_SUM || K == GPUOS_OP_MAX || K == GPUOS_OP_MIN);
     constexpr bool LN = (K == GPUOS_OP_LAYERNORM);
     constexpr uint32_t LN_PRE = KMAX / 2;
-    const uint64_t r = u.tile;
-    if (r >= u.size) return;
     const uint32_t h = u.dim[0];
     const uint8_t* X = (const uint8_t*)u.a + r * h * ES;
     uint8_t* O = (uint8_t*)u.out + (RED ? r * ES : r * h * ES);
@@ -408,8 +411,7 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
                 }
         }
         float v[KMAX][VE];
-        float acc = 0.0f, mx = -INFINITY;
-        bool has = false;
+        float acc = K == GPUOS_OP_MAX ? -INFINITY : (K == GPUOS_OP_MIN ? INFINITY : 0.0f), mx = -INFINITY;
 #pragma unroll
         for (uint32_t k = 0; k < KMAX; ++k) {
             if (k < kn) {
@@ -421,9 +423,8 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
                     if constexpr (K == GPUOS_OP_SUM || LN) {
                         acc += x;
                     } else if constexpr (K == GPUOS_OP_MAX || K == GPUOS_OP_MIN) {
-                        const float c = has ? (K == GPUOS_OP_MAX ? tmax(acc, x) : tmin(acc, x)) : x;
+                        const float c = K == GPUOS_OP_MAX ? tmax(acc, x) : tmin(acc, x);
                         acc = valid ? c : acc;
-                        has = has || valid;
                     } else {
                         mx = valid ? fmaxf(mx, x) : mx;
                     }
@@ -435,9 +436,7 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
             acc = wsum(acc);
             if (lane == 0) st_elem<DT>(O, 0, acc);
         } else if constexpr (K == GPUOS_OP_MAX || K == GPUOS_OP_MIN) {
-            // lanes that saw no element take lane 0's value (lane 0 always has one)
-            const float ref = rlf(acc, 0);
-            acc = has ? acc : ref;
+            // lanes that saw no element hold the identity
             acc = K == GPUOS_OP_MAX ? wtmax(acc) : wtmin(acc);
             if (lane == 0) st_elem<DT>(O, 0, acc);
         } else if constexpr (K == GPUOS_OP_SOFTMAX) {
@@ -503,21 +502,17 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
     }
     // streaming path
     if constexpr (RED) {
-        float acc = 0.0f;
-        bool has = false;
+        float acc = K == GPUOS_OP_MAX ? -INFINITY : (K == GPUOS_OP_MIN ? INFINITY : 0.0f);
         for (uint32_t i = lane; i < h; i += 64u) {
             const float x = ld_elem<DT>(X, i);
             if constexpr (K == GPUOS_OP_SUM) acc += x;
-            else if constexpr (K == GPUOS_OP_MAX) acc = has ? tmax(acc, x) : x;
-            else acc = has ? tmin(acc, x) : x;
-            has = true;
+            else if constexpr (K == GPUOS_OP_MAX) acc = tmax(acc, x);
+            else acc = tmin(acc, x);
         }
         if constexpr (K == GPUOS_OP_SUM) {
             acc = wsum(acc);
         } else {
-            const float ref = rlf(acc, 0);  // lane 0 has element 0
-            if (!has) acc = ref;
-            acc = K == GPUOS_OP_MAX ? wtmax(acc) : wtmin(acc);
+            acc = K == GPUOS_OP_MAX ? wtmax(acc) : wtmin(acc);  // lanes without elements hold the identity
         }
         if (lane == 0) st_elem<DT>(O, 0, acc);
     } else if constexpr (K == GPUOS_OP_SOFTMAX) {
@@ -538,6 +533,15 @@ __device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
         for (uint32_t i = lane; i < h; i += 64u)
             st_elem<DT>(O, i, (ld_elem<DT>(X, i) - mean) * rstd * ld_elem<DT>(G, i) + ld_elem<DT>(Bt, i));
     }
+}
+
+
+template <uint32_t K, uint32_t DT>
+__device__ __forceinline__ void row_tile(const Unit& u, uint32_t lane) {
+    const uint32_t g = rows_per_unit(u.dim[0], DT);
+    const uint64_t r0 = (uint64_t)u.tile * g;
+    const uint64_t r1 = r0 + g < u.size ? r0 + g : u.size;
+    for (uint64_t r = r0; r < r1; ++r) row_one<K, DT>(u, r, lane);
 }
 
 // ------------------------------------------------------------------ RoPE

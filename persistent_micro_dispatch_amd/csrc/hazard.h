@@ -24,6 +24,8 @@
 //  - An interval keeps up to MAXR readers; beyond that it keeps the oldest
 //    overflowed reader, and a writer then depends on the whole range from it
 //    (reported through `range_from`).
+//  - Clusters are found through a small direct-mapped cache keyed by the
+//    access's start address, else the map; a merge invalidates the cache.
 //  - A cluster that holds more than SPLIT_AT live intervals (a long-lived
 //    buffer written piece by piece, such as an output arena) is split in two
 //    at an interval boundary, so that inserting an interval never moves more
@@ -34,6 +36,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <deque>
 #include <iterator>
 #include <map>
 #include <vector>
@@ -95,10 +98,15 @@ public:
             if (cp[i] && cp[i]->regs.size() > SPLIT_AT) split(*cp[i], floor);
     }
 
-    void clear() { cl_.clear(); }
+    void clear() {
+        cl_.clear();
+        store_.clear();
+        free_.clear();
+        std::fill(hits_.begin(), hits_.end(), Hit{});
+    }
     size_t size() const {
         size_t n = 0;
-        for (auto& kv : cl_) n += kv.second.regs.size();
+        for (auto& kv : cl_) n += kv.second->regs.size();
         return n;
     }
     size_t clusters() const { return cl_.size(); }
@@ -112,12 +120,46 @@ private:
         uint64_t readers[MAXR];
     };
     struct Cluster {
-        uint64_t lo, hi;  // lo is also the map key
+        uint64_t lo = 0, hi = 0;  // lo is also the map key
         std::vector<Region> regs;  // sorted by lo, disjoint, inside [key, hi)
         size_t prune_at = 64;
+        bool alive = false;
     };
-    std::map<uint64_t, Cluster> cl_;
+    // Clusters live in a pool and are recycled, never freed, so a pointer to
+    // one always points to some cluster object; cl_ maps live ones by start.
+    std::map<uint64_t, Cluster*> cl_;
+    std::deque<Cluster> store_;
+    std::vector<Cluster*> free_;
     uint64_t merges_ = 0;
+    // A direct-mapped cache from an access's start address to its cluster,
+    // checked against the cluster's current span (merges retire clusters,
+    // splits shrink them, recycling reuses them).
+    struct Hit {
+        uint64_t lo = 0;
+        Cluster* c = nullptr;
+    };
+    static constexpr size_t NHIT = 4096;  // 2^12: the hash below keeps 12 bits
+    std::vector<Hit> hits_ = std::vector<Hit>(NHIT);
+
+    Cluster* alloc_cluster() {
+        Cluster* c;
+        if (!free_.empty()) {
+            c = free_.back();
+            free_.pop_back();
+        } else {
+            store_.emplace_back();
+            c = &store_.back();
+        }
+        c->alive = true;
+        c->prune_at = 64;
+        return c;
+    }
+    void retire(Cluster* c) {
+        c->alive = false;
+        c->lo = c->hi = 0;
+        c->regs.clear();
+        free_.push_back(c);
+    }
 
     static Region make(uint64_t lo, uint64_t hi, uint64_t writer) {
         Region r;
@@ -131,12 +173,18 @@ private:
 
     // The cluster containing [lo, hi), created, extended or merged as needed.
     Cluster& cluster_for(uint64_t lo, uint64_t hi) {
+        Hit& h = hits_[(lo * 0x9E3779B97F4A7C15ull) >> 52];  // Fibonacci hash to 12 bits
+        if (h.c && h.lo == lo && h.c->alive && h.c->lo <= lo && h.c->hi >= hi) return *h.c;
         auto it = cl_.upper_bound(lo);
         if (it != cl_.begin()) {
             auto p = std::prev(it);
-            if (p->second.hi > lo) it = p;
+            if (p->second->hi > lo) it = p;
         }
-        if (it != cl_.end() && it->first <= lo && it->second.hi >= hi) return it->second;  // common case
+        if (it != cl_.end() && it->first <= lo && it->second->hi >= hi) {  // common case
+            h.lo = lo;
+            h.c = it->second;
+            return *it->second;
+        }
         // collect every cluster overlapping [lo, hi)
         ++merges_;
         auto first = it;
@@ -144,18 +192,22 @@ private:
         size_t k = 0;
         for (auto j = it; j != cl_.end() && j->first < hi; ++j, ++k) {
             nlo = std::min(nlo, j->first);
-            nhi = std::max(nhi, j->second.hi);
+            nhi = std::max(nhi, j->second->hi);
         }
-        Cluster merged;
-        merged.lo = nlo;
-        merged.hi = nhi;
+        std::vector<Region> regs;
         auto j = first;
         for (size_t q = 0; q < k; ++q) {
-            merged.regs.insert(merged.regs.end(), j->second.regs.begin(), j->second.regs.end());
+            regs.insert(regs.end(), j->second->regs.begin(), j->second->regs.end());
+            retire(j->second);
             j = cl_.erase(j);
         }
-        merged.prune_at = std::max<size_t>(64, 2 * merged.regs.size());
-        return cl_.emplace_hint(j, nlo, std::move(merged))->second;
+        Cluster* m = alloc_cluster();
+        m->lo = nlo;
+        m->hi = nhi;
+        m->regs = std::move(regs);
+        m->prune_at = std::max<size_t>(64, 2 * m->regs.size());
+        cl_.emplace_hint(j, nlo, m);
+        return *m;
     }
 
     // index of the first region with hi > x
@@ -254,21 +306,21 @@ private:
     }
 
     // Prune, and if the cluster is still large move its upper half into a
-    // cluster of its own (map nodes do not move, so other Cluster pointers
-    // stay valid).
+    // cluster of its own (pool entries do not move, so other Cluster
+    // pointers stay valid).
     void split(Cluster& c, uint64_t floor) {
         prune(c, floor);
         if (c.regs.size() <= SPLIT_AT) return;
         const size_t mid = c.regs.size() / 2;
-        Cluster up;
-        up.lo = c.regs[mid].lo;
-        up.hi = c.hi;
-        up.regs.assign(c.regs.begin() + (long)mid, c.regs.end());
-        up.prune_at = std::max<size_t>(64, 2 * up.regs.size());
+        Cluster* up = alloc_cluster();  // the pool is a deque: c stays valid
+        up->lo = c.regs[mid].lo;
+        up->hi = c.hi;
+        up->regs.assign(c.regs.begin() + (long)mid, c.regs.end());
+        up->prune_at = std::max<size_t>(64, 2 * up->regs.size());
         c.regs.resize(mid);
-        c.hi = up.lo;
+        c.hi = up->lo;
         c.prune_at = std::max<size_t>(64, 2 * c.regs.size());
-        cl_.emplace(up.lo, std::move(up));
+        cl_.emplace(up->lo, up);
     }
 
     // drop intervals that carry no live information

@@ -71,7 +71,8 @@ def test_elementwise(ctx, op, dt):
 def test_rows(ctx, op, dt):
     say(f"rows op={W.OP_NAMES[op]} dt={dt}")
     recs, arrays = [], []
-    for rows, h in [(1, 768), (3, 1024), (64, 2048), (5, 4096), (2, 100), (3, 5000), (1, 1)]:
+    for rows, h in [(1, 768), (3, 1024), (64, 2048), (5, 4096), (2, 100), (3, 5000), (1, 1), (37, 256),
+                    (21, 768)]:
         x = (RNG.standard_normal(rows * h) * 2).astype(np.float32)
         if op in (W.OP_MAX, W.OP_MIN) and rows * h > 10:
             x[3] = -0.0

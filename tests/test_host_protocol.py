@@ -323,3 +323,44 @@ def test_hbm_probe_rejects_bad_arguments():
     for src, dst, n, mode, reps in [(0, 64, 4096, 0, 1), (64, 64, 4100, 1, 1), (64, 64, 1024, 0, 1),
                                     (64, 64, (1 << 30) + 16, 1, 1), (64, 64, 4096, 2, 1), (64, 64, 4096, 1, 0)]:
         assert lib.gpuos_hbm_probe(src, dst, n, mode, reps, None, G.ctypes.byref(g)) == G.GPUOS_E_INVAL
+
+
+def test_loopback_respects_hazards_with_merging_ranges():
+    """Random byte ranges in one 1 MiB region, from a few bytes to many KiB,
+    so that clusters of the tracker are created, merged, split and recycled
+    all the time, with the same start addresses recurring (the lookup cache
+    keyed by start address must never return a retired or shrunk cluster)."""
+    rng = np.random.default_rng(11)
+    n = 4000
+    base = 0x20_0000_0000
+    starts = rng.integers(0, 1 << 20, 64) // 16 * 16  # recurring start addresses
+    d = G.new_descs(n)
+    d["op_id"] = G.GPUOS_OP_COPY
+    ranges = []
+    for i in range(n):
+        a = int(starts[rng.integers(64)]) if rng.random() < 0.5 else int(rng.integers(0, 1 << 20))
+        o = int(starts[rng.integers(64)]) if rng.random() < 0.5 else int(rng.integers(0, 1 << 20))
+        size = int(min(rng.choice([16, 256, 4096, 65536]) * rng.random() + 1, (1 << 20) - max(a, o)))
+        d["input_a"][i], d["output"][i], d["size"][i] = base + a, base + o, size
+        if a < o + size and o < a + size:  # a copy's input and output must coincide or not overlap
+            d["output"][i] = base + a
+            o = a
+        ranges.append(((a, a + size, False), (o, o + size, True)))
+    ctx = _loopback()
+    try:
+        first = _run(ctx, d, np.full(n // 16, 16))
+        order = G.gpuos_loopback_order(ctx)
+    finally:
+        assert G.gpuos_shutdown(ctx) == 0
+    pos = np.empty(n, np.int64)
+    idx = np.asarray(order, np.int64) - first
+    assert sorted(idx.tolist()) == list(range(n))
+    pos[idx] = np.arange(n)
+    bad = 0
+    for j in range(n):
+        for i in range(max(0, j - 300), j):
+            if pos[i] < pos[j]:
+                continue
+            if any(l1 < h2 and l2 < h1 and (w1 or w2) for (l1, h1, w1) in ranges[i] for (l2, h2, w2) in ranges[j]):
+                bad += 1
+    assert bad == 0
