@@ -30,7 +30,9 @@ Printed: one JSON line with micro-ops/s (the headline value), p50/p99
 closed-loop per-op latency, the eager hipLaunchKernel-per-op and hipGraph
 baselines, null-launch cost, host submission cost, element-wise ops/s and
 GB/s per log2-size bucket (in stream order with hazard ordering, and as
-independent ops), the achievable HBM read and copy bandwidth with the op
+independent ops), the latency of binding an injected element-wise program
+and its throughput beside the built-in op, the achievable HBM read and copy
+bandwidth with the op
 bodies' memory instructions (a plain streaming kernel), the roofline of
 the executor kernel and the CPU oracle timed on a bounded sample of the
 stream.
@@ -311,6 +313,40 @@ def main():
                 row[key + "_ops_per_s"] = len(idx) / el
                 row[key + "_gbs"] = float(per_op[idx].sum()) / el / 1e9
             buckets[f"2^{b}"] = row
+    # ---- injected operator (an element-wise program bound by a table flip):
+    # registration latency, and add/mul descriptors of the stream run as
+    # built-in ops and as the program a+b / a*b (independent ops)
+    injection = None
+    if args.workload == "elementwise":
+        sel = np.nonzero((recs["op"] == W.OP_ADD) | (recs["op"] == W.OP_MUL))[0][:20000]
+        sub = descs[sel].copy()
+        nbk = np.full(len(sub) // 64, 64, np.uint32)
+        sub = sub[:int(nbk.sum())]
+        fl = G.GPUOS_SUBMIT_BLOCK | G.GPUOS_SUBMIT_NOHAZARD
+        X, P = W.xins, W.program
+        progs = {W.OP_ADD: P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_ADD, 0, 1, 2)]),
+                 W.OP_MUL: P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_MUL, 0, 1, 2)])}
+        t_reg = []
+        for i in range(20):
+            ta = time.perf_counter_ns()
+            assert G.gpuos_register_expr(ctx, 200 + (i & 1), progs[W.OP_ADD if i & 1 else W.OP_MUL]) == 0
+            t_reg.append((time.perf_counter_ns() - ta) / 1e3)
+        assert G.gpuos_register_expr(ctx, 200, progs[W.OP_ADD]) == 0
+        assert G.gpuos_register_expr(ctx, 201, progs[W.OP_MUL]) == 0
+        by = float(W.algorithmic_bytes(recs[sel[:len(sub)]]).sum())
+        row = {"register_us_p50": float(np.median(t_reg)), "descriptors": int(len(sub)),
+               "bytes_per_op": by / max(1, len(sub))}
+        for key, ids in (("builtin", None), ("program", (200, 201))):
+            dd = sub.copy()
+            if ids:
+                dd["op_id"] = np.where(dd["op_id"] == W.OP_ADD, ids[0], ids[1]).astype(np.uint32)
+            ta = time.perf_counter()
+            rc, _, _ = G.gpuos_submit_bursts(ctx, dd, nbk, fl)
+            assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
+            el = time.perf_counter() - ta
+            row[key + "_ops_per_s"] = len(sub) / el
+            row[key + "_gbs"] = by / el / 1e9
+        injection = row
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     chain_ok = float(chain_buf.cpu()[0]) == 5000.0
     st_end = G.gpuos_stats_get(ctx)
@@ -427,6 +463,7 @@ def main():
         "host_annotate_ns_per_desc": st_end["ns_annotate"] / max(1, st_end["submitted"]),
         "size_buckets": buckets,
         "hbm_probe": hbm_probe,
+        "injection": injection,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 2
+#define GPUOS_ABI_VERSION 3
 
 /* ---------------------------------------------------------------- errors */
 #define GPUOS_OK 0
@@ -53,8 +53,9 @@ extern "C" {
 
 /* -------------------------------------------------------- operator kinds */
 /* Built-in operator bodies (digest page, section 3 Q2 "Operator library").
- * At init op_id k is bound to kind k for every built-in kind; op ids from
- * GPUOS_OP_USER upward start empty and can be bound with gpuos_register_op. */
+ * At init op_id k is bound to kind k for every built-in kind except EXPR;
+ * op id 15 and the op ids from GPUOS_OP_USER upward start empty and can be
+ * bound with gpuos_register_op or gpuos_register_expr. */
 enum gpuos_kind {
     GPUOS_OP_NOP = 0,        /* nothing; the analogue of a null kernel */
     GPUOS_OP_ADD = 1,        /* out[i] = a[i] + b[i], i < size */
@@ -71,7 +72,8 @@ enum gpuos_kind {
     GPUOS_OP_SDPA = 12,      /* single-query attention over keys [0, L_b) */
     GPUOS_OP_GEMV = 13,      /* y[N] = x[K] . W[K, N] (W row-major) */
     GPUOS_OP_COPY = 14,      /* byte copy of `size` bytes */
-    GPUOS_KIND_COUNT = 15,
+    GPUOS_OP_EXPR = 15,      /* element-wise program bound by gpuos_register_expr */
+    GPUOS_KIND_COUNT = 16,
     GPUOS_KIND_EMPTY = 0xFFFFFFFFu /* register_op: unbind an op id */
 };
 #define GPUOS_MAX_OPS 256
@@ -176,6 +178,47 @@ int gpuos_init(const gpuos_init_params* params, void** out);
  * call returns use the new entry; earlier ones keep the old one.
  * Errors: E_NOOP (op_id >= GPUOS_MAX_OPS or unknown kind), E_INVAL, E_HIP. */
 int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* consts, uint32_t len);
+
+/* Bind op_id to an element-wise program (kind EXPR).  The pages inject
+ * operators as code compiled at run time from curated templates with
+ * parameters substituted, written to the inactive table slot and enabled by
+ * the version flip (digest page, section 3 Q2 "Dynamic Operator Table";
+ * section 4, core technical barriers).  Here the curated template is an
+ * element-wise register machine and the parameters are its program: the
+ * resident executor interprets it, so a new operator is installed by the
+ * same table write and flip as gpuos_register_op, with no compilation, code
+ * loading or relaunch.
+ *
+ * A descriptor of such an op reads a[i] (and b[i] if the program uses it),
+ * i < size elements of the input dtype, and writes out[i] in the same dtype
+ * (out may coincide with a or b).  For each element the program runs on
+ * four fp32 registers r0..r3 (initially 0) and r0 is the result, rounded to
+ * the dtype (bf16: to nearest even).  Layout (32-bit words):
+ *   word 0: n_instr | n_consts << 8 (1..32 instructions, 0..16 constants);
+ *   words 1..n_instr: instructions, op | dst << 8 | src1 << 12 | src2 << 16
+ *     | const index << 20 (register numbers 0..3);
+ *   then n_consts fp32 constants (bit patterns).
+ * Ops (fp32; + - * / and sqrt correctly rounded, min/max propagate NaN and
+ * order -0 below +0, exp/log/tanh/sigmoid from the hardware's exp2/log2
+ * with errors near 1e-7 relative, absolute where the result is near 0):
+ *   GPUOS_X_LDA d = a[i]; GPUOS_X_LDB d = b[i]; GPUOS_X_CONST d = k[c];
+ *   GPUOS_X_MOV d = s1; ADD, SUB, MUL, DIV, MIN, MAX d = s1 op s2;
+ *   NEG, ABS, EXP, LOG, SQRT, TANH, SIGMOID (1/(1+e^-x)), RELU d = f(s1).
+ * Descriptors submitted after this call returns use the program; earlier
+ * ones keep what they were submitted under.
+ * Errors: E_NOOP (op_id >= GPUOS_MAX_OPS), E_INVAL (malformed program),
+ * E_HIP. */
+enum gpuos_expr_op {
+    GPUOS_X_LDA = 1, GPUOS_X_LDB = 2, GPUOS_X_CONST = 3, GPUOS_X_MOV = 4,
+    GPUOS_X_ADD = 5, GPUOS_X_SUB = 6, GPUOS_X_MUL = 7, GPUOS_X_DIV = 8,
+    GPUOS_X_MIN = 9, GPUOS_X_MAX = 10, GPUOS_X_NEG = 11, GPUOS_X_ABS = 12,
+    GPUOS_X_EXP = 13, GPUOS_X_LOG = 14, GPUOS_X_SQRT = 15, GPUOS_X_TANH = 16,
+    GPUOS_X_SIGMOID = 17, GPUOS_X_RELU = 18,
+    GPUOS_X_COUNT = 19
+};
+#define GPUOS_EXPR_MAX_INSTR 32
+#define GPUOS_EXPR_MAX_CONSTS 16
+int gpuos_register_expr(void* ctx, uint32_t op_id, const uint32_t* program, uint32_t n_words);
 
 /* --------------------------------------------------------------- submit */
 #define GPUOS_SUBMIT_BLOCK (1u << 0)     /* wait for free slots instead of E_FULL */

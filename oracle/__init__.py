@@ -51,6 +51,9 @@ def lib():
         for nm in ("orc_max2", "orc_min2"):
             getattr(L, nm).restype = ctypes.c_double
             getattr(L, nm).argtypes = [ctypes.c_double, ctypes.c_double]
+        L.orc_expr_eval.restype = ctypes.c_float
+        L.orc_expr_eval.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
+                                    ctypes.POINTER(ctypes.c_int32)]
         L.orc_record_size.restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -117,6 +120,17 @@ def gelu(x: float) -> float:
 
 def max2(a: float, b: float) -> float:
     return lib().orc_max2(float(a), float(b))
+
+
+def expr_eval(program, a: float, b: float) -> float:
+    """One element of an injected element-wise program (binary32 steps);
+    raises ValueError for a malformed program."""
+    w = np.ascontiguousarray(np.asarray(program, np.uint32))
+    err = ctypes.c_int32(0)
+    v = lib().orc_expr_eval(w.ctypes.data, len(w), a, b, ctypes.byref(err))
+    if err.value:
+        raise ValueError("malformed program")
+    return v
 
 
 def min2(a: float, b: float) -> float:

@@ -39,6 +39,10 @@
  *  - KV append writes K[b,h,L_b-1,:] and V[b,h,L_b-1,:]; the cache is
  *    [B, H, C, D].  SDPA attends one query over keys [0, L_b).
  *  - GEMV: y[n] = sum_k x[k] W[k,n] with W row-major [K, N].
+ *  - An injected operator (the pages' run-time operator injection, digest
+ *    page section 3 Q2 "Dynamic Operator Table") is an element-wise program
+ *    on four binary32 registers, applied per element; its definition is the
+ *    program run step by step in binary32 (orc_expr_eval below).
  *
  * Parity pins: every function here is checked in the CPU test suite against
  * closed forms, invariants, brute force or library routines.
@@ -60,7 +64,7 @@ typedef struct {
 } orc_rec;
 
 enum { ORC_NOP = 0, ORC_ADD, ORC_MUL, ORC_RELU, ORC_GELU, ORC_SUM, ORC_MAX, ORC_MIN,
-       ORC_SOFTMAX, ORC_LAYERNORM, ORC_ROPE, ORC_KV_APPEND, ORC_SDPA, ORC_GEMV, ORC_COPY };
+       ORC_SOFTMAX, ORC_LAYERNORM, ORC_ROPE, ORC_KV_APPEND, ORC_SDPA, ORC_GEMV, ORC_COPY, ORC_EXPR };
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { R_A = 0, R_B, R_OUT, R_AUX0, R_AUX1, R_AUX2 };
 
@@ -152,6 +156,63 @@ double orc_min2(double a, double b) {
     if (isnan(a)) return a;
     if (isnan(b)) return b;
     return lt_total(b, a) ? b : a;
+}
+
+/* ---- injected element-wise programs ----
+ * Program words: w[0] = number of instructions (bits 0-7) | number of
+ * constants (bits 8-15); then one word per instruction: operation (bits
+ * 0-7), destination register (8-11), sources (12-15, 16-19), constant index
+ * (20-27); then the constants as binary32 bit patterns.  Registers r0..r3
+ * start at 0; r0 is the result.  Every step yields a binary32 value: + - *
+ * / and sqrt are the correctly rounded operations (computed in double and
+ * rounded once, which is innocuous for these, Figueroa 1995); exp, log,
+ * tanh and the logistic function are the double functions rounded once to
+ * binary32; min/max as orc_min2/orc_max2; relu as orc_relu; neg and abs
+ * flip and clear the sign. */
+enum { X_LDA = 1, X_LDB, X_CONST, X_MOV, X_ADD, X_SUB, X_MUL, X_DIV, X_MIN, X_MAX, X_NEG, X_ABS,
+       X_EXP, X_LOG, X_SQRT, X_TANH, X_SIGMOID, X_RELU, X_END };
+
+static float to_f32(double v) { return (float)v; }
+
+/* Evaluate the program for one element; *err = 1 for a malformed program. */
+float orc_expr_eval(const uint32_t* w, int64_t n_words, float a, float b, int32_t* err) {
+    float R[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    *err = 1;
+    if (n_words < 1) return 0.0f;
+    const uint32_t ni = w[0] & 0xFFu, nk = (w[0] >> 8) & 0xFFu;
+    if (ni < 1 || ni > 32 || nk > 16 || (w[0] >> 16) != 0 || n_words != 1 + (int64_t)ni + nk) return 0.0f;
+    for (uint32_t i = 0; i < ni; ++i) {
+        const uint32_t ins = w[1 + i];
+        const uint32_t op = ins & 0xFFu, d = (ins >> 8) & 0xFu, s1 = (ins >> 12) & 0xFu, s2 = (ins >> 16) & 0xFu;
+        const uint32_t k = (ins >> 20) & 0xFFu;
+        if (op < X_LDA || op >= X_END || d > 3 || s1 > 3 || s2 > 3 || (ins >> 28) != 0) return 0.0f;
+        if (op == X_CONST && k >= nk) return 0.0f;
+        const double x = R[s1], y = R[s2];
+        float v;
+        switch (op) {
+            case X_LDA: v = a; break;
+            case X_LDB: v = b; break;
+            case X_CONST: memcpy(&v, &w[1 + ni + k], 4); break;
+            case X_MOV: v = R[s1]; break;
+            case X_ADD: v = to_f32(x + y); break;
+            case X_SUB: v = to_f32(x - y); break;
+            case X_MUL: v = to_f32(x * y); break;
+            case X_DIV: v = to_f32(x / y); break;
+            case X_MIN: v = to_f32(orc_min2(x, y)); break;
+            case X_MAX: v = to_f32(orc_max2(x, y)); break;
+            case X_NEG: v = -R[s1]; break;
+            case X_ABS: v = fabsf(R[s1]); break;
+            case X_EXP: v = to_f32(exp(x)); break;
+            case X_LOG: v = to_f32(log(x)); break;
+            case X_SQRT: v = to_f32(sqrt(x)); break;
+            case X_TANH: v = to_f32(tanh(x)); break;
+            case X_SIGMOID: v = to_f32(1.0 / (1.0 + exp(-x))); break;
+            default: v = to_f32(orc_relu(x)); break; /* X_RELU */
+        }
+        R[d] = v;
+    }
+    *err = 0;
+    return R[0];
 }
 
 /* ---- pool access with bounds checks ---- */
@@ -378,6 +439,27 @@ static int op_gemv(const pool_t* P, const orc_rec* r) {
     return 0;
 }
 
+/* injected program: a, b, out of `size` elements; the program's dim[2]
+ * words in aux2 (at the record's aux2 offset); no b -> b reads a */
+static int op_expr(const pool_t* P, const orc_rec* r) {
+    int64_t n = r->size, nw = r->dim[2];
+    int di = r->dtype, dout = r->out_dtype;
+    const uint8_t* a = span(P, r, R_A, n * esize(di));
+    const uint8_t* b = r->buf[R_B] >= 0 ? span(P, r, R_B, n * esize(di)) : a;
+    uint8_t* o = span(P, r, R_OUT, n * esize(dout));
+    const uint8_t* pw = span(P, r, R_AUX2, nw * 4);
+    if (!a || !b || !o || !pw || nw < 1 || nw > 64) return ORC_E_BOUNDS;
+    uint32_t w[64];
+    memcpy(w, pw, (size_t)nw * 4);
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t err = 0;
+        const float v = orc_expr_eval(w, nw, (float)ld(a, di, i), (float)ld(b, di, i), &err);
+        if (err) return ORC_E_OP;
+        st(o, dout, i, (double)v);
+    }
+    return 0;
+}
+
 static int op_copy(const pool_t* P, const orc_rec* r) {
     const uint8_t* a = span(P, r, R_A, r->size);
     uint8_t* o = span(P, r, R_OUT, r->size);
@@ -402,6 +484,7 @@ static int run_one(const pool_t* P, const orc_rec* r) {
         case ORC_SDPA: return op_sdpa(P, r);
         case ORC_GEMV: return op_gemv(P, r);
         case ORC_COPY: return op_copy(P, r);
+        case ORC_EXPR: return op_expr(P, r);
         default: return ORC_E_OP;
     }
 }

@@ -138,7 +138,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             Unit U;
             const uint64_t w0 = rl64(w, 0), w6 = rl64(w, 6), w7 = rl64(w, 7);
             const uint64_t w13 = rl64(w, 13), w14 = rl64(w, 14), w15 = rl64(w, 15);
-            const uint64_t m0 = rl64(w, 16), m1 = rl64(w, 17), m3 = rl64(w, 19);
+            const uint64_t m0 = rl64(w, 16), m1 = rl64(w, 17), m3 = rl64(w, 19), m5 = rl64(w, 21);
             U.seq = seq;
             U.flags = (uint32_t)(w0 >> 32);
             U.tile = tile;
@@ -156,6 +156,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             U.ntiles = (uint32_t)m1;
             U.p0 = __uint_as_float((uint32_t)(m1 >> 32));
             U.scratch = m3 == NO_SCRATCH ? nullptr : A.scratch + (m3 % A.scratch_bytes);
+            U.prog = m5;
             if (rstatus != GPUOS_ST_OK) {
                 status = rstatus;
                 if (lane == 0) {
@@ -363,10 +364,14 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         pin.lensw[1] = dw[14];
         uint32_t kind = KIND_BAD;
         float p0 = 0.0f;
+        uint64_t prog = 0;
+        pin.kflags = 0;
         if (op_id < GPUOS_MAX_OPS) {
             const TableEntry* te = &A.table[(ver & 1u) * GPUOS_MAX_OPS + op_id];
             kind = te->kind;
             p0 = te->p0;
+            pin.kflags = te->flags;
+            prog = te->fn;
         }
         Plan pl;
         if (kind < GPUOS_KIND_COUNT) {
@@ -444,6 +449,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             wst64(mm + 2, ubegin);
             wst64(mm + 3, my_sv);
             wst64(mm + 4, my_mark);
+            wst64(mm + 5, prog);
             wst32(&A.tiles_done[slot], 0u);
             pref[lane] = inc - nt;
         }
@@ -530,6 +536,7 @@ extern "C" __global__ void __launch_bounds__(256) gpuos_eager_kernel(gpuos_desc 
     U.lensw[1] = (uint64_t)d.param.u[2] | ((uint64_t)d.param.u[3] << 32);
     U.p0 = 0.0f;
     U.scratch = scratch;
+    U.prog = 0;
     run_unit(U, lane);
 }
 

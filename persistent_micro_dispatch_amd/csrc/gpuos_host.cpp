@@ -140,15 +140,21 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
             add(d.input_a, sz, false);
             add(d.output, sz, true);
             break;
+        case GPUOS_OP_EXPR:  // b is counted as read whenever it is given
+            add(d.input_a, sz * es, false);
+            add(d.input_b, sz * es, false);
+            add(d.output, sz * eo, true);
+            break;
         default:
             break;
     }
     return n;
 }
 
-PlanIn plan_in(uint32_t kind, const gpuos_desc& d) {
+PlanIn plan_in(uint32_t kind, const gpuos_desc& d, uint32_t kflags = 0) {
     PlanIn p;
     p.kind = kind;
+    p.kflags = kflags;
     p.flags = d.flags;
     p.size = d.size;
     for (int i = 0; i < 4; ++i) p.dim[i] = d.dim[i];
@@ -196,6 +202,7 @@ struct gpuos_ctx {
     uint32_t* tiles_done = nullptr;
     uint64_t* queue = nullptr;
     TableEntry* table = nullptr;
+    uint32_t* prog = nullptr;  // [2][GPUOS_MAX_OPS][PROG_WORDS] element-wise programs
     uint8_t* scratch = nullptr;
     gpuos_trace_rec* trace = nullptr;
     uint64_t trace_cap = 0;
@@ -210,6 +217,7 @@ struct gpuos_ctx {
     HazardTracker hz;
     std::vector<uint64_t> deps;
     TableEntry shadow[2][GPUOS_MAX_OPS];
+    uint32_t shadow_prog[2][GPUOS_MAX_OPS][PROG_WORDS];
     uint32_t version = 0;
     uint64_t flip_seq = 0;  // first seq submitted under the current version
     // errors
@@ -369,9 +377,9 @@ void loopback_main(gpuos_ctx* c) {
             if (op >= GPUOS_MAX_OPS) st = GPUOS_ST_BAD_OP;
             else {
                 std::lock_guard<std::mutex> g(c->lb_mu);
-                const uint32_t kind = c->shadow[p.d.table_version & 1u][op].kind;
-                if (kind >= GPUOS_KIND_COUNT) st = GPUOS_ST_BAD_OP;
-                else st = make_plan(plan_in(kind, p.d)).status;
+                const TableEntry& te = c->shadow[p.d.table_version & 1u][op];
+                if (te.kind >= GPUOS_KIND_COUNT) st = GPUOS_ST_BAD_OP;
+                else st = make_plan(plan_in(te.kind, p.d, te.flags)).status;
             }
             {
                 std::lock_guard<std::mutex> g(c->lb_mu);
@@ -421,7 +429,8 @@ void free_ctx(gpuos_ctx* c) {
     if (c->stamp) (void)hipHostFree(c->stamp);
     if (c->status) (void)hipHostFree(c->status);
     if (c->hctl) (void)hipHostFree(c->hctl);
-    void* dev[] = {c->dctl, c->mirror, c->meta, c->done, c->tiles_done, c->depd, c->queue, c->table, c->scratch, c->trace};
+    void* dev[] = {c->dctl, c->mirror, c->meta, c->done, c->tiles_done, c->depd, c->queue, c->table, c->prog, c->scratch,
+                   c->trace};
     for (void* p : dev)
         if (p) (void)hipFree(p);
     if (c->ev_start) (void)hipEventDestroy(c->ev_start);
@@ -458,7 +467,9 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     c->flip_seq = c->N;
     for (int v = 0; v < 2; ++v)
         for (uint32_t i = 0; i < GPUOS_MAX_OPS; ++i)
-            c->shadow[v][i] = TableEntry{i < GPUOS_KIND_COUNT ? i : (uint32_t)GPUOS_KIND_EMPTY, 0, 0.f, 0.f, 0, 0};
+            c->shadow[v][i] = TableEntry{i < GPUOS_KIND_COUNT && i != GPUOS_OP_EXPR ? i : (uint32_t)GPUOS_KIND_EMPTY,
+                                         0, 0.f, 0.f, 0, 0};
+    memset(c->shadow_prog, 0, sizeof(c->shadow_prog));
     const size_t N = c->N;
     if (c->loopback) {
         c->ring = (gpuos_desc*)aligned_zalloc(N * sizeof(gpuos_desc));
@@ -515,6 +526,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     HIPCHK(hipMalloc((void**)&c->depd, N * 8 * DEPX_WORDS));
     HIPCHK(hipMalloc((void**)&c->queue, (size_t)c->Q * 8));
     HIPCHK(hipMalloc((void**)&c->table, 2 * GPUOS_MAX_OPS * sizeof(TableEntry)));
+    HIPCHK(hipMalloc((void**)&c->prog, sizeof(c->shadow_prog)));
     HIPCHK(hipMalloc((void**)&c->scratch, P.scratch_bytes));
     if (P.flags & GPUOS_INIT_TRACE) {
         c->trace_cap = 1u << 20;
@@ -540,6 +552,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
         HIPCHK(hipMemsetAsync(c->meta, 0, N * sizeof(MirrorMeta), c->aux));
         HIPCHK(hipMemsetAsync(c->scratch, 0, P.scratch_bytes, c->aux));
         HIPCHK(hipMemcpyAsync(c->table, c->shadow, sizeof(c->shadow), hipMemcpyHostToDevice, c->aux));
+        HIPCHK(hipMemcpyAsync(c->prog, c->shadow_prog, sizeof(c->shadow_prog), hipMemcpyHostToDevice, c->aux));
         HIPCHK(hipStreamSynchronize(c->aux));
     }
 #undef HIPCHK
@@ -549,12 +562,12 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     return GPUOS_OK;
 }
 
-int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* consts, uint32_t len) {
-    gpuos_ctx* c = (gpuos_ctx*)ctx;
-    if (!c) return GPUOS_E_INVAL;
-    if (op_id >= GPUOS_MAX_OPS || (kind >= GPUOS_KIND_COUNT && kind != GPUOS_KIND_EMPTY)) return GPUOS_E_NOOP;
-    if (len > 8 || (len && !consts)) return GPUOS_E_INVAL;
-    std::lock_guard<std::mutex> g(c->mu);
+// Write entry `te` (and, for EXPR, its program) for op_id into the inactive
+// table slot, then flip.  The inactive slot is first made a copy of the
+// active one, programs included; every EXPR entry's program address is set
+// to the copy in the new slot, so a slot's entries only ever point into
+// that slot's program area.  Caller holds c->mu.
+static int table_flip(gpuos_ctx* c, uint32_t op_id, TableEntry te, const uint32_t* prog) {
     // Grace period: the slot about to be rewritten was last used by version
     // (version - 1); every descriptor submitted before the current version's
     // flip must have completed (and so been resolved) first.
@@ -565,16 +578,21 @@ int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* cons
         if (now_ns() - t0 > 60000000000ull) return GPUOS_E_TIMEOUT;
         GPUOS_PAUSE();
     }
-    const uint32_t nv = c->version + 1, slot = nv & 1u;
-    TableEntry te{kind, 0, 0.f, 0.f, 0, 0};
-    if (len >= 4) memcpy(&te.p0, consts, 4);
-    if (len >= 8) memcpy(&te.p1, (const char*)consts + 4, 4);
+    const uint32_t nv = c->version + 1, slot = nv & 1u, old = c->version & 1u;
     {
         std::lock_guard<std::mutex> lg(c->lb_mu);
-        memcpy(c->shadow[slot], c->shadow[c->version & 1u], sizeof(c->shadow[0]));
+        memcpy(c->shadow[slot], c->shadow[old], sizeof(c->shadow[0]));
+        memcpy(c->shadow_prog[slot], c->shadow_prog[old], sizeof(c->shadow_prog[0]));
         c->shadow[slot][op_id] = te;
+        if (prog) memcpy(c->shadow_prog[slot][op_id], prog, sizeof(c->shadow_prog[0][0]));
+        for (uint32_t i = 0; i < GPUOS_MAX_OPS; ++i)
+            if (c->shadow[slot][i].kind == GPUOS_OP_EXPR)
+                c->shadow[slot][i].fn = c->prog ? (uint64_t)(c->prog + ((size_t)slot * GPUOS_MAX_OPS + i) * PROG_WORDS) : 0;
     }
     if (!c->loopback) {
+        if (hipMemcpyAsync(c->prog + (size_t)slot * GPUOS_MAX_OPS * PROG_WORDS, c->shadow_prog[slot],
+                           sizeof(c->shadow_prog[0]), hipMemcpyHostToDevice, c->aux) != hipSuccess)
+            return GPUOS_E_HIP;
         if (hipMemcpyAsync(c->table + (size_t)slot * GPUOS_MAX_OPS, c->shadow[slot], sizeof(c->shadow[0]),
                            hipMemcpyHostToDevice, c->aux) != hipSuccess)
             return GPUOS_E_HIP;
@@ -584,9 +602,49 @@ int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* cons
     c->version = nv;
     c->flip_seq = c->next_seq;
     if (getenv("GPUOS_AUDIT"))
-        fprintf(stderr, "gpuos: op %u -> kind %u (version %u, from seq %llu)\n", op_id, kind, nv,
+        fprintf(stderr, "gpuos: op %u -> kind %u (version %u, from seq %llu)\n", op_id, te.kind, nv,
                 (unsigned long long)c->next_seq);
     return GPUOS_OK;
+}
+
+int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* consts, uint32_t len) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c) return GPUOS_E_INVAL;
+    if (op_id >= GPUOS_MAX_OPS || (kind >= GPUOS_KIND_COUNT && kind != GPUOS_KIND_EMPTY)) return GPUOS_E_NOOP;
+    if (kind == GPUOS_OP_EXPR) return GPUOS_E_INVAL;  // a program is bound with gpuos_register_expr
+    if (len > 8 || (len && !consts)) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    TableEntry te{kind, 0, 0.f, 0.f, 0, 0};
+    if (len >= 4) memcpy(&te.p0, consts, 4);
+    if (len >= 8) memcpy(&te.p1, (const char*)consts + 4, 4);
+    return table_flip(c, op_id, te, nullptr);
+}
+
+int gpuos_register_expr(void* ctx, uint32_t op_id, const uint32_t* program, uint32_t n_words) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c || !program || n_words == 0) return GPUOS_E_INVAL;
+    if (op_id >= GPUOS_MAX_OPS) return GPUOS_E_NOOP;
+    const uint32_t w0 = program[0];
+    const uint32_t ni = w0 & 0xFFu, nk = (w0 >> 8) & 0xFFu;
+    if ((w0 >> 16) != 0 || ni == 0 || ni > GPUOS_EXPR_MAX_INSTR || nk > GPUOS_EXPR_MAX_CONSTS ||
+        n_words != 1 + ni + nk)
+        return GPUOS_E_INVAL;
+    uint32_t kflags = ni << 8;
+    uint32_t slot[PROG_WORDS] = {};
+    slot[0] = w0;
+    for (uint32_t i = 0; i < ni; ++i) {
+        const uint32_t w = program[1 + i];
+        const uint32_t op = w & 0xFFu, d = (w >> 8) & 0xFu, s1 = (w >> 12) & 0xFu, s2 = (w >> 16) & 0xFu;
+        const uint32_t k = (w >> 20) & 0xFFu;
+        if (op == 0 || op >= GPUOS_X_COUNT || d > 3 || s1 > 3 || s2 > 3 || (w >> 28) != 0) return GPUOS_E_INVAL;
+        if (op == GPUOS_X_CONST && k >= nk) return GPUOS_E_INVAL;
+        if (op == GPUOS_X_LDB) kflags |= EXPR_USES_B;
+        slot[PROG_INSTR + i] = w;
+    }
+    for (uint32_t i = 0; i < nk; ++i) slot[PROG_CONST + i] = program[1 + ni + i];
+    std::lock_guard<std::mutex> g(c->mu);
+    TableEntry te{GPUOS_OP_EXPR, kflags, 0.f, 0.f, 0, 0};
+    return table_flip(c, op_id, te, slot);
 }
 
 int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t flags, uint64_t* first_seq) {
@@ -607,7 +665,7 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
         const gpuos_desc& d = descs[i];
         uint32_t kind = d.op_id < GPUOS_MAX_OPS ? tab[d.op_id].kind : (uint32_t)GPUOS_KIND_EMPTY;
         if (kind < GPUOS_KIND_COUNT) {
-            const Plan pl = make_plan(plan_in(kind, d));
+            const Plan pl = make_plan(plan_in(kind, d, tab[d.op_id].flags));
             if (pl.status != GPUOS_ST_OK) return GPUOS_E_INVAL;
             if (pl.ntiles > c->Q / 2 || pl.scratch > c->P.scratch_bytes / 2) return GPUOS_E_INVAL;
         } else {
@@ -896,7 +954,7 @@ uint64_t gpuos_eager_scratch_bytes(const gpuos_desc* descs, uint32_t count) {
     uint64_t m = COUNTER_AREA;
     for (uint32_t i = 0; i < count; ++i) {
         const uint32_t kind = descs[i].op_id;
-        if (kind >= GPUOS_KIND_COUNT) continue;
+        if (kind >= GPUOS_KIND_COUNT || kind == GPUOS_OP_EXPR) continue;
         const Plan p = make_plan(plan_in(kind, descs[i]));
         m = std::max<uint64_t>(m, p.scratch);
     }
@@ -909,7 +967,7 @@ int gpuos_eager_submit(const gpuos_desc* descs, uint32_t count, void* hip_stream
     hipStream_t s = (hipStream_t)hip_stream;
     for (uint32_t i = 0; i < count; ++i) {
         const gpuos_desc& d = descs[i];
-        if (d.op_id >= GPUOS_KIND_COUNT) return GPUOS_E_INVAL;
+        if (d.op_id >= GPUOS_KIND_COUNT || d.op_id == GPUOS_OP_EXPR) return GPUOS_E_INVAL;  // no table here
         const Plan p = make_plan(plan_in(d.op_id, d));
         if (p.status != GPUOS_ST_OK) return GPUOS_E_INVAL;
         if (p.scratch > 0 && (!scratch || p.scratch > scratch_bytes)) return GPUOS_E_INVAL;

@@ -16,15 +16,25 @@ namespace gpuos {
 // ---------------------------------------------------------------------------
 struct alignas(32) TableEntry {
     uint32_t kind;     // gpuos_kind, or GPUOS_KIND_EMPTY
-    uint32_t flags;    // reserved
+    uint32_t flags;    // EXPR: EXPR_USES_B | n_instr << 8
     float p0;          // kind's default parameter (eps / theta / scale), 0 = built-in
     float p1;          // reserved
-    uint64_t fn;       // reserved for injected code objects (not used by built-ins)
+    uint64_t fn;       // EXPR: device address of this slot's copy of the program
     uint64_t reserved;
 };
 static_assert(sizeof(TableEntry) == 32, "TableEntry is 32 bytes");
 
 constexpr uint32_t KIND_BAD = 0xFEu;  // internal: descriptor rejected on the device
+
+// Element-wise programs (kind EXPR) as the library stores them: one slot of
+// PROG_WORDS 32-bit words per op id and table slot; word 0 = n_instr |
+// n_consts << 8, instructions at PROG_INSTR, constants at PROG_CONST.
+constexpr uint32_t PROG_WORDS = 64;
+constexpr uint32_t PROG_INSTR = 1;
+constexpr uint32_t PROG_CONST = 1 + GPUOS_EXPR_MAX_INSTR;
+static_assert(PROG_CONST + GPUOS_EXPR_MAX_CONSTS <= PROG_WORDS, "program slot");
+static_assert(PROG_WORDS <= 64, "one program word per lane");
+constexpr uint32_t EXPR_USES_B = 1u;
 
 // Per-slot metadata the fetcher writes next to the mirrored descriptor.
 struct alignas(64) MirrorMeta {
@@ -35,7 +45,8 @@ struct alignas(64) MirrorMeta {
     uint64_t ubegin;        // first unit number (this launch's numbering)
     uint64_t scratch_v;     // virtual scratch offset (physical = v % scratch_bytes), or ~0
     uint64_t scratch_mark;  // scratch watermark before this descriptor's allocation
-    uint64_t pad[3];
+    uint64_t prog;          // EXPR: device address of the program
+    uint64_t pad[2];
 };
 static_assert(sizeof(MirrorMeta) == 64, "MirrorMeta is 64 bytes");
 
@@ -97,6 +108,10 @@ constexpr uint32_t EW_TILE_BYTES_GELU = 2048;  // GELU costs ~40 instructions pe
 __host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind) {
     return kind == GPUOS_OP_GELU ? EW_TILE_BYTES_GELU : EW_TILE_BYTES;
 }
+// programs longer than 8 instructions cost as much per element as GELU
+__host__ __device__ constexpr uint32_t expr_tile_bytes(uint32_t kflags) {
+    return ((kflags >> 8) & 0xFFu) > 8u ? EW_TILE_BYTES_GELU : EW_TILE_BYTES;
+}
 constexpr uint32_t COPY_TILE_BYTES = 32768;
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
 constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit
@@ -117,6 +132,7 @@ __host__ __device__ inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b
 // The fields of a descriptor the plan depends on.
 struct PlanIn {
     uint32_t kind, flags;
+    uint32_t kflags;  // the table entry's flags (EXPR: EXPR_USES_B | n_instr << 8)
     uint64_t size;
     uint32_t dim[4];
     uint64_t lensw[2];  // lens[0..7] as packed 16-bit fields (descriptor bytes 104..120)
@@ -241,6 +257,15 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (ncb * nks > MAX_TILES || ncb * 4 > COUNTER_AREA) return bad();
             p.ntiles = (uint32_t)(ncb * nks);
             if (nks > 1) p.scratch = COUNTER_AREA + nks * (uint64_t)N * 4u;
+            return p;
+        }
+        case GPUOS_OP_EXPR: {
+            if (di != dout) return bad();
+            if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
+            if ((d.kflags & EXPR_USES_B) && d.size > 0 && d.b == 0) return bad();
+            uint64_t t = cdiv(d.size, expr_tile_bytes(d.kflags) / esz(di));
+            if (t > MAX_TILES) return bad();
+            p.ntiles = t ? (uint32_t)t : 1u;
             return p;
         }
         case GPUOS_OP_COPY: {

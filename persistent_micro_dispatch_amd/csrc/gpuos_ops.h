@@ -57,6 +57,7 @@ struct Unit {
     uint64_t lensw[2];  // lens[0..7], packed (see lens_at)
     float p0;         // table default parameter
     uint8_t* scratch; // this descriptor's scratch (physical), or null
+    uint64_t prog;    // EXPR: the program (device memory), else 0
 };
 
 // ------------------------------------------------------------------ scalars
@@ -363,6 +364,149 @@ __device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
         for (uint32_t i = lane; i < cnt; i += 64u) {
             if constexpr (RELU16) wst16b(O + 2u * i, (uint16_t)relu_bf16(ld2(A + 2u * i)));
             else st_elem<DT>(O, i, ew_op<K>(ld_elem<DT>(A, i), BIN ? ld_elem<DT>(B, i) : 0.0f));
+        }
+    }
+}
+
+// ------------------------------------------------------------ EXPR ops
+// An element-wise program bound with gpuos_register_expr, interpreted per
+// element on four fp32 registers.  The program (at most PROG_WORDS words)
+// is read once per unit, word i into lane i with device-scope loads, and
+// every instruction is then taken from a lane with readlane, so decoding is
+// wave-uniform.  Tiles are laid out as for the built-in element-wise ops,
+// but chunks are interpreted in a loop (the next chunk's loads issued before
+// the current one is used) rather than unrolled: the interpreter is inlined
+// once per element count, which keeps the executor's code small.
+//
+// exp, log, tanh and the logistic function use the hardware's exp2 and log2
+// instructions (about 1 ulp) with the argument scaled in two parts, so their
+// error stays near 1e-7 relative (absolute where the result is near 0).
+__device__ __forceinline__ float xexp(float x) {
+    // e^x = 2^t * 2^r with t = fl(x log2 e), r the rounding error of t plus
+    // the low part of log2 e; |r| is tiny, so 2^r = 1 + r ln 2
+    // (results below 2^-126 are formed as 2^(t+64) * 2^-64: the
+    // instruction does not produce subnormals)
+    const float t = x * 1.44269504f;
+    const float r = fmaf(x, 1.44269504f, -t) + x * 1.9259629e-8f;
+    const bool sub = t < -126.0f;
+    const float p = __builtin_amdgcn_exp2f(sub ? t + 64.0f : t) * fmaf(r, 0.693147181f, 1.0f);
+    return sub ? p * 5.42101086e-20f : p;
+}
+__device__ __forceinline__ float xlog(float x) {
+    // subnormal arguments are scaled by 2^24 first
+    const bool sub = x > 0.0f && x < 1.17549435e-38f;
+    return __builtin_amdgcn_logf(sub ? x * 16777216.0f : x) * 0.693147181f - (sub ? 16.6355324f : 0.0f);
+}
+__device__ __forceinline__ float xtanh(float x) {
+    const float e = xexp(2.0f * fabsf(x));
+    const float t = 1.0f - 2.0f / (e + 1.0f);
+    return x != x ? x : copysignf(t, x);
+}
+struct XRegs4 {
+    float r[4];
+};
+__device__ __forceinline__ float xsel(const XRegs4& R, uint32_t i) {
+    return i == 0 ? R.r[0] : i == 1 ? R.r[1] : i == 2 ? R.r[2] : R.r[3];
+}
+__device__ __forceinline__ void xput(XRegs4& R, uint32_t i, float v) {
+    R.r[0] = i == 0 ? v : R.r[0];
+    R.r[1] = i == 1 ? v : R.r[1];
+    R.r[2] = i == 2 ? v : R.r[2];
+    R.r[3] = i == 3 ? v : R.r[3];
+}
+__device__ __forceinline__ float xop(uint32_t op, float x, float y, float a, float b, float k) {
+    switch (op) {
+        case GPUOS_X_LDA: return a;
+        case GPUOS_X_LDB: return b;
+        case GPUOS_X_CONST: return k;
+        case GPUOS_X_MOV: return x;
+        case GPUOS_X_ADD: return x + y;
+        case GPUOS_X_SUB: return x - y;
+        case GPUOS_X_MUL: return x * y;
+        case GPUOS_X_DIV: return x / y;
+        case GPUOS_X_MIN: return tmin(x, y);
+        case GPUOS_X_MAX: return tmax(x, y);
+        case GPUOS_X_NEG: return __uint_as_float(__float_as_uint(x) ^ 0x80000000u);
+        case GPUOS_X_ABS: return __uint_as_float(__float_as_uint(x) & 0x7FFFFFFFu);
+        case GPUOS_X_EXP: return xexp(x);
+        case GPUOS_X_LOG: return xlog(x);
+        case GPUOS_X_SQRT: return sqrtf(x);
+        case GPUOS_X_TANH: return xtanh(x);
+        case GPUOS_X_SIGMOID: return 1.0f / (1.0f + xexp(-x));
+        default: return x > 0.0f ? x : (x != x ? x : 0.0f);  // RELU (the host admits no other op)
+    }
+}
+// Run the program on N elements; pw holds program word `lane` in each lane.
+template <uint32_t N>
+__device__ __forceinline__ void xrun(uint32_t pw, uint32_t ni, const float* a, const float* b, float* out) {
+    XRegs4 R[N];
+#pragma unroll
+    for (uint32_t e = 0; e < N; ++e) R[e] = XRegs4{{0.0f, 0.0f, 0.0f, 0.0f}};
+    for (uint32_t i = 0; i < ni; ++i) {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_readlane((int)pw, (int)(PROG_INSTR + i));
+        const uint32_t op = w & 0xFFu, d = (w >> 8) & 3u, s1 = (w >> 12) & 3u, s2 = (w >> 16) & 3u;
+        const float k = __uint_as_float(
+            (uint32_t)__builtin_amdgcn_readlane((int)pw, (int)(PROG_CONST + ((w >> 20) & (GPUOS_EXPR_MAX_CONSTS - 1)))));
+#pragma unroll
+        for (uint32_t e = 0; e < N; ++e) xput(R[e], d, xop(op, xsel(R[e], s1), xsel(R[e], s2), a[e], b[e], k));
+    }
+#pragma unroll
+    for (uint32_t e = 0; e < N; ++e) out[e] = R[e].r[0];
+}
+
+template <uint32_t DT>
+__device__ __forceinline__ void expr_tile(const Unit& u, uint32_t lane) {
+    constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
+    constexpr uint32_t VE = 16u / ES;
+    const uint32_t pw = lane < PROG_WORDS ? ld4((const uint8_t*)u.prog + 4u * lane) : 0u;
+    const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)pw, 0);
+    const uint32_t ni = w0 & 0xFFu;
+    const uint32_t tb = expr_tile_bytes(ni << 8);
+    const uint32_t TILE = tb / ES, CH = tb / 16u / 64u;
+    const uint64_t start = (uint64_t)u.tile * TILE;
+    if (start >= u.size) return;
+    const uint32_t cnt = (uint32_t)(u.size - start < TILE ? u.size - start : TILE);
+    const bool useb = u.b != 0;
+    const uint8_t* A = (const uint8_t*)u.a + start * ES;
+    const uint8_t* B = useb ? (const uint8_t*)u.b + start * ES : A;
+    uint8_t* O = (uint8_t*)u.out + start * ES;
+    const bool aligned = (((u.a | u.out | u.b) & 15ull) == 0);
+    if (aligned) {
+        const uint32_t full = cnt / VE;  // whole 16-byte chunks
+        const RBuf ra = rbuf(A, full * 16u), rb = rbuf(B, full * 16u);
+        const WBuf ob = wbuf(O, full * 16u);
+        const uint32_t rem = full * VE;
+        const bool tl = rem + lane < cnt;
+        float xt = 0.0f, yt = 0.0f;
+        if (tl) {
+            xt = ld_elem<DT>(A, rem + lane);
+            yt = ld_elem<DT>(B, rem + lane);
+        }
+        u32x4 na = rld16(ra, lane * 16u), nb = rld16(rb, lane * 16u);
+#pragma unroll 1
+        for (uint32_t c = 0; c < CH; ++c) {
+            const u32x4 ca = na, cb = nb;
+            // the next chunk (past the tile: outside the window, reads zero)
+            na = rld16(ra, (lane + 64u * (c + 1)) * 16u);
+            nb = rld16(rb, (lane + 64u * (c + 1)) * 16u);
+            __builtin_amdgcn_sched_barrier(0);
+            float x[VE], y[VE], r[VE];
+            unpack<DT>(ca, x);
+            unpack<DT>(cb, y);
+            xrun<VE>(pw, ni, x, y, r);
+            wst16(ob, (lane + 64u * c) * 16u, pack<DT>(r));  // chunks past `full` are dropped
+        }
+        if (tl) {
+            float r;
+            xrun<1>(pw, ni, &xt, &yt, &r);
+            st_elem<DT>(O, rem + lane, r);
+        }
+    } else {
+        for (uint32_t i = lane; i < cnt; i += 64u) {
+            const float x = ld_elem<DT>(A, i), y = ld_elem<DT>(B, i);
+            float r;
+            xrun<1>(pw, ni, &x, &y, &r);
+            st_elem<DT>(O, i, r);
         }
     }
 }
@@ -1090,6 +1234,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, uint32_t lane) {
         case GPUOS_OP_MUL: bf ? ew_tile<GPUOS_OP_MUL, GPUOS_BF16>(u, lane) : ew_tile<GPUOS_OP_MUL, GPUOS_F32>(u, lane); break;
         case GPUOS_OP_RELU: bf ? ew_tile<GPUOS_OP_RELU, GPUOS_BF16>(u, lane) : ew_tile<GPUOS_OP_RELU, GPUOS_F32>(u, lane); break;
         case GPUOS_OP_GELU: bf ? ew_tile<GPUOS_OP_GELU, GPUOS_BF16>(u, lane) : ew_tile<GPUOS_OP_GELU, GPUOS_F32>(u, lane); break;
+        case GPUOS_OP_EXPR: bf ? expr_tile<GPUOS_BF16>(u, lane) : expr_tile<GPUOS_F32>(u, lane); break;
         case GPUOS_OP_SUM: bf ? row_tile<GPUOS_OP_SUM, GPUOS_BF16>(u, lane) : row_tile<GPUOS_OP_SUM, GPUOS_F32>(u, lane); break;
         case GPUOS_OP_MAX: bf ? row_tile<GPUOS_OP_MAX, GPUOS_BF16>(u, lane) : row_tile<GPUOS_OP_MAX, GPUOS_F32>(u, lane); break;
         case GPUOS_OP_MIN: bf ? row_tile<GPUOS_OP_MIN, GPUOS_BF16>(u, lane) : row_tile<GPUOS_OP_MIN, GPUOS_F32>(u, lane); break;

@@ -22,10 +22,14 @@ GPUOS_E_TIMEOUT, GPUOS_E_DEVICE, GPUOS_E_HIP, GPUOS_E_STATE = -4, -5, -6, -7
 GPUOS_ST_OK, GPUOS_ST_BAD_OP, GPUOS_ST_BAD_SHAPE, GPUOS_ST_SPIN = 0, 1, 2, 3
 (GPUOS_OP_NOP, GPUOS_OP_ADD, GPUOS_OP_MUL, GPUOS_OP_RELU, GPUOS_OP_GELU, GPUOS_OP_SUM, GPUOS_OP_MAX,
  GPUOS_OP_MIN, GPUOS_OP_SOFTMAX, GPUOS_OP_LAYERNORM, GPUOS_OP_ROPE, GPUOS_OP_KV_APPEND, GPUOS_OP_SDPA,
- GPUOS_OP_GEMV, GPUOS_OP_COPY) = range(15)
-GPUOS_KIND_COUNT = 15
+ GPUOS_OP_GEMV, GPUOS_OP_COPY, GPUOS_OP_EXPR) = range(16)
+GPUOS_KIND_COUNT = 16
 GPUOS_KIND_EMPTY = 0xFFFFFFFF
 GPUOS_MAX_OPS = 256
+(GPUOS_X_LDA, GPUOS_X_LDB, GPUOS_X_CONST, GPUOS_X_MOV, GPUOS_X_ADD, GPUOS_X_SUB, GPUOS_X_MUL, GPUOS_X_DIV,
+ GPUOS_X_MIN, GPUOS_X_MAX, GPUOS_X_NEG, GPUOS_X_ABS, GPUOS_X_EXP, GPUOS_X_LOG, GPUOS_X_SQRT, GPUOS_X_TANH,
+ GPUOS_X_SIGMOID, GPUOS_X_RELU) = range(1, 19)
+GPUOS_EXPR_MAX_INSTR, GPUOS_EXPR_MAX_CONSTS = 32, 16
 GPUOS_OP_USER = 64
 GPUOS_F32, GPUOS_BF16 = 0, 1
 GPUOS_F_ROPE_HALF = 1 << 8
@@ -103,7 +107,7 @@ EXPORTS = [
     "gpuos_query", "gpuos_pause", "gpuos_resume", "gpuos_shutdown", "gpuos_stats_get",
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
     "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_trace_read",
-    "gpuos_hbm_probe",
+    "gpuos_hbm_probe", "gpuos_register_expr",
 ]
 
 TRACE_DTYPE = np.dtype([("seq", "<u8"), ("tile", "<u4"), ("hw", "<u4"), ("t_claim", "<u8"), ("t_ready", "<u8"),
@@ -141,6 +145,7 @@ def lib():
         "gpuos_null_launch_bench": ([vp, u32, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "gpuos_hbm_probe": ([vp, vp, u64, u32, u32, vp, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "gpuos_register_expr": ([vp, u32, vp, u32], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -198,6 +203,12 @@ def gpuos_register_op(ctx: int, op_id: int, kind: int, consts=None) -> int:
         arr = np.ascontiguousarray(np.asarray(consts, np.float32).reshape(-1))
         buf, n = arr.ctypes.data, arr.nbytes
     return lib().gpuos_register_op(ctx, op_id, kind, buf, n)
+
+
+def gpuos_register_expr(ctx: int, op_id: int, program) -> int:
+    """Bind op_id to an element-wise program (uint32 words, gpuos.h layout)."""
+    w = np.ascontiguousarray(np.asarray(program, np.uint32).reshape(-1))
+    return lib().gpuos_register_expr(ctx, op_id, w.ctypes.data if len(w) else None, len(w))
 
 
 def gpuos_submit(ctx: int, descs: np.ndarray, flags: int = 0) -> Tuple[int, int]:

@@ -67,6 +67,9 @@ def check_record(r, inputs: List[np.ndarray], gpu: List[np.ndarray], orc: List[n
     buf, off = r["buf"], r["off"]
     res = {"op": W.OP_NAMES[op], "ok": True, "worst": 0.0}
     exact = op in (W.OP_NOP, W.OP_ADD, W.OP_MUL, W.OP_RELU, W.OP_MAX, W.OP_MIN, W.OP_KV_APPEND, W.OP_COPY)
+    if op == W.OP_EXPR:
+        pw = inputs[int(buf[W.AUX2])][int(off[W.AUX2]): int(off[W.AUX2]) + 4 * d[2]].copy().view(np.uint32)
+        exact = W.program_is_exact(pw)
     tol = TOL["f32"] if do == W.F32 else TOL["bf16"]
     for (b, o, nbytes) in W.output_ranges(r):
         g = gpu[b][o: o + nbytes]
@@ -86,7 +89,9 @@ def check_record(r, inputs: List[np.ndarray], gpu: List[np.ndarray], orc: List[n
             ok, worst = rel_check(gf, rf, denom + extra / tol, tol)
         elif op == W.OP_SOFTMAX:
             ok, worst = rel_check(gf, rf, np.abs(rf) + extra / tol, tol)
-        elif op == W.OP_LAYERNORM:
+        elif op in (W.OP_LAYERNORM, W.OP_EXPR):
+            # EXPR with exp/log/tanh/sigmoid steps: library functions within a
+            # few ulps, compared on the unit scale like LayerNorm
             ok, worst = rel_check(gf, rf, np.maximum(np.abs(rf), 1.0) + extra / tol, tol)
         elif op == W.OP_SUM:
             h = d[0]

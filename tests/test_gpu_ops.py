@@ -194,3 +194,84 @@ def test_large_descriptors(ctx):
         arrays += [_vals(m, dt), _vals(m, dt), np.zeros_like(_vals(m, dt))]
         recs.append(rec(op, dtype=dt, size=m, a=base, b=base + 1, out=base + 2))
     _run_and_check(ctx, arrays, np.concatenate(recs))
+
+
+# ------------------------------------------------ injected element-wise programs
+def _programs():
+    X, P = W.xins, W.program
+    return {
+        "a+b": (P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_ADD, 0, 1, 2)]), True),
+        "(a-b)/(|b|+1)": (P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_SUB, 0, 1, 2), X(W.X_ABS, 3, 2),
+                             X(W.X_CONST, 2, 0, 0, 0), X(W.X_ADD, 3, 3, 2), X(W.X_DIV, 0, 0, 3)], [1.0]), True),
+        "max(a,-b)*0.5": (P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_NEG, 2, 2), X(W.X_MAX, 0, 1, 2),
+                             X(W.X_CONST, 3, 0, 0, 0), X(W.X_MUL, 0, 0, 3)], [0.5]), True),
+        "sqrt|a|+relu(b)": (P([X(W.X_LDA, 1), X(W.X_ABS, 1, 1), X(W.X_SQRT, 1, 1), X(W.X_LDB, 2),
+                               X(W.X_RELU, 2, 2), X(W.X_ADD, 0, 1, 2)]), True),
+        "min(a,2)*a": (P([X(W.X_LDA, 1), X(W.X_CONST, 2, 0, 0, 0), X(W.X_MIN, 0, 1, 2), X(W.X_MUL, 0, 0, 1)],
+                         [2.0]), True),
+        "sigmoid(a)*b": (P([X(W.X_LDA, 1), X(W.X_SIGMOID, 1, 1), X(W.X_LDB, 2), X(W.X_MUL, 0, 1, 2)]), False),
+        "tanh(a)+b/2": (P([X(W.X_LDA, 1), X(W.X_TANH, 1, 1), X(W.X_LDB, 2), X(W.X_CONST, 3, 0, 0, 0),
+                           X(W.X_MUL, 2, 2, 3), X(W.X_ADD, 0, 1, 2)], [0.5]), False),
+        "exp(-a^2)": (P([X(W.X_LDA, 1), X(W.X_MUL, 1, 1, 1), X(W.X_NEG, 1, 1), X(W.X_EXP, 0, 1)]), False),
+        "log(1+|a|)": (P([X(W.X_LDA, 1), X(W.X_ABS, 1, 1), X(W.X_CONST, 2, 0, 0, 0), X(W.X_ADD, 1, 1, 2),
+                          X(W.X_LOG, 0, 1)], [1.0]), False),
+        "gelu (14 steps)": (P([X(W.X_LDA, 1), X(W.X_MUL, 2, 1, 1), X(W.X_MUL, 2, 2, 1), X(W.X_CONST, 3, 0, 0, 0),
+                               X(W.X_MUL, 2, 2, 3), X(W.X_ADD, 2, 2, 1), X(W.X_CONST, 3, 0, 0, 1),
+                               X(W.X_MUL, 2, 2, 3), X(W.X_TANH, 2, 2), X(W.X_CONST, 3, 0, 0, 2),
+                               X(W.X_ADD, 2, 2, 3), X(W.X_MUL, 2, 2, 1), X(W.X_CONST, 3, 0, 0, 3),
+                               X(W.X_MUL, 0, 2, 3)], [0.044715, 0.7978845608028654, 1.0, 0.5]), False),
+    }
+
+
+@pytest.mark.parametrize("dt", [W.F32, W.BF16])
+def test_expr_programs(ctx, dt):
+    from persistent_micro_dispatch_amd import gpuos as G
+    say(f"expr programs dt={dt}")
+    recs, arrays = [], []
+    for k, (name, (prog, exact)) in enumerate(_programs().items()):
+        op_id = 80 + k
+        assert G.gpuos_register_expr(ctx, op_id, prog) == 0
+        unary = not any((int(w) & 0xFF) == W.X_LDB for w in prog[1:1 + (int(prog[0]) & 0xFF)])
+        for n, sh in [(1, 0), (777, 0), (2053, 1), (70001, 0)]:
+            if exact:
+                a, b = _vals(n + sh, dt), _vals(n + sh, dt)[::-1].copy()
+            else:
+                a = (RNG.standard_normal(n + sh)).astype(np.float32)
+                b = (RNG.standard_normal(n + sh)).astype(np.float32)
+                if dt == W.BF16:
+                    a, b = bf16(a), bf16(b)
+            base = len(arrays)
+            arrays += [a, b, np.zeros_like(a), prog]
+            roles = dict(a=(base, sh * a.itemsize), out=(base + 2, sh * a.itemsize), aux2=base + 3)
+            if not unary:
+                roles["b"] = (base + 1, sh * a.itemsize)
+            recs.append(rec(W.OP_EXPR, dtype=dt, size=n, dim=(0, 0, len(prog), op_id), **roles))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))
+
+
+def test_expr_reregistration_flips_between_descriptors(ctx):
+    """Descriptors submitted before a re-registration run the old program,
+    those after it the new one (the dual-slot table with a version flip)."""
+    from persistent_micro_dispatch_amd import gpuos as G
+    from workloads.gpu import DevicePool, to_descs
+    X, P = W.xins, W.program
+    p1 = P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_ADD, 0, 1, 2)])
+    p2 = P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_MUL, 0, 1, 2)])
+    n = 50000
+    a = (RNG.standard_normal(n)).astype(np.float32)
+    b = (RNG.standard_normal(n)).astype(np.float32)
+    arrays = [a, b, np.zeros_like(a), np.zeros_like(a), p1, p2]
+    r1 = rec(W.OP_EXPR, size=n, dim=(0, 0, len(p1), 90), a=0, b=1, out=2, aux2=4)
+    r2 = rec(W.OP_EXPR, size=n, dim=(0, 0, len(p2), 90), a=0, b=1, out=3, aux2=5)
+    pool = DevicePool(arrays)
+    d = to_descs(np.concatenate([r1, r2]), pool.ptrs)
+    assert G.gpuos_register_expr(ctx, 90, p1) == 0
+    rc, _ = G.gpuos_submit(ctx, d[:1], G.GPUOS_SUBMIT_BLOCK)
+    assert rc == 0
+    assert G.gpuos_register_expr(ctx, 90, p2) == 0  # the first may still be running
+    rc, _ = G.gpuos_submit(ctx, d[1:], G.GPUOS_SUBMIT_BLOCK)
+    assert rc == 0
+    assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 30_000_000_000)[0] == 0
+    assert np.array_equal(pool.download(2).view(np.float32), a + b)
+    assert np.array_equal(pool.download(3).view(np.float32), a * b)

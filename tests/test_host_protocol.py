@@ -28,7 +28,7 @@ def test_library_exports_every_declared_entry_point():
     L = G.lib()
     for name in declared:
         assert hasattr(L, name), name
-    assert G.gpuos_abi_version() == 2
+    assert G.gpuos_abi_version() == 3
 
 
 def _ranges(recs):
@@ -364,3 +364,57 @@ def test_loopback_respects_hazards_with_merging_ranges():
             if any(l1 < h2 and l2 < h1 and (w1 or w2) for (l1, h1, w1) in ranges[i] for (l2, h2, w2) in ranges[j]):
                 bad += 1
     assert bad == 0
+
+
+def test_register_expr_validates_programs():
+    X, P = W.xins, W.program
+    ctx = _loopback()
+    try:
+        good = P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_ADD, 0, 1, 2)])
+        assert G.gpuos_register_expr(ctx, 100, good) == 0
+        assert G.gpuos_register_expr(ctx, 256, good) == G.GPUOS_E_NOOP
+        assert G.gpuos_register_op(ctx, 100, G.GPUOS_OP_EXPR) == G.GPUOS_E_INVAL
+        for bad in [P([X(0, 0)]), P([X(W.X_RELU + 1, 0)]), P([X(W.X_LDA, 4)]), P([X(W.X_MOV, 0, 7)]),
+                    P([X(W.X_CONST, 0, 0, 0, 1)], [1.0]), good[:-1], np.array([0], np.uint32),
+                    P([X(W.X_LDA, 0)] * 33), P([X(W.X_LDA, 0)], [1.0] * 17),
+                    P([X(W.X_LDA, 0) | (1 << 28)])]:
+            assert G.gpuos_register_expr(ctx, 100, bad) == G.GPUOS_E_INVAL
+        # a program that reads b needs b; one that does not may omit it
+        d = G.new_descs(2)
+        d["op_id"] = 100
+        d["size"] = 64
+        d["input_a"], d["output"] = 0x1000, 0x2000
+        assert G.gpuos_submit(ctx, d[:1], G.GPUOS_SUBMIT_BLOCK)[0] == G.GPUOS_E_INVAL
+        assert G.gpuos_register_expr(ctx, 101, P([X(W.X_LDA, 1), X(W.X_EXP, 0, 1)])) == 0
+        d["op_id"] = 101
+        assert G.gpuos_submit(ctx, d, G.GPUOS_SUBMIT_BLOCK)[0] == 0
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 10_000_000_000)[0] == 0
+    finally:
+        assert G.gpuos_shutdown(ctx) == 0
+
+
+def test_loopback_orders_expr_ops_like_binary_ops():
+    """EXPR descriptors read a (and b) and write out: the tracker orders
+    them against the element-wise ops on the same tensors."""
+    s = W.make_elementwise(n_desc=2000)
+    r = s.recs.copy()
+    sel = np.arange(len(r)) % 3 == 0
+    r["op"][sel] = W.OP_EXPR
+    r["dim"][sel, 3] = 120
+    ctx = _loopback()
+    try:
+        X, P = W.xins, W.program
+        assert G.gpuos_register_expr(ctx, 120, P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_SUB, 0, 1, 2)])) == 0
+        ptrs = _fake_ptrs(len(s.buffers))
+        descs = to_descs(r, ptrs)
+        # unary ops have no b: give EXPR descriptors their a as b (the program reads b)
+        m = sel & (descs["input_b"] == 0)
+        descs["input_b"][m] = descs["input_a"][m]
+        first = _run(ctx, descs, s.bursts)
+        order = G.gpuos_loopback_order(ctx)
+    finally:
+        G.gpuos_shutdown(ctx)
+    r2 = r.copy()
+    r2["op"][sel] = W.OP_ADD  # same operand roles for the order check
+    r2["buf"][m, W.B] = r2["buf"][m, W.A]
+    assert _check_order(r2, order, first) == 0

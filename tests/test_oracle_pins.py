@@ -504,3 +504,103 @@ def test_pr1_prefix_matches_numpy_replay():
         nan = np.isnan(v)
         assert np.array_equal(np.isnan(got), nan)
         assert np.array_equal(f32_bits(got)[~nan], f32_bits(v)[~nan])
+
+
+# ------------------------------------------------ injected element-wise programs
+P = W.program
+X = W.xins
+
+
+def _eval_vec(prog, a, b):
+    return np.array([oracle.expr_eval(prog, float(x), float(y)) for x, y in zip(a, b)], np.float32)
+
+
+def test_expr_exact_steps_equal_ieee_binary32():
+    rng = np.random.default_rng(5)
+    a = np.concatenate([rng.standard_normal(300), rng.standard_normal(100) * 1e-39, [0.0, -0.0, 1e38, -1e38]])
+    a = a.astype(np.float32)
+    b = np.concatenate([rng.standard_normal(300), rng.standard_normal(100) * 1e-39, [-0.0, 0.0, 1e38, 3e38]])
+    b = b.astype(np.float32)
+    lda_ldb = [X(W.X_LDA, 1), X(W.X_LDB, 2)]
+    with np.errstate(all="ignore"):
+        cases = [(W.X_ADD, a + b), (W.X_SUB, a - b), (W.X_MUL, a * b), (W.X_DIV, a / b)]
+        for op, ref in cases:
+            got = _eval_vec(P(lda_ldb + [X(op, 0, 1, 2)]), a, b)
+            assert np.array_equal(f32_bits(got), f32_bits(ref)), op
+        got = _eval_vec(P([X(W.X_LDA, 1), X(W.X_ABS, 1, 1), X(W.X_SQRT, 0, 1)]), a, b)
+        assert np.array_equal(f32_bits(got), f32_bits(np.sqrt(np.abs(a))))
+    got = _eval_vec(P([X(W.X_LDA, 1), X(W.X_NEG, 0, 1)]), a, b)
+    assert np.array_equal(f32_bits(got), f32_bits(-a))
+
+
+def test_expr_min_max_relu_match_the_op_definitions():
+    v = np.array([1.0, -2.0, np.nan, 0.0, -0.0, np.inf, -np.inf, 3.5], np.float32)
+    for x in v:
+        for y in v:
+            mx = oracle.expr_eval(P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_MAX, 0, 1, 2)]), float(x), float(y))
+            mn = oracle.expr_eval(P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_MIN, 0, 1, 2)]), float(x), float(y))
+            rmx, rmn = oracle.max2(float(x), float(y)), oracle.min2(float(x), float(y))
+            assert (math.isnan(mx) and math.isnan(rmx)) or f32_bits(np.float32(mx)) == f32_bits(np.float32(rmx))
+            assert (math.isnan(mn) and math.isnan(rmn)) or f32_bits(np.float32(mn)) == f32_bits(np.float32(rmn))
+        r = oracle.expr_eval(P([X(W.X_LDA, 1), X(W.X_RELU, 0, 1)]), float(x), 0.0)
+        rr = oracle.relu(float(x))
+        assert (math.isnan(r) and math.isnan(rr)) or f32_bits(np.float32(r)) == f32_bits(np.float32(rr))
+
+
+def test_expr_transcendentals_are_rounded_double_functions():
+    x = np.linspace(-6, 6, 241).astype(np.float32)
+    pos = np.abs(x) + np.float32(1e-3)
+    for op, fn, arg in [(W.X_EXP, np.exp, x), (W.X_TANH, np.tanh, x), (W.X_LOG, np.log, pos),
+                        (W.X_SIGMOID, lambda t: 1.0 / (1.0 + np.exp(-t)), x)]:
+        got = _eval_vec(P([X(W.X_LDA, 1), X(op, 0, 1)]), arg, arg)
+        ref = fn(arg.astype(np.float64))
+        ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 0.5 * ulp * 1.0001 + 1e-45), op
+
+
+def test_expr_constants_registers_and_composite_gelu():
+    # registers start at zero; constants come from the program's tail
+    assert oracle.expr_eval(P([X(W.X_ADD, 0, 1, 2)]), 5.0, 7.0) == 0.0
+    assert oracle.expr_eval(P([X(W.X_CONST, 0, 0, 0, 1)], [2.0, -3.25]), 0.0, 0.0) == -3.25
+    # tanh-GELU written as a program, step by step in binary32, stays within
+    # a few binary32 ulps of the double definition where nothing cancels
+    k, c = math.sqrt(2 / math.pi), 0.044715
+    prog = P([X(W.X_LDA, 1), X(W.X_MUL, 2, 1, 1), X(W.X_MUL, 2, 2, 1), X(W.X_CONST, 3, 0, 0, 0),
+              X(W.X_MUL, 2, 2, 3), X(W.X_ADD, 2, 2, 1), X(W.X_CONST, 3, 0, 0, 1), X(W.X_MUL, 2, 2, 3),
+              X(W.X_TANH, 2, 2), X(W.X_CONST, 3, 0, 0, 2), X(W.X_ADD, 2, 2, 3), X(W.X_MUL, 2, 2, 1),
+              X(W.X_CONST, 3, 0, 0, 3), X(W.X_MUL, 0, 2, 3)], [c, k, 1.0, 0.5])
+    x = np.linspace(-2, 3, 101).astype(np.float32)
+    got = _eval_vec(prog, x, x)
+    ref = np.array([oracle.gelu(float(t)) for t in x])
+    assert np.all(np.abs(got - ref) <= 8 * np.spacing(np.maximum(np.abs(ref), 1e-3).astype(np.float32)))
+
+
+def test_expr_malformed_programs_are_rejected():
+    good = [X(W.X_LDA, 0)]
+    for words in [P([X(0, 0)]), P([X(W.X_RELU + 1, 0)]), P([X(W.X_LDA, 4)]), P([X(W.X_MOV, 0, 5)]),
+                  P([X(W.X_CONST, 0, 0, 0, 1)], [1.0]), P(good)[:1], np.array([0], np.uint32),
+                  np.array([33], np.uint32), P(good) | np.array([1 << 16, 0], np.uint32)]:
+        with pytest.raises(ValueError):
+            oracle.expr_eval(words, 1.0, 2.0)
+
+
+def test_expr_record_matches_builtin_ops_bit_exactly():
+    """A program a+b (a*b) on bf16 rounds the binary32 result to bf16, which
+    equals one rounding of the exact result (24 >= 2*8+2), so it matches the
+    built-in add (mul) record bit for bit; the same holds in fp32."""
+    rng = np.random.default_rng(8)
+    for dt in (W.F32, W.BF16):
+        n = 1000
+        a = rng.standard_normal(n).astype(np.float32)
+        b = (rng.standard_normal(n) * np.exp(rng.uniform(-20, 20, n))).astype(np.float32)
+        if dt == W.BF16:
+            a, b = bf16(a), bf16(b)
+        for op, xop in ((W.OP_ADD, W.X_ADD), (W.OP_MUL, W.X_MUL)):
+            prog = P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(xop, 0, 1, 2)])
+            zeros = np.zeros_like(a)
+            arrays = [a, b, zeros.copy(), zeros.copy(), prog]
+            recs = np.concatenate([rec(op, dtype=dt, size=n, a=0, b=1, out=2),
+                                   rec(W.OP_EXPR, dtype=dt, size=n, dim=(0, 0, len(prog), 70), a=0, b=1, out=3,
+                                       aux2=4)])
+            out = run(recs, arrays)
+            assert np.array_equal(out[2].view(np.uint8), out[3].view(np.uint8)), (dt, op)

@@ -29,12 +29,37 @@ import numpy as np
 OP_NOP, OP_ADD, OP_MUL, OP_RELU, OP_GELU = 0, 1, 2, 3, 4
 OP_SUM, OP_MAX, OP_MIN, OP_SOFTMAX, OP_LAYERNORM = 5, 6, 7, 8, 9
 OP_ROPE, OP_KV_APPEND, OP_SDPA, OP_GEMV, OP_COPY = 10, 11, 12, 13, 14
+OP_EXPR = 15  # injected element-wise program (program words in AUX2, dim[2] words, op id in dim[3])
 OP_NAMES = {
     OP_NOP: "nop", OP_ADD: "add", OP_MUL: "mul", OP_RELU: "relu", OP_GELU: "gelu",
     OP_SUM: "sum", OP_MAX: "max", OP_MIN: "min", OP_SOFTMAX: "softmax",
     OP_LAYERNORM: "layernorm", OP_ROPE: "rope", OP_KV_APPEND: "kv_append",
-    OP_SDPA: "sdpa", OP_GEMV: "gemv", OP_COPY: "copy",
+    OP_SDPA: "sdpa", OP_GEMV: "gemv", OP_COPY: "copy", OP_EXPR: "expr",
 }
+
+# Injected element-wise programs: instruction codes and encoding (the word
+# layout of gpuos.h and of the oracle; data formatting only, no arithmetic).
+(X_LDA, X_LDB, X_CONST, X_MOV, X_ADD, X_SUB, X_MUL, X_DIV, X_MIN, X_MAX, X_NEG, X_ABS,
+ X_EXP, X_LOG, X_SQRT, X_TANH, X_SIGMOID, X_RELU) = range(1, 19)
+X_EXACT = {X_LDA, X_LDB, X_CONST, X_MOV, X_ADD, X_SUB, X_MUL, X_DIV, X_MIN, X_MAX, X_NEG, X_ABS, X_SQRT,
+           X_RELU}
+
+
+def xins(op: int, d: int = 0, s1: int = 0, s2: int = 0, k: int = 0) -> int:
+    return op | (d << 8) | (s1 << 12) | (s2 << 16) | (k << 20)
+
+
+def program(instrs, consts=()) -> np.ndarray:
+    """Program words: header, instructions, constants (fp32 bit patterns)."""
+    c = np.asarray(consts, np.float32).view(np.uint32)
+    return np.concatenate([np.array([len(instrs) | (len(c) << 8)], np.uint32),
+                           np.asarray(instrs, np.uint32), c]).astype(np.uint32)
+
+
+def program_is_exact(words) -> bool:
+    """True when every instruction is one of the correctly rounded steps."""
+    n = int(words[0]) & 0xFF
+    return all((int(w) & 0xFF) in X_EXACT for w in words[1:1 + n])
 F32, BF16 = 0, 1
 DTYPE_BYTES = {F32: 4, BF16: 2}
 FLAG_ROPE_HALF = 1  # rotate-half pairing (x_i, x_{i+D/2}) instead of adjacent pairs
@@ -498,7 +523,7 @@ def output_ranges(r) -> list:
     size = int(r["size"])
     d = [int(v) for v in r["dim"]]
     buf, off = r["buf"], r["off"]
-    if op in (OP_ADD, OP_MUL, OP_RELU, OP_GELU):
+    if op in (OP_ADD, OP_MUL, OP_RELU, OP_GELU, OP_EXPR):
         return [(int(buf[OUT]), int(off[OUT]), size * eo)]
     if op in (OP_SUM, OP_MAX, OP_MIN):
         return [(int(buf[OUT]), int(off[OUT]), size * eo)]
@@ -535,8 +560,10 @@ def algorithmic_bytes(recs: np.ndarray) -> np.ndarray:
     n = recs["size"].astype(np.int64)
     d0, d1 = recs["dim"][:, 0].astype(np.int64), recs["dim"][:, 1].astype(np.int64)
     out = np.zeros(len(recs), np.int64)
-    m = (op == OP_ADD) | (op == OP_MUL)
+    m = (op == OP_ADD) | (op == OP_MUL) | ((op == OP_EXPR) & (recs["buf"][:, B] >= 0))
     out[m] = (2 * es[m] + eo[m]) * n[m]
+    m = (op == OP_EXPR) & (recs["buf"][:, B] < 0)
+    out[m] = (es[m] + eo[m]) * n[m]
     m = (op == OP_RELU) | (op == OP_GELU)
     out[m] = (es[m] + eo[m]) * n[m]
     m = (op == OP_SUM) | (op == OP_MAX) | (op == OP_MIN)

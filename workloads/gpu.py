@@ -74,7 +74,7 @@ def to_descs(recs: np.ndarray, ptrs: Sequence[int]) -> np.ndarray:
         base = P[np.where(b < 0, len(P) - 1, b)]
         return np.where(b < 0, np.uint64(0), base + recs["off"][:, role].astype(np.uint64))
 
-    d["op_id"] = recs["op"].astype(np.uint32)
+    d["op_id"] = np.where(recs["op"] == W.OP_EXPR, recs["dim"][:, 3], recs["op"]).astype(np.uint32)
     d["flags"] = (recs["dtype"].astype(np.uint32) | (recs["out_dtype"].astype(np.uint32) << 4)
                   | np.where(recs["flags"] & W.FLAG_ROPE_HALF, G.GPUOS_F_ROPE_HALF, 0).astype(np.uint32))
     d["input_a"] = addr(W.A)
