@@ -33,6 +33,14 @@ def test_pr1_bit_exact(n):
     for i, b in enumerate(s.buffers):
         eq = bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype)
         assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
+    if n == 1000:  # and byte for byte the recorded final pool (tests/golden)
+        import hashlib
+        import os
+        h = hashlib.sha256()
+        for a in gpu:
+            h.update(np.ascontiguousarray(a).tobytes())
+        rec_file = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pr1_final_pool.sha256")
+        assert h.hexdigest() == open(rec_file).read().split()[0]
 
 
 @pytest.mark.parametrize("ring,waves,upw", [(8, 4, 1), (4096, 1, 1), (8, 4, 2), (64, 1, 2)])
