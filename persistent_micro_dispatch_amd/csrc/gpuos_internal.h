@@ -114,7 +114,7 @@ __host__ __device__ constexpr uint32_t expr_tile_bytes(uint32_t kflags) {
 }
 constexpr uint32_t COPY_TILE_BYTES = 32768;
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
-constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit
+constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit (fewer for small attention ops)
 constexpr uint32_t GEMV_KC = 128;          // rows of W per GEMV unit
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
@@ -168,6 +168,28 @@ __host__ __device__ inline uint32_t rope_heads_per_unit(uint32_t D, uint32_t dt)
     const uint32_t rb = D * esz(dt);
     if (rb == 0 || rb % 16u != 0 || rb > 1024u || (1024u % rb) != 0) return 1u;
     return 1024u / rb;
+}
+
+// Keys per SDPA unit: SDPA_KT, halved (down to 64) while the op would give
+// fewer than 256 units, as long as no row needs more than 64 splits.  A small
+// attention op (one sequence, few heads) is latency-bound: more, shorter
+// units finish sooner; a large one keeps long units, whose split merges
+// then cost less.
+__host__ __device__ inline uint32_t sdpa_keys_per_unit(uint32_t B, uint32_t H, const uint64_t* lensw) {
+    uint32_t kt = SDPA_KT;
+    while (kt > 64u) {
+        const uint32_t h = kt / 2u;
+        uint64_t units = 0;
+        bool fits = true;
+        for (uint32_t i = 0; i < B; ++i) {
+            const uint32_t L = lens_at(lensw, i);
+            units += (uint64_t)H * ((L + kt - 1u) / kt);
+            fits = fits && (L + h - 1u) / h <= 64u;
+        }
+        if (units >= 256u || !fits) break;
+        kt = h;
+    }
+    return kt;
 }
 
 // a GEMV unit covers 16 lanes x 16 bytes of columns (four rows per load)
@@ -239,7 +261,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             for (uint32_t i = 0; i < B; ++i) {
                 const uint32_t L = lens_at(d.lensw, i);
                 if (L == 0 || L > C) return bad();
-                uint64_t ns = cdiv(L, SDPA_KT);
+                uint64_t ns = cdiv(L, sdpa_keys_per_unit((uint32_t)B, H, d.lensw));
                 if (ns > 64) return bad();  // the split merge reads one split per lane
                 if (ns > 1) split = true;
                 units += ns * H;

@@ -841,7 +841,8 @@ __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
 }
 
 // ------------------------------------------------------------ decode SDPA
-// Unit = (b, h, split of SDPA_KT keys).  One key row of D bf16 is DV = D/8
+// Unit = (b, h, split of kt = sdpa_keys_per_unit keys: 256, or down to 64 for
+// small ops).  One key row of D bf16 is DV = D/8
 // lanes x 16 bytes, so one load instruction covers RPI = 64/DV keys and the
 // wave reads keys in chunks of 8 instructions (8 RPI keys, 16 KiB of K and V
 // for D = 128).  The next chunk's loads are issued before the current chunk
@@ -862,18 +863,19 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t PSTRIDE = D + 4u;  // floats per partial record: m, l, pad, pad, acc[D]
     const uint32_t H = u.dim[0], C = u.dim[2];
     const uint32_t Bn = (uint32_t)u.size;
+    const uint32_t kt = sdpa_keys_per_unit(Bn, H, u.lensw);
     uint32_t t = u.tile, base = 0, b = 0, ns = 1, L = 0;
     for (b = 0; b < Bn; ++b) {
         L = lens_at(u.lensw, b);
-        ns = (L + SDPA_KT - 1) / SDPA_KT;
+        ns = (L + kt - 1) / kt;
         const uint32_t nu = H * ns;
         if (t < base + nu) break;
         base += nu;
     }
     if (b >= Bn) return;
     const uint32_t local = t - base, h = local / ns, sp = local % ns;
-    const uint32_t k0 = sp * SDPA_KT;
-    const uint32_t nk = min(L - k0, SDPA_KT);
+    const uint32_t k0 = sp * kt;
+    const uint32_t nk = min(L - k0, kt);
     const uint64_t bh = (uint64_t)b * H + h;
     const float scale = u.pf[4] != 0.0f ? u.pf[4] : (u.p0 != 0.0f ? u.p0 : 1.0f / sqrtf((float)D));
     const float sl2 = scale * 1.4426950408889634f;  // scores in the log2 domain
