@@ -14,6 +14,8 @@ op body, completion) over one seeded synthetic descriptor stream:
   decode                 25 decode steps x 32 layers x {RoPE, KV append,
                          SDPA}: B in {1,2,4,8}, 32 heads x 128, bf16 KV cache
                          of 4096 per sequence (16 GiB), L in [128, 4096]
+  decode_gqa             the same with 32 query heads sharing 8 key/value
+                         heads (grouped-query attention, 4 GiB of cache)
   copy                   one 1 GiB COPY descriptor (calibrates HBM counters)
   mixed                  10 tokens x 32 layers x 11 ops at hidden 1024 (LN,
                          GEMV 1024x3072, RoPE, KV append, SDPA, add, LN, GEMV
@@ -119,6 +121,11 @@ def make_stream(name):
         s, fill = W.make_decode(steps=25), "device"
         desc = ("attention decoding: 25 decode steps x 32 layers x {RoPE(theta 1e4), KV append, SDPA}; "
                 "B in {1,2,4,8}, 32 heads x 128, bf16 KV cache 4096/sequence, L in [128, 4096] +1 per step")
+    elif name == "decode_gqa":
+        s, fill = W.make_decode(steps=25, kv_heads=8), "device"
+        desc = ("attention decoding with grouped-query attention: 25 decode steps x 32 layers x {RoPE(theta 1e4), "
+                "KV append, SDPA}; B in {1,2,4,8}, 32 query heads sharing 8 key/value heads x 128, bf16 KV cache "
+                "4096/sequence, L in [128, 4096] +1 per step")
     elif name == "mixed":
         s, fill = W.make_mixed(tokens=10), "device"
         desc = ("mixed decode pipeline: 10 tokens x 32 layers x 11 ops at hidden 1024, 8 heads x 128, bf16: "
@@ -140,7 +147,7 @@ def main():
                     help="ring entries: descriptors in flight, which is also the window of hazard tracking")
     ap.add_argument("--units-per-wave", type=int, default=0, choices=(0, 1, 2),
                     help="units a worker wave holds at once (2 lets a ready unit overtake a waiting one); "
-                         "0: 2 for decode and rows, else 1")
+                         "0: 2 for decode, decode_gqa and rows, else 1")
     ap.add_argument("--num-wgs", type=int, default=0,
                     help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
     ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop (mixed workload)")
@@ -148,7 +155,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.units_per_wave == 0:
-        args.units_per_wave = 2 if args.workload in ("decode", "rows") else 1
+        args.units_per_wave = 2 if args.workload in ("decode", "decode_gqa", "rows") else 1
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the dispatcher is a "
               "single-device path; the design notes describe how it would shard.", file=sys.stderr)

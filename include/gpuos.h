@@ -100,12 +100,17 @@ enum gpuos_kind {
  *   SOFTMAX         a = x [size, dim[0]]; output [size, dim[0]].
  *   LAYERNORM       as SOFTMAX; aux[0] = gamma [dim[0]], aux[1] = beta;
  *                   param.f[0] = eps (0 -> the table entry's default).
- *   ROPE            a = q, b = k, both [size=B, dim[0]=H, dim[1]=D], rotated
- *                   in place at position lens[b]-1; param.f[4] = theta
- *                   (0 -> table default, 10000).
+ *   ROPE            a = q [size=B, dim[0]=H, dim[1]=D], b = k [B, Hk, D]
+ *                   with Hk = dim[3] (0 -> H, at most H: fewer key heads
+ *                   under grouped-query attention), rotated in place at
+ *                   position lens[b]-1; param.f[4] = theta (0 -> table
+ *                   default, 10000).
  *   KV_APPEND       a = k, b = v [B, H, D]; aux[0] = K cache, aux[1] = V cache
  *                   [B, H, dim[2]=C, D]; writes row lens[b]-1.
- *   SDPA            a = q [B, H, D]; aux[0] = K, aux[1] = V [B, H, C, D];
+ *   SDPA            a = q [B, H, D]; aux[0] = K, aux[1] = V [B, Hkv, C, D]
+ *                   with Hkv = dim[3] (0 -> H) dividing H: query head h
+ *                   attends with key/value head h / (H / Hkv) (grouped-
+ *                   query attention; Hkv = 1 is multi-query attention);
  *                   output [B, H, D] in the output dtype; keys [0, lens[b]);
  *                   param.f[4] = scale (0 -> 1/sqrt(D)).  D must be 64 or 128;
  *                   lens[b] at most 16384 (64 splits of 256 keys).

@@ -329,12 +329,14 @@ static int op_layernorm(const pool_t* P, const orc_rec* r) {
 
 /* Rotary embedding in place on q and k ([B, H, D] each) at pos = L_b - 1:
  * pair i (i < D/2) turns by angle pos * theta^(-2i/D). */
+/* RoPE on q [B, H, D] and k [B, Hk, D]; Hk = dim[3] (0: H) is the number
+ * of key heads, fewer than the query heads under grouped-query attention. */
 static int op_rope(const pool_t* P, const orc_rec* r) {
-    int64_t B = r->size, H = r->dim[0], D = r->dim[1];
+    int64_t B = r->size, H = r->dim[0], D = r->dim[1], Hk = r->dim[3] > 0 ? r->dim[3] : r->dim[0];
     int dt = r->dtype;
-    if (D <= 0 || (D & 1) || B > 8) return ORC_E_BOUNDS;
+    if (D <= 0 || (D & 1) || B > 8 || Hk > H) return ORC_E_BOUNDS;
     uint8_t* q = span(P, r, R_A, B * H * D * esize(dt));
-    uint8_t* k = span(P, r, R_B, B * H * D * esize(dt));
+    uint8_t* k = span(P, r, R_B, B * Hk * D * esize(dt));
     if (!q || !k) return ORC_E_BOUNDS;
     double theta = r->fparam[0] != 0.0f ? (double)r->fparam[0] : 10000.0;
     int half = (r->flags & 1) != 0;
@@ -342,8 +344,9 @@ static int op_rope(const pool_t* P, const orc_rec* r) {
         double pos = (double)(r->lens[b] - 1);
         for (int64_t h = 0; h < H; ++h) {
             for (int t = 0; t < 2; ++t) {
+                if (t == 1 && h >= Hk) continue;
                 uint8_t* v = t == 0 ? q : k;
-                int64_t base = (b * H + h) * D;
+                int64_t base = (b * (t == 0 ? H : Hk) + h) * D;
                 for (int64_t i = 0; i < D / 2; ++i) {
                     int64_t i0 = half ? i : 2 * i, i1 = half ? i + D / 2 : 2 * i + 1;
                     double ang = pos * pow(theta, -2.0 * (double)i / (double)D);
@@ -381,14 +384,19 @@ static int op_kv_append(const pool_t* P, const orc_rec* r) {
 }
 
 /* Single-query SDPA: for each (b, h), s_j = scale * q . K_j for j < L_b,
- * p = softmax(s), o = sum_j p_j V_j.  scale defaults to 1/sqrt(D). */
+ * p = softmax(s), o = sum_j p_j V_j.  scale defaults to 1/sqrt(D).  The
+ * caches hold Hkv = dim[3] (0: H) heads [B, Hkv, C, D]; query head h reads
+ * key/value head h / (H / Hkv) (grouped-query attention; Hkv = 1 is
+ * multi-query attention). */
 static int op_sdpa(const pool_t* P, const orc_rec* r) {
     int64_t B = r->size, H = r->dim[0], D = r->dim[1], C = r->dim[2];
+    int64_t Hkv = r->dim[3] > 0 ? r->dim[3] : H;
     int dt = r->dtype, dout = r->out_dtype;
-    if (B > 8) return ORC_E_BOUNDS;
+    if (B > 8 || H % Hkv != 0) return ORC_E_BOUNDS;
+    const int64_t G = H / Hkv;
     const uint8_t* q = span(P, r, R_A, B * H * D * esize(dt));
-    const uint8_t* K = span(P, r, R_AUX0, B * H * C * D * esize(dt));
-    const uint8_t* V = span(P, r, R_AUX1, B * H * C * D * esize(dt));
+    const uint8_t* K = span(P, r, R_AUX0, B * Hkv * C * D * esize(dt));
+    const uint8_t* V = span(P, r, R_AUX1, B * Hkv * C * D * esize(dt));
     uint8_t* o = span(P, r, R_OUT, B * H * D * esize(dout));
     if (!q || !K || !V || !o) return ORC_E_BOUNDS;
     double scale = r->fparam[1] != 0.0f ? (double)r->fparam[1] : 1.0 / sqrt((double)D);
@@ -400,7 +408,7 @@ static int op_sdpa(const pool_t* P, const orc_rec* r) {
         int64_t L = r->lens[b];
         if (L < 1 || L > C) { rc = ORC_E_BOUNDS; break; }
         for (int64_t h = 0; h < H; ++h) {
-            int64_t kv = (b * H + h) * C * D, qo = (b * H + h) * D;
+            int64_t kv = (b * Hkv + h / G) * C * D, qo = (b * H + h) * D;
             double m = -INFINITY;
             for (int64_t j = 0; j < L; ++j) {
                 double dot = 0.0;

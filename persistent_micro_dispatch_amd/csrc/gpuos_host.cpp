@@ -98,11 +98,12 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
             add(d.output, sz * d.dim[0] * eo, true);
             break;
         case GPUOS_OP_ROPE: {
-            const uint64_t bytes = sz * d.dim[0] * d.dim[1] * es;
-            add(d.input_a, bytes, false);
-            add(d.input_b, bytes, false);
-            add(d.input_a, bytes, true);
-            add(d.input_b, bytes, true);
+            const uint64_t bq = sz * d.dim[0] * d.dim[1] * es;
+            const uint64_t bk = sz * (d.dim[3] ? d.dim[3] : d.dim[0]) * d.dim[1] * es;
+            add(d.input_a, bq, false);
+            add(d.input_b, bk, false);
+            add(d.input_a, bq, true);
+            add(d.input_b, bk, true);
             break;
         }
         case GPUOS_OP_KV_APPEND: {
@@ -120,11 +121,12 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
         }
         case GPUOS_OP_SDPA: {
             const uint64_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            const uint64_t Hkv = d.dim[3] ? d.dim[3] : H;
             add(d.input_a, sz * H * D * es, false);
             for (uint32_t b = 0; b < sz && b < MAX_B; ++b) {
                 const uint64_t L = lens_at(lensw, b);
-                const uint64_t lo = (b * H) * C * D * es;
-                const uint64_t hi = ((b * H + H - 1) * C + L) * D * es;
+                const uint64_t lo = (b * Hkv) * C * D * es;
+                const uint64_t hi = ((b * Hkv + Hkv - 1) * C + L) * D * es;
                 add(d.aux[0] + lo, hi - lo, false);
                 add(d.aux[1] + lo, hi - lo, false);
             }

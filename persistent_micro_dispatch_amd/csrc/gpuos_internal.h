@@ -233,7 +233,8 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             const uint32_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
             if (B == 0 || B > MAX_B || H == 0 || D == 0 || di != dout) return bad();
             if (d.kind == GPUOS_OP_ROPE) {
-                if ((D & 1u) || D > 256u || d.a == 0 || d.b == 0) return bad();
+                // k has dim[3] heads (0: H), at most H
+                if ((D & 1u) || D > 256u || d.a == 0 || d.b == 0 || d.dim[3] > H) return bad();
             } else {
                 if (C == 0 || d.a == 0 || d.b == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
             }
@@ -254,6 +255,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             const uint64_t B = d.size;
             const uint32_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
             if (B == 0 || B > MAX_B || H == 0 || C == 0 || (D != 64u && D != 128u)) return bad();
+            if (d.dim[3] != 0 && H % d.dim[3] != 0) return bad();  // key/value heads divide the query heads
             if (di != GPUOS_BF16) return bad();
             if (d.a == 0 || d.out == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
             uint64_t units = 0;

@@ -705,6 +705,7 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
     constexpr uint32_t VE = 16u / ES;
     const uint32_t H = u.dim[0], D = u.dim[1];
+    const uint32_t Hk = u.dim[3] ? u.dim[3] : H;  // k's heads (fewer under grouped-query attention)
     const uint32_t RH = rope_heads_per_unit(D, DT);
     const uint32_t ng = (H + RH - 1) / RH;
     const uint32_t b = u.tile / ng, h0 = (u.tile - b * ng) * RH;
@@ -722,9 +723,9 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
         // and their stores are dropped by the window
         const uint32_t cc = lane % CPR, sub = lane / CPR;
         uint8_t* P0 = (uint8_t*)u.a + (uint64_t)b * H * RB;
-        uint8_t* P1 = (uint8_t*)u.b + (uint64_t)b * H * RB;
-        const WBuf w0 = wbuf(P0, H * RB), w1 = wbuf(P1, H * RB);
-        const RBuf r0 = rbuf(P0, H * RB), r1 = rbuf(P1, H * RB);
+        uint8_t* P1 = (uint8_t*)u.b + (uint64_t)b * Hk * RB;
+        const WBuf w0 = wbuf(P0, H * RB), w1 = wbuf(P1, Hk * RB);  // rows past Hk: dropped
+        const RBuf r0 = rbuf(P0, H * RB), r1 = rbuf(P1, Hk * RB);
         const uint32_t off = ((h0 + sub) * CPR + cc) * 16u;
         const u32x4 v0 = rld16(r0, off), v1 = rld16(r1, off);
         double cs[VE / 2], sn[VE / 2];
@@ -768,8 +769,9 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
         const uint32_t i0 = half ? pi : 2u * pi, i1 = half ? pi + D / 2 : 2u * pi + 1u;
         for (uint32_t t = 0; t < 2; ++t) {
             uint8_t* P = (uint8_t*)(t == 0 ? u.a : u.b);
-            for (uint32_t hh = h0; hh < h0 + hn; ++hh) {
-                const uint64_t base = ((uint64_t)b * H + hh) * D;
+            const uint32_t Ht = t == 0 ? H : Hk;
+            for (uint32_t hh = h0; hh < h0 + hn && hh < Ht; ++hh) {
+                const uint64_t base = ((uint64_t)b * Ht + hh) * D;
                 const double x0 = (double)ld_elem<DT>(P, base + i0);
                 const double x1 = (double)ld_elem<DT>(P, base + i1);
                 const double y0 = x0 * c - x1 * s;
@@ -874,14 +876,16 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     }
     if (b >= Bn) return;
     const uint32_t local = t - base, h = local / ns, sp = local % ns;
+    const uint32_t Hkv = u.dim[3] ? u.dim[3] : H;  // grouped-query attention: head h reads kv head h / (H / Hkv)
+    const uint64_t bkv = (uint64_t)b * Hkv + h / (H / Hkv);
     const uint32_t k0 = sp * kt;
     const uint32_t nk = min(L - k0, kt);
     const uint64_t bh = (uint64_t)b * H + h;
     const float scale = u.pf[4] != 0.0f ? u.pf[4] : (u.p0 != 0.0f ? u.p0 : 1.0f / sqrtf((float)D));
     const float sl2 = scale * 1.4426950408889634f;  // scores in the log2 domain
     const uint32_t g = lane / DV, c = lane % DV;
-    const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bh * C + k0) * D * 2u, nk * D * 2u);
-    const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bh * C + k0) * D * 2u, nk * D * 2u);
+    const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bkv * C + k0) * D * 2u, nk * D * 2u);
+    const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bkv * C + k0) * D * 2u, nk * D * 2u);
     const u32x4 qr = rld16(rbuf((const uint8_t*)u.a + bh * D * 2u, D * 2u), c * 16u);
     const bf16x2 q0 = as_bf2(qr.x), q1 = as_bf2(qr.y), q2 = as_bf2(qr.z), q3 = as_bf2(qr.w);
     float m = -INFINITY, lsum = 0.0f;

@@ -107,9 +107,11 @@ def check_record(r, inputs: List[np.ndarray], gpu: List[np.ndarray], orc: List[n
                 ok, worst = rel_check(gf, rf, np.maximum(np.abs(rf), 1e-30), 2.0 ** -22)
         elif op == W.OP_SDPA:
             H, D, C = d[0], d[1], d[2]
+            Hkv = d[3] or H  # grouped-query attention: kv head h // (H // Hkv)
             q = _f(inputs[int(buf[W.A])], int(off[W.A]), size * H * D, dt).reshape(size, H, D)
-            K = _f(inputs[int(buf[W.AUX0])], int(off[W.AUX0]), size * H * C * D, dt).reshape(size, H, C, D)
-            V = _f(inputs[int(buf[W.AUX1])], int(off[W.AUX1]), size * H * C * D, dt).reshape(size, H, C, D)
+            K = _f(inputs[int(buf[W.AUX0])], int(off[W.AUX0]), size * Hkv * C * D, dt).reshape(size, Hkv, C, D)
+            V = _f(inputs[int(buf[W.AUX1])], int(off[W.AUX1]), size * Hkv * C * D, dt).reshape(size, Hkv, C, D)
+            K, V = np.repeat(K, H // Hkv, axis=1), np.repeat(V, H // Hkv, axis=1)
             denom = np.zeros((size, H, D))
             scale = float(r["fparam"][1]) or 1.0 / np.sqrt(D)
             for bb in range(size):

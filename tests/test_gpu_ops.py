@@ -275,3 +275,38 @@ def test_expr_reregistration_flips_between_descriptors(ctx):
     assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 30_000_000_000)[0] == 0
     assert np.array_equal(pool.download(2).view(np.float32), a + b)
     assert np.array_equal(pool.download(3).view(np.float32), a * b)
+
+
+# ------------------------------------------------ grouped-query attention
+@pytest.mark.parametrize("out_dt", [W.F32, W.BF16])
+def test_sdpa_grouped_kv_heads(ctx, out_dt):
+    say(f"sdpa gqa out={out_dt}")
+    recs, arrays = [], []
+    for B, H, Hkv, D, C, lens in [(2, 8, 2, 128, 600, [300, 17]), (1, 32, 8, 128, 4096, [4096]),
+                                  (3, 4, 1, 64, 700, [1, 256, 700]), (8, 32, 8, 128, 512, list(RNG.integers(1, 513, 8)))]:
+        q = bf16(RNG.standard_normal(B * H * D))
+        K, V = bf16(RNG.standard_normal(B * Hkv * C * D)), bf16(RNG.standard_normal(B * Hkv * C * D))
+        o = np.zeros(B * H * D, np.float32 if out_dt == W.F32 else np.uint16)
+        base = len(arrays)
+        arrays += [q, K, V, o]
+        recs.append(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=out_dt, size=B, dim=(H, D, C, Hkv), lens=lens,
+                        a=base, aux0=base + 1, aux1=base + 2, out=base + 3))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))
+
+
+@pytest.mark.parametrize("dt,half", [(W.BF16, False), (W.F32, False), (W.BF16, True)])
+def test_rope_fewer_key_heads(ctx, dt, half):
+    say(f"rope gqa dt={dt} half={half}")
+    recs, arrays = [], []
+    for B, H, Hk, D, lens in [(3, 32, 8, 128, [1, 77, 4096]), (1, 6, 2, 64, [1234]), (2, 8, 1, 128, [9, 10])]:
+        if dt == W.F32:
+            q = RNG.standard_normal(B * H * D).astype(np.float32)
+            k = RNG.standard_normal(B * Hk * D).astype(np.float32)
+        else:
+            q, k = bf16(RNG.standard_normal(B * H * D)), bf16(RNG.standard_normal(B * Hk * D))
+        base = len(arrays)
+        arrays += [q, k]
+        recs.append(rec(W.OP_ROPE, dtype=dt, size=B, dim=(H, D, 0, Hk), fparam=(10000.0,), lens=lens,
+                        flags=W.FLAG_ROPE_HALF if half else 0, a=base, b=base + 1))
+    _run_and_check(ctx, arrays, np.concatenate(recs))

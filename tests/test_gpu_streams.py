@@ -101,3 +101,10 @@ def test_mixed_stream_verify(upw):
     say(f"mixed verify, units_per_wave={upw}")
     res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, units_per_wave=upw)
     _report("mixed", res)
+
+
+def test_decode_grouped_kv_heads_stream_verify():
+    s = W.make_decode(steps=3, layers=2, heads=8, kv_heads=2, capacity=512, l_min=100, n_triples=4, n_out=16)
+    say("decode verify, 8 query heads sharing 2 key/value heads")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, units_per_wave=2)
+    _report("decode gqa", res)

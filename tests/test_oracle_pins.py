@@ -604,3 +604,39 @@ def test_expr_record_matches_builtin_ops_bit_exactly():
                                        aux2=4)])
             out = run(recs, arrays)
             assert np.array_equal(out[2].view(np.uint8), out[3].view(np.uint8)), (dt, op)
+
+
+# ------------------------------------------------ grouped-query attention
+def test_sdpa_grouped_kv_heads_match_repeated_heads_and_torch():
+    """Hkv key/value heads shared by H/Hkv query heads each: the same as
+    multi-head attention with every key/value head repeated H/Hkv times
+    (checked through the oracle's own MHA path and through torch)."""
+    for (B, H, Hkv, D, C) in [(2, 8, 2, 8, 12), (1, 4, 1, 16, 9), (3, 6, 3, 128, 40)]:
+        G = H // Hkv
+        q = bf16(RNG.standard_normal((B, H, D)))
+        K = bf16(RNG.standard_normal((B, Hkv, C, D)))
+        V = bf16(RNG.standard_normal((B, Hkv, C, D)))
+        lens = list(RNG.integers(1, C + 1, B))
+        o = np.zeros((B, H, D), np.float32)
+        got = run(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=B, dim=(H, D, C, Hkv), lens=lens,
+                      a=0, aux0=1, aux1=2, out=3), [q, K, V, o])[3]
+        Kr, Vr = np.repeat(K, G, axis=1), np.repeat(V, G, axis=1)
+        mha = run(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=B, dim=(H, D, C), lens=lens,
+                      a=0, aux0=1, aux1=2, out=3), [q, Kr, Vr, o])[3]
+        assert np.array_equal(got, mha)
+        ref = _sdpa_torch(*(bf16_val(t).astype(np.float64) for t in (q, Kr, Vr)), lens)
+        assert np.max(np.abs(got - ref.reshape(got.shape))) <= 2 ** -23 * np.max(np.abs(ref)) + 1e-12
+
+
+def test_rope_with_fewer_key_heads_rotates_each_tensor_by_its_own_heads():
+    B, H, Hk, D = 2, 8, 2, 16
+    lens = [5, 300]
+    q = (RNG.standard_normal(B * H * D)).astype(np.float32)
+    k = (RNG.standard_normal(B * Hk * D)).astype(np.float32)
+    both = run(rec(W.OP_ROPE, dtype=W.F32, size=B, dim=(H, D, 0, Hk), fparam=(10000.0,), lens=lens, a=0, b=1),
+               [q, k])
+    q_only = run(rec(W.OP_ROPE, dtype=W.F32, size=B, dim=(H, D), fparam=(10000.0,), lens=lens, a=0, b=1),
+                 [q, np.zeros_like(q)])[0]
+    k_only = run(rec(W.OP_ROPE, dtype=W.F32, size=B, dim=(Hk, D), fparam=(10000.0,), lens=lens, a=0, b=1),
+                 [np.zeros_like(k), k])[1]
+    assert np.array_equal(both[0], q_only) and np.array_equal(both[1], k_only)

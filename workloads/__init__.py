@@ -351,17 +351,21 @@ def make_decode(seed: int = 4, steps: int = 2000, layers: int = 32, heads: int =
                 head_dim: int = 128, capacity: int = 4096, max_batch: int = 8,
                 l_min: int = 128, n_triples: int = 256, theta: float = 10000.0,
                 out_dtype: int = F32, n_out: int = 64,
-                batches: Sequence[int] = (1, 2, 4, 8)) -> Stream:
+                batches: Sequence[int] = (1, 2, 4, 8), kv_heads: int = 0) -> Stream:
+    """kv_heads (0: heads) below heads gives grouped-query attention: k, v
+    and the caches have kv_heads heads, shared by heads/kv_heads queries."""
     H, D, C, Bm = heads, head_dim, capacity, max_batch
+    Hkv = kv_heads or H
+    assert H % Hkv == 0
     bufs: List[Buffer] = []
     kc0 = len(bufs)
     for l in range(layers):
-        bufs.append(Buffer(f"K{l}", BF16, Bm * H * C * D, ("normal", 1.0), _buffer_seed(seed, 10 * l)))
-        bufs.append(Buffer(f"V{l}", BF16, Bm * H * C * D, ("normal", 1.0), _buffer_seed(seed, 10 * l + 1)))
+        bufs.append(Buffer(f"K{l}", BF16, Bm * Hkv * C * D, ("normal", 1.0), _buffer_seed(seed, 10 * l)))
+        bufs.append(Buffer(f"V{l}", BF16, Bm * Hkv * C * D, ("normal", 1.0), _buffer_seed(seed, 10 * l + 1)))
     tq = len(bufs)
     for t in range(n_triples):
         for j, nm in enumerate("qkv"):
-            bufs.append(Buffer(f"{nm}{t}", BF16, Bm * H * D, ("normal", 1.0),
+            bufs.append(Buffer(f"{nm}{t}", BF16, Bm * (H if nm == "q" else Hkv) * D, ("normal", 1.0),
                                _buffer_seed(seed, 100_000 + 3 * t + j)))
     o0 = len(bufs)
     for i in range(n_out):
@@ -402,13 +406,14 @@ def make_decode(seed: int = 4, steps: int = 2000, layers: int = 32, heads: int =
                 if x["op"] != OP_SDPA:
                     x["out_dtype"] = BF16
                 x["size"] = Bsz
-                x["dim"][:] = (H, D, C, 0)
+                x["dim"][:] = (H, D, C, Hkv if Hkv != H else 0)
                 x["lens"][:] = lens_row
+            rr[1]["dim"][:] = (Hkv, D, C, 0)
             recs.append(rr)
     r = np.concatenate(recs) if recs else _new_recs(0)
     bursts = np.full(steps * layers, 3) if steps else np.zeros(0, np.int64)
     return Stream("decode", bufs, r, bursts,
-                  {"seed": seed, "kv_first": kc0, "layers": layers, "heads": H,
+                  {"seed": seed, "kv_first": kc0, "layers": layers, "heads": H, "kv_heads": Hkv,
                    "head_dim": D, "capacity": C})
 
 
@@ -530,8 +535,8 @@ def output_ranges(r) -> list:
     if op in (OP_SOFTMAX, OP_LAYERNORM):
         return [(int(buf[OUT]), int(off[OUT]), size * d[0] * eo)]
     if op == OP_ROPE:
-        n = size * d[0] * d[1] * es
-        return [(int(buf[A]), int(off[A]), n), (int(buf[B]), int(off[B]), n)]
+        hk = d[3] if d[3] else d[0]
+        return [(int(buf[A]), int(off[A]), size * d[0] * d[1] * es), (int(buf[B]), int(off[B]), size * hk * d[1] * es)]
     if op == OP_KV_APPEND:
         H, D, C = d[0], d[1], d[2]
         out = []
@@ -572,14 +577,18 @@ def algorithmic_bytes(recs: np.ndarray) -> np.ndarray:
     out[m] = (es[m] + eo[m]) * n[m] * d0[m]
     m = op == OP_LAYERNORM
     out[m] = (es[m] + eo[m]) * n[m] * d0[m] + 2 * es[m] * d0[m]
-    m = (op == OP_ROPE) | (op == OP_KV_APPEND)
+    d3 = recs["dim"][:, 3].astype(np.int64)
+    hk = np.where(d3 > 0, d3, d0)  # key/value heads (grouped-query attention)
+    m = op == OP_ROPE
+    out[m] = 2 * n[m] * (d0[m] + hk[m]) * d1[m] * es[m]
+    m = op == OP_KV_APPEND
     out[m] = 4 * n[m] * d0[m] * d1[m] * es[m]
     m = op == OP_SDPA
     if m.any():
         L = recs["lens"][m].astype(np.int64)
         bmask = np.arange(8)[None, :] < n[m][:, None]
         keys = (L * bmask).sum(axis=1)
-        out[m] = (n[m] * d0[m] * d1[m] * (es[m] + eo[m])) + 2 * keys * d0[m] * d1[m] * es[m]
+        out[m] = (n[m] * d0[m] * d1[m] * (es[m] + eo[m])) + 2 * keys * hk[m] * d1[m] * es[m]
     m = op == OP_GEMV
     out[m] = es[m] * d0[m] + es[m] * d0[m] * d1[m] + eo[m] * d1[m]
     m = op == OP_COPY
