@@ -192,6 +192,15 @@ __host__ __device__ inline uint32_t sdpa_keys_per_unit(uint32_t B, uint32_t H, c
     return kt;
 }
 
+// Query heads per SDPA unit: under grouped-query attention the query heads
+// of a group share their key/value rows, so with D = 128 and groups of a
+// multiple of 4 heads a unit takes 4 of them and reads each key/value chunk
+// once for all four.
+__host__ __device__ inline uint32_t sdpa_heads_per_unit(uint32_t H, uint32_t Hkv, uint32_t D) {
+    const uint32_t g = Hkv ? H / Hkv : 1u;
+    return (D == 128u && g % 4u == 0u) ? 4u : 1u;
+}
+
 // a GEMV unit covers 16 lanes x 16 bytes of columns (four rows per load)
 __host__ __device__ inline uint32_t gemv_cols_per_block(uint32_t dt) { return 16u * (16u / esz(dt)); }
 
@@ -269,7 +278,9 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
                 units += ns * H;
             }
             if (units > MAX_TILES || (uint64_t)B * H * 4 > COUNTER_AREA) return bad();
-            p.ntiles = (uint32_t)units;
+            // a unit covers sdpa_heads_per_unit query heads; partial records
+            // and counters stay per head
+            p.ntiles = (uint32_t)(units / sdpa_heads_per_unit(H, d.dim[3], D));
             if (split) p.scratch = COUNTER_AREA + units * (uint64_t)(D + 4) * 4u;
             return p;
         }

@@ -857,89 +857,112 @@ __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
 // zero through the bounded buffer window and get weight 0.  Dense MFMA does
 // not apply: one query per head makes q.K^T and P.V matrix-vector products
 // with no reuse.
-template <uint32_t DV, uint32_t DTO>
+template <uint32_t DV, uint32_t DTO, uint32_t GP>
 __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t D = DV * 8u;
     constexpr uint32_t RPI = 64u / DV;
-    constexpr uint32_t CK = 8u * RPI;     // keys per chunk
+    constexpr uint32_t NI = GP == 1u ? 8u : 4u;  // load instructions per chunk (fewer with more heads)
+    constexpr uint32_t CK = NI * RPI;     // keys per chunk
     constexpr uint32_t PSTRIDE = D + 4u;  // floats per partial record: m, l, pad, pad, acc[D]
     const uint32_t H = u.dim[0], C = u.dim[2];
+    const uint32_t Hkv = u.dim[3] ? u.dim[3] : H;
     const uint32_t Bn = (uint32_t)u.size;
     const uint32_t kt = sdpa_keys_per_unit(Bn, H, u.lensw);
-    uint32_t t = u.tile, base = 0, b = 0, ns = 1, L = 0;
+    const uint32_t HG = H / GP;  // units per (b, split): groups of GP query heads
+    // unit -> (b, head group, split); mbase numbers the per-head splits of
+    // earlier batch rows (the partial records and counters are per head)
+    uint32_t t = u.tile, base = 0, mbase = 0, b = 0, ns = 1, L = 0;
     for (b = 0; b < Bn; ++b) {
         L = lens_at(u.lensw, b);
         ns = (L + kt - 1) / kt;
-        const uint32_t nu = H * ns;
+        const uint32_t nu = HG * ns;
         if (t < base + nu) break;
         base += nu;
+        mbase += H * ns;
     }
     if (b >= Bn) return;
-    const uint32_t local = t - base, h = local / ns, sp = local % ns;
-    const uint32_t Hkv = u.dim[3] ? u.dim[3] : H;  // grouped-query attention: head h reads kv head h / (H / Hkv)
-    const uint64_t bkv = (uint64_t)b * Hkv + h / (H / Hkv);
+    const uint32_t local = t - base, hg = local / ns, sp = local % ns;
+    const uint32_t h0 = hg * GP;  // the unit's first query head; all GP share a key/value head
+    const uint64_t bkv = (uint64_t)b * Hkv + h0 / (H / Hkv);
     const uint32_t k0 = sp * kt;
     const uint32_t nk = min(L - k0, kt);
-    const uint64_t bh = (uint64_t)b * H + h;
     const float scale = u.pf[4] != 0.0f ? u.pf[4] : (u.p0 != 0.0f ? u.p0 : 1.0f / sqrtf((float)D));
     const float sl2 = scale * 1.4426950408889634f;  // scores in the log2 domain
     const uint32_t g = lane / DV, c = lane % DV;
     const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bkv * C + k0) * D * 2u, nk * D * 2u);
     const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bkv * C + k0) * D * 2u, nk * D * 2u);
-    const u32x4 qr = rld16(rbuf((const uint8_t*)u.a + bh * D * 2u, D * 2u), c * 16u);
-    const bf16x2 q0 = as_bf2(qr.x), q1 = as_bf2(qr.y), q2 = as_bf2(qr.z), q3 = as_bf2(qr.w);
-    float m = -INFINITY, lsum = 0.0f;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    bf16x2 qv[GP][4];
+#pragma unroll
+    for (uint32_t gi = 0; gi < GP; ++gi) {
+        const uint64_t bh = (uint64_t)b * H + h0 + gi;
+        const u32x4 qr = rld16(rbuf((const uint8_t*)u.a + bh * D * 2u, D * 2u), c * 16u);
+        qv[gi][0] = as_bf2(qr.x); qv[gi][1] = as_bf2(qr.y); qv[gi][2] = as_bf2(qr.z); qv[gi][3] = as_bf2(qr.w);
+    }
+    float m[GP], lsum[GP], acc[GP][8];
+#pragma unroll
+    for (uint32_t gi = 0; gi < GP; ++gi) {
+        m[gi] = -INFINITY;
+        lsum[gi] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[gi][e] = 0.0f;
+    }
     const uint32_t nch = (nk + CK - 1) / CK;
     auto load = [&](u32x4* kv, u32x4* vv, uint32_t ci) {
 #pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) {
+        for (uint32_t j = 0; j < NI; ++j) {
             const uint32_t off = ((ci * CK + j * RPI + g) * D) * 2u + c * 16u;
             kv[j] = rld16(rk, off);
             vv[j] = rld16(rv, off);
         }
     };
     auto consume = [&](const u32x4* kv, const u32x4* vv, uint32_t ci) {
-        float s[8];
-        float cm = -INFINITY;
+        float s[GP][NI];
+        float mn[GP];
 #pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) {
-            float d = 0.0f;
-            d = __builtin_amdgcn_fdot2_f32_bf16(q0, as_bf2(kv[j].x), d, false);
-            d = __builtin_amdgcn_fdot2_f32_bf16(q1, as_bf2(kv[j].y), d, false);
-            d = __builtin_amdgcn_fdot2_f32_bf16(q2, as_bf2(kv[j].z), d, false);
-            d = __builtin_amdgcn_fdot2_f32_bf16(q3, as_bf2(kv[j].w), d, false);
-            d = gred<DV>(d, OpAdd{}) * sl2;
-            const bool valid = ci * CK + j * RPI + g < nk;
-            s[j] = valid ? d : -INFINITY;
-            cm = fmaxf(cm, s[j]);
+        for (uint32_t gi = 0; gi < GP; ++gi) {
+            float cm = -INFINITY;
+#pragma unroll
+            for (uint32_t j = 0; j < NI; ++j) {
+                float d = 0.0f;
+                d = __builtin_amdgcn_fdot2_f32_bf16(qv[gi][0], as_bf2(kv[j].x), d, false);
+                d = __builtin_amdgcn_fdot2_f32_bf16(qv[gi][1], as_bf2(kv[j].y), d, false);
+                d = __builtin_amdgcn_fdot2_f32_bf16(qv[gi][2], as_bf2(kv[j].z), d, false);
+                d = __builtin_amdgcn_fdot2_f32_bf16(qv[gi][3], as_bf2(kv[j].w), d, false);
+                d = gred<DV>(d, OpAdd{}) * sl2;
+                const bool valid = ci * CK + j * RPI + g < nk;
+                s[gi][j] = valid ? d : -INFINITY;
+                cm = fmaxf(cm, s[gi][j]);
+            }
+            // chunk max over the RPI key groups of the wave
+            if constexpr (DV == 16) {
+                cm = fmaxf(fmaxf(rlf(cm, 0), rlf(cm, 16)), fmaxf(rlf(cm, 32), rlf(cm, 48)));
+            } else {
+#pragma unroll
+                for (uint32_t mm = DV; mm < 64; mm <<= 1) cm = fmaxf(cm, __shfl_xor(cm, mm, 64));
+            }
+            mn[gi] = fmaxf(m[gi], cm);                // finite: every chunk has at least one key
+            const float alpha = exp2f(m[gi] - mn[gi]);  // 0 on the first chunk (m = -inf)
+            lsum[gi] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[gi][e] *= alpha;
+            m[gi] = mn[gi];
         }
-        // chunk max over the RPI key groups of the wave
-        if constexpr (DV == 16) {
-            cm = fmaxf(fmaxf(rlf(cm, 0), rlf(cm, 16)), fmaxf(rlf(cm, 32), rlf(cm, 48)));
-        } else {
 #pragma unroll
-            for (uint32_t mm = DV; mm < 64; mm <<= 1) cm = fmaxf(cm, __shfl_xor(cm, mm, 64));
-        }
-        const float mn = fmaxf(m, cm);          // finite: every chunk has at least one key
-        const float alpha = exp2f(m - mn);      // 0 on the first chunk (m = -inf)
-        lsum *= alpha;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] *= alpha;
-#pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) {
-            const float p = exp2f(s[j] - mn);   // 0 for keys past L
+        for (uint32_t j = 0; j < NI; ++j) {
             float vf[8];
             unpack<GPUOS_BF16>(vv[j], vf);
-            lsum += p;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] += p * vf[e];
+            for (uint32_t gi = 0; gi < GP; ++gi) {
+                const float p = exp2f(s[gi][j] - mn[gi]);  // 0 for keys past L
+                lsum[gi] += p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[gi][e] += p * vf[e];
+            }
         }
-        m = mn;
     };
     // The scheduling barriers keep the compiler from sinking the next chunk's
     // loads below the use of the current one (it would to save registers).
-    u32x4 ka[8], va[8], kb[8], vb[8];
+    u32x4 ka[NI], va[NI], kb[NI], vb[NI];
     load(ka, va, 0);
     for (uint32_t ci = 0; ci < nch; ci += 2) {
         load(kb, vb, ci + 1);  // past the last chunk: outside the window, reads nothing
@@ -951,93 +974,106 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
             consume(kb, vb, ci + 1);
         }
     }
-    // combine the RPI key groups (lanes with equal c)
-#pragma unroll
-    for (uint32_t mm = DV; mm < 64; mm <<= 1) {
-        lsum += __shfl_xor(lsum, mm, 64);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], mm, 64);
-    }
     constexpr uint32_t ESO = DTO == GPUOS_F32 ? 4u : 2u;
-    uint8_t* O = (uint8_t*)u.out + bh * D * ESO;
-    if (ns == 1) {
-        if (g == 0) {
-            float o[8];
-            const float inv = 1.0f / lsum;
+    float* parts = (float*)(u.scratch + COUNTER_AREA);
+    // per head: combine the RPI key groups (lanes with equal c), then store
+    // the output (one split) or this split's partial record
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = acc[e] * inv;
-            const WBuf ob = wbuf(O);
-            if constexpr (DTO == GPUOS_F32) {
-                wst16(ob, c * 32u, pack<GPUOS_F32>(o));
-                wst16(ob, c * 32u + 16u, pack<GPUOS_F32>(o + 4));
-            } else {
-                wst16(ob, c * 16u, pack<GPUOS_BF16>(o));
-            }
+    for (uint32_t gi = 0; gi < GP; ++gi) {
+#pragma unroll
+        for (uint32_t mm = DV; mm < 64; mm <<= 1) {
+            lsum[gi] += __shfl_xor(lsum[gi], mm, 64);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[gi][e] += __shfl_xor(acc[gi][e], mm, 64);
         }
-        return;
-    }
-    // several splits: publish this partial, the last arriver merges
-    float* part = (float*)(u.scratch + COUNTER_AREA) + (uint64_t)t * PSTRIDE;
-    if (g == 0) {
-        const WBuf pb = wbuf(part);
-        wst16(pb, (4u + 8u * c) * 4u, pack<GPUOS_F32>(acc));
-        wst16(pb, (8u + 8u * c) * 4u, pack<GPUOS_F32>(acc + 4));
-    }
-    if (lane == 0) { wstf(part, m); wstf(part + 1, lsum); }
-    uint32_t* ctr = (uint32_t*)u.scratch + bh;
-    uint32_t prev = 0;
-    stores_done();  // this unit's partial is published before it is counted
-    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
-    if (prev != ns - 1) return;
-    // merge (log2 domain): M = max m_i, Ls = sum l_i 2^{m_i - M}, o = sum acc_i 2^{m_i - M} / Ls.
-    // Lane i < ns reads split i's (m, l).  A record's acc is CH = D/4 chunks
-    // of 16 bytes, so one load instruction covers SPI = 64/CH splits: lane l
-    // reads chunk l % CH of split l / CH (+ SPI per instruction), up to 16
-    // instructions in flight; each lane adds its splits in order, then the
-    // SPI lane groups are added in a fixed tree.
-    const uint8_t* p0 = (const uint8_t*)((const float*)(u.scratch + COUNTER_AREA) + (uint64_t)(t - sp) * PSTRIDE);
-    constexpr uint32_t CH = D / 4u;
-    constexpr uint32_t SPI = 64u / CH;
-    constexpr uint32_t NB = 16;  // load instructions per batch
-    float mi = -INFINITY, li = 0.0f;
-    if (lane < ns) {
-        mi = __uint_as_float(ld4(p0 + (uint64_t)lane * PSTRIDE * 4u));
-        li = __uint_as_float(ld4(p0 + (uint64_t)lane * PSTRIDE * 4u + 4u));
-    }
-    const float M = wmaxf(mi);
-    const float wi = lane < ns ? exp2f(mi - M) : 0.0f;
-    const float Ls = wsum(li * wi);
-    const uint32_t j = lane / CH, cc = lane % CH;
-    const RBuf rp = rbuf(p0, ns * PSTRIDE * 4u);  // splits past ns read zero
-    float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (uint32_t i0 = 0; i0 < ns; i0 += NB * SPI) {
-        u32x4 v[NB];
+        const uint64_t bh = (uint64_t)b * H + h0 + gi;
+        if (ns == 1) {
+            if (g == 0) {
+                uint8_t* O = (uint8_t*)u.out + bh * D * ESO;
+                float o[8];
+                const float inv = 1.0f / lsum[gi];
 #pragma unroll
-        for (uint32_t k = 0; k < NB; ++k)
-            if (i0 + k * SPI < ns) v[k] = rld16(rp, ((i0 + k * SPI + j) * PSTRIDE + 4u + 4u * cc) * 4u);
-#pragma unroll
-        for (uint32_t k = 0; k < NB; ++k) {
-            if (i0 + k * SPI < ns) {
-                const float w = __shfl(wi, (int)((i0 + k * SPI + j) & 63u), 64);  // 0 past ns
-                o[0] += w * __uint_as_float(v[k].x);
-                o[1] += w * __uint_as_float(v[k].y);
-                o[2] += w * __uint_as_float(v[k].z);
-                o[3] += w * __uint_as_float(v[k].w);
+                for (int e = 0; e < 8; ++e) o[e] = acc[gi][e] * inv;
+                const WBuf ob = wbuf(O);
+                if constexpr (DTO == GPUOS_F32) {
+                    wst16(ob, c * 32u, pack<GPUOS_F32>(o));
+                    wst16(ob, c * 32u + 16u, pack<GPUOS_F32>(o + 4));
+                } else {
+                    wst16(ob, c * 16u, pack<GPUOS_BF16>(o));
+                }
             }
+        } else {
+            float* part = parts + ((uint64_t)mbase + (uint64_t)(h0 + gi) * ns + sp) * PSTRIDE;
+            if (g == 0) {
+                const WBuf pb = wbuf(part);
+                wst16(pb, (4u + 8u * c) * 4u, pack<GPUOS_F32>(acc[gi]));
+                wst16(pb, (8u + 8u * c) * 4u, pack<GPUOS_F32>(acc[gi] + 4));
+            }
+            if (lane == 0) { wstf(part, m[gi]); wstf(part + 1, lsum[gi]); }
         }
     }
+    if (ns == 1) return;
+    stores_done();  // the partials are published before they are counted
+    // per head: count this split; the last arriver merges the head's splits
+#pragma unroll 1
+    for (uint32_t gi = 0; gi < GP; ++gi) {
+        const uint32_t head = h0 + gi;
+        const uint64_t bh = (uint64_t)b * H + head;
+        uint32_t* ctr = (uint32_t*)u.scratch + bh;
+        uint32_t prev = 0;
+        if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
+        if (prev != ns - 1) continue;
+        uint8_t* O = (uint8_t*)u.out + bh * D * ESO;
+        // merge (log2 domain): M = max m_i, Ls = sum l_i 2^{m_i - M}, o = sum acc_i 2^{m_i - M} / Ls.
+        // Lane i < ns reads split i's (m, l).  A record's acc is CH = D/4
+        // chunks of 16 bytes, so one load instruction covers SPI = 64/CH
+        // splits: lane l reads chunk l % CH of split l / CH (+ SPI per
+        // instruction), up to 16 instructions in flight; each lane adds its
+        // splits in order, then the SPI lane groups are added in a fixed tree.
+        const uint8_t* p0 = (const uint8_t*)(parts + ((uint64_t)mbase + (uint64_t)head * ns) * PSTRIDE);
+        constexpr uint32_t CH = D / 4u;
+        constexpr uint32_t SPI = 64u / CH;
+        constexpr uint32_t NB = 16;  // load instructions per batch
+        float mi = -INFINITY, li = 0.0f;
+        if (lane < ns) {
+            mi = __uint_as_float(ld4(p0 + (uint64_t)lane * PSTRIDE * 4u));
+            li = __uint_as_float(ld4(p0 + (uint64_t)lane * PSTRIDE * 4u + 4u));
+        }
+        const float M = wmaxf(mi);
+        const float wi = lane < ns ? exp2f(mi - M) : 0.0f;
+        const float Ls = wsum(li * wi);
+        const uint32_t jj = lane / CH, cc = lane % CH;
+        const RBuf rp = rbuf(p0, ns * PSTRIDE * 4u);  // splits past ns read zero
+        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (uint32_t i0 = 0; i0 < ns; i0 += NB * SPI) {
+            u32x4 v[NB];
 #pragma unroll
-    for (uint32_t mm = CH; mm < 64; mm <<= 1) {
+            for (uint32_t k = 0; k < NB; ++k)
+                if (i0 + k * SPI < ns) v[k] = rld16(rp, ((i0 + k * SPI + jj) * PSTRIDE + 4u + 4u * cc) * 4u);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], (int)mm, 64);
+            for (uint32_t k = 0; k < NB; ++k) {
+                if (i0 + k * SPI < ns) {
+                    const float w = __shfl(wi, (int)((i0 + k * SPI + jj) & 63u), 64);  // 0 past ns
+                    o[0] += w * __uint_as_float(v[k].x);
+                    o[1] += w * __uint_as_float(v[k].y);
+                    o[2] += w * __uint_as_float(v[k].z);
+                    o[3] += w * __uint_as_float(v[k].w);
+                }
+            }
+        }
+#pragma unroll
+        for (uint32_t mm = CH; mm < 64; mm <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] += __shfl_xor(o[e], (int)mm, 64);
+        }
+        if (lane < CH) {
+            const float inv = 1.0f / Ls;
+#pragma unroll
+            for (uint32_t e = 0; e < 4; ++e) st_elem<DTO>(O, 4u * cc + e, o[e] * inv);
+        }
+        if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (lane < CH) {
-        const float inv = 1.0f / Ls;
-#pragma unroll
-        for (uint32_t e = 0; e < 4; ++e) st_elem<DTO>(O, 4u * cc + e, o[e] * inv);
-    }
-    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------------------------ GEMV
@@ -1250,9 +1286,12 @@ __device__ __forceinline__ void run_unit(const Unit& u, uint32_t lane) {
         case GPUOS_OP_KV_APPEND: kv_tile(u, lane); break;
         case GPUOS_OP_SDPA:
             if (u.dim[1] == 128u) {
-                dout == GPUOS_F32 ? sdpa_tile<16, GPUOS_F32>(u, lane) : sdpa_tile<16, GPUOS_BF16>(u, lane);
+                if (sdpa_heads_per_unit(u.dim[0], u.dim[3], 128u) == 4u)
+                    dout == GPUOS_F32 ? sdpa_tile<16, GPUOS_F32, 4>(u, lane) : sdpa_tile<16, GPUOS_BF16, 4>(u, lane);
+                else
+                    dout == GPUOS_F32 ? sdpa_tile<16, GPUOS_F32, 1>(u, lane) : sdpa_tile<16, GPUOS_BF16, 1>(u, lane);
             } else {
-                dout == GPUOS_F32 ? sdpa_tile<8, GPUOS_F32>(u, lane) : sdpa_tile<8, GPUOS_BF16>(u, lane);
+                dout == GPUOS_F32 ? sdpa_tile<8, GPUOS_F32, 1>(u, lane) : sdpa_tile<8, GPUOS_BF16, 1>(u, lane);
             }
             break;
         case GPUOS_OP_GEMV:
