@@ -861,7 +861,7 @@ template <uint32_t DV, uint32_t DTO, uint32_t GP>
 __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t D = DV * 8u;
     constexpr uint32_t RPI = 64u / DV;
-    constexpr uint32_t NI = GP == 1u ? 8u : 4u;  // load instructions per chunk (fewer with more heads)
+    constexpr uint32_t NI = 8u;  // load instructions per chunk
     constexpr uint32_t CK = NI * RPI;     // keys per chunk
     constexpr uint32_t PSTRIDE = D + 4u;  // floats per partial record: m, l, pad, pad, acc[D]
     const uint32_t H = u.dim[0], C = u.dim[2];
