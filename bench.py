@@ -333,6 +333,10 @@ def main():
         X, P = W.xins, W.program
         progs = {W.OP_ADD: P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_ADD, 0, 1, 2)]),
                  W.OP_MUL: P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_MUL, 0, 1, 2)])}
+        # bound while the executor is paused: the table copy is a separate
+        # dispatch, which a profiler that serialises dispatches would queue
+        # behind a resident executor (binding during execution is tested)
+        assert G.gpuos_pause(ctx, 30_000_000_000) == 0
         t_reg = []
         for i in range(20):
             ta = time.perf_counter_ns()
@@ -340,6 +344,7 @@ def main():
             t_reg.append((time.perf_counter_ns() - ta) / 1e3)
         assert G.gpuos_register_expr(ctx, 200, progs[W.OP_ADD]) == 0
         assert G.gpuos_register_expr(ctx, 201, progs[W.OP_MUL]) == 0
+        assert G.gpuos_resume(ctx) == 0
         by = float(W.algorithmic_bytes(recs[sel[:len(sub)]]).sum())
         row = {"register_us_p50": float(np.median(t_reg)), "descriptors": int(len(sub)),
                "bytes_per_op": by / max(1, len(sub))}
