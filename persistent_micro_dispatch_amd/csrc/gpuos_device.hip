@@ -46,7 +46,7 @@ __device__ __forceinline__ void nap(uint32_t n) {
 }
 
 constexpr uint64_t STOP_DRAIN = 1, STOP_ABORT = 2;
-constexpr uint32_t DEP_BACKOFF_MAX = 16;
+constexpr uint32_t DEP_BACKOFF_MAX = 2;
 constexpr uint64_t NO_SCRATCH = ~0ull;
 
 // ------------------------------------------------------------------ worker
