@@ -142,7 +142,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="elementwise")
-    ap.add_argument("--waves", type=int, default=1, help="wave64s per workgroup (one workgroup per CU)")
+    ap.add_argument("--waves", type=int, default=0,
+                    help="wave64s per workgroup (one workgroup per CU); 0: 4 for rows, decode, decode_gqa "
+                         "and copy, else 1")
     ap.add_argument("--ring", type=int, default=256,
                     help="ring entries: descriptors in flight, which is also the window of hazard tracking")
     ap.add_argument("--units-per-wave", type=int, default=0, choices=(0, 1, 2),
@@ -154,6 +156,8 @@ def main():
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
+    if args.waves == 0:
+        args.waves = 4 if args.workload in ("rows", "decode", "decode_gqa", "copy") else 1
     if args.units_per_wave == 0:
         args.units_per_wave = 2 if args.workload in ("decode", "decode_gqa", "rows") else 1
     if args.gpus != 1:

@@ -102,7 +102,7 @@ struct ExecArgs {
 // how much scratch it needs.  Shared by the fetcher (device), the eager
 // launcher and host-side validation so that all three agree.
 // ---------------------------------------------------------------------------
-constexpr uint32_t EW_TILE_BYTES = 8192;   // per operand per element-wise tile
+constexpr uint32_t EW_TILE_BYTES = 4096;   // per operand per element-wise tile
 constexpr uint32_t EW_TILE_BYTES_GELU = 2048;  // GELU costs ~40 instructions per element: smaller units
 
 __host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind) {
