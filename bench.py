@@ -145,7 +145,7 @@ def main():
     ap.add_argument("--waves", type=int, default=0,
                     help="wave64s per workgroup (one workgroup per CU); 0: 4 for rows, decode, decode_gqa "
                          "and copy, else 1")
-    ap.add_argument("--ring", type=int, default=256,
+    ap.add_argument("--ring", type=int, default=512,
                     help="ring entries: descriptors in flight, which is also the window of hazard tracking")
     ap.add_argument("--units-per-wave", type=int, default=0, choices=(0, 1, 2),
                     help="units a worker wave holds at once (2 lets a ready unit overtake a waiting one); "

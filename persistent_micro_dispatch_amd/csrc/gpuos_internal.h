@@ -102,15 +102,23 @@ struct ExecArgs {
 // how much scratch it needs.  Shared by the fetcher (device), the eager
 // launcher and host-side validation so that all three agree.
 // ---------------------------------------------------------------------------
-constexpr uint32_t EW_TILE_BYTES = 4096;   // per operand per element-wise tile
+// Element-wise tiles, per operand.  Small and mid-sized ops take 4 KiB
+// units, which spreads a dependency level over more waves; ops of at least
+// EW_BIG_OP_BYTES per operand take units of 8 KiB, done as two 4 KiB tiles
+// one after the other, which halves their claims (many big ops at once are
+// bound by the rate of unit claims).
+constexpr uint32_t EW_TILE_BYTES = 4096;
+constexpr uint32_t EW_TILE_BYTES_BIG = 8192;
+constexpr uint64_t EW_BIG_OP_BYTES = 131072;
 constexpr uint32_t EW_TILE_BYTES_GELU = 2048;  // GELU costs ~40 instructions per element: smaller units
 
-__host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind) {
-    return kind == GPUOS_OP_GELU ? EW_TILE_BYTES_GELU : EW_TILE_BYTES;
+__host__ __device__ constexpr bool ew_big(uint64_t size, uint32_t es) { return size * es >= EW_BIG_OP_BYTES; }
+__host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind, bool big) {
+    return kind == GPUOS_OP_GELU ? EW_TILE_BYTES_GELU : big ? EW_TILE_BYTES_BIG : EW_TILE_BYTES;
 }
 // programs longer than 8 instructions cost as much per element as GELU
-__host__ __device__ constexpr uint32_t expr_tile_bytes(uint32_t kflags) {
-    return ((kflags >> 8) & 0xFFu) > 8u ? EW_TILE_BYTES_GELU : EW_TILE_BYTES;
+__host__ __device__ constexpr uint32_t expr_tile_bytes(uint32_t kflags, bool big) {
+    return ((kflags >> 8) & 0xFFu) > 8u ? EW_TILE_BYTES_GELU : big ? EW_TILE_BYTES_BIG : EW_TILE_BYTES;
 }
 constexpr uint32_t COPY_TILE_BYTES = 32768;
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
@@ -219,7 +227,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (di != dout) return bad();
             if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
             if ((d.kind == GPUOS_OP_ADD || d.kind == GPUOS_OP_MUL) && d.size > 0 && d.b == 0) return bad();
-            uint64_t t = cdiv(d.size, ew_tile_bytes(d.kind) / esz(di));
+            uint64_t t = cdiv(d.size, ew_tile_bytes(d.kind, ew_big(d.size, esz(di))) / esz(di));
             if (t > MAX_TILES) return bad();
             p.ntiles = t ? (uint32_t)t : 1u;
             return p;
@@ -298,7 +306,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (di != dout) return bad();
             if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
             if ((d.kflags & EXPR_USES_B) && d.size > 0 && d.b == 0) return bad();
-            uint64_t t = cdiv(d.size, expr_tile_bytes(d.kflags) / esz(di));
+            uint64_t t = cdiv(d.size, expr_tile_bytes(d.kflags, ew_big(d.size, esz(di))) / esz(di));
             if (t > MAX_TILES) return bad();
             p.ntiles = t ? (uint32_t)t : 1u;
             return p;

@@ -304,19 +304,19 @@ __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 v) {
     return o;
 }
 
-// One tile of ew_tile_bytes(K) per operand: CH chunks of 16 bytes per lane
-// (8 for add/mul/ReLU, 2 for GELU), all loads issued first.  The elements
-// after the last whole chunk (fewer than one chunk) are one per lane.
-// Misaligned operands take an element loop.
+// One tile of ew_tile_bytes(K, false) per operand: CH chunks of 16 bytes
+// per lane (4 for add/mul/ReLU, 2 for GELU), all loads issued first.  The
+// elements after the last whole chunk (fewer than one chunk) are one per
+// lane.  Misaligned operands take an element loop.
 template <uint32_t K, uint32_t DT>
-__device__ __forceinline__ void ew_tile(const Unit& u, uint32_t lane) {
+__device__ __forceinline__ void ew_tile(const Unit& u, uint32_t tile, uint32_t lane) {
     constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
-    constexpr uint32_t TILE = ew_tile_bytes(K) / ES;
+    constexpr uint32_t TILE = ew_tile_bytes(K, false) / ES;
     constexpr uint32_t VE = 16u / ES;
     constexpr uint32_t CH = TILE / VE / 64u;
     constexpr bool BIN = (K == GPUOS_OP_ADD || K == GPUOS_OP_MUL);
     constexpr bool RELU16 = (K == GPUOS_OP_RELU && DT == GPUOS_BF16);
-    const uint64_t start = (uint64_t)u.tile * TILE;
+    const uint64_t start = (uint64_t)tile * TILE;
     if (start >= u.size) return;
     const uint32_t cnt = (uint32_t)(u.size - start < TILE ? u.size - start : TILE);
     const uint8_t* A = (const uint8_t*)u.a + start * ES;
@@ -461,7 +461,7 @@ __device__ __forceinline__ void expr_tile(const Unit& u, uint32_t lane) {
     const uint32_t pw = lane < PROG_WORDS ? ld4((const uint8_t*)u.prog + 4u * lane) : 0u;
     const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)pw, 0);
     const uint32_t ni = w0 & 0xFFu;
-    const uint32_t tb = expr_tile_bytes(ni << 8);
+    const uint32_t tb = expr_tile_bytes(ni << 8, ew_big(u.size, ES));
     const uint32_t TILE = tb / ES, CH = tb / 16u / 64u;
     const uint64_t start = (uint64_t)u.tile * TILE;
     if (start >= u.size) return;
@@ -1264,6 +1264,24 @@ __device__ __forceinline__ void copy_tile(const Unit& u, uint32_t lane) {
     }
 }
 
+// add/mul/ReLU: a unit of a big op (see ew_big) is two consecutive tiles
+template <uint32_t K, uint32_t DT>
+__device__ __forceinline__ void ew_unit(const Unit& u, uint32_t lane) {
+    constexpr uint32_t ES = DT == GPUOS_F32 ? 4u : 2u;
+    constexpr uint32_t S = EW_TILE_BYTES_BIG / EW_TILE_BYTES;
+    if (ew_big(u.size, ES)) {
+#pragma unroll 1
+        for (uint32_t j = 0; j < S; ++j) ew_tile<K, DT>(u, u.tile * S + j, lane);
+    } else {
+        ew_tile<K, DT>(u, u.tile, lane);
+    }
+}
+template <uint32_t K>
+__device__ __forceinline__ void ew_dispatch(const Unit& u, uint32_t lane, bool bf) {
+    if (bf) ew_unit<K, GPUOS_BF16>(u, lane);
+    else ew_unit<K, GPUOS_F32>(u, lane);
+}
+
 // ------------------------------------------------------------- dispatch
 // Wave-uniform switch on the resolved kind (indirect calls would force a
 // conservative register and stack budget on AMDGPU).
@@ -1272,10 +1290,10 @@ __device__ __forceinline__ void run_unit(const Unit& u, uint32_t lane) {
     const bool bf = di == GPUOS_BF16;
     switch (u.kind) {
         case GPUOS_OP_NOP: break;
-        case GPUOS_OP_ADD: bf ? ew_tile<GPUOS_OP_ADD, GPUOS_BF16>(u, lane) : ew_tile<GPUOS_OP_ADD, GPUOS_F32>(u, lane); break;
-        case GPUOS_OP_MUL: bf ? ew_tile<GPUOS_OP_MUL, GPUOS_BF16>(u, lane) : ew_tile<GPUOS_OP_MUL, GPUOS_F32>(u, lane); break;
-        case GPUOS_OP_RELU: bf ? ew_tile<GPUOS_OP_RELU, GPUOS_BF16>(u, lane) : ew_tile<GPUOS_OP_RELU, GPUOS_F32>(u, lane); break;
-        case GPUOS_OP_GELU: bf ? ew_tile<GPUOS_OP_GELU, GPUOS_BF16>(u, lane) : ew_tile<GPUOS_OP_GELU, GPUOS_F32>(u, lane); break;
+        case GPUOS_OP_ADD: ew_dispatch<GPUOS_OP_ADD>(u, lane, bf); break;
+        case GPUOS_OP_MUL: ew_dispatch<GPUOS_OP_MUL>(u, lane, bf); break;
+        case GPUOS_OP_RELU: ew_dispatch<GPUOS_OP_RELU>(u, lane, bf); break;
+        case GPUOS_OP_GELU: bf ? ew_tile<GPUOS_OP_GELU, GPUOS_BF16>(u, u.tile, lane) : ew_tile<GPUOS_OP_GELU, GPUOS_F32>(u, u.tile, lane); break;
         case GPUOS_OP_EXPR: bf ? expr_tile<GPUOS_BF16>(u, lane) : expr_tile<GPUOS_F32>(u, lane); break;
         case GPUOS_OP_SUM: bf ? row_tile<GPUOS_OP_SUM, GPUOS_BF16>(u, lane) : row_tile<GPUOS_OP_SUM, GPUOS_F32>(u, lane); break;
         case GPUOS_OP_MAX: bf ? row_tile<GPUOS_OP_MAX, GPUOS_BF16>(u, lane) : row_tile<GPUOS_OP_MAX, GPUOS_F32>(u, lane); break;

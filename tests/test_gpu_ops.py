@@ -48,7 +48,7 @@ def _run_and_check(ctx, arrays, recs):
 @pytest.mark.parametrize("op", [W.OP_ADD, W.OP_MUL, W.OP_RELU, W.OP_GELU])
 def test_elementwise(ctx, op, dt):
     say(f"elementwise op={W.OP_NAMES[op]} dt={dt}")
-    sizes = [1, 7, 255, 256, 2047, 2048, 2049, 4095, 4097, 8192, 12345, 65536]
+    sizes = [1, 7, 255, 256, 2047, 2048, 2049, 4095, 4097, 8192, 12345, 65536, 16383, 16389, 40000, 32771, 65541]
     recs, arrays = [], []
     for i, n in enumerate(sizes):
         cap = n + 16
