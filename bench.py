@@ -17,6 +17,7 @@ op body, completion) over one seeded synthetic descriptor stream:
   decode_gqa             the same with 32 query heads sharing 8 key/value
                          heads (grouped-query attention, 4 GiB of cache)
   copy                   one 1 GiB COPY descriptor (calibrates HBM counters)
+  copy64                 the same 1 GiB copied by 64 independent 16 MiB descriptors
   mixed                  10 tokens x 32 layers x 11 ops at hidden 1024 (LN,
                          GEMV 1024x3072, RoPE, KV append, SDPA, add, LN, GEMV
                          1024x3072, GELU, GEMV 3072x1024, add); with --gemm a
@@ -104,15 +105,19 @@ def make_stream(name):
         s.bursts = np.full(len(s) // 8, 8)
         desc = ("PR1: 1,000 fp32 descriptors over 16 vectors of 4096 values U[-1,1]; op uniform over "
                 "{add, mul, relu}; operands and outputs uniform over the pool")
-    elif name == "copy":
-        s = W.Stream("copy", [W.Buffer("src", W.F32, 1 << 28, ("uniform", -1.0, 1.0), 77), W.Buffer("dst", W.F32, 1 << 28, ("zeros",))],
-                     np.zeros(1, W.REC_DTYPE), np.array([1]))
+    elif name in ("copy", "copy64"):
+        parts = 1 if name == "copy" else 64
+        s = W.Stream(name, [W.Buffer("src", W.F32, 1 << 28, ("uniform", -1.0, 1.0), 77), W.Buffer("dst", W.F32, 1 << 28, ("zeros",))],
+                     np.zeros(parts, W.REC_DTYPE), np.array([parts]))
         s.recs["buf"] = -1
         s.recs["op"] = W.OP_COPY
-        s.recs["size"] = 1 << 30
-        s.recs["buf"][0, W.A], s.recs["buf"][0, W.OUT] = 0, 1
+        s.recs["size"] = (1 << 30) // parts
+        s.recs["buf"][:, W.A], s.recs["buf"][:, W.OUT] = 0, 1
+        s.recs["off"][:, W.A] = np.arange(parts) * ((1 << 30) // parts)
+        s.recs["off"][:, W.OUT] = s.recs["off"][:, W.A]
         fill = "device"
-        desc = "one 1 GiB copy descriptor (counter calibration: 1 GiB read + 1 GiB written)"
+        desc = ("one 1 GiB copy descriptor (counter calibration: 1 GiB read + 1 GiB written)" if parts == 1 else
+                "1 GiB copied by 64 independent descriptors of 16 MiB")
     elif name == "rows":
         s, fill = W.make_rows(), "device"
         desc = ("row ops: 50,000 descriptors of [r, h] fp32, r in {1,2,...,64}, h in {768,1024,2048,4096}, "
@@ -157,7 +162,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.waves == 0:
-        args.waves = 4 if args.workload in ("rows", "decode", "decode_gqa", "copy") else 1
+        args.waves = 4 if args.workload in ("rows", "decode", "decode_gqa", "copy", "copy64") else 1
     if args.units_per_wave == 0:
         args.units_per_wave = 2 if args.workload in ("decode", "decode_gqa", "rows") else 1
     if args.gpus != 1:

@@ -52,11 +52,13 @@ constexpr uint64_t NO_SCRATCH = ~0ull;
 // ------------------------------------------------------------------ worker
 // A worker wave holds up to SLOTS claimed units and runs whichever of them
 // has its dependencies satisfied (the oldest such), so a unit waiting on a
-// long chain does not hold back a ready unit claimed after it.  Claims stay
-// in queue order, so the executor always progresses: if the oldest
-// unfinished unit is unclaimed, every claimed unit is older, hence finished,
-// and a wave with a free slot claims it; if it is claimed, its holder finds
-// it ready.  No wave waits on one unit alone.
+// long chain does not hold back a ready unit claimed after it.  Each claim
+// shard hands out its units in queue order, so the executor always
+// progresses: if the oldest unfinished unit is unclaimed, every unit its
+// shard has handed out is older, hence finished, and a wave of that shard
+// (every shard has one, and all waves are resident) claims it once a slot
+// is free; if it is claimed, its holder finds it ready.  No wave waits on
+// one unit alone.
 // SLOTS is 1 or 2 (gpuos_init_params.units_per_wave): with one, a wave
 // claims its next unit only after running the current one; two let a ready
 // unit overtake one that waits, at the price of holding two claims.
@@ -92,6 +94,12 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
     }
     bool stop_seen = false;
     uint32_t bo = 1;
+    // this wave's claim shard: workgroups take the shards in turn, so that
+    // (with workgroups placed on the XCDs in turn) each XCD claims from
+    // counters of its own
+    const uint32_t S = A.shards;
+    const uint32_t shard = blockIdx.x % S;
+    uint64_t* const claim_ctr = &C->claim[shard].next;
     for (;;) {
         // One dependency load per waiting slot and the queue tail, issued
         // together.  Claims come after the run below, so their atomic round
@@ -226,8 +234,8 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         for (uint32_t k = 0; k < SLOTS; ++k) {
             if (state[k] != SL_FREE) continue;
             uint64_t c = 0;
-            if (lane == 0) c = __hip_atomic_fetch_add(&C->q_head, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            su[k] = rl64(c, 0);
+            if (lane == 0) c = __hip_atomic_fetch_add(claim_ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            su[k] = rl64(c, 0) * S + shard;
             state[k] = SL_CLAIMED;
         }
         asm volatile("" ::: "memory");

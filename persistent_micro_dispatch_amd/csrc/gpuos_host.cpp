@@ -257,6 +257,18 @@ void refresh_wm(gpuos_ctx* c) {
     }
 }
 
+// Claim shards: workgroup b claims from shard b % shards, so every shard
+// needs a worker wave (workgroup 0's first wave is the fetcher), and all
+// of them must be resident at once, or a shard could wait for a workgroup
+// that never starts.  One workgroup per compute unit at most guarantees
+// that; otherwise one shared counter is used.
+static uint32_t claim_shards(uint32_t num_wgs, uint32_t waves_per_wg, uint32_t cu_count) {
+    if (num_wgs > cu_count) return 1;
+    const uint32_t worker_wgs = waves_per_wg > 1 ? num_wgs : num_wgs - 1;
+    uint32_t s = worker_wgs < CLAIM_SHARDS_MAX ? worker_wgs : CLAIM_SHARDS_MAX;
+    return s ? s : 1;
+}
+
 int executor_launch(gpuos_ctx* c) {
     if (c->loopback || c->running) return GPUOS_OK;
     hipError_t e = hipMemsetAsync(c->dctl, 0, sizeof(DevCtl), c->exec);
@@ -287,6 +299,7 @@ int executor_launch(gpuos_ctx* c) {
     a.mask = c->mask;
     a.qmask = c->Q - 1;
     a.backoff_max = c->P.backoff_max;
+    a.shards = claim_shards(c->P.num_wgs, c->P.waves_per_wg, c->cu_count);
     if (c->trace && hipMemsetAsync(c->trace, 0, c->trace_cap * sizeof(gpuos_trace_rec), c->exec) != hipSuccess)
         return GPUOS_E_HIP;
     if (hipEventRecord(c->ev_start, c->exec) != hipSuccess) return GPUOS_E_HIP;

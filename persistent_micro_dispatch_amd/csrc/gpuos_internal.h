@@ -59,8 +59,17 @@ struct HostCtl {
 };
 
 // Control words in device memory (one 128-byte line each).
+// Unit tickets are handed out by CLAIM_SHARDS_MAX counters, each on a
+// cache line of its own: shard x owns the units whose queue index is
+// x modulo the shard count, and its counter numbers them in queue order.
+// One counter for all waves saturates under contention (the more waves
+// claim, the fewer claims per second succeed).
+constexpr uint32_t CLAIM_SHARDS_MAX = 8;
+struct alignas(256) ClaimLine {
+    uint64_t next;  // next ticket of this shard (workers fetch_add)
+};
 struct DevCtl {
-    alignas(128) uint64_t q_head;    // next unit ticket (workers fetch_add)
+    ClaimLine claim[CLAIM_SHARDS_MAX];
     alignas(128) uint64_t q_tail;    // units published by the fetcher
     alignas(128) uint64_t stop;      // fetcher -> workers
     alignas(128) uint64_t error;     // sticky device error
@@ -94,7 +103,7 @@ struct ExecArgs {
     uint32_t mask;              // ring_entries - 1
     uint32_t qmask;             // unit-queue entries - 1
     uint32_t backoff_max;
-    uint32_t pad;
+    uint32_t shards;            // claim shards in use (1..CLAIM_SHARDS_MAX)
 };
 
 // ---------------------------------------------------------------------------

@@ -53,6 +53,18 @@ def test_pr1_bit_exact_small_ring_and_one_wave(ring, waves, upw):
         assert bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype).all()
 
 
+# few workgroups: claim shards of one or two workgroups each (with one wave
+# per workgroup, workgroup 0 holds only the fetcher)
+@pytest.mark.parametrize("num_wgs,waves,upw", [(2, 1, 1), (3, 1, 1), (9, 1, 2), (5, 2, 1), (12, 4, 2)])
+def test_pr1_bit_exact_few_workgroups(num_wgs, waves, upw):
+    s = W.make_pr1()
+    s.bursts = np.full(125, 8)
+    say(f"pr1 num_wgs={num_wgs} waves={waves} units_per_wave={upw}")
+    gpu, orc = _final_pools(s, 1000, ring_entries=64, num_wgs=num_wgs, waves_per_wg=waves, units_per_wave=upw)
+    for i, b in enumerate(s.buffers):
+        assert bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype).all()
+
+
 @pytest.mark.parametrize("upw", [1, 2])
 def test_elementwise_exact_ops_bit_exact(upw):
     s = W.make_elementwise(n_desc=5000, ops=(W.OP_ADD, W.OP_MUL, W.OP_RELU))
