@@ -157,6 +157,8 @@ def main():
                          "0: 2 for decode, decode_gqa and rows, else 1")
     ap.add_argument("--num-wgs", type=int, default=0,
                     help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
+    ap.add_argument("--backoff", type=int, default=0,
+                    help="s_sleep cap of idle waits, 1..127 (0: the library's default)")
     ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop (mixed workload)")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -206,7 +208,7 @@ def main():
     torch.cuda.current_stream().synchronize()
     log(f"hbm probe: read {hbm_probe['read_gbs']:.0f} GB/s, copy {hbm_probe['copy_gbs']:.0f} GB/s")
     ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring, num_wgs=args.num_wgs,
-                       units_per_wave=args.units_per_wave)
+                       units_per_wave=args.units_per_wave, backoff_max=args.backoff)
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     st0 = G.gpuos_stats_get(ctx)
 

@@ -109,7 +109,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         for (uint32_t k = 0; k < SLOTS; ++k) {
             const bool need = state[k] == SL_WAIT && sdl[k] != 0;
             const uint64_t d = need ? sseq[k] - sdl[k] : 0;
-            dv[k] = ld_agent(&A.done[d & A.mask]);
+            dv[k] = ld_agent(&A.done[(d & A.mask) * DONE_STRIDE]);
         }
         const uint64_t tail = ld_agent(&C->q_tail);
         const uint64_t now = wall_clock64();
@@ -125,7 +125,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
                 if (srlo[k] < sseq[k]) {
                     // range dependency: advance over up to 64 completed seqs per check
                     const uint64_t x = srlo[k] + lane;
-                    const bool okr = x >= sseq[k] || ld_agent(&A.done[x & A.mask]) >= x;
+                    const bool okr = x >= sseq[k] || ld_agent(&A.done[(x & A.mask) * DONE_STRIDE]) >= x;
                     const uint64_t bal = __ballot(okr);
                     srlo[k] += bal == ~0ull ? 64u : (uint64_t)(__ffsll((long long)~bal) - 1);
                 }
@@ -198,7 +198,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             }
             if (last) {
                 if (lane == 0) {
-                    st_agent(&A.done[slot], seq);
+                    st_agent(&A.done[slot * DONE_STRIDE], seq);
                     if (status != GPUOS_ST_OK) {
                         __hip_atomic_store(&A.status[slot], status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                         stores_done();  // the status reaches the host before the stamp
@@ -422,7 +422,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             for (;;) {
                 if (cw >= f) break;
                 const uint64_t x = cw + lane;
-                const bool ok = x >= f || ld_agent(&A.done[x & mask]) >= x;
+                const bool ok = x >= f || ld_agent(&A.done[(x & mask) * DONE_STRIDE]) >= x;
                 const uint64_t bal = __ballot(ok);
                 if (bal == ~0ull) { cw = cw + 64 < f ? cw + 64 : f; continue; }
                 cw += (uint64_t)(__ffsll((long long)~bal) - 1);

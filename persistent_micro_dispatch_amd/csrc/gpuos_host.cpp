@@ -536,7 +536,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     HIPCHK(hipMalloc((void**)&c->dctl, sizeof(DevCtl)));
     HIPCHK(hipMalloc((void**)&c->mirror, N * sizeof(gpuos_desc)));
     HIPCHK(hipMalloc((void**)&c->meta, N * sizeof(MirrorMeta)));
-    HIPCHK(hipMalloc((void**)&c->done, N * 8));
+    HIPCHK(hipMalloc((void**)&c->done, N * 8 * DONE_STRIDE));
     HIPCHK(hipMalloc((void**)&c->tiles_done, N * 4));
     HIPCHK(hipMalloc((void**)&c->depd, N * 8 * DEPX_WORDS));
     HIPCHK(hipMalloc((void**)&c->queue, (size_t)c->Q * 8));
@@ -560,9 +560,9 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     HIPCHK(hipEventCreate(&c->ev_start));
     HIPCHK(hipEventCreate(&c->ev_stop));
     {
-        std::vector<uint64_t> d(N);
-        for (size_t i = 0; i < N; ++i) d[i] = i;
-        HIPCHK(hipMemcpyAsync(c->done, d.data(), N * 8, hipMemcpyHostToDevice, c->aux));
+        std::vector<uint64_t> d(N * DONE_STRIDE, 0);
+        for (size_t i = 0; i < N; ++i) d[i * DONE_STRIDE] = i;
+        HIPCHK(hipMemcpyAsync(c->done, d.data(), N * 8 * DONE_STRIDE, hipMemcpyHostToDevice, c->aux));
         HIPCHK(hipMemsetAsync(c->tiles_done, 0, N * 4, c->aux));
         HIPCHK(hipMemsetAsync(c->meta, 0, N * sizeof(MirrorMeta), c->aux));
         HIPCHK(hipMemsetAsync(c->scratch, 0, P.scratch_bytes, c->aux));

@@ -119,7 +119,17 @@ struct ExecArgs {
 constexpr uint32_t EW_TILE_BYTES = 4096;
 constexpr uint32_t EW_TILE_BYTES_BIG = 8192;
 constexpr uint64_t EW_BIG_OP_BYTES = 131072;
-constexpr uint32_t EW_TILE_BYTES_GELU = 2048;  // GELU costs ~40 instructions per element: smaller units
+#ifndef GPUOS_GELU_TILE
+#define GPUOS_GELU_TILE 2048
+#endif
+// done[] words per ring slot: one per 128-byte line, so that waves polling
+// different slots, and the store that completes one, do not share a line
+// (element-wise stream +3% with one wave per workgroup, +8% with four).
+#ifndef GPUOS_DONE_STRIDE
+#define GPUOS_DONE_STRIDE 16
+#endif
+constexpr uint32_t DONE_STRIDE = GPUOS_DONE_STRIDE;
+constexpr uint32_t EW_TILE_BYTES_GELU = GPUOS_GELU_TILE;  // GELU costs ~40 instructions per element: smaller units
 
 __host__ __device__ constexpr bool ew_big(uint64_t size, uint32_t es) { return size * es >= EW_BIG_OP_BYTES; }
 __host__ __device__ constexpr uint32_t ew_tile_bytes(uint32_t kind, bool big) {

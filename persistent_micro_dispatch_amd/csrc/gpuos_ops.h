@@ -63,13 +63,17 @@ struct Unit {
 // ------------------------------------------------------------------ scalars
 __device__ __forceinline__ float bf2f(uint32_t h) { return __uint_as_float(h << 16); }
 
-// fp32 -> bf16, round to nearest even on the bit pattern; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x0040u) & 0xFFFFu;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  gfx950
+// converts two floats per instruction (v_cvt_pk_bf16_f32, under the default
+// round-to-nearest-even mode); over all 2^32 inputs it matches rounding the
+// bit pattern (add 0x7FFF plus the lowest kept bit, truncate), NaN aside.
+typedef __bf16 bf16v2 __attribute__((ext_vector_type(2)));
+typedef float f32v2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+    const f32v2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16v2));
 }
+__device__ __forceinline__ uint32_t f2bf(float f) { return f2bf2(f, 0.0f) & 0xFFFFu; }
 
 // double -> bf16 with one rounding: round to odd into fp32 (24 >= 8 + 2
 // bits), then to nearest even (Boldo and Melquiond, "Emulation of FMA and
@@ -186,8 +190,8 @@ __device__ __forceinline__ u32x4 pack(const float* f) {
         v.x = __float_as_uint(f[0]); v.y = __float_as_uint(f[1]);
         v.z = __float_as_uint(f[2]); v.w = __float_as_uint(f[3]);
     } else {
-        v.x = f2bf(f[0]) | (f2bf(f[1]) << 16); v.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
-        v.z = f2bf(f[4]) | (f2bf(f[5]) << 16); v.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
+        v.x = f2bf2(f[0], f[1]); v.y = f2bf2(f[2], f[3]);
+        v.z = f2bf2(f[4], f[5]); v.w = f2bf2(f[6], f[7]);
     }
     return v;
 }
@@ -196,8 +200,12 @@ __device__ __forceinline__ float relu_f(float x) { return x > 0.0f ? x : (x != x
 
 // GELU, tanh approximation, evaluated as x / (1 + exp(-2u)) with
 // u = sqrt(2/pi) (x + 0.044715 x^3) (the same function; no cancellation).
-// For |x| < 3 (|2u| < 7) fp32 arithmetic keeps the relative error near
-// 1e-6.  Beyond that the exponent a = -2u is formed in double and split as
+// For x > -3 the exponent a = -2u stays below 7.3, and fp32 arithmetic with
+// the hardware exp2 and reciprocal keeps the relative error below 1.1e-6
+// (largest over every fp32 x > -3, against a double evaluation; the result's
+// sensitivity to an absolute error in a is at most 1).  For x <= -3 the
+// result is about x e^{-a} with a large, so a must be exact to well below
+// 1e-5 in absolute terms: there a is formed in double and split as
 // k ln2 + r with |r| <= ln2/2, so only r goes through the fp32 exp; for
 // a > 0 (x < 0) the result x e^{-a} / (1 + e^{-a}) is formed as a normal
 // float and scaled by 2^-k last, so results in the denormal range are
@@ -218,9 +226,12 @@ __device__ __forceinline__ float gelu_wide(float x) {
     return x / (1.0f + ldexpf(expf(r), (int)k));
 }
 __device__ __forceinline__ float gelu_f(float x) {
-    if (!(fabsf(x) < 3.0f)) return gelu_wide(x);   // also NaN and infinities
-    const float a = -1.5957691216057308f * (x + 0.044715f * x * x * x);
-    return x / (1.0f + expf(a));
+    if (!(x > -3.0f)) return gelu_wide(x);   // also NaN and -inf
+    // a = -2 sqrt(2/pi) (x + 0.044715 x^3) = x (-1.5957691 - 0.0713548 x^2);
+    // +inf gives a = -inf, e = 0 and the result +inf
+    const float a = x * fmaf(-0.0713548162726f, x * x, -1.5957691216057308f);
+    const float e = __builtin_amdgcn_exp2f(a * 1.44269504f);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // max / min under a total order: NaN wins, -0 < +0.
