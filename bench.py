@@ -92,6 +92,35 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def dag_levels(recs):
+    """Depth of the dependency DAG of an element-wise stream under sequential
+    semantics (read-after-write, write-after-read, write-after-write).  Every
+    access of these streams covers a prefix of one pool tensor, so any two
+    accesses to the same tensor overlap and tensor granularity is exact."""
+    import workloads as W
+    assert (recs["off"][:, [W.A, W.B, W.OUT]] == 0).all()
+    last_w, readers = {}, {}
+    depth = np.zeros(len(recs), np.int64)
+    ops, bufs = recs["op"], recs["buf"]
+    for i in range(len(recs)):
+        ins = [int(bufs[i, W.A])] + ([int(bufs[i, W.B])] if ops[i] in (W.OP_ADD, W.OP_MUL) else [])
+        o = int(bufs[i, W.OUT])
+        d = 0
+        for t in ins:
+            if t in last_w:
+                d = max(d, depth[last_w[t]])
+        if o in last_w:
+            d = max(d, depth[last_w[o]])
+        for r in readers.get(o, ()):
+            d = max(d, depth[r])
+        depth[i] = d + 1
+        for t in ins:
+            readers.setdefault(t, []).append(i)
+        last_w[o] = i
+        readers[o] = []
+    return int(depth.max())
+
+
 def make_stream(name):
     import workloads as W
     fill = "host"
@@ -438,22 +467,35 @@ def main():
             "kernel": "gpuos_executor_s2" if args.units_per_wave == 2 else "gpuos_executor",
             "launch_ms": mean_launch_ms, "bytes_per_launch": step_bytes}
 
+    levels = dag_levels(recs) if args.workload in ("elementwise", "pr1") else None
     cpu = None
-    if not args.no_cpu and fill == "host":
+    if not args.no_cpu:
+        # the oracle on a bounded prefix of the same stream, grown until it
+        # takes about 10 s.  Host-filled streams use the same inputs as the
+        # GPU; device-filled ones (pools of GiBs) use zero-filled host
+        # buffers of the same shapes, which leaves the oracle's work (every
+        # op runs the same loops whatever the values) unchanged.
         import oracle
-        n_cpu = min(nd, 1000)
-        p = oracle.Pool([a.copy() for a in arrays])
-        ta = time.perf_counter()
+        if fill == "host":
+            def make_pool():
+                return oracle.Pool([a.copy() for a in arrays])
+            n_cpu, what = min(nd, 1000), "the same inputs"
+        else:
+            def make_pool():
+                return oracle.Pool([np.zeros(b.nbytes, np.uint8) for b in stream.buffers])
+            n_cpu, what = min(nd, 8), "zero-filled host buffers of the stream's shapes"
         while True:
+            p = make_pool()
+            ta = time.perf_counter()
             p.run(recs[:n_cpu])
             el = time.perf_counter() - ta
+            del p
             if el > 10.0 or n_cpu >= nd:
                 break
-            n_cpu = min(nd, n_cpu * 4)
-            p = oracle.Pool([a.copy() for a in arrays])
-            ta = time.perf_counter()
+            n_cpu = min(nd, n_cpu * (4 if el < 2.0 else 2))
         cpu = {"value": n_cpu / el, "unit": "micro-ops/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {n_cpu} descriptors of the same stream, sequential C oracle (fp64), one thread"}
+               "sample": f"first {n_cpu} of {nd} descriptors of the same stream on {what}, "
+                         f"sequential C oracle (fp64), one thread, {el:.1f} s"}
 
     steps_total = max(1, args.steps + args.warmup)
     out = {
@@ -478,6 +520,8 @@ def main():
         "dependent_chain_us_per_op": chain_s / len(chain) * 1e6,
         "dependent_chain_ok": chain_ok,
         "stream_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "dag_levels": levels,
+        "us_per_dag_level": ms_per_step * 1e3 / levels if levels else None,
         "units_per_step": (st["units"] - st0["units"]) / steps_total,
         "dep_waits_per_step": (st["dep_waits"] - st0["dep_waits"]) / steps_total,
         "fetch_batches_per_step": (st["fetch_batches"] - st0["fetch_batches"]) / steps_total,

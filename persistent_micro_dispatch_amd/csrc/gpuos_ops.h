@@ -306,13 +306,17 @@ __device__ __forceinline__ uint32_t relu_bf16(uint32_t h) {
     if ((h & 0x7FFFu) > 0x7F80u) return h;  // NaN
     return (h & 0x8000u) ? 0u : h;          // negatives and -0 -> +0
 }
+// Both halves of a dword at once: a half is NaN exactly when its magnitude
+// plus 0x7F carries into bit 15 (magnitudes are at most 0x7FFF, so no carry
+// crosses into the other half); halves with the sign set and not NaN become
+// +0, through a mask spread from bit 15 over the half by a multiply.
+__device__ __forceinline__ uint32_t relu_bf16x2(uint32_t v) {
+    const uint32_t nan = ((v & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u;
+    const uint32_t z = v & 0x80008000u & ~nan;
+    return v & ~((z >> 15) * 0xFFFFu);
+}
 __device__ __forceinline__ u32x4 relu_bf16x8(u32x4 v) {
-    u32x4 o;
-    o.x = relu_bf16(v.x & 0xFFFFu) | (relu_bf16(v.x >> 16) << 16);
-    o.y = relu_bf16(v.y & 0xFFFFu) | (relu_bf16(v.y >> 16) << 16);
-    o.z = relu_bf16(v.z & 0xFFFFu) | (relu_bf16(v.z >> 16) << 16);
-    o.w = relu_bf16(v.w & 0xFFFFu) | (relu_bf16(v.w >> 16) << 16);
-    return o;
+    return u32x4{relu_bf16x2(v.x), relu_bf16x2(v.y), relu_bf16x2(v.z), relu_bf16x2(v.w)};
 }
 
 // One tile of ew_tile_bytes(K, false) per operand: CH chunks of 16 bytes
