@@ -305,6 +305,9 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     uint32_t cur_ver = 0xFFFFFFFFu, bo = 1;
     uint64_t batches = 0, fetched = 0;
     uint64_t stop_code = STOP_DRAIN;
+    // capacity watermarks (unit queue, scratch) as of the last look at
+    // done[]: older than the true ones, hence conservative
+    uint64_t cw_units = 0, cw_scr = 0;
     for (;;) {
         const uint64_t sl = f + lane;
         const uint64_t st = ld_sys(&A.stamp[sl & mask]);
@@ -415,26 +418,31 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             if ((int)lane > j) my_mark = sv;
         }
         const uint64_t sv_end_i = my_sv != NO_SCRATCH ? my_sv + need : my_mark;
-        // capacity: units and scratch still held by incomplete descriptors
+        // capacity: units and scratch still held by incomplete descriptors.
+        // The watermarks of the last look usually leave room for the whole
+        // batch; done[] is read again only when they do not.
         uint32_t fit;
-        for (;;) {
-            // advance the completion watermark cw
-            for (;;) {
-                if (cw >= f) break;
-                const uint64_t x = cw + lane;
-                const bool ok = x >= f || ld_agent(&A.done[(x & mask) * DONE_STRIDE]) >= x;
-                const uint64_t bal = __ballot(ok);
-                if (bal == ~0ull) { cw = cw + 64 < f ? cw + 64 : f; continue; }
-                cw += (uint64_t)(__ffsll((long long)~bal) - 1);
-                break;
+        for (bool fresh = false;; fresh = true) {
+            if (fresh) {
+                // advance the completion watermark cw
+                for (;;) {
+                    if (cw >= f) break;
+                    const uint64_t x = cw + lane;
+                    const bool ok = x >= f || ld_agent(&A.done[(x & mask) * DONE_STRIDE]) >= x;
+                    const uint64_t bal = __ballot(ok);
+                    if (bal == ~0ull) { cw = cw + 64 < f ? cw + 64 : f; continue; }
+                    cw += (uint64_t)(__ffsll((long long)~bal) - 1);
+                    break;
+                }
+                cw_units = cw < f ? A.meta[cw & mask].ubegin : u_next;
+                cw_scr = cw < f ? A.meta[cw & mask].scratch_mark : sv_next;
             }
-            const uint64_t cw_units = cw < f ? A.meta[cw & mask].ubegin : u_next;
-            const uint64_t cw_scr = cw < f ? A.meta[cw & mask].scratch_mark : sv_next;
             const bool ok = !act || ((u_next + inc - cw_units <= Q) && (sv_end_i - cw_scr <= S));
             const uint64_t fb = __ballot(ok);
             fit = fb == ~0ull ? 64u : (uint32_t)(__ffsll((long long)~fb) - 1);
             if (fit > count) fit = count;
-            if (fit > 0) break;
+            if (fit == count || (fresh && fit > 0)) break;
+            if (!fresh) continue;
             if (ld_sys(&A.hctl->abort)) { stop_code = STOP_ABORT; break; }
             nap(A.backoff_max);
         }
