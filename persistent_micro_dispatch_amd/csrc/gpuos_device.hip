@@ -47,6 +47,14 @@ __device__ __forceinline__ void nap(uint32_t n) {
 
 constexpr uint64_t STOP_DRAIN = 1, STOP_ABORT = 2;
 constexpr uint32_t DEP_BACKOFF_MAX = 2;
+#ifndef GPUOS_NEAR_UNITS
+#define GPUOS_NEAR_UNITS 64
+#endif
+constexpr uint64_t NEAR_UNITS = GPUOS_NEAR_UNITS;
+#ifndef GPUOS_FETCH_BACKOFF_MAX
+#define GPUOS_FETCH_BACKOFF_MAX 8
+#endif
+constexpr uint32_t FETCH_BACKOFF_MAX = GPUOS_FETCH_BACKOFF_MAX;
 constexpr uint64_t NO_SCRATCH = ~0ull;
 
 // ------------------------------------------------------------------ worker
@@ -281,9 +289,15 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         if (stp == STOP_ABORT) break;
         if (stp) { stop_seen = true; continue; }
         // dependency waits back off to at most DEP_BACKOFF_MAX x 64 clocks
-        // (the awaited op is in flight); waits for publication up to
-        // backoff_max
-        const uint32_t cap = any_wait ? DEP_BACKOFF_MAX : A.backoff_max;
+        // (the awaited op is in flight).  A wave waiting for publication
+        // whose ticket is among the next NEAR_UNITS units to be published
+        // does the same (its unit is the next work to arrive); the others
+        // back off up to backoff_max.
+        bool near = false;
+#pragma unroll
+        for (uint32_t k = 0; k < SLOTS; ++k)
+            near = near || (state[k] == SL_CLAIMED && su[k] - tail < NEAR_UNITS);
+        const uint32_t cap = any_wait || near ? DEP_BACKOFF_MAX : A.backoff_max;
         nap(bo);
         bo = bo * 2 < cap ? bo * 2 : cap;
     }
@@ -308,22 +322,27 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     // capacity watermarks (unit queue, scratch) as of the last look at
     // done[]: older than the true ones, hence conservative
     uint64_t cw_units = 0, cw_scr = 0;
+    // the fetcher's idle polls go to host memory and cost the device's
+    // memory system nothing, so its backoff stops early: a descriptor
+    // committed to an idle ring is seen sooner
+    const uint32_t fcap = A.backoff_max < FETCH_BACKOFF_MAX ? A.backoff_max : FETCH_BACKOFF_MAX;
     for (;;) {
+        // the stamps and both control words in one round trip over PCIe
         const uint64_t sl = f + lane;
         const uint64_t st = ld_sys(&A.stamp[sl & mask]);
+        const uint64_t abt = ld_sys(&A.hctl->abort);
+        const uint64_t stp = ld_sys(&A.hctl->stop);
         const uint64_t rb = __ballot(st == sl + 1);
         uint32_t count = rb == ~0ull ? 64u : (uint32_t)(__ffsll((long long)~rb) - 1);
         if (count == 0) {
-            const uint64_t abt = ld_sys(&A.hctl->abort);
             if (abt) { stop_code = STOP_ABORT; break; }
-            const uint64_t stp = ld_sys(&A.hctl->stop);
             if (stp) {
                 // the host commits before it sets stop: look once more
                 if (ld_sys(&A.stamp[f & mask]) == f + 1) continue;
                 break;
             }
             nap(bo);
-            bo = bo * 2 < A.backoff_max ? bo * 2 : A.backoff_max;
+            bo = bo * 2 < fcap ? bo * 2 : fcap;
             continue;
         }
         bo = 1;
