@@ -154,7 +154,8 @@ typedef struct gpuos_init_params {
     uint32_t num_wgs;           /* executor workgroups, at most 4 per CU, and at least
                                    2 waves in all (one fetches); 0 -> one per CU */
     uint32_t waves_per_wg;      /* wave64s per workgroup, 1..4; 0 -> 4 */
-    uint32_t backoff_max;       /* s_sleep cap, 1..127; 0 -> 64 */
+    uint32_t backoff_max;       /* s_sleep cap of idle waits, 1..127; 0 -> 64 (the fetcher
+                                   wave, whose polls go over PCIe, stops at 8) */
     uint32_t flags;             /* GPUOS_INIT_* */
     void* hip_stream;           /* optional hipStream_t for the executor (must be
                                    non-blocking); NULL -> the library creates one */
