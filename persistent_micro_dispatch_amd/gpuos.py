@@ -121,6 +121,16 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    # One HIP runtime per process: torch ships its own libamdhip64.so.7, and
+    # whichever copy is loaded first serves every library that needs that
+    # soname.  Loading torch first binds libgpuos.so to torch's runtime, the
+    # same one torch's allocations and streams come from; loading libgpuos.so
+    # first would leave torch on a runtime it was not built with (its GPU
+    # initialisation then fails).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, u32, u64, i64 = ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64
     sig = {

@@ -66,6 +66,47 @@ def test_elementwise(ctx, op, dt):
     say("  worst", max(r["worst"] for r in res))
 
 
+@pytest.mark.parametrize("dt", [W.F32, W.BF16])
+def test_gelu_dense_sweep(ctx, dt):
+    """GELU over a dense grid of [-14, 14], every fp32 value in the last few
+    ulps on both sides of -3 (where the body switches from its fp32 path to
+    the one with a double-precision exponent), the tails where the result
+    becomes subnormal and underflows, and the specials."""
+    say(f"gelu sweep dt={dt}")
+    grid = np.linspace(-14.0, 14.0, 1 << 16, dtype=np.float32)
+    m3 = np.float32(-3.0)
+    near = np.concatenate([m3 + np.arange(-64, 65, dtype=np.float32) * np.spacing(m3),
+                           np.nextafter(m3, np.float32(0)) - np.arange(8, dtype=np.float32) * 1e-7])
+    tails = -np.geomspace(9.0, 1e4, 2048).astype(np.float32)
+    sp = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e-45, -1e-45, 1e-38, -1e-38, 3e38, -3e38], np.float32)
+    x = np.concatenate([grid, near, tails, -tails, sp]).astype(np.float32)
+    xs = x if dt == W.F32 else bf16(x)
+    arrays = [xs, np.zeros_like(xs)]
+    res = _run_and_check(ctx, arrays, rec(W.OP_GELU, dtype=dt, size=len(x), a=0, out=1))
+    say("  worst", max(r["worst"] for r in res))
+
+
+def test_bf16_rounding_ties_through_add(ctx):
+    """bf16 add of pairs whose exact fp32 sums fall exactly half-way between
+    two bf16 values (both parities), just above and below half-way, and
+    overflow to infinity: the rounding of the fp32 result to bf16 decides
+    every bit, and must equal the oracle's round-to-nearest-even."""
+    say("bf16 rounding ties")
+    base = np.ldexp(np.float32(1) + np.arange(128, dtype=np.float32) / 128, np.arange(-20, 20)[:, None]).astype(
+        np.float32).reshape(-1)                               # every bf16 significand, many exponents
+    ulp = np.ldexp(np.float32(1), (np.frexp(base)[1] - 8)).astype(np.float32)   # bf16 ulp of base
+    a_parts, b_parts = [], []
+    for frac in (0.5, 0.5 + 2.0 ** -8, 0.5 - 2.0 ** -8, 0.25, 0.75, 1.5):
+        a_parts.append(base)
+        b_parts.append((ulp * np.float32(frac)).astype(np.float32))
+    a = np.concatenate(a_parts + [np.float32([3.3895e38, -3.3895e38])])
+    b = np.concatenate(b_parts + [np.float32([1.5e36, -1.5e36])])
+    # b must be a bf16 value itself for the test to be about the sum's rounding
+    ab, bb = bf16(a), bf16(b)
+    arrays = [ab, bb, np.zeros_like(ab)]
+    _run_and_check(ctx, arrays, rec(W.OP_ADD, dtype=W.BF16, size=len(a), a=0, b=1, out=2))
+
+
 @pytest.mark.parametrize("op", [W.OP_SUM, W.OP_MAX, W.OP_MIN, W.OP_SOFTMAX, W.OP_LAYERNORM])
 @pytest.mark.parametrize("dt", [W.F32, W.BF16])
 def test_rows(ctx, op, dt):
