@@ -121,6 +121,48 @@ def dag_levels(recs):
     return int(depth.max())
 
 
+def torch_eager_calls(recs, pool, nmax):
+    """The pages' eager baseline: each descriptor as the PyTorch op a framework
+    would call, on views of the same device pool (one op call per descriptor;
+    out= variants where torch has them).  Only for streams whose ops all map
+    onto single torch ops (element-wise and row ops); None otherwise."""
+    import functools
+    import torch
+    import torch.nn.functional as F
+    import workloads as W
+    TD = {W.F32: torch.float32, W.BF16: torch.bfloat16}
+
+    def view(r, role, count):
+        b, off = int(r["buf"][role]), int(r["off"][role])
+        es = W.DTYPE_BYTES[int(r["dtype"])]
+        return pool.tensors[b][off: off + count * es].view(TD[int(r["dtype"])])
+
+    calls = []
+    for r in recs[:nmax]:
+        op, n, h = int(r["op"]), int(r["size"]), int(r["dim"][0])
+        P = functools.partial
+        if op in (W.OP_ADD, W.OP_MUL):
+            fn = torch.add if op == W.OP_ADD else torch.mul
+            calls.append(P(fn, view(r, W.A, n), view(r, W.B, n), out=view(r, W.OUT, n)))
+        elif op == W.OP_RELU:
+            calls.append(P(torch.clamp, view(r, W.A, n), min=0, out=view(r, W.OUT, n)))
+        elif op == W.OP_GELU:
+            calls.append(P(torch.ops.aten.gelu.out, view(r, W.A, n), approximate="tanh", out=view(r, W.OUT, n)))
+        elif op in (W.OP_SUM, W.OP_MAX, W.OP_MIN):
+            fn = {W.OP_SUM: torch.sum, W.OP_MAX: torch.amax, W.OP_MIN: torch.amin}[op]
+            calls.append(P(fn, view(r, W.A, n * h).view(n, h), 1, out=view(r, W.OUT, n)))
+        elif op == W.OP_SOFTMAX:
+            calls.append(P(torch.ops.aten._softmax.out, view(r, W.A, n * h).view(n, h), 1, False,
+                           out=view(r, W.OUT, n * h).view(n, h)))
+        elif op == W.OP_LAYERNORM:
+            x, o = view(r, W.A, n * h).view(n, h), view(r, W.OUT, n * h).view(n, h)
+            g, b, eps = view(r, W.AUX0, h), view(r, W.AUX1, h), float(r["fparam"][0])
+            calls.append(lambda x=x, o=o, g=g, b=b, eps=eps, h=h: o.copy_(F.layer_norm(x, (h,), g, b, eps)))
+        else:
+            return None
+    return calls
+
+
 def make_stream(name):
     import workloads as W
     fill = "host"
@@ -444,6 +486,19 @@ def main():
             G.gpuos_graph_destroy(ge)
         gdesc = int(offs[ng])
         null_async, null_sync = G.gpuos_null_launch_bench(sp, 20000)
+        # ---- PyTorch eager, the pages' baseline: one torch op per descriptor
+        calls = torch_eager_calls(recs, pool, 20_000)
+        torch_rate = None
+        if calls:
+            for c in calls[:200]:
+                c()
+            torch.cuda.current_stream().synchronize()
+            ta = time.perf_counter()
+            for c in calls:
+                c()
+            torch.cuda.current_stream().synchronize()
+            torch_rate = len(calls) / (time.perf_counter() - ta)
+            extra.update({"torch_eager_ops_per_s": torch_rate, "speedup_vs_torch_eager": ops_per_s / torch_rate})
         extra.update({
             "eager_ops_per_s": nb_e / eager_s,
             "eager_p50_us": float(np.percentile(eager_lat, 50)),
