@@ -75,6 +75,18 @@ def test_elementwise_exact_ops_bit_exact(upw):
         assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
 
 
+def test_elementwise_exact_ops_small_unit_queue():
+    # A unit queue of 4096 entries: 512 descriptors in flight hold more units
+    # than that, so the fetcher keeps waiting for queue capacity (and reads
+    # done[] again to see it free up).
+    s = W.make_elementwise(n_desc=3000, ops=(W.OP_ADD, W.OP_MUL, W.OP_RELU))
+    say("elementwise exact 3000, unit queue of 4096 entries")
+    gpu, orc = _final_pools(s, len(s), unit_queue_log2=12, ring_entries=512)
+    for i, b in enumerate(s.buffers):
+        eq = bits_equal(gpu[i].copy(), orc[i].copy(), b.dtype)
+        assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
+
+
 # --------------------------------------------------------------------------
 # Verify mode (every output logged on the GPU, teacher-forced oracle replay)
 # --------------------------------------------------------------------------
@@ -120,3 +132,13 @@ def test_decode_grouped_kv_heads_stream_verify():
     say("decode verify, 8 query heads sharing 2 key/value heads")
     res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, units_per_wave=2)
     _report("decode gqa", res)
+
+
+def test_mixed_stream_verify_small_scratch():
+    # 1 MiB of scratch: the split partials of the vector-matrix products and
+    # attention ops in flight need more, so the fetcher waits for scratch
+    # held by incomplete descriptors to be released.
+    s = W.make_mixed(tokens=2, layers=2, capacity=256, l0_range=(32, 200))
+    say("mixed verify, 1 MiB of scratch")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, scratch_bytes=1 << 20)
+    _report("mixed small scratch", res)
