@@ -361,6 +361,17 @@ int gpuos_graph_destroy(void* graph_exec);
 int gpuos_null_launch_bench(void* hip_stream, uint32_t n, double* ns_per_launch_async,
                             double* ns_launch_sync);
 
+/* Closed-loop per-op latency as a C caller sees it: for each of the count
+ * descriptors in turn, gpuos_submit it alone (BLOCK) and gpuos_sync until it
+ * has completed; out_us[i] (host memory, count doubles, owned by the caller)
+ * receives the time from before the submit to the return of the sync, in
+ * microseconds.  Stops at the first error and returns it (E_INVAL for a null
+ * ctx, descs or out_us; E_TIMEOUT if one descriptor takes longer than 10 s;
+ * any error of gpuos_submit or gpuos_sync).  What it measures is the
+ * per-op latency of the GPUOS digest page, section 3 Q3 (results), latency
+ * breakdown on H100. */
+int gpuos_latency_bench(void* ctx, const gpuos_desc* descs, uint32_t count, double* out_us);
+
 /* Achievable HBM bandwidth with the memory instructions the op bodies use
  * (device-scope 16-byte loads, write-through stores), one workgroup of four
  * waves per CU: mode 0 reads `bytes` at src (dst: device memory of at least

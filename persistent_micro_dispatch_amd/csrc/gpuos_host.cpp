@@ -1045,6 +1045,20 @@ int gpuos_null_launch_bench(void* hip_stream, uint32_t n, double* ns_async, doub
     return GPUOS_OK;
 }
 
+int gpuos_latency_bench(void* ctx, const gpuos_desc* descs, uint32_t count, double* out_us) {
+    if (!ctx || (count && (!descs || !out_us))) return GPUOS_E_INVAL;
+    for (uint32_t i = 0; i < count; ++i) {
+        const uint64_t t0 = now_ns();
+        uint64_t seq = 0;
+        int rc = gpuos_submit(ctx, descs + i, 1, GPUOS_SUBMIT_BLOCK, &seq);
+        if (rc != GPUOS_OK) return rc;
+        rc = gpuos_sync(ctx, seq, 10'000'000'000ll, nullptr, nullptr);
+        if (rc != GPUOS_OK) return rc;
+        out_us[i] = (double)(now_ns() - t0) * 1e-3;
+    }
+    return GPUOS_OK;
+}
+
 int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps, void* hip_stream,
                     double* gbs) {
     if (!src || !dst || bytes == 0 || (bytes & 15u) || bytes > (1ull << 30) || mode > 1 || reps == 0)

@@ -106,7 +106,7 @@ EXPORTS = [
     "gpuos_abi_version", "gpuos_init", "gpuos_register_op", "gpuos_submit", "gpuos_submit_bursts", "gpuos_sync",
     "gpuos_query", "gpuos_pause", "gpuos_resume", "gpuos_shutdown", "gpuos_stats_get",
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
-    "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_trace_read",
+    "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_latency_bench", "gpuos_trace_read",
     "gpuos_hbm_probe", "gpuos_register_expr",
 ]
 
@@ -152,6 +152,7 @@ def lib():
         "gpuos_graph_launch": ([vp, vp], ctypes.c_int),
         "gpuos_graph_destroy": ([vp], ctypes.c_int),
         "gpuos_trace_read": ([vp, vp, u64, ctypes.POINTER(u64)], ctypes.c_int),
+        "gpuos_latency_bench": ([vp, vp, u32, vp], ctypes.c_int),
         "gpuos_null_launch_bench": ([vp, u32, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "gpuos_hbm_probe": ([vp, vp, u64, u32, u32, vp, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
@@ -305,6 +306,13 @@ def gpuos_null_launch_bench(hip_stream: int, n: int) -> Tuple[float, float]:
     _check("gpuos_null_launch_bench",
            lib().gpuos_null_launch_bench(hip_stream or None, n, ctypes.byref(a), ctypes.byref(s)))
     return a.value, s.value
+
+
+def gpuos_latency_bench(ctx: int, descs: np.ndarray) -> np.ndarray:
+    """Closed-loop latency (us) of each descriptor, submitted alone and waited for."""
+    out = np.zeros(len(descs), np.float64)
+    _check("gpuos_latency_bench", lib().gpuos_latency_bench(ctx, _descs_ptr(descs), len(descs), out.ctypes.data))
+    return out
 
 
 def gpuos_hbm_probe(src: int, dst: int, nbytes: int, mode: int, reps: int, hip_stream: int) -> float:

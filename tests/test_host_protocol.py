@@ -418,3 +418,18 @@ def test_loopback_orders_expr_ops_like_binary_ops():
     r2["op"][sel] = W.OP_ADD  # same operand roles for the order check
     r2["buf"][m, W.B] = r2["buf"][m, W.A]
     assert _check_order(r2, order, first) == 0
+
+
+def test_latency_bench_submits_and_waits_one_at_a_time():
+    s = W.make_elementwise(n_desc=50)
+    descs = to_descs(s.recs, _fake_ptrs(len(s.buffers)))
+    ctx = _loopback()
+    try:
+        lat = G.gpuos_latency_bench(ctx, descs)
+        order = G.gpuos_loopback_order(ctx)
+        st = G.gpuos_stats_get(ctx)
+    finally:
+        G.gpuos_shutdown(ctx)
+    assert lat.shape == (50,) and (lat > 0).all()
+    assert len(order) == 50 and np.array_equal(np.sort(order), order)  # one at a time: in order
+    assert st["full_rejections"] == 0
