@@ -225,7 +225,7 @@ def main():
                     help="ring entries: descriptors in flight, which is also the window of hazard tracking")
     ap.add_argument("--units-per-wave", type=int, default=0, choices=(0, 1, 2),
                     help="units a worker wave holds at once (2 lets a ready unit overtake a waiting one); "
-                         "0: 2 for decode and rows, else 1")
+                         "0: 2 for decode, decode_gqa and rows, else 1")
     ap.add_argument("--num-wgs", type=int, default=0,
                     help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
     ap.add_argument("--backoff", type=int, default=0,
@@ -237,7 +237,7 @@ def main():
     if args.waves == 0:
         args.waves = 4 if args.workload in ("rows", "decode", "decode_gqa", "copy", "copy64") else 1
     if args.units_per_wave == 0:
-        args.units_per_wave = 2 if args.workload in ("decode", "rows") else 1
+        args.units_per_wave = 2 if args.workload in ("decode", "decode_gqa", "rows") else 1
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): the dispatcher is a "
               "single-device path; the design notes describe how it would shard.", file=sys.stderr)

@@ -47,6 +47,10 @@ __device__ __forceinline__ void nap(uint32_t n) {
 
 constexpr uint64_t STOP_DRAIN = 1, STOP_ABORT = 2;
 constexpr uint32_t DEP_BACKOFF_MAX = 2;
+#ifndef GPUOS_SHORT_FIRST
+#define GPUOS_SHORT_FIRST 1
+#endif
+constexpr uint32_t PASS_MAX = 4;
 #ifndef GPUOS_NEAR_UNITS
 #define GPUOS_NEAR_UNITS 64
 #endif
@@ -59,14 +63,17 @@ constexpr uint64_t NO_SCRATCH = ~0ull;
 
 // ------------------------------------------------------------------ worker
 // A worker wave holds up to SLOTS claimed units and runs whichever of them
-// has its dependencies satisfied (the oldest such), so a unit waiting on a
-// long chain does not hold back a ready unit claimed after it.  Each claim
-// shard hands out its units in queue order, so the executor always
-// progresses: if the oldest unfinished unit is unclaimed, every unit its
-// shard has handed out is older, hence finished, and a wave of that shard
-// (every shard has one, and all waves are resident) claims it once a slot
-// is free; if it is claimed, its holder finds it ready.  No wave waits on
-// one unit alone.
+// has its dependencies satisfied, so a unit waiting on a long chain does not
+// hold back a ready unit claimed after it.  Among ready units, one of a
+// short body (anything but attention, vector-matrix products and copies)
+// goes first, then the oldest; a ready long unit is passed over at most
+// PASS_MAX times in a row.  Each claim shard hands out its units in queue
+// order, so the executor always progresses: if the oldest unfinished unit
+// is unclaimed, every unit its shard has handed out is older, hence
+// finished, and a wave of that shard (every shard has one, and all waves
+// are resident) claims it once a slot is free; if it is claimed, its holder
+// finds it ready and runs it after at most PASS_MAX other units.  No wave
+// waits on one unit alone.
 // SLOTS is 1 or 2 (gpuos_init_params.units_per_wave): with one, a wave
 // claims its next unit only after running the current one; two let a ready
 // unit overtake one that waits, at the price of holding two claims.
@@ -90,6 +97,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
     uint64_t sw[SLOTS];   // per lane: mirror words in lanes 0..15, meta words in 16..23
     uint32_t sdl[SLOTS];  // per lane: dependency delta (lanes 0..13), 0 = none
     uint32_t stile[SLOTS];
+    uint32_t spass[SLOTS];  // times a ready unit was passed over in a row
     bool sdeps[SLOTS], swaited[SLOTS];
 #pragma unroll
     for (uint32_t k = 0; k < SLOTS; ++k) {
@@ -98,6 +106,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         sw[k] = 0;
         sdl[k] = 0;
         stile[k] = 0;
+        spass[k] = 0;
         sdeps[k] = swaited[k] = false;
     }
     bool stop_seen = false;
@@ -123,8 +132,10 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         const uint64_t now = wall_clock64();
         uint32_t r = SLOTS, rstatus = GPUOS_ST_OK;
         uint64_t rseq = ~0ull;
+        bool rdy[SLOTS];
 #pragma unroll
         for (uint32_t k = 0; k < SLOTS; ++k) {
+            rdy[k] = false;
             if (state[k] != SL_WAIT) continue;
             bool ready = true;
             if (sdeps[k]) {
@@ -144,11 +155,27 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
                 if (!swaited[k]) { swaited[k] = true; st0[k] = now; ++n_depw; }
                 if (now - st0[k] > A.spin_limit_ticks) { ready = true; stat = GPUOS_ST_SPIN; }
             }
-            if (ready && sseq[k] < rseq) { r = k; rseq = sseq[k]; rstatus = stat; }
+            // among ready units, those of short bodies go first, then the
+            // oldest: a RoPE or KV append held beside an attention unit
+            // would otherwise wait out that unit's whole body, and the
+            // attention units of its layer, held by other waves, with it
+            uint64_t key = sseq[k];
+#if GPUOS_SHORT_FIRST
+            if constexpr (SLOTS > 1) {
+                const uint32_t kind = (uint32_t)rl64(sw[k], 16);
+                const bool lng = kind == GPUOS_OP_SDPA || kind == GPUOS_OP_GEMV || kind == GPUOS_OP_COPY;
+                if (lng && spass[k] < PASS_MAX) key |= 1ull << 63;
+            }
+#endif
+            if (ready && key < rseq) { r = k; rseq = key; rstatus = stat; }
+            rdy[k] = ready;
         }
+#pragma unroll
+        for (uint32_t k = 0; k < SLOTS; ++k)  // ready units passed over this time
+            spass[k] = k == r ? 0u : spass[k] + ((r < SLOTS && rdy[k]) ? 1u : 0u);
         if (r < SLOTS) {
             const uint64_t w = pick<SLOTS>(sw, r);
-            const uint64_t seq = rseq, u = pick<SLOTS>(su, r), t_claim = pick<SLOTS>(tclaim, r);
+            const uint64_t seq = pick<SLOTS>(sseq, r), u = pick<SLOTS>(su, r), t_claim = pick<SLOTS>(tclaim, r);
             const uint32_t tile = pick<SLOTS>(stile, r);
             const uint64_t slot = seq & A.mask;
             Unit U;
