@@ -113,7 +113,7 @@ enum gpuos_kind {
  *                   query attention; Hkv = 1 is multi-query attention);
  *                   output [B, H, D] in the output dtype; keys [0, lens[b]);
  *                   param.f[4] = scale (0 -> 1/sqrt(D)).  D must be 64 or 128;
- *                   lens[b] at most 16384 (64 splits of 256 keys).
+ *                   lens[b] up to 65535 (at most 64 splits of 1024 keys).
  *   GEMV            a = x [dim[0]=K], b = W [K, dim[1]=N] row-major, output [N].
  *   COPY            a -> output, `size` bytes.
  * Within one descriptor an output must coincide exactly with an input or

@@ -141,7 +141,10 @@ __host__ __device__ constexpr uint32_t expr_tile_bytes(uint32_t kflags, bool big
 }
 constexpr uint32_t COPY_TILE_BYTES = 32768;
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
-constexpr uint32_t SDPA_KT = 256;          // keys per SDPA unit (fewer for small attention ops)
+#ifndef GPUOS_SDPA_KT
+#define GPUOS_SDPA_KT 1024
+#endif
+constexpr uint32_t SDPA_KT = GPUOS_SDPA_KT;  // keys per SDPA unit (fewer for small attention ops)
 constexpr uint32_t GEMV_KC = 128;          // rows of W per GEMV unit
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
