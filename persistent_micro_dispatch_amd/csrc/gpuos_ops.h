@@ -144,6 +144,10 @@ __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)
 // A window of `nbytes` at `base` (raw buffer, stride 0).  Word 3 selects the
 // 32-bit data format that raw buffer instructions require on gfx9-family
 // parts.  Offsets are 32-bit: callers keep windows below 2 GiB.
+#ifndef GPUOS_GEMV_DOT2
+#define GPUOS_GEMV_DOT2 1
+#endif
+constexpr bool GEMV_DOT2 = GPUOS_GEMV_DOT2;
 constexpr int CPOL_SC1 = 16;
 // Data read once per descriptor and never again soon (attention's keys and
 // values, a vector-matrix product's weights) is loaded with the
@@ -1158,13 +1162,34 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
             }
         };
         auto consume = [&](const u32x4* w, float xv) {
+            if constexpr (DT == GPUOS_BF16 && GEMV_DOT2) {
+                // rows r and r + 4 (loads i and i + 1) paired for the bf16
+                // dot instruction: per column, a permute packs the two
+                // weights and one dot adds both products to the column's sum
 #pragma unroll
-            for (uint32_t i = 0; i < 16; ++i) {
-                const float xr = __shfl(xv, (int)(i * 4u + g), 64);
-                float wf[VE];
-                unpack<DT>(w[i], wf);
+                for (uint32_t i = 0; i < 16; i += 2) {
+                    const float x1 = __shfl(xv, (int)(i * 4u + g), 64);
+                    const float x2 = __shfl(xv, (int)((i + 1u) * 4u + g), 64);
+                    const bf16x2 xb = as_bf2(f2bf2(x1, x2));  // exact: both are bf16 values
+                    const uint32_t a[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+                    const uint32_t b[4] = {w[i + 1].x, w[i + 1].y, w[i + 1].z, w[i + 1].w};
 #pragma unroll
-                for (uint32_t e = 0; e < VE; ++e) acc[e] += xr * wf[e];
+                    for (uint32_t k = 0; k < 4; ++k) {
+                        const uint32_t lo = __builtin_amdgcn_perm(b[k], a[k], 0x05040100u);
+                        const uint32_t hi = __builtin_amdgcn_perm(b[k], a[k], 0x07060302u);
+                        acc[2 * k] = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(lo), xb, acc[2 * k], false);
+                        acc[2 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf2(hi), xb, acc[2 * k + 1], false);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (uint32_t i = 0; i < 16; ++i) {
+                    const float xr = __shfl(xv, (int)(i * 4u + g), 64);
+                    float wf[VE];
+                    unpack<DT>(w[i], wf);
+#pragma unroll
+                    for (uint32_t e = 0; e < VE; ++e) acc[e] += xr * wf[e];
+                }
             }
         };
         u32x4 wa[16], wb[16];
