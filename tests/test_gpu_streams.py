@@ -142,3 +142,13 @@ def test_mixed_stream_verify_small_scratch():
     say("mixed verify, 1 MiB of scratch")
     res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, scratch_bytes=1 << 20)
     _report("mixed small scratch", res)
+
+
+def test_decode_stream_verify_few_waves_two_units():
+    # seven worker waves holding two units each: ready RoPE and KV-append
+    # units keep running before ready attention units, and every attention
+    # unit still runs (a ready long unit is passed over at most four times)
+    s = W.make_decode(steps=4, layers=2, heads=8, capacity=512, l_min=100, n_triples=4, n_out=16)
+    say("decode verify, 4 workgroups x 2 waves, two units per wave")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, num_wgs=4, waves_per_wg=2, units_per_wave=2)
+    _report("decode few waves", res)
