@@ -170,7 +170,10 @@ typedef struct gpuos_init_params {
 } gpuos_init_params;
 
 /* Allocate the ring (fine-grained coherent host memory), the device tables
- * and counters, bind the built-in op ids and launch the executor once.
+ * and counters, bind the built-in op ids and launch the executor once: it
+ * stays resident, one workgroup per compute unit by default, until the host
+ * stops it (digest page, section 3 Q2 "Persistent Kernel Executor": launched
+ * once, never exits on its own, a small share of each SM/CU).
  * params may be NULL for defaults.  *out receives the context.
  * Errors: E_INVAL (bad params), E_HIP (allocation or launch failed). */
 int gpuos_init(const gpuos_init_params* params, void** out);
@@ -232,7 +235,10 @@ int gpuos_register_expr(void* ctx, uint32_t op_id, const uint32_t* program, uint
 #define GPUOS_SUBMIT_SERIAL (1u << 2)    /* each descriptor waits for its predecessor */
 
 /* Copy `count` descriptors into consecutive ring slots and commit them in
- * order (store-release of each slot's stamp).  Before writing, every
+ * order (store-release of each slot's stamp): the host side of the ring
+ * protocol, prepare descriptor -> acquire slot -> write -> commit with a
+ * store-release (digest page, section 3 Q2 "Ring Buffer Communication
+ * Channel").  Before writing, every
  * descriptor is checked and annotated with dependencies on earlier
  * descriptors whose byte ranges it reads or writes (read-after-write,
  * write-after-read, write-after-write), so results equal sequential
@@ -262,7 +268,10 @@ int gpuos_submit_bursts(void* ctx, const gpuos_desc* descs, const uint32_t* burs
 #define GPUOS_SEQ_ALL 0xFFFFFFFFFFFFFFFFull
 
 /* Wait until every descriptor with seq <= upto_seq (GPUOS_SEQ_ALL: every
- * submitted one) has completed.  timeout_ns < 0 waits forever.  Returns
+ * submitted one) has completed, that is until the executor has released its
+ * ring slot, the last device step after dispatch (digest page, section 3 Q2
+ * "Ring Buffer Communication Channel", device side: poll -> claim ->
+ * dispatch -> release slot).  timeout_ns < 0 waits forever.  Returns
  * E_DEVICE if any of them completed with a non-zero status (the first one's
  * seq and status go to *err_seq and *err_status, either may be NULL),
  * E_TIMEOUT if the deadline passed. */
@@ -275,12 +284,15 @@ int gpuos_query(void* ctx, uint64_t seq);
 /* ----------------------------------------------------- pause / shutdown */
 /* Wait for all submitted work, then stop the executor kernel (it exits and
  * frees the compute units) while keeping the ring, tables and sequence
- * numbers.  The next gpuos_submit or gpuos_resume relaunches it. */
+ * numbers.  The resident executor of the pages never exits (digest page,
+ * section 3 Q2 "Persistent Kernel Executor"); pausing it is this library's
+ * way to give every CU back between bursts of work.  The next gpuos_submit or gpuos_resume relaunches it. */
 int gpuos_pause(void* ctx, int64_t timeout_ns);
 int gpuos_resume(void* ctx);
 
 /* Stop the executor (work already submitted is finished first) and free
- * every resource.  The context pointer is invalid afterwards.  If the
+ * every resource: the end of the executor's life that starts with
+ * gpuos_init (digest page, section 3 Q2 "Persistent Kernel Executor").  The context pointer is invalid afterwards.  If the
  * executor does not exit within the timeout the device is told to abort
  * and E_TIMEOUT is returned after the context is freed as far as safe. */
 int gpuos_shutdown(void* ctx);
@@ -315,6 +327,16 @@ int gpuos_stats_get(void* ctx, gpuos_stats* out);
 /* Test only (GPUOS_INIT_LOOPBACK contexts): copy up to max sequence
  * numbers in the order the loopback consumer completed them. */
 int gpuos_loopback_order(void* ctx, uint64_t* out, uint64_t max, uint64_t* n_out);
+
+/* Test only: copy the descriptor committed with sequence number seq, as the
+ * executor reads it (seq, dependencies and table version filled in), into
+ * *out (host memory), and its side dependency deltas -- 56 uint16 values,
+ * each "wait for seq - delta", 0 = none; all 0 unless dep_delta[5] is set --
+ * into extra (host memory, may be NULL).  The descriptor must still be in
+ * its ring slot: seq in [next_seq - ring_entries, next_seq).  The ring is
+ * ordinary host memory, so this is safe while the executor runs.
+ * Errors: E_INVAL (null ctx or out), E_STATE (seq not in the ring). */
+int gpuos_ring_peek(void* ctx, uint64_t seq, gpuos_desc* out, uint16_t* extra);
 
 /* ---------------------------------------------------------------- trace */
 /* One record per executed work unit (GPUOS_INIT_TRACE contexts).  Times are

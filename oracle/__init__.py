@@ -55,6 +55,10 @@ def lib():
         L.orc_expr_eval.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_float,
                                     ctypes.POINTER(ctypes.c_int32)]
         L.orc_record_size.restype = ctypes.c_int32
+        L.orc_run_capture.restype = ctypes.c_int64
+        L.orc_run_capture.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         _lib = L
     return _lib
 
@@ -92,6 +96,28 @@ class Pool:
                            self._sizes.ctypes.data, len(self.arrays), ctypes.byref(err))
         if rc != 0:
             raise OracleError(f"record {-rc - 1} failed with oracle error {err.value}")
+
+    def run_capture(self, rec: np.ndarray, windows) -> List[np.ndarray]:
+        """Execute one record in place and return, for each output window
+        (buffer, byte offset, bytes, element bytes) -- at most two -- the
+        unrounded double of every element the record stored there (NaN where
+        it stored nothing)."""
+        rec = np.ascontiguousarray(np.asarray(rec).reshape(1))
+        assert rec.dtype.itemsize == lib().orc_record_size() and len(windows) <= 2
+        outs = [np.full(int(nb) // int(es), np.nan) for (_, _, nb, es) in windows]
+        nw = len(windows)
+        wb = np.array([w[0] for w in windows] + [0] * (2 - nw), np.int32)
+        wo = np.array([w[1] for w in windows] + [0] * (2 - nw), np.int64)
+        wn = np.array([w[2] for w in windows] + [0] * (2 - nw), np.int64)
+        optr = (ctypes.c_void_p * 2)(*([o.ctypes.data for o in outs] + [None] * (2 - nw)))
+        err = ctypes.c_int32(0)
+        rc = lib().orc_run_capture(rec.ctypes.data, ctypes.cast(self._ptrs, ctypes.c_void_p),
+                                   self._sizes.ctypes.data, len(self.arrays), ctypes.byref(err), nw,
+                                   wb.ctypes.data, wo.ctypes.data, wn.ctypes.data,
+                                   ctypes.cast(optr, ctypes.c_void_p))
+        if rc != 0:
+            raise OracleError(f"record failed with oracle error {err.value}")
+        return outs
 
     def view(self, buf: int, dtype, off: int = 0, count: int = -1) -> np.ndarray:
         a = self.arrays[buf][off:]

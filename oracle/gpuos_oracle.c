@@ -118,7 +118,22 @@ static double ld(const uint8_t* p, int dt, int64_t i) {
     uint16_t h; memcpy(&h, p + 2 * i, 2); return orc_bf16_to_double(h);
 }
 
+/* Observation windows (set only by orc_run_capture): every value an op
+ * stores into a window is also written there as the double it computed,
+ * before rounding to the output type.  Comparisons of a rounded GPU result
+ * against the exact value then carry no second rounding.  This observes the
+ * arithmetic and changes none of it. */
+typedef struct { const uint8_t* base; int64_t nbytes; double* out; } cap_t;
+static cap_t cap_win[2];
+static int cap_n = 0;
+
 static void st(uint8_t* p, int dt, int64_t i, double v) {
+    const int64_t es = dt == ORC_F32 ? 4 : 2;
+    for (int w = 0; w < cap_n; ++w) {
+        const uint8_t* q = p + es * i;
+        if (q >= cap_win[w].base && q < cap_win[w].base + cap_win[w].nbytes)
+            cap_win[w].out[(q - cap_win[w].base) / es] = v;
+    }
     if (dt == ORC_F32) { float f = (float)v; memcpy(p + 4 * i, &f, 4); }
     else { uint16_t h = orc_round_bf16(v); memcpy(p + 2 * i, &h, 2); }
 }
@@ -508,6 +523,31 @@ int64_t orc_run(const orc_rec* recs, int64_t n, uint8_t** bufs, const int64_t* n
     }
     if (err) *err = 0;
     return 0;
+}
+
+/* Run one record like orc_run and also report, for up to two output
+ * windows (buffer index win_buf[w], byte offset win_off[w], win_bytes[w]
+ * bytes), the unrounded double of every element the record stores there
+ * into out[w][element], elements counted in the stored type.  Elements the record does not
+ * store keep what the caller put in out[w].  Returns like orc_run. */
+int64_t orc_run_capture(const orc_rec* rec, uint8_t** bufs, const int64_t* nbytes, int32_t nbuf,
+                        int32_t* err, int32_t n_win, const int32_t* win_buf, const int64_t* win_off,
+                        const int64_t* win_bytes, double** out) {
+    if (n_win < 0 || n_win > 2) { if (err) *err = ORC_E_BOUNDS; return -1; }
+    for (int w = 0; w < n_win; ++w) {
+        if (win_buf[w] < 0 || win_buf[w] >= nbuf || win_off[w] < 0 || win_bytes[w] < 0 ||
+            win_off[w] + win_bytes[w] > nbytes[win_buf[w]]) {
+            if (err) *err = ORC_E_BOUNDS;
+            return -1;
+        }
+        cap_win[w].base = bufs[win_buf[w]] + win_off[w];
+        cap_win[w].nbytes = win_bytes[w];
+        cap_win[w].out = out[w];
+    }
+    cap_n = n_win;
+    const int64_t rc = orc_run(rec, 1, bufs, nbytes, nbuf, err);
+    cap_n = 0;
+    return rc;
 }
 
 int32_t orc_record_size(void) { return (int32_t)sizeof(orc_rec); }

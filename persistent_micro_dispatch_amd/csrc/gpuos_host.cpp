@@ -767,7 +767,10 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
                 ++c->deps_range;
             }
         }
-        if (c->deps.size() > 6)  // the side words are read only when dep_delta[5] is set
+        // the side words are read whenever dep_delta[5] is set, that is with
+        // six dependencies or more: clear every one past the last in use, so
+        // that none is left from an earlier descriptor at this stage index
+        if (c->deps.size() >= 6)
             for (size_t k = c->deps.size() - 6; k < 4 * DEPX_WORDS; ++k) ex[k] = 0;
     }
     const uint64_t t_hz1 = now_ns();
@@ -946,6 +949,20 @@ int gpuos_loopback_order(void* ctx, uint64_t* out, uint64_t max, uint64_t* n_out
     const uint64_t n = std::min<uint64_t>(max, c->lb_order.size());
     if (out) memcpy(out, c->lb_order.data(), n * 8);
     if (n_out) *n_out = c->lb_order.size();
+    return GPUOS_OK;
+}
+
+int gpuos_ring_peek(void* ctx, uint64_t seq, gpuos_desc* out, uint16_t* extra) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (!c || !out) return GPUOS_E_INVAL;
+    std::lock_guard<std::mutex> g(c->mu);
+    if (seq >= c->next_seq || seq + c->N < c->next_seq) return GPUOS_E_STATE;
+    const uint64_t slot = seq & c->mask;
+    memcpy(out, &c->ring[slot], sizeof(gpuos_desc));
+    if (extra) {
+        if (out->dep_delta[5]) memcpy(extra, &c->depx[slot * DEPX_WORDS], 8 * DEPX_WORDS);
+        else memset(extra, 0, 8 * DEPX_WORDS);
+    }
     return GPUOS_OK;
 }
 

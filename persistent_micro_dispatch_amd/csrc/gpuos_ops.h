@@ -875,8 +875,8 @@ __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
 }
 
 // ------------------------------------------------------------ decode SDPA
-// Unit = (b, h, split of kt = sdpa_keys_per_unit keys: 256, or down to 64 for
-// small ops).  One key row of D bf16 is DV = D/8
+// Unit = (b, h, split of kt = sdpa_keys_per_unit keys: 1024, halved down to 64
+// while the op would give fewer than 256 units).  One key row of D bf16 is DV = D/8
 // lanes x 16 bytes, so one load instruction covers RPI = 64/DV keys and the
 // wave reads keys in chunks of 8 instructions (8 RPI keys, 16 KiB of K and V
 // for D = 128).  The next chunk's loads are issued before the current chunk

@@ -107,7 +107,7 @@ EXPORTS = [
     "gpuos_query", "gpuos_pause", "gpuos_resume", "gpuos_shutdown", "gpuos_stats_get",
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
     "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_latency_bench", "gpuos_trace_read",
-    "gpuos_hbm_probe", "gpuos_register_expr",
+    "gpuos_hbm_probe", "gpuos_register_expr", "gpuos_ring_peek",
 ]
 
 TRACE_DTYPE = np.dtype([("seq", "<u8"), ("tile", "<u4"), ("hw", "<u4"), ("t_claim", "<u8"), ("t_ready", "<u8"),
@@ -157,6 +157,7 @@ def lib():
                                      ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "gpuos_hbm_probe": ([vp, vp, u64, u32, u32, vp, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "gpuos_register_expr": ([vp, u32, vp, u32], ctypes.c_int),
+        "gpuos_ring_peek": ([vp, u64, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -320,6 +321,14 @@ def gpuos_hbm_probe(src: int, dst: int, nbytes: int, mode: int, reps: int, hip_s
     g = ctypes.c_double(0)
     _check("gpuos_hbm_probe", lib().gpuos_hbm_probe(src, dst, nbytes, mode, reps, hip_stream or None, ctypes.byref(g)))
     return g.value
+
+
+def gpuos_ring_peek(ctx: int, seq: int) -> Tuple[int, np.ndarray, np.ndarray]:
+    """(rc, descriptor as committed, 56 side dependency deltas)."""
+    d = new_descs(1)
+    ex = np.zeros(56, np.uint16)
+    rc = lib().gpuos_ring_peek(ctx, seq, d.ctypes.data, ex.ctypes.data)
+    return rc, d[0], ex
 
 
 def gpuos_trace_read(ctx: int, max_records: int = 1 << 20) -> np.ndarray:

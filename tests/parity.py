@@ -12,8 +12,11 @@ toleranced op uses the denominator its arithmetic fixes:
   SDPA       |g_d-r_d| <= tol * sum_j p_j |V_jd|
   GEMV       |g_n-r_n| <= tol * sum_k |x_k W_kn|
   RoPE       within one bf16 ulp of the exact double result
-For bf16 outputs the bf16 rounding of the oracle's own output is added to
-the allowance (the oracle is compared after rounding to the output type).
+Toleranced outputs are compared with the oracle's unrounded double (the
+value it would round to the output type), so a bf16 output carries its own
+rounding only, with no second rounding of the reference and no extra
+allowance.  RoPE is compared with the rounded oracle value (its bar is one
+bf16 ulp of it).
 """
 from __future__ import annotations
 

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_harness import check_record, run_gpu, say
+from gpu_harness import check_record, run_gpu, run_record_oracle, say
 from parity import bits_equal
 from persistent_micro_dispatch_amd import gpuos as G
 from workloads.gpu import DevicePool, to_descs
@@ -34,6 +34,20 @@ def test_elementwise_full_stream_exact_ops_bit_exact():
     for i, b in enumerate(s.buffers):
         eq = bits_equal(gpu[i].copy(), p.arrays[i].copy(), b.dtype)
         assert eq.all(), f"buffer {i}: {int((~eq).sum())} mismatches"
+
+
+def test_elementwise_full_stream_with_gelu_verify():
+    """All 100,000 descriptors of the element-wise stream, GELU included, in
+    verify mode (every output logged on the GPU, 3.5 GB of log): add, mul and
+    ReLU bit-exact from identical inputs, GELU within its tolerance of the
+    oracle's unrounded value."""
+    from gpu_harness import verify_stream
+    s = W.make_elementwise()
+    say(f"elementwise full stream with GELU, verify mode, {len(s)} descriptors, ring 512, one wave per workgroup")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ring_entries=512,
+                        waves_per_wg=1, units_per_wave=1)
+    say(f"  logged {res['n_logged']}; worst error / allowance {res['worst']}; plain relative {res['plain']}")
+    assert not res["fails"], res["fails"][:3]
 
 
 def test_rows_full_stream_sampled_outputs():
@@ -85,9 +99,9 @@ def test_rows_full_stream_sampled_outputs():
         arrays.append(np.zeros(out_n * es, np.uint8))
         r["buf"][0, W.OUT], r["off"][0, W.OUT] = len(arrays) - 1, 0
         p = oracle.Pool([a.copy() for a in arrays])
-        p.run(r)
+        hp = run_record_oracle(p, r[0], op in (W.OP_MAX, W.OP_MIN))
         gpu_arrays = [a.copy() for a in arrays[:-1]] + [g_out]
-        res = check_record(r[0], arrays, gpu_arrays, p.arrays)
+        res = check_record(r[0], arrays, gpu_arrays, p.arrays, hp)
         if not res["ok"]:
             bad.append((i, res))
     assert not bad, bad[:3]
@@ -142,7 +156,7 @@ def test_decode_full_stream_last_step_sampled():
         r["buf"][0, W.A], r["buf"][0, W.AUX0], r["buf"][0, W.AUX1], r["buf"][0, W.OUT] = 0, 1, 2, 3
         r["off"][0] = 0
         p = oracle.Pool([a.copy() for a in arrays])
-        p.run(r)
-        res = check_record(r[0], arrays, arrays[:3] + [g_out], p.arrays)
+        hp = run_record_oracle(p, r[0], False)
+        res = check_record(r[0], arrays, arrays[:3] + [g_out], p.arrays, hp)
         say(f"    worst {res['worst']:.3g}")
         assert res["ok"], res

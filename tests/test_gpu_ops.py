@@ -35,9 +35,9 @@ def _vals(n, dt):
 
 def _run_and_check(ctx, arrays, recs):
     gpu = run_gpu(arrays, recs, ctx=ctx)
-    orc = run_oracle(arrays, recs)
+    orc, hps = run_oracle(arrays, recs, capture=True)
     inputs = [np.ascontiguousarray(a).view(np.uint8).reshape(-1) for a in arrays]
-    results = [check_record(r, inputs, gpu, orc) for r in recs]
+    results = [check_record(r, inputs, gpu, orc, hp) for r, hp in zip(recs, hps)]
     bad = [x for x in results if not x["ok"]]
     assert not bad, bad[:5]
     assert untouched_equal(recs, gpu, orc)
@@ -222,7 +222,7 @@ def test_copy_and_nop(ctx):
 
 
 def test_large_descriptors(ctx):
-    """Descriptors of hundreds of units (completion counted in sub-counters)."""
+    """Descriptors of hundreds of units (completion counted by one per-slot counter)."""
     say("large descriptors: copy 8 MiB + 37 B, add/mul 1M + 3 elements")
     recs, arrays = [], []
     n = (8 << 20) + 37

@@ -94,14 +94,19 @@ from gpu_harness import verify_stream  # noqa: E402
 
 
 def _report(name, res):
-    say(f"{name}: logged {res['n_logged']} outputs; worst ratio per op {res['worst']}")
+    say(f"{name}: logged {res['n_logged']} outputs; worst error / allowance per op {res['worst']}; "
+        f"plain relative error per op {res['plain']}")
     assert not res["fails"], res["fails"][:3]
     assert res["kv_ok"]
 
 
 def test_elementwise_stream_verify():
-    s = W.make_elementwise(n_desc=3000)
-    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs)
+    # the element-wise stream with GELU, 20,000 descriptors, in the bench's
+    # launch configuration (512-entry ring, one wave per workgroup)
+    s = W.make_elementwise(n_desc=20000)
+    say("elementwise verify, 20000 descriptors with GELU")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ring_entries=512,
+                        waves_per_wg=1, units_per_wave=1)
     _report("elementwise", res)
 
 
@@ -125,6 +130,22 @@ def test_mixed_stream_verify(upw):
     say(f"mixed verify, units_per_wave={upw}")
     res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, units_per_wave=upw)
     _report("mixed", res)
+
+
+def test_mixed_stream_verify_bench_shape():
+    """The mixed pipeline at the shape bench.py times: 32 layers, hidden 1024,
+    8 heads x 128, KV capacity 4096, L0 in [64, 2048]; two tokens (706
+    descriptors, every output logged), with the bench's launch configuration
+    (512-entry ring, one wave per workgroup, one unit per wave, 256 MiB of
+    scratch).  The 1.1 GiB pool (weights N(0, 0.02), caches N(0, 1)) is drawn
+    on the GPU and its initial contents downloaded for the oracle."""
+    from workloads.gpu import DevicePool
+    s = W.make_mixed(tokens=2)
+    say(f"mixed verify at the bench shape: {len(s.recs)} descriptors, 32 layers, C=4096")
+    pool = DevicePool.from_stream(s, fill="device")
+    res = verify_stream(None, s.recs, bursts=s.bursts, pool=pool, ring_entries=512, waves_per_wg=1,
+                        units_per_wave=1)
+    _report("mixed (bench shape)", res)
 
 
 def test_decode_grouped_kv_heads_stream_verify():

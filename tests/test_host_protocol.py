@@ -433,3 +433,47 @@ def test_latency_bench_submits_and_waits_one_at_a_time():
     assert lat.shape == (50,) and (lat > 0).all()
     assert len(order) == 50 and np.array_equal(np.sort(order), order)  # one at a time: in order
     assert st["full_rejections"] == 0
+
+
+def test_six_dependencies_leave_no_stale_side_words():
+    """A descriptor with more than six dependencies keeps the extra ones in
+    side words of its stage index; a later descriptor at the same stage index
+    with exactly six (dep_delta[5] set, so the side words are read) must
+    carry none of them: stale words would make it wait on unrelated older
+    descriptors."""
+    def relu(a, out):
+        r = np.zeros(1, W.REC_DTYPE)
+        r["buf"] = -1
+        r["dtype"] = r["out_dtype"] = W.F32
+        r["op"] = W.OP_RELU
+        r["size"] = 256
+        r["buf"][0, W.A], r["buf"][0, W.OUT] = a, out
+        return r
+
+    def nop():
+        r = np.zeros(1, W.REC_DTYPE)
+        r["buf"] = -1
+        return r
+    ptrs = _fake_ptrs(32)
+    # call 1: ten readers of buffer 0, then a writer of buffer 0 (ten deps) at index 10
+    c1 = np.concatenate([relu(0, 1 + i) for i in range(10)] + [relu(30, 0)])
+    # call 2: four NOPs, six readers of buffer 0, then a writer (six deps) at index 10
+    c2 = np.concatenate([nop() for _ in range(4)] + [relu(0, 11 + i) for i in range(6)] + [relu(31, 0)])
+    ctx = _loopback()
+    try:
+        rc, f1 = G.gpuos_submit(ctx, to_descs(c1, ptrs), G.GPUOS_SUBMIT_BLOCK)
+        assert rc == 0
+        rc, d1, x1 = G.gpuos_ring_peek(ctx, f1 + 10)
+        assert rc == 0
+        rc, f2 = G.gpuos_submit(ctx, to_descs(c2, ptrs), G.GPUOS_SUBMIT_BLOCK)
+        assert rc == 0
+        rc, d2, x2 = G.gpuos_ring_peek(ctx, f2 + 10)
+        assert rc == 0
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 20_000_000_000)[0] == 0
+        assert G.gpuos_ring_peek(ctx, f2 + 11)[0] == G.GPUOS_E_STATE  # not submitted
+    finally:
+        G.gpuos_shutdown(ctx)
+    deps1 = sorted(int(v) for v in list(d1["dep_delta"]) + list(x1) if v)
+    assert deps1 == list(range(1, 11))          # the ten readers, by delta
+    assert sorted(int(v) for v in d2["dep_delta"]) == list(range(1, 7))
+    assert not x2.any(), f"stale side words {x2[:8]}"

@@ -640,3 +640,95 @@ def test_rope_with_fewer_key_heads_rotates_each_tensor_by_its_own_heads():
     k_only = run(rec(W.OP_ROPE, dtype=W.F32, size=B, dim=(Hk, D), fparam=(10000.0,), lens=lens, a=0, b=1),
                  [np.zeros_like(k), k])[1]
     assert np.array_equal(both[0], q_only) and np.array_equal(both[1], k_only)
+
+
+# ---------------------------------------------------------------------------
+# Unrounded capture (orc_run_capture): the doubles it reports are the values
+# the record rounds to its output type -- they round to exactly the stored
+# bytes -- and they equal an independent double evaluation of each op.  A
+# window that reports the wrong element, another op's value or a rounded
+# value fails one of these.
+# ---------------------------------------------------------------------------
+def _capture(r, arrays, role=W.OUT, es=None, nbytes=None):
+    pool = oracle.Pool([np.array(a, copy=True) for a in arrays])
+    b, off = int(r["buf"][0, role]), int(r["off"][0, role])
+    es = es or W.DTYPE_BYTES[int(r["out_dtype"][0])]
+    nbytes = nbytes or pool.arrays[b].nbytes - off
+    (hp,) = pool.run_capture(r, [(b, off, nbytes, es)])
+    return hp, pool.arrays[b][off: off + nbytes]
+
+
+@pytest.mark.parametrize("dt", [W.F32, W.BF16])
+def test_capture_rounds_to_stored_output(dt):
+    n = 4099
+    x = RNG.standard_normal(n).astype(np.float32) * 3
+    y = RNG.standard_normal(n).astype(np.float32)
+    if dt == W.BF16:
+        xa, ya = bf16(x), bf16(y)
+    else:
+        xa, ya = x, y
+    gam = (1 + 0.1 * RNG.standard_normal(1024)).astype(np.float32)
+    bet = (0.1 * RNG.standard_normal(1024)).astype(np.float32)
+    if dt == W.BF16:
+        gam, bet = bf16(gam), bf16(bet)
+    cases = [
+        rec(W.OP_GELU, dtype=dt, size=n, a=0, out=2),
+        rec(W.OP_ADD, dtype=dt, size=n, a=0, b=1, out=2),
+        rec(W.OP_SOFTMAX, dtype=dt, size=4, dim=(1024,), a=0, out=2),
+        rec(W.OP_LAYERNORM, dtype=dt, size=4, dim=(1024,), fparam=(1e-5,), a=0, aux0=3, aux1=4, out=2),
+        rec(W.OP_SUM, dtype=dt, size=4, dim=(1024,), a=0, out=2),
+    ]
+    for r in cases:
+        arrays = [xa, ya, np.zeros_like(xa), gam, bet]
+        hp, stored = _capture(r, arrays)
+        m = ~np.isnan(hp)
+        assert m.sum() > 0
+        if dt == W.F32:
+            assert np.array_equal(hp[m].astype(np.float32).view(np.uint32), stored.view(np.uint32)[m])
+        else:
+            assert np.array_equal(np.array([oracle.round_bf16(v) for v in hp[m]], np.uint16),
+                                  stored.view(np.uint16)[m])
+    # the values themselves, against independent double evaluations
+    xd = bf16_val(xa).astype(np.float64) if dt == W.BF16 else x.astype(np.float64)
+    hp, _ = _capture(cases[0], [xa, ya, np.zeros_like(xa), gam, bet])
+    for i in range(0, n, 97):
+        assert abs(hp[i] - _gelu_decimal(float(xd[i]))) <= 1e-14 * max(abs(hp[i]), 1e-300) + 1e-300
+    hp, _ = _capture(cases[2], [xa, ya, np.zeros_like(xa), gam, bet])
+    ref = torch.softmax(torch.tensor(xd[:4096].reshape(4, 1024)), dim=1).numpy().reshape(-1)
+    assert np.allclose(hp[:4096], ref, rtol=1e-13, atol=0)
+
+
+def test_capture_of_sdpa_and_gemv_match_torch_in_double():
+    B, H, D, C = 2, 4, 64, 40
+    q = bf16(RNG.standard_normal(B * H * D))
+    K, V = bf16(RNG.standard_normal(B * H * C * D)), bf16(RNG.standard_normal(B * H * C * D))
+    o = np.zeros(B * H * D, np.uint16)
+    r = rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.BF16, size=B, dim=(H, D, C, H), lens=[40, 7],
+            a=0, aux0=1, aux1=2, out=3)
+    hp, _ = _capture(r, [q, K, V, o])
+    ref = _sdpa_torch(bf16_val(q).astype(np.float64).reshape(B, H, D),
+                      bf16_val(K).astype(np.float64).reshape(B, H, C, D),
+                      bf16_val(V).astype(np.float64).reshape(B, H, C, D), [40, 7])
+    assert np.allclose(hp, ref.reshape(-1), rtol=1e-12, atol=1e-12)
+    Kd, Nd = 96, 40
+    x = bf16(RNG.standard_normal(Kd))
+    Wm = bf16(0.02 * RNG.standard_normal(Kd * Nd))
+    r = rec(W.OP_GEMV, dtype=W.BF16, out_dtype=W.BF16, dim=(Kd, Nd), a=0, b=1, out=2)
+    hp, _ = _capture(r, [x, Wm, np.zeros(Nd, np.uint16)])
+    ref = bf16_val(x).astype(np.float64) @ bf16_val(Wm).astype(np.float64).reshape(Kd, Nd)
+    assert np.allclose(hp, ref, rtol=1e-13, atol=1e-15)
+
+
+def test_capture_of_inplace_rope_reports_both_tensors():
+    B, H, Hk, D = 1, 2, 1, 8
+    q = bf16(RNG.standard_normal(B * H * D))
+    k = bf16(RNG.standard_normal(B * Hk * D))
+    r = rec(W.OP_ROPE, dtype=W.BF16, size=B, dim=(H, D, 0, Hk), fparam=(10000.0,), lens=[5], a=0, b=1)
+    pool = oracle.Pool([q.copy(), k.copy()])
+    hq, hk = pool.run_capture(r, [(0, 0, q.nbytes, 2), (1, 0, k.nbytes, 2)])
+    assert not np.isnan(hq).any() and not np.isnan(hk).any()
+    ref_q = _rope_complex(bf16_val(q).astype(np.float64).reshape(B, H, D), np.array([4.0]), 10000.0)
+    ref_k = _rope_complex(bf16_val(k).astype(np.float64).reshape(B, Hk, D), np.array([4.0]), 10000.0)
+    assert np.allclose(hq, ref_q.reshape(-1), rtol=1e-12, atol=1e-14)
+    assert np.allclose(hk, ref_k.reshape(-1), rtol=1e-12, atol=1e-14)
+    assert np.array_equal(np.array([oracle.round_bf16(v) for v in hq], np.uint16), pool.arrays[0].view(np.uint16))

@@ -2,18 +2,37 @@
 the oracle standing in for the device every record passes, and a planted
 error in one logged output (a perturbed oracle result) is caught."""
 import numpy as np
+import pytest
 
 import gpu_harness as H
 import workloads as W
 
 
+class _HostPool:
+    """Stands in for the device pool: host arrays."""
+
+    def __init__(self, arrays):
+        self.tensors = [np.ascontiguousarray(a).view(np.uint8).reshape(-1).copy() for a in arrays]
+
+    def append_zeros(self, nbytes):
+        self.tensors.append(np.zeros(nbytes, np.uint8))
+
+    def download(self, i):
+        return self.tensors[i].copy()
+
+
 def _fake_run_gpu(perturb=None):
-    def run(arrays, recs, bursts=None, ctx=None, **kw):
-        out = H.run_oracle(arrays, recs)
+    def run(pool, recs, bursts=None, ctx=None, **kw):
+        out = H.run_oracle(pool.tensors, recs)
         if perturb is not None:
             perturb(out)
         return out
     return run
+
+
+@pytest.fixture(autouse=True)
+def _host_pool(monkeypatch):
+    monkeypatch.setattr(H, "DevicePool", _HostPool)
 
 
 def test_verify_passes_when_device_equals_oracle(monkeypatch):

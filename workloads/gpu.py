@@ -55,6 +55,14 @@ class DevicePool:
         torch.cuda.current_stream().synchronize()
         return self
 
+    def append_zeros(self, nbytes: int, device: str = "cuda:0") -> int:
+        """Add a zero-filled buffer of nbytes on the device; returns its index."""
+        import torch
+        self.tensors.append(torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device))
+        self.nbytes.append(int(nbytes))
+        torch.cuda.current_stream().synchronize()
+        return len(self.tensors) - 1
+
     @property
     def ptrs(self) -> List[int]:
         return [t.data_ptr() for t in self.tensors]
