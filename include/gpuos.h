@@ -370,6 +370,23 @@ int gpuos_eager_submit(const gpuos_desc* descs, uint32_t count, void* hip_stream
 /* Scratch bytes gpuos_eager_submit needs for these descriptors. */
 uint64_t gpuos_eager_scratch_bytes(const gpuos_desc* descs, uint32_t count);
 
+/* gpuos_eager_submit without a workspace argument and without allocating,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The split
+ * partials and counters of attention and vector-matrix descriptors live in a
+ * file-scope device array of GPUOS_EAGER_STATIC_SCRATCH_BYTES (16 MiB) that
+ * each GPU holds until the process ends; the call clears its counters with a
+ * small kernel first (no memset, so it can be captured).  Descriptors are
+ * those gpuos_eager_submit takes; all are checked before anything is
+ * launched.  Every call on one GPU shares the array, so calls that overlap
+ * on one GPU (on different streams, or from different threads) race: issue
+ * them on one stream, or order them.  Asynchronous: returns after
+ * enqueueing on hip_stream.  Errors: E_INVAL (a bad descriptor, or one whose
+ * split partials need more than GPUOS_EAGER_STATIC_SCRATCH_BYTES -- see
+ * gpuos_eager_scratch_bytes), E_HIP. */
+#define GPUOS_EAGER_STATIC_SCRATCH_BYTES (16u << 20)
+int gpuos_eager_submit_static(const gpuos_desc* descs, uint32_t count, void* hip_stream);
+
 /* hipGraph baseline: capture the eager launches of `descs` into a graph
  * and instantiate it; *graph_exec receives an opaque handle. */
 int gpuos_graph_build(const gpuos_desc* descs, uint32_t count, void* hip_stream, void* scratch,

@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gpuos_internal.h"
 #include "gpuos_ops.h"
 
@@ -603,6 +605,49 @@ extern "C" __global__ void __launch_bounds__(256) gpuos_eager_kernel(gpuos_desc 
 }
 
 extern "C" __global__ void gpuos_null_kernel() {}
+
+// ------------------------------------------------ eager launches, no allocation
+// gpuos_eager_submit_static runs the eager launches with the split-op
+// partials and counters in this file-scope array instead of a caller
+// workspace (for callers that cannot allocate).  Host code never uses the
+// array's name as an address: it takes each device's copy through
+// hipGetSymbolAddress once, with that device current, and passes that.
+namespace noalloc {
+static __device__ __align__(256) uint8_t scratch[GPUOS_EAGER_STATIC_SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+std::mutex mu;
+uint8_t* dev_ptr[MAX_DEVICES];  // device address of `scratch` per device, once taken
+}  // namespace noalloc
+
+// zero n 16-byte words (the split counters, which must start at zero)
+extern "C" __global__ void __launch_bounds__(256) gpuos_fill_zero_kernel(uint8_t* p, uint32_t n16) {
+    const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n16) wst16(wbuf(p, n16 * 16u), i * 16u, u32x4{0, 0, 0, 0});
+}
+
+// device address of the static scratch on the current device (taken once per device)
+hipError_t static_scratch(uint8_t** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= noalloc::MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(noalloc::mu);
+    if (!noalloc::dev_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc::scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        noalloc::dev_ptr[dev] = (uint8_t*)p;
+    }
+    *out = noalloc::dev_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_fill_zero(uint8_t* p, uint32_t bytes, hipStream_t s) {
+    const uint32_t n16 = bytes / 16u;
+    hipLaunchKernelGGL(gpuos_fill_zero_kernel, dim3((n16 + 255u) / 256u), dim3(256), 0, s, p, n16);
+    return hipGetLastError();
+}
 
 // ------------------------------------------------------------- HBM probe
 // Achievable bandwidth with the memory instructions the op bodies use

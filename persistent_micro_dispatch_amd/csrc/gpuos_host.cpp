@@ -38,6 +38,8 @@ hipError_t launch_executor(const ExecArgs& a, uint32_t slots, uint32_t grid, uin
 hipError_t launch_eager(const gpuos_desc& d, uint32_t kind, uint32_t ntiles, uint8_t* scratch, hipStream_t s);
 hipError_t launch_null(hipStream_t s);
 hipError_t launch_hbm_probe(const void* src, void* dst, uint32_t n, bool copy, uint32_t grid, hipStream_t s);
+hipError_t static_scratch(uint8_t** out);
+hipError_t launch_fill_zero(uint8_t* p, uint32_t bytes, hipStream_t s);
 }  // namespace gpuos
 
 using namespace gpuos;
@@ -1008,6 +1010,37 @@ int gpuos_eager_submit(const gpuos_desc* descs, uint32_t count, void* hip_stream
             continue;
         }
         if (launch_eager(d, d.op_id, p.ntiles, (uint8_t*)scratch, s) != hipSuccess) return GPUOS_E_HIP;
+    }
+    return GPUOS_OK;
+}
+
+int gpuos_eager_submit_static(const gpuos_desc* descs, uint32_t count, void* hip_stream) {
+    if (count && !descs) return GPUOS_E_INVAL;
+    // every descriptor is checked before anything is launched
+    bool split = false;
+    for (uint32_t i = 0; i < count; ++i) {
+        const gpuos_desc& d = descs[i];
+        if (d.op_id >= GPUOS_KIND_COUNT || d.op_id == GPUOS_OP_EXPR) return GPUOS_E_INVAL;
+        const Plan p = make_plan(plan_in(d.op_id, d));
+        if (p.status != GPUOS_ST_OK || p.scratch > GPUOS_EAGER_STATIC_SCRATCH_BYTES) return GPUOS_E_INVAL;
+        split = split || p.scratch > 0;
+    }
+    if (count == 0) return GPUOS_OK;
+    uint8_t* scr = nullptr;
+    if (static_scratch(&scr) != hipSuccess) return GPUOS_E_HIP;
+    hipStream_t s = (hipStream_t)hip_stream;
+    // the split counters start at zero (each merge leaves them at zero, but
+    // an earlier call may have ended early): a fill kernel, which a graph
+    // capture records as an ordinary kernel node
+    if (split && launch_fill_zero(scr, (uint32_t)COUNTER_AREA, s) != hipSuccess) return GPUOS_E_HIP;
+    for (uint32_t i = 0; i < count; ++i) {
+        const gpuos_desc& d = descs[i];
+        if (d.op_id == GPUOS_OP_NOP) {
+            if (launch_null(s) != hipSuccess) return GPUOS_E_HIP;
+            continue;
+        }
+        const Plan p = make_plan(plan_in(d.op_id, d));
+        if (launch_eager(d, d.op_id, p.ntiles, scr, s) != hipSuccess) return GPUOS_E_HIP;
     }
     return GPUOS_OK;
 }

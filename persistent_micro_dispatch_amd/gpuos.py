@@ -108,6 +108,7 @@ EXPORTS = [
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
     "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_latency_bench", "gpuos_trace_read",
     "gpuos_hbm_probe", "gpuos_register_expr", "gpuos_ring_peek",
+    "gpuos_eager_submit_static",
 ]
 
 TRACE_DTYPE = np.dtype([("seq", "<u8"), ("tile", "<u4"), ("hw", "<u4"), ("t_claim", "<u8"), ("t_ready", "<u8"),
@@ -158,6 +159,7 @@ def lib():
         "gpuos_hbm_probe": ([vp, vp, u64, u32, u32, vp, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
         "gpuos_register_expr": ([vp, u32, vp, u32], ctypes.c_int),
         "gpuos_ring_peek": ([vp, u64, vp, vp], ctypes.c_int),
+        "gpuos_eager_submit_static": ([vp, u32, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -285,6 +287,14 @@ def gpuos_eager_scratch_bytes(descs: np.ndarray) -> int:
 def gpuos_eager_submit(descs: np.ndarray, hip_stream: int, scratch: int, scratch_bytes: int) -> int:
     return lib().gpuos_eager_submit(_descs_ptr(descs), len(descs), hip_stream or None, scratch or None,
                                     scratch_bytes)
+
+
+GPUOS_EAGER_STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def gpuos_eager_submit_static(descs: np.ndarray, hip_stream: int) -> int:
+    """gpuos_eager_submit with the library's static scratch (no allocation)."""
+    return lib().gpuos_eager_submit_static(_descs_ptr(descs), len(descs), hip_stream or None)
 
 
 def gpuos_graph_build(descs: np.ndarray, hip_stream: int, scratch: int, scratch_bytes: int) -> int:

@@ -477,3 +477,20 @@ def test_six_dependencies_leave_no_stale_side_words():
     assert deps1 == list(range(1, 11))          # the ten readers, by delta
     assert sorted(int(v) for v in d2["dep_delta"]) == list(range(1, 7))
     assert not x2.any(), f"stale side words {x2[:8]}"
+
+
+def test_static_eager_submit_rejects_oversized_split_partials_before_launching():
+    """A vector-matrix product whose split partials exceed the static array
+    (here 1024 row splits x 65536 columns x 4 B = 256 MiB) is refused with
+    E_INVAL before anything is launched (the pointers are never used)."""
+    d = G.new_descs(2)
+    d["op_id"] = G.GPUOS_OP_GEMV
+    d["flags"] = G.flags(G.GPUOS_BF16)
+    d["input_a"], d["input_b"], d["output"] = 0x10_0000_0000, 0x20_0000_0000, 0x30_0000_0000
+    d["dim"][:, 0], d["dim"][:, 1] = 1024, 64
+    d["dim"][1, 0], d["dim"][1, 1] = 131072, 65536
+    assert G.gpuos_eager_scratch_bytes(d[1:]) > G.GPUOS_EAGER_STATIC_SCRATCH_BYTES
+    assert G.gpuos_eager_submit_static(d, 0) == G.GPUOS_E_INVAL
+    bad = G.new_descs(1)
+    bad["op_id"] = G.GPUOS_OP_EXPR  # needs a table; the eager path has none
+    assert G.gpuos_eager_submit_static(bad, 0) == G.GPUOS_E_INVAL
