@@ -11,14 +11,14 @@ op body, completion) over one seeded synthetic descriptor stream:
   rows                   50,000 row ops (sum/max/min/softmax/LayerNorm) on
                          [r in 1..64, h in {768,1024,2048,4096}] fp32 slices
                          of a 2 GiB pool
-  decode                 25 decode steps x 32 layers x {RoPE, KV append,
+  decode                 2,000 decode steps x 32 layers x {RoPE, KV append,
                          SDPA}: B in {1,2,4,8}, 32 heads x 128, bf16 KV cache
                          of 4096 per sequence (16 GiB), L in [128, 4096]
   decode_gqa             the same with 32 query heads sharing 8 key/value
                          heads (grouped-query attention, 4 GiB of cache)
   copy                   one 1 GiB COPY descriptor (calibrates HBM counters)
   copy64                 the same 1 GiB copied by 64 independent 16 MiB descriptors
-  mixed                  10 tokens x 32 layers x 11 ops at hidden 1024 (LN,
+  mixed                  500 tokens x 32 layers x 11 ops at hidden 1024 (LN,
                          GEMV 1024x3072, RoPE, KV append, SDPA, add, LN, GEMV
                          1024x3072, GELU, GEMV 3072x1024, add); with --gemm a
                          bf16 8192^3 GEMM loop co-runs on a second stream
@@ -194,17 +194,17 @@ def make_stream(name):
         desc = ("row ops: 50,000 descriptors of [r, h] fp32, r in {1,2,...,64}, h in {768,1024,2048,4096}, "
                 "x ~ N(0,2) from a 2 GiB pool; op uniform over {sum, max, min, softmax, LayerNorm}")
     elif name == "decode":
-        s, fill = W.make_decode(steps=25), "device"
-        desc = ("attention decoding: 25 decode steps x 32 layers x {RoPE(theta 1e4), KV append, SDPA}; "
+        s, fill = W.make_decode(steps=2000), "device"
+        desc = ("attention decoding: 2,000 decode steps x 32 layers x {RoPE(theta 1e4), KV append, SDPA}; "
                 "B in {1,2,4,8}, 32 heads x 128, bf16 KV cache 4096/sequence, L in [128, 4096] +1 per step")
     elif name == "decode_gqa":
-        s, fill = W.make_decode(steps=25, kv_heads=8), "device"
-        desc = ("attention decoding with grouped-query attention: 25 decode steps x 32 layers x {RoPE(theta 1e4), "
+        s, fill = W.make_decode(steps=2000, kv_heads=8), "device"
+        desc = ("attention decoding with grouped-query attention: 2,000 decode steps x 32 layers x {RoPE(theta 1e4), "
                 "KV append, SDPA}; B in {1,2,4,8}, 32 query heads sharing 8 key/value heads x 128, bf16 KV cache "
                 "4096/sequence, L in [128, 4096] +1 per step")
     elif name == "mixed":
-        s, fill = W.make_mixed(tokens=10), "device"
-        desc = ("mixed decode pipeline: 10 tokens x 32 layers x 11 ops at hidden 1024, 8 heads x 128, bf16: "
+        s, fill = W.make_mixed(tokens=500), "device"
+        desc = ("mixed decode pipeline: 500 tokens x 32 layers x 11 ops at hidden 1024, 8 heads x 128, bf16: "
                 "LN, GEMV 1x1024.1024x3072, RoPE, KV append, SDPA (L in [64, 2048]), add, LN, GEMV 1024x3072, "
                 "GELU, GEMV 3072x1024, add")
     else:
@@ -212,48 +212,84 @@ def make_stream(name):
     return s, desc, fill
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="elementwise")
-    ap.add_argument("--waves", type=int, default=0,
-                    help="wave64s per workgroup (one workgroup per CU); 0: 4 for rows, decode, decode_gqa "
-                         "and copy, else 1")
-    ap.add_argument("--ring", type=int, default=512,
-                    help="ring entries: descriptors in flight, which is also the window of hazard tracking")
-    ap.add_argument("--units-per-wave", type=int, default=0, choices=(0, 1, 2),
-                    help="units a worker wave holds at once (2 lets a ready unit overtake a waiting one); "
-                         "0: 2 for decode, decode_gqa and rows, else 1")
-    ap.add_argument("--num-wgs", type=int, default=0,
-                    help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
-    ap.add_argument("--backoff", type=int, default=0,
-                    help="s_sleep cap of idle waits, 1..127 (0: the library's default)")
-    ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop (mixed workload)")
-    ap.add_argument("--no-baselines", action="store_true")
-    ap.add_argument("--no-cpu", action="store_true")
-    args = ap.parse_args()
-    if args.waves == 0:
-        args.waves = 4 if args.workload in ("rows", "decode", "decode_gqa", "copy", "copy64") else 1
-    if args.units_per_wave == 0:
-        args.units_per_wave = 2 if args.workload in ("decode", "decode_gqa", "rows") else 1
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the dispatcher is a "
-              "single-device path; the design notes describe how it would shard.", file=sys.stderr)
-        sys.exit(2)
+WAVES_DEFAULT = {"rows": 4, "decode": 4, "decode_gqa": 4, "copy": 4, "copy64": 4}
+UPW_DEFAULT = {"decode": 2, "decode_gqa": 2, "rows": 2}
+# the workloads reported beside the headline in a default run, with the
+# steps each times (the decode and mixed streams run about 1-2 s per step)
+SUB_WORKLOADS = ("pr1", "rows", "decode", "decode_gqa", "mixed")
+SUB_STEPS = {"pr1": 20, "rows": 10, "decode": 2, "decode_gqa": 3, "mixed": 3}
 
+
+def host_cpu():
+    """Core count and CPU model of this host (the oracle leg's machine)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "model": model}
+
+
+def cpu_oracle(stream, recs, arrays, fill, budget_s):
+    """The oracle on a bounded prefix of the same stream, grown until it
+    takes about budget_s, on one host core (the process is pinned to one
+    CPU for the duration).  Host-filled streams use the same inputs as the
+    GPU; device-filled ones (pools of GiBs) use zero-filled host buffers of
+    the same shapes, which leaves the oracle's work (every op runs the same
+    loops whatever the values) unchanged."""
+    import oracle
+    nd = len(recs)
+    if fill == "host":
+        def make_pool():
+            return oracle.Pool([a.copy() for a in arrays])
+        n_cpu, what = min(nd, 1000), "the same inputs"
+    else:
+        def make_pool():
+            return oracle.Pool([np.zeros(b.nbytes, np.uint8) for b in stream.buffers])
+        n_cpu, what = min(nd, 8), "zero-filled host buffers of the stream's shapes"
+    before = os.sched_getaffinity(0)
+    core = min(before)
+    os.sched_setaffinity(0, {core})
+    try:
+        while True:
+            p = make_pool()
+            ta = time.perf_counter()
+            p.run(recs[:n_cpu])
+            el = time.perf_counter() - ta
+            del p
+            if el > budget_s or n_cpu >= nd:
+                break
+            n_cpu = min(nd, n_cpu * (4 if el < budget_s / 5 else 2))
+    finally:
+        os.sched_setaffinity(0, before)
+    hc = host_cpu()
+    return {"value": n_cpu / el, "unit": "micro-ops/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n_cpu} of {nd} descriptors of the same stream on {what}, sequential C "
+                      f"oracle (fp64), one thread pinned to CPU {core}, {el:.1f} s",
+            "host_nproc": hc["nproc"], "host_cpu_model": hc["model"]}
+
+
+def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_wgs=0, backoff=0,
+                 headline=False, baselines=True, cpu_budget_s=10.0, gemm=False, probe=None):
+    """Time `steps` executor launches over one workload's stream (after
+    `warmup` untimed ones) and measure its closed-loop latency, roofline,
+    baselines and CPU oracle.  Returns the record (the headline adds the
+    dispatch micro-benchmarks, size buckets and injection figures)."""
     import torch
 
     import workloads as W
     from persistent_micro_dispatch_amd import gpuos as G
     from workloads.gpu import DevicePool, to_descs
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    stream, wdesc, fill = make_stream(args.workload)
+    waves = waves or WAVES_DEFAULT.get(name, 1)
+    units_per_wave = units_per_wave or UPW_DEFAULT.get(name, 1)
+    stream, wdesc, fill = make_stream(name)
     recs = stream.recs
     nd = len(recs)
-    log(f"workload {args.workload}: {nd} descriptors, {len(stream.bursts)} bursts, fill={fill}")
+    log(f"workload {name}: {nd} descriptors, {len(stream.bursts)} bursts, fill={fill}")
     arrays = [b.host_bytes() for b in stream.buffers] if fill == "host" else None
     pool = DevicePool(arrays) if fill == "host" else DevicePool.from_stream(stream, fill="device")
     descs = to_descs(recs, pool.ptrs)
@@ -265,21 +301,9 @@ def main():
     # dispatches would otherwise queue it behind the executor)
     chain_buf = torch.zeros(256, dtype=torch.float32, device="cuda")
     one_buf = torch.ones(256, dtype=torch.float32, device="cuda")
-    # achievable HBM bandwidth with the op bodies' memory instructions (1 GiB
-    # read and copy), measured before the executor is resident
-    pb = 1 << 30
-    p_src = torch.empty(pb, dtype=torch.uint8, device="cuda").fill_(7)
-    p_dst = torch.empty(pb, dtype=torch.uint8, device="cuda")
     torch.cuda.current_stream().synchronize()
-    sp0 = torch.cuda.current_stream().cuda_stream
-    hbm_probe = {"bytes": pb,
-                 "read_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 0, 5, sp0),
-                 "copy_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 1, 5, sp0)}
-    del p_src, p_dst
-    torch.cuda.current_stream().synchronize()
-    log(f"hbm probe: read {hbm_probe['read_gbs']:.0f} GB/s, copy {hbm_probe['copy_gbs']:.0f} GB/s")
-    ctx = G.gpuos_init(waves_per_wg=args.waves, ring_entries=args.ring, num_wgs=args.num_wgs,
-                       units_per_wave=args.units_per_wave, backoff_max=args.backoff)
+    ctx = G.gpuos_init(waves_per_wg=waves, ring_entries=ring, num_wgs=num_wgs,
+                       units_per_wave=units_per_wave, backoff_max=backoff)
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     st0 = G.gpuos_stats_get(ctx)
 
@@ -292,22 +316,24 @@ def main():
         assert G.gpuos_pause(ctx, 30_000_000_000) == 0
         return G.gpuos_stats_get(ctx)["last_launch_ms"]
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         one_step()
-        log(f"warmup step {i} done")
+        log(f"{name}: warmup step {i} done")
+    st_w = G.gpuos_stats_get(ctx)
     launch_ms = []
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         launch_ms.append(one_step())
-        log(f"step {i}: executor launch {launch_ms[-1]:.2f} ms")
+        log(f"{name}: step {i}: executor launch {launch_ms[-1]:.2f} ms")
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    ops_per_s = nd * args.steps / (t1 - t0)
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    ops_per_s = nd * steps / (t1 - t0)
     st = G.gpuos_stats_get(ctx)
     extra = {}
 
-    # ---- co-running GEMM (mixed workload): bf16 8192^3 loop on its own stream
-    if args.gemm:
+    # ---- co-running GEMM: a bf16 8192^3 loop on its own stream, alone and
+    # while the micro-op stream runs
+    if gemm:
         gs = torch.cuda.Stream()
         with torch.cuda.stream(gs):
             a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
@@ -324,7 +350,9 @@ def main():
             e1.record(gs)
         gs.synchronize()
         gemm_alone_ms = e0.elapsed_time(e1) / n_gemm
-        # GEMMs and the micro-op stream together
+        # enough GEMMs to cover about two seconds, so that the steps timed
+        # beside them run while they do
+        n_gemm = max(n_gemm, int(2000.0 / gemm_alone_ms))
         with torch.cuda.stream(gs):
             e0.record(gs)
             for _ in range(n_gemm):
@@ -346,43 +374,48 @@ def main():
             "corun_steps": k_co,
             "ops_per_s_with_gemm": nd * k_co / (tc1 - tc0) if k_co else None,
         })
+        del a, b, c
         log(f"gemm alone {gemm_alone_ms:.3f} ms, co-run {gemm_co_ms:.3f} ms; {k_co} steps during the GEMMs")
 
     # ---- closed-loop latency: one descriptor at a time, waited for
-    assert G.gpuos_resume(ctx) == 0
     # (measured inside the library, as a C caller sees it; the same loop
     # through the Python binding adds its call overhead, reported beside)
-    nlat = min(nd, 2000)
+    assert G.gpuos_resume(ctx) == 0
+    nlat = min(nd, 2000 if headline else 500)
     lat = G.gpuos_latency_bench(ctx, descs[:nlat])
-    lat_py = np.zeros(min(nlat, 500))
-    for i in range(len(lat_py)):
-        ta = time.perf_counter_ns()
-        rc, f = G.gpuos_submit(ctx, descs[i:i + 1], G.GPUOS_SUBMIT_BLOCK)
-        rc2 = G.gpuos_sync(ctx, f, 10_000_000_000)[0]
-        lat_py[i] = (time.perf_counter_ns() - ta) / 1e3
-        assert rc == 0 and rc2 == 0
-    # ---- dispatch micro-benchmarks: NOP stream (bursts of 64) and a chain
-    nop = G.new_descs(100_000)
-    nb = np.full(len(nop) // 64, 64, np.uint32)
-    ta = time.perf_counter()
-    rc, _, _ = G.gpuos_submit_bursts(ctx, nop, nb, G.GPUOS_SUBMIT_BLOCK)
-    assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
-    nop_s = time.perf_counter() - ta
-    chain = G.new_descs(5000)
-    chain["op_id"] = G.GPUOS_OP_ADD
-    chain["flags"] = G.flags(G.GPUOS_F32)
-    chain["size"] = 256
-    chain["input_a"] = chain["output"] = chain_buf.data_ptr()
-    chain["input_b"] = one_buf.data_ptr()
-    ta = time.perf_counter()
-    rc, _, _ = G.gpuos_submit_bursts(ctx, chain, np.full(len(chain) // 50, 50, np.uint32), G.GPUOS_SUBMIT_BLOCK)
-    assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
-    chain_s = time.perf_counter() - ta
+    lat_py = None
+    nop_s = chain_s = None
+    buckets = injection = None
+    chain = nop = None
+    if headline:
+        lat_py = np.zeros(min(nlat, 500))
+        for i in range(len(lat_py)):
+            ta = time.perf_counter_ns()
+            rc, f = G.gpuos_submit(ctx, descs[i:i + 1], G.GPUOS_SUBMIT_BLOCK)
+            rc2 = G.gpuos_sync(ctx, f, 10_000_000_000)[0]
+            lat_py[i] = (time.perf_counter_ns() - ta) / 1e3
+            assert rc == 0 and rc2 == 0
+        # ---- dispatch micro-benchmarks: NOP stream (bursts of 64) and a chain
+        nop = G.new_descs(100_000)
+        nb = np.full(len(nop) // 64, 64, np.uint32)
+        ta = time.perf_counter()
+        rc, _, _ = G.gpuos_submit_bursts(ctx, nop, nb, G.GPUOS_SUBMIT_BLOCK)
+        assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
+        nop_s = time.perf_counter() - ta
+        chain = G.new_descs(5000)
+        chain["op_id"] = G.GPUOS_OP_ADD
+        chain["flags"] = G.flags(G.GPUOS_F32)
+        chain["size"] = 256
+        chain["input_a"] = chain["output"] = chain_buf.data_ptr()
+        chain["input_b"] = one_buf.data_ptr()
+        ta = time.perf_counter()
+        rc, _, _ = G.gpuos_submit_bursts(ctx, chain, np.full(len(chain) // 50, 50, np.uint32), G.GPUOS_SUBMIT_BLOCK)
+        assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
+        chain_s = time.perf_counter() - ta
     # ---- element-wise throughput per log2-size bucket: the bucket's
     # descriptors in stream order, once with hazard ordering and once as
     # independent ops (NOHAZARD; outputs race, nothing reads them after)
-    buckets = None
-    if args.workload in ("elementwise", "pr1"):
+    if headline and name in ("elementwise", "pr1"):
         buckets = {}
         lg = np.minimum(np.floor(np.log2(recs["size"])).astype(np.int64), 15)
         per_op = W.algorithmic_bytes(recs)
@@ -408,8 +441,7 @@ def main():
     # ---- injected operator (an element-wise program bound by a table flip):
     # registration latency, and add/mul descriptors of the stream run as
     # built-in ops and as the program a+b / a*b (independent ops)
-    injection = None
-    if args.workload == "elementwise":
+    if headline and name == "elementwise":
         sel = np.nonzero((recs["op"] == W.OP_ADD) | (recs["op"] == W.OP_MUL))[0][:20000]
         sub = descs[sel].copy()
         nbk = np.full(len(sub) // 64, 64, np.uint32)
@@ -445,32 +477,32 @@ def main():
             row[key + "_gbs"] = by / el / 1e9
         injection = row
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
-    chain_ok = float(chain_buf.cpu()[0]) == 5000.0
-    st_end = G.gpuos_stats_get(ctx)
+    chain_ok = float(chain_buf.cpu()[0]) == 5000.0 if headline else None
 
-    if not args.no_baselines:
-        # ---- eager: one hipLaunchKernel per descriptor on a torch stream
+    if baselines:
+        # ---- eager: one hipLaunchKernel per descriptor (same op bodies) on
+        # a torch stream
         s_eager = torch.cuda.Stream()
-        nb_e = min(nd, 20_000)
+        nb_e = min(nd, 20_000 if headline else 5_000)
         scratch_b = G.gpuos_eager_scratch_bytes(descs[:nb_e])
         scratch = torch.zeros(scratch_b, dtype=torch.uint8, device="cuda")
         torch.cuda.current_stream().synchronize()
         sp = s_eager.cuda_stream
-        assert G.gpuos_eager_submit(descs[:200], sp, scratch.data_ptr(), scratch_b) == 0
+        assert G.gpuos_eager_submit(descs[:min(nd, 200)], sp, scratch.data_ptr(), scratch_b) == 0
         s_eager.synchronize()
         ta = time.perf_counter()
         assert G.gpuos_eager_submit(descs[:nb_e], sp, scratch.data_ptr(), scratch_b) == 0
         s_eager.synchronize()
         eager_s = time.perf_counter() - ta
-        eager_lat = np.zeros(500)
-        for i in range(500):
+        eager_lat = np.zeros(min(nd, 500))
+        for i in range(len(eager_lat)):
             ta = time.perf_counter_ns()
-            assert G.gpuos_eager_submit(descs[i % nd:i % nd + 1], sp, scratch.data_ptr(), scratch_b) == 0
+            assert G.gpuos_eager_submit(descs[i:i + 1], sp, scratch.data_ptr(), scratch_b) == 0
             s_eager.synchronize()
             eager_lat[i] = (time.perf_counter_ns() - ta) / 1e3
         # ---- hipGraph: captured per burst; stable = replay prebuilt graphs,
         #      variable = capture + instantiate + launch for every burst
-        ng = min(len(bursts), 300)
+        ng = min(len(bursts), 300 if headline else 100)
         offs = np.r_[0, np.cumsum(bursts[:ng])].astype(np.int64)
         ta = time.perf_counter()
         graphs = []
@@ -488,10 +520,8 @@ def main():
         for ge in graphs:
             G.gpuos_graph_destroy(ge)
         gdesc = int(offs[ng])
-        null_async, null_sync = G.gpuos_null_launch_bench(sp, 20000)
         # ---- PyTorch eager, the pages' baseline: one torch op per descriptor
-        calls = torch_eager_calls(recs, pool, 20_000)
-        torch_rate = None
+        calls = torch_eager_calls(recs, pool, 20_000 if headline else 5_000)
         if calls:
             for c in calls[:200]:
                 c()
@@ -509,91 +539,154 @@ def main():
             "graph_stable_ops_per_s": gdesc / stable_s,
             "graph_variable_ops_per_s": gdesc / var_s,
             "speedup_vs_graph_stable": ops_per_s / (gdesc / stable_s),
-            "null_launch_us": null_async / 1e3,
-            "null_launch_sync_us": null_sync / 1e3,
         })
+        if headline:
+            null_async, null_sync = G.gpuos_null_launch_bench(sp, 20000)
+            extra.update({"null_launch_us": null_async / 1e3, "null_launch_sync_us": null_sync / 1e3})
+        del scratch
     assert G.gpuos_shutdown(ctx) == 0
 
     # ---- roofline of the executor kernel (one launch = one step)
     mean_launch_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (mean_launch_ms * 1e-3) / 1e9
-    tb = recorded_traffic(args.workload if args.units_per_wave == 1 else f"{args.workload}/upw2")
+    tb = recorded_traffic(name if units_per_wave == 1 else f"{name}/upw2")
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": tb / (mean_launch_ms * 1e-3) / 1e9 if tb else None,
             "traffic_bytes_per_launch": tb,
-            "kernel": "gpuos_executor_s2" if args.units_per_wave == 2 else "gpuos_executor",
+            "kernel": "gpuos_executor_s2" if units_per_wave == 2 else "gpuos_executor",
             "launch_ms": mean_launch_ms, "bytes_per_launch": step_bytes}
+    levels = dag_levels(recs) if name in ("elementwise", "pr1") else None
+    cpu = cpu_oracle(stream, recs, arrays, fill, cpu_budget_s) if cpu_budget_s > 0 else None
 
-    levels = dag_levels(recs) if args.workload in ("elementwise", "pr1") else None
-    cpu = None
-    if not args.no_cpu:
-        # the oracle on a bounded prefix of the same stream, grown until it
-        # takes about 10 s.  Host-filled streams use the same inputs as the
-        # GPU; device-filled ones (pools of GiBs) use zero-filled host
-        # buffers of the same shapes, which leaves the oracle's work (every
-        # op runs the same loops whatever the values) unchanged.
-        import oracle
-        if fill == "host":
-            def make_pool():
-                return oracle.Pool([a.copy() for a in arrays])
-            n_cpu, what = min(nd, 1000), "the same inputs"
-        else:
-            def make_pool():
-                return oracle.Pool([np.zeros(b.nbytes, np.uint8) for b in stream.buffers])
-            n_cpu, what = min(nd, 8), "zero-filled host buffers of the stream's shapes"
-        while True:
-            p = make_pool()
-            ta = time.perf_counter()
-            p.run(recs[:n_cpu])
-            el = time.perf_counter() - ta
-            del p
-            if el > 10.0 or n_cpu >= nd:
-                break
-            n_cpu = min(nd, n_cpu * (4 if el < 2.0 else 2))
-        cpu = {"value": n_cpu / el, "unit": "micro-ops/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {n_cpu} of {nd} descriptors of the same stream on {what}, "
-                         f"sequential C oracle (fp64), one thread, {el:.1f} s"}
-
-    steps_total = max(1, args.steps + args.warmup)
-    out = {
-        "metric": "micro-ops/sec (+ p50 per-op latency us, vs per-op hipLaunch; HBM GB/s frac)",
+    # host cost over the warmup and timed steps only
+    dsub = max(1, st["submitted"] - st0["submitted"])
+    steps_total = max(1, steps + warmup)
+    rec = {
         "value": ops_per_s,
         "unit": "micro-ops/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32 (bf16 operands computed in f32)",
-        "data": "synthetic",
-        "config": {"workload": wdesc, "descriptors_per_step": nd, "waves_per_wg": args.waves,
+        "config": {"workload": wdesc, "descriptors_per_step": nd, "waves_per_wg": waves,
                    "num_wgs": st["num_wgs"], "ring_entries": st["ring_entries"],
-                   "units_per_wave": args.units_per_wave, "fill": fill},
+                   "units_per_wave": units_per_wave, "fill": fill},
         "p50_us": float(np.percentile(lat, 50)),
         "p99_us": float(np.percentile(lat, 99)),
-        "p50_us_python": float(np.percentile(lat_py, 50)),
-        "dispatch_interval_us_nop": nop_s / len(nop) * 1e6,
-        "dependent_chain_us_per_op": chain_s / len(chain) * 1e6,
-        "dependent_chain_ok": chain_ok,
         "stream_gbs": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "dag_levels": levels,
         "us_per_dag_level": ms_per_step * 1e3 / levels if levels else None,
         "units_per_step": (st["units"] - st0["units"]) / steps_total,
         "dep_waits_per_step": (st["dep_waits"] - st0["dep_waits"]) / steps_total,
         "fetch_batches_per_step": (st["fetch_batches"] - st0["fetch_batches"]) / steps_total,
-        "host_submit_ns_per_desc": st_end["ns_submit"] / max(1, st_end["submitted"]),
-        "host_blocked_ns_per_desc": st_end["ns_blocked"] / max(1, st_end["submitted"]),
-        "host_annotate_ns_per_desc": st_end["ns_annotate"] / max(1, st_end["submitted"]),
-        "size_buckets": buckets,
-        "hbm_probe": hbm_probe,
-        "injection": injection,
+        "host_submit_ns_per_desc": (st["ns_submit"] - st0["ns_submit"]) / dsub,
+        "host_blocked_ns_per_desc": (st["ns_blocked"] - st0["ns_blocked"]) / dsub,
+        "host_annotate_ns_per_desc": (st["ns_annotate"] - st0["ns_annotate"]) / dsub,
+        "timed_steps_host_submit_ns_per_desc": (st["ns_submit"] - st_w["ns_submit"]) / max(1, st["submitted"] - st_w["submitted"]),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    out.update(extra)
+    if headline:
+        rec.update({
+            "p50_us_python": float(np.percentile(lat_py, 50)),
+            "dispatch_interval_us_nop": nop_s / len(nop) * 1e6,
+            "dependent_chain_us_per_op": chain_s / len(chain) * 1e6,
+            "dependent_chain_ok": chain_ok,
+            "size_buckets": buckets,
+            "injection": injection,
+        })
+    rec.update(extra)
+    del pool, descs, chain_buf, one_buf
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="elementwise")
+    ap.add_argument("--waves", type=int, default=0,
+                    help="wave64s per workgroup (one workgroup per CU); 0: 4 for rows, decode, decode_gqa "
+                         "and copy, else 1")
+    ap.add_argument("--ring", type=int, default=512,
+                    help="ring entries: descriptors in flight, which is also the window of hazard tracking")
+    ap.add_argument("--units-per-wave", type=int, default=0, choices=(0, 1, 2),
+                    help="units a worker wave holds at once (2 lets a ready unit overtake a waiting one); "
+                         "0: 2 for decode, decode_gqa and rows, else 1")
+    ap.add_argument("--num-wgs", type=int, default=0,
+                    help="executor workgroups (0: one per CU); fewer leave whole CUs to other kernels")
+    ap.add_argument("--backoff", type=int, default=0,
+                    help="s_sleep cap of idle waits, 1..127 (0: the library's default)")
+    ap.add_argument("--gemm", action="store_true", help="co-run a bf16 8192^3 GEMM loop")
+    ap.add_argument("--no-baselines", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-sub", action="store_true",
+                    help="skip the other workloads' records (pr1, rows, decode, decode_gqa, mixed)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the dispatcher is a "
+              "single-device path; the design notes describe how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from persistent_micro_dispatch_amd import gpuos as G
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    # achievable HBM bandwidth with the op bodies' memory instructions (1 GiB
+    # read and copy), measured before the executor is resident
+    pb = 1 << 30
+    p_src = torch.empty(pb, dtype=torch.uint8, device="cuda").fill_(7)
+    p_dst = torch.empty(pb, dtype=torch.uint8, device="cuda")
+    torch.cuda.current_stream().synchronize()
+    sp0 = torch.cuda.current_stream().cuda_stream
+    hbm_probe = {"bytes": pb,
+                 "read_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 0, 5, sp0),
+                 "copy_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 1, 5, sp0)}
+    del p_src, p_dst
+    torch.cuda.current_stream().synchronize()
+    torch.cuda.empty_cache()
+    log(f"hbm probe: read {hbm_probe['read_gbs']:.0f} GB/s, copy {hbm_probe['copy_gbs']:.0f} GB/s")
+
+    head = run_workload(args.workload, args.steps, args.warmup, waves=args.waves,
+                        units_per_wave=args.units_per_wave, ring=args.ring, num_wgs=args.num_wgs,
+                        backoff=args.backoff, headline=True, baselines=not args.no_baselines,
+                        cpu_budget_s=0.0 if args.no_cpu else 10.0, gemm=args.gemm)
+    subs = {}
+    if not args.no_sub and args.workload == "elementwise":
+        for name in SUB_WORKLOADS:
+            k = min(args.steps, SUB_STEPS[name])
+            subs[name] = run_workload(name, k, 1, baselines=not args.no_baselines,
+                                      cpu_budget_s=0.0 if args.no_cpu else 4.0)
+            log(f"{name}: {subs[name]['value']:.0f} micro-ops/s, {subs[name]['ms_per_step']:.2f} ms per step")
+        # the mixed pipeline beside a bf16 8192^3 GEMM loop, with the executor
+        # on 64 workgroups of two waves (the rest of the chip left to the GEMM)
+        subs["mixed_with_gemm"] = run_workload("mixed", 1, 1, waves=2, num_wgs=64, baselines=False,
+                                               cpu_budget_s=0.0, gemm=True)
+    out = {
+        "metric": "micro-ops/sec (+ p50 per-op latency us, vs per-op hipLaunch; HBM GB/s frac)",
+        "value": head.pop("value"),
+        "unit": head.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 operands computed in f32)",
+        "data": "synthetic",
+        "config": head.pop("config"),
+    }
+    head.pop("steps")
+    head.pop("warmup")
+    out.update(head)
+    out["hbm_probe"] = hbm_probe
+    out["host_cpu"] = host_cpu()
+    if subs:
+        out["workloads"] = subs
     print(json.dumps(out))
 
 

@@ -58,8 +58,15 @@ template <typename T>
 inline void st_rel(T* p, T v) { __atomic_store_n(p, v, __ATOMIC_RELEASE); }
 
 // --------------------------------------------------------------------------
-// Operand byte ranges of a descriptor for hazard tracking (conservative
-// bounding boxes for the strided KV-cache rows).
+// Operand byte ranges of a descriptor for hazard tracking.  A declared range
+// may be larger than what the op touches (an extra wait, never a missing
+// one: the op itself waits for every earlier conflict in the range, so a
+// later op that waits for it is ordered after those too).  The KV caches
+// are declared whole: an append writes one row per head, H rows C rows
+// apart, and attention reads each head's first L rows; declaring the
+// batch rows' whole span of each cache gives the same conflicts between
+// the appends and attention ops of a decode stream, and keeps the tracker
+// from cutting the cache into a new sliver of intervals at every step.
 // --------------------------------------------------------------------------
 int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
     int n = 0;
@@ -112,25 +119,19 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
             const uint64_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
             add(d.input_a, sz * H * D * es, false);
             add(d.input_b, sz * H * D * es, false);
-            for (uint32_t b = 0; b < sz && b < MAX_B; ++b) {
-                const uint64_t pos = lens_at(lensw, b) - 1;
-                const uint64_t lo = ((b * H) * C + pos) * D * es;
-                const uint64_t hi = ((b * H + H - 1) * C + pos) * D * es + D * es;
-                add(d.aux[0] + lo, hi - lo, true);
-                add(d.aux[1] + lo, hi - lo, true);
-            }
+            add(d.aux[0], sz * H * C * D * es, true);  // batch rows 0..B-1 of each cache, whole
+            add(d.aux[1], sz * H * C * D * es, true);
             break;
         }
         case GPUOS_OP_SDPA: {
             const uint64_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
             const uint64_t Hkv = d.dim[3] ? d.dim[3] : H;
             add(d.input_a, sz * H * D * es, false);
-            for (uint32_t b = 0; b < sz && b < MAX_B; ++b) {
-                const uint64_t L = lens_at(lensw, b);
-                const uint64_t lo = (b * Hkv) * C * D * es;
-                const uint64_t hi = ((b * Hkv + Hkv - 1) * C + L) * D * es;
-                add(d.aux[0] + lo, hi - lo, false);
-                add(d.aux[1] + lo, hi - lo, false);
+            if (sz > 0 && sz <= MAX_B) {
+                // from the first key of batch row 0 to the last key read in row B-1
+                const uint64_t hi = (((sz - 1) * Hkv + Hkv - 1) * C + lens_at(lensw, (uint32_t)sz - 1)) * D * es;
+                add(d.aux[0], hi, false);
+                add(d.aux[1], hi, false);
             }
             add(d.output, sz * H * D * eo, true);
             break;

@@ -108,7 +108,7 @@ def test_rows_full_stream_sampled_outputs():
 
 
 def test_decode_full_stream_last_step_sampled():
-    """The decode stream bench.py times (25 steps x 32 layers, caches of
+    """The decode stream bench.py times (2,000 steps x 32 layers, caches of
     [8, 32, 4096, 128] bf16 per layer, 16 GiB, drawn on the GPU), with four
     waves and two units per wave.  The last step's attention outputs are
     final (their output buffers are not written again), and so are the
@@ -116,7 +116,7 @@ def test_decode_full_stream_last_step_sampled():
     not used again): for sampled layers the oracle recomputes that step's
     SDPA from them, and the appended cache rows must equal k bit for bit."""
     import torch
-    s = W.make_decode(steps=25)
+    s = W.make_decode(steps=2000)
     recs = s.recs
     L = s.meta["layers"]
     say(f"decode full stream, {len(recs)} descriptors, 16 GiB of caches, ring 512, 4 waves, 2 units per wave")

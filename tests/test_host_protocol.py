@@ -494,3 +494,92 @@ def test_static_eager_submit_rejects_oversized_split_partials_before_launching()
     bad = G.new_descs(1)
     bad["op_id"] = G.GPUOS_OP_EXPR  # needs a table; the eager path has none
     assert G.gpuos_eager_submit_static(bad, 0) == G.GPUOS_E_INVAL
+
+
+def _precise_ranges(r):
+    """Exact byte ranges a record reads and writes, from the op definitions
+    (per-head KV-cache rows, per-row attention keys), independent of the
+    library's declared ranges: [(buf, lo, hi, write)]."""
+    op = int(r["op"])
+    es = W.DTYPE_BYTES[int(r["dtype"])]
+    n = int(r["size"])
+    d = [int(v) for v in r["dim"]]
+    buf, off = r["buf"], r["off"]
+
+    def rng(role, nbytes, rel=0):
+        b = int(buf[role])
+        return (b, int(off[role]) + rel, int(off[role]) + rel + nbytes)
+    reads = []
+    if op in (W.OP_ADD, W.OP_MUL):
+        reads = [rng(W.A, n * es), rng(W.B, n * es)]
+    elif op in (W.OP_RELU, W.OP_GELU):
+        reads = [rng(W.A, n * es)]
+    elif op in (W.OP_SUM, W.OP_MAX, W.OP_MIN, W.OP_SOFTMAX):
+        reads = [rng(W.A, n * d[0] * es)]
+    elif op == W.OP_LAYERNORM:
+        reads = [rng(W.A, n * d[0] * es), rng(W.AUX0, d[0] * es), rng(W.AUX1, d[0] * es)]
+    elif op == W.OP_ROPE:
+        reads = [(b, o, o + k) for (b, o, k) in W.output_ranges(r)]
+    elif op == W.OP_KV_APPEND:
+        reads = [rng(W.A, n * d[0] * d[1] * es), rng(W.B, n * d[0] * d[1] * es)]
+    elif op == W.OP_SDPA:
+        H, D, C = d[0], d[1], d[2]
+        hkv = d[3] or H
+        reads = [rng(W.A, n * H * D * es)]
+        for bb in range(n):
+            L = int(r["lens"][bb])
+            for h in range(hkv):
+                rel = (bb * hkv + h) * C * D * es
+                reads += [rng(W.AUX0, L * D * es, rel), rng(W.AUX1, L * D * es, rel)]
+    elif op == W.OP_GEMV:
+        reads = [rng(W.A, d[0] * es), rng(W.B, d[0] * d[1] * es)]
+    elif op == W.OP_COPY:
+        reads = [rng(W.A, n)]
+    writes = [(b, o, o + k) for (b, o, k) in W.output_ranges(r)]
+    return [(b, lo, hi, False) for (b, lo, hi) in reads] + [(b, lo, hi, True) for (b, lo, hi) in writes]
+
+
+def _check_order_precise(recs, order, first_seq, window=600):
+    """Every pair of records whose exact ranges conflict completed in order."""
+    n = len(recs)
+    idx = np.asarray(order, np.int64) - first_seq
+    assert sorted(idx.tolist()) == list(range(n)), "each descriptor completes exactly once"
+    pos = np.empty(n, np.int64)
+    pos[idx] = np.arange(n)
+    R = [np.array(_precise_ranges(r), np.int64).reshape(-1, 4) for r in recs]
+    owner = [np.full(len(x), i) for i, x in enumerate(R)]
+    violations = 0
+    for j in range(1, n):
+        lo_i = max(0, j - window)
+        A = np.concatenate(R[lo_i:j])
+        own = np.concatenate(owner[lo_i:j])
+        Bj = R[j]
+        if not len(A) or not len(Bj):
+            continue
+        c = ((A[:, None, 0] == Bj[None, :, 0]) & (A[:, None, 1] < Bj[None, :, 2]) & (Bj[None, :, 1] < A[:, None, 2])
+             & ((A[:, None, 3] | Bj[None, :, 3]) != 0)).any(axis=1)
+        earlier = np.unique(own[c])
+        violations += int((pos[earlier] > pos[j]).sum())
+    return violations
+
+
+@pytest.mark.parametrize("kind", ["decode", "decode_gqa", "mixed"])
+def test_loopback_respects_hazards_attention_streams(kind):
+    """Decode and mixed streams: the library declares the KV caches whole;
+    every pair of descriptors whose exact accesses (per-head cache rows,
+    per-row keys) conflict must still complete in submission order."""
+    if kind == "mixed":
+        s = W.make_mixed(tokens=4, layers=3, capacity=64, l0_range=(8, 40), n_tok_pool=2)
+    else:
+        s = W.make_decode(steps=30, layers=3, heads=8, kv_heads=2 if kind == "decode_gqa" else 0,
+                          capacity=64, l_min=8, n_triples=4, n_out=8)
+    descs = to_descs(s.recs, _fake_ptrs(len(s.buffers)))
+    ctx = _loopback(ring=64)
+    try:
+        first = _run(ctx, descs, np.full(len(descs) // 16 + 1, 16)[: (len(descs) + 15) // 16])
+        order = G.gpuos_loopback_order(ctx)
+    finally:
+        G.gpuos_shutdown(ctx)
+    assert _check_order_precise(s.recs, order, first) == 0
+    if kind != "mixed":  # the mixed pipeline is one dependency chain per token
+        assert not np.array_equal(order, np.arange(first, first + len(descs)))
