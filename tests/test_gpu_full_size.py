@@ -46,7 +46,7 @@ def test_elementwise_full_stream_with_gelu_verify():
     say(f"elementwise full stream with GELU, verify mode, {len(s)} descriptors, ring 512, one wave per workgroup")
     res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ring_entries=512,
                         waves_per_wg=1, units_per_wave=1)
-    say(f"  logged {res['n_logged']}; worst error / allowance {res['worst']}; plain relative {res['plain']}")
+    say(f"  logged {res['n_logged']}; worst error ratio {res['worst']}; plain relative {res['plain']}")
     assert not res["fails"], res["fails"][:3]
 
 

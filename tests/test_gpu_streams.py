@@ -94,7 +94,7 @@ from gpu_harness import verify_stream  # noqa: E402
 
 
 def _report(name, res):
-    say(f"{name}: logged {res['n_logged']} outputs; worst error / allowance per op {res['worst']}; "
+    say(f"{name}: logged {res['n_logged']} outputs; worst error ratio per op {res['worst']}; "
         f"plain relative error per op {res['plain']}")
     assert not res["fails"], res["fails"][:3]
     assert res["kv_ok"]
