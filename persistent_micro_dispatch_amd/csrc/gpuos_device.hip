@@ -117,7 +117,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
     // (with workgroups placed on the XCDs in turn) each XCD claims from
     // counters of its own
     const uint32_t S = A.shards;
-    const uint32_t shard = blockIdx.x % S;
+    const uint32_t shard = wg_shard(blockIdx.x, S);
     uint64_t* const claim_ctr = &C->claim[shard].next;
     for (;;) {
         // One dependency load per waiting slot and the queue tail, issued
@@ -272,7 +272,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             if (state[k] != SL_FREE) continue;
             uint64_t c = 0;
             if (lane == 0) c = __hip_atomic_fetch_add(claim_ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            su[k] = rl64(c, 0) * S + shard;
+            su[k] = ticket_unit(rl64(c, 0), S, shard);
             state[k] = SL_CLAIMED;
         }
         asm volatile("" ::: "memory");
@@ -281,7 +281,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
         for (uint32_t k = 0; k < SLOTS; ++k) {
             if (state[k] == SL_CLAIMED && tail > su[k]) {
                 const uint64_t ent = ld_agent(&A.queue[su[k] & A.qmask]);
-                const uint64_t seq = ent >> 24;
+                const uint64_t seq = entry_seq(ent);
                 const uint64_t slot = seq & A.mask;
                 uint64_t w = 0;
                 if (lane < 16) w = ld_agent(&((const uint64_t*)&A.mirror[slot])[lane]);
@@ -301,7 +301,7 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
                 swaited[k] = false;
                 sw[k] = w;
                 sseq[k] = seq;
-                stile[k] = (uint32_t)(ent & 0xFFFFFFu);
+                stile[k] = entry_tile(ent);
                 tclaim[k] = A.trace ? wall_clock64() : 0;
                 state[k] = SL_WAIT;
                 fresh = true;
@@ -485,7 +485,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
                 cw_units = cw < f ? A.meta[cw & mask].ubegin : u_next;
                 cw_scr = cw < f ? A.meta[cw & mask].scratch_mark : sv_next;
             }
-            const bool ok = !act || ((u_next + inc - cw_units <= Q) && (sv_end_i - cw_scr <= S));
+            const bool ok = !act || (units_fit(u_next + inc, cw_units, Q) && scratch_fits(sv_end_i, cw_scr, S));
             const uint64_t fb = __ballot(ok);
             fit = fb == ~0ull ? 64u : (uint32_t)(__ffsll((long long)~fb) - 1);
             if (fit > count) fit = count;
@@ -531,14 +531,14 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         if (lane == 0) pref[count] = T;
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
         __builtin_amdgcn_wave_barrier();
-        // one queue entry per unit: (seq << 24) | tile
+        // one queue entry per unit: its descriptor and index
         for (uint64_t wi = lane; wi < T; wi += 64u) {
             uint32_t lo = 0, hi = count;  // find j with pref[j] <= wi < pref[j+1]
             while (hi - lo > 1) {
                 const uint32_t mid = (lo + hi) >> 1;
                 if (pref[mid] <= wi) lo = mid; else hi = mid;
             }
-            wst64(&A.queue[(u_next + wi) & A.qmask], ((f + lo) << 24) | (wi - pref[lo]));
+            wst64(&A.queue[(u_next + wi) & A.qmask], queue_entry(f + lo, wi - pref[lo]));
         }
         stores_done();  // entries, mirror, meta and counters are written through
         if (lane == 0) st_agent(&C->q_tail, u_next + T);

@@ -260,18 +260,6 @@ void refresh_wm(gpuos_ctx* c) {
     }
 }
 
-// Claim shards: workgroup b claims from shard b % shards, so every shard
-// needs a worker wave (workgroup 0's first wave is the fetcher), and all
-// of them must be resident at once, or a shard could wait for a workgroup
-// that never starts.  One workgroup per compute unit at most guarantees
-// that; otherwise one shared counter is used.
-static uint32_t claim_shards(uint32_t num_wgs, uint32_t waves_per_wg, uint32_t cu_count) {
-    if (num_wgs > cu_count) return 1;
-    const uint32_t worker_wgs = waves_per_wg > 1 ? num_wgs : num_wgs - 1;
-    uint32_t s = worker_wgs < CLAIM_SHARDS_MAX ? worker_wgs : CLAIM_SHARDS_MAX;
-    return s ? s : 1;
-}
-
 int executor_launch(gpuos_ctx* c) {
     if (c->loopback || c->running) return GPUOS_OK;
     hipError_t e = hipMemsetAsync(c->dctl, 0, sizeof(DevCtl), c->exec);
@@ -685,7 +673,7 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
         if (kind < GPUOS_KIND_COUNT) {
             const Plan pl = make_plan(plan_in(kind, d, tab[d.op_id].flags));
             if (pl.status != GPUOS_ST_OK) return GPUOS_E_INVAL;
-            if (pl.ntiles > c->Q / 2 || pl.scratch > c->P.scratch_bytes / 2) return GPUOS_E_INVAL;
+            if (pl.ntiles > max_units_per_descriptor(c->Q) || pl.scratch > c->P.scratch_bytes / 2) return GPUOS_E_INVAL;
         } else {
             kind = GPUOS_KIND_EMPTY;  // the device reports BAD_OP; nothing to order
         }

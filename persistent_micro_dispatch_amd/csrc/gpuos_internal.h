@@ -79,6 +79,44 @@ struct DevCtl {
     uint64_t stat_fetched;
 };
 
+// ---------------------------------------------------------------------------
+// Executor protocol arithmetic, shared by the executor, the host runtime and
+// the host-side model of the protocol that the CPU tests drive.
+// ---------------------------------------------------------------------------
+// Claim shards: workgroup b claims from shard b % shards, so every shard
+// needs a worker wave (workgroup 0's first wave is the fetcher), and all of
+// them must be resident at once, or a shard could wait for a workgroup that
+// never starts.  One workgroup per compute unit at most guarantees that;
+// otherwise one shared counter is used.
+__host__ __device__ inline uint32_t claim_shards(uint32_t num_wgs, uint32_t waves_per_wg, uint32_t cu_count) {
+    if (num_wgs > cu_count) return 1;
+    const uint32_t worker_wgs = waves_per_wg > 1 ? num_wgs : num_wgs - 1;
+    const uint32_t s = worker_wgs < CLAIM_SHARDS_MAX ? worker_wgs : CLAIM_SHARDS_MAX;
+    return s ? s : 1;
+}
+__host__ __device__ inline uint32_t wg_shard(uint32_t block, uint32_t shards) { return block % shards; }
+// the unit (queue position) that ticket t of a shard stands for: shard x
+// owns the positions congruent to x modulo the shard count, in order
+__host__ __device__ inline uint64_t ticket_unit(uint64_t ticket, uint32_t shards, uint32_t shard) {
+    return ticket * shards + shard;
+}
+// a unit-queue entry: the descriptor's sequence number and the unit's index in it
+constexpr uint32_t QE_TILE_BITS = 24;
+static_assert((1ull << QE_TILE_BITS) >= (1ull << 22), "tile field holds MAX_TILES");
+__host__ __device__ inline uint64_t queue_entry(uint64_t seq, uint64_t tile) { return (seq << QE_TILE_BITS) | tile; }
+__host__ __device__ inline uint64_t entry_seq(uint64_t e) { return e >> QE_TILE_BITS; }
+__host__ __device__ inline uint32_t entry_tile(uint64_t e) { return (uint32_t)(e & ((1u << QE_TILE_BITS) - 1u)); }
+// the fetcher may publish units up to position u_end only while the oldest
+// incomplete descriptor's first unit (cw_units) is at most Q positions back:
+// a position is reused only after the unit that held it has run
+__host__ __device__ inline bool units_fit(uint64_t u_end, uint64_t cw_units, uint64_t Q) { return u_end - cw_units <= Q; }
+__host__ __device__ inline bool scratch_fits(uint64_t sv_end, uint64_t cw_scr, uint64_t S) { return sv_end - cw_scr <= S; }
+// gpuos_submit refuses a descriptor of more units than this (or more
+// scratch than half the scratch ring): once every earlier descriptor has
+// completed, any single descriptor then fits, so the fetcher always
+// progresses
+__host__ __device__ inline uint64_t max_units_per_descriptor(uint64_t Q) { return Q / 2; }
+
 // Kernel arguments of the executor.
 struct ExecArgs {
     const gpuos_desc* ring;   // host-mapped
