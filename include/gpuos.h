@@ -86,6 +86,7 @@ enum gpuos_kind {
 /* descriptor flags: bits 0-3 input dtype, bits 4-7 output dtype */
 #define GPUOS_FLAGS(in_dtype, out_dtype) ((uint32_t)(in_dtype) | ((uint32_t)(out_dtype) << 4))
 #define GPUOS_F_ROPE_HALF (1u << 8)  /* RoPE pairs (x_i, x_{i+D/2}) instead of (x_2i, x_2i+1) */
+#define GPUOS_F_SDPA_MASK (1u << 9)  /* SDPA adds an fp32 mask [B, C] (aux[2]) to the scaled scores */
 
 /* ------------------------------------------------------------ descriptor */
 /* One ring entry, 128 bytes (the pages give 64-128 B holding op_id,
@@ -114,6 +115,11 @@ enum gpuos_kind {
  *                   output [B, H, D] in the output dtype; keys [0, lens[b]);
  *                   param.f[4] = scale (0 -> 1/sqrt(D)).  D must be 64 or 128;
  *                   lens[b] up to 65535 (at most 64 splits of 1024 keys).
+ *                   Attention masking (the pages' operator library lists it
+ *                   with SDPA): with flag GPUOS_F_SDPA_MASK, aux[2] = an fp32
+ *                   mask [B, C] added to the scaled score of key j in row b
+ *                   (the same for every head; -inf removes the key; a row
+ *                   with every key removed gives NaN).
  *   GEMV            a = x [dim[0]=K], b = W [K, dim[1]=N] row-major, output [N].
  *   COPY            a -> output, `size` bytes.
  * Within one descriptor an output must coincide exactly with an input or

@@ -402,7 +402,9 @@ static int op_kv_append(const pool_t* P, const orc_rec* r) {
  * p = softmax(s), o = sum_j p_j V_j.  scale defaults to 1/sqrt(D).  The
  * caches hold Hkv = dim[3] (0: H) heads [B, Hkv, C, D]; query head h reads
  * key/value head h / (H / Hkv) (grouped-query attention; Hkv = 1 is
- * multi-query attention). */
+ * multi-query attention).  Attention masking (record flag 2): s_j gets
+ * mask[b, j] added, an fp32 mask [B, C] in aux2 shared by all heads; a row
+ * whose scores are all -inf is softmax over nothing and gives NaN. */
 static int op_sdpa(const pool_t* P, const orc_rec* r) {
     int64_t B = r->size, H = r->dim[0], D = r->dim[1], C = r->dim[2];
     int64_t Hkv = r->dim[3] > 0 ? r->dim[3] : H;
@@ -414,6 +416,11 @@ static int op_sdpa(const pool_t* P, const orc_rec* r) {
     const uint8_t* V = span(P, r, R_AUX1, B * Hkv * C * D * esize(dt));
     uint8_t* o = span(P, r, R_OUT, B * H * D * esize(dout));
     if (!q || !K || !V || !o) return ORC_E_BOUNDS;
+    const uint8_t* mask = NULL;
+    if (r->flags & 2) {
+        mask = span(P, r, R_AUX2, B * C * 4);
+        if (!mask) return ORC_E_BOUNDS;
+    }
     double scale = r->fparam[1] != 0.0f ? (double)r->fparam[1] : 1.0 / sqrt((double)D);
     double* s = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
     double* acc = (double*)malloc(sizeof(double) * (size_t)D);
@@ -429,6 +436,7 @@ static int op_sdpa(const pool_t* P, const orc_rec* r) {
                 double dot = 0.0;
                 for (int64_t d = 0; d < D; ++d) dot += ld(q, dt, qo + d) * ld(K, dt, kv + j * D + d);
                 s[j] = dot * scale;
+                if (mask) s[j] += ld(mask, ORC_F32, b * C + j);
                 if (s[j] > m) m = s[j];
             }
             double z = 0.0;

@@ -418,7 +418,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         pin.size = dw[5];
         pin.dim[0] = (uint32_t)dw[6]; pin.dim[1] = (uint32_t)(dw[6] >> 32);
         pin.dim[2] = (uint32_t)dw[7]; pin.dim[3] = (uint32_t)(dw[7] >> 32);
-        pin.a = dw[2]; pin.b = dw[3]; pin.out = dw[4]; pin.aux0 = dw[8]; pin.aux1 = dw[9];
+        pin.a = dw[2]; pin.b = dw[3]; pin.out = dw[4]; pin.aux0 = dw[8]; pin.aux1 = dw[9]; pin.aux2 = dw[10];
         pin.lensw[0] = dw[13];
         pin.lensw[1] = dw[14];
         uint32_t kind = KIND_BAD;

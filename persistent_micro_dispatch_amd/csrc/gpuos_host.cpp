@@ -132,6 +132,7 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
                 const uint64_t hi = (((sz - 1) * Hkv + Hkv - 1) * C + lens_at(lensw, (uint32_t)sz - 1)) * D * es;
                 add(d.aux[0], hi, false);
                 add(d.aux[1], hi, false);
+                if (d.flags & GPUOS_F_SDPA_MASK) add(d.aux[2], sz * C * 4, false);
             }
             add(d.output, sz * H * D * eo, true);
             break;
@@ -170,6 +171,7 @@ PlanIn plan_in(uint32_t kind, const gpuos_desc& d, uint32_t kflags = 0) {
     p.out = d.output;
     p.aux0 = d.aux[0];
     p.aux1 = d.aux[1];
+    p.aux2 = d.aux[2];
     return p;
 }
 

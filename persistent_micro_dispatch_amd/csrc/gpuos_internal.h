@@ -204,7 +204,7 @@ struct PlanIn {
     uint64_t size;
     uint32_t dim[4];
     uint64_t lensw[2];  // lens[0..7] as packed 16-bit fields (descriptor bytes 104..120)
-    uint64_t a, b, out, aux0, aux1;
+    uint64_t a, b, out, aux0, aux1, aux2;
 };
 
 // lens[i] from the two packed words (kept packed: a dynamically indexed
@@ -335,6 +335,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (d.dim[3] != 0 && H % d.dim[3] != 0) return bad();  // key/value heads divide the query heads
             if (di != GPUOS_BF16) return bad();
             if (d.a == 0 || d.out == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
+            if ((d.flags & GPUOS_F_SDPA_MASK) && d.aux2 == 0) return bad();
             uint64_t units = 0;
             bool split = false;
             for (uint32_t i = 0; i < B; ++i) {

@@ -178,6 +178,9 @@ __device__ __forceinline__ u32x4 rld16(RBuf b, uint32_t off) {
 __device__ __forceinline__ u32x4 rld16s(RBuf b, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(b.r, (int)off, 0, CPOL_STREAM);
 }
+__device__ __forceinline__ uint32_t rld4(RBuf b, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(b.r, (int)off, 0, CPOL_LD);
+}
 __device__ __forceinline__ void wst16(WBuf b, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, b.r, (int)off, 0, CPOL_ST);
 }
@@ -888,7 +891,13 @@ __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
 // merges them (the split softmax of flash-decoding).  Keys past L read as
 // zero through the bounded buffer window and get weight 0.  Dense MFMA does
 // not apply: one query per head makes q.K^T and P.V matrix-vector products
-// with no reuse.
+// with no reuse.  Attention masking: with GPUOS_F_SDPA_MASK an fp32 mask
+// [B, C] (aux2, per batch row and key, the same for every head) is added to
+// the scaled scores; the chunk's mask values are loaded with its keys.  A
+// key with mask -inf gets weight 0; a chunk or split whose keys are all
+// masked adds nothing (its running max stays -inf and is not subtracted
+// from itself), and a row with every key masked gives NaN, as softmax over
+// nothing does.
 template <uint32_t DV, uint32_t DTO, uint32_t GP>
 __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t D = DV * 8u;
@@ -923,6 +932,8 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     const uint32_t g = lane / DV, c = lane % DV;
     const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bkv * C + k0) * D * 2u, nk * D * 2u);
     const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bkv * C + k0) * D * 2u, nk * D * 2u);
+    const bool masked = (u.flags & GPUOS_F_SDPA_MASK) != 0u;
+    const RBuf rm = rbuf((const uint8_t*)u.aux2 + ((uint64_t)b * C + k0) * 4u, masked ? nk * 4u : 0u);
     bf16x2 qv[GP][4];
 #pragma unroll
     for (uint32_t gi = 0; gi < GP; ++gi) {
@@ -939,15 +950,19 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
         for (int e = 0; e < 8; ++e) acc[gi][e] = 0.0f;
     }
     const uint32_t nch = (nk + CK - 1) / CK;
-    auto load = [&](u32x4* kv, u32x4* vv, uint32_t ci) {
+    auto load = [&](u32x4* kv, u32x4* vv, float* mk, uint32_t ci) {
 #pragma unroll
         for (uint32_t j = 0; j < NI; ++j) {
             const uint32_t off = ((ci * CK + j * RPI + g) * D) * 2u + c * 16u;
             kv[j] = rld16s(rk, off);
             vv[j] = rld16s(rv, off);
         }
+        if (masked) {
+#pragma unroll
+            for (uint32_t j = 0; j < NI; ++j) mk[j] = __uint_as_float(rld4(rm, (ci * CK + j * RPI + g) * 4u));
+        }
     };
-    auto consume = [&](const u32x4* kv, const u32x4* vv, uint32_t ci) {
+    auto consume = [&](const u32x4* kv, const u32x4* vv, const float* mk, uint32_t ci) {
         float s[GP][NI];
         float mn[GP];
 #pragma unroll
@@ -961,6 +976,7 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
                 d = __builtin_amdgcn_fdot2_f32_bf16(qv[gi][2], as_bf2(kv[j].z), d, false);
                 d = __builtin_amdgcn_fdot2_f32_bf16(qv[gi][3], as_bf2(kv[j].w), d, false);
                 d = gred<DV>(d, OpAdd{}) * sl2;
+                if (masked) d += mk[j] * 1.4426950408889634f;  // the mask, in the log2 domain too
                 const bool valid = ci * CK + j * RPI + g < nk;
                 s[gi][j] = valid ? d : -INFINITY;
                 cm = fmaxf(cm, s[gi][j]);
@@ -972,8 +988,9 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
 #pragma unroll
                 for (uint32_t mm = DV; mm < 64; mm <<= 1) cm = fmaxf(cm, __shfl_xor(cm, mm, 64));
             }
-            mn[gi] = fmaxf(m[gi], cm);                // finite: every chunk has at least one key
-            const float alpha = exp2f(m[gi] - mn[gi]);  // 0 on the first chunk (m = -inf)
+            mn[gi] = fmaxf(m[gi], cm);  // -inf only while every key so far is masked
+            // 0 on the first chunk with a live key (m = -inf); 1 while nothing is live
+            const float alpha = mn[gi] == -INFINITY ? 1.0f : exp2f(m[gi] - mn[gi]);
             lsum[gi] *= alpha;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[gi][e] *= alpha;
@@ -985,7 +1002,7 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
             unpack<GPUOS_BF16>(vv[j], vf);
 #pragma unroll
             for (uint32_t gi = 0; gi < GP; ++gi) {
-                const float p = exp2f(s[gi][j] - mn[gi]);  // 0 for keys past L
+                const float p = s[gi][j] == -INFINITY ? 0.0f : exp2f(s[gi][j] - mn[gi]);  // 0 past L, or masked
                 lsum[gi] += p;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[gi][e] += p * vf[e];
@@ -995,15 +1012,16 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     // The scheduling barriers keep the compiler from sinking the next chunk's
     // loads below the use of the current one (it would to save registers).
     u32x4 ka[NI], va[NI], kb[NI], vb[NI];
-    load(ka, va, 0);
+    float ma[NI], mb[NI];
+    load(ka, va, ma, 0);
     for (uint32_t ci = 0; ci < nch; ci += 2) {
-        load(kb, vb, ci + 1);  // past the last chunk: outside the window, reads nothing
+        load(kb, vb, mb, ci + 1);  // past the last chunk: outside the window, reads nothing
         __builtin_amdgcn_sched_barrier(0);
-        consume(ka, va, ci);
+        consume(ka, va, ma, ci);
         if (ci + 1 < nch) {
-            load(ka, va, ci + 2);
+            load(ka, va, ma, ci + 2);
             __builtin_amdgcn_sched_barrier(0);
-            consume(kb, vb, ci + 1);
+            consume(kb, vb, mb, ci + 1);
         }
     }
     constexpr uint32_t ESO = DTO == GPUOS_F32 ? 4u : 2u;

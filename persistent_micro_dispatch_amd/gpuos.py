@@ -33,6 +33,7 @@ GPUOS_EXPR_MAX_INSTR, GPUOS_EXPR_MAX_CONSTS = 32, 16
 GPUOS_OP_USER = 64
 GPUOS_F32, GPUOS_BF16 = 0, 1
 GPUOS_F_ROPE_HALF = 1 << 8
+GPUOS_F_SDPA_MASK = 1 << 9
 GPUOS_INIT_LOOPBACK = 1
 GPUOS_INIT_TRACE = 2
 GPUOS_SUBMIT_BLOCK, GPUOS_SUBMIT_NOHAZARD, GPUOS_SUBMIT_SERIAL = 1, 2, 4

@@ -176,6 +176,9 @@ def check_outputs(r, inputs: List[np.ndarray], pairs, hp=None) -> dict:
             kb, ko = inputs[int(buf[W.AUX0])], int(off[W.AUX0])
             vb, vo = inputs[int(buf[W.AUX1])], int(off[W.AUX1])
             es = W.DTYPE_BYTES[dt]
+            mask = None
+            if int(r["flags"]) & W.FLAG_SDPA_MASK:
+                mask = _f(inputs[int(buf[W.AUX2])], int(off[W.AUX2]), size * C, W.F32).reshape(size, C)
             for bb in range(size):
                 L = int(r["lens"][bb])
                 for hk in range(Hkv):
@@ -184,7 +187,10 @@ def check_outputs(r, inputs: List[np.ndarray], pairs, hp=None) -> dict:
                     V = _f(vb, vo + row, L * D, dt).reshape(L, D)
                     hs = slice(hk * (H // Hkv), (hk + 1) * (H // Hkv))
                     s = (q[bb, hs] @ K.T) * scale
-                    p = np.exp(s - s.max(axis=1, keepdims=True))
+                    if mask is not None:
+                        s = s + mask[bb, :L]
+                    with np.errstate(invalid="ignore"):
+                        p = np.exp(s - s.max(axis=1, keepdims=True))
                     p /= p.sum(axis=1, keepdims=True)
                     denom[bb, hs] = p @ np.abs(V)
             t = TOL["sdpa"] if do == W.F32 else TOL["bf16"]

@@ -351,3 +351,40 @@ def test_rope_fewer_key_heads(ctx, dt, half):
         recs.append(rec(W.OP_ROPE, dtype=dt, size=B, dim=(H, D, 0, Hk), fparam=(10000.0,), lens=lens,
                         flags=W.FLAG_ROPE_HALF if half else 0, a=base, b=base + 1))
     _run_and_check(ctx, arrays, np.concatenate(recs))
+
+
+# ------------------------------------------------ attention masking
+def _mask(B, C, lens, kind):
+    """fp32 [B, C] additive masks: random finite values, padding (-inf on a
+    random subset), a causal-like band, and rows with every key masked."""
+    m = np.zeros((B, C), np.float32)
+    for b in range(B):
+        L = int(lens[b])
+        if kind == "random":
+            m[b] = (RNG.standard_normal(C) * 2).astype(np.float32)
+        elif kind == "padding":
+            m[b, RNG.random(C) < 0.3] = -np.inf
+            m[b, L - 1] = 0.0
+        elif kind == "band":
+            m[b, : max(0, L - 100)] = -np.inf   # only the last 100 keys
+        elif kind == "all":
+            m[b] = -np.inf if b % 2 == 0 else 0.0
+    return m.reshape(-1)
+
+
+@pytest.mark.parametrize("out_dt", [W.F32, W.BF16])
+@pytest.mark.parametrize("kind", ["random", "padding", "band", "all"])
+def test_sdpa_masked(ctx, out_dt, kind):
+    say(f"sdpa masked ({kind}) out={out_dt}")
+    recs, arrays = [], []
+    for B, H, Hkv, D, C, lens in [(2, 8, 2, 128, 600, [300, 17]), (1, 32, 8, 128, 4096, [4096]),
+                                  (3, 4, 4, 64, 700, [1, 256, 700]), (4, 8, 8, 128, 3000, [3000, 2049, 1500, 64])]:
+        q = bf16(RNG.standard_normal(B * H * D))
+        K, V = bf16(RNG.standard_normal(B * Hkv * C * D)), bf16(RNG.standard_normal(B * Hkv * C * D))
+        o = np.zeros(B * H * D, np.float32 if out_dt == W.F32 else np.uint16)
+        base = len(arrays)
+        arrays += [q, K, V, o, _mask(B, C, lens, kind)]
+        recs.append(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=out_dt, size=B, dim=(H, D, C, Hkv), lens=lens,
+                        flags=W.FLAG_SDPA_MASK, a=base, aux0=base + 1, aux1=base + 2, out=base + 3, aux2=base + 4))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))

@@ -732,3 +732,80 @@ def test_capture_of_inplace_rope_reports_both_tensors():
     assert np.allclose(hq, ref_q.reshape(-1), rtol=1e-12, atol=1e-14)
     assert np.allclose(hk, ref_k.reshape(-1), rtol=1e-12, atol=1e-14)
     assert np.array_equal(np.array([oracle.round_bf16(v) for v in hq], np.uint16), pool.arrays[0].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# decode SDPA with an additive mask [B, C] (record flag FLAG_SDPA_MASK)
+# ---------------------------------------------------------------------------
+def _sdpa_masked_case(B=3, H=4, Hkv=2, D=16, C=24, lens=(24, 9, 17), seed=5):
+    rng = np.random.default_rng(seed)
+    q = bf16(rng.standard_normal(B * H * D))
+    K = bf16(rng.standard_normal(B * Hkv * C * D))
+    V = bf16(rng.standard_normal(B * Hkv * C * D))
+    return q, K, V, list(lens), (B, H, Hkv, D, C)
+
+
+def _run_masked(q, K, V, lens, dims, mask):
+    B, H, Hkv, D, C = dims
+    o = np.zeros(B * H * D, np.float32)
+    r = rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=B, dim=(H, D, C, Hkv), lens=lens,
+            flags=W.FLAG_SDPA_MASK if mask is not None else 0, a=0, aux0=1, aux1=2, out=3,
+            **({"aux2": 4} if mask is not None else {}))
+    arrays = [q, K, V, o] + ([np.asarray(mask, np.float32)] if mask is not None else [])
+    return run(r, arrays)[3].reshape(B, H, D).astype(np.float64)
+
+
+def test_sdpa_zero_mask_equals_no_mask():
+    q, K, V, lens, dims = _sdpa_masked_case()
+    B, H, Hkv, D, C = dims
+    a = _run_masked(q, K, V, lens, dims, None)
+    b = _run_masked(q, K, V, lens, dims, np.zeros(B * C))
+    assert np.array_equal(a, b)
+
+
+def test_sdpa_minus_inf_mask_equals_attention_over_the_kept_keys():
+    q, K, V, lens, dims = _sdpa_masked_case()
+    B, H, Hkv, D, C = dims
+    rng = np.random.default_rng(8)
+    keep = rng.random((B, C)) < 0.6
+    keep[:, 0] = True  # at least one key per row
+    mask = np.where(keep, 0.0, -np.inf)
+    got = _run_masked(q, K, V, lens, dims, mask.reshape(-1))
+    qf = bf16_val(q).astype(np.float64).reshape(B, H, D)
+    Kf = bf16_val(K).astype(np.float64).reshape(B, Hkv, C, D)
+    Vf = bf16_val(V).astype(np.float64).reshape(B, Hkv, C, D)
+    for b in range(B):
+        idx = [j for j in range(lens[b]) if keep[b, j]]
+        Kk = np.repeat(Kf[b][:, idx], H // Hkv, axis=0)[None]
+        Vk = np.repeat(Vf[b][:, idx], H // Hkv, axis=0)[None]
+        ref = _sdpa_torch(qf[b][None], Kk, Vk, [len(idx)])[0]
+        assert np.allclose(got[b], ref, rtol=1e-5, atol=1e-6), b
+
+
+def test_sdpa_mask_shift_invariance_and_torch_attn_mask():
+    import torch
+    q, K, V, lens, dims = _sdpa_masked_case(seed=9)
+    B, H, Hkv, D, C = dims
+    rng = np.random.default_rng(10)
+    mask = (rng.standard_normal((B, C)) * 3).astype(np.float32)
+    got = _run_masked(q, K, V, lens, dims, mask.reshape(-1))
+    shifted = _run_masked(q, K, V, lens, dims, (mask + np.float32(4.0)).reshape(-1))
+    assert np.allclose(got, shifted, rtol=1e-5, atol=1e-6)
+    qf = torch.tensor(bf16_val(q).astype(np.float64).reshape(B, H, 1, D))
+    Kf = torch.tensor(np.repeat(bf16_val(K).astype(np.float64).reshape(B, Hkv, C, D), H // Hkv, axis=1))
+    Vf = torch.tensor(np.repeat(bf16_val(V).astype(np.float64).reshape(B, Hkv, C, D), H // Hkv, axis=1))
+    for b in range(B):
+        L = lens[b]
+        am = torch.tensor(mask[b, :L].astype(np.float64)).reshape(1, 1, 1, L)
+        ref = torch.nn.functional.scaled_dot_product_attention(qf[b:b + 1], Kf[b:b + 1, :, :L], Vf[b:b + 1, :, :L],
+                                                                attn_mask=am)[0, :, 0].numpy()
+        assert np.allclose(got[b], ref, rtol=1e-5, atol=1e-6), b
+
+
+def test_sdpa_fully_masked_row_is_nan():
+    q, K, V, lens, dims = _sdpa_masked_case()
+    B, H, Hkv, D, C = dims
+    mask = np.zeros((B, C))
+    mask[1, :] = -np.inf
+    got = _run_masked(q, K, V, lens, dims, mask.reshape(-1))
+    assert np.isnan(got[1]).all() and np.isfinite(got[0]).all() and np.isfinite(got[2]).all()

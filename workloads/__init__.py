@@ -63,6 +63,7 @@ def program_is_exact(words) -> bool:
 F32, BF16 = 0, 1
 DTYPE_BYTES = {F32: 4, BF16: 2}
 FLAG_ROPE_HALF = 1  # rotate-half pairing (x_i, x_{i+D/2}) instead of adjacent pairs
+FLAG_SDPA_MASK = 2  # SDPA adds an fp32 mask [B, C] (AUX2) to the scaled scores
 
 # Operand roles: index into buf/off.
 A, B, OUT, AUX0, AUX1, AUX2 = 0, 1, 2, 3, 4, 5

@@ -84,7 +84,8 @@ def to_descs(recs: np.ndarray, ptrs: Sequence[int]) -> np.ndarray:
 
     d["op_id"] = np.where(recs["op"] == W.OP_EXPR, recs["dim"][:, 3], recs["op"]).astype(np.uint32)
     d["flags"] = (recs["dtype"].astype(np.uint32) | (recs["out_dtype"].astype(np.uint32) << 4)
-                  | np.where(recs["flags"] & W.FLAG_ROPE_HALF, G.GPUOS_F_ROPE_HALF, 0).astype(np.uint32))
+                  | np.where(recs["flags"] & W.FLAG_ROPE_HALF, G.GPUOS_F_ROPE_HALF, 0).astype(np.uint32)
+                  | np.where(recs["flags"] & W.FLAG_SDPA_MASK, G.GPUOS_F_SDPA_MASK, 0).astype(np.uint32))
     d["input_a"] = addr(W.A)
     d["input_b"] = addr(W.B)
     d["output"] = addr(W.OUT)
