@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 3
+#define GPUOS_ABI_VERSION 4
 
 /* ---------------------------------------------------------------- errors */
 #define GPUOS_OK 0
@@ -54,8 +54,9 @@ extern "C" {
 /* -------------------------------------------------------- operator kinds */
 /* Built-in operator bodies (digest page, section 3 Q2 "Operator library").
  * At init op_id k is bound to kind k for every built-in kind except EXPR;
- * op id 15 and the op ids from GPUOS_OP_USER upward start empty and can be
- * bound with gpuos_register_op or gpuos_register_expr. */
+ * op id 15 and the op ids from GPUOS_KIND_COUNT upward start empty and can be
+ * bound with gpuos_register_op or gpuos_register_expr (user op ids are
+ * GPUOS_OP_USER and above). */
 enum gpuos_kind {
     GPUOS_OP_NOP = 0,        /* nothing; the analogue of a null kernel */
     GPUOS_OP_ADD = 1,        /* out[i] = a[i] + b[i], i < size */
@@ -73,7 +74,8 @@ enum gpuos_kind {
     GPUOS_OP_GEMV = 13,      /* y[N] = x[K] . W[K, N] (W row-major) */
     GPUOS_OP_COPY = 14,      /* byte copy of `size` bytes */
     GPUOS_OP_EXPR = 15,      /* element-wise program bound by gpuos_register_expr */
-    GPUOS_KIND_COUNT = 16,
+    GPUOS_OP_MATMUL = 16,    /* y[M, N] = x[M, K] . Wt[N, K]^T, M <= 64 (small matmul) */
+    GPUOS_KIND_COUNT = 17,
     GPUOS_KIND_EMPTY = 0xFFFFFFFFu /* register_op: unbind an op id */
 };
 #define GPUOS_MAX_OPS 256
@@ -121,6 +123,12 @@ enum gpuos_kind {
  *                   (the same for every head; -inf removes the key; a row
  *                   with every key removed gives NaN).
  *   GEMV            a = x [dim[0]=K], b = W [K, dim[1]=N] row-major, output [N].
+ *   MATMUL          a = x [size=M, dim[0]=K] row-major, b = Wt [dim[1]=N, K]
+ *                   row-major (the [out, in] weight of a linear layer),
+ *                   output y [M, N] = x . Wt^T; bf16 inputs, fp32
+ *                   accumulation on the matrix cores, output in the output
+ *                   dtype; 1 <= M <= 64, K a multiple of 32 (the pages'
+ *                   "small matmuls", too small for a BLAS call).
  *   COPY            a -> output, `size` bytes.
  * Within one descriptor an output must coincide exactly with an input or
  * not overlap it.  B must be at most 8 (lens are inline). */

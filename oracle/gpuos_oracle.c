@@ -39,6 +39,8 @@
  *  - KV append writes K[b,h,L_b-1,:] and V[b,h,L_b-1,:]; the cache is
  *    [B, H, C, D].  SDPA attends one query over keys [0, L_b).
  *  - GEMV: y[n] = sum_k x[k] W[k,n] with W row-major [K, N].
+ *  - Small matmul: y[m,n] = sum_k x[m,k] Wt[n,k], x row-major [M, K] and the
+ *    weight Wt row-major [N, K] (a linear layer's [out, in] layout).
  *  - An injected operator (the pages' run-time operator injection, digest
  *    page section 3 Q2 "Dynamic Operator Table") is an element-wise program
  *    on four binary32 registers, applied per element; its definition is the
@@ -64,7 +66,8 @@ typedef struct {
 } orc_rec;
 
 enum { ORC_NOP = 0, ORC_ADD, ORC_MUL, ORC_RELU, ORC_GELU, ORC_SUM, ORC_MAX, ORC_MIN,
-       ORC_SOFTMAX, ORC_LAYERNORM, ORC_ROPE, ORC_KV_APPEND, ORC_SDPA, ORC_GEMV, ORC_COPY, ORC_EXPR };
+       ORC_SOFTMAX, ORC_LAYERNORM, ORC_ROPE, ORC_KV_APPEND, ORC_SDPA, ORC_GEMV, ORC_COPY, ORC_EXPR,
+       ORC_MATMUL };
 enum { ORC_F32 = 0, ORC_BF16 = 1 };
 enum { R_A = 0, R_B, R_OUT, R_AUX0, R_AUX1, R_AUX2 };
 
@@ -470,6 +473,24 @@ static int op_gemv(const pool_t* P, const orc_rec* r) {
     return 0;
 }
 
+/* small matmul: y[m, n] = sum_k x[m, k] * Wt[n, k]; x [M = size, K = dim[0]],
+ * Wt [N = dim[1], K], both row-major */
+static int op_matmul(const pool_t* P, const orc_rec* r) {
+    int64_t M = r->size, K = r->dim[0], N = r->dim[1];
+    int dt = r->dtype, dout = r->out_dtype;
+    const uint8_t* x = span(P, r, R_A, M * K * esize(dt));
+    const uint8_t* Wt = span(P, r, R_B, N * K * esize(dt));
+    uint8_t* y = span(P, r, R_OUT, M * N * esize(dout));
+    if (!x || !Wt || !y) return ORC_E_BOUNDS;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += ld(x, dt, m * K + k) * ld(Wt, dt, n * K + k);
+            st(y, dout, m * N + n, acc);
+        }
+    return 0;
+}
+
 /* injected program: a, b, out of `size` elements; the program's dim[2]
  * words in aux2 (at the record's aux2 offset); no b -> b reads a */
 static int op_expr(const pool_t* P, const orc_rec* r) {
@@ -516,6 +537,7 @@ static int run_one(const pool_t* P, const orc_rec* r) {
         case ORC_GEMV: return op_gemv(P, r);
         case ORC_COPY: return op_copy(P, r);
         case ORC_EXPR: return op_expr(P, r);
+        case ORC_MATMUL: return op_matmul(P, r);
         default: return ORC_E_OP;
     }
 }

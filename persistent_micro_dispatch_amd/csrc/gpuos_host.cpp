@@ -146,6 +146,11 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
             add(d.input_a, sz, false);
             add(d.output, sz, true);
             break;
+        case GPUOS_OP_MATMUL:
+            add(d.input_a, sz * d.dim[0] * es, false);
+            add(d.input_b, (uint64_t)d.dim[1] * d.dim[0] * es, false);
+            add(d.output, sz * d.dim[1] * eo, true);
+            break;
         case GPUOS_OP_EXPR:  // b is counted as read whenever it is given
             add(d.input_a, sz * es, false);
             add(d.input_b, sz * es, false);

@@ -184,6 +184,9 @@ constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in reg
 #endif
 constexpr uint32_t SDPA_KT = GPUOS_SDPA_KT;  // keys per SDPA unit (fewer for small attention ops)
 constexpr uint32_t GEMV_KC = 128;          // rows of W per GEMV unit
+constexpr uint32_t MM_NB = 64;             // output columns per MATMUL unit (four 16-column tiles)
+constexpr uint32_t MM_KC = 256;            // k per MATMUL unit
+constexpr uint32_t MM_MAX_M = 64;          // rows of x (four 16-row tiles)
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
 constexpr uint32_t MAX_TILES = 1u << 22;   // hard cap of units per descriptor
@@ -361,6 +364,18 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (ncb * nks > MAX_TILES || ncb * 4 > COUNTER_AREA) return bad();
             p.ntiles = (uint32_t)(ncb * nks);
             if (nks > 1) p.scratch = COUNTER_AREA + nks * (uint64_t)N * 4u;
+            return p;
+        }
+        case GPUOS_OP_MATMUL: {
+            const uint64_t M = d.size;
+            const uint32_t K = d.dim[0], N = d.dim[1];
+            if (di != GPUOS_BF16 || M == 0 || M > MM_MAX_M || K == 0 || N == 0 || K % 32u != 0) return bad();
+            if (d.a == 0 || d.b == 0 || d.out == 0) return bad();
+            if ((uint64_t)MM_MAX_M * K * 2u >= (1ull << 31)) return bad();  // 32-bit buffer offsets
+            const uint64_t ncb = cdiv(N, MM_NB), nks = cdiv(K, MM_KC);
+            if (ncb * nks > MAX_TILES || ncb * 4 > COUNTER_AREA) return bad();
+            p.ntiles = (uint32_t)(ncb * nks);
+            if (nks > 1) p.scratch = COUNTER_AREA + nks * M * (uint64_t)N * 4u;
             return p;
         }
         case GPUOS_OP_EXPR: {

@@ -37,6 +37,8 @@ namespace gpuos {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 gc_u32x4;
 typedef __attribute__((address_space(1))) const uint32_t gc_u32;
 typedef __attribute__((address_space(1))) const uint16_t gc_u16;
@@ -1311,6 +1313,115 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------- MATMUL
+// y[M,N] = x[M,K] Wt[N,K]^T, the weight in the [out, in] layout of a linear
+// layer; bf16 inputs, M <= 64 (the pages' "small matmuls").  At M rows per
+// weight element the product is dense enough for the matrix cores: fp32
+// vector FMAs would cap it near 20 flop per byte of weights, while the
+// weights stream from HBM.  Unit = (block of MM_NB = 64 output columns,
+// k-split of MM_KC = 256).  Per step of 32 k the wave loads, for each
+// 16-row tile of x and each 16-column tile of Wt, one 16-byte piece of a
+// row per lane (lane l: row l % 16, k offset 8 (l / 16)), which is the
+// operand layout of v_mfma_f32_16x16x32_bf16, and issues one MFMA per
+// (row tile, column tile) pair into fp32 accumulators (lane l holds rows
+// 4 (l / 16) + i, column l % 16 of each 16x16 tile); the next step's loads
+// are issued before the current step's MFMAs.  Rows past M and columns past
+// N read zero through the bounded windows.  With several k-splits each unit
+// writes fp32 partial tiles and the last unit of a column block adds them
+// in split order.
+template <uint32_t DTO>
+__device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
+    const uint32_t M = (uint32_t)u.size, K = u.dim[0], N = u.dim[1];
+    const uint32_t ncb = (N + MM_NB - 1) / MM_NB, nks = (K + MM_KC - 1) / MM_KC;
+    const uint32_t cb = u.tile % ncb, ks = u.tile / ncb;
+    const uint32_t kb = ks * MM_KC, kn = min(K - kb, MM_KC);  // a multiple of 32
+    const uint32_t MT = (M + 15u) / 16u;                       // row tiles in use (wave-uniform)
+    const uint32_t r16 = lane % 16u, kg = lane / 16u;
+    const uint32_t ncol = min(N - cb * MM_NB, MM_NB);
+    const RBuf rx = rbuf((const uint8_t*)u.a, M * K * 2u);
+    const RBuf rw = rbuf((const uint8_t*)u.b + (uint64_t)cb * MM_NB * K * 2u, ncol * K * 2u);
+    f32x4 acc[4][4];
+#pragma unroll
+    for (uint32_t mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (uint32_t nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto load = [&](u32x4* xv, u32x4* wv, uint32_t st) {
+        const uint32_t k = kb + st * 32u + kg * 8u;
+#pragma unroll
+        for (uint32_t t = 0; t < 4; ++t) {
+            xv[t] = rld16(rx, ((t * 16u + r16) * K + k) * 2u);   // rows past M: outside the window
+            wv[t] = rld16s(rw, ((t * 16u + r16) * K + k) * 2u);  // columns past N: likewise
+        }
+    };
+    auto mma = [&](const u32x4* xv, const u32x4* wv) {
+#pragma unroll
+        for (uint32_t mt = 0; mt < 4; ++mt) {
+            if (mt >= MT) break;
+#pragma unroll
+            for (uint32_t nt = 0; nt < 4; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[mt]),
+                                                                      __builtin_bit_cast(bf16x8, wv[nt]),
+                                                                      acc[mt][nt], 0, 0, 0);
+        }
+    };
+    const uint32_t nst = kn / 32u;
+    u32x4 xa[4], wa[4], xb[4], wb[4];
+    load(xa, wa, 0);
+    for (uint32_t st = 0; st < nst; st += 2) {
+        if (st + 1 < nst) load(xb, wb, st + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch above the use
+        mma(xa, wa);
+        if (st + 1 < nst) {
+            if (st + 2 < nst) load(xa, wa, st + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(xb, wb);
+        }
+    }
+    uint8_t* Y = (uint8_t*)u.out;
+    float* part = (float*)(u.scratch + COUNTER_AREA);
+#pragma unroll
+    for (uint32_t mt = 0; mt < 4; ++mt) {
+        if (mt >= MT) break;
+#pragma unroll
+        for (uint32_t nt = 0; nt < 4; ++nt) {
+            const uint32_t n = cb * MM_NB + nt * 16u + r16;
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) {
+                const uint32_t m = mt * 16u + kg * 4u + i;
+                if (m < M && n < N) {
+                    if (nks == 1) st_elem<DTO>(Y, (uint64_t)m * N + n, acc[mt][nt][i]);
+                    else wstf(part + ((uint64_t)ks * M + m) * N + n, acc[mt][nt][i]);
+                }
+            }
+        }
+    }
+    if (nks == 1) return;
+    uint32_t* ctr = (uint32_t*)u.scratch + cb;
+    uint32_t prev = 0;
+    stores_done();  // this unit's partial tiles are published before they are counted
+    if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
+    if (prev != nks - 1) return;
+    // merge: lane c owns column cb * MM_NB + c and adds its M rows over the
+    // splits in split order, 16 splits' loads in flight at a time
+    const uint32_t col = cb * MM_NB + lane;
+    constexpr uint32_t MAXS = 16;
+    for (uint32_t m = 0; m < M; ++m) {
+        float sm = 0.0f;
+        for (uint32_t k0 = 0; k0 < nks; k0 += MAXS) {
+            float pv[MAXS];
+#pragma unroll
+            for (uint32_t k = 0; k < MAXS; ++k)
+                pv[k] = k0 + k < nks && col < N ? __uint_as_float(ld4((const uint8_t*)(part + ((uint64_t)(k0 + k) * M + m) * N + col))) : 0.0f;
+#pragma unroll
+            for (uint32_t k = 0; k < MAXS; ++k)
+                if (k0 + k < nks) sm += pv[k];
+        }
+        if (col < N) st_elem<DTO>(Y, (uint64_t)m * N + col, sm);
+    }
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ COPY
 // COPY_TILE_BYTES per unit: 32 chunks of 16 bytes per lane, all loads first.
 __device__ __forceinline__ void copy_tile(const Unit& u, uint32_t lane) {
@@ -1388,6 +1499,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, uint32_t lane) {
             else dout == GPUOS_F32 ? gemv_tile<GPUOS_F32, GPUOS_F32>(u, lane) : gemv_tile<GPUOS_F32, GPUOS_BF16>(u, lane);
             break;
         case GPUOS_OP_COPY: copy_tile(u, lane); break;
+        case GPUOS_OP_MATMUL: dout == GPUOS_F32 ? matmul_tile<GPUOS_F32>(u, lane) : matmul_tile<GPUOS_BF16>(u, lane); break;
         default: break;
     }
 }

@@ -22,8 +22,8 @@ GPUOS_E_TIMEOUT, GPUOS_E_DEVICE, GPUOS_E_HIP, GPUOS_E_STATE = -4, -5, -6, -7
 GPUOS_ST_OK, GPUOS_ST_BAD_OP, GPUOS_ST_BAD_SHAPE, GPUOS_ST_SPIN = 0, 1, 2, 3
 (GPUOS_OP_NOP, GPUOS_OP_ADD, GPUOS_OP_MUL, GPUOS_OP_RELU, GPUOS_OP_GELU, GPUOS_OP_SUM, GPUOS_OP_MAX,
  GPUOS_OP_MIN, GPUOS_OP_SOFTMAX, GPUOS_OP_LAYERNORM, GPUOS_OP_ROPE, GPUOS_OP_KV_APPEND, GPUOS_OP_SDPA,
- GPUOS_OP_GEMV, GPUOS_OP_COPY, GPUOS_OP_EXPR) = range(16)
-GPUOS_KIND_COUNT = 16
+ GPUOS_OP_GEMV, GPUOS_OP_COPY, GPUOS_OP_EXPR, GPUOS_OP_MATMUL) = range(17)
+GPUOS_KIND_COUNT = 17
 GPUOS_KIND_EMPTY = 0xFFFFFFFF
 GPUOS_MAX_OPS = 256
 (GPUOS_X_LDA, GPUOS_X_LDB, GPUOS_X_CONST, GPUOS_X_MOV, GPUOS_X_ADD, GPUOS_X_SUB, GPUOS_X_MUL, GPUOS_X_DIV,

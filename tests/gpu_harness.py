@@ -195,6 +195,13 @@ def check_outputs(r, inputs: List[np.ndarray], pairs, hp=None) -> dict:
                     denom[bb, hs] = p @ np.abs(V)
             t = TOL["sdpa"] if do == W.F32 else TOL["bf16"]
             ok, worst = rel_check(gf, rf, denom.reshape(-1), t)
+        elif op == W.OP_MATMUL:
+            M_, K_, N_ = size, d[0], d[1]
+            x = _f(inputs[int(buf[W.A])], int(off[W.A]), M_ * K_, dt).reshape(M_, K_)
+            Wt = _f(inputs[int(buf[W.B])], int(off[W.B]), N_ * K_, dt).reshape(N_, K_)
+            denom = (np.abs(x) @ np.abs(Wt).T).reshape(-1)
+            t = TOL["f32"] if do == W.F32 else TOL["bf16"]
+            ok, worst = rel_check(gf, rf, denom, t)
         elif op == W.OP_GEMV:
             K_, N_ = d[0], d[1]
             x = _f(inputs[int(buf[W.A])], int(off[W.A]), K_, dt)

@@ -11,6 +11,7 @@ toleranced op uses the denominator its arithmetic fixes:
   sum        |g-r| <= tol * sum|x_i|         (summation condition number)
   SDPA       |g_d-r_d| <= tol * sum_j p_j |V_jd|
   GEMV       |g_n-r_n| <= tol * sum_k |x_k W_kn|
+  matmul     |g_mn-r_mn| <= tol * sum_k |x_mk Wt_nk|
   RoPE       within one bf16 ulp of the exact double result
 Toleranced outputs are compared with the oracle's unrounded double (the
 value it would round to the output type), so a bf16 output carries its own

@@ -388,3 +388,21 @@ def test_sdpa_masked(ctx, out_dt, kind):
                         flags=W.FLAG_SDPA_MASK, a=base, aux0=base + 1, aux1=base + 2, out=base + 3, aux2=base + 4))
     res = _run_and_check(ctx, arrays, np.concatenate(recs))
     say("  worst", max(r["worst"] for r in res))
+
+
+# ------------------------------------------------ small matmul (matrix cores)
+@pytest.mark.parametrize("out_dt", [W.F32, W.BF16])
+def test_matmul(ctx, out_dt):
+    say(f"matmul out={out_dt}")
+    recs, arrays = [], []
+    for M, K, N in [(1, 1024, 3072), (16, 1024, 3072), (33, 3072, 1024), (64, 256, 100), (7, 32, 17),
+                    (64, 4096, 64), (2, 1056, 300), (48, 512, 1000)]:
+        x = bf16(RNG.standard_normal(M * K))
+        wt = bf16(0.05 * RNG.standard_normal(N * K))
+        y = np.zeros(M * N, np.float32 if out_dt == W.F32 else np.uint16)
+        base = len(arrays)
+        arrays += [x, wt, y]
+        recs.append(rec(W.OP_MATMUL, dtype=W.BF16, out_dtype=out_dt, size=M, dim=(K, N), a=base, b=base + 1,
+                        out=base + 2))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res), "plain", max(r["plain"] for r in res))

@@ -809,3 +809,55 @@ def test_sdpa_fully_masked_row_is_nan():
     mask[1, :] = -np.inf
     got = _run_masked(q, K, V, lens, dims, mask.reshape(-1))
     assert np.isnan(got[1]).all() and np.isfinite(got[0]).all() and np.isfinite(got[2]).all()
+
+
+# ---------------------------------------------------------------------------
+# small matmul: y[M, N] = x[M, K] . Wt[N, K]^T (weight in [out, in] layout)
+# ---------------------------------------------------------------------------
+def _matmul(x, wt, M, K, N, dt=W.BF16, out_dt=W.F32):
+    y = np.zeros(M * N, np.float32 if out_dt == W.F32 else np.uint16)
+    r = rec(W.OP_MATMUL, dtype=dt, out_dtype=out_dt, size=M, dim=(K, N), a=0, b=1, out=2)
+    return run(r, [x, wt, y])[2]
+
+
+def test_matmul_exact_on_small_integers_and_against_numpy():
+    rng = np.random.default_rng(21)
+    M, K, N = 5, 64, 7
+    xi = rng.integers(-8, 9, M * K).astype(np.float32)
+    wi = rng.integers(-8, 9, N * K).astype(np.float32)
+    got = _matmul(bf16(xi), bf16(wi), M, K, N)
+    ref = xi.reshape(M, K).astype(np.float64) @ wi.reshape(N, K).astype(np.float64).T
+    assert np.array_equal(got.reshape(M, N), ref.astype(np.float32))  # exact: integers below 2^24
+    xf, wf = bf16(rng.standard_normal(M * K)), bf16(rng.standard_normal(N * K))
+    got = _matmul(xf, wf, M, K, N).reshape(M, N).astype(np.float64)
+    ref = bf16_val(xf).astype(np.float64).reshape(M, K) @ bf16_val(wf).astype(np.float64).reshape(N, K).T
+    assert np.allclose(got, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_matmul_weight_layout_is_transposed_and_m1_equals_gemv():
+    """The weight is read as Wt[n, k] (not W[k, n]): with a non-square weight
+    the transposed reading would differ; one row equals the vector-matrix
+    product with W = Wt^T laid out [K, N]."""
+    rng = np.random.default_rng(22)
+    K, N = 32, 12
+    x = bf16(rng.standard_normal(K))
+    wt = bf16(rng.standard_normal(N * K))
+    y = _matmul(x, wt, 1, K, N)
+    w_kn = bf16_val(wt).reshape(N, K).T.copy()  # [K, N]
+    g = np.zeros(N, np.float32)
+    r = rec(W.OP_GEMV, dtype=W.BF16, out_dtype=W.F32, dim=(K, N), a=0, b=1, out=2)
+    gemv = run(r, [x, W.to_bf16_bits(w_kn.astype(np.float32)).reshape(-1), g])[2]
+    assert np.array_equal(y, gemv)
+    wrong = bf16_val(x).astype(np.float64) @ bf16_val(wt).astype(np.float64).reshape(K, N)
+    assert not np.allclose(y, wrong, rtol=1e-3)
+
+
+def test_matmul_bf16_output_rounds_once():
+    rng = np.random.default_rng(23)
+    M, K, N = 3, 96, 10
+    x, wt = bf16(rng.standard_normal(M * K)), bf16(rng.standard_normal(N * K))
+    y32 = _matmul(x, wt, M, K, N, out_dt=W.F32)
+    y16 = _matmul(x, wt, M, K, N, out_dt=W.BF16)
+    exact = bf16_val(x).astype(np.float64).reshape(M, K) @ bf16_val(wt).astype(np.float64).reshape(N, K).T
+    assert np.array_equal(y16, np.array([oracle.round_bf16(v) for v in exact.reshape(-1)], np.uint16))
+    assert np.allclose(y32.reshape(M, N), exact, rtol=1e-6)

@@ -30,11 +30,12 @@ OP_NOP, OP_ADD, OP_MUL, OP_RELU, OP_GELU = 0, 1, 2, 3, 4
 OP_SUM, OP_MAX, OP_MIN, OP_SOFTMAX, OP_LAYERNORM = 5, 6, 7, 8, 9
 OP_ROPE, OP_KV_APPEND, OP_SDPA, OP_GEMV, OP_COPY = 10, 11, 12, 13, 14
 OP_EXPR = 15  # injected element-wise program (program words in AUX2, dim[2] words, op id in dim[3])
+OP_MATMUL = 16  # small matmul: y[M = size, N = dim[1]] = x[M, K = dim[0]] . Wt[N, K]^T
 OP_NAMES = {
     OP_NOP: "nop", OP_ADD: "add", OP_MUL: "mul", OP_RELU: "relu", OP_GELU: "gelu",
     OP_SUM: "sum", OP_MAX: "max", OP_MIN: "min", OP_SOFTMAX: "softmax",
     OP_LAYERNORM: "layernorm", OP_ROPE: "rope", OP_KV_APPEND: "kv_append",
-    OP_SDPA: "sdpa", OP_GEMV: "gemv", OP_COPY: "copy", OP_EXPR: "expr",
+    OP_SDPA: "sdpa", OP_GEMV: "gemv", OP_COPY: "copy", OP_EXPR: "expr", OP_MATMUL: "matmul",
 }
 
 # Injected element-wise programs: instruction codes and encoding (the word
@@ -552,6 +553,8 @@ def output_ranges(r) -> list:
         return [(int(buf[OUT]), int(off[OUT]), size * d[0] * d[1] * eo)]
     if op == OP_GEMV:
         return [(int(buf[OUT]), int(off[OUT]), d[1] * eo)]
+    if op == OP_MATMUL:
+        return [(int(buf[OUT]), int(off[OUT]), size * d[1] * eo)]
     if op == OP_COPY:
         return [(int(buf[OUT]), int(off[OUT]), size)]
     return []
@@ -594,4 +597,6 @@ def algorithmic_bytes(recs: np.ndarray) -> np.ndarray:
     out[m] = es[m] * d0[m] + es[m] * d0[m] * d1[m] + eo[m] * d1[m]
     m = op == OP_COPY
     out[m] = 2 * n[m]
+    m = op == OP_MATMUL
+    out[m] = es[m] * n[m] * d0[m] + es[m] * d1[m] * d0[m] + eo[m] * n[m] * d1[m]
     return out
