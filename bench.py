@@ -202,6 +202,11 @@ def make_stream(name):
         desc = ("attention decoding with grouped-query attention: 2,000 decode steps x 32 layers x {RoPE(theta 1e4), "
                 "KV append, SDPA}; B in {1,2,4,8}, 32 query heads sharing 8 key/value heads x 128, bf16 KV cache "
                 "4096/sequence, L in [128, 4096] +1 per step")
+    elif name == "matmul":
+        s, fill = W.make_matmul(), "device"
+        desc = ("small matmuls of batched decoding on the matrix cores: 32 tokens through the QKV (1024->3072), "
+                "up (1024->3072) and down (3072->1024) projections of 32 layers, bf16, weights [out, in] N(0,0.02) "
+                "(604 MB), 20 passes (1,920 independent descriptors)")
     elif name == "mixed":
         s, fill = W.make_mixed(tokens=500), "device"
         desc = ("mixed decode pipeline: 500 tokens x 32 layers x 11 ops at hidden 1024, 8 heads x 128, bf16: "
@@ -212,12 +217,12 @@ def make_stream(name):
     return s, desc, fill
 
 
-WAVES_DEFAULT = {"rows": 4, "decode": 4, "decode_gqa": 4, "copy": 4, "copy64": 4}
+WAVES_DEFAULT = {"rows": 4, "decode": 4, "decode_gqa": 4, "copy": 4, "copy64": 4, "matmul": 4}
 UPW_DEFAULT = {"decode": 2, "decode_gqa": 2, "rows": 2}
 # the workloads reported beside the headline in a default run, with the
 # steps each times (the decode and mixed streams run about 1-2 s per step)
-SUB_WORKLOADS = ("pr1", "rows", "decode", "decode_gqa", "mixed")
-SUB_STEPS = {"pr1": 20, "rows": 10, "decode": 2, "decode_gqa": 3, "mixed": 3}
+SUB_WORKLOADS = ("pr1", "rows", "decode", "decode_gqa", "mixed", "matmul")
+SUB_STEPS = {"pr1": 20, "rows": 10, "decode": 2, "decode_gqa": 3, "mixed": 3, "matmul": 10}
 
 
 def host_cpu():
@@ -556,6 +561,12 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
             "traffic_bytes_per_launch": tb,
             "kernel": "gpuos_executor_s2" if units_per_wave == 2 else "gpuos_executor",
             "launch_ms": mean_launch_ms, "bytes_per_launch": step_bytes}
+    if name == "matmul":
+        # the matrix cores' own roofline beside the HBM one: the products are
+        # bf16 at M = 32 rows per weight element (32 flop per byte of weights)
+        tflops = stream.meta["flops"] / (mean_launch_ms * 1e-3) / 1e12
+        extra["roofline_mfma"] = {"bound": "mfma", "achieved": tflops, "peak": 2500.0, "unit": "TFLOP/s",
+                                  "frac": tflops / 2500.0, "flops_per_launch": stream.meta["flops"]}
     levels = dag_levels(recs) if name in ("elementwise", "pr1") else None
     cpu = cpu_oracle(stream, recs, arrays, fill, cpu_budget_s) if cpu_budget_s > 0 else None
 

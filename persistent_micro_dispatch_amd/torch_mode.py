@@ -15,9 +15,13 @@ run as usual.
 Here:
   1. the aten ops with an executor body: add/mul (same shape and dtype,
      alpha 1, also in place), relu, gelu(tanh), softmax and sum/amax/amin
-     over the last dimension, and contiguous same-size copy_ (cache
-     updates); fp32 or bf16, contiguous, on the context's device;
-  2. at most `max_elems` elements per operand;
+     over the last dimension, contiguous same-size copy_ (cache updates),
+     and small bf16 matmuls x[M, K] @ W^T with M <= 64 (mm with the weight
+     given as the transpose of a contiguous [N, K] tensor, which is what a
+     linear layer without bias calls); fp32 or bf16, contiguous, on the
+     context's device;
+  2. at most `max_elems` elements per operand (for a matmul, of the
+     activation: the weights of a small matmul are read once either way);
   3. an op is routed once its (op, shapes, dtype) key has been seen
      `hot_after` times inside the mode (a recurring inner-loop op), so
      one-off calls stay on the normal path;
@@ -168,6 +172,20 @@ class RoutingFilter:
             if h == 0:
                 return Decision(False, "empty rows")
             return Decision(True, "softmax", G.GPUOS_OP_SOFTMAX, (a,), None, tuple(a.shape), a.dtype, a.numel() // h, h)
+        if func is aten.mm.default:
+            a, b = args[0], args[1]
+            why = self._tensor_ok(a)
+            if why:
+                return Decision(False, why)
+            if not isinstance(b, torch.Tensor) or b.device != a.device or b.dtype != a.dtype:
+                return Decision(False, "mixed operands")
+            if a.dtype != torch.bfloat16 or a.dim() != 2 or b.dim() != 2 or not b.t().is_contiguous():
+                return Decision(False, "matmul form")
+            M, K = a.shape
+            N = b.shape[1]
+            if M == 0 or M > 64 or K == 0 or K % 32 != 0 or N == 0 or b.shape[0] != K:
+                return Decision(False, "matmul size")
+            return Decision(True, "small matmul", G.GPUOS_OP_MATMUL, (a, b), None, (M, N), a.dtype, M, K)
         if func is aten.copy_.default:
             dst, src = args[0], args[1]
             for t in (dst, src):
@@ -287,6 +305,11 @@ class GpuosMode(TorchDispatchMode):
         desc["output"] = out.data_ptr()
         if d.kind == G.GPUOS_OP_COPY:
             desc["size"] = out.numel() * out.element_size()
+        elif d.kind == G.GPUOS_OP_MATMUL:
+            # b is the transposed view of the [N, K] weight: its storage is Wt
+            desc["size"] = d.rows
+            desc["dim"][0, 0] = d.h
+            desc["dim"][0, 1] = d.out_shape[1]
         elif d.rows:
             desc["size"] = d.rows
             desc["dim"][0, 0] = d.h

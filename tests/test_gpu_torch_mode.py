@@ -110,3 +110,25 @@ def test_hybrid_loop_matches_plain_pytorch():
         assert torch.allclose(p2, p, rtol=1e-4, atol=1e-8), it
         assert torch.allclose(q2, q, rtol=1e-4, atol=1e-6), it
         assert torch.allclose(mx2, mx, rtol=1e-4, atol=1e-8), it
+
+
+def test_linear_layers_route_to_the_matrix_cores():
+    """F.linear without bias on bf16 activations of up to 64 rows runs as the
+    executor's small matmul; results agree with torch's own bf16 matmul."""
+    import torch
+    import torch.nn.functional as F
+    from persistent_micro_dispatch_amd.torch_mode import GpuosMode, RoutingFilter
+
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    xs = [torch.randn(m, 1024, generator=gen).to(torch.bfloat16).cuda() for m in (1, 16, 64)]
+    w = (torch.randn(3072, 1024, generator=gen) * 0.02).to(torch.bfloat16).cuda()
+    ref = [F.linear(x, w).float().cpu() for x in xs]
+    torch.cuda.current_stream().synchronize()
+    with GpuosMode(filter=RoutingFilter(hot_after=1)) as m:
+        got = [F.linear(x, w) for x in xs]
+        got = [g.float().cpu() for g in got]
+    say(f"routed {dict(m.stats.routed)}, normal {dict(m.stats.fallback)}")
+    assert m.stats.routed["small matmul"] == 3
+    for g, r in zip(got, ref):
+        # two bf16 roundings of the same fp32-accumulated sums
+        assert torch.allclose(g, r, rtol=2 ** -7, atol=2e-3)

@@ -28,7 +28,8 @@ def test_filter_operation_type_size_and_context():
     assert flt.decide(aten.add.Tensor, (_f(8, 64), _f(8, 64)), {}).reason == "cold"
     flt.hot_after = 1
     # dimension 1: operation type and the forms its body takes
-    assert flt.decide(aten.mm.default, (a, b.t()), {}).reason == "op type"
+    assert flt.decide(aten.mm.default, (a, b.t()), {}).reason == "matmul form"  # fp32: not a bf16 matmul
+    assert flt.decide(aten.bmm.default, (a[None], b.t()[None]), {}).reason == "op type"
     assert flt.decide(aten.add.Tensor, (a, b), {"alpha": 2}).reason == "op form"
     assert flt.decide(aten.add.Tensor, (a, _f(1, 64)), {}).reason == "broadcast"
     assert flt.decide(aten.add.Tensor, (a, 2.0), {}).reason == "not a tensor"
@@ -116,3 +117,16 @@ def test_routed_and_normal_ops_are_ordered_by_storage(monkeypatch):
     assert lib.syncs == 2              # the exit waits for everything in flight
     assert m.stats.routed == {"elementwise": 2, "softmax": 1, "reduction": 1}
     assert w.shape == (3,) and s.shape == (4,)
+
+
+def test_filter_routes_small_bf16_matmuls_in_linear_layout():
+    flt = TM.RoutingFilter(hot_after=1, device_type="cpu")
+    x = _f(16, 256, dtype=torch.bfloat16)
+    w = _f(512, 256, dtype=torch.bfloat16)          # [out, in]
+    d = flt.decide(aten.mm.default, (x, w.t()), {})
+    assert d.route and d.kind == G.GPUOS_OP_MATMUL and (d.rows, d.h, d.out_shape) == (16, 256, (16, 512))
+    assert flt.decide(aten.mm.default, (x, w.t().contiguous()), {}).reason == "matmul form"
+    assert flt.decide(aten.mm.default, (x.float(), w.t().float()), {}).reason == "matmul form"
+    assert flt.decide(aten.mm.default, (_f(65, 256, dtype=torch.bfloat16), w.t()), {}).reason == "matmul size"
+    assert flt.decide(aten.mm.default, (_f(16, 100, dtype=torch.bfloat16),
+                                        _f(512, 100, dtype=torch.bfloat16).t()), {}).reason == "matmul size"

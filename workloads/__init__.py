@@ -517,6 +517,45 @@ def make_mixed(seed: int = 5, tokens: int = 500, layers: int = 32, hidden: int =
                   {"seed": seed, "layers": layers, "x": x, "ops_per_token": per_tok})
 
 
+def make_matmul(seed: int = 6, passes: int = 20, layers: int = 32, rows: int = 32, hidden: int = 1024,
+                ffn: int = 3072) -> Stream:
+    """Small matmuls of batched decoding: `rows` tokens through the QKV
+    (hidden -> 3 hidden), up (hidden -> ffn) and down (ffn -> hidden)
+    projections of `layers` layers, bf16, weights N(0, 0.02) in the [out, in]
+    layout (604 MB at the defaults, more than the 256 MB last-level cache),
+    `passes` times.  Every projection reads the same token activations and
+    writes its own output, so the descriptors are independent and the
+    stream measures the operator's own rate."""
+    Hd, F = hidden, ffn
+    bufs: List[Buffer] = []
+
+    def add(name, dtype, n, init, key):
+        bufs.append(Buffer(name, dtype, n, init, _buffer_seed(seed, key)))
+        return len(bufs) - 1
+    xh = add("x_hidden", BF16, rows * Hd, ("normal", 1.0), 1)
+    xf = add("x_ffn", BF16, rows * F, ("normal", 1.0), 2)
+    shapes = (("qkv", Hd, 3 * Hd, xh), ("up", Hd, F, xh), ("down", F, Hd, xf))
+    wts, outs = [], []
+    for l in range(layers):
+        for j, (nm, K, N, x) in enumerate(shapes):
+            wts.append((add(f"w{nm}{l}", BF16, N * K, ("normal", 0.02), 100 * l + 10 + j), K, N, x))
+            outs.append(add(f"y{nm}{l}", BF16, rows * N, ("zeros",), 100 * l + 20 + j))
+    recs = _new_recs(passes * len(wts))
+    i = 0
+    for _ in range(passes):
+        for (w, K, N, x), y in zip(wts, outs):
+            r = recs[i]
+            r["op"] = OP_MATMUL
+            r["dtype"] = r["out_dtype"] = BF16
+            r["size"] = rows
+            r["dim"][:2] = (K, N)
+            r["buf"][A], r["buf"][B], r["buf"][OUT] = x, w, y
+            i += 1
+    per_pass = len(wts)
+    return Stream("matmul", bufs, recs, np.full(passes, per_pass),
+                  {"seed": seed, "rows": rows, "layers": layers, "flops": 2 * rows * sum(K * N for (_, K, N, _) in wts) * passes})
+
+
 # ---------------------------------------------------------------------------
 # Byte ranges each record touches: used by tests and by harnesses that need
 # to know which buffer bytes a descriptor writes.  These are the operands'
