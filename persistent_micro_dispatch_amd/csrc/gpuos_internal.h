@@ -185,7 +185,7 @@ constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in reg
 constexpr uint32_t SDPA_KT = GPUOS_SDPA_KT;  // keys per SDPA unit (fewer for small attention ops)
 constexpr uint32_t GEMV_KC = 128;          // rows of W per GEMV unit
 constexpr uint32_t MM_NB = 64;             // output columns per MATMUL unit (four 16-column tiles)
-constexpr uint32_t MM_KC = 256;            // k per MATMUL unit
+constexpr uint32_t MM_KC = 1024;           // k per MATMUL unit
 constexpr uint32_t MM_MAX_M = 64;          // rows of x (four 16-row tiles)
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
 constexpr uint64_t COUNTER_AREA = 4096;    // bytes of per-descriptor group counters
@@ -374,6 +374,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if ((uint64_t)MM_MAX_M * K * 2u >= (1ull << 31)) return bad();  // 32-bit buffer offsets
             const uint64_t ncb = cdiv(N, MM_NB), nks = cdiv(K, MM_KC);
             if (ncb * nks > MAX_TILES || ncb * 4 > COUNTER_AREA) return bad();
+            if (nks > 1 && nks * M * (uint64_t)N * 4u >= (1ull << 31)) return bad();  // partials in one window
             p.ntiles = (uint32_t)(ncb * nks);
             if (nks > 1) p.scratch = COUNTER_AREA + nks * M * (uint64_t)N * 4u;
             return p;

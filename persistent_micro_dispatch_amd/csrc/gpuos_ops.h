@@ -1319,7 +1319,7 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
 // weight element the product is dense enough for the matrix cores: fp32
 // vector FMAs would cap it near 20 flop per byte of weights, while the
 // weights stream from HBM.  Unit = (block of MM_NB = 64 output columns,
-// k-split of MM_KC = 256).  Per step of 32 k the wave loads, for each
+// k-split of MM_KC = 1024).  Per step of 32 k the wave loads, for each
 // 16-row tile of x and each 16-column tile of Wt, one 16-byte piece of a
 // row per lane (lane l: row l % 16, k offset 8 (l / 16)), which is the
 // operand layout of v_mfma_f32_16x16x32_bf16, and issues one MFMA per
@@ -1403,21 +1403,36 @@ __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != nks - 1) return;
     // merge: lane c owns column cb * MM_NB + c and adds its M rows over the
-    // splits in split order, 16 splits' loads in flight at a time
+    // splits in split order; the loads of 8 rows x 8 splits are in flight at
+    // once (the row loop does not wait for one row's loads before the next)
     const uint32_t col = cb * MM_NB + lane;
-    constexpr uint32_t MAXS = 16;
-    for (uint32_t m = 0; m < M; ++m) {
-        float sm = 0.0f;
-        for (uint32_t k0 = 0; k0 < nks; k0 += MAXS) {
-            float pv[MAXS];
+    constexpr uint32_t MR = 8, MS = 8;
+    const RBuf rp = rbuf(part, (uint32_t)((uint64_t)nks * M * N * 4u));
+    for (uint32_t m0 = 0; m0 < M; m0 += MR) {
+        float sm[MR];
 #pragma unroll
-            for (uint32_t k = 0; k < MAXS; ++k)
-                pv[k] = k0 + k < nks && col < N ? __uint_as_float(ld4((const uint8_t*)(part + ((uint64_t)(k0 + k) * M + m) * N + col))) : 0.0f;
+        for (uint32_t i = 0; i < MR; ++i) sm[i] = 0.0f;
+        for (uint32_t k0 = 0; k0 < nks; k0 += MS) {
+            float pv[MR][MS];
 #pragma unroll
-            for (uint32_t k = 0; k < MAXS; ++k)
-                if (k0 + k < nks) sm += pv[k];
+            for (uint32_t i = 0; i < MR; ++i)
+#pragma unroll
+                for (uint32_t k = 0; k < MS; ++k) {
+                    // splits past nks, rows past M and columns past N are
+                    // sent outside the window (reads zero, never added)
+                    const bool in = k0 + k < nks && m0 + i < M && col < N;
+                    pv[i][k] = __uint_as_float(rld4(rp, in ? (uint32_t)((((uint64_t)(k0 + k) * M + m0 + i) * N + col) * 4u)
+                                                          : 0xFFFFFFF0u));
+                }
+#pragma unroll
+            for (uint32_t i = 0; i < MR; ++i)
+#pragma unroll
+                for (uint32_t k = 0; k < MS; ++k)
+                    if (k0 + k < nks) sm[i] += pv[i][k];
         }
-        if (col < N) st_elem<DTO>(Y, (uint64_t)m * N + col, sm);
+#pragma unroll
+        for (uint32_t i = 0; i < MR; ++i)
+            if (m0 + i < M && col < N) st_elem<DTO>(Y, (uint64_t)(m0 + i) * N + col, sm[i]);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
