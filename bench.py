@@ -656,6 +656,23 @@ def main():
     hbm_probe = {"bytes": pb,
                  "read_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 0, 5, sp0),
                  "copy_gbs": G.gpuos_hbm_probe(p_src.data_ptr(), p_dst.data_ptr(), pb, 1, 5, sp0)}
+    # bandwidth against the number of active CUs: one workgroup (four waves,
+    # 64 KiB of loads in flight) per CU; by Little's law the latency is
+    # in-flight bytes / bandwidth while few CUs are active, and the bytes in
+    # flight per CU that half of the peak needs follow from it
+    sweep = []
+    sb = 256 << 20
+    for wg in (8, 16, 32, 64, 128, 256):
+        sweep.append({"workgroups": wg,
+                      "read_gbs": G.gpuos_hbm_probe_grid(p_src.data_ptr(), p_dst.data_ptr(), sb, 0, 3, wg, sp0),
+                      "copy_gbs": G.gpuos_hbm_probe_grid(p_src.data_ptr(), p_dst.data_ptr(), sb, 1, 3, wg, sp0)})
+    inflight_wg = 256 * 16 * 16
+    lat_s = sweep[0]["workgroups"] * inflight_wg / (sweep[0]["read_gbs"] * 1e9)
+    half = next((p["workgroups"] for p in sweep if p["read_gbs"] >= HBM_PEAK_GBS / 2), None)
+    hbm_probe.update({"sweep_bytes": sb, "sweep": sweep, "inflight_bytes_per_workgroup": inflight_wg,
+                      "latency_us_little": lat_s * 1e6,
+                      "inflight_bytes_per_cu_for_half_peak": HBM_PEAK_GBS / 2 * 1e9 * lat_s / 256,
+                      "cus_reaching_half_peak": half})
     del p_src, p_dst
     torch.cuda.current_stream().synchronize()
     torch.cuda.empty_cache()

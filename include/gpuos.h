@@ -437,6 +437,17 @@ int gpuos_latency_bench(void* ctx, const gpuos_desc* descs, uint32_t count, doub
 int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps, void* hip_stream,
                     double* gbs);
 
+/* gpuos_hbm_probe with the grid given: `workgroups` workgroups of four
+ * waves (0: one per compute unit, as gpuos_hbm_probe does; at most 4096).
+ * Each lane keeps 16 loads of 16 bytes in flight, 64 KiB per workgroup; with
+ * one workgroup per CU, a sweep over the workgroup count gives achievable
+ * bandwidth against the number of active CUs, and by Little's law the
+ * latency and the bytes in flight per CU that a share of the peak needs
+ * (the method of "The GPU Needs an Operating System", appendix A.3).
+ * Errors: as gpuos_hbm_probe; E_INVAL for more than 4096 workgroups. */
+int gpuos_hbm_probe_grid(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps,
+                         uint32_t workgroups, void* hip_stream, double* gbs);
+
 /* ABI version of the loaded library. */
 int gpuos_abi_version(void);
 

@@ -1105,16 +1105,21 @@ int gpuos_latency_bench(void* ctx, const gpuos_desc* descs, uint32_t count, doub
     return GPUOS_OK;
 }
 
-int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps, void* hip_stream,
-                    double* gbs) {
-    if (!src || !dst || bytes == 0 || (bytes & 15u) || bytes > (1ull << 30) || mode > 1 || reps == 0)
+int gpuos_hbm_probe_grid(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps,
+                         uint32_t workgroups, void* hip_stream, double* gbs) {
+    if (!src || !dst || bytes == 0 || (bytes & 15u) || bytes > (1ull << 30) || mode > 1 || reps == 0 ||
+        workgroups > 4096)
         return GPUOS_E_INVAL;
     if (mode == 0 && bytes < 4096) return GPUOS_E_INVAL;
     hipStream_t s = (hipStream_t)hip_stream;
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return GPUOS_E_HIP;
+    uint32_t grid = workgroups;
+    if (grid == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            return GPUOS_E_HIP;
+        grid = (uint32_t)cus;
+    }
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return GPUOS_E_HIP;
     if (hipEventCreate(&e1) != hipSuccess) {
@@ -1124,12 +1129,12 @@ int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, u
     int rc = GPUOS_OK;
     const bool copy = mode == 1;
     float ms = 0.0f;
-    if (launch_hbm_probe(src, dst, (uint32_t)bytes, copy, (uint32_t)cus, s) != hipSuccess ||
+    if (launch_hbm_probe(src, dst, (uint32_t)bytes, copy, grid, s) != hipSuccess ||
         hipEventRecord(e0, s) != hipSuccess) {
         rc = GPUOS_E_HIP;
     } else {
         for (uint32_t i = 0; i < reps && rc == GPUOS_OK; ++i)
-            if (launch_hbm_probe(src, dst, (uint32_t)bytes, copy, (uint32_t)cus, s) != hipSuccess) rc = GPUOS_E_HIP;
+            if (launch_hbm_probe(src, dst, (uint32_t)bytes, copy, grid, s) != hipSuccess) rc = GPUOS_E_HIP;
         if (rc == GPUOS_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
                                hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
             rc = GPUOS_E_HIP;
@@ -1138,6 +1143,11 @@ int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, u
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     return rc;
+}
+
+int gpuos_hbm_probe(const void* src, void* dst, uint64_t bytes, uint32_t mode, uint32_t reps, void* hip_stream,
+                    double* gbs) {
+    return gpuos_hbm_probe_grid(src, dst, bytes, mode, reps, 0, hip_stream, gbs);
 }
 
 }  // extern "C"

@@ -109,7 +109,7 @@ EXPORTS = [
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
     "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_latency_bench", "gpuos_trace_read",
     "gpuos_hbm_probe", "gpuos_register_expr", "gpuos_ring_peek",
-    "gpuos_eager_submit_static",
+    "gpuos_eager_submit_static", "gpuos_hbm_probe_grid",
 ]
 
 TRACE_DTYPE = np.dtype([("seq", "<u8"), ("tile", "<u4"), ("hw", "<u4"), ("t_claim", "<u8"), ("t_ready", "<u8"),
@@ -161,6 +161,7 @@ def lib():
         "gpuos_register_expr": ([vp, u32, vp, u32], ctypes.c_int),
         "gpuos_ring_peek": ([vp, u64, vp, vp], ctypes.c_int),
         "gpuos_eager_submit_static": ([vp, u32, vp], ctypes.c_int),
+        "gpuos_hbm_probe_grid": ([vp, vp, u64, u32, u32, u32, vp, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -340,6 +341,14 @@ def gpuos_ring_peek(ctx: int, seq: int) -> Tuple[int, np.ndarray, np.ndarray]:
     ex = np.zeros(56, np.uint16)
     rc = lib().gpuos_ring_peek(ctx, seq, d.ctypes.data, ex.ctypes.data)
     return rc, d[0], ex
+
+
+def gpuos_hbm_probe_grid(src: int, dst: int, nbytes: int, mode: int, reps: int, workgroups: int,
+                         hip_stream: int) -> float:
+    g = ctypes.c_double(0)
+    _check("gpuos_hbm_probe_grid", lib().gpuos_hbm_probe_grid(src, dst, nbytes, mode, reps, workgroups,
+                                                                hip_stream or None, ctypes.byref(g)))
+    return g.value
 
 
 def gpuos_trace_read(ctx: int, max_records: int = 1 << 20) -> np.ndarray:

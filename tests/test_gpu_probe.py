@@ -23,3 +23,17 @@ def test_hbm_probe_copy_and_read():
     assert torch.equal(src, dst)
     say(f"  copy {g_copy:.0f} GB/s, read {g_read:.0f} GB/s")
     assert g_copy > 0 and g_read > 0
+
+
+@pytest.mark.parametrize("wg", [1, 8, 64, 300])
+def test_hbm_probe_grid_copy_reproduces_its_source(wg):
+    import torch
+    n = (16 << 20) + 4096 + 16
+    say(f"hbm probe grid {wg} workgroups, {n} bytes")
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream()
+    s.synchronize()
+    g = G.gpuos_hbm_probe_grid(src.data_ptr(), dst.data_ptr(), n, 1, 1, wg, s.cuda_stream)
+    assert torch.equal(src, dst) and g > 0
+    say(f"  copy {g:.0f} GB/s")
