@@ -33,7 +33,7 @@
 extern "C" {
 #endif
 
-#define GPUOS_ABI_VERSION 4
+#define GPUOS_ABI_VERSION 5
 
 /* ---------------------------------------------------------------- errors */
 #define GPUOS_OK 0
@@ -75,7 +75,9 @@ enum gpuos_kind {
     GPUOS_OP_COPY = 14,      /* byte copy of `size` bytes */
     GPUOS_OP_EXPR = 15,      /* element-wise program bound by gpuos_register_expr */
     GPUOS_OP_MATMUL = 16,    /* y[M, N] = x[M, K] . Wt[N, K]^T, M <= 64 (small matmul) */
-    GPUOS_KIND_COUNT = 17,
+    GPUOS_OP_JIT = 17,       /* element-wise program compiled at run time, bound by
+                                gpuos_register_jit (GPUOS_INIT_JIT contexts only) */
+    GPUOS_KIND_COUNT = 18,
     GPUOS_KIND_EMPTY = 0xFFFFFFFFu /* register_op: unbind an op id */
 };
 #define GPUOS_MAX_OPS 256
@@ -161,6 +163,9 @@ static_assert(sizeof(gpuos_desc) == 128, "gpuos_desc must be 128 bytes");
                                          consumer, completes descriptors in a random
                                          dependency-respecting order and computes nothing */
 #define GPUOS_INIT_TRACE (1u << 1)    /* record one gpuos_trace_rec per work unit */
+#define GPUOS_INIT_JIT (1u << 2)      /* run the executor build that can call code injected
+                                         with gpuos_register_jit (one unit per wave; its
+                                         injected calls use a stack in scratch memory) */
 
 typedef struct gpuos_init_params {
     int32_t device;             /* HIP device ordinal */
@@ -242,6 +247,52 @@ enum gpuos_expr_op {
 #define GPUOS_EXPR_MAX_INSTR 32
 #define GPUOS_EXPR_MAX_CONSTS 16
 int gpuos_register_expr(void* ctx, uint32_t op_id, const uint32_t* program, uint32_t n_words);
+
+/* Bind op_id to compiled code (kind JIT): the pages' operator injection as
+ * they describe it, a curated template compiled at run time with its
+ * parameters substituted, loaded, its address written into the inactive
+ * table slot and enabled by the version flip while the executor keeps
+ * running (digest page, section 3 Q2 "Dynamic Operator Table", steps 1-5;
+ * section 4, core technical barriers, template-based JIT).  The template is
+ * an element-wise loop over one work unit and the parameters are an
+ * element-wise program in the gpuos_register_expr format, with the same
+ * meaning: the program becomes straight-line fp32 code (hipRTC, gfx950,
+ * no contraction of * and + into fused multiply-adds, no flush of
+ * subnormals; exp/log/tanh/sigmoid evaluated as in the interpreter), one
+ * function per dtype, loaded into this context's device.  The running
+ * executor reaches it through a function pointer: the library refuses
+ * code that needs more registers or stack than the executor reserves for
+ * injected calls (GPUOS_JIT_MAX_VGPRS VGPRs, GPUOS_JIT_MAX_AGPRS AGPRs,
+ * GPUOS_JIT_MAX_SGPRS SGPRs, no stack of its own).  Loaded code stays
+ * loaded until gpuos_shutdown.  Compiling the same program again in one
+ * context reuses the loaded code.
+ * info (may be NULL) receives the timings and the code's resources.
+ * Errors: E_NOOP (op_id >= GPUOS_MAX_OPS), E_INVAL (malformed program, or a
+ * context made without GPUOS_INIT_JIT), E_STATE (the compiled code exceeds
+ * the reserved budget), E_HIP (compile, load or copy failed; the compiler's
+ * log goes to stderr). */
+#define GPUOS_JIT_MAX_VGPRS 96u
+#define GPUOS_JIT_MAX_AGPRS 32u
+#define GPUOS_JIT_MAX_SGPRS 102u
+#define GPUOS_JIT_MAX_STACK 0u
+typedef struct gpuos_jit_info {
+    double compile_ms;   /* hipRTC compile of the generated source (0 when reused) */
+    double load_ms;      /* code-object load and address resolution */
+    double flip_ms;      /* table write and version flip */
+    uint32_t vgprs;      /* resources of the compiled body (upper bounds) */
+    uint32_t agprs;
+    uint32_t sgprs;
+    uint32_t stack_bytes;
+    uint64_t code_bytes; /* size of the code object */
+    uint32_t reused;     /* 1 if an earlier identical program's code was reused */
+    uint32_t pad;
+} gpuos_jit_info;
+int gpuos_register_jit(void* ctx, uint32_t op_id, const uint32_t* program, uint32_t n_words,
+                       gpuos_jit_info* info);
+/* The HIP source gpuos_register_jit compiles for `program` (NUL-terminated,
+ * truncated to cap bytes); *len_out receives the full length.  Needs no
+ * context or GPU.  Errors: E_INVAL (malformed program). */
+int gpuos_jit_source(const uint32_t* program, uint32_t n_words, char* out, uint64_t cap, uint64_t* len_out);
 
 /* --------------------------------------------------------------- submit */
 #define GPUOS_SUBMIT_BLOCK (1u << 0)     /* wait for free slots instead of E_FULL */

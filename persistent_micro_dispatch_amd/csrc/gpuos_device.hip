@@ -89,8 +89,29 @@ __device__ __forceinline__ T pick(const T* v, uint32_t r) {
     return x;
 }
 
-template <uint32_t SLOTS>
+// Bodies injected with gpuos_register_jit are called through this pointer
+// type by the executor build that allows it (JIT = true).
+typedef void (*jit_body_fn)(const uint8_t* a, const uint8_t* b, uint8_t* out, uint64_t n, uint32_t tile,
+                            uint32_t lane);
+
+// For a call through a pointer the compiler gives the calling kernel the
+// registers of the largest non-kernel function in this module, which the
+// callee may then use.  This function is never called; its clobbers fix
+// that budget at GPUOS_JIT_MAX_VGPRS VGPRs (v0..v95), GPUOS_JIT_MAX_AGPRS
+// AGPRs (a0..a31) and SGPRs up to s95 (GPUOS_JIT_MAX_SGPRS with the special
+// registers), and gpuos_register_jit refuses injected code that reports
+// more.
+extern "C" __device__ __attribute__((noinline, used)) void gpuos_jit_budget(const uint8_t*, const uint8_t*, uint8_t*,
+                                                                            uint64_t, uint32_t, uint32_t) {
+    asm volatile("" ::: "v95", "a31", "s95");
+}
+static_assert(GPUOS_JIT_MAX_VGPRS == 96u && GPUOS_JIT_MAX_AGPRS == 32u && GPUOS_JIT_MAX_SGPRS == 102u,
+              "budget clobbers above");
+__device__ jit_body_fn gpuos_jit_budget_addr = gpuos_jit_budget;
+
+template <uint32_t SLOTS, bool JIT>
 __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
+    uint64_t jit_seen = 0;  // the injected body this wave called last
     DevCtl* C = A.dctl;
     uint64_t n_units = 0, n_depw = 0;
     const uint64_t N = (uint64_t)A.mask + 1;
@@ -217,7 +238,21 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
             // would hold registers for the kernel's whole life.
             uint32_t ln = lane;
             asm volatile("" : "+v"(ln));
-            if (status == GPUOS_ST_OK && U.kind != KIND_BAD) run_unit(U, ln);
+            if constexpr (JIT) {
+                if (status == GPUOS_ST_OK && U.kind == GPUOS_OP_JIT) {
+                    // new code: an acquire first, so that nothing this XCD's
+                    // caches hold from before the code was loaded is used
+                    if (U.prog != jit_seen) {
+                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+                        jit_seen = U.prog;
+                    }
+                    ((jit_body_fn)U.prog)((const uint8_t*)U.a, (const uint8_t*)U.b, (uint8_t*)U.out, U.size, U.tile, ln);
+                } else if (status == GPUOS_ST_OK && U.kind != KIND_BAD) {
+                    run_unit(U, ln);
+                }
+            } else {
+                if (status == GPUOS_ST_OK && U.kind != KIND_BAD) run_unit(U, ln);
+            }
             ++n_units;
             const uint64_t t_body = A.trace ? wall_clock64() : 0;
             // completion: publish this unit's (write-through) outputs, count
@@ -430,7 +465,8 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             kind = te->kind;
             p0 = te->p0;
             pin.kflags = te->flags;
-            prog = te->fn;
+            // an injected body has one entry per operand type
+            prog = kind == GPUOS_OP_JIT && dt_in(pin.flags) == GPUOS_BF16 ? te->reserved : te->fn;
         }
         Plan pl;
         if (kind < GPUOS_KIND_COUNT) {
@@ -556,11 +592,11 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     }
 }
 
-template <uint32_t SLOTS>
+template <uint32_t SLOTS, bool JIT = false>
 __device__ __forceinline__ void executor_body(const ExecArgs& A, uint64_t* lds) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
     if (blockIdx.x == 0 && wave == 0) fetcher_loop(A, lane, lds, lds + 64 * 16);
-    else worker_loop<SLOTS>(A, lane);
+    else worker_loop<SLOTS, JIT>(A, lane);
     if (lane == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
         __hip_atomic_fetch_add(&A.hctl->exited, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -577,6 +613,13 @@ extern "C" __global__ void __launch_bounds__(256) gpuos_executor(ExecArgs A) {
 extern "C" __global__ void __launch_bounds__(256) gpuos_executor_s2(ExecArgs A) {
     __shared__ uint64_t lds[64 * 16 + 72];
     executor_body<2>(A, lds);
+}
+
+// one unit per worker wave, and calls into bodies injected with
+// gpuos_register_jit (a stack in scratch memory for those calls)
+extern "C" __global__ void __launch_bounds__(256) gpuos_executor_jit(ExecArgs A) {
+    __shared__ uint64_t lds[64 * 16 + 72];
+    executor_body<1, true>(A, lds);
 }
 
 // ------------------------------------------------------------ eager kernels
@@ -686,8 +729,9 @@ __global__ void __launch_bounds__(256) gpuos_hbm_probe_kernel(const uint8_t* src
 }
 
 // ------------------------------------------------------ host-side launchers
-hipError_t launch_executor(const ExecArgs& a, uint32_t slots, uint32_t grid, uint32_t block, hipStream_t s) {
-    if (slots == 2) hipLaunchKernelGGL(gpuos_executor_s2, dim3(grid), dim3(block), 0, s, a);
+hipError_t launch_executor(const ExecArgs& a, uint32_t slots, bool jit, uint32_t grid, uint32_t block, hipStream_t s) {
+    if (jit) hipLaunchKernelGGL(gpuos_executor_jit, dim3(grid), dim3(block), 0, s, a);
+    else if (slots == 2) hipLaunchKernelGGL(gpuos_executor_s2, dim3(grid), dim3(block), 0, s, a);
     else hipLaunchKernelGGL(gpuos_executor, dim3(grid), dim3(block), 0, s, a);
     return hipGetLastError();
 }

@@ -17,13 +17,16 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <map>
 #include <mutex>
 #include <random>
+#include <string>
 #include <thread>
 #include <vector>
 
 #include "gpuos.h"
 #include "gpuos_internal.h"
+#include "gpuos_jit.h"
 #include "hazard.h"
 
 #if defined(__x86_64__)
@@ -34,7 +37,7 @@
 #endif
 
 namespace gpuos {
-hipError_t launch_executor(const ExecArgs& a, uint32_t slots, uint32_t grid, uint32_t block, hipStream_t s);
+hipError_t launch_executor(const ExecArgs& a, uint32_t slots, bool jit, uint32_t grid, uint32_t block, hipStream_t s);
 hipError_t launch_eager(const gpuos_desc& d, uint32_t kind, uint32_t ntiles, uint8_t* scratch, hipStream_t s);
 hipError_t launch_null(hipStream_t s);
 hipError_t launch_hbm_probe(const void* src, void* dst, uint32_t n, bool copy, uint32_t grid, hipStream_t s);
@@ -152,6 +155,7 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
             add(d.output, sz * d.dim[1] * eo, true);
             break;
         case GPUOS_OP_EXPR:  // b is counted as read whenever it is given
+        case GPUOS_OP_JIT:
             add(d.input_a, sz * es, false);
             add(d.input_b, sz * es, false);
             add(d.output, sz * eo, true);
@@ -244,6 +248,11 @@ struct gpuos_ctx {
     uint64_t acc_units = 0, acc_depw = 0, acc_batches = 0, acc_fetched = 0;
     uint64_t deps_explicit = 0, deps_range = 0;
     uint64_t ns_submit = 0, ns_blocked = 0, ns_hazard = 0;  // host time inside gpuos_submit
+    // injected code (gpuos_register_jit): the device's target name and every
+    // code object loaded so far, by source (each stays loaded until shutdown)
+    std::string arch;
+    std::mutex jit_mu;
+    std::map<std::string, JitCode> jit_code;
     // loopback consumer
     std::thread lb_thread;
     std::atomic<bool> lb_stop{false};
@@ -301,7 +310,8 @@ int executor_launch(gpuos_ctx* c) {
     if (c->trace && hipMemsetAsync(c->trace, 0, c->trace_cap * sizeof(gpuos_trace_rec), c->exec) != hipSuccess)
         return GPUOS_E_HIP;
     if (hipEventRecord(c->ev_start, c->exec) != hipSuccess) return GPUOS_E_HIP;
-    if (launch_executor(a, c->P.units_per_wave, c->P.num_wgs, 64u * c->P.waves_per_wg, c->exec) != hipSuccess)
+    if (launch_executor(a, c->P.units_per_wave, (c->P.flags & GPUOS_INIT_JIT) != 0, c->P.num_wgs, 64u * c->P.waves_per_wg,
+                        c->exec) != hipSuccess)
         return GPUOS_E_HIP;
     if (hipEventRecord(c->ev_stop, c->exec) != hipSuccess) return GPUOS_E_HIP;
     c->running = true;
@@ -414,6 +424,7 @@ int validate_params(gpuos_init_params& P) {
     if (P.waves_per_wg > 4) return GPUOS_E_INVAL;
     if (P.units_per_wave == 0) P.units_per_wave = 1;
     if (P.units_per_wave > 2) return GPUOS_E_INVAL;
+    if ((P.flags & GPUOS_INIT_JIT) && P.units_per_wave != 1) return GPUOS_E_INVAL;  // one build: one unit per wave
     if (P.backoff_max == 0) P.backoff_max = 64;
     if (P.backoff_max > 127) return GPUOS_E_INVAL;
     if (P.scratch_bytes == 0) P.scratch_bytes = 256ull << 20;
@@ -450,6 +461,8 @@ void free_ctx(gpuos_ctx* c) {
     if (c->ev_stop) (void)hipEventDestroy(c->ev_stop);
     if (c->aux) (void)hipStreamDestroy(c->aux);
     if (c->own_exec && c->exec) (void)hipStreamDestroy(c->exec);
+    for (auto& kv : c->jit_code)  // the executor has exited: nothing runs this code any more
+        if (kv.second.mod) (void)hipModuleUnload(kv.second.mod);
     delete c;
 }
 
@@ -480,7 +493,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     c->flip_seq = c->N;
     for (int v = 0; v < 2; ++v)
         for (uint32_t i = 0; i < GPUOS_MAX_OPS; ++i)
-            c->shadow[v][i] = TableEntry{i < GPUOS_KIND_COUNT && i != GPUOS_OP_EXPR ? i : (uint32_t)GPUOS_KIND_EMPTY,
+            c->shadow[v][i] = TableEntry{i < GPUOS_KIND_COUNT && i != GPUOS_OP_EXPR && i != GPUOS_OP_JIT ? i : (uint32_t)GPUOS_KIND_EMPTY,
                                          0, 0.f, 0.f, 0, 0};
     memset(c->shadow_prog, 0, sizeof(c->shadow_prog));
     const size_t N = c->N;
@@ -509,6 +522,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     hipDeviceProp_t prop;
     HIPCHK(hipGetDeviceProperties(&prop, P.device));
     c->cu_count = (uint32_t)prop.multiProcessorCount;
+    c->arch = prop.gcnArchName;
     if (c->P.num_wgs == 0) c->P.num_wgs = c->cu_count;
     // one fetcher wave plus at least one worker; every workgroup must be able
     // to be resident at once (at most four one-wave workgroups per CU)
@@ -624,7 +638,7 @@ int gpuos_register_op(void* ctx, uint32_t op_id, uint32_t kind, const void* cons
     gpuos_ctx* c = (gpuos_ctx*)ctx;
     if (!c) return GPUOS_E_INVAL;
     if (op_id >= GPUOS_MAX_OPS || (kind >= GPUOS_KIND_COUNT && kind != GPUOS_KIND_EMPTY)) return GPUOS_E_NOOP;
-    if (kind == GPUOS_OP_EXPR) return GPUOS_E_INVAL;  // a program is bound with gpuos_register_expr
+    if (kind == GPUOS_OP_EXPR || kind == GPUOS_OP_JIT) return GPUOS_E_INVAL;  // bound with register_expr / _jit
     if (len > 8 || (len && !consts)) return GPUOS_E_INVAL;
     std::lock_guard<std::mutex> g(c->mu);
     TableEntry te{kind, 0, 0.f, 0.f, 0, 0};
@@ -637,27 +651,81 @@ int gpuos_register_expr(void* ctx, uint32_t op_id, const uint32_t* program, uint
     gpuos_ctx* c = (gpuos_ctx*)ctx;
     if (!c || !program || n_words == 0) return GPUOS_E_INVAL;
     if (op_id >= GPUOS_MAX_OPS) return GPUOS_E_NOOP;
-    const uint32_t w0 = program[0];
-    const uint32_t ni = w0 & 0xFFu, nk = (w0 >> 8) & 0xFFu;
-    if ((w0 >> 16) != 0 || ni == 0 || ni > GPUOS_EXPR_MAX_INSTR || nk > GPUOS_EXPR_MAX_CONSTS ||
-        n_words != 1 + ni + nk)
-        return GPUOS_E_INVAL;
-    uint32_t kflags = ni << 8;
-    uint32_t slot[PROG_WORDS] = {};
-    slot[0] = w0;
-    for (uint32_t i = 0; i < ni; ++i) {
-        const uint32_t w = program[1 + i];
-        const uint32_t op = w & 0xFFu, d = (w >> 8) & 0xFu, s1 = (w >> 12) & 0xFu, s2 = (w >> 16) & 0xFu;
-        const uint32_t k = (w >> 20) & 0xFFu;
-        if (op == 0 || op >= GPUOS_X_COUNT || d > 3 || s1 > 3 || s2 > 3 || (w >> 28) != 0) return GPUOS_E_INVAL;
-        if (op == GPUOS_X_CONST && k >= nk) return GPUOS_E_INVAL;
-        if (op == GPUOS_X_LDB) kflags |= EXPR_USES_B;
-        slot[PROG_INSTR + i] = w;
-    }
-    for (uint32_t i = 0; i < nk; ++i) slot[PROG_CONST + i] = program[1 + ni + i];
+    uint32_t slot[PROG_WORDS], kflags = 0;
+    if (!expr_validate(program, n_words, slot, &kflags)) return GPUOS_E_INVAL;
     std::lock_guard<std::mutex> g(c->mu);
     TableEntry te{GPUOS_OP_EXPR, kflags, 0.f, 0.f, 0, 0};
     return table_flip(c, op_id, te, slot);
+}
+
+int gpuos_register_jit(void* ctx, uint32_t op_id, const uint32_t* program, uint32_t n_words, gpuos_jit_info* info) {
+    gpuos_ctx* c = (gpuos_ctx*)ctx;
+    if (info) memset(info, 0, sizeof(*info));
+    if (!c || !program || n_words == 0) return GPUOS_E_INVAL;
+    if (op_id >= GPUOS_MAX_OPS) return GPUOS_E_NOOP;
+    uint32_t slot[PROG_WORDS], kflags = 0;
+    if (!expr_validate(program, n_words, slot, &kflags)) return GPUOS_E_INVAL;
+    if (!(c->P.flags & GPUOS_INIT_JIT)) return GPUOS_E_INVAL;
+    const std::string src = jit_source(slot, kflags);
+    JitCode jc;
+    bool reused = false;
+    {
+        // compiled and loaded without the producer lock: submissions go on
+        std::lock_guard<std::mutex> jg(c->jit_mu);
+        auto it = c->jit_code.find(src);
+        if (it != c->jit_code.end()) {
+            jc = it->second;
+            reused = true;
+        } else {
+            std::string log;
+            // loopback contexts compile and check the code but load nothing
+            const std::string arch = c->loopback ? std::string("gfx950") : c->arch;
+            if (!c->loopback && hipSetDevice(c->P.device) != hipSuccess) return GPUOS_E_HIP;
+            const int rc = jit_build(src, arch, !c->loopback, c->aux, &jc, &log);
+            if (info) {
+                info->compile_ms = jc.compile_ms;
+                info->vgprs = jc.vgprs;
+                info->agprs = jc.agprs;
+                info->sgprs = jc.sgprs;
+                info->stack_bytes = jc.stack;
+                info->code_bytes = jc.code_bytes;
+            }
+            if (rc != GPUOS_OK) {
+                if (rc == GPUOS_E_HIP && !log.empty()) fprintf(stderr, "gpuos_register_jit: compiler log:\n%s\n", log.c_str());
+                return rc;
+            }
+            c->jit_code[src] = jc;
+        }
+    }
+    if (info) {
+        info->load_ms = reused ? 0.0 : jc.load_ms;
+        info->vgprs = jc.vgprs;
+        info->agprs = jc.agprs;
+        info->sgprs = jc.sgprs;
+        info->stack_bytes = jc.stack;
+        info->code_bytes = jc.code_bytes;
+        info->reused = reused ? 1u : 0u;
+        if (!reused) info->compile_ms = jc.compile_ms;
+    }
+    std::lock_guard<std::mutex> g(c->mu);
+    const uint64_t t0 = now_ns();
+    TableEntry te{GPUOS_OP_JIT, kflags, 0.f, 0.f, jc.fn_f32, jc.fn_bf16};
+    const int rc = table_flip(c, op_id, te, nullptr);
+    if (info) info->flip_ms = (double)(now_ns() - t0) * 1e-6;
+    return rc;
+}
+
+int gpuos_jit_source(const uint32_t* program, uint32_t n_words, char* out, uint64_t cap, uint64_t* len_out) {
+    uint32_t slot[PROG_WORDS], kflags = 0;
+    if (!expr_validate(program, n_words, slot, &kflags)) return GPUOS_E_INVAL;
+    const std::string src = jit_source(slot, kflags);
+    if (len_out) *len_out = src.size();
+    if (out && cap) {
+        const uint64_t n = std::min<uint64_t>(cap - 1, src.size());
+        memcpy(out, src.data(), n);
+        out[n] = '\0';
+    }
+    return GPUOS_OK;
 }
 
 int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t flags, uint64_t* first_seq) {
@@ -984,7 +1052,7 @@ uint64_t gpuos_eager_scratch_bytes(const gpuos_desc* descs, uint32_t count) {
     uint64_t m = COUNTER_AREA;
     for (uint32_t i = 0; i < count; ++i) {
         const uint32_t kind = descs[i].op_id;
-        if (kind >= GPUOS_KIND_COUNT || kind == GPUOS_OP_EXPR) continue;
+        if (kind >= GPUOS_KIND_COUNT || kind == GPUOS_OP_EXPR || kind == GPUOS_OP_JIT) continue;
         const Plan p = make_plan(plan_in(kind, descs[i]));
         m = std::max<uint64_t>(m, p.scratch);
     }
@@ -997,7 +1065,8 @@ int gpuos_eager_submit(const gpuos_desc* descs, uint32_t count, void* hip_stream
     hipStream_t s = (hipStream_t)hip_stream;
     for (uint32_t i = 0; i < count; ++i) {
         const gpuos_desc& d = descs[i];
-        if (d.op_id >= GPUOS_KIND_COUNT || d.op_id == GPUOS_OP_EXPR) return GPUOS_E_INVAL;  // no table here
+        if (d.op_id >= GPUOS_KIND_COUNT || d.op_id == GPUOS_OP_EXPR || d.op_id == GPUOS_OP_JIT)
+            return GPUOS_E_INVAL;  // no table here
         const Plan p = make_plan(plan_in(d.op_id, d));
         if (p.status != GPUOS_ST_OK) return GPUOS_E_INVAL;
         if (p.scratch > 0 && (!scratch || p.scratch > scratch_bytes)) return GPUOS_E_INVAL;
@@ -1016,7 +1085,7 @@ int gpuos_eager_submit_static(const gpuos_desc* descs, uint32_t count, void* hip
     bool split = false;
     for (uint32_t i = 0; i < count; ++i) {
         const gpuos_desc& d = descs[i];
-        if (d.op_id >= GPUOS_KIND_COUNT || d.op_id == GPUOS_OP_EXPR) return GPUOS_E_INVAL;
+        if (d.op_id >= GPUOS_KIND_COUNT || d.op_id == GPUOS_OP_EXPR || d.op_id == GPUOS_OP_JIT) return GPUOS_E_INVAL;
         const Plan p = make_plan(plan_in(d.op_id, d));
         if (p.status != GPUOS_ST_OK || p.scratch > GPUOS_EAGER_STATIC_SCRATCH_BYTES) return GPUOS_E_INVAL;
         split = split || p.scratch > 0;

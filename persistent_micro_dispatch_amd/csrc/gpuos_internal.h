@@ -178,6 +178,7 @@ __host__ __device__ constexpr uint32_t expr_tile_bytes(uint32_t kflags, bool big
     return ((kflags >> 8) & 0xFFu) > 8u ? EW_TILE_BYTES_GELU : big ? EW_TILE_BYTES_BIG : EW_TILE_BYTES;
 }
 constexpr uint32_t COPY_TILE_BYTES = 32768;
+constexpr uint32_t JIT_TILE_BYTES = 4096;     // bytes of each operand per unit of an injected (JIT) body
 constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in registers
 #ifndef GPUOS_SDPA_KT
 #define GPUOS_SDPA_KT 1024
@@ -384,6 +385,15 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
             if ((d.kflags & EXPR_USES_B) && d.size > 0 && d.b == 0) return bad();
             uint64_t t = cdiv(d.size, expr_tile_bytes(d.kflags, ew_big(d.size, esz(di))) / esz(di));
+            if (t > MAX_TILES) return bad();
+            p.ntiles = t ? (uint32_t)t : 1u;
+            return p;
+        }
+        case GPUOS_OP_JIT: {
+            if (di != dout) return bad();
+            if (d.size > 0 && (d.a == 0 || d.out == 0)) return bad();
+            if ((d.kflags & EXPR_USES_B) && d.size > 0 && d.b == 0) return bad();
+            uint64_t t = cdiv(d.size, JIT_TILE_BYTES / esz(di));
             if (t > MAX_TILES) return bad();
             p.ntiles = t ? (uint32_t)t : 1u;
             return p;

@@ -22,8 +22,8 @@ GPUOS_E_TIMEOUT, GPUOS_E_DEVICE, GPUOS_E_HIP, GPUOS_E_STATE = -4, -5, -6, -7
 GPUOS_ST_OK, GPUOS_ST_BAD_OP, GPUOS_ST_BAD_SHAPE, GPUOS_ST_SPIN = 0, 1, 2, 3
 (GPUOS_OP_NOP, GPUOS_OP_ADD, GPUOS_OP_MUL, GPUOS_OP_RELU, GPUOS_OP_GELU, GPUOS_OP_SUM, GPUOS_OP_MAX,
  GPUOS_OP_MIN, GPUOS_OP_SOFTMAX, GPUOS_OP_LAYERNORM, GPUOS_OP_ROPE, GPUOS_OP_KV_APPEND, GPUOS_OP_SDPA,
- GPUOS_OP_GEMV, GPUOS_OP_COPY, GPUOS_OP_EXPR, GPUOS_OP_MATMUL) = range(17)
-GPUOS_KIND_COUNT = 17
+ GPUOS_OP_GEMV, GPUOS_OP_COPY, GPUOS_OP_EXPR, GPUOS_OP_MATMUL, GPUOS_OP_JIT) = range(18)
+GPUOS_KIND_COUNT = 18
 GPUOS_KIND_EMPTY = 0xFFFFFFFF
 GPUOS_MAX_OPS = 256
 (GPUOS_X_LDA, GPUOS_X_LDB, GPUOS_X_CONST, GPUOS_X_MOV, GPUOS_X_ADD, GPUOS_X_SUB, GPUOS_X_MUL, GPUOS_X_DIV,
@@ -36,6 +36,8 @@ GPUOS_F_ROPE_HALF = 1 << 8
 GPUOS_F_SDPA_MASK = 1 << 9
 GPUOS_INIT_LOOPBACK = 1
 GPUOS_INIT_TRACE = 2
+GPUOS_INIT_JIT = 4
+GPUOS_JIT_MAX_VGPRS, GPUOS_JIT_MAX_AGPRS, GPUOS_JIT_MAX_SGPRS, GPUOS_JIT_MAX_STACK = 96, 32, 102, 0
 GPUOS_SUBMIT_BLOCK, GPUOS_SUBMIT_NOHAZARD, GPUOS_SUBMIT_SERIAL = 1, 2, 4
 GPUOS_SEQ_ALL = 0xFFFFFFFFFFFFFFFF
 
@@ -109,8 +111,15 @@ EXPORTS = [
     "gpuos_loopback_order", "gpuos_eager_submit", "gpuos_eager_scratch_bytes", "gpuos_graph_build",
     "gpuos_graph_launch", "gpuos_graph_destroy", "gpuos_null_launch_bench", "gpuos_latency_bench", "gpuos_trace_read",
     "gpuos_hbm_probe", "gpuos_register_expr", "gpuos_ring_peek",
-    "gpuos_eager_submit_static", "gpuos_hbm_probe_grid",
+    "gpuos_eager_submit_static", "gpuos_hbm_probe_grid", "gpuos_register_jit", "gpuos_jit_source",
 ]
+
+
+class JitInfo(ctypes.Structure):
+    _fields_ = [("compile_ms", ctypes.c_double), ("load_ms", ctypes.c_double), ("flip_ms", ctypes.c_double),
+                ("vgprs", ctypes.c_uint32), ("agprs", ctypes.c_uint32), ("sgprs", ctypes.c_uint32),
+                ("stack_bytes", ctypes.c_uint32), ("code_bytes", ctypes.c_uint64), ("reused", ctypes.c_uint32),
+                ("pad", ctypes.c_uint32)]
 
 TRACE_DTYPE = np.dtype([("seq", "<u8"), ("tile", "<u4"), ("hw", "<u4"), ("t_claim", "<u8"), ("t_ready", "<u8"),
                         ("t_body", "<u8"), ("t_done", "<u8"), ("unit", "<u8"), ("pad", "<u8")])
@@ -162,6 +171,8 @@ def lib():
         "gpuos_ring_peek": ([vp, u64, vp, vp], ctypes.c_int),
         "gpuos_eager_submit_static": ([vp, u32, vp], ctypes.c_int),
         "gpuos_hbm_probe_grid": ([vp, vp, u64, u32, u32, u32, vp, ctypes.POINTER(ctypes.c_double)], ctypes.c_int),
+        "gpuos_register_jit": ([vp, u32, vp, u32, ctypes.POINTER(JitInfo)], ctypes.c_int),
+        "gpuos_jit_source": ([vp, u32, vp, u64, ctypes.POINTER(u64)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -225,6 +236,27 @@ def gpuos_register_expr(ctx: int, op_id: int, program) -> int:
     """Bind op_id to an element-wise program (uint32 words, gpuos.h layout)."""
     w = np.ascontiguousarray(np.asarray(program, np.uint32).reshape(-1))
     return lib().gpuos_register_expr(ctx, op_id, w.ctypes.data if len(w) else None, len(w))
+
+
+def gpuos_register_jit(ctx: int, op_id: int, program) -> Tuple[int, dict]:
+    """Bind op_id to the program compiled at run time.  Returns (rc, info)
+    with the compile, load and flip times and the code's resources."""
+    w = np.ascontiguousarray(np.asarray(program, np.uint32).reshape(-1))
+    info = JitInfo()
+    rc = lib().gpuos_register_jit(ctx, op_id, w.ctypes.data if len(w) else None, len(w), ctypes.byref(info))
+    return rc, {k: getattr(info, k) for k, _ in JitInfo._fields_ if k != "pad"}
+
+
+def gpuos_jit_source(program) -> Tuple[int, str]:
+    """The HIP source gpuos_register_jit compiles for `program`."""
+    w = np.ascontiguousarray(np.asarray(program, np.uint32).reshape(-1))
+    n = ctypes.c_uint64(0)
+    rc = lib().gpuos_jit_source(w.ctypes.data if len(w) else None, len(w), None, 0, ctypes.byref(n))
+    if rc != GPUOS_OK:
+        return rc, ""
+    buf = ctypes.create_string_buffer(n.value + 1)
+    rc = lib().gpuos_jit_source(w.ctypes.data, len(w), buf, n.value + 1, ctypes.byref(n))
+    return rc, buf.value.decode()
 
 
 def gpuos_submit(ctx: int, descs: np.ndarray, flags: int = 0) -> Tuple[int, int]:

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_entry_point():
     L = G.lib()
     for name in declared:
         assert hasattr(L, name), name
-    assert G.gpuos_abi_version() == 4
+    assert G.gpuos_abi_version() == 5
 
 
 def _ranges(recs):
