@@ -88,6 +88,103 @@ def recorded_traffic(workload):
     return None
 
 
+def jit_injection(sub, nbk, by, waves, ring, num_wgs):
+    """Compiled injection, in a context whose executor build calls injected
+    code: the latency of binding a new program (hipRTC compile, code-object
+    load, table flip; five programs that differ in a constant, so each is
+    compiled anew), and the stream's independent add/mul descriptors run as
+    the built-in bodies, as compiled a+b / a*b and as interpreted a+b / a*b
+    in that same executor."""
+    import workloads as W
+    from persistent_micro_dispatch_amd import gpuos as G
+    ctx = G.gpuos_init(ring_entries=ring, waves_per_wg=waves, num_wgs=num_wgs, flags=G.GPUOS_INIT_JIT)
+    try:
+        X, P = W.xins, W.program
+        # bound while the executor is paused, as for the interpreted programs
+        assert G.gpuos_pause(ctx, 30_000_000_000) == 0
+        reg, comp, load, flip = [], [], [], []
+        vgprs = 0
+        for i in range(5):
+            prog = P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_ADD, 0, 1, 2), X(W.X_CONST, 3, 0, 0, 0),
+                      X(W.X_ADD, 0, 0, 3)], [0.5 * (i + 1)])
+            ta = time.perf_counter()
+            rc, info = G.gpuos_register_jit(ctx, 210 + i, prog)
+            assert rc == 0, (rc, info)
+            reg.append((time.perf_counter() - ta) * 1e3)
+            comp.append(info["compile_ms"]); load.append(info["load_ms"]); flip.append(info["flip_ms"])
+            vgprs = max(vgprs, info["vgprs"])
+        p_add = P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_ADD, 0, 1, 2)])
+        p_mul = P([X(W.X_LDA, 1), X(W.X_LDB, 2), X(W.X_MUL, 0, 1, 2)])
+        assert G.gpuos_register_jit(ctx, 200, p_add)[0] == 0 and G.gpuos_register_jit(ctx, 201, p_mul)[0] == 0
+        assert G.gpuos_register_expr(ctx, 202, p_add) == 0 and G.gpuos_register_expr(ctx, 203, p_mul) == 0
+        assert G.gpuos_resume(ctx) == 0
+        row = {"register_ms_p50": float(np.median(reg)), "compile_ms_p50": float(np.median(comp)),
+               "load_ms_p50": float(np.median(load)), "flip_ms_p50": float(np.median(flip)),
+               "max_vgprs": int(vgprs), "descriptors": int(len(sub))}
+        fl = G.GPUOS_SUBMIT_BLOCK | G.GPUOS_SUBMIT_NOHAZARD
+        for key, ids in (("builtin", None), ("compiled", (200, 201)), ("interpreted", (202, 203))):
+            dd = sub.copy()
+            if ids:
+                dd["op_id"] = np.where(dd["op_id"] == W.OP_ADD, ids[0], ids[1]).astype(np.uint32)
+            best = 0.0
+            for _ in range(2):
+                ta = time.perf_counter()
+                rc, _, _ = G.gpuos_submit_bursts(ctx, dd, nbk, fl)
+                assert rc == 0 and G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
+                best = max(best, len(sub) / (time.perf_counter() - ta))
+            row[key + "_ops_per_s"] = best
+            row[key + "_gbs"] = best * by / len(sub) / 1e9
+        return row
+    finally:
+        assert G.gpuos_shutdown(ctx) == 0
+
+
+def chain_hops_by_xcd(num_wgs=512, n=4000, n_elem=256):
+    """A dependent chain of `n` single-unit adds on one buffer, traced: the
+    median time from one descriptor's completion to the next one's (a hop),
+    and from a completion to the consumer finding it, split by whether the
+    producer's last unit and the consumer's unit ran on the same XCD.  With
+    more workgroups than CUs the executor uses one claim shard, so
+    consecutive units land on any XCD."""
+    import torch
+    from persistent_micro_dispatch_amd import gpuos as G
+    buf = torch.zeros(n_elem, dtype=torch.float32, device="cuda")
+    one = torch.ones(n_elem, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    ctx = G.gpuos_init(num_wgs=num_wgs, waves_per_wg=1, ring_entries=512, flags=G.GPUOS_INIT_TRACE)
+    try:
+        d = G.new_descs(n)
+        d["op_id"] = G.GPUOS_OP_ADD
+        d["flags"] = G.flags(G.GPUOS_F32)
+        d["size"] = n_elem
+        d["input_a"] = d["output"] = buf.data_ptr()
+        d["input_b"] = one.data_ptr()
+        for i in range(0, n, 512):
+            assert G.gpuos_submit(ctx, d[i:i + 512], G.GPUOS_SUBMIT_BLOCK)[0] == 0
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 60_000_000_000)[0] == 0
+        assert G.gpuos_pause(ctx, 30_000_000_000) == 0
+        tr = G.gpuos_trace_read(ctx)
+    finally:
+        assert G.gpuos_shutdown(ctx) == 0
+    assert float(buf[0].item()) == float(n)
+    done, xcc_done, ready, xcc_ready = {}, {}, {}, {}
+    for r in tr:
+        q = int(r["seq"])
+        if q not in done or r["t_done"] > done[q]:
+            done[q], xcc_done[q] = int(r["t_done"]), int(r["hw"]) >> 16
+        if q not in ready or r["t_ready"] < ready[q]:
+            ready[q], xcc_ready[q] = int(r["t_ready"]), int(r["hw"]) >> 16
+    hop, seen = {"same": [], "other": []}, {"same": [], "other": []}
+    qs = sorted(done)
+    for a, b in zip(qs[:-1], qs[1:]):
+        if b == a + 1:
+            k = "same" if xcc_done[a] == xcc_ready[b] else "other"
+            hop[k].append((done[b] - done[a]) * 1e-2)    # 100 MHz wall clock -> us
+            seen[k].append((ready[b] - done[a]) * 1e-2)
+    return {k: {"hops": len(hop[k]), "hop_us_p50": float(np.median(hop[k])) if hop[k] else None,
+                "seen_after_done_us_p50": float(np.median(seen[k])) if seen[k] else None} for k in hop}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -390,7 +487,7 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
     lat = G.gpuos_latency_bench(ctx, descs[:nlat])
     lat_py = None
     nop_s = chain_s = None
-    buckets = injection = None
+    buckets = injection = jit_in = None
     chain = nop = None
     if headline:
         lat_py = np.zeros(min(nlat, 500))
@@ -481,6 +578,7 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
             row[key + "_ops_per_s"] = len(sub) / el
             row[key + "_gbs"] = by / el / 1e9
         injection = row
+        jit_in = (sub, nbk, by)
     assert G.gpuos_pause(ctx, 30_000_000_000) == 0
     chain_ok = float(chain_buf.cpu()[0]) == 5000.0 if headline else None
 
@@ -550,6 +648,9 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
             extra.update({"null_launch_us": null_async / 1e3, "null_launch_sync_us": null_sync / 1e3})
         del scratch
     assert G.gpuos_shutdown(ctx) == 0
+    if jit_in is not None:
+        injection["compiled"] = jit_injection(*jit_in, waves=waves, ring=ring, num_wgs=num_wgs)
+    xcd_hops = chain_hops_by_xcd() if headline else None
 
     # ---- roofline of the executor kernel (one launch = one step)
     mean_launch_ms = float(np.mean(launch_ms))
@@ -605,6 +706,7 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
             "dependent_chain_ok": chain_ok,
             "size_buckets": buckets,
             "injection": injection,
+            "chain_hops_by_xcd": xcd_hops,
         })
     rec.update(extra)
     del pool, descs, chain_buf, one_buf
