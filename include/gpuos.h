@@ -91,6 +91,7 @@ enum gpuos_kind {
 #define GPUOS_FLAGS(in_dtype, out_dtype) ((uint32_t)(in_dtype) | ((uint32_t)(out_dtype) << 4))
 #define GPUOS_F_ROPE_HALF (1u << 8)  /* RoPE pairs (x_i, x_{i+D/2}) instead of (x_2i, x_2i+1) */
 #define GPUOS_F_SDPA_MASK (1u << 9)  /* SDPA adds an fp32 mask [B, C] (aux[2]) to the scaled scores */
+#define GPUOS_F_KV_PAGED (1u << 10)  /* KV_APPEND / SDPA: caches are page pools with a block table */
 
 /* ------------------------------------------------------------ descriptor */
 /* One ring entry, 128 bytes (the pages give 64-128 B holding op_id,
@@ -131,6 +132,21 @@ enum gpuos_kind {
  *                   accumulation on the matrix cores, output in the output
  *                   dtype; 1 <= M <= 64, K a multiple of 32 (the pages'
  *                   "small matmuls", too small for a BLAS call).
+ *   Paged caches (flag GPUOS_F_KV_PAGED on KV_APPEND and SDPA): the caches
+ *                   are pools of P pages [P, Hkv, PS, D] (K in aux[0], V in
+ *                   aux[1]; Hkv = the append's dim[0] heads, SDPA's dim[3])
+ *                   and a block table [B, MP] of int32 page numbers maps
+ *                   position j of batch row b to page table[b][j / PS], row
+ *                   j % PS (the usual paged-attention layout).  size = B in
+ *                   the low 32 bits and P in the high 32 bits; dim[2] = PS, a
+ *                   power of two from 64 to 1024; param.u[5] = MP (lens[b] at
+ *                   most MP * PS, and for SDPA at most 64 * PS).  The table
+ *                   is in aux[2] for KV_APPEND and in b for SDPA (whose
+ *                   mask, with GPUOS_F_SDPA_MASK, stays in aux[2], [B, MP *
+ *                   PS]).  A table entry outside [0, P) writes nothing (append)
+ *                   or drops that page's keys (SDPA).  Hazard tracking takes
+ *                   each pool as one range: an append orders with every
+ *                   earlier attention that reads the pool, and so on.
  *   COPY            a -> output, `size` bytes.
  * Within one descriptor an output must coincide exactly with an input or
  * not overlap it.  B must be at most 8 (lens are inline). */

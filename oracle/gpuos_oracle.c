@@ -379,8 +379,49 @@ static int op_rope(const pool_t* P, const orc_rec* r) {
     return 0;
 }
 
+/* Paged caches (record flag 4): the cache is a pool of NP pages, page p
+ * holding positions of H heads as [H, PS, D]; the block table (int32,
+ * [B, MP]) gives the page of position j of batch row b as table[b][j / PS]
+ * and its row as j % PS.  The record's size packs B (bits 0-15), MP (bits
+ * 16-31) and NP (bits 32-63); dim[2] is PS.  paged_row returns the element
+ * offset of position j, head h, of row b in the pool, or -1 if the table
+ * entry is outside [0, NP). */
+static int64_t paged_row(const uint8_t* table, int64_t MP, int64_t NP, int64_t H, int64_t PS, int64_t D,
+                         int64_t b, int64_t h, int64_t j) {
+    int32_t page;
+    memcpy(&page, table + (b * MP + j / PS) * 4, 4);
+    if (page < 0 || page >= NP) return -1;
+    return (((int64_t)page * H + h) * PS + j % PS) * D;
+}
+
+/* KV append into paged caches: position L_b - 1 of every head of row b */
+static int op_kv_append_paged(const pool_t* P, const orc_rec* r) {
+    int64_t B = r->size & 0xFFFF, MP = (r->size >> 16) & 0xFFFF, NP = r->size >> 32;
+    int64_t H = r->dim[0], D = r->dim[1], PS = r->dim[2];
+    int es = esize(r->dtype);
+    if (B > 8 || MP < 1 || NP < 1 || PS < 1) return ORC_E_BOUNDS;
+    const uint8_t* k = span(P, r, R_A, B * H * D * es);
+    const uint8_t* v = span(P, r, R_B, B * H * D * es);
+    uint8_t* K = span(P, r, R_AUX0, NP * H * PS * D * es);
+    uint8_t* V = span(P, r, R_AUX1, NP * H * PS * D * es);
+    const uint8_t* table = span(P, r, R_AUX2, B * MP * 4);
+    if (!k || !v || !K || !V || !table) return ORC_E_BOUNDS;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t pos = r->lens[b] - 1;
+        if (pos < 0 || pos >= MP * PS) return ORC_E_BOUNDS;
+        for (int64_t h = 0; h < H; ++h) {
+            int64_t at = paged_row(table, MP, NP, H, PS, D, b, h, pos);
+            if (at < 0) continue;  /* a page outside the pool: nothing is written */
+            memcpy(K + at * es, k + (b * H + h) * D * es, (size_t)(D * es));
+            memcpy(V + at * es, v + (b * H + h) * D * es, (size_t)(D * es));
+        }
+    }
+    return 0;
+}
+
 /* KV append: K[b,h,L_b-1,:] = k[b,h,:], V[b,h,L_b-1,:] = v[b,h,:] (bit copy) */
 static int op_kv_append(const pool_t* P, const orc_rec* r) {
+    if (r->flags & 4) return op_kv_append_paged(P, r);
     int64_t B = r->size, H = r->dim[0], D = r->dim[1], C = r->dim[2];
     int es = esize(r->dtype);
     if (B > 8) return ORC_E_BOUNDS;
@@ -409,16 +450,24 @@ static int op_kv_append(const pool_t* P, const orc_rec* r) {
  * mask[b, j] added, an fp32 mask [B, C] in aux2 shared by all heads; a row
  * whose scores are all -inf is softmax over nothing and gives NaN. */
 static int op_sdpa(const pool_t* P, const orc_rec* r) {
-    int64_t B = r->size, H = r->dim[0], D = r->dim[1], C = r->dim[2];
+    /* paged caches (flag 4): the caches are pools of NP pages [Hkv, PS, D],
+     * the block table is in b, and a row holds C = MP * PS positions */
+    const int paged = (r->flags & 4) != 0;
+    int64_t B = paged ? (r->size & 0xFFFF) : r->size, H = r->dim[0], D = r->dim[1];
+    int64_t MP = paged ? (r->size >> 16) & 0xFFFF : 0, NP = paged ? r->size >> 32 : 0, PS = r->dim[2];
+    int64_t C = paged ? MP * PS : r->dim[2];
     int64_t Hkv = r->dim[3] > 0 ? r->dim[3] : H;
     int dt = r->dtype, dout = r->out_dtype;
     if (B > 8 || H % Hkv != 0) return ORC_E_BOUNDS;
+    if (paged && (MP < 1 || NP < 1 || PS < 1)) return ORC_E_BOUNDS;
     const int64_t G = H / Hkv;
+    const int64_t cache = paged ? NP * Hkv * PS * D : B * Hkv * C * D;
     const uint8_t* q = span(P, r, R_A, B * H * D * esize(dt));
-    const uint8_t* K = span(P, r, R_AUX0, B * Hkv * C * D * esize(dt));
-    const uint8_t* V = span(P, r, R_AUX1, B * Hkv * C * D * esize(dt));
+    const uint8_t* K = span(P, r, R_AUX0, cache * esize(dt));
+    const uint8_t* V = span(P, r, R_AUX1, cache * esize(dt));
     uint8_t* o = span(P, r, R_OUT, B * H * D * esize(dout));
-    if (!q || !K || !V || !o) return ORC_E_BOUNDS;
+    const uint8_t* table = paged ? span(P, r, R_B, B * MP * 4) : NULL;
+    if (!q || !K || !V || !o || (paged && !table)) return ORC_E_BOUNDS;
     const uint8_t* mask = NULL;
     if (r->flags & 2) {
         mask = span(P, r, R_AUX2, B * C * 4);
@@ -436,8 +485,12 @@ static int op_sdpa(const pool_t* P, const orc_rec* r) {
             int64_t kv = (b * Hkv + h / G) * C * D, qo = (b * H + h) * D;
             double m = -INFINITY;
             for (int64_t j = 0; j < L; ++j) {
+                /* key j: row j of the (b, head) cache, or its place in a page;
+                 * a page outside the pool leaves key j out */
+                int64_t kj = paged ? paged_row(table, MP, NP, Hkv, PS, D, b, h / G, j) : kv + j * D;
+                if (kj < 0) { s[j] = -INFINITY; continue; }
                 double dot = 0.0;
-                for (int64_t d = 0; d < D; ++d) dot += ld(q, dt, qo + d) * ld(K, dt, kv + j * D + d);
+                for (int64_t d = 0; d < D; ++d) dot += ld(q, dt, qo + d) * ld(K, dt, kj + d);
                 s[j] = dot * scale;
                 if (mask) s[j] += ld(mask, ORC_F32, b * C + j);
                 if (s[j] > m) m = s[j];
@@ -447,7 +500,9 @@ static int op_sdpa(const pool_t* P, const orc_rec* r) {
             for (int64_t d = 0; d < D; ++d) acc[d] = 0.0;
             for (int64_t j = 0; j < L; ++j) {
                 double p = s[j] / z;
-                for (int64_t d = 0; d < D; ++d) acc[d] += p * ld(V, dt, kv + j * D + d);
+                int64_t kj = paged ? paged_row(table, MP, NP, Hkv, PS, D, b, h / G, j) : kv + j * D;
+                if (kj < 0) continue;  /* a key left out has no value row */
+                for (int64_t d = 0; d < D; ++d) acc[d] += p * ld(V, dt, kj + d);
             }
             for (int64_t d = 0; d < D; ++d) st(o, dout, qo + d, acc[d]);
         }

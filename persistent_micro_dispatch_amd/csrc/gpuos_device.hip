@@ -456,6 +456,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         pin.a = dw[2]; pin.b = dw[3]; pin.out = dw[4]; pin.aux0 = dw[8]; pin.aux1 = dw[9]; pin.aux2 = dw[10];
         pin.lensw[0] = dw[13];
         pin.lensw[1] = dw[14];
+        pin.pu5 = (uint32_t)(dw[15] >> 32);
         uint32_t kind = KIND_BAD;
         float p0 = 0.0f;
         uint64_t prog = 0;

@@ -120,6 +120,15 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
         }
         case GPUOS_OP_KV_APPEND: {
             const uint64_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            if (kv_paged(d.flags)) {  // whole pools: which pages are written is in device memory
+                const uint64_t B = kv_rows(d.size, d.flags), pool = kv_pages(d.size) * H * C * D * es;
+                add(d.input_a, B * H * D * es, false);
+                add(d.input_b, B * H * D * es, false);
+                add(d.aux[2], B * d.param.u[5] * 4ull, false);
+                add(d.aux[0], pool, true);
+                add(d.aux[1], pool, true);
+                break;
+            }
             add(d.input_a, sz * H * D * es, false);
             add(d.input_b, sz * H * D * es, false);
             add(d.aux[0], sz * H * C * D * es, true);  // batch rows 0..B-1 of each cache, whole
@@ -129,6 +138,16 @@ int accesses(uint32_t kind, const gpuos_desc& d, Access* out) {
         case GPUOS_OP_SDPA: {
             const uint64_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
             const uint64_t Hkv = d.dim[3] ? d.dim[3] : H;
+            if (kv_paged(d.flags)) {
+                const uint64_t B = kv_rows(d.size, d.flags), pool = kv_pages(d.size) * Hkv * C * D * es;
+                add(d.input_a, B * H * D * es, false);
+                add(d.input_b, B * d.param.u[5] * 4ull, false);
+                add(d.aux[0], pool, false);
+                add(d.aux[1], pool, false);
+                if (d.flags & GPUOS_F_SDPA_MASK) add(d.aux[2], B * d.param.u[5] * C * 4, false);
+                add(d.output, B * H * D * eo, true);
+                break;
+            }
             add(d.input_a, sz * H * D * es, false);
             if (sz > 0 && sz <= MAX_B) {
                 // from the first key of batch row 0 to the last key read in row B-1
@@ -175,6 +194,7 @@ PlanIn plan_in(uint32_t kind, const gpuos_desc& d, uint32_t kflags = 0) {
     for (int i = 0; i < 4; ++i) p.dim[i] = d.dim[i];
     p.lensw[0] = (uint64_t)d.param.u[0] | ((uint64_t)d.param.u[1] << 32);
     p.lensw[1] = (uint64_t)d.param.u[2] | ((uint64_t)d.param.u[3] << 32);
+    p.pu5 = d.param.u[5];
     p.a = d.input_a;
     p.b = d.input_b;
     p.out = d.output;

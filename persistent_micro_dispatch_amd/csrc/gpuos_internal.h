@@ -208,6 +208,7 @@ struct PlanIn {
     uint64_t size;
     uint32_t dim[4];
     uint64_t lensw[2];  // lens[0..7] as packed 16-bit fields (descriptor bytes 104..120)
+    uint32_t pu5;       // param.u[5] (paged caches: table row length MP)
     uint64_t a, b, out, aux0, aux1, aux2;
 };
 
@@ -264,6 +265,22 @@ __host__ __device__ inline uint32_t sdpa_keys_per_unit(uint32_t B, uint32_t H, c
     return kt;
 }
 
+// Paged caches (GPUOS_F_KV_PAGED): `size` carries the batch rows in its low
+// 32 bits and the pool's page count in its high 32 bits; pages hold a power
+// of two of positions, 64 to 1024, so that an attention unit (at most 1024
+// keys, halved in powers of two) never spans two pages.
+__host__ __device__ inline bool kv_paged(uint32_t flags) { return (flags & GPUOS_F_KV_PAGED) != 0u; }
+__host__ __device__ inline uint64_t kv_rows(uint64_t size, uint32_t flags) {
+    return kv_paged(flags) ? (size & 0xFFFFFFFFull) : size;
+}
+__host__ __device__ inline uint64_t kv_pages(uint64_t size) { return size >> 32; }
+__host__ __device__ inline bool page_size_ok(uint32_t ps) { return ps >= 64u && ps <= 1024u && (ps & (ps - 1u)) == 0u; }
+__host__ __device__ inline uint32_t sdpa_unit_keys(uint32_t B, uint32_t H, const uint64_t* lensw, uint32_t flags,
+                                                   uint32_t ps) {
+    const uint32_t kt = sdpa_keys_per_unit(B, H, lensw);
+    return kv_paged(flags) && ps < kt ? ps : kt;
+}
+
 // Query heads per SDPA unit: under grouped-query attention the query heads
 // of a group share their key/value rows, so with D = 128 and groups of a
 // multiple of 4 heads a unit takes 4 of them and reads each key/value chunk
@@ -310,14 +327,18 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
         }
         case GPUOS_OP_ROPE:
         case GPUOS_OP_KV_APPEND: {
-            const uint64_t B = d.size;
-            const uint32_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            const bool paged = d.kind == GPUOS_OP_KV_APPEND && kv_paged(d.flags);
+            const uint64_t B = paged ? kv_rows(d.size, d.flags) : d.size;
+            const uint32_t H = d.dim[0], D = d.dim[1];
+            // capacity: positions per row (paged: MP pages of PS positions)
+            const uint64_t C = paged ? (uint64_t)d.pu5 * d.dim[2] : d.dim[2];
             if (B == 0 || B > MAX_B || H == 0 || D == 0 || di != dout) return bad();
             if (d.kind == GPUOS_OP_ROPE) {
                 // k has dim[3] heads (0: H), at most H
                 if ((D & 1u) || D > 256u || d.a == 0 || d.b == 0 || d.dim[3] > H) return bad();
             } else {
                 if (C == 0 || d.a == 0 || d.b == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
+                if (paged && (!page_size_ok(d.dim[2]) || kv_pages(d.size) == 0 || d.aux2 == 0)) return bad();
             }
             for (uint32_t i = 0; i < B; ++i) {
                 if (lens_at(d.lensw, i) == 0) return bad();
@@ -333,19 +354,23 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             return p;
         }
         case GPUOS_OP_SDPA: {
-            const uint64_t B = d.size;
-            const uint32_t H = d.dim[0], D = d.dim[1], C = d.dim[2];
+            const bool paged = kv_paged(d.flags);
+            const uint64_t B = kv_rows(d.size, d.flags);
+            const uint32_t H = d.dim[0], D = d.dim[1];
+            const uint64_t C = paged ? (uint64_t)d.pu5 * d.dim[2] : d.dim[2];
             if (B == 0 || B > MAX_B || H == 0 || C == 0 || (D != 64u && D != 128u)) return bad();
             if (d.dim[3] != 0 && H % d.dim[3] != 0) return bad();  // key/value heads divide the query heads
             if (di != GPUOS_BF16) return bad();
             if (d.a == 0 || d.out == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
             if ((d.flags & GPUOS_F_SDPA_MASK) && d.aux2 == 0) return bad();
+            if (paged && (!page_size_ok(d.dim[2]) || kv_pages(d.size) == 0 || d.b == 0)) return bad();
+            const uint32_t kt = sdpa_unit_keys((uint32_t)B, H, d.lensw, d.flags, d.dim[2]);
             uint64_t units = 0;
             bool split = false;
             for (uint32_t i = 0; i < B; ++i) {
                 const uint32_t L = lens_at(d.lensw, i);
                 if (L == 0 || L > C) return bad();
-                uint64_t ns = cdiv(L, sdpa_keys_per_unit((uint32_t)B, H, d.lensw));
+                uint64_t ns = cdiv(L, kt);
                 if (ns > 64) return bad();  // the split merge reads one split per lane
                 if (ns > 1) split = true;
                 units += ns * H;

@@ -826,6 +826,40 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
 }
 
 // -------------------------------------------------------------- KV append
+// Paged caches: row pos = L_b - 1 of batch row b lives on page
+// table[b][pos / PS] at row pos % PS; that page holds [H, PS, D], so the
+// destinations of all heads lie in one window of H * PS rows.  A page
+// number outside the pool writes nothing.
+__device__ __forceinline__ void kv_tile_paged(const Unit& u, uint32_t b, uint32_t lane) {
+    const uint32_t H = u.dim[0], D = u.dim[1], PS = u.dim[2];
+    const uint32_t MP = __float_as_uint(u.pf[5]);
+    const uint32_t ES = esz(dt_in(u.flags));
+    const uint32_t pos = lens_at(u.lensw, b) - 1u;
+    const uint32_t pg = ld4((const uint8_t*)u.aux2 + ((uint64_t)b * MP + pos / PS) * 4u);
+    if ((uint64_t)pg >= kv_pages(u.size)) return;
+    const uint64_t RB = (uint64_t)D * ES;
+    const uint64_t page_bytes = (uint64_t)H * PS * RB;
+    const uint64_t rowoff = (uint64_t)(pos % PS) * RB;
+    for (uint32_t t = 0; t < 2; ++t) {
+        const uint8_t* src = (const uint8_t*)(t == 0 ? u.a : u.b) + (uint64_t)b * H * RB;
+        uint8_t* dst = (uint8_t*)(t == 0 ? u.aux0 : u.aux1) + (uint64_t)pg * page_bytes + rowoff;
+        if (RB % 16u == 0 && (((uint64_t)src | (uint64_t)dst) & 15ull) == 0 && page_bytes < (1ull << 31)) {
+            const uint32_t cpr = (uint32_t)(RB / 16u), total = cpr * H;
+            const RBuf rs = rbuf(src, total * 16u);
+            const WBuf wd = wbuf(dst, (uint32_t)(page_bytes - rowoff));
+            for (uint32_t j = lane; j < total; j += 64u) {
+                const uint32_t hh = j / cpr;
+                wst16(wd, (uint32_t)((uint64_t)hh * PS * RB) + (j % cpr) * 16u, rld16(rs, j * 16u));
+            }
+        } else {
+            for (uint64_t j = lane; j < RB * H / 2u; j += 64u) {  // 2-byte words
+                const uint64_t byte = j * 2u, hh = byte / RB, off = byte % RB;
+                wst16b(dst + hh * PS * RB + off, (uint16_t)ld2(src + hh * RB + off));
+            }
+        }
+    }
+}
+
 // Unit = one batch row b: K[b, h, L_b-1, :] = k[b, h, :] and the same for V.
 // Fast path: rows a multiple of 16 bytes, aligned, and the strided window of
 // destination rows below 2 GiB; 8 chunks per lane of each tensor are loaded
@@ -833,6 +867,10 @@ __device__ __forceinline__ void rope_tile(const Unit& u, uint32_t lane) {
 __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t NI = 8;
     const uint32_t b = u.tile;
+    if (kv_paged(u.flags)) {
+        kv_tile_paged(u, b, lane);
+        return;
+    }
     const uint32_t H = u.dim[0], D = u.dim[1], C = u.dim[2];
     const uint32_t ES = esz(dt_in(u.flags));
     const uint64_t pos = (uint64_t)lens_at(u.lensw, b) - 1;
@@ -907,10 +945,13 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t NI = 8u;  // load instructions per chunk
     constexpr uint32_t CK = NI * RPI;     // keys per chunk
     constexpr uint32_t PSTRIDE = D + 4u;  // floats per partial record: m, l, pad, pad, acc[D]
-    const uint32_t H = u.dim[0], C = u.dim[2];
+    const bool paged = kv_paged(u.flags);
+    const uint32_t H = u.dim[0], PS = u.dim[2];
+    const uint32_t MP = __float_as_uint(u.pf[5]);  // paged: table row length
+    const uint32_t C = paged ? MP * PS : u.dim[2];  // positions per batch row
     const uint32_t Hkv = u.dim[3] ? u.dim[3] : H;
     const uint32_t Bn = (uint32_t)u.size;
-    const uint32_t kt = sdpa_keys_per_unit(Bn, H, u.lensw);
+    const uint32_t kt = sdpa_unit_keys(Bn, H, u.lensw, u.flags, PS);
     const uint32_t HG = H / GP;  // units per (b, split): groups of GP query heads
     // unit -> (b, head group, split); mbase numbers the per-head splits of
     // earlier batch rows (the partial records and counters are per head)
@@ -928,12 +969,21 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     const uint32_t h0 = hg * GP;  // the unit's first query head; all GP share a key/value head
     const uint64_t bkv = (uint64_t)b * Hkv + h0 / (H / Hkv);
     const uint32_t k0 = sp * kt;
-    const uint32_t nk = min(L - k0, kt);
+    uint32_t nk = min(L - k0, kt);
     const float scale = u.pf[4] != 0.0f ? u.pf[4] : (u.p0 != 0.0f ? u.p0 : 1.0f / sqrtf((float)D));
     const float sl2 = scale * 1.4426950408889634f;  // scores in the log2 domain
     const uint32_t g = lane / DV, c = lane % DV;
-    const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bkv * C + k0) * D * 2u, nk * D * 2u);
-    const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bkv * C + k0) * D * 2u, nk * D * 2u);
+    // the unit's keys: a stretch of one (b, key/value head) row, or of one
+    // page (units never span two pages); a page outside the pool drops them
+    uint64_t kbase = (bkv * C + k0) * D * 2u;
+    if (paged) {
+        const uint32_t pg = ld4((const uint8_t*)u.b + ((uint64_t)b * MP + k0 / PS) * 4u);
+        const uint64_t hkv = bkv - (uint64_t)b * Hkv;
+        kbase = (((uint64_t)pg * Hkv + hkv) * PS + k0 % PS) * D * 2u;
+        if ((uint64_t)pg >= kv_pages(u.size)) nk = 0;
+    }
+    const RBuf rk = rbuf((const uint8_t*)u.aux0 + kbase, nk * D * 2u);
+    const RBuf rv = rbuf((const uint8_t*)u.aux1 + kbase, nk * D * 2u);
     const bool masked = (u.flags & GPUOS_F_SDPA_MASK) != 0u;
     const RBuf rm = rbuf((const uint8_t*)u.aux2 + ((uint64_t)b * C + k0) * 4u, masked ? nk * 4u : 0u);
     bf16x2 qv[GP][4];

@@ -34,6 +34,7 @@ GPUOS_OP_USER = 64
 GPUOS_F32, GPUOS_BF16 = 0, 1
 GPUOS_F_ROPE_HALF = 1 << 8
 GPUOS_F_SDPA_MASK = 1 << 9
+GPUOS_F_KV_PAGED = 1 << 10
 GPUOS_INIT_LOOPBACK = 1
 GPUOS_INIT_TRACE = 2
 GPUOS_INIT_JIT = 4

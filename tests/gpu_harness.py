@@ -112,6 +112,35 @@ def plain_rel(g: np.ndarray, r: np.ndarray) -> float:
     return float(np.max(np.abs(g[m] - r[m]) / a[m]))
 
 
+def kv_rows(inputs: List[np.ndarray], r, bb: int, hk: int, L: int):
+    """Key and value rows 0..L-1 of batch row bb and key/value head hk of an
+    SDPA record, as float arrays [L, D], from contiguous caches or through the
+    block table of paged ones; `kept` is False for keys whose page lies
+    outside the pool (they take no part)."""
+    d = [int(v) for v in r["dim"]]
+    buf, off = r["buf"], r["off"]
+    dt = int(r["dtype"])
+    H, D = d[0], d[1]
+    Hkv = d[3] or H
+    es = W.DTYPE_BYTES[dt]
+    kb, ko = inputs[int(buf[W.AUX0])], int(off[W.AUX0])
+    vb, vo = inputs[int(buf[W.AUX1])], int(off[W.AUX1])
+    if not int(r["flags"]) & W.FLAG_KV_PAGED:
+        row = (bb * Hkv + hk) * d[2] * D * es
+        return (_f(kb, ko + row, L * D, dt).reshape(L, D), _f(vb, vo + row, L * D, dt).reshape(L, D),
+                np.ones(L, bool))
+    PS, MP, NP = d[2], (int(r["size"]) >> 16) & 0xFFFF, int(r["size"]) >> 32
+    tb, to = inputs[int(buf[W.B])], int(off[W.B])
+    table = tb[to + bb * MP * 4: to + (bb + 1) * MP * 4].copy().view(np.int32).astype(np.int64)
+    j = np.arange(L)
+    page = table[j // PS]
+    kept = (page >= 0) & (page < NP)
+    start = (((np.where(kept, page, 0) * Hkv + hk) * PS + j % PS) * D * es)[:, None] + np.arange(D * es)[None, :]
+    K = as_float(kb[ko + start].reshape(-1).copy(), dt).reshape(L, D)
+    V = as_float(vb[vo + start].reshape(-1).copy(), dt).reshape(L, D)
+    return np.where(kept[:, None], K, 0.0), np.where(kept[:, None], V, 0.0), kept
+
+
 def check_outputs(r, inputs: List[np.ndarray], pairs, hp=None) -> dict:
     """Compare the outputs of one record.  inputs: the pool before it ran;
     pairs: (gpu bytes, oracle bytes) per output range in W.output_ranges
@@ -168,25 +197,24 @@ def check_outputs(r, inputs: List[np.ndarray], pairs, hp=None) -> dict:
             x = _f(inputs[int(buf[W.A])], int(off[W.A]), size * h, dt).reshape(size, h)
             ok, worst = rel_check(gf, rf, np.abs(x).sum(axis=1), tol)
         elif op == W.OP_SDPA:
-            H, D, C = d[0], d[1], d[2]
+            H, D = d[0], d[1]
+            size = W.rec_rows(r)
+            paged = bool(int(r["flags"]) & W.FLAG_KV_PAGED)
+            C = ((int(r["size"]) >> 16) & 0xFFFF) * d[2] if paged else d[2]
             Hkv = d[3] or H  # grouped-query attention: kv head h // (H // Hkv)
             q = _f(inputs[int(buf[W.A])], int(off[W.A]), size * H * D, dt).reshape(size, H, D)
             denom = np.zeros((size, H, D))
             scale = float(r["fparam"][1]) or 1.0 / np.sqrt(D)
-            kb, ko = inputs[int(buf[W.AUX0])], int(off[W.AUX0])
-            vb, vo = inputs[int(buf[W.AUX1])], int(off[W.AUX1])
-            es = W.DTYPE_BYTES[dt]
             mask = None
             if int(r["flags"]) & W.FLAG_SDPA_MASK:
                 mask = _f(inputs[int(buf[W.AUX2])], int(off[W.AUX2]), size * C, W.F32).reshape(size, C)
             for bb in range(size):
                 L = int(r["lens"][bb])
                 for hk in range(Hkv):
-                    row = (bb * Hkv + hk) * C * D * es
-                    K = _f(kb, ko + row, L * D, dt).reshape(L, D)
-                    V = _f(vb, vo + row, L * D, dt).reshape(L, D)
+                    K, V, kept = kv_rows(inputs, r, bb, hk, L)
                     hs = slice(hk * (H // Hkv), (hk + 1) * (H // Hkv))
                     s = (q[bb, hs] @ K.T) * scale
+                    s[:, ~kept] = -np.inf
                     if mask is not None:
                         s = s + mask[bb, :L]
                     with np.errstate(invalid="ignore"):

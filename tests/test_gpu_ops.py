@@ -381,3 +381,72 @@ def test_matmul(ctx, out_dt):
                         out=base + 2))
     res = _run_and_check(ctx, arrays, np.concatenate(recs))
     say("  worst", max(r["worst"] for r in res), "plain", max(r["plain"] for r in res))
+
+
+# ------------------------------------------------ paged KV caches
+def _paged_case(B, Hkv, D, PS, MP, extra):
+    """A pool of B*MP+extra pages (NaN-filled, so a read of an unmapped page
+    shows) and a block table giving every batch row its own random pages."""
+    NP = B * MP + extra
+    pool_k = bf16(RNG.standard_normal(NP * Hkv * PS * D))
+    pool_v = bf16(RNG.standard_normal(NP * Hkv * PS * D))
+    table = RNG.permutation(NP)[:B * MP].astype(np.int32)
+    unmapped = np.setdiff1d(np.arange(NP), table)
+    for p in (pool_k, pool_v):
+        p.reshape(NP, -1)[unmapped] = 0x7FC0  # bf16 NaN
+    return pool_k, pool_v, table, NP
+
+
+@pytest.mark.parametrize("out_dt", [W.F32, W.BF16])
+@pytest.mark.parametrize("masked", [False, True])
+def test_sdpa_paged(ctx, out_dt, masked):
+    say(f"sdpa paged out={out_dt} masked={masked}")
+    recs, arrays = [], []
+    for B, H, Hkv, D, PS, MP, lens in [(2, 8, 8, 128, 64, 8, [512, 17]), (1, 32, 8, 128, 1024, 4, [4096]),
+                                       (3, 4, 1, 64, 256, 3, [1, 256, 700]),
+                                       (8, 32, 8, 128, 128, 4, list(RNG.integers(1, 513, 8))),
+                                       (4, 16, 16, 128, 64, 40, [2560, 65, 1000, 63])]:
+        pk, pv, table, NP = _paged_case(B, Hkv, D, PS, MP, extra=3)
+        q = bf16(RNG.standard_normal(B * H * D))
+        o = np.zeros(B * H * D, np.float32 if out_dt == W.F32 else np.uint16)
+        base = len(arrays)
+        arrays += [q, pk, pv, o, table]
+        roles = dict(a=base, aux0=base + 1, aux1=base + 2, out=base + 3, b=base + 4)
+        fl = W.FLAG_KV_PAGED
+        if masked:
+            mask = np.where(RNG.random(B * MP * PS) < 0.25, -np.inf, RNG.standard_normal(B * MP * PS))
+            mask.reshape(B, -1)[:, 0] = 0.0  # every row keeps a key
+            arrays.append(mask.astype(np.float32))
+            roles["aux2"] = base + 5
+            fl |= W.FLAG_SDPA_MASK
+        recs.append(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=out_dt, size=W.paged_size(B, MP, NP),
+                        dim=(H, D, PS, Hkv), lens=lens, flags=fl, **roles))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))
+
+
+def test_kv_append_paged(ctx):
+    say("kv append paged")
+    recs, arrays = [], []
+    for B, H, D, PS, MP, lens in [(2, 8, 128, 64, 8, [512, 1]), (8, 8, 128, 128, 4, list(RNG.integers(1, 513, 8))),
+                                  (3, 4, 64, 1024, 2, [1024, 1025, 2048]), (1, 2, 36, 64, 3, [100])]:
+        pk, pv, table, NP = _paged_case(B, H, D, PS, MP, extra=2)
+        k, v = bf16(RNG.standard_normal(B * H * D)), bf16(RNG.standard_normal(B * H * D))
+        base = len(arrays)
+        arrays += [k, v, pk, pv, table]
+        recs.append(rec(W.OP_KV_APPEND, dtype=W.BF16, size=W.paged_size(B, MP, NP), dim=(H, D, PS), lens=lens,
+                        flags=W.FLAG_KV_PAGED, a=base, b=base + 1, aux0=base + 2, aux1=base + 3, aux2=base + 4))
+    _run_and_check(ctx, arrays, np.concatenate(recs))
+
+
+def test_paged_decode_stream_verify():
+    """A short decode stream on paged caches (64-position pages placed at
+    random per row), in verify mode: RoPE, append through the table and
+    attention over the pages, against the oracle step by step; the final
+    pools bit for bit."""
+    from gpu_harness import verify_stream
+    s = W.make_decode(steps=3, layers=2, capacity=512, l_min=100, n_triples=8, n_out=8, page_size=64)
+    say(f"paged decode verify, {len(s)} descriptors")
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts)
+    assert not res["fails"], res["fails"][:3]
+    assert res["kv_ok"]

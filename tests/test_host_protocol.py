@@ -583,3 +583,62 @@ def test_loopback_respects_hazards_attention_streams(kind):
     assert _check_order_precise(s.recs, order, first) == 0
     if kind != "mixed":  # the mixed pipeline is one dependency chain per token
         assert not np.array_equal(order, np.arange(first, first + len(descs)))
+
+
+def test_paged_cache_descriptors_validated_and_ordered():
+    """Paged caches: the page size must be a power of two from 64 to 1024,
+    the pool and the table must be given, rows may not pass MP pages (nor 64
+    attention splits); an append and the attentions around it order through
+    the whole-pool ranges (loopback consumer)."""
+    ctx = _loopback()
+    try:
+        B, H, D, PS, MP, NP = 2, 8, 128, 64, 8, 20
+        base = 1 << 40
+        app = G.new_descs(1)
+        app["op_id"] = G.GPUOS_OP_KV_APPEND
+        app["flags"] = G.flags(G.GPUOS_BF16) | G.GPUOS_F_KV_PAGED
+        app["size"] = B | (NP << 32)
+        app["dim"] = (H, D, PS, 0)
+        app["input_a"], app["input_b"] = base, base + (1 << 20)
+        app["aux"][0] = (base + (1 << 30), base + (2 << 30), base + (3 << 30))
+        app["param"][0, 5] = MP
+        G.set_lens(app, [300, 512])
+        att = G.new_descs(1)
+        att["op_id"] = G.GPUOS_OP_SDPA
+        att["flags"] = G.flags(G.GPUOS_BF16, G.GPUOS_F32) | G.GPUOS_F_KV_PAGED
+        att["size"] = B | (NP << 32)
+        att["dim"] = (H, D, PS, 0)
+        att["input_a"], att["output"], att["input_b"] = base + (4 << 20), base + (5 << 20), base + (3 << 30)
+        att["aux"][0, :2] = (base + (1 << 30), base + (2 << 30))
+        att["param"][0, 5] = MP
+        G.set_lens(att, [300, 512])
+        for d in (app, att):
+            for bad in ("ps", "np", "table", "len"):
+                x = d.copy()
+                if bad == "ps":
+                    x["dim"][0, 2] = 96                  # not a power of two
+                elif bad == "np":
+                    x["size"] = B                         # no pool pages
+                elif bad == "table":
+                    if d is app:
+                        x["aux"][0, 2] = 0
+                    else:
+                        x["input_b"] = 0
+                else:
+                    G.set_lens(x, [MP * PS + 1, 5])       # past the table row
+                assert G.gpuos_submit(ctx, x, 0)[0] == G.GPUOS_E_INVAL, (int(d["op_id"][0]), bad)
+        x = att.copy()
+        x["param"][0, 5] = 80
+        G.set_lens(x, [64 * PS + 1, 5])                   # 65 splits of one page each
+        assert G.gpuos_submit(ctx, x, 0)[0] == G.GPUOS_E_INVAL
+        # append, attention, append: each waits for the one before
+        rc, first = G.gpuos_submit(ctx, np.concatenate([app, att, app]), G.GPUOS_SUBMIT_BLOCK)
+        assert rc == 0
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 5_000_000_000)[0] == 0
+        order = list(G.gpuos_loopback_order(ctx))
+        assert order.index(first) < order.index(first + 1) < order.index(first + 2)
+        for i in (1, 2):  # the attention waits on the append, the second append on the attention
+            rc, dd, _ = G.gpuos_ring_peek(ctx, first + i)
+            assert rc == 0 and 1 in list(dd["dep_delta"])
+    finally:
+        G.gpuos_shutdown(ctx)

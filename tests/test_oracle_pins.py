@@ -861,3 +861,120 @@ def test_matmul_bf16_output_rounds_once():
     exact = bf16_val(x).astype(np.float64).reshape(M, K) @ bf16_val(wt).astype(np.float64).reshape(N, K).T
     assert np.array_equal(y16, np.array([oracle.round_bf16(v) for v in exact.reshape(-1)], np.uint16))
     assert np.allclose(y32.reshape(M, N), exact, rtol=1e-6)
+
+
+# ------------------------------------------------ paged KV caches
+# Pinned against the contiguous-cache path (itself pinned to torch above):
+# a pool that holds the contiguous caches' rows scattered to randomly placed
+# pages, read through the block table, must give the same attention bit for
+# bit, and an append through the table must land where the contiguous
+# append does.
+def _paged_layout(B=3, Hkv=2, D=16, PS=8, MP=4, extra_pages=5, seed=12):
+    rng = np.random.default_rng(seed)
+    NP = B * MP + extra_pages
+    perm = rng.permutation(NP)[:B * MP].astype(np.int32)
+    return perm.reshape(B, MP), NP
+
+
+def _scatter(cache, table, NP, B, Hkv, C, D, PS, fill):
+    """contiguous [B, Hkv, C, D] -> pool [NP, Hkv, PS, D] through the table"""
+    c = cache.reshape(B, Hkv, C, D)
+    pool = np.full((NP, Hkv, PS, D), fill, dtype=cache.dtype)
+    for b in range(B):
+        for i in range(C // PS):
+            pool[table[b, i]] = c[b, :, i * PS:(i + 1) * PS, :]
+    return pool.reshape(-1)
+
+
+def _gather(pool, table, NP, B, Hkv, C, D, PS):
+    p = pool.reshape(NP, Hkv, PS, D)
+    out = np.zeros((B, Hkv, C, D), dtype=pool.dtype)
+    for b in range(B):
+        for i in range(C // PS):
+            out[b, :, i * PS:(i + 1) * PS, :] = p[table[b, i]]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_paged_sdpa_equals_contiguous_sdpa(masked):
+    B, H, Hkv, D, PS, MP = 3, 4, 2, 16, 8, 4
+    C = PS * MP
+    rng = np.random.default_rng(31)
+    q = bf16(rng.standard_normal(B * H * D))
+    K = bf16(rng.standard_normal(B * Hkv * C * D))
+    V = bf16(rng.standard_normal(B * Hkv * C * D))
+    lens = [C, 1, 19]
+    table, NP = _paged_layout(B, Hkv, D, PS, MP)
+    mask = np.where(rng.random(B * C) < 0.3, -np.inf, rng.standard_normal(B * C)).astype(np.float32)
+    mask.reshape(B, C)[:, 0] = 0.0
+    Kp = _scatter(K, table, NP, B, Hkv, C, D, PS, np.uint16(0x7FC0))  # NaN where no page is mapped
+    Vp = _scatter(V, table, NP, B, Hkv, C, D, PS, np.uint16(0x7FC0))
+    fl = W.FLAG_SDPA_MASK if masked else 0
+    mk = {"aux2": 4} if masked else {}
+    o = np.zeros(B * H * D, np.float32)
+    ref = rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=B, dim=(H, D, C, Hkv), lens=lens, flags=fl,
+              a=0, aux0=1, aux1=2, out=3, **mk)
+    got = rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=W.paged_size(B, MP, NP), dim=(H, D, PS, Hkv),
+              lens=lens, flags=fl | W.FLAG_KV_PAGED, a=0, aux0=1, aux1=2, out=3, b=5, **mk)
+    a = run(ref, [q, K, V, o.copy(), mask])[3]
+    b = run(got, [q, Kp, Vp, o.copy(), mask, table.reshape(-1)])[3]
+    assert np.isfinite(a).all()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_paged_kv_append_equals_contiguous_append():
+    B, H, D, PS, MP = 3, 2, 16, 8, 4
+    C = PS * MP
+    rng = np.random.default_rng(32)
+    K = bf16(rng.standard_normal(B * H * C * D))
+    V = bf16(rng.standard_normal(B * H * C * D))
+    k = bf16(rng.standard_normal(B * H * D))
+    v = bf16(rng.standard_normal(B * H * D))
+    lens = [C, 1, 13]   # appends at the last row of the last page, the first row, mid-page
+    table, NP = _paged_layout(B, H, D, PS, MP, seed=13)
+    Kp, Vp = _scatter(K, table, NP, B, H, C, D, PS, 0), _scatter(V, table, NP, B, H, C, D, PS, 0)
+    ref = rec(W.OP_KV_APPEND, dtype=W.BF16, size=B, dim=(H, D, C), lens=lens, a=0, b=1, aux0=2, aux1=3)
+    got = rec(W.OP_KV_APPEND, dtype=W.BF16, size=W.paged_size(B, MP, NP), dim=(H, D, PS), lens=lens,
+              flags=W.FLAG_KV_PAGED, a=0, b=1, aux0=2, aux1=3, aux2=4)
+    _, _, Kr, Vr = run(ref, [k, v, K, V])
+    _, _, Kg, Vg, _ = run(got, [k, v, Kp, Vp, table.reshape(-1)])
+    assert np.array_equal(_gather(Kg, table, NP, B, H, C, D, PS), Kr)
+    assert np.array_equal(_gather(Vg, table, NP, B, H, C, D, PS), Vr)
+    # pages no row maps are untouched
+    unused = np.setdiff1d(np.arange(NP), table.reshape(-1))
+    assert np.array_equal(Kg.reshape(NP, -1)[unused], Kp.reshape(NP, -1)[unused])
+
+
+def test_paged_table_entry_outside_the_pool():
+    """A page number outside the pool: the append writes nothing there, and
+    attention leaves that page's keys out (the same as masking them)."""
+    B, H, Hkv, D, PS, MP = 2, 2, 2, 16, 8, 3
+    C = PS * MP
+    rng = np.random.default_rng(33)
+    q = bf16(rng.standard_normal(B * H * D))
+    K = bf16(rng.standard_normal(B * Hkv * C * D))
+    V = bf16(rng.standard_normal(B * Hkv * C * D))
+    table, NP = _paged_layout(B, Hkv, D, PS, MP, extra_pages=0, seed=14)
+    Kp, Vp = _scatter(K, table, NP, B, Hkv, C, D, PS, 0), _scatter(V, table, NP, B, Hkv, C, D, PS, 0)
+    bad = table.copy()
+    bad[1, 1] = NP + 7
+    bad[0, 2] = -1
+    lens = [C, C]
+    o = np.zeros(B * H * D, np.float32)
+    got = rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=W.paged_size(B, MP, NP), dim=(H, D, PS, Hkv),
+              lens=lens, flags=W.FLAG_KV_PAGED, a=0, aux0=1, aux1=2, out=3, b=4)
+    b_out = run(got, [q, Kp, Vp, o.copy(), bad.reshape(-1)])[3]
+    mask = np.zeros((B, C), np.float32)
+    mask[1, PS:2 * PS] = -np.inf
+    mask[0, 2 * PS:3 * PS] = -np.inf
+    a_out = _run_masked(q, K, V, lens, (B, H, Hkv, D, C), mask.reshape(-1))
+    assert np.array_equal(b_out.reshape(B, H, D).astype(np.float64), a_out)
+    k = bf16(rng.standard_normal(B * Hkv * D))
+    app = rec(W.OP_KV_APPEND, dtype=W.BF16, size=W.paged_size(B, MP, NP), dim=(Hkv, D, PS), lens=[PS + 3, 2 * PS + 1],
+              flags=W.FLAG_KV_PAGED, a=0, b=0, aux0=1, aux1=2, aux2=3)
+    bad2 = table.copy()
+    bad2[0, 1] = NP          # row 0 appends at position PS + 2: page index 1 -> outside
+    _, Kg, _, _ = run(app, [k, Kp, Vp, bad2.reshape(-1)])
+    # row 1 (position 2 PS, page table[1, 2]) was written; nothing else changed
+    changed = np.nonzero(Kg.reshape(NP, -1) != Kp.reshape(NP, -1))[0]
+    assert set(np.unique(changed)) == {int(table[1, 2])}

@@ -62,9 +62,23 @@ def program_is_exact(words) -> bool:
     n = int(words[0]) & 0xFF
     return all((int(w) & 0xFF) in X_EXACT for w in words[1:1 + n])
 F32, BF16 = 0, 1
-DTYPE_BYTES = {F32: 4, BF16: 2}
+I32 = 2  # int32 buffers (block tables of paged caches); never an op dtype
+DTYPE_BYTES = {F32: 4, BF16: 2, I32: 4}
 FLAG_ROPE_HALF = 1  # rotate-half pairing (x_i, x_{i+D/2}) instead of adjacent pairs
 FLAG_SDPA_MASK = 2  # SDPA adds an fp32 mask [B, C] (AUX2) to the scaled scores
+# KV_APPEND / SDPA on paged caches: pools of NP pages [heads, PS, D] and an
+# int32 block table [B, MP] (AUX2 for KV_APPEND, B for SDPA); the record's
+# size packs B (bits 0-15), MP (bits 16-31) and NP (bits 32-63), dim[2] = PS
+FLAG_KV_PAGED = 4
+
+
+def paged_size(b: int, mp: int, n_pages: int) -> int:
+    return int(b) | (int(mp) << 16) | (int(n_pages) << 32)
+
+
+def rec_rows(r) -> int:
+    """Batch rows of an attention record (the low bits of size when paged)."""
+    return int(r["size"]) & 0xFFFF if int(r["flags"]) & FLAG_KV_PAGED else int(r["size"])
 
 # Operand roles: index into buf/off.
 A, B, OUT, AUX0, AUX1, AUX2 = 0, 1, 2, 3, 4, 5
@@ -153,7 +167,9 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 @dataclasses.dataclass
 class Buffer:
     """One pool buffer.  init = ("normal", std, mean) | ("uniform", lo, hi) |
-    ("zeros",).  Values are drawn from SplitMix64 stream `seed`."""
+    ("zeros",) | ("pages", n_pages) (int32: the first nelem entries of a
+    random permutation of range(n_pages), a block table whose rows never
+    share a page).  Values are drawn from SplitMix64 stream `seed`."""
     name: str
     dtype: int
     nelem: int
@@ -167,6 +183,16 @@ class Buffer:
     def host_values(self) -> np.ndarray:
         """Materialise on the host: float32 array, or uint16 bf16 bits."""
         kind = self.init[0]
+        if kind == "pages":
+            n_pages = int(self.init[1])
+            assert self.dtype == I32 and self.nelem <= n_pages
+            rng = Rng(self.seed)
+            perm = np.arange(n_pages, dtype=np.int64)
+            u = rng.uniform24(n_pages)  # Fisher-Yates with the stream's uniforms
+            for i in range(n_pages - 1, 0, -1):
+                j = min(int(u[i] * (i + 1)), i)
+                perm[i], perm[j] = perm[j], perm[i]
+            return perm[:self.nelem].astype(np.int32)
         if kind == "zeros":
             v = np.zeros(self.nelem, np.float64)
         else:
@@ -353,17 +379,29 @@ def make_decode(seed: int = 4, steps: int = 2000, layers: int = 32, heads: int =
                 head_dim: int = 128, capacity: int = 4096, max_batch: int = 8,
                 l_min: int = 128, n_triples: int = 256, theta: float = 10000.0,
                 out_dtype: int = F32, n_out: int = 64,
-                batches: Sequence[int] = (1, 2, 4, 8), kv_heads: int = 0) -> Stream:
+                batches: Sequence[int] = (1, 2, 4, 8), kv_heads: int = 0, page_size: int = 0) -> Stream:
     """kv_heads (0: heads) below heads gives grouped-query attention: k, v
-    and the caches have kv_heads heads, shared by heads/kv_heads queries."""
+    and the caches have kv_heads heads, shared by heads/kv_heads queries.
+    page_size > 0 stores each layer's caches as pools of max_batch *
+    capacity / page_size pages of page_size positions, with a block table per
+    layer that gives every batch row its own randomly placed pages (the same
+    bytes as the contiguous caches, in paged layout)."""
     H, D, C, Bm = heads, head_dim, capacity, max_batch
     Hkv = kv_heads or H
     assert H % Hkv == 0
+    PS = page_size
+    MP = C // PS if PS else 0
+    NP = Bm * MP
+    assert not PS or C % PS == 0
     bufs: List[Buffer] = []
     kc0 = len(bufs)
     for l in range(layers):
         bufs.append(Buffer(f"K{l}", BF16, Bm * Hkv * C * D, ("normal", 1.0), _buffer_seed(seed, 10 * l)))
         bufs.append(Buffer(f"V{l}", BF16, Bm * Hkv * C * D, ("normal", 1.0), _buffer_seed(seed, 10 * l + 1)))
+    tb0 = len(bufs)
+    if PS:
+        for l in range(layers):
+            bufs.append(Buffer(f"T{l}", I32, Bm * MP, ("pages", NP), _buffer_seed(seed, 10 * l + 2)))
     tq = len(bufs)
     for t in range(n_triples):
         for j, nm in enumerate("qkv"):
@@ -411,12 +449,19 @@ def make_decode(seed: int = 4, steps: int = 2000, layers: int = 32, heads: int =
                 x["dim"][:] = (H, D, C, Hkv if Hkv != H else 0)
                 x["lens"][:] = lens_row
             rr[1]["dim"][:] = (Hkv, D, C, 0)
+            if PS:
+                for x in rr[1:]:
+                    x["flags"] |= FLAG_KV_PAGED
+                    x["size"] = paged_size(Bsz, MP, NP)
+                    x["dim"][2] = PS
+                rr[1]["buf"][AUX2] = tb0 + l
+                rr[2]["buf"][B] = tb0 + l
             recs.append(rr)
     r = np.concatenate(recs) if recs else _new_recs(0)
     bursts = np.full(steps * layers, 3) if steps else np.zeros(0, np.int64)
     return Stream("decode", bufs, r, bursts,
                   {"seed": seed, "kv_first": kc0, "layers": layers, "heads": H, "kv_heads": Hkv,
-                   "head_dim": D, "capacity": C})
+                   "head_dim": D, "capacity": C, "page_size": PS, "tables_first": tb0 if PS else None})
 
 
 # ---------------------------------------------------------------------------
@@ -578,6 +623,11 @@ def output_ranges(r) -> list:
     if op == OP_ROPE:
         hk = d[3] if d[3] else d[0]
         return [(int(buf[A]), int(off[A]), size * d[0] * d[1] * es), (int(buf[B]), int(off[B]), size * hk * d[1] * es)]
+    if op == OP_KV_APPEND and int(r["flags"]) & FLAG_KV_PAGED:
+        # the pages written depend on the block table: the whole pools
+        n_pages = size >> 32
+        pool = n_pages * d[0] * d[2] * d[1] * es
+        return [(int(buf[AUX0]), int(off[AUX0]), pool), (int(buf[AUX1]), int(off[AUX1]), pool)]
     if op == OP_KV_APPEND:
         H, D, C = d[0], d[1], d[2]
         out = []
@@ -589,7 +639,7 @@ def output_ranges(r) -> list:
                 out.append((int(buf[AUX1]), int(off[AUX1]) + row, D * es))
         return out
     if op == OP_SDPA:
-        return [(int(buf[OUT]), int(off[OUT]), size * d[0] * d[1] * eo)]
+        return [(int(buf[OUT]), int(off[OUT]), rec_rows(r) * d[0] * d[1] * eo)]
     if op == OP_GEMV:
         return [(int(buf[OUT]), int(off[OUT]), d[1] * eo)]
     if op == OP_MATMUL:
@@ -606,6 +656,7 @@ def algorithmic_bytes(recs: np.ndarray) -> np.ndarray:
     es = np.where(recs["dtype"] == BF16, 2, 4).astype(np.int64)
     eo = np.where(recs["out_dtype"] == BF16, 2, 4).astype(np.int64)
     n = recs["size"].astype(np.int64)
+    n = np.where(recs["flags"] & FLAG_KV_PAGED, n & 0xFFFF, n)  # paged attention: batch rows
     d0, d1 = recs["dim"][:, 0].astype(np.int64), recs["dim"][:, 1].astype(np.int64)
     out = np.zeros(len(recs), np.int64)
     m = (op == OP_ADD) | (op == OP_MUL) | ((op == OP_EXPR) & (recs["buf"][:, B] >= 0))

@@ -38,6 +38,10 @@ class DevicePool:
         self = cls.__new__(cls)
         self.tensors, self.nbytes = [], []
         for b in stream.buffers:
+            if b.init[0] == "pages":  # a block table: small, drawn on the host
+                self.tensors.append(torch.from_numpy(b.host_bytes().copy()).to(device))
+                self.nbytes.append(b.nbytes)
+                continue
             dt = torch.float32 if b.dtype == W.F32 else torch.bfloat16
             g = torch.Generator(device=device)
             g.manual_seed(int(b.seed) & 0x7FFFFFFFFFFFFFFF)
@@ -85,7 +89,8 @@ def to_descs(recs: np.ndarray, ptrs: Sequence[int]) -> np.ndarray:
     d["op_id"] = np.where(recs["op"] == W.OP_EXPR, recs["dim"][:, 3], recs["op"]).astype(np.uint32)
     d["flags"] = (recs["dtype"].astype(np.uint32) | (recs["out_dtype"].astype(np.uint32) << 4)
                   | np.where(recs["flags"] & W.FLAG_ROPE_HALF, G.GPUOS_F_ROPE_HALF, 0).astype(np.uint32)
-                  | np.where(recs["flags"] & W.FLAG_SDPA_MASK, G.GPUOS_F_SDPA_MASK, 0).astype(np.uint32))
+                  | np.where(recs["flags"] & W.FLAG_SDPA_MASK, G.GPUOS_F_SDPA_MASK, 0).astype(np.uint32)
+                  | np.where(recs["flags"] & W.FLAG_KV_PAGED, G.GPUOS_F_KV_PAGED, 0).astype(np.uint32))
     d["input_a"] = addr(W.A)
     d["input_b"] = addr(W.B)
     d["output"] = addr(W.OUT)
@@ -93,6 +98,11 @@ def to_descs(recs: np.ndarray, ptrs: Sequence[int]) -> np.ndarray:
     d["aux"][:, 1] = addr(W.AUX1)
     d["aux"][:, 2] = addr(W.AUX2)
     d["size"] = recs["size"].astype(np.uint64)
+    paged = (recs["flags"] & W.FLAG_KV_PAGED) != 0
+    if paged.any():
+        # record: B | MP << 16 | pages << 32; descriptor: B | pages << 32, MP in param.u[5]
+        sz = d["size"][paged]
+        d["size"][paged] = (sz & np.uint64(0xFFFF)) | ((sz >> np.uint64(32)) << np.uint64(32))
     d["dim"] = recs["dim"].astype(np.uint32)
     op = recs["op"]
     attn = (op == W.OP_ROPE) | (op == W.OP_KV_APPEND) | (op == W.OP_SDPA)
@@ -107,6 +117,8 @@ def to_descs(recs: np.ndarray, ptrs: Sequence[int]) -> np.ndarray:
         d["param"][attn, 0:4] = words[attn]
         f4 = np.where(op == W.OP_ROPE, recs["fparam"][:, 0], np.where(op == W.OP_SDPA, recs["fparam"][:, 1], 0))
         d["param"][attn, 4] = f4.astype(np.float32).view(np.uint32)[attn]
+    if paged.any():
+        d["param"][paged, 5] = ((recs["size"][paged].astype(np.uint64) >> np.uint64(16)) & np.uint64(0xFFFF)).astype(np.uint32)
     return d
 
 
