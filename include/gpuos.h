@@ -209,8 +209,11 @@ typedef struct gpuos_init_params {
  * stays resident, one workgroup per compute unit by default, until the host
  * stops it (digest page, section 3 Q2 "Persistent Kernel Executor": launched
  * once, never exits on its own, a small share of each SM/CU).
- * params may be NULL for defaults.  *out receives the context.
- * Errors: E_INVAL (bad params), E_HIP (allocation or launch failed). */
+ * params may be NULL for defaults.  *out receives the context.  One live
+ * context per device and process: a second one's resident executor could
+ * not be placed beside the first one's.
+ * Errors: E_INVAL (bad params), E_STATE (the device already has a live
+ * context in this process), E_HIP (allocation or launch failed). */
 int gpuos_init(const gpuos_init_params* params, void** out);
 
 /* ------------------------------------------------------------- register */

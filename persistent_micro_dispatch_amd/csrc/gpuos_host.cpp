@@ -273,6 +273,7 @@ struct gpuos_ctx {
     std::string arch;
     std::mutex jit_mu;
     std::map<std::string, JitCode> jit_code;
+    bool holds_device = false;  // counted in g_live
     // loopback consumer
     std::thread lb_thread;
     std::atomic<bool> lb_stop{false};
@@ -282,6 +283,13 @@ struct gpuos_ctx {
 };
 
 namespace {
+
+// Devices with a live (GPU) context in this process.  A resident executor
+// holds a share of every CU it runs on; a second one on the same device
+// could not be placed beside a full-size first one and would wait forever,
+// so gpuos_init refuses it.
+std::mutex g_live_mu;
+std::map<int, int> g_live;
 
 void refresh_wm(gpuos_ctx* c) {
     const uint64_t N = c->N;
@@ -483,6 +491,10 @@ void free_ctx(gpuos_ctx* c) {
     if (c->own_exec && c->exec) (void)hipStreamDestroy(c->exec);
     for (auto& kv : c->jit_code)  // the executor has exited: nothing runs this code any more
         if (kv.second.mod) (void)hipModuleUnload(kv.second.mod);
+    if (c->holds_device) {
+        std::lock_guard<std::mutex> lg(g_live_mu);
+        --g_live[c->P.device];
+    }
     delete c;
 }
 
@@ -538,6 +550,17 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
         e = (x);                                       \
         if (e != hipSuccess) { free_ctx(c); return GPUOS_E_HIP; } \
     } while (0)
+    {
+        std::lock_guard<std::mutex> lg(g_live_mu);
+        if (g_live[P.device] > 0) {
+            fprintf(stderr, "gpuos_init: device %d already has a live context in this process (its resident "
+                            "executor would keep a second one from being placed)\n", P.device);
+            free_ctx(c);
+            return GPUOS_E_STATE;
+        }
+        ++g_live[P.device];
+        c->holds_device = true;
+    }
     HIPCHK(hipSetDevice(P.device));
     hipDeviceProp_t prop;
     HIPCHK(hipGetDeviceProperties(&prop, P.device));

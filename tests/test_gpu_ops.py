@@ -439,14 +439,16 @@ def test_kv_append_paged(ctx):
     _run_and_check(ctx, arrays, np.concatenate(recs))
 
 
-def test_paged_decode_stream_verify():
+def test_paged_decode_stream_verify(ctx):
     """A short decode stream on paged caches (64-position pages placed at
     random per row), in verify mode: RoPE, append through the table and
     attention over the pages, against the oracle step by step; the final
-    pools bit for bit."""
+    pools bit for bit.  It runs on this module's context: a second context
+    would launch a second resident executor, which cannot be placed while
+    the first holds the CUs."""
     from gpu_harness import verify_stream
     s = W.make_decode(steps=3, layers=2, capacity=512, l_min=100, n_triples=8, n_out=8, page_size=64)
     say(f"paged decode verify, {len(s)} descriptors")
-    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts)
+    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ctx=ctx)
     assert not res["fails"], res["fails"][:3]
     assert res["kv_ok"]

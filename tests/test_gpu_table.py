@@ -206,3 +206,19 @@ def test_shutdown_with_work_in_flight_finishes_it():
     say("shutdown right after the last submit")
     assert G.gpuos_shutdown(ctx) == 0
     _assert_pool_equal(pool, _oracle_final(arrays, s.recs), s.buffers)
+
+
+def test_second_live_context_on_a_device_is_refused():
+    """One live context per device and process: the second gpuos_init gets
+    E_STATE (its executor could not be placed beside the first one's), and
+    a context can be made again once the first is shut down."""
+    say("second context refused")
+    c1 = G.gpuos_init()
+    try:
+        with pytest.raises(G.GpuosError) as e:
+            G.gpuos_init()
+        assert e.value.rc == G.GPUOS_E_STATE
+    finally:
+        assert G.gpuos_shutdown(c1) == 0
+    c2 = G.gpuos_init(num_wgs=8, waves_per_wg=1)
+    assert G.gpuos_shutdown(c2) == 0
