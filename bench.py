@@ -299,6 +299,11 @@ def make_stream(name):
         desc = ("attention decoding with grouped-query attention: 2,000 decode steps x 32 layers x {RoPE(theta 1e4), "
                 "KV append, SDPA}; B in {1,2,4,8}, 32 query heads sharing 8 key/value heads x 128, bf16 KV cache "
                 "4096/sequence, L in [128, 4096] +1 per step")
+    elif name == "decode_paged":
+        s, fill = W.make_decode(steps=2000, page_size=64), "device"
+        desc = ("attention decoding on paged KV caches: the decode stream (2,000 steps x 32 layers x {RoPE, KV "
+                "append, SDPA}, B in {1,2,4,8}, 32 heads x 128, L in [128, 4096]) with each layer's caches in pages "
+                "of 64 positions placed at random through a block table per layer")
     elif name == "matmul":
         s, fill = W.make_matmul(), "device"
         desc = ("small matmuls of batched decoding on the matrix cores: 32 tokens through the QKV (1024->3072), "
@@ -314,12 +319,12 @@ def make_stream(name):
     return s, desc, fill
 
 
-WAVES_DEFAULT = {"rows": 4, "decode": 4, "decode_gqa": 4, "copy": 4, "copy64": 4, "matmul": 4}
-UPW_DEFAULT = {"decode": 2, "decode_gqa": 2, "rows": 2}
+WAVES_DEFAULT = {"rows": 4, "decode": 4, "decode_gqa": 4, "decode_paged": 4, "copy": 4, "copy64": 4, "matmul": 4}
+UPW_DEFAULT = {"decode": 2, "decode_gqa": 2, "decode_paged": 2, "rows": 2}
 # the workloads reported beside the headline in a default run, with the
 # steps each times (the decode and mixed streams run about 1-2 s per step)
-SUB_WORKLOADS = ("pr1", "rows", "decode", "decode_gqa", "mixed", "matmul")
-SUB_STEPS = {"pr1": 20, "rows": 10, "decode": 2, "decode_gqa": 3, "mixed": 3, "matmul": 10}
+SUB_WORKLOADS = ("pr1", "rows", "decode", "decode_gqa", "decode_paged", "mixed", "matmul")
+SUB_STEPS = {"pr1": 20, "rows": 10, "decode": 2, "decode_gqa": 3, "decode_paged": 2, "mixed": 3, "matmul": 10}
 
 
 def host_cpu():

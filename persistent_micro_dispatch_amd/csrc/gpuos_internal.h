@@ -185,7 +185,8 @@ constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in reg
 #endif
 constexpr uint32_t SDPA_KT = GPUOS_SDPA_KT;  // keys per SDPA unit (fewer for small attention ops)
 constexpr uint32_t GEMV_KC = 128;          // rows of W per GEMV unit
-constexpr uint32_t MM_NB = 64;             // output columns per MATMUL unit (four 16-column tiles)
+constexpr uint32_t MM_NB = 64;             // output columns per MATMUL unit above 32 rows (four 16-column tiles)
+constexpr uint32_t MM_NB_SMALL = 128;      // ... at most 32 rows (eight tiles: x is re-read by half as many units)
 constexpr uint32_t MM_KC = 1024;           // k per MATMUL unit
 constexpr uint32_t MM_MAX_M = 64;          // rows of x (four 16-row tiles)
 constexpr uint32_t MAX_B = 8;              // batch rows with inline lengths
@@ -289,6 +290,10 @@ __host__ __device__ inline uint32_t sdpa_heads_per_unit(uint32_t H, uint32_t Hkv
     const uint32_t g = Hkv ? H / Hkv : 1u;
     return (D == 128u && g % 4u == 0u) ? 4u : 1u;
 }
+
+// output columns of a MATMUL unit: every unit reads all of x [M, K] beside
+// its slice of the weights, so at few rows wider units read x fewer times
+__host__ __device__ inline uint32_t mm_cols_per_unit(uint32_t M) { return M <= 32u ? MM_NB_SMALL : MM_NB; }
 
 // a GEMV unit covers 16 lanes x 16 bytes of columns (four rows per load)
 __host__ __device__ inline uint32_t gemv_cols_per_block(uint32_t dt) { return 16u * (16u / esz(dt)); }
@@ -398,7 +403,8 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (di != GPUOS_BF16 || M == 0 || M > MM_MAX_M || K == 0 || N == 0 || K % 32u != 0) return bad();
             if (d.a == 0 || d.b == 0 || d.out == 0) return bad();
             if ((uint64_t)MM_MAX_M * K * 2u >= (1ull << 31)) return bad();  // 32-bit buffer offsets
-            const uint64_t ncb = cdiv(N, MM_NB), nks = cdiv(K, MM_KC);
+            if ((uint64_t)mm_cols_per_unit((uint32_t)M) * K * 2u >= (1ull << 31)) return bad();
+            const uint64_t ncb = cdiv(N, mm_cols_per_unit((uint32_t)M)), nks = cdiv(K, MM_KC);
             if (ncb * nks > MAX_TILES || ncb * 4 > COUNTER_AREA) return bad();
             if (nks > 1 && nks * M * (uint64_t)N * 4u >= (1ull << 31)) return bad();  // partials in one window
             p.ntiles = (uint32_t)(ncb * nks);

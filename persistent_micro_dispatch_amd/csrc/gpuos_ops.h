@@ -1368,54 +1368,57 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
 // layer; bf16 inputs, M <= 64 (the pages' "small matmuls").  At M rows per
 // weight element the product is dense enough for the matrix cores: fp32
 // vector FMAs would cap it near 20 flop per byte of weights, while the
-// weights stream from HBM.  Unit = (block of MM_NB = 64 output columns,
-// k-split of MM_KC = 1024).  Per step of 32 k the wave loads, for each
-// 16-row tile of x and each 16-column tile of Wt, one 16-byte piece of a
-// row per lane (lane l: row l % 16, k offset 8 (l / 16)), which is the
-// operand layout of v_mfma_f32_16x16x32_bf16, and issues one MFMA per
-// (row tile, column tile) pair into fp32 accumulators (lane l holds rows
-// 4 (l / 16) + i, column l % 16 of each 16x16 tile); the next step's loads
-// are issued before the current step's MFMAs.  Rows past M and columns past
-// N read zero through the bounded windows.  With several k-splits each unit
-// writes fp32 partial tiles and the last unit of a column block adds them
-// in split order.
-template <uint32_t DTO>
+// weights stream from HBM.  Unit = (block of NB = 16 NT output columns,
+// k-split of MM_KC = 1024), with NT = 8 column tiles and MT <= 2 row tiles
+// at M <= 32 and NT = 4, MT <= 4 above (the same 16 accumulator tiles;
+// every unit reads all of x beside its weight slice, so the wider units
+// read x half as often).  Per step of 32 k the wave loads, for each 16-row
+// tile of x and each 16-column tile of Wt, one 16-byte piece of a row per
+// lane (lane l: row l % 16, k offset 8 (l / 16)), which is the operand
+// layout of v_mfma_f32_16x16x32_bf16, and issues one MFMA per (row tile,
+// column tile) pair into fp32 accumulators (lane l holds rows 4 (l / 16) +
+// i, column l % 16 of each 16x16 tile); the next step's loads are issued
+// before the current step's MFMAs.  Rows past M and columns past N read zero
+// through the bounded windows.  With several k-splits each unit writes fp32
+// partial tiles and the last unit of a column block adds them in split
+// order.
+template <uint32_t DTO, uint32_t MTMAX, uint32_t NT>
 __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
+    constexpr uint32_t NB = 16u * NT;
     const uint32_t M = (uint32_t)u.size, K = u.dim[0], N = u.dim[1];
-    const uint32_t ncb = (N + MM_NB - 1) / MM_NB, nks = (K + MM_KC - 1) / MM_KC;
+    const uint32_t ncb = (N + NB - 1) / NB, nks = (K + MM_KC - 1) / MM_KC;
     const uint32_t cb = u.tile % ncb, ks = u.tile / ncb;
     const uint32_t kb = ks * MM_KC, kn = min(K - kb, MM_KC);  // a multiple of 32
     const uint32_t MT = (M + 15u) / 16u;                       // row tiles in use (wave-uniform)
     const uint32_t r16 = lane % 16u, kg = lane / 16u;
-    const uint32_t ncol = min(N - cb * MM_NB, MM_NB);
+    const uint32_t ncol = min(N - cb * NB, NB);
     const RBuf rx = rbuf((const uint8_t*)u.a, M * K * 2u);
-    const RBuf rw = rbuf((const uint8_t*)u.b + (uint64_t)cb * MM_NB * K * 2u, ncol * K * 2u);
-    f32x4 acc[4][4];
+    const RBuf rw = rbuf((const uint8_t*)u.b + (uint64_t)cb * NB * K * 2u, ncol * K * 2u);
+    f32x4 acc[MTMAX][NT];
 #pragma unroll
-    for (uint32_t mt = 0; mt < 4; ++mt)
+    for (uint32_t mt = 0; mt < MTMAX; ++mt)
 #pragma unroll
-        for (uint32_t nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (uint32_t nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     auto load = [&](u32x4* xv, u32x4* wv, uint32_t st) {
         const uint32_t k = kb + st * 32u + kg * 8u;
 #pragma unroll
-        for (uint32_t t = 0; t < 4; ++t) {
-            xv[t] = rld16(rx, ((t * 16u + r16) * K + k) * 2u);   // rows past M: outside the window
-            wv[t] = rld16s(rw, ((t * 16u + r16) * K + k) * 2u);  // columns past N: likewise
-        }
+        for (uint32_t t = 0; t < MTMAX; ++t) xv[t] = rld16(rx, ((t * 16u + r16) * K + k) * 2u);   // rows past M: outside the window
+#pragma unroll
+        for (uint32_t t = 0; t < NT; ++t) wv[t] = rld16s(rw, ((t * 16u + r16) * K + k) * 2u);  // columns past N: likewise
     };
     auto mma = [&](const u32x4* xv, const u32x4* wv) {
 #pragma unroll
-        for (uint32_t mt = 0; mt < 4; ++mt) {
+        for (uint32_t mt = 0; mt < MTMAX; ++mt) {
             if (mt >= MT) break;
 #pragma unroll
-            for (uint32_t nt = 0; nt < 4; ++nt)
+            for (uint32_t nt = 0; nt < NT; ++nt)
                 acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[mt]),
                                                                       __builtin_bit_cast(bf16x8, wv[nt]),
                                                                       acc[mt][nt], 0, 0, 0);
         }
     };
     const uint32_t nst = kn / 32u;
-    u32x4 xa[4], wa[4], xb[4], wb[4];
+    u32x4 xa[MTMAX], wa[NT], xb[MTMAX], wb[NT];
     load(xa, wa, 0);
     for (uint32_t st = 0; st < nst; st += 2) {
         if (st + 1 < nst) load(xb, wb, st + 1);
@@ -1430,11 +1433,11 @@ __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
     uint8_t* Y = (uint8_t*)u.out;
     float* part = (float*)(u.scratch + COUNTER_AREA);
 #pragma unroll
-    for (uint32_t mt = 0; mt < 4; ++mt) {
+    for (uint32_t mt = 0; mt < MTMAX; ++mt) {
         if (mt >= MT) break;
 #pragma unroll
-        for (uint32_t nt = 0; nt < 4; ++nt) {
-            const uint32_t n = cb * MM_NB + nt * 16u + r16;
+        for (uint32_t nt = 0; nt < NT; ++nt) {
+            const uint32_t n = cb * NB + nt * 16u + r16;
 #pragma unroll
             for (uint32_t i = 0; i < 4; ++i) {
                 const uint32_t m = mt * 16u + kg * 4u + i;
@@ -1452,37 +1455,41 @@ __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
     if (lane == 0) prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     prev = (uint32_t)__builtin_amdgcn_readlane((int)prev, 0);
     if (prev != nks - 1) return;
-    // merge: lane c owns column cb * MM_NB + c and adds its M rows over the
-    // splits in split order; the loads of 8 rows x 8 splits are in flight at
-    // once (the row loop does not wait for one row's loads before the next)
-    const uint32_t col = cb * MM_NB + lane;
+    // merge: lane c owns columns cb * NB + c + 64 g and adds their M rows
+    // over the splits in split order; the loads of 8 rows x 8 splits are in
+    // flight at once (the row loop does not wait for one row's loads before
+    // the next)
     constexpr uint32_t MR = 8, MS = 8;
     const RBuf rp = rbuf(part, (uint32_t)((uint64_t)nks * M * N * 4u));
-    for (uint32_t m0 = 0; m0 < M; m0 += MR) {
-        float sm[MR];
+#pragma unroll 1
+    for (uint32_t cg = 0; cg < NB / 64u; ++cg) {
+        const uint32_t col = cb * NB + cg * 64u + lane;
+        for (uint32_t m0 = 0; m0 < M; m0 += MR) {
+            float sm[MR];
 #pragma unroll
-        for (uint32_t i = 0; i < MR; ++i) sm[i] = 0.0f;
-        for (uint32_t k0 = 0; k0 < nks; k0 += MS) {
-            float pv[MR][MS];
+            for (uint32_t i = 0; i < MR; ++i) sm[i] = 0.0f;
+            for (uint32_t k0 = 0; k0 < nks; k0 += MS) {
+                float pv[MR][MS];
+#pragma unroll
+                for (uint32_t i = 0; i < MR; ++i)
+#pragma unroll
+                    for (uint32_t k = 0; k < MS; ++k) {
+                        // splits past nks, rows past M and columns past N are
+                        // sent outside the window (reads zero, never added)
+                        const bool in = k0 + k < nks && m0 + i < M && col < N;
+                        pv[i][k] = __uint_as_float(rld4(rp, in ? (uint32_t)((((uint64_t)(k0 + k) * M + m0 + i) * N + col) * 4u)
+                                                              : 0xFFFFFFF0u));
+                    }
+#pragma unroll
+                for (uint32_t i = 0; i < MR; ++i)
+#pragma unroll
+                    for (uint32_t k = 0; k < MS; ++k)
+                        if (k0 + k < nks) sm[i] += pv[i][k];
+            }
 #pragma unroll
             for (uint32_t i = 0; i < MR; ++i)
-#pragma unroll
-                for (uint32_t k = 0; k < MS; ++k) {
-                    // splits past nks, rows past M and columns past N are
-                    // sent outside the window (reads zero, never added)
-                    const bool in = k0 + k < nks && m0 + i < M && col < N;
-                    pv[i][k] = __uint_as_float(rld4(rp, in ? (uint32_t)((((uint64_t)(k0 + k) * M + m0 + i) * N + col) * 4u)
-                                                          : 0xFFFFFFF0u));
-                }
-#pragma unroll
-            for (uint32_t i = 0; i < MR; ++i)
-#pragma unroll
-                for (uint32_t k = 0; k < MS; ++k)
-                    if (k0 + k < nks) sm[i] += pv[i][k];
+                if (m0 + i < M && col < N) st_elem<DTO>(Y, (uint64_t)(m0 + i) * N + col, sm[i]);
         }
-#pragma unroll
-        for (uint32_t i = 0; i < MR; ++i)
-            if (m0 + i < M && col < N) st_elem<DTO>(Y, (uint64_t)(m0 + i) * N + col, sm[i]);
     }
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1564,7 +1571,10 @@ __device__ __forceinline__ void run_unit(const Unit& u, uint32_t lane) {
             else dout == GPUOS_F32 ? gemv_tile<GPUOS_F32, GPUOS_F32>(u, lane) : gemv_tile<GPUOS_F32, GPUOS_BF16>(u, lane);
             break;
         case GPUOS_OP_COPY: copy_tile(u, lane); break;
-        case GPUOS_OP_MATMUL: dout == GPUOS_F32 ? matmul_tile<GPUOS_F32>(u, lane) : matmul_tile<GPUOS_BF16>(u, lane); break;
+        case GPUOS_OP_MATMUL:
+            if (u.size <= 32u) dout == GPUOS_F32 ? matmul_tile<GPUOS_F32, 2, 8>(u, lane) : matmul_tile<GPUOS_BF16, 2, 8>(u, lane);
+            else dout == GPUOS_F32 ? matmul_tile<GPUOS_F32, 4, 4>(u, lane) : matmul_tile<GPUOS_BF16, 4, 4>(u, lane);
+            break;
         default: break;
     }
 }

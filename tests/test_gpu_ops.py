@@ -371,7 +371,7 @@ def test_matmul(ctx, out_dt):
     say(f"matmul out={out_dt}")
     recs, arrays = [], []
     for M, K, N in [(1, 1024, 3072), (16, 1024, 3072), (33, 3072, 1024), (64, 256, 100), (7, 32, 17),
-                    (64, 4096, 64), (2, 1056, 300), (48, 512, 1000)]:
+                    (64, 4096, 64), (2, 1056, 300), (48, 512, 1000), (32, 3072, 1000), (32, 2048, 130)]:
         x = bf16(RNG.standard_normal(M * K))
         wt = bf16(0.05 * RNG.standard_normal(N * K))
         y = np.zeros(M * N, np.float32 if out_dt == W.F32 else np.uint16)
