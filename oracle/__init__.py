@@ -16,7 +16,9 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gpuos_oracle.c")
-LIB = os.path.join(HERE, "liboracle.so")
+# GPUOS_ORACLE_LIB names another build of the same source (the sanitizer
+# test loads an AddressSanitizer build this way)
+LIB = os.environ.get("GPUOS_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 
 _lib = None
 
@@ -35,7 +37,8 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        if "GPUOS_ORACLE_LIB" not in os.environ and (not os.path.exists(LIB) or
+                                                     os.path.getmtime(LIB) < os.path.getmtime(SRC)):
             build(force=True)
         L = ctypes.CDLL(LIB)
         L.orc_run.restype = ctypes.c_int64
