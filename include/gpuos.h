@@ -202,6 +202,13 @@ typedef struct gpuos_init_params {
                                    its dependencies (helps streams of long bodies, such
                                    as decode attention), but each wave holds two claims
                                    (slower on long dependency chains of short ops) */
+    uint32_t idle_exit_ms;      /* 0: the executor stays resident until gpuos_pause or
+                                   gpuos_shutdown.  Else it leaves the GPU once no
+                                   descriptor is committed and no call of this context
+                                   (each one is a heartbeat) has come for this long, so
+                                   that a host that stops (hangs, waits elsewhere)
+                                   does not hold the CUs; the next submit, sync or
+                                   query launches it again */
 } gpuos_init_params;
 
 /* Allocate the ring (fine-grained coherent host memory), the device tables
@@ -401,6 +408,7 @@ typedef struct gpuos_stats {
     uint64_t ns_submit;          /* host time spent inside gpuos_submit */
     uint64_t ns_blocked;         /*   of which waiting for free ring slots (BLOCK) */
     uint64_t ns_annotate;        /*   of which annotating and writing descriptors */
+    uint64_t idle_exits;         /* executor launches that ended for lack of heartbeat */
 } gpuos_stats;
 
 /* Snapshot of the counters.  Device counters are added up when a launch

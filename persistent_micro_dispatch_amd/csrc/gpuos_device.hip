@@ -390,12 +390,16 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     // memory system nothing, so its backoff stops early: a descriptor
     // committed to an idle ring is seen sooner
     const uint32_t fcap = A.backoff_max < FETCH_BACKOFF_MAX ? A.backoff_max : FETCH_BACKOFF_MAX;
+    // idle exit: the heartbeat last seen, and when it (or work) last changed
+    uint64_t hb_seen = 0, hb_t = wall_clock64();
+    bool worked = false;
     for (;;) {
-        // the stamps and both control words in one round trip over PCIe
+        // the stamps and the control words in one round trip over PCIe
         const uint64_t sl = f + lane;
         const uint64_t st = ld_sys(&A.stamp[sl & mask]);
         const uint64_t abt = ld_sys(&A.hctl->abort);
         const uint64_t stp = ld_sys(&A.hctl->stop);
+        const uint64_t hb = A.idle_exit_ticks ? ld_sys(&A.hctl->heartbeat) : 0;
         const uint64_t rb = __ballot(st == sl + 1);
         uint32_t count = rb == ~0ull ? 64u : (uint32_t)(__ffsll((long long)~rb) - 1);
         if (count == 0) {
@@ -405,11 +409,26 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
                 if (ld_sys(&A.stamp[f & mask]) == f + 1) continue;
                 break;
             }
+            if (A.idle_exit_ticks) {
+                const uint64_t now = wall_clock64();
+                if (hb != hb_seen || worked) {
+                    hb_seen = hb;
+                    hb_t = now;
+                    worked = false;
+                } else if (now - hb_t > A.idle_exit_ticks) {
+                    // no work and no call for the whole interval: look once
+                    // more, then leave (the host relaunches from fetch_end)
+                    if (ld_sys(&A.stamp[f & mask]) == f + 1) continue;
+                    if (lane == 0) st_sys(&A.hctl->idle_exit, 1ull);
+                    break;
+                }
+            }
             nap(bo);
             bo = bo * 2 < fcap ? bo * 2 : fcap;
             continue;
         }
         bo = 1;
+        worked = true;
         // read the committed bodies (count x 16 words) in one go
         const uint32_t nw = count * 16u;
         uint64_t v[16];
@@ -587,6 +606,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if (lane == 0) {
+        st_sys(&A.hctl->fetch_end, f);
         st_agent(&C->stop, stop_code);
         __hip_atomic_fetch_add(&C->stat_batches, batches, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_fetch_add(&C->stat_fetched, fetched, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

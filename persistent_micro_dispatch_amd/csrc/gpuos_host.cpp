@@ -246,6 +246,8 @@ struct gpuos_ctx {
     bool own_exec = false;
     hipEvent_t ev_start = nullptr, ev_stop = nullptr;
     uint64_t spin_ticks = 0;
+    uint64_t idle_ticks = 0;   // idle exit after this many wall-clock ticks (0: never)
+    uint64_t idle_exits = 0;
     // producer state
     std::mutex mu;
     uint64_t next_seq = 0;
@@ -304,13 +306,24 @@ void refresh_wm(gpuos_ctx* c) {
     }
 }
 
+void executor_finished(gpuos_ctx* c);
+
+// Every call of a context is a heartbeat: an executor with an idle-exit
+// interval leaves the GPU only when none has come for that long.
+void beat(gpuos_ctx* c) { __atomic_fetch_add(&c->hctl->heartbeat, 1ull, __ATOMIC_RELEASE); }
+
+// A launch starts fetching where the previous one stopped: after a host
+// stop that is every committed descriptor; after an idle exit the host may
+// have committed more since the fetcher's last look.
 int executor_launch(gpuos_ctx* c) {
     if (c->loopback || c->running) return GPUOS_OK;
     hipError_t e = hipMemsetAsync(c->dctl, 0, sizeof(DevCtl), c->exec);
     if (e != hipSuccess) return GPUOS_E_HIP;
+    const uint64_t start = ld_acq(&c->hctl->fetch_end);
     st_rel(&c->hctl->stop, (uint64_t)0);
     st_rel(&c->hctl->abort, (uint64_t)0);
     st_rel(&c->hctl->exited, (uint64_t)0);
+    st_rel(&c->hctl->idle_exit, (uint64_t)0);
     ExecArgs a{};
     a.ring = c->ring;
     a.depx = c->depx;
@@ -329,8 +342,9 @@ int executor_launch(gpuos_ctx* c) {
     a.scratch_bytes = c->P.scratch_bytes;
     a.trace = c->trace;
     a.trace_cap = c->trace_cap;
-    a.start_seq = c->next_seq;
+    a.start_seq = start;
     a.spin_limit_ticks = c->spin_ticks;
+    a.idle_exit_ticks = c->idle_ticks;
     a.mask = c->mask;
     a.qmask = c->Q - 1;
     a.backoff_max = c->P.backoff_max;
@@ -365,6 +379,12 @@ int executor_stop(gpuos_ctx* c, int64_t timeout_ns) {
         if (aborted && el > (uint64_t)timeout_ns + 5000000000ull) return GPUOS_E_TIMEOUT;
         std::this_thread::sleep_for(std::chrono::microseconds(20));
     }
+    executor_finished(c);
+    return aborted ? GPUOS_E_TIMEOUT : GPUOS_OK;
+}
+
+// The launch has ended: its duration and device counters.
+void executor_finished(gpuos_ctx* c) {
     float ms = 0.f;
     if (hipEventElapsedTime(&ms, c->ev_start, c->ev_stop) == hipSuccess) {
         c->last_ms = ms;
@@ -379,7 +399,19 @@ int executor_stop(gpuos_ctx* c, int64_t timeout_ns) {
         c->acc_batches += d.stat_batches;
         c->acc_fetched += d.stat_fetched;
     }
-    return aborted ? GPUOS_E_TIMEOUT : GPUOS_OK;
+}
+
+// An executor with an idle-exit interval may have left by itself: account
+// for the launch and, when descriptors are waiting (`pending`), launch again
+// from where its fetcher stopped.  Caller holds c->mu.
+int revive(gpuos_ctx* c, bool pending) {
+    if (c->loopback || !c->idle_ticks) return GPUOS_OK;
+    if (c->running) {
+        if (hipEventQuery(c->ev_stop) != hipSuccess || !ld_acq(&c->hctl->idle_exit)) return GPUOS_OK;
+        executor_finished(c);
+        ++c->idle_exits;
+    }
+    return pending ? executor_launch(c) : GPUOS_OK;
 }
 
 // ---- loopback consumer (test only): completes descriptors in a random order
@@ -577,6 +609,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     if (hipDeviceGetAttribute(&wclk, hipDeviceAttributeWallClockRate, P.device) != hipSuccess || wclk <= 0)
         wclk = 100000;  // kHz
     c->spin_ticks = (uint64_t)P.spin_limit_ms * (uint64_t)wclk;
+    c->idle_ticks = (uint64_t)P.idle_exit_ms * (uint64_t)wclk;
     const unsigned hflags = hipHostMallocCoherent | hipHostMallocMapped;
     HIPCHK(hipHostMalloc((void**)&c->ring, N * sizeof(gpuos_desc), hflags));
     HIPCHK(hipHostMalloc((void**)&c->depx, N * 8 * DEPX_WORDS, hflags));
@@ -587,6 +620,7 @@ int gpuos_init(const gpuos_init_params* params, void** out) {
     memset(c->depx, 0, N * 8 * DEPX_WORDS);
     memset(c->status, 0, N * 4);
     memset(c->hctl, 0, sizeof(HostCtl));
+    c->hctl->fetch_end = c->next_seq;  // the first launch fetches from the first seq
     for (size_t i = 0; i < N; ++i) c->stamp[i] = N + i;
     HIPCHK(hipMalloc((void**)&c->dctl, sizeof(DevCtl)));
     HIPCHK(hipMalloc((void**)&c->mirror, N * sizeof(gpuos_desc)));
@@ -645,6 +679,8 @@ static int table_flip(gpuos_ctx* c, uint32_t op_id, TableEntry te, const uint32_
     for (;;) {
         refresh_wm(c);
         if (c->wm >= c->flip_seq) break;
+        beat(c);
+        if (const int rr = revive(c, true)) return rr;
         if (now_ns() - t0 > 60000000000ull) return GPUOS_E_TIMEOUT;
         GPUOS_PAUSE();
     }
@@ -797,6 +833,8 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
         }
         kinds[i] = kind;
     }
+    beat(c);
+    if (const int rr = revive(c, false)) return rr;
     if (!c->running && !c->loopback) {
         int rc = executor_launch(c);
         if (rc) return rc;
@@ -808,8 +846,13 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
         const uint64_t tb = now_ns();
         while (c->wm < upto) {
             if (c->hctl && ld_acq(&c->hctl->dev_error)) return GPUOS_E_DEVICE;
-            if (++spins > 1000) std::this_thread::yield();
-            else GPUOS_PAUSE();
+            if (++spins > 1000) {
+                std::this_thread::yield();
+                beat(c);
+                if (const int rr = revive(c, true)) return rr;
+            } else {
+                GPUOS_PAUSE();
+            }
             refresh_wm(c);
         }
         c->ns_blocked += now_ns() - tb;
@@ -907,8 +950,11 @@ int gpuos_submit(void* ctx, const gpuos_desc* descs, uint32_t count, uint32_t fl
     c->next_seq += count;
     c->submitted += count;
     c->ns_hazard += t_hz1 - t_hz0;
+    // an executor that left for lack of heartbeat just before this commit
+    // became visible would not see it: launch again from its stopping point
+    const int rr = revive(c, true);
     c->ns_submit += now_ns() - t_enter;
-    return GPUOS_OK;
+    return rr;
 }
 
 int gpuos_submit_bursts(void* ctx, const gpuos_desc* descs, const uint32_t* burst_sizes, uint32_t n_bursts,
@@ -937,7 +983,9 @@ int gpuos_query(void* ctx, uint64_t seq) {
     gpuos_ctx* c = (gpuos_ctx*)ctx;
     if (!c) return GPUOS_E_INVAL;
     std::lock_guard<std::mutex> g(c->mu);
+    beat(c);
     refresh_wm(c);
+    if (const int rr = revive(c, c->wm < c->next_seq)) return rr;
     return seq < c->wm ? 1 : 0;
 }
 
@@ -962,6 +1010,8 @@ int gpuos_sync(void* ctx, uint64_t upto, int64_t timeout_ns, uint64_t* err_seq, 
                 }
                 return GPUOS_OK;
             }
+            beat(c);
+            if (const int rr = revive(c, true)) return rr;  // an idle exit: launched again
             if (!c->loopback && c->running && hipEventQuery(c->ev_stop) == hipSuccess) {
                 // the executor exited with work outstanding
                 return GPUOS_E_DEVICE;
@@ -1010,8 +1060,10 @@ int gpuos_stats_get(void* ctx, gpuos_stats* out) {
     gpuos_ctx* c = (gpuos_ctx*)ctx;
     if (!c || !out) return GPUOS_E_INVAL;
     std::lock_guard<std::mutex> g(c->mu);
+    beat(c);
     refresh_wm(c);
     memset(out, 0, sizeof(*out));
+    out->idle_exits = c->idle_exits;
     out->submitted = c->submitted;
     out->completed = c->completed;
     out->full_rejections = c->full_rej;

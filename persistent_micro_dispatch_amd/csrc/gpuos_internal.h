@@ -56,6 +56,9 @@ struct HostCtl {
     alignas(64) uint64_t abort;      // host -> device: exit at once
     alignas(64) uint64_t dev_error;  // device -> host: sticky error code
     alignas(64) uint64_t exited;     // device -> host: number of waves that left
+    alignas(64) uint64_t heartbeat;  // host -> device: bumped by every call of the context
+    alignas(64) uint64_t fetch_end;  // device -> host: first seq the fetcher did not take
+    alignas(64) uint64_t idle_exit;  // device -> host: 1 if the launch ended for lack of heartbeat
 };
 
 // Control words in device memory (one 128-byte line each).
@@ -138,6 +141,7 @@ struct ExecArgs {
     uint64_t trace_cap;         // records (power of two)
     uint64_t start_seq;
     uint64_t spin_limit_ticks;  // in wall-clock ticks
+    uint64_t idle_exit_ticks;   // 0, or leave after this long without heartbeat or work
     uint32_t mask;              // ring_entries - 1
     uint32_t qmask;             // unit-queue entries - 1
     uint32_t backoff_max;

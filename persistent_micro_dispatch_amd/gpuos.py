@@ -89,7 +89,7 @@ class InitParams(ctypes.Structure):
                 ("backoff_max", ctypes.c_uint32), ("flags", ctypes.c_uint32),
                 ("hip_stream", ctypes.c_void_p), ("scratch_bytes", ctypes.c_uint64),
                 ("unit_queue_log2", ctypes.c_uint32), ("spin_limit_ms", ctypes.c_uint32),
-                ("units_per_wave", ctypes.c_uint32)]
+                ("units_per_wave", ctypes.c_uint32), ("idle_exit_ms", ctypes.c_uint32)]
 
 
 class Stats(ctypes.Structure):
@@ -102,7 +102,8 @@ class Stats(ctypes.Structure):
                 ("ring_entries", ctypes.c_uint32), ("cu_count", ctypes.c_uint32),
                 ("next_seq", ctypes.c_uint64), ("deps_explicit", ctypes.c_uint64),
                 ("deps_range", ctypes.c_uint64), ("ns_submit", ctypes.c_uint64),
-                ("ns_blocked", ctypes.c_uint64), ("ns_annotate", ctypes.c_uint64)]
+                ("ns_blocked", ctypes.c_uint64), ("ns_annotate", ctypes.c_uint64),
+                ("idle_exits", ctypes.c_uint64)]
 
 
 _lib = None
@@ -216,9 +217,11 @@ atexit.register(_shutdown_live)
 
 def gpuos_init(device: int = 0, ring_entries: int = 0, num_wgs: int = 0, waves_per_wg: int = 0,
                backoff_max: int = 0, flags: int = 0, hip_stream: int = 0, scratch_bytes: int = 0,
-               unit_queue_log2: int = 0, spin_limit_ms: int = 0, units_per_wave: int = 0) -> int:
+               unit_queue_log2: int = 0, spin_limit_ms: int = 0, units_per_wave: int = 0,
+               idle_exit_ms: int = 0) -> int:
     p = InitParams(device, ring_entries, num_wgs, waves_per_wg, backoff_max, flags,
-                   hip_stream or None, scratch_bytes, unit_queue_log2, spin_limit_ms, units_per_wave)
+                   hip_stream or None, scratch_bytes, unit_queue_log2, spin_limit_ms, units_per_wave,
+                   idle_exit_ms)
     out = ctypes.c_void_p()
     _check("gpuos_init", lib().gpuos_init(ctypes.byref(p), ctypes.byref(out)))
     _LIVE.add(out.value)

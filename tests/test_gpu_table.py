@@ -222,3 +222,39 @@ def test_second_live_context_on_a_device_is_refused():
         assert G.gpuos_shutdown(c1) == 0
     c2 = G.gpuos_init(num_wgs=8, waves_per_wg=1)
     assert G.gpuos_shutdown(c2) == 0
+
+
+def test_idle_exit_and_relaunch():
+    """With an idle-exit interval the executor leaves the GPU once nothing is
+    committed and no call of the context has come for that long; the next
+    call that has work for it launches it again from where its fetcher
+    stopped, and the stream's results are unchanged.  Calls keep it
+    resident."""
+    import time
+    s = W.make_elementwise(n_desc=2000, ops=(W.OP_ADD, W.OP_MUL, W.OP_RELU))
+    arrays = [b.host_bytes() for b in s.buffers]
+    pool = DevicePool(arrays)
+    descs = to_descs(s.recs, pool.ptrs)
+    say("idle exit and relaunch, 2000 descriptors, 50 ms interval")
+    ctx = G.gpuos_init(ring_entries=256, idle_exit_ms=50)
+    try:
+        for i in range(0, 1000, 250):
+            assert G.gpuos_submit(ctx, descs[i:i + 250], G.GPUOS_SUBMIT_BLOCK)[0] == 0
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, SYNC_NS)[0] == 0
+        # calls every 10 ms for 0.3 s: the executor stays
+        for _ in range(30):
+            assert G.gpuos_query(ctx, 0) >= 0
+            time.sleep(0.01)
+        assert G.gpuos_stats_get(ctx)["idle_exits"] == 0
+        time.sleep(0.5)  # no call: it leaves
+        assert G.gpuos_query(ctx, 0) >= 0
+        st = G.gpuos_stats_get(ctx)
+        assert st["idle_exits"] == 1 and st["launches"] == 1, st
+        for i in range(1000, 2000, 250):
+            assert G.gpuos_submit(ctx, descs[i:i + 250], G.GPUOS_SUBMIT_BLOCK)[0] == 0
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, SYNC_NS)[0] == 0
+        st = G.gpuos_stats_get(ctx)
+        assert st["launches"] == 2 and st["completed"] == 2000, st
+    finally:
+        assert G.gpuos_shutdown(ctx) == 0
+    _assert_pool_equal(pool, _oracle_final(arrays, s.recs), s.buffers)
