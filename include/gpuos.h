@@ -140,7 +140,7 @@ enum gpuos_kind {
  *                   j % PS (the usual paged-attention layout).  size = B in
  *                   the low 32 bits and P in the high 32 bits; dim[2] = PS, a
  *                   power of two from 64 to 1024; param.u[5] = MP (lens[b] at
- *                   most MP * PS, and for SDPA at most 64 * PS).  The table
+ *                   most MP * PS).  The table
  *                   is in aux[2] for KV_APPEND and in b for SDPA (whose
  *                   mask, with GPUOS_F_SDPA_MASK, stays in aux[2], [B, MP *
  *                   PS]).  A table entry outside [0, P) writes nothing (append)

@@ -272,19 +272,15 @@ __host__ __device__ inline uint32_t sdpa_keys_per_unit(uint32_t B, uint32_t H, c
 
 // Paged caches (GPUOS_F_KV_PAGED): `size` carries the batch rows in its low
 // 32 bits and the pool's page count in its high 32 bits; pages hold a power
-// of two of positions, 64 to 1024, so that an attention unit (at most 1024
-// keys, halved in powers of two) never spans two pages.
+// of two of positions, 64 to 1024, so that a page holds a whole number of an
+// attention unit's chunks of keys (32 or 64) and a unit spans at most 16
+// pages.
 __host__ __device__ inline bool kv_paged(uint32_t flags) { return (flags & GPUOS_F_KV_PAGED) != 0u; }
 __host__ __device__ inline uint64_t kv_rows(uint64_t size, uint32_t flags) {
     return kv_paged(flags) ? (size & 0xFFFFFFFFull) : size;
 }
 __host__ __device__ inline uint64_t kv_pages(uint64_t size) { return size >> 32; }
 __host__ __device__ inline bool page_size_ok(uint32_t ps) { return ps >= 64u && ps <= 1024u && (ps & (ps - 1u)) == 0u; }
-__host__ __device__ inline uint32_t sdpa_unit_keys(uint32_t B, uint32_t H, const uint64_t* lensw, uint32_t flags,
-                                                   uint32_t ps) {
-    const uint32_t kt = sdpa_keys_per_unit(B, H, lensw);
-    return kv_paged(flags) && ps < kt ? ps : kt;
-}
 
 // Query heads per SDPA unit: under grouped-query attention the query heads
 // of a group share their key/value rows, so with D = 128 and groups of a
@@ -373,7 +369,7 @@ __host__ __device__ inline Plan make_plan(const PlanIn& d) {
             if (d.a == 0 || d.out == 0 || d.aux0 == 0 || d.aux1 == 0) return bad();
             if ((d.flags & GPUOS_F_SDPA_MASK) && d.aux2 == 0) return bad();
             if (paged && (!page_size_ok(d.dim[2]) || kv_pages(d.size) == 0 || d.b == 0)) return bad();
-            const uint32_t kt = sdpa_unit_keys((uint32_t)B, H, d.lensw, d.flags, d.dim[2]);
+            const uint32_t kt = sdpa_keys_per_unit((uint32_t)B, H, d.lensw);
             uint64_t units = 0;
             bool split = false;
             for (uint32_t i = 0; i < B; ++i) {

@@ -951,7 +951,7 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     const uint32_t C = paged ? MP * PS : u.dim[2];  // positions per batch row
     const uint32_t Hkv = u.dim[3] ? u.dim[3] : H;
     const uint32_t Bn = (uint32_t)u.size;
-    const uint32_t kt = sdpa_unit_keys(Bn, H, u.lensw, u.flags, PS);
+    const uint32_t kt = sdpa_keys_per_unit(Bn, H, u.lensw);
     const uint32_t HG = H / GP;  // units per (b, split): groups of GP query heads
     // unit -> (b, head group, split); mbase numbers the per-head splits of
     // earlier batch rows (the partial records and counters are per head)
@@ -969,21 +969,19 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     const uint32_t h0 = hg * GP;  // the unit's first query head; all GP share a key/value head
     const uint64_t bkv = (uint64_t)b * Hkv + h0 / (H / Hkv);
     const uint32_t k0 = sp * kt;
-    uint32_t nk = min(L - k0, kt);
+    const uint32_t nk = min(L - k0, kt);
     const float scale = u.pf[4] != 0.0f ? u.pf[4] : (u.p0 != 0.0f ? u.p0 : 1.0f / sqrtf((float)D));
     const float sl2 = scale * 1.4426950408889634f;  // scores in the log2 domain
     const uint32_t g = lane / DV, c = lane % DV;
-    // the unit's keys: a stretch of one (b, key/value head) row, or of one
-    // page (units never span two pages); a page outside the pool drops them
-    uint64_t kbase = (bkv * C + k0) * D * 2u;
-    if (paged) {
-        const uint32_t pg = ld4((const uint8_t*)u.b + ((uint64_t)b * MP + k0 / PS) * 4u);
-        const uint64_t hkv = bkv - (uint64_t)b * Hkv;
-        kbase = (((uint64_t)pg * Hkv + hkv) * PS + k0 % PS) * D * 2u;
-        if ((uint64_t)pg >= kv_pages(u.size)) nk = 0;
-    }
-    const RBuf rk = rbuf((const uint8_t*)u.aux0 + kbase, nk * D * 2u);
-    const RBuf rv = rbuf((const uint8_t*)u.aux1 + kbase, nk * D * 2u);
+    // the unit's keys: a stretch of one (b, key/value head) row; or, with
+    // paged caches, of up to kt / PS pages, whose numbers lane i holds (page
+    // k0 / PS + i of the row) and each chunk of keys (one page holds a
+    // whole number of chunks) reads through its page's window
+    const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bkv * C + k0) * D * 2u, paged ? 0u : nk * D * 2u);
+    const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bkv * C + k0) * D * 2u, paged ? 0u : nk * D * 2u);
+    const uint64_t hkv = bkv - (uint64_t)b * Hkv, NP = kv_pages(u.size);
+    uint32_t ptab = 0;
+    if (paged && lane < (nk + PS - 1) / PS) ptab = ld4((const uint8_t*)u.b + ((uint64_t)b * MP + k0 / PS + lane) * 4u);
     const bool masked = (u.flags & GPUOS_F_SDPA_MASK) != 0u;
     const RBuf rm = rbuf((const uint8_t*)u.aux2 + ((uint64_t)b * C + k0) * 4u, masked ? nk * 4u : 0u);
     bf16x2 qv[GP][4];
@@ -1002,19 +1000,34 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
         for (int e = 0; e < 8; ++e) acc[gi][e] = 0.0f;
     }
     const uint32_t nch = (nk + CK - 1) / CK;
-    auto load = [&](u32x4* kv, u32x4* vv, float* mk, uint32_t ci) {
+    // returns false for a chunk on a page outside the pool (its keys drop out)
+    auto load = [&](u32x4* kv, u32x4* vv, float* mk, uint32_t ci) -> bool {
+        RBuf ck = rk, cv = rv;
+        uint32_t cbase = ci * CK * D * 2u;
+        bool live = true;
+        if (paged) {
+            const uint32_t key0 = k0 + ci * CK;  // chunks past the unit read nothing
+            const uint32_t pg = (uint32_t)__builtin_amdgcn_readlane((int)ptab, (int)((key0 / PS - k0 / PS) & 63u));
+            live = pg < NP;
+            const uint32_t keys = ci < nch && live ? min(CK, nk - ci * CK) : 0u;
+            const uint64_t at = (((uint64_t)pg * Hkv + hkv) * PS + key0 % PS) * D * 2u;
+            ck = rbuf((const uint8_t*)u.aux0 + at, keys * D * 2u);
+            cv = rbuf((const uint8_t*)u.aux1 + at, keys * D * 2u);
+            cbase = 0;
+        }
 #pragma unroll
         for (uint32_t j = 0; j < NI; ++j) {
-            const uint32_t off = ((ci * CK + j * RPI + g) * D) * 2u + c * 16u;
-            kv[j] = rld16s(rk, off);
-            vv[j] = rld16s(rv, off);
+            const uint32_t off = cbase + ((j * RPI + g) * D) * 2u + c * 16u;
+            kv[j] = rld16s(ck, off);
+            vv[j] = rld16s(cv, off);
         }
         if (masked) {
 #pragma unroll
             for (uint32_t j = 0; j < NI; ++j) mk[j] = __uint_as_float(rld4(rm, (ci * CK + j * RPI + g) * 4u));
         }
+        return live;
     };
-    auto consume = [&](const u32x4* kv, const u32x4* vv, const float* mk, uint32_t ci) {
+    auto consume = [&](const u32x4* kv, const u32x4* vv, const float* mk, uint32_t ci, bool live) {
         float s[GP][NI];
         float mn[GP];
 #pragma unroll
@@ -1029,7 +1042,7 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
                 d = __builtin_amdgcn_fdot2_f32_bf16(qv[gi][3], as_bf2(kv[j].w), d, false);
                 d = gred<DV>(d, OpAdd{}) * sl2;
                 if (masked) d += mk[j] * 1.4426950408889634f;  // the mask, in the log2 domain too
-                const bool valid = ci * CK + j * RPI + g < nk;
+                const bool valid = live && ci * CK + j * RPI + g < nk;
                 s[gi][j] = valid ? d : -INFINITY;
                 cm = fmaxf(cm, s[gi][j]);
             }
@@ -1065,15 +1078,15 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     // loads below the use of the current one (it would to save registers).
     u32x4 ka[NI], va[NI], kb[NI], vb[NI];
     float ma[NI], mb[NI];
-    load(ka, va, ma, 0);
+    bool la = load(ka, va, ma, 0), lb = true;
     for (uint32_t ci = 0; ci < nch; ci += 2) {
-        load(kb, vb, mb, ci + 1);  // past the last chunk: outside the window, reads nothing
+        lb = load(kb, vb, mb, ci + 1);  // past the last chunk: outside the window, reads nothing
         __builtin_amdgcn_sched_barrier(0);
-        consume(ka, va, ma, ci);
+        consume(ka, va, ma, ci, la);
         if (ci + 1 < nch) {
-            load(ka, va, ma, ci + 2);
+            la = load(ka, va, ma, ci + 2);
             __builtin_amdgcn_sched_barrier(0);
-            consume(kb, vb, mb, ci + 1);
+            consume(kb, vb, mb, ci + 1, lb);
         }
     }
     constexpr uint32_t ESO = DTO == GPUOS_F32 ? 4u : 2u;

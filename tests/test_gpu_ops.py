@@ -452,3 +452,26 @@ def test_paged_decode_stream_verify(ctx):
     res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ctx=ctx)
     assert not res["fails"], res["fails"][:3]
     assert res["kv_ok"]
+
+
+def test_sdpa_paged_entries_outside_the_pool(ctx):
+    """Block-table entries outside the pool (too large, negative) drop that
+    page's keys, in units that span several pages and in units within one."""
+    say("sdpa paged, entries outside the pool")
+    recs, arrays = [], []
+    for B, H, Hkv, D, PS, MP, lens in [(2, 8, 8, 128, 64, 40, [2560, 700]), (3, 16, 4, 128, 256, 8, [2048, 1500, 300]),
+                                       (1, 4, 4, 64, 1024, 2, [2000])]:
+        pk, pv, table, NP = _paged_case(B, Hkv, D, PS, MP, extra=1)
+        t = table.reshape(B, MP).copy()
+        t[0, 1] = NP + 5          # one page of row 0 outside the pool
+        if B > 1:
+            t[1, 0] = -3          # the first page of row 1
+        q = bf16(RNG.standard_normal(B * H * D))
+        o = np.zeros(B * H * D, np.float32)
+        base = len(arrays)
+        arrays += [q, pk, pv, o, t.reshape(-1).astype(np.int32)]
+        recs.append(rec(W.OP_SDPA, dtype=W.BF16, out_dtype=W.F32, size=W.paged_size(B, MP, NP), dim=(H, D, PS, Hkv),
+                        lens=lens, flags=W.FLAG_KV_PAGED, a=base, aux0=base + 1, aux1=base + 2, out=base + 3,
+                        b=base + 4))
+    res = _run_and_check(ctx, arrays, np.concatenate(recs))
+    say("  worst", max(r["worst"] for r in res))

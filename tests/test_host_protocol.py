@@ -587,9 +587,9 @@ def test_loopback_respects_hazards_attention_streams(kind):
 
 def test_paged_cache_descriptors_validated_and_ordered():
     """Paged caches: the page size must be a power of two from 64 to 1024,
-    the pool and the table must be given, rows may not pass MP pages (nor 64
-    attention splits); an append and the attentions around it order through
-    the whole-pool ranges (loopback consumer)."""
+    the pool and the table must be given, rows may not pass MP pages; an
+    append and the attentions around it order through the whole-pool ranges
+    (loopback consumer)."""
     ctx = _loopback()
     try:
         B, H, D, PS, MP, NP = 2, 8, 128, 64, 8, 20
@@ -628,9 +628,10 @@ def test_paged_cache_descriptors_validated_and_ordered():
                     G.set_lens(x, [MP * PS + 1, 5])       # past the table row
                 assert G.gpuos_submit(ctx, x, 0)[0] == G.GPUOS_E_INVAL, (int(d["op_id"][0]), bad)
         x = att.copy()
-        x["param"][0, 5] = 80
-        G.set_lens(x, [64 * PS + 1, 5])                   # 65 splits of one page each
-        assert G.gpuos_submit(ctx, x, 0)[0] == G.GPUOS_E_INVAL
+        x["param"][0, 5] = 1024
+        G.set_lens(x, [65535, 5])                          # attention units span pages: up to 64 splits of 1024
+        assert G.gpuos_submit(ctx, x, 0)[0] == 0
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 5_000_000_000)[0] == 0
         # append, attention, append: each waits for the one before
         rc, first = G.gpuos_submit(ctx, np.concatenate([app, att, app]), G.GPUOS_SUBMIT_BLOCK)
         assert rc == 0
