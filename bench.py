@@ -319,7 +319,7 @@ def make_stream(name):
     return s, desc, fill
 
 
-WAVES_DEFAULT = {"rows": 4, "decode": 4, "decode_gqa": 4, "decode_paged": 4, "copy": 4, "copy64": 4, "matmul": 4}
+WAVES_DEFAULT = {"elementwise": 2, "rows": 4, "decode": 4, "decode_gqa": 4, "decode_paged": 4, "copy": 4, "copy64": 4, "matmul": 4}
 UPW_DEFAULT = {"decode": 2, "decode_gqa": 2, "decode_paged": 2, "rows": 2}
 # the workloads reported beside the headline in a default run, with the
 # steps each times (the decode and mixed streams run about 1-2 s per step)

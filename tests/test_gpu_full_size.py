@@ -1,5 +1,5 @@
 """GPU parity at the full sizes of the element-wise and row-op streams, in
-the launch configuration bench.py times (512-entry ring; one wave per
+the launch configuration bench.py times (512-entry ring; two waves per
 workgroup for the element-wise stream, four waves and two units per wave
 for the row ops), through the C ABI.
 
@@ -26,9 +26,9 @@ pytestmark = pytest.mark.gpu
 
 def test_elementwise_full_stream_exact_ops_bit_exact():
     s = W.make_elementwise(ops=(W.OP_ADD, W.OP_MUL, W.OP_RELU))
-    say(f"elementwise full stream, {len(s)} descriptors, ring 512, one wave per workgroup")
+    say(f"elementwise full stream, {len(s)} descriptors, ring 512, two waves per workgroup")
     arrays = [b.host_bytes() for b in s.buffers]
-    gpu = run_gpu(arrays, s.recs, bursts=s.bursts, ring_entries=512, waves_per_wg=1, units_per_wave=1)
+    gpu = run_gpu(arrays, s.recs, bursts=s.bursts, ring_entries=512, waves_per_wg=2, units_per_wave=1)
     p = oracle.Pool([a.copy() for a in arrays])
     p.run(s.recs)
     for i, b in enumerate(s.buffers):
@@ -43,9 +43,9 @@ def test_elementwise_full_stream_with_gelu_verify():
     oracle's unrounded value."""
     from gpu_harness import verify_stream
     s = W.make_elementwise()
-    say(f"elementwise full stream with GELU, verify mode, {len(s)} descriptors, ring 512, one wave per workgroup")
+    say(f"elementwise full stream with GELU, verify mode, {len(s)} descriptors, ring 512, two waves per workgroup")
     res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ring_entries=512,
-                        waves_per_wg=1, units_per_wave=1)
+                        waves_per_wg=2, units_per_wave=1)
     say(f"  logged {res['n_logged']}; worst error ratio {res['worst']}; plain relative {res['plain']}")
     assert not res["fails"], res["fails"][:3]
 

@@ -102,12 +102,14 @@ def _report(name, res):
 
 def test_elementwise_stream_verify():
     # the element-wise stream with GELU, 20,000 descriptors, in the bench's
-    # launch configuration (512-entry ring, one wave per workgroup)
+    # launch configuration (512-entry ring, two waves per workgroup), and with
+    # one wave per workgroup
     s = W.make_elementwise(n_desc=20000)
-    say("elementwise verify, 20000 descriptors with GELU")
-    res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ring_entries=512,
-                        waves_per_wg=1, units_per_wave=1)
-    _report("elementwise", res)
+    for waves in (2, 1):
+        say(f"elementwise verify, 20000 descriptors with GELU, {waves} waves per workgroup")
+        res = verify_stream([b.host_bytes() for b in s.buffers], s.recs, bursts=s.bursts, ring_entries=512,
+                            waves_per_wg=waves, units_per_wave=1)
+        _report("elementwise", res)
 
 
 def test_rows_stream_verify():
