@@ -1417,7 +1417,11 @@ __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
 #pragma unroll
         for (uint32_t t = 0; t < MTMAX; ++t) xv[t] = rld16(rx, ((t * 16u + r16) * K + k) * 2u);   // rows past M: outside the window
 #pragma unroll
-        for (uint32_t t = 0; t < NT; ++t) wv[t] = rld16s(rw, ((t * 16u + r16) * K + k) * 2u);  // columns past N: likewise
+        for (uint32_t t = 0; t < NT; ++t) wv[t] = rld16(rw, ((t * 16u + r16) * K + k) * 2u);  // columns past N: likewise
+        // (no non-temporal hint on the weights, unlike attention's keys: one
+        // load reads 64 bytes of each row and the next step the other half
+        // of the line, which the hint had evicted in between: 1.77x the
+        // weights' bytes from memory with it, 1.05x without)
     };
     auto mma = [&](const u32x4* xv, const u32x4* wv) {
 #pragma unroll
