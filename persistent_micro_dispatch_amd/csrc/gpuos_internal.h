@@ -188,7 +188,10 @@ constexpr uint32_t ROW_MAX_CACHED = 4096;  // rows up to this length stay in reg
 #define GPUOS_SDPA_KT 1024
 #endif
 constexpr uint32_t SDPA_KT = GPUOS_SDPA_KT;  // keys per SDPA unit (fewer for small attention ops)
-constexpr uint32_t GEMV_KC = 128;          // rows of W per GEMV unit
+#ifndef GPUOS_GEMV_KC
+#define GPUOS_GEMV_KC 128
+#endif
+constexpr uint32_t GEMV_KC = GPUOS_GEMV_KC;  // rows of W per GEMV unit (a multiple of 64)
 constexpr uint32_t MM_NB = 64;             // output columns per MATMUL unit above 32 rows (four 16-column tiles)
 constexpr uint32_t MM_NB_SMALL = 128;      // ... at most 32 rows (eight tiles: x is re-read by half as many units)
 constexpr uint32_t MM_KC = 1024;           // k per MATMUL unit
