@@ -938,6 +938,10 @@ __device__ __forceinline__ void kv_tile(const Unit& u, uint32_t lane) {
 // masked adds nothing (its running max stays -inf and is not subtracted
 // from itself), and a row with every key masked gives NaN, as softmax over
 // nothing does.
+template <uint32_t DTO, uint32_t D>
+__device__ __forceinline__ void sdpa_merge_splits(const Unit& u, uint32_t lane, uint32_t b, uint32_t h0, uint32_t gp,
+                                                  uint32_t ns, uint32_t mbase);
+
 template <uint32_t DV, uint32_t DTO, uint32_t GP>
 __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t D = DV * 8u;
@@ -1128,10 +1132,23 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
         }
     }
     if (ns == 1) return;
+    sdpa_merge_splits<DTO, D>(u, lane, b, h0, GP, ns, mbase);
+}
+
+// The split softmax of flash-decoding: each of the `gp` heads from h0 on
+// counts this split (its partial record already stored); the last split of
+// a head to arrive merges the head's ns records into the output.
+template <uint32_t DTO, uint32_t D>
+__device__ __forceinline__ void sdpa_merge_splits(const Unit& u, uint32_t lane, uint32_t b, uint32_t h0, uint32_t gp,
+                                                  uint32_t ns, uint32_t mbase) {
+    constexpr uint32_t PSTRIDE = D + 4u;
+    constexpr uint32_t ESO = DTO == GPUOS_F32 ? 4u : 2u;
+    const uint32_t H = u.dim[0];
+    float* parts = (float*)(u.scratch + COUNTER_AREA);
     stores_done();  // the partials are published before they are counted
     // per head: count this split; the last arriver merges the head's splits
 #pragma unroll 1
-    for (uint32_t gi = 0; gi < GP; ++gi) {
+    for (uint32_t gi = 0; gi < gp; ++gi) {
         const uint32_t head = h0 + gi;
         const uint64_t bh = (uint64_t)b * H + head;
         uint32_t* ctr = (uint32_t*)u.scratch + bh;
@@ -1189,6 +1206,243 @@ __device__ __forceinline__ void sdpa_tile(const Unit& u, uint32_t lane) {
         }
         if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+// LDS for the value chunk of sdpa_gqa_tile: one 32-key chunk per wave of a
+// workgroup of up to four waves (one array for every instantiation)
+constexpr uint32_t SDPA_VCHUNK_BYTES = 32u * 264u;
+__shared__ uint64_t sdpa_vlds[4u * SDPA_VCHUNK_BYTES / 8u];
+
+// --------------------------------------- decode SDPA, grouped heads (MFMA)
+// GP = 4 query heads that share one key/value head (D = 128), on the matrix
+// cores.  With four queries per key row the vector-ALU form does four dot
+// products and four weighted sums per 512 bytes of K and V, which bounds it
+// well below the memory system; here both contractions run as
+// v_mfma_f32_16x16x32_bf16, the four heads taking 4 of the 16 rows.
+// The unit (b, head group, split of kt keys) and its split records are those
+// of sdpa_tile; keys come in chunks of CK = 32, the next chunk's loads
+// issued before the current chunk is used.
+//  - Scores: S^T[key, h] = K Q^T per 16-key block, K as the A operand (lane
+//    l: key row l % 16, dims 8 (l / 16) + 32 s, 16 bytes per load) and Q^T
+//    as B (lane l: head l % 16, the same dims; rows past GP read zero).  Lane
+//    (h = l % 16, q = l / 16) then holds head h's scores of keys 4q + i and
+//    16 + 4q + i (i < 4): its head's softmax needs only the exchange over q.
+//  - P.V: O[h, d] += P[h, key] V[key, d] per 16-column tile of d.  A matrix
+//    product may number its contraction index in any order that both
+//    operands share: key slot 8q + j of P is the j-th score lane (h, q)
+//    holds, so P is used where it was computed.  V comes in with coalesced
+//    loads (16 bytes of one key row per lane) and is written to LDS, from
+//    which each lane reads the 8 keys of its slots at one d (the row stride
+//    of 264 bytes puts the four q groups on different banks).
+//  - P has 24 significant bits; it goes in as a bf16 high part and a bf16
+//    low part (two MFMAs), so the weights keep 16 bits, as the fp32 FMAs of
+//    the vector form keep more than the 2e-3 bar needs.  Products of bf16
+//    are exact in the fp32 accumulators.
+//  - O accumulates in the C tiles (lane l < 16 holds heads 0..3 of column
+//    l); when a head's running max moves, its rows are rescaled.
+// Masking, paged caches and keys past L are handled as in sdpa_tile.
+template <uint32_t DTO>
+__device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
+    constexpr uint32_t D = 128u, GP = 4u, CK = 32u;
+    constexpr uint32_t PSTRIDE = D + 4u;
+    constexpr uint32_t VRS = 264u;  // bytes per key row of the LDS value chunk
+    constexpr uint32_t ESO = DTO == GPUOS_F32 ? 4u : 2u;
+    static_assert(CK * VRS == SDPA_VCHUNK_BYTES, "value chunk size");
+    uint8_t* vl = (uint8_t*)sdpa_vlds + (threadIdx.x >> 6) * SDPA_VCHUNK_BYTES;
+    const bool paged = kv_paged(u.flags);
+    const uint32_t H = u.dim[0], PS = u.dim[2];
+    const uint32_t MP = __float_as_uint(u.pf[5]);
+    const uint32_t C = paged ? MP * PS : u.dim[2];
+    const uint32_t Hkv = u.dim[3] ? u.dim[3] : H;
+    const uint32_t Bn = (uint32_t)u.size;
+    const uint32_t kt = sdpa_keys_per_unit(Bn, H, u.lensw);
+    const uint32_t HG = H / GP;
+    uint32_t t = u.tile, base = 0, mbase = 0, b = 0, ns = 1, L = 0;
+    for (b = 0; b < Bn; ++b) {
+        L = lens_at(u.lensw, b);
+        ns = (L + kt - 1) / kt;
+        const uint32_t nu = HG * ns;
+        if (t < base + nu) break;
+        base += nu;
+        mbase += H * ns;
+    }
+    if (b >= Bn) return;
+    const uint32_t local = t - base, hg = local / ns, sp = local % ns;
+    const uint32_t h0 = hg * GP;
+    const uint64_t bkv = (uint64_t)b * Hkv + h0 / (H / Hkv);
+    const uint32_t k0 = sp * kt;
+    const uint32_t nk = min(L - k0, kt);
+    const float scale = u.pf[4] != 0.0f ? u.pf[4] : (u.p0 != 0.0f ? u.p0 : 1.0f / sqrtf((float)D));
+    const float sl2 = scale * 1.4426950408889634f;
+    const uint32_t r16 = lane % 16u, q = lane / 16u;
+    const RBuf rk = rbuf((const uint8_t*)u.aux0 + (bkv * C + k0) * D * 2u, paged ? 0u : nk * D * 2u);
+    const RBuf rv = rbuf((const uint8_t*)u.aux1 + (bkv * C + k0) * D * 2u, paged ? 0u : nk * D * 2u);
+    const uint64_t hkv = bkv - (uint64_t)b * Hkv, NP = kv_pages(u.size);
+    uint32_t ptab = 0;
+    if (paged && lane < (nk + PS - 1) / PS) ptab = ld4((const uint8_t*)u.b + ((uint64_t)b * MP + k0 / PS + lane) * 4u);
+    const bool masked = (u.flags & GPUOS_F_SDPA_MASK) != 0u;
+    const RBuf rm = rbuf((const uint8_t*)u.aux2 + ((uint64_t)b * C + k0) * 4u, masked ? nk * 4u : 0u);
+    // Q^T (B operand of the scores): rows past the GP heads fall outside the window
+    const RBuf rq = rbuf((const uint8_t*)u.a + ((uint64_t)b * H + h0) * D * 2u, GP * D * 2u);
+    u32x4 qb[4];
+#pragma unroll
+    for (uint32_t s = 0; s < 4; ++s) qb[s] = rld16(rq, (r16 * D + 8u * q + 32u * s) * 2u);
+    float m = -INFINITY, lsum = 0.0f;
+    f32x4 oacc[8];
+#pragma unroll
+    for (uint32_t i = 0; i < 8; ++i) oacc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t nch = (nk + CK - 1) / CK;
+    // K in the operand layout (block kb of 16 keys, dims step s), V as rows
+    // (instruction j: key row 4j + q, bytes 16 (l % 16)), the mask of keys
+    // 16 kb + 4q .. +3; false for a chunk on a page outside the pool
+    auto load = [&](u32x4* kv, u32x4* vv, u32x4* mk, uint32_t ci) -> bool {
+        RBuf ck = rk, cv = rv;
+        uint32_t cbase = ci * CK * D * 2u;
+        bool live = true;
+        if (paged) {
+            const uint32_t key0 = k0 + ci * CK;
+            const uint32_t pg = (uint32_t)__builtin_amdgcn_readlane((int)ptab, (int)((key0 / PS - k0 / PS) & 63u));
+            live = pg < NP;
+            const uint32_t keys = ci < nch && live ? min(CK, nk - ci * CK) : 0u;
+            const uint64_t at = (((uint64_t)pg * Hkv + hkv) * PS + key0 % PS) * D * 2u;
+            ck = rbuf((const uint8_t*)u.aux0 + at, keys * D * 2u);
+            cv = rbuf((const uint8_t*)u.aux1 + at, keys * D * 2u);
+            cbase = 0;
+        }
+#pragma unroll
+        for (uint32_t kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (uint32_t s = 0; s < 4; ++s)
+                kv[kb * 4u + s] = rld16s(ck, cbase + ((kb * 16u + r16) * D + 8u * q + 32u * s) * 2u);
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j) vv[j] = rld16s(cv, cbase + (j * 4u + q) * D * 2u + r16 * 16u);
+        if (masked) {
+#pragma unroll
+            for (uint32_t kb = 0; kb < 2; ++kb) mk[kb] = rld16(rm, (ci * CK + kb * 16u + 4u * q) * 4u);
+        }
+        return live;
+    };
+    auto consume = [&](const u32x4* kv, const u32x4* vv, const u32x4* mk, uint32_t ci, bool live) {
+        f32x4 st[2];
+#pragma unroll
+        for (uint32_t kb = 0; kb < 2; ++kb) {
+            st[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (uint32_t s = 0; s < 4; ++s)
+                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[kb * 4u + s]),
+                                                                 __builtin_bit_cast(bf16x8, qb[s]), st[kb], 0, 0, 0);
+        }
+        // the value rows go to LDS while the scores are finished
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j) {
+            uint64_t* w = (uint64_t*)(vl + (j * 4u + q) * VRS + r16 * 16u);
+            w[0] = (uint64_t)vv[j].x | ((uint64_t)vv[j].y << 32);
+            w[1] = (uint64_t)vv[j].z | ((uint64_t)vv[j].w << 32);
+        }
+        float sv[8], cm = -INFINITY;
+#pragma unroll
+        for (uint32_t kb = 0; kb < 2; ++kb) {
+            float mv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (masked) {
+                mv[0] = __uint_as_float(mk[kb].x); mv[1] = __uint_as_float(mk[kb].y);
+                mv[2] = __uint_as_float(mk[kb].z); mv[3] = __uint_as_float(mk[kb].w);
+            }
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) {
+                float x = st[kb][i] * sl2;
+                if (masked) x += mv[i] * 1.4426950408889634f;  // the mask, in the log2 domain too
+                const bool valid = live && ci * CK + kb * 16u + 4u * q + i < nk;
+                sv[kb * 4u + i] = valid ? x : -INFINITY;
+                cm = fmaxf(cm, sv[kb * 4u + i]);
+            }
+        }
+        cm = fmaxf(cm, __shfl_xor(cm, 16, 64));  // this head's other key groups
+        cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+        const float mn = fmaxf(m, cm);  // -inf only while every key so far is masked
+        const float alpha = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+        m = mn;
+        float p[8], ps = 0.0f;
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j) {
+            p[j] = sv[j] == -INFINITY ? 0.0f : exp2f(sv[j] - mn);  // 0 past L, or masked
+            ps += p[j];
+        }
+        lsum = lsum * alpha + ps;
+        if (__ballot(alpha != 1.0f) != 0ull) {
+            // row i of the accumulators (lanes 0..15) is head i
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) {
+                const float a = rlf(alpha, (int)i);
+#pragma unroll
+                for (uint32_t tt = 0; tt < 8; ++tt) oacc[tt][i] *= a;
+            }
+        }
+        u32x4 ph, pl;
+        uint32_t* phw = (uint32_t*)&ph;
+        uint32_t* plw = (uint32_t*)&pl;
+#pragma unroll
+        for (uint32_t e = 0; e < 4; ++e) {
+            const uint32_t hi = f2bf2(p[2 * e], p[2 * e + 1]);
+            phw[e] = hi;
+            plw[e] = f2bf2(p[2 * e] - bf2f(hi & 0xFFFFu), p[2 * e + 1] - __uint_as_float(hi & 0xFFFF0000u));
+        }
+        // B operand of tile tt: slot 8q + j is key 16 (j / 4) + 4q + j % 4, column 16 tt + l % 16
+#pragma unroll
+        for (uint32_t tt = 0; tt < 8; ++tt) {
+            u32x4 vb;
+            uint32_t* vbw = (uint32_t*)&vb;
+#pragma unroll
+            for (uint32_t e = 0; e < 4; ++e) {
+                const uint32_t j0 = 2u * e, j1 = 2u * e + 1u;
+                const uint32_t key0 = 16u * (j0 / 4u) + 4u * q + j0 % 4u, key1 = 16u * (j1 / 4u) + 4u * q + j1 % 4u;
+                const uint32_t lo = *(const uint16_t*)(vl + key0 * VRS + (16u * tt + r16) * 2u);
+                const uint32_t hi = *(const uint16_t*)(vl + key1 * VRS + (16u * tt + r16) * 2u);
+                vbw[e] = lo | (hi << 16);
+            }
+            oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph),
+                                                               __builtin_bit_cast(bf16x8, vb), oacc[tt], 0, 0, 0);
+            oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl),
+                                                               __builtin_bit_cast(bf16x8, vb), oacc[tt], 0, 0, 0);
+        }
+    };
+    u32x4 ka[8], va[8], kb2[8], vb2[8], ma[2], mb[2];
+    bool la = load(ka, va, ma, 0), lb = true;
+    for (uint32_t ci = 0; ci < nch; ci += 2) {
+        lb = load(kb2, vb2, mb, ci + 1);  // past the last chunk: outside the window, reads nothing
+        __builtin_amdgcn_sched_barrier(0);
+        consume(ka, va, ma, ci, la);
+        if (ci + 1 < nch) {
+            la = load(ka, va, ma, ci + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(kb2, vb2, mb, ci + 1, lb);
+        }
+    }
+    // each head's sum over its four key groups; lanes 0..3 then hold heads 0..3
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    float* parts = (float*)(u.scratch + COUNTER_AREA);
+#pragma unroll
+    for (uint32_t i = 0; i < GP; ++i) {
+        const float li = rlf(lsum, (int)i), mi = rlf(m, (int)i);
+        const uint64_t bh = (uint64_t)b * H + h0 + i;
+        if (ns == 1) {
+            if (q == 0) {
+                uint8_t* O = (uint8_t*)u.out + bh * D * ESO;
+                const float inv = 1.0f / li;
+#pragma unroll
+                for (uint32_t tt = 0; tt < 8; ++tt) st_elem<DTO>(O, 16u * tt + r16, oacc[tt][i] * inv);
+            }
+        } else {
+            float* part = parts + ((uint64_t)mbase + (uint64_t)(h0 + i) * ns + sp) * PSTRIDE;
+            if (q == 0) {
+#pragma unroll
+                for (uint32_t tt = 0; tt < 8; ++tt) wstf(part + 4u + 16u * tt + r16, oacc[tt][i]);
+            }
+            if (lane == 0) { wstf(part, mi); wstf(part + 1, li); }
+        }
+    }
+    if (ns == 1) return;
+    sdpa_merge_splits<DTO, D>(u, lane, b, h0, GP, ns, mbase);
 }
 
 // ------------------------------------------------------------------ GEMV
@@ -1576,7 +1830,7 @@ __device__ __forceinline__ void run_unit(const Unit& u, uint32_t lane) {
         case GPUOS_OP_SDPA:
             if (u.dim[1] == 128u) {
                 if (sdpa_heads_per_unit(u.dim[0], u.dim[3], 128u) == 4u)
-                    dout == GPUOS_F32 ? sdpa_tile<16, GPUOS_F32, 4>(u, lane) : sdpa_tile<16, GPUOS_BF16, 4>(u, lane);
+                    dout == GPUOS_F32 ? sdpa_gqa_tile<GPUOS_F32>(u, lane) : sdpa_gqa_tile<GPUOS_BF16>(u, lane);
                 else
                     dout == GPUOS_F32 ? sdpa_tile<16, GPUOS_F32, 1>(u, lane) : sdpa_tile<16, GPUOS_BF16, 1>(u, lane);
             } else {

@@ -299,7 +299,8 @@ def test_sdpa_grouped_kv_heads(ctx, out_dt):
     say(f"sdpa gqa out={out_dt}")
     recs, arrays = [], []
     for B, H, Hkv, D, C, lens in [(2, 8, 2, 128, 600, [300, 17]), (1, 32, 8, 128, 4096, [4096]),
-                                  (3, 4, 1, 64, 700, [1, 256, 700]), (8, 32, 8, 128, 512, list(RNG.integers(1, 513, 8)))]:
+                                  (3, 4, 1, 64, 700, [1, 256, 700]), (8, 32, 8, 128, 512, list(RNG.integers(1, 513, 8))),
+                                  (2, 16, 1, 128, 1100, [1025, 31]), (1, 8, 2, 128, 40, [33])]:
         q = bf16(RNG.standard_normal(B * H * D))
         K, V = bf16(RNG.standard_normal(B * Hkv * C * D)), bf16(RNG.standard_normal(B * Hkv * C * D))
         o = np.zeros(B * H * D, np.float32 if out_dt == W.F32 else np.uint16)
