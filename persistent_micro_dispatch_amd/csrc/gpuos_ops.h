@@ -39,6 +39,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(1))) const u32x4 gc_u32x4;
 typedef __attribute__((address_space(1))) const uint32_t gc_u32;
 typedef __attribute__((address_space(1))) const uint16_t gc_u16;
@@ -1210,7 +1213,7 @@ __device__ __forceinline__ void sdpa_merge_splits(const Unit& u, uint32_t lane, 
 
 // LDS for the value chunk of sdpa_gqa_tile: one 32-key chunk per wave of a
 // workgroup of up to four waves (one array for every instantiation)
-constexpr uint32_t SDPA_VCHUNK_BYTES = 32u * 264u;
+constexpr uint32_t SDPA_VCHUNK_BYTES = 32u * 288u;
 __shared__ uint64_t sdpa_vlds[4u * SDPA_VCHUNK_BYTES / 8u];
 
 // --------------------------------------- decode SDPA, grouped heads (MFMA)
@@ -1231,24 +1234,33 @@ __shared__ uint64_t sdpa_vlds[4u * SDPA_VCHUNK_BYTES / 8u];
 //    product may number its contraction index in any order that both
 //    operands share: key slot 8q + j of P is the j-th score lane (h, q)
 //    holds, so P is used where it was computed.  V comes in with coalesced
-//    loads (16 bytes of one key row per lane) and is written to LDS, from
-//    which each lane reads the 8 keys of its slots at one d (the row stride
-//    of 264 bytes puts the four q groups on different banks).
+//    loads (16 bytes of one key row per lane) and is written to LDS as rows;
+//    the LDS transpose read (ds_read_b64_tr_b16) then gives each lane four
+//    keys at one d: in each 16-lane group, lane i receives element i % 4 of
+//    the 8 bytes that lanes 4e + i / 4 (e < 4) point at, so lane p of group
+//    q points at row key(slot 8q + e), columns d0 + 4 (p % 4) .. +4, two
+//    reads per tile.  Rows are 288 bytes apart, which spreads the 16 rows of
+//    a read over the banks evenly.
 //  - P has 24 significant bits; it goes in as a bf16 high part and a bf16
 //    low part (two MFMAs), so the weights keep 16 bits, as the fp32 FMAs of
 //    the vector form keep more than the 2e-3 bar needs.  Products of bf16
 //    are exact in the fp32 accumulators.
 //  - O accumulates in the C tiles (lane l < 16 holds heads 0..3 of column
-//    l); when a head's running max moves, its rows are rescaled.
+//    l).  A head's reference max moves only when a chunk's max exceeds it by
+//    more than 8 (log2 domain), so weights stay below 2^8 and the rescaling
+//    of its accumulator rows (and sum) is rare after the first chunk; the
+//    result is the same softmax, and partial records carry the reference
+//    max they were computed with.
 // Masking, paged caches and keys past L are handled as in sdpa_tile.
 template <uint32_t DTO>
 __device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t D = 128u, GP = 4u, CK = 32u;
     constexpr uint32_t PSTRIDE = D + 4u;
-    constexpr uint32_t VRS = 264u;  // bytes per key row of the LDS value chunk
+    constexpr uint32_t VRS = 288u;  // bytes per key row of the LDS value chunk
     constexpr uint32_t ESO = DTO == GPUOS_F32 ? 4u : 2u;
     static_assert(CK * VRS == SDPA_VCHUNK_BYTES, "value chunk size");
-    uint8_t* vl = (uint8_t*)sdpa_vlds + (threadIdx.x >> 6) * SDPA_VCHUNK_BYTES;
+    __attribute__((address_space(3))) uint8_t* vl =
+        (__attribute__((address_space(3))) uint8_t*)sdpa_vlds + (threadIdx.x >> 6) * SDPA_VCHUNK_BYTES;
     const bool paged = kv_paged(u.flags);
     const uint32_t H = u.dim[0], PS = u.dim[2];
     const uint32_t MP = __float_as_uint(u.pf[5]);
@@ -1335,7 +1347,8 @@ __device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
         // the value rows go to LDS while the scores are finished
 #pragma unroll
         for (uint32_t j = 0; j < 8; ++j) {
-            uint64_t* w = (uint64_t*)(vl + (j * 4u + q) * VRS + r16 * 16u);
+            __attribute__((address_space(3))) uint64_t* w =
+                (__attribute__((address_space(3))) uint64_t*)(vl + (j * 4u + q) * VRS + r16 * 16u);
             w[0] = (uint64_t)vv[j].x | ((uint64_t)vv[j].y << 32);
             w[1] = (uint64_t)vv[j].z | ((uint64_t)vv[j].w << 32);
         }
@@ -1358,17 +1371,20 @@ __device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
         }
         cm = fmaxf(cm, __shfl_xor(cm, 16, 64));  // this head's other key groups
         cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-        const float mn = fmaxf(m, cm);  // -inf only while every key so far is masked
-        const float alpha = mn == -INFINITY ? 1.0f : exp2f(m - mn);
-        m = mn;
+        // the reference max moves to this chunk's max when that is more than
+        // 8 above it (always from -inf: m + 8 is -inf); the old sum and
+        // accumulators are scaled by alpha = 2^(m - cm), 0 from -inf
+        const bool move = cm > m + 8.0f;
+        const float alpha = move ? exp2f(m - cm) : 1.0f;
+        if (move) m = cm;  // -inf only while every key so far is masked
         float p[8], ps = 0.0f;
 #pragma unroll
         for (uint32_t j = 0; j < 8; ++j) {
-            p[j] = sv[j] == -INFINITY ? 0.0f : exp2f(sv[j] - mn);  // 0 past L, or masked
+            p[j] = sv[j] == -INFINITY ? 0.0f : exp2f(sv[j] - m);  // 0 past L, or masked; below 2^8
             ps += p[j];
         }
         lsum = lsum * alpha + ps;
-        if (__ballot(alpha != 1.0f) != 0ull) {
+        if (__ballot(move) != 0ull) {
             // row i of the accumulators (lanes 0..15) is head i
 #pragma unroll
             for (uint32_t i = 0; i < 4; ++i) {
@@ -1386,19 +1402,15 @@ __device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
             phw[e] = hi;
             plw[e] = f2bf2(p[2 * e] - bf2f(hi & 0xFFFFu), p[2 * e + 1] - __uint_as_float(hi & 0xFFFF0000u));
         }
-        // B operand of tile tt: slot 8q + j is key 16 (j / 4) + 4q + j % 4, column 16 tt + l % 16
+        // B operand of tile tt: slot 8q + j is key 16 (j / 4) + 4q + j % 4,
+        // column 16 tt + l % 16; lane p of group q points at row 4q + p / 4
+        // (then 16 + 4q + p / 4), columns 16 tt + 4 (p % 4) .. +4
+        const uint32_t ra = (4u * q + r16 / 4u) * VRS + 8u * (r16 % 4u);
 #pragma unroll
         for (uint32_t tt = 0; tt < 8; ++tt) {
-            u32x4 vb;
-            uint32_t* vbw = (uint32_t*)&vb;
-#pragma unroll
-            for (uint32_t e = 0; e < 4; ++e) {
-                const uint32_t j0 = 2u * e, j1 = 2u * e + 1u;
-                const uint32_t key0 = 16u * (j0 / 4u) + 4u * q + j0 % 4u, key1 = 16u * (j1 / 4u) + 4u * q + j1 % 4u;
-                const uint32_t lo = *(const uint16_t*)(vl + key0 * VRS + (16u * tt + r16) * 2u);
-                const uint32_t hi = *(const uint16_t*)(vl + key1 * VRS + (16u * tt + r16) * 2u);
-                vbw[e] = lo | (hi << 16);
-            }
+            const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + ra + 32u * tt));
+            const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vl + ra + 16u * VRS + 32u * tt));
+            const u32x4 vb = __builtin_shufflevector(__builtin_bit_cast(u32x2, x0), __builtin_bit_cast(u32x2, x1), 0, 1, 2, 3);
             oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph),
                                                                __builtin_bit_cast(bf16x8, vb), oacc[tt], 0, 0, 0);
             oacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl),
