@@ -372,7 +372,17 @@ __device__ __forceinline__ void worker_loop(const ExecArgs& A, uint32_t lane) {
 }
 
 // ----------------------------------------------------------------- fetcher
-__device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, uint64_t* lds, uint64_t* pref) {
+// OR over the wave (DPP within 16-lane groups, then the four groups)
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_XOR1, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_XOR2, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_HALF_MIRROR, 0xF, 0xF, false);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, DPP_MIRROR, 0xF, 0xF, false);
+    return (uint32_t)(__builtin_amdgcn_readlane((int)v, 0) | __builtin_amdgcn_readlane((int)v, 16) |
+                      __builtin_amdgcn_readlane((int)v, 32) | __builtin_amdgcn_readlane((int)v, 48));
+}
+
+__device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, uint64_t* lds) {
     DevCtl* C = A.dctl;
     const uint64_t mask = A.mask;
     const uint64_t Q = (uint64_t)A.qmask + 1;
@@ -393,6 +403,9 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
     // idle exit: the heartbeat last seen, and when it (or work) last changed
     uint64_t hb_seen = 0, hb_t = wall_clock64();
     bool worked = false;
+    // whether the last batch held a descriptor with extra-dependency side
+    // words: then this batch's side words are read with its bodies
+    bool xpre = false;
     for (;;) {
         // the stamps and the control words in one round trip over PCIe
         const uint64_t sl = f + lane;
@@ -437,6 +450,18 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             const uint32_t wi = lane + 64u * k;
             if (wi < nw) v[k] = ld_sys(&ringw[((f + (wi >> 4)) & mask) * 16u + (wi & 15u)]);
         }
+        // In a stream of many-dependency descriptors the side words of the
+        // whole batch come in the same round trip over PCIe as the bodies
+        // (a few KB) instead of a second round trip after the bodies are
+        // parsed; the host writes them before the stamp.  Word wi of the
+        // batch goes to lane wi % 64, xv[wi / 64].
+        const uint32_t nx = xpre ? count * DEPX_WORDS : 0u;
+        uint64_t xv[DEPX_WORDS];
+#pragma unroll
+        for (uint32_t k = 0; k < DEPX_WORDS; ++k) {
+            const uint32_t wi = lane + 64u * k;
+            xv[k] = wi < nx ? ld_sys(&A.depx[((f + wi / DEPX_WORDS) & mask) * DEPX_WORDS + wi % DEPX_WORDS]) : 0ull;
+        }
 #pragma unroll
         for (uint32_t k = 0; k < 16; ++k) {
             const uint32_t wi = lane + 64u * k;
@@ -452,13 +477,15 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         // DEPX_WORDS side words of the host array: copy them to HBM for the
         // workers (the slot's previous descriptor has completed, so nobody
         // reads its copy any more)
-        if (act && ((d12 >> 16) & 0xFFFFu) != 0) {
+        // (read on demand when they were not read with the bodies; copied to
+        // HBM with the batch's other stores, after every load of the batch:
+        // loads and stores retire in order, so a load behind these stores
+        // would wait for their acknowledgements)
+        const uint64_t xneed = __ballot(act && ((d12 >> 16) & 0xFFFFu) != 0);
+        if (!xpre && act && ((xneed >> lane) & 1ull)) {
             const uint64_t sl = (f + lane) & mask;
-            uint64_t xw[DEPX_WORDS];
 #pragma unroll
-            for (uint32_t k = 0; k < DEPX_WORDS; ++k) xw[k] = ld_sys(&A.depx[sl * DEPX_WORDS + k]);
-#pragma unroll
-            for (uint32_t k = 0; k < DEPX_WORDS; ++k) wst64(&A.depd[sl * DEPX_WORDS + k], xw[k]);
+            for (uint32_t k = 0; k < DEPX_WORDS; ++k) xv[k] = ld_sys(&A.depx[sl * DEPX_WORDS + k]);
         }
         const uint32_t op_id = (uint32_t)d0;
         const uint32_t ver = (uint32_t)(d12 >> 48);
@@ -498,7 +525,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             pl.scratch = 0;
         }
         if (pl.status != GPUOS_ST_OK) { kind = KIND_BAD; pl.ntiles = 1; pl.scratch = 0; }
-        uint32_t nt = act ? pl.ntiles : 0u;
+        uint32_t nt = act ? max(pl.ntiles, 1u) : 0u;  // every plan has a unit
         // inclusive prefix of units over lanes
         uint64_t inc = nt;
 #pragma unroll
@@ -555,6 +582,21 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
         const bool keep = lane < count;
         const uint64_t T = rl64(inc, (int)count - 1);
         const uint64_t ubegin = u_next + inc - nt;
+        // extra-dependency side words (batch layout when read with the
+        // bodies, else lane i holds descriptor i's)
+        if (xpre) {
+#pragma unroll
+            for (uint32_t k = 0; k < DEPX_WORDS; ++k) {
+                const uint32_t wi = lane + 64u * k;
+                if (wi < nx && ((xneed >> (wi / DEPX_WORDS)) & 1ull))
+                    wst64(&A.depd[((f + wi / DEPX_WORDS) & mask) * DEPX_WORDS + wi % DEPX_WORDS], xv[k]);
+            }
+        } else if (act && ((xneed >> lane) & 1ull)) {
+            const uint64_t sl = (f + lane) & mask;
+#pragma unroll
+            for (uint32_t k = 0; k < DEPX_WORDS; ++k) wst64(&A.depd[sl * DEPX_WORDS + k], xv[k]);
+        }
+        xpre = xneed != 0;
         // mirror bodies, meta, per-slot unit counters
 #pragma unroll
         for (uint32_t k = 0; k < 16; ++k) {
@@ -571,7 +613,6 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             wst64(mm + 4, my_mark);
             wst64(mm + 5, prog);
             wst32(&A.tiles_done[slot], 0u);
-            pref[lane] = inc - nt;
         }
         // zero the group counters of descriptors that use scratch
         uint64_t zm = __ballot(keep && my_sv != NO_SCRATCH);
@@ -584,17 +625,29 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             for (uint32_t k = 0; k < COUNTER_AREA / 16u / 64u; ++k)
                 wst16(zb, (lane + 64u * k) * 16u, u32x4{0, 0, 0, 0});
         }
-        if (lane == 0) pref[count] = T;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        // one queue entry per unit: its descriptor and index
-        for (uint64_t wi = lane; wi < T; wi += 64u) {
-            uint32_t lo = 0, hi = count;  // find j with pref[j] <= wi < pref[j+1]
-            while (hi - lo > 1) {
-                const uint32_t mid = (lo + hi) >> 1;
-                if (pref[mid] <= wi) lo = mid; else hi = mid;
-            }
-            wst64(&A.queue[(u_next + wi) & A.qmask], queue_entry(f + lo, wi - pref[lo]));
+        // one queue entry per unit: its descriptor and index, 64 per store.
+        // Descriptor j's units start at its exclusive prefix ustart; in each
+        // window of 64 units the starts that fall inside form a mask M (OR
+        // over the descriptor lanes); a unit's descriptor is the number of
+        // starts at or below it (plus those before the window) minus one,
+        // and its index counts from the highest such start.
+        const uint64_t ustart = inc - nt;
+        uint32_t jbase = 0;    // descriptors started before the window
+        uint64_t cstart = 0;   // the start of the last of them
+        for (uint64_t w0 = 0; w0 < T; w0 += 64u) {
+            const uint64_t rel = ustart - w0;
+            const bool here = nt > 0u && ustart >= w0 && rel < 64u;
+            const uint32_t mlo = wave_or(here && rel < 32u ? 1u << rel : 0u);
+            const uint32_t mhi = wave_or(here && rel >= 32u ? 1u << (rel - 32u) : 0u);
+            const uint64_t M = (uint64_t)mlo | ((uint64_t)mhi << 32);
+            const uint64_t below = M & (lane == 63u ? ~0ull : (2ull << lane) - 1ull);
+            const uint32_t c = (uint32_t)__popcll(below);
+            const uint32_t j = jbase + c - 1u;  // c = 0: the descriptor begun before the window
+            const uint64_t st = c ? w0 + 63u - (uint64_t)__clzll(below) : cstart;
+            const uint64_t wi = w0 + lane;
+            if (wi < T) wst64(&A.queue[(u_next + wi) & A.qmask], queue_entry(f + j, wi - st));
+            jbase += (uint32_t)__popcll(M);
+            if (M) cstart = w0 + 63u - (uint64_t)__clzll(M);
         }
         stores_done();  // entries, mirror, meta and counters are written through
         if (lane == 0) st_agent(&C->q_tail, u_next + T);
@@ -616,7 +669,7 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
 template <uint32_t SLOTS, bool JIT = false>
 __device__ __forceinline__ void executor_body(const ExecArgs& A, uint64_t* lds) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
-    if (blockIdx.x == 0 && wave == 0) fetcher_loop(A, lane, lds, lds + 64 * 16);
+    if (blockIdx.x == 0 && wave == 0) fetcher_loop(A, lane, lds);
     else worker_loop<SLOTS, JIT>(A, lane);
     if (lane == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
@@ -626,20 +679,20 @@ __device__ __forceinline__ void executor_body(const ExecArgs& A, uint64_t* lds) 
 
 // one unit per worker wave
 extern "C" __global__ void __launch_bounds__(256) gpuos_executor(ExecArgs A) {
-    __shared__ uint64_t lds[64 * 16 + 72];
+    __shared__ uint64_t lds[64 * 16];
     executor_body<1>(A, lds);
 }
 
 // two units per worker wave
 extern "C" __global__ void __launch_bounds__(256) gpuos_executor_s2(ExecArgs A) {
-    __shared__ uint64_t lds[64 * 16 + 72];
+    __shared__ uint64_t lds[64 * 16];
     executor_body<2>(A, lds);
 }
 
 // one unit per worker wave, and calls into bodies injected with
 // gpuos_register_jit (a stack in scratch memory for those calls)
 extern "C" __global__ void __launch_bounds__(256) gpuos_executor_jit(ExecArgs A) {
-    __shared__ uint64_t lds[64 * 16 + 72];
+    __shared__ uint64_t lds[64 * 16];
     executor_body<1, true>(A, lds);
 }
 
