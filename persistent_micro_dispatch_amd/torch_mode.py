@@ -211,13 +211,19 @@ def _storages(args) -> List[int]:
 class GpuosMode(TorchDispatchMode):
     """Route eligible aten ops to a gpuos context (created on entry unless
     one is given; shut down on exit if created here).  `stats` counts routed
-    ops by kind and normal-path ops by reason."""
+    ops by kind and normal-path ops by reason.
+
+    A context created here has one executor wave per workgroup unless `init`
+    says otherwise: the PyTorch kernels of the ops that take the normal path
+    run beside the resident executor, and with one wave per CU three SIMDs of
+    every CU stay free for them whatever registers they need (an executor
+    wave on every SIMD leaves each only what the executor does not use)."""
 
     def __init__(self, ctx: Optional[int] = None, filter: Optional[RoutingFilter] = None, **init):
         super().__init__()
         self.ctx = ctx
         self.own = ctx is None
-        self.init = init
+        self.init = {"waves_per_wg": 1, **init}
         self.filter = filter or RoutingFilter()
         self.stats = RouteStats()
         self.inflight: collections.deque = collections.deque()  # (seq, tensors kept alive)
