@@ -8,37 +8,29 @@
 // complete before running it.  Descriptors without conflicts run
 // concurrently.
 //
-// Data structure.  Byte intervals are kept in clusters: a cluster covers a
-// contiguous span that accesses have touched (in practice one tensor, or one
-// arena) and holds a small sorted vector of disjoint intervals, each with
-// its last writer and the readers since that write.  An access costs one
-// cluster lookup plus a few edits of a short vector; clusters are created,
-// extended or merged only when an access reaches memory not seen before.
-//  - A read never splits an interval: the reader is recorded on every
-//    interval it overlaps, whole, so intervals are created only by writes
-//    (which coalesce what they cover) and by reads of untouched bytes.  A
-//    later write to the part that was not read then waits for that reader
-//    too: an extra wait, never a missing one.
-//  - A writer's dependency on the interval's previous writer is dropped when
-//    the interval has a live reader: every reader waited for that writer.
-//  - An interval keeps up to MAXR readers; beyond that it keeps the oldest
-//    overflowed reader, and a writer then depends on the whole range from it
-//    (reported through `range_from`).
-//  - Readers are kept as the low 32 bits of their sequence numbers (a live
-//    one is at most a ring's length older than the descriptor being
-//    annotated, so the full number is the largest one not above it with
-//    those bits) and are dropped from the front by advancing a start index,
-//    so an interval is 160 bytes and nothing is shifted when readers retire.
+// Data structure.  Memory that accesses have touched is kept in clusters: a
+// cluster covers a contiguous span (in practice one tensor, or one arena).
+// It holds
+//  - the writes as a sorted vector of disjoint intervals, each with its last
+//    writer (a write coalesces what it covers, so every byte has exactly the
+//    last writer a later access must order after), and
+//  - the reads as a log in sequence order (byte range and sequence number),
+//    appended to in O(1): reads never conflict with reads, so a read is not
+//    spread over the write intervals.
+// A read waits for the live writers of the intervals it overlaps.  A write
+// waits for those too and for every live logged read it overlaps; a logged
+// read that lies inside the write's range is then dropped from the log, since
+// any later access that conflicts with it overlaps the write, which waited
+// for it.  Reads below the watermark leave from the front of the log.
 //  - Clusters are found through a small direct-mapped cache keyed by the
 //    access's start address, else by binary search in a sorted array of
 //    cluster starts.  An access that reaches past one cluster's span, and
-//    touches no other, extends that cluster in place; only an access that
-//    touches several clusters merges them (moving the intervals of the later
-//    ones into the first).
-//  - A cluster that holds more than SPLIT_AT live intervals (a long-lived
-//    buffer written piece by piece, such as an output arena) is split in two
-//    at an interval boundary, so that inserting an interval never moves more
-//    than a few dozen of them.
+//    touches no other, extends that cluster in place; one that touches
+//    several merges them (intervals concatenated, logs merged by sequence).
+//  - A cluster whose write intervals or read log grow past SPLIT_AT live
+//    entries (a long-lived buffer written piece by piece, such as an output
+//    arena) is split in two at an interval boundary; logged reads that
+//    straddle the cut go to both halves.
 // Sequence numbers below the host's completion watermark are known complete
 // and are never returned.
 #pragma once
@@ -57,56 +49,46 @@ struct Access {
 
 class HazardTracker {
 public:
-    static constexpr uint32_t MAXR = 30;
     static constexpr size_t SPLIT_AT = 96;
 
-    // Appends to `deps` every live seq (>= floor) that `seq` must wait for
-    // and lowers *range_from to the first seq of a range that must be waited
-    // for entirely (left untouched if none); then records the accesses.
+    // Appends to `deps` every live seq (>= floor) that `seq` must wait for;
+    // then records the accesses.  `range_from` is for trackers that return a
+    // whole range of earlier descriptors to wait for; this one returns
+    // explicit dependencies only and leaves it untouched.
     void analyze(uint64_t seq, const Access* acc, int n, uint64_t floor, std::vector<uint64_t>& deps,
                  uint64_t* range_from) {
-        cur_ = seq;
-        // resolve each access's cluster once (a merge invalidates earlier
-        // ones: resolve again until no merge happens)
+        (void)range_from;
+        floor_ = floor;
         Cluster* cp[24];
         if (n > 24) n = 24;
+        // resolve each access's cluster (a merge retires clusters found
+        // earlier: resolve again until no merge happens)
         for (int round = 0; round < 4; ++round) {
             const uint64_t m0 = merges_;
             for (int i = 0; i < n; ++i) cp[i] = acc[i].hi > acc[i].lo ? &cluster_for(acc[i].lo, acc[i].hi) : nullptr;
             if (merges_ == m0) break;
         }
-        bool distinct = true;
-        for (int i = 0; i < n && distinct; ++i)
-            for (int j = 0; j < i; ++j)
-                if (cp[i] && cp[i] == cp[j]) { distinct = false; break; }
-        if (distinct) {
-            // no two accesses share a cluster: each can be collected and
-            // recorded in one pass without seeing the others
-            for (int i = 0; i < n; ++i) {
-                if (!cp[i]) continue;
-                if (acc[i].write) {
-                    collect(*cp[i], acc[i], floor, deps, range_from);
-                    record_write(*cp[i], acc[i].lo, acc[i].hi, seq);
-                } else {
-                    read_pass(*cp[i], acc[i].lo, acc[i].hi, seq, floor, deps);
-                }
-                if (cp[i]->regs.size() > cp[i]->prune_at) prune(*cp[i], floor);
-            }
-        } else {
-            for (int i = 0; i < n; ++i)
-                if (cp[i]) collect(*cp[i], acc[i], floor, deps, range_from);
-            for (int pass = 0; pass < 2; ++pass) {
-                for (int i = 0; i < n; ++i) {
-                    if (!cp[i] || acc[i].write != (pass == 1)) continue;
-                    if (acc[i].write) record_write(*cp[i], acc[i].lo, acc[i].hi, seq);
-                    else record_read(*cp[i], acc[i].lo, acc[i].hi, seq, floor);
-                    if (cp[i]->regs.size() > cp[i]->prune_at) prune(*cp[i], floor);
-                }
+        // every access is checked before any is recorded, so that a
+        // descriptor never waits for itself
+        for (int i = 0; i < n; ++i) {
+            if (!cp[i]) continue;
+            prune_reads(*cp[i]);
+            writers(*cp[i], acc[i].lo, acc[i].hi, deps);
+            if (acc[i].write) readers(*cp[i], acc[i].lo, acc[i].hi, deps);
+        }
+        for (int i = 0; i < n; ++i) {
+            if (!cp[i]) continue;
+            Cluster& c = *cp[i];
+            if (acc[i].write) {
+                record_write(c, acc[i].lo, acc[i].hi, seq);
+                if (c.w.size() > c.prune_at) prune_writes(c);
+            } else {
+                push_read(c, Ent{acc[i].lo, acc[i].hi, seq});
             }
         }
         // split large clusters only now: the pointers in cp stay valid above
         for (int i = 0; i < n; ++i)
-            if (cp[i] && cp[i]->regs.size() > SPLIT_AT) split(*cp[i], floor);
+            if (cp[i] && (cp[i]->w.size() > SPLIT_AT || cp[i]->rlive() > cp[i]->rsplit_at)) split(*cp[i]);
     }
 
     void clear() {
@@ -115,9 +97,10 @@ public:
         free_.clear();
         std::fill(hits_.begin(), hits_.end(), Hit{});
     }
+    // write intervals plus live logged reads over all clusters (diagnostics)
     size_t size() const {
         size_t n = 0;
-        for (const Entry& e : idx_) n += e.c->regs.size();
+        for (const Entry& e : idx_) n += e.c->w.size() + e.c->rlive();
         return n;
     }
     size_t clusters() const { return idx_.size(); }
@@ -125,16 +108,20 @@ public:
 private:
     struct Region {
         uint64_t lo, hi;
-        uint64_t writer;    // 0 = none
-        uint64_t overflow;  // 0 = none; else the oldest reader not kept
-        uint16_t r0, nr;    // the kept readers are rd[r0 .. nr), in sequence order
-        uint32_t rd[MAXR];  // low 32 bits of the readers' sequence numbers
+        uint64_t writer;  // 0 = none
+    };
+    static constexpr uint64_t DEAD_LO = UINT64_MAX;  // a dropped read overlaps nothing
+    struct Ent {
+        uint64_t lo, hi, seq;
     };
     struct Cluster {
         uint64_t lo = 0, hi = 0;
-        std::vector<Region> regs;  // sorted by lo, disjoint, inside [lo, hi)
-        size_t prune_at = 64;
+        std::vector<Region> w;  // sorted by lo, disjoint, inside [lo, hi)
+        std::vector<Ent> r;     // reads in sequence order; [rhead, size) may be live
+        size_t rhead = 0, rdead = 0;
+        size_t prune_at = 64, rsplit_at = SPLIT_AT;
         bool alive = false;
+        size_t rlive() const { return r.size() - rhead - rdead; }
     };
     // Clusters live in a pool and are recycled, never freed, so a pointer to
     // one always points to some cluster object; idx_ lists the live ones,
@@ -147,7 +134,7 @@ private:
     std::deque<Cluster> store_;
     std::vector<Cluster*> free_;
     uint64_t merges_ = 0;
-    uint64_t cur_ = 0;  // the sequence number being annotated
+    uint64_t floor_ = 0;
     // A direct-mapped cache from an access's start address to its cluster,
     // checked against the cluster's current span (merges retire clusters,
     // splits shrink them, recycling reuses them).
@@ -157,10 +144,6 @@ private:
     };
     static constexpr size_t NHIT = 4096;  // 2^12: the hash below keeps 12 bits
     std::vector<Hit> hits_ = std::vector<Hit>(NHIT);
-
-    // full sequence number of a kept reader: the largest one not above the
-    // descriptor being annotated that has these low 32 bits
-    uint64_t widen(uint32_t r) const { return cur_ - (uint32_t)((uint32_t)cur_ - r); }
 
     Cluster* alloc_cluster() {
         Cluster* c;
@@ -173,23 +156,16 @@ private:
         }
         c->alive = true;
         c->prune_at = 64;
+        c->rsplit_at = SPLIT_AT;
         return c;
     }
     void retire(Cluster* c) {
         c->alive = false;
         c->lo = c->hi = 0;
-        c->regs.clear();
+        c->w.clear();
+        c->r.clear();
+        c->rhead = c->rdead = 0;
         free_.push_back(c);
-    }
-
-    static Region make(uint64_t lo, uint64_t hi, uint64_t writer) {
-        Region r;
-        r.lo = lo;
-        r.hi = hi;
-        r.writer = writer;
-        r.overflow = 0;
-        r.r0 = r.nr = 0;
-        return r;
     }
 
     // index of the first cluster starting above x
@@ -200,6 +176,22 @@ private:
             if (idx_[m].lo > x) b = m; else a = m + 1;
         }
         return a;
+    }
+
+    // the live reads of c's log, merged by sequence number with those of o
+    void merge_reads(Cluster& c, Cluster& o) {
+        prune_reads(c);
+        prune_reads(o);
+        std::vector<Ent> out;
+        out.reserve(c.rlive() + o.rlive());
+        size_t i = c.rhead, j = o.rhead;
+        while (i < c.r.size() || j < o.r.size()) {
+            const bool take_c = j == o.r.size() || (i < c.r.size() && c.r[i].seq <= o.r[j].seq);
+            const Ent& t = take_c ? c.r[i++] : o.r[j++];
+            if (t.lo != DEAD_LO) out.push_back(t);
+        }
+        c.r.swap(out);
+        c.rhead = c.rdead = 0;
     }
 
     // The cluster containing [lo, hi), created, extended or merged as needed.
@@ -222,16 +214,18 @@ private:
             c = idx_[first].c;
             if (last > first + 1) {
                 // several clusters: move the later ones' intervals into the
-                // first (all are sorted and lie above it)
+                // first (all are sorted and lie above it) and merge the logs
                 ++merges_;
                 for (size_t q = first + 1; q < last; ++q) {
                     Cluster* o = idx_[q].c;
-                    c->regs.insert(c->regs.end(), o->regs.begin(), o->regs.end());
+                    c->w.insert(c->w.end(), o->w.begin(), o->w.end());
+                    if (o->rlive()) merge_reads(*c, *o);
                     c->hi = std::max(c->hi, o->hi);
                     retire(o);
                 }
                 idx_.erase(idx_.begin() + (long)(first + 1), idx_.begin() + (long)last);
-                c->prune_at = std::max<size_t>(64, 2 * c->regs.size());
+                c->prune_at = std::max<size_t>(64, 2 * c->w.size());
+                c->rsplit_at = std::max(SPLIT_AT, 2 * c->rlive());
             }
             // extend in place (no other cluster overlaps [lo, hi) now)
             if (lo < c->lo) {
@@ -245,7 +239,7 @@ private:
         return *c;
     }
 
-    // index of the first region with hi > x
+    // index of the first interval with hi > x
     static size_t first_after(const std::vector<Region>& v, uint64_t x) {
         size_t a = 0, b = v.size();
         while (a < b) {
@@ -255,43 +249,61 @@ private:
         return a;
     }
 
-    // readers are appended in sequence order, so the completed ones (below
-    // the watermark) form a prefix of the kept ones
-    void prune_readers(Region& r, uint64_t floor) const {
-        if (r.overflow && r.overflow < floor) r.overflow = 0;
-        while (r.r0 < r.nr && widen(r.rd[r.r0]) < floor) ++r.r0;
-        if (r.r0 == r.nr) r.r0 = r.nr = 0;
+    void prune_reads(Cluster& c) const {
+        while (c.rhead < c.r.size() && c.r[c.rhead].seq < floor_) {
+            if (c.r[c.rhead].lo == DEAD_LO) --c.rdead;
+            ++c.rhead;
+        }
+        if (c.rhead == c.r.size()) {
+            c.r.clear();
+            c.rhead = c.rdead = 0;
+        }
+    }
+    void compact_reads(Cluster& c) const {
+        size_t k = 0;
+        for (size_t i = c.rhead; i < c.r.size(); ++i)
+            if (c.r[i].lo != DEAD_LO) c.r[k++] = c.r[i];
+        c.r.resize(k);
+        c.rhead = c.rdead = 0;
+    }
+    void push_read(Cluster& c, const Ent& x) const {
+        if (c.rhead + c.rdead > 16 && 2 * (c.rhead + c.rdead) > c.r.size()) compact_reads(c);
+        c.r.push_back(x);
     }
 
-    void collect(Cluster& c, const Access& a, uint64_t floor, std::vector<uint64_t>& deps, uint64_t* range_from) {
-        for (size_t i = first_after(c.regs, a.lo); i < c.regs.size() && c.regs[i].lo < a.hi; ++i) {
-            Region& r = c.regs[i];
-            prune_readers(r, floor);
-            const bool live_w = r.writer >= floor && r.writer != 0;
-            if (!a.write || (r.r0 == r.nr && !r.overflow)) {
-                if (live_w) deps.push_back(r.writer);
-                continue;
+    // the live writers of the intervals overlapping [lo, hi)
+    void writers(const Cluster& c, uint64_t lo, uint64_t hi, std::vector<uint64_t>& deps) const {
+        for (size_t i = first_after(c.w, lo); i < c.w.size() && c.w[i].lo < hi; ++i)
+            if (c.w[i].writer >= floor_ && c.w[i].writer != 0) deps.push_back(c.w[i].writer);
+    }
+    // the live logged reads overlapping [lo, hi) (a write); those inside it
+    // are dropped: the write orders every later conflicting access after them
+    void readers(Cluster& c, uint64_t lo, uint64_t hi, std::vector<uint64_t>& deps) const {
+        for (size_t i = c.rhead; i < c.r.size(); ++i) {
+            Ent& x = c.r[i];
+            if (x.lo >= hi || x.hi <= lo) continue;  // also every dropped read
+            deps.push_back(x.seq);
+            if (x.lo >= lo && x.hi <= hi) {
+                x.lo = DEAD_LO;
+                x.hi = 0;
+                ++c.rdead;
             }
-            for (uint32_t k = r.r0; k < r.nr; ++k) deps.push_back(widen(r.rd[k]));
-            if (r.overflow && r.overflow < *range_from) *range_from = r.overflow;
         }
     }
 
     static void record_write(Cluster& c, uint64_t lo, uint64_t hi, uint64_t seq) {
-        auto& v = c.regs;
+        auto& v = c.w;
         const size_t i0 = first_after(v, lo);
         size_t i1 = i0;
         while (i1 < v.size() && v[i1].lo < hi) ++i1;
         if (i1 == i0 + 1 && v[i0].lo == lo && v[i0].hi == hi) {  // exact match: reuse
             v[i0].writer = seq;
-            v[i0].r0 = v[i0].nr = 0;
-            v[i0].overflow = 0;
             return;
         }
         Region parts[3];
         int np = 0;
         if (i1 > i0 && v[i0].lo < lo) { parts[np] = v[i0]; parts[np].hi = lo; ++np; }
-        parts[np++] = make(lo, hi, seq);
+        parts[np++] = Region{lo, hi, seq};
         if (i1 > i0 && v[i1 - 1].hi > hi) { parts[np] = v[i1 - 1]; parts[np].lo = hi; ++np; }
         const size_t old = i1 - i0;
         if ((size_t)np <= old) {
@@ -303,102 +315,67 @@ private:
         }
     }
 
-    void add_reader(Region& r, uint64_t seq) const {
-        if (r.nr == MAXR) {
-            if (r.r0 > 0) {  // room at the front: move the kept readers down
-                std::copy(r.rd + r.r0, r.rd + r.nr, r.rd);
-                r.nr = (uint16_t)(r.nr - r.r0);
-                r.r0 = 0;
-            } else {
-                const uint64_t oldest = widen(r.rd[0]);
-                if (!r.overflow || oldest < r.overflow) r.overflow = oldest;
-                std::copy(r.rd + 1, r.rd + MAXR, r.rd);
-                r.nr = MAXR - 1;
-            }
-        }
-        r.rd[r.nr++] = (uint32_t)seq;
-    }
-
-    void record_read(Cluster& c, uint64_t lo, uint64_t hi, uint64_t seq, uint64_t floor) const {
-        auto& v = c.regs;
-        size_t i = first_after(v, lo);
-        uint64_t cur = lo;
-        while (cur < hi) {
-            if (i == v.size() || v[i].lo > cur) {
-                // gap [cur, next start or hi): an interval with no writer
-                const uint64_t end = (i == v.size() || v[i].lo > hi) ? hi : v[i].lo;
-                Region g = make(cur, end, 0);
-                g.nr = 1;
-                g.rd[0] = (uint32_t)seq;
-                v.insert(v.begin() + (long)i, g);
-                ++i;
-                cur = end;
-                continue;
-            }
-            prune_readers(v[i], floor);
-            add_reader(v[i], seq);
-            cur = v[i].hi;
-            ++i;
-        }
-    }
-
-    // collect and record_read of one read in a single pass: each interval it
-    // overlaps yields its live writer and gets the reader; gaps become
-    // intervals with no writer
-    void read_pass(Cluster& c, uint64_t lo, uint64_t hi, uint64_t seq, uint64_t floor,
-                   std::vector<uint64_t>& deps) const {
-        auto& v = c.regs;
-        size_t i = first_after(v, lo);
-        uint64_t cur = lo;
-        while (cur < hi) {
-            if (i == v.size() || v[i].lo > cur) {
-                const uint64_t end = (i == v.size() || v[i].lo > hi) ? hi : v[i].lo;
-                Region g = make(cur, end, 0);
-                g.nr = 1;
-                g.rd[0] = (uint32_t)seq;
-                v.insert(v.begin() + (long)i, g);
-                ++i;
-                cur = end;
-                continue;
-            }
-            Region& r = v[i];
-            if (r.writer >= floor && r.writer != 0) deps.push_back(r.writer);
-            prune_readers(r, floor);
-            add_reader(r, seq);
-            cur = r.hi;
-            ++i;
-        }
-    }
-
-    // Prune, and if the cluster is still large move its upper half into a
-    // cluster of its own (pool entries do not move, so other Cluster
-    // pointers stay valid).
-    void split(Cluster& c, uint64_t floor) {
-        prune(c, floor);
-        if (c.regs.size() <= SPLIT_AT) return;
-        const size_t mid = c.regs.size() / 2;
-        Cluster* up = alloc_cluster();  // the pool is a deque: c stays valid
-        up->lo = c.regs[mid].lo;
-        up->hi = c.hi;
-        up->regs.assign(c.regs.begin() + (long)mid, c.regs.end());
-        up->prune_at = std::max<size_t>(64, 2 * up->regs.size());
-        c.regs.resize(mid);
-        c.hi = up->lo;
-        c.prune_at = std::max<size_t>(64, 2 * c.regs.size());
-        idx_.insert(idx_.begin() + (long)idx_upper(c.lo), Entry{up->lo, up});
-    }
-
-    // drop intervals that carry no live information
-    void prune(Cluster& c, uint64_t floor) const {
-        auto& v = c.regs;
+    // drop write intervals whose writer is complete
+    void prune_writes(Cluster& c) const {
+        auto& v = c.w;
         size_t k = 0;
-        for (size_t i = 0; i < v.size(); ++i) {
-            prune_readers(v[i], floor);
-            const bool live = (v[i].writer >= floor && v[i].writer != 0) || v[i].nr > v[i].r0 || v[i].overflow;
-            if (live) v[k++] = v[i];
-        }
+        for (size_t i = 0; i < v.size(); ++i)
+            if (v[i].writer >= floor_ && v[i].writer != 0) v[k++] = v[i];
         v.resize(k);
         c.prune_at = std::max<size_t>(64, 2 * v.size());
+    }
+
+    // Prune, and if the cluster is still large move its upper half (by the
+    // write intervals, else by the logged reads' starts) into a cluster of
+    // its own (pool entries do not move, so other Cluster pointers stay
+    // valid).
+    void split(Cluster& c) {
+        prune_writes(c);
+        prune_reads(c);
+        compact_reads(c);
+        const bool by_w = c.w.size() > SPLIT_AT;
+        if (!by_w && c.rlive() <= c.rsplit_at) return;
+        uint64_t cut;
+        if (by_w) {
+            cut = c.w[c.w.size() / 2].lo;
+        } else {
+            std::vector<uint64_t> starts;
+            starts.reserve(c.r.size());
+            for (const Ent& x : c.r) starts.push_back(x.lo);
+            std::nth_element(starts.begin(), starts.begin() + (long)(starts.size() / 2), starts.end());
+            cut = starts[starts.size() / 2];
+            size_t below = 0, above = 0;
+            for (const Ent& x : c.r) { below += x.lo < cut; above += x.hi > cut; }
+            if (cut <= c.lo || 4 * below > 3 * c.r.size() || 4 * above > 3 * c.r.size()) {
+                c.rsplit_at = 2 * c.r.size();  // reads of one range: no useful cut
+                return;
+            }
+            // the cut must not fall inside a write interval
+            const size_t i = first_after(c.w, cut);
+            if (i < c.w.size() && c.w[i].lo < cut) cut = c.w[i].lo > c.lo ? c.w[i].lo : c.w[i].hi;
+            if (cut <= c.lo || cut >= c.hi) {
+                c.rsplit_at = 2 * c.r.size();
+                return;
+            }
+        }
+        Cluster* up = alloc_cluster();  // the pool is a deque: c stays valid
+        up->lo = cut;
+        up->hi = c.hi;
+        const size_t wi = first_after(c.w, cut);  // every interval from wi on starts at or above cut
+        up->w.assign(c.w.begin() + (long)wi, c.w.end());
+        c.w.resize(wi);
+        size_t k = 0;
+        for (const Ent& x : c.r) {
+            if (x.hi > cut) up->r.push_back(Ent{std::max(x.lo, cut), x.hi, x.seq});
+            if (x.lo < cut) c.r[k++] = Ent{x.lo, std::min(x.hi, cut), x.seq};
+        }
+        c.r.resize(k);
+        c.hi = cut;
+        c.prune_at = std::max<size_t>(64, 2 * c.w.size());
+        up->prune_at = std::max<size_t>(64, 2 * up->w.size());
+        c.rsplit_at = std::max(SPLIT_AT, 2 * c.rlive());
+        up->rsplit_at = std::max(SPLIT_AT, 2 * up->rlive());
+        idx_.insert(idx_.begin() + (long)idx_upper(c.lo), Entry{up->lo, up});
     }
 };
 

@@ -3,7 +3,8 @@
 // Random descriptor streams of byte-range accesses: prefixes and arbitrary
 // sub-ranges of a few dozen "tensors", accesses spanning neighbouring
 // tensors (cluster merges), long-lived arenas written piece by piece
-// (cluster splits), hot tensors read by many descriptors (reader overflow),
+// (cluster splits), hot tensors read by many descriptors (more than the 62
+// dependencies a descriptor carries),
 // and a completion process that retires descriptors in a random order
 // allowed by their dependencies, so the watermark passed to the tracker
 // moves the way the library's does.

@@ -156,11 +156,12 @@ def test_loopback_respects_hazards_in_a_large_arena():
     assert _check_order(r, order, first) == 0
 
 
-@pytest.mark.parametrize("n_read", [25, 40])
+@pytest.mark.parametrize("n_read", [25, 40, 62, 70])
 def test_many_readers_give_explicit_dependencies(n_read):
     """A write after n reads of its output waits on exactly those n
-    descriptors: explicit dependencies up to the tracker's 30 readers per
-    interval, beyond that a range from the oldest reader."""
+    descriptors: explicit dependencies up to the 62 a descriptor carries (six
+    in the body, 56 in the side words), beyond that a range from the oldest
+    reader."""
     r = np.zeros(n_read + 1, W.REC_DTYPE)
     r["buf"] = -1
     r["dtype"] = r["out_dtype"] = W.F32
@@ -178,7 +179,7 @@ def test_many_readers_give_explicit_dependencies(n_read):
         st = G.gpuos_stats_get(ctx)
     finally:
         G.gpuos_shutdown(ctx)
-    if n_read <= 30:
+    if n_read <= 62:
         assert st["deps_range"] == 0 and st["deps_explicit"] == n_read
     else:
         assert st["deps_range"] == 1
