@@ -167,22 +167,45 @@ def chain_hops_by_xcd(num_wgs=512, n=4000, n_elem=256):
     finally:
         assert G.gpuos_shutdown(ctx) == 0
     assert float(buf[0].item()) == float(n)
-    done, xcc_done, ready, xcc_ready = {}, {}, {}, {}
+    done, xcc_done, ready, xcc_ready, claim, body = {}, {}, {}, {}, {}, {}
     for r in tr:
         q = int(r["seq"])
         if q not in done or r["t_done"] > done[q]:
             done[q], xcc_done[q] = int(r["t_done"]), int(r["hw"]) >> 16
+            body[q] = int(r["t_body"])
         if q not in ready or r["t_ready"] < ready[q]:
-            ready[q], xcc_ready[q] = int(r["t_ready"]), int(r["hw"]) >> 16
+            ready[q], xcc_ready[q], claim[q] = int(r["t_ready"]), int(r["hw"]) >> 16, int(r["t_claim"])
     hop, seen = {"same": [], "other": []}, {"same": [], "other": []}
+    # where a hop's time goes (all hops): the consumer's unit claimed (and
+    # its descriptor read) before or after the producer completed; from the
+    # producer's completion to the consumer's dependencies found satisfied
+    # (detect); the consumer's body; its completion written (publish)
+    waiting, detect, bodies, publish = [], [], [], []
+    us = 1e-2  # 100 MHz wall clock -> us
     qs = sorted(done)
     for a, b in zip(qs[:-1], qs[1:]):
         if b == a + 1:
             k = "same" if xcc_done[a] == xcc_ready[b] else "other"
-            hop[k].append((done[b] - done[a]) * 1e-2)    # 100 MHz wall clock -> us
-            seen[k].append((ready[b] - done[a]) * 1e-2)
-    return {k: {"hops": len(hop[k]), "hop_us_p50": float(np.median(hop[k])) if hop[k] else None,
-                "seen_after_done_us_p50": float(np.median(seen[k])) if seen[k] else None} for k in hop}
+            hop[k].append((done[b] - done[a]) * us)
+            seen[k].append((ready[b] - done[a]) * us)
+            waiting.append(claim[b] <= done[a])
+            detect.append((ready[b] - done[a]) * us)
+            bodies.append((body[b] - ready[b]) * us)
+            publish.append((done[b] - body[b]) * us)
+    out = {k: {"hops": len(hop[k]), "hop_us_p50": float(np.median(hop[k])) if hop[k] else None,
+               "seen_after_done_us_p50": float(np.median(seen[k])) if seen[k] else None} for k in hop}
+    if waiting:
+        w = np.asarray(waiting)
+        pct = lambda x, p: float(np.percentile(np.asarray(x), p))  # noqa: E731
+        out["phases"] = {
+            "consumer_claimed_before_producer_done": float(w.mean()),
+            "detect_us_p50": pct(detect, 50), "detect_us_p90": pct(detect, 90),
+            "detect_us_p50_when_claimed_before": pct(np.asarray(detect)[w], 50) if w.any() else None,
+            "detect_us_p50_when_claimed_after": pct(np.asarray(detect)[~w], 50) if (~w).any() else None,
+            "body_us_p50": pct(bodies, 50), "publish_us_p50": pct(publish, 50),
+            "hop_us_p50": pct(np.asarray(detect) + np.asarray(bodies) + np.asarray(publish), 50),
+        }
+    return out
 
 
 def log(*a):
