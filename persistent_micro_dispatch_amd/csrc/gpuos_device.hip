@@ -648,6 +648,14 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
             if (wi < T) wst64(&A.queue[(u_next + wi) & A.qmask], queue_entry(f + j, wi - st));
             jbase += (uint32_t)__popcll(M);
             if (M) cstart = w0 + 63u - (uint64_t)__clzll(M);
+            // a large batch is published in prefixes, so that workers start
+            // on its first units while the rest of its entries are written
+            // (the mirror, meta and counters written above are covered by
+            // the first acknowledgement)
+            if (((w0 + 64u) & (PUBLISH_STEP - 1u)) == 0 && w0 + 64u < T) {
+                stores_done();
+                if (lane == 0) st_agent(&C->q_tail, u_next + w0 + 64u);
+            }
         }
         stores_done();  // entries, mirror, meta and counters are written through
         if (lane == 0) st_agent(&C->q_tail, u_next + T);
@@ -669,12 +677,13 @@ __device__ __forceinline__ void fetcher_loop(const ExecArgs& A, uint32_t lane, u
 template <uint32_t SLOTS, bool JIT = false>
 __device__ __forceinline__ void executor_body(const ExecArgs& A, uint64_t* lds) {
     const uint32_t lane = threadIdx.x & 63u, wave = threadIdx.x >> 6;
+    // The host learns that the executor has finished from the launch's
+    // completion event, which also makes every write of the kernel visible
+    // to it: a wave leaves without a fence or a word in host memory (a
+    // system-scope release and atomic per wave made an empty launch of 1,024
+    // waves take about a millisecond).
     if (blockIdx.x == 0 && wave == 0) fetcher_loop(A, lane, lds);
     else worker_loop<SLOTS, JIT>(A, lane);
-    if (lane == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-        __hip_atomic_fetch_add(&A.hctl->exited, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
 }
 
 // one unit per worker wave

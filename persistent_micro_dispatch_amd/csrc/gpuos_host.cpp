@@ -322,7 +322,6 @@ int executor_launch(gpuos_ctx* c) {
     const uint64_t start = ld_acq(&c->hctl->fetch_end);
     st_rel(&c->hctl->stop, (uint64_t)0);
     st_rel(&c->hctl->abort, (uint64_t)0);
-    st_rel(&c->hctl->exited, (uint64_t)0);
     st_rel(&c->hctl->idle_exit, (uint64_t)0);
     ExecArgs a{};
     a.ring = c->ring;

@@ -55,7 +55,6 @@ struct HostCtl {
     alignas(64) uint64_t stop;       // host -> device: finish and exit when idle
     alignas(64) uint64_t abort;      // host -> device: exit at once
     alignas(64) uint64_t dev_error;  // device -> host: sticky error code
-    alignas(64) uint64_t exited;     // device -> host: number of waves that left
     alignas(64) uint64_t heartbeat;  // host -> device: bumped by every call of the context
     alignas(64) uint64_t fetch_end;  // device -> host: first seq the fetcher did not take
     alignas(64) uint64_t idle_exit;  // device -> host: 1 if the launch ended for lack of heartbeat
@@ -106,6 +105,10 @@ __host__ __device__ inline uint64_t ticket_unit(uint64_t ticket, uint32_t shards
 // a unit-queue entry: the descriptor's sequence number and the unit's index in it
 constexpr uint32_t QE_TILE_BITS = 24;
 static_assert((1ull << QE_TILE_BITS) >= (1ull << 22), "tile field holds MAX_TILES");
+// units of a batch after which the fetcher publishes the prefix written so
+// far (a large descriptor's first units start while the rest are queued)
+constexpr uint64_t PUBLISH_STEP = 2048;
+static_assert((PUBLISH_STEP & (PUBLISH_STEP - 1)) == 0 && PUBLISH_STEP % 64 == 0, "a power of two, whole windows");
 __host__ __device__ inline uint64_t queue_entry(uint64_t seq, uint64_t tile) { return (seq << QE_TILE_BITS) | tile; }
 __host__ __device__ inline uint64_t entry_seq(uint64_t e) { return e >> QE_TILE_BITS; }
 __host__ __device__ inline uint32_t entry_tile(uint64_t e) { return (uint32_t)(e & ((1u << QE_TILE_BITS) - 1u)); }

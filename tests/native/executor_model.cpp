@@ -39,6 +39,9 @@
 
 #include "gpuos_internal.h"
 
+constexpr uint64_t MODEL_PUBLISH_STEP = 32;
+static_assert(gpuos::PUBLISH_STEP % MODEL_PUBLISH_STEP == 0, "the executor's step is a multiple of the model's");
+
 using namespace gpuos;
 
 namespace {
@@ -191,6 +194,11 @@ void fetcher(Model& m) {
             const uint64_t pos = (u_next + wi) & (m.Q - 1);
             m.queue.at(pos).store(queue_entry(f + j, wi - first), std::memory_order_relaxed);
             m.queue_tag.at(pos).store(u_next + wi, std::memory_order_relaxed);
+            // a large batch is published in prefixes, as the executor's
+            // fetcher does every PUBLISH_STEP units; the model uses 32 so
+            // that its small queues see prefixes too
+            if ((wi + 1) % MODEL_PUBLISH_STEP == 0 && wi + 1 < T)
+                m.q_tail.store(u_next + wi + 1, std::memory_order_release);
         }
         m.q_tail.store(u_next + T, std::memory_order_release);
         f += fit;
