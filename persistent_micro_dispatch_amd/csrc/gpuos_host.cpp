@@ -376,7 +376,11 @@ int executor_stop(gpuos_ctx* c, int64_t timeout_ns) {
             aborted = true;
         }
         if (aborted && el > (uint64_t)timeout_ns + 5000000000ull) return GPUOS_E_TIMEOUT;
-        std::this_thread::sleep_for(std::chrono::microseconds(20));
+        // a drained executor leaves within tens of microseconds: yield at
+        // first (a sleep can take several times what it asks for), sleep
+        // once the wait has gone on
+        if (el < 5000000ull) std::this_thread::yield();
+        else std::this_thread::sleep_for(std::chrono::microseconds(20));
     }
     executor_finished(c);
     return aborted ? GPUOS_E_TIMEOUT : GPUOS_OK;
