@@ -238,6 +238,21 @@ def test_large_descriptors(ctx):
     _run_and_check(ctx, arrays, np.concatenate(recs))
 
 
+def test_batch_of_many_units_published_in_prefixes(ctx):
+    """One batch of more units than several publication steps (the fetcher
+    publishes a large batch 2,048 units at a time): a copy of 96 MiB + 5 B
+    (3,073 units) and an fp32 add of 8M + 1 elements (4,097 units) submitted
+    together, both exact."""
+    say("one batch of about 7,000 units: copy 96 MiB + 5 B, add 8M + 1")
+    n = (96 << 20) + 5
+    a = RNG.integers(0, 255, n).astype(np.uint8)
+    m = (8 << 20) + 1
+    x, y = _vals(m, W.F32), _vals(m, W.F32)
+    arrays = [a, np.zeros(n, np.uint8), x, y, np.zeros(m, np.float32)]
+    recs = np.concatenate([rec(W.OP_COPY, size=n, a=0, out=1), rec(W.OP_ADD, dtype=W.F32, size=m, a=2, b=3, out=4)])
+    _run_and_check(ctx, arrays, recs)
+
+
 # ------------------------------------------------ injected element-wise programs
 @pytest.mark.parametrize("dt", [W.F32, W.BF16])
 def test_expr_programs(ctx, dt):
