@@ -208,6 +208,101 @@ def chain_hops_by_xcd(num_wgs=512, n=4000, n_elem=256):
     return out
 
 
+
+def critical_path(recs, descs, bursts, waves, ring, num_wgs, units_per_wave):
+    """The element-wise stream once more, in the timed configuration but
+    with the unit trace on, and its critical path: from the descriptor that
+    completed last, each step goes to its dependency (read-after-write,
+    write-after-read, write-after-write on whole prefixes of pool tensors,
+    which is exact for this stream) that completed last.  Each hop of the
+    path (from that dependency's completion to the consumer's) splits into
+    claim-late (the consumer's first unit claimed only after the dependency
+    completed), detect (until the first unit found its dependencies
+    satisfied), spread (until the last unit did) and tail (the last unit's
+    body and the descriptor's completion).  Times are device wall-clock
+    stamps (100 MHz)."""
+    import workloads as W
+    from persistent_micro_dispatch_amd import gpuos as G
+    ctx = G.gpuos_init(waves_per_wg=waves, ring_entries=ring, num_wgs=num_wgs,
+                       units_per_wave=units_per_wave, flags=G.GPUOS_INIT_TRACE)
+    try:
+        assert G.gpuos_pause(ctx, 30_000_000_000) == 0
+        for _ in range(2):  # the trace keeps the last launch
+            assert G.gpuos_resume(ctx) == 0
+            rc, first, n = G.gpuos_submit_bursts(ctx, descs, bursts, G.GPUOS_SUBMIT_BLOCK)
+            assert rc == 0 and n == len(descs), (rc, n)
+            assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 300_000_000_000)[0] == 0
+            assert G.gpuos_pause(ctx, 30_000_000_000) == 0
+        tr = G.gpuos_trace_read(ctx, 1 << 21)
+    finally:
+        assert G.gpuos_shutdown(ctx) == 0
+    tr = tr[tr["seq"] >= first]
+    order = np.argsort(tr["seq"], kind="stable")
+    tr = tr[order]
+    u, idx = np.unique(tr["seq"].astype(np.int64), return_index=True)
+    if len(u) != len(recs):
+        return {"error": f"trace holds {len(u)} of {len(recs)} descriptors"}
+    t = {f: tr[f].astype(np.int64) for f in ("t_claim", "t_ready", "t_body", "t_done")}
+    claim0 = np.minimum.reduceat(t["t_claim"], idx)
+    ready0 = np.minimum.reduceat(t["t_ready"], idx)
+    ready1 = np.maximum.reduceat(t["t_ready"], idx)
+    done1 = np.maximum.reduceat(t["t_done"], idx)
+    nunits = np.diff(np.append(idx, len(tr)))
+    assert (recs["off"][:, [W.A, W.B, W.OUT]] == 0).all()
+    crit = np.full(len(recs), -1, np.int64)
+    last_w, readers = {}, {}
+    ops, bufs = recs["op"], recs["buf"]
+    for i in range(len(recs)):
+        ins = [int(bufs[i, W.A])] + ([int(bufs[i, W.B])] if ops[i] in (W.OP_ADD, W.OP_MUL) else [])
+        o = int(bufs[i, W.OUT])
+        deps = {last_w[x] for x in ins + [o] if x in last_w}
+        deps.update(readers.get(o, ()))
+        if deps:
+            dl = np.fromiter(deps, np.int64, len(deps))
+            crit[i] = dl[np.argmax(done1[dl])]
+        for x in ins:
+            readers.setdefault(x, []).append(i)
+        last_w[o] = i
+        readers[o] = []
+    k, path = int(np.argmax(done1)), []
+    while k >= 0:
+        path.append(k)
+        k = int(crit[k])
+    q = np.asarray(path[::-1][1:], np.int64)
+    c = crit[q]
+    us = 1e-2
+    hop = (done1[q] - done1[c]) * us
+    ph = {"claim_late": np.maximum(0, claim0[q] - done1[c]) * us,
+          "detect": (ready0[q] - np.maximum(done1[c], claim0[q])) * us,
+          "spread": (ready1[q] - ready0[q]) * us,
+          "tail": (done1[q] - ready1[q]) * us}
+    span = (done1.max() - claim0.min()) * us
+    out = {"span_us": float(span), "hops": int(len(q)), "hop_us_mean": float(hop.mean()),
+           "hop_us_p50": float(np.median(hop)), "path_share_of_span": float(hop.sum() / span),
+           "claimed_after_dependency_done": float((claim0[q] > done1[c]).mean()),
+           "phases_us_mean": {k2: float(v.mean()) for k2, v in ph.items()},
+           "units_mean_on_path": float(nunits[q].mean()), "units_mean_all": float(nunits.mean())}
+    by_units = {}
+    for lo, hi in ((1, 1), (2, 4), (5, 16), (17, 1 << 30)):
+        m = (nunits[q] >= lo) & (nunits[q] <= hi)
+        if m.any():
+            key = str(lo) if lo == hi else (f"{lo}-{hi}" if hi < (1 << 30) else f"{lo}+")
+            by_units[key] = {"hops": int(m.sum()), "hop_us_mean": float(hop[m].mean()),
+                             **{k2 + "_us_mean": float(v[m].mean()) for k2, v in ph.items()}}
+    out["by_units"] = by_units
+    names = {W.OP_ADD: "add", W.OP_MUL: "mul", W.OP_RELU: "relu", W.OP_GELU: "gelu"}
+    dts = {W.F32: "f32", W.BF16: "bf16"}
+    by_op = {}
+    for o, on in names.items():
+        for dt, dn in dts.items():
+            m = (ops[q] == o) & (recs["dtype"][q] == dt)
+            if m.any():
+                by_op[f"{on}/{dn}"] = {"hops": int(m.sum()), "hop_us_mean": float(hop[m].mean()),
+                                       "tail_us_mean": float(ph["tail"][m].mean()),
+                                       "share_of_path": float(hop[m].sum() / hop.sum())}
+    out["by_op"] = by_op
+    return out
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -679,6 +774,8 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
     if jit_in is not None:
         injection["compiled"] = jit_injection(*jit_in, waves=waves, ring=ring, num_wgs=num_wgs)
     xcd_hops = chain_hops_by_xcd() if headline else None
+    cpath = critical_path(recs, descs, bursts, waves, ring, num_wgs, units_per_wave) \
+        if headline and name == "elementwise" else None
 
     # ---- roofline of the executor kernel (one launch = one step)
     mean_launch_ms = float(np.mean(launch_ms))
@@ -735,6 +832,7 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
             "size_buckets": buckets,
             "injection": injection,
             "chain_hops_by_xcd": xcd_hops,
+            "critical_path": cpath,
         })
     rec.update(extra)
     del pool, descs, chain_buf, one_buf

@@ -67,3 +67,59 @@ def test_torch_eager_baseline_row_ops_within_tolerance():
             g = got[bi][off: off + nb].view(np.float32).astype(np.float64)
             x = ref[bi][off: off + nb].view(np.float32).astype(np.float64)
             assert np.allclose(g, x, rtol=1e-4, atol=1e-4 * max(1.0, float(np.abs(x).max()))), W.OP_NAMES[int(r["op"])]
+
+
+def _conflict(recs, i, j):
+    """Descriptors i and j touch a common pool tensor and one of them writes
+    it (every access of the element-wise stream is a prefix of a tensor)."""
+    def acc(k):
+        ins = {int(recs["buf"][k, W.A])} | ({int(recs["buf"][k, W.B])} if int(recs["buf"][k, W.B]) >= 0 else set())
+        return ins, int(recs["buf"][k, W.OUT])
+    ri, wi = acc(i)
+    rj, wj = acc(j)
+    return wi in rj or wj in ri or wi == wj
+
+
+def test_critical_path_walks_dependencies(monkeypatch):
+    """critical_path on a synthetic trace: every step of the path goes to a
+    conflicting earlier descriptor, the one among them that completed last,
+    and the phases add up to the hop."""
+    from persistent_micro_dispatch_amd import gpuos as G
+    s = W.make_elementwise(n_desc=300, n_per_dtype=4)
+    recs = s.recs
+    n = len(recs)
+    rng = np.random.default_rng(7)
+    units = rng.integers(1, 4, n)
+    seq = np.repeat(np.arange(n), units)
+    tr = np.zeros(len(seq), G.TRACE_DTYPE)
+    tr["seq"] = 500 + seq
+    # completion times rise with sequence (plus jitter); units of one
+    # descriptor start 0-3 ticks apart and finish together
+    done = 1000 + 100 * np.arange(n) + rng.integers(0, 90, n)
+    off = rng.integers(0, 4, len(seq))
+    tr["t_done"] = done[seq]
+    tr["t_body"] = done[seq] - 5
+    tr["t_ready"] = done[seq] - 40 + off
+    tr["t_claim"] = done[seq] - 60 + off
+    tr = tr[rng.permutation(len(tr))]
+    for f, v in (("gpuos_init", lambda **k: 1), ("gpuos_pause", lambda c, t: 0), ("gpuos_resume", lambda c: 0),
+                 ("gpuos_submit_bursts", lambda c, d, b, fl: (0, 500, len(d))),
+                 ("gpuos_sync", lambda c, u, t: (0, 0, 0)), ("gpuos_trace_read", lambda c, m: tr),
+                 ("gpuos_shutdown", lambda c: 0)):
+        monkeypatch.setattr(G, f, v)
+    out = bench.critical_path(recs, np.zeros(n), np.ones(1, np.uint32), 1, 512, 0, 1)
+    assert out["hops"] >= 1 and 0.0 < out["path_share_of_span"] <= 1.0
+    # rebuild the path by brute force and compare its length and hop time
+    k, path = int(np.argmax(done)), [int(np.argmax(done))]
+    while True:
+        deps = [j for j in range(k) if _conflict(recs, k, j)]
+        if not deps:
+            break
+        k = max(deps, key=lambda j: done[j])
+        path.append(k)
+    assert out["hops"] == len(path) - 1
+    hops = [(done[a] - done[b]) * 1e-2 for a, b in zip(path[:-1], path[1:])]
+    assert abs(out["hop_us_mean"] - np.mean(hops)) < 1e-9
+    ph = out["phases_us_mean"]
+    assert abs(sum(ph.values()) - out["hop_us_mean"]) < 1e-9  # the four phases partition each hop
+    assert abs(ph["tail"] - np.mean([(done[a] - (done[a] - 40 + 3)) * 1e-2 for a in path[:-1]])) < 0.03 + 1e-9
