@@ -222,6 +222,29 @@ def test_copy_and_nop(ctx):
     _run_and_check(ctx, arrays, np.concatenate(recs))
 
 
+def test_empty_descriptors(ctx):
+    """Element-wise and row ops of size 0 (one unit each that does nothing)
+    complete and write nothing; the ordinary descriptors after them still run."""
+    say("empty descriptors: element-wise and row ops of size 0, then ordinary ones")
+    recs, arrays = [], []
+    for dt in (W.F32, W.BF16):
+        es = W.DTYPE_BYTES[dt]
+        base = len(arrays)
+        arrays += [_vals(4096, dt), _vals(4096, dt), RNG.integers(0, 255, 4096 * es).astype(np.uint8),
+                   _vals(4096, dt) if dt == W.F32 else bf16(1.0 + 0.1 * RNG.standard_normal(4096).astype(np.float32)),
+                   _vals(4096, dt)]
+        for op in (W.OP_ADD, W.OP_MUL, W.OP_RELU, W.OP_GELU):
+            recs.append(rec(op, dtype=dt, size=0, a=base, b=base + 1, out=base + 2))
+        for op in (W.OP_SUM, W.OP_MAX, W.OP_MIN, W.OP_SOFTMAX):
+            recs.append(rec(op, dtype=dt, size=0, dim=(1024,), a=base, out=base + 2))
+        recs.append(rec(W.OP_LAYERNORM, dtype=dt, size=0, dim=(1024,), fparam=(1e-5,), a=base, aux0=base + 3,
+                        aux1=base + 4, out=base + 2))
+        # ordinary work after the empty descriptors, on the same output
+        recs.append(rec(W.OP_ADD, dtype=dt, size=777, a=base, b=base + 1, out=(base + 2, es * 100)))
+        recs.append(rec(W.OP_SOFTMAX, dtype=dt, size=2, dim=(1024,), a=(base, es * 1024), out=(base + 2, es * 2048)))
+    _run_and_check(ctx, arrays, np.concatenate(recs))
+
+
 def test_large_descriptors(ctx):
     """Descriptors of hundreds of units (completion counted by one per-slot counter)."""
     say("large descriptors: copy 8 MiB + 37 B, add/mul 1M + 3 elements")
