@@ -249,6 +249,34 @@ def test_bad_op_id_is_reported_by_sync():
         G.gpuos_shutdown(ctx)
 
 
+def test_descriptor_unit_limit_follows_the_unit_queue():
+    """A descriptor may take at most half the unit queue: with 2^12 queue
+    positions, an fp32 add of 2048 units of 2048 values and a copy of 2048
+    units of 32 KiB are accepted, one element more of either is refused
+    before submission (the pointers are never used)."""
+    ctx = G.gpuos_init(flags=G.GPUOS_INIT_LOOPBACK, ring_entries=64, unit_queue_log2=12)
+    try:
+        d = G.new_descs(1)
+        d["op_id"] = G.GPUOS_OP_ADD
+        d["flags"] = G.flags(G.GPUOS_F32)
+        d["input_a"], d["input_b"], d["output"] = 1 << 40, 2 << 40, 3 << 40
+        d["size"] = 2048 * 2048            # 16 MiB per operand: units of 8 KiB
+        assert G.gpuos_submit(ctx, d, G.GPUOS_SUBMIT_BLOCK)[0] == 0
+        d["size"] = 2048 * 2048 + 1
+        assert G.gpuos_submit(ctx, d, 0)[0] == G.GPUOS_E_INVAL
+        c = G.new_descs(1)
+        c["op_id"] = G.GPUOS_OP_COPY
+        c["input_a"], c["output"] = 1 << 40, 3 << 40
+        c["size"] = 2048 * 32768            # units of 32 KiB
+        assert G.gpuos_submit(ctx, c, G.GPUOS_SUBMIT_BLOCK)[0] == 0
+        c["size"] = 2048 * 32768 + 1
+        assert G.gpuos_submit(ctx, c, 0)[0] == G.GPUOS_E_INVAL
+        assert G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 5_000_000_000)[0] == 0
+        assert G.gpuos_stats_get(ctx)["submitted"] == 2
+    finally:
+        G.gpuos_shutdown(ctx)
+
+
 def test_invalid_shapes_rejected_before_submission():
     ctx = _loopback()
     try:
