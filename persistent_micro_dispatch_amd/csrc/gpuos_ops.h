@@ -1226,10 +1226,14 @@ __shared__ uint64_t sdpa_vlds[4u * SDPA_VCHUNK_BYTES / 8u];
 // of sdpa_tile; keys come in chunks of CK = 32, the next chunk's loads
 // issued before the current chunk is used.
 //  - Scores: S^T[key, h] = K Q^T per 16-key block, K as the A operand (lane
-//    l: key row l % 16, dims 8 (l / 16) + 32 s, 16 bytes per load) and Q^T
-//    as B (lane l: head l % 16, the same dims; rows past GP read zero).  Lane
-//    (h = l % 16, q = l / 16) then holds head h's scores of keys 4q + i and
-//    16 + 4q + i (i < 4): its head's softmax needs only the exchange over q.
+//    l: key row l % 16, dims 8 (l / 16) + 32 s) and Q^T as B (lane l: head
+//    l % 16, the same dims; rows past GP read zero).  K comes in as V does,
+//    whole rows per load instruction, and goes through the wave's LDS area
+//    into that layout: loaded in the operand layout directly, each
+//    instruction took half of sixteen 128-byte lines, and the grouped decode
+//    stream ran about 11% slower.  Lane (h = l % 16, q = l / 16) then holds
+//    head h's scores of keys 4q + i and 16 + 4q + i (i < 4): its head's
+//    softmax needs only the exchange over q.
 //  - P.V: O[h, d] += P[h, key] V[key, d] per 16-column tile of d.  A matrix
 //    product may number its contraction index in any order that both
 //    operands share: key slot 8q + j of P is the j-th score lane (h, q)
@@ -1257,8 +1261,9 @@ __device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
     constexpr uint32_t D = 128u, GP = 4u, CK = 32u;
     constexpr uint32_t PSTRIDE = D + 4u;
     constexpr uint32_t VRS = 288u;  // bytes per key row of the LDS value chunk
+    constexpr uint32_t KRS = 272u;  // ... of the key chunk, staged in the same place first
     constexpr uint32_t ESO = DTO == GPUOS_F32 ? 4u : 2u;
-    static_assert(CK * VRS == SDPA_VCHUNK_BYTES, "value chunk size");
+    static_assert(CK * VRS == SDPA_VCHUNK_BYTES && CK * KRS <= SDPA_VCHUNK_BYTES, "chunk sizes");
     __attribute__((address_space(3))) uint8_t* vl =
         (__attribute__((address_space(3))) uint8_t*)sdpa_vlds + (threadIdx.x >> 6) * SDPA_VCHUNK_BYTES;
     const bool paged = kv_paged(u.flags);
@@ -1322,12 +1327,10 @@ __device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
             cbase = 0;
         }
 #pragma unroll
-        for (uint32_t kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (uint32_t s = 0; s < 4; ++s)
-                kv[kb * 4u + s] = rld16s(ck, cbase + ((kb * 16u + r16) * D + 8u * q + 32u * s) * 2u);
-#pragma unroll
-        for (uint32_t j = 0; j < 8; ++j) vv[j] = rld16s(cv, cbase + (j * 4u + q) * D * 2u + r16 * 16u);
+        for (uint32_t j = 0; j < 8; ++j) {
+            kv[j] = rld16s(ck, cbase + (j * 4u + q) * D * 2u + r16 * 16u);
+            vv[j] = rld16s(cv, cbase + (j * 4u + q) * D * 2u + r16 * 16u);
+        }
         if (masked) {
 #pragma unroll
             for (uint32_t kb = 0; kb < 2; ++kb) mk[kb] = rld16(rm, (ci * CK + kb * 16u + 4u * q) * 4u);
@@ -1335,13 +1338,26 @@ __device__ __forceinline__ void sdpa_gqa_tile(const Unit& u, uint32_t lane) {
         return live;
     };
     auto consume = [&](const u32x4* kv, const u32x4* vv, const u32x4* mk, uint32_t ci, bool live) {
+        // K rows into LDS, then back in the operand layout (row kb 16 + l % 16,
+        // dims 8 (l / 16) + 32 s); rows KRS bytes apart put the 8 lanes of
+        // each quarter-wave of a read on distinct banks
+#pragma unroll
+        for (uint32_t j = 0; j < 8; ++j)
+            *(__attribute__((address_space(3))) u32x4*)(vl + (j * 4u + q) * KRS + r16 * 16u) = kv[j];
+        u32x4 ko[8];
+#pragma unroll
+        for (uint32_t kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (uint32_t s = 0; s < 4; ++s)
+                ko[kb * 4u + s] = *(const __attribute__((address_space(3))) u32x4*)(
+                    vl + (kb * 16u + r16) * KRS + (8u * q + 32u * s) * 2u);
         f32x4 st[2];
 #pragma unroll
         for (uint32_t kb = 0; kb < 2; ++kb) {
             st[kb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (uint32_t s = 0; s < 4; ++s)
-                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv[kb * 4u + s]),
+                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ko[kb * 4u + s]),
                                                                  __builtin_bit_cast(bf16x8, qb[s]), st[kb], 0, 0, 0);
         }
         // the value rows go to LDS while the scores are finished
