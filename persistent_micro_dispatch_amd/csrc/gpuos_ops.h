@@ -1717,16 +1717,94 @@ __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
         }
     };
     const uint32_t nst = kn / 32u;
-    u32x4 xa[MTMAX], wa[NT], xb[MTMAX], wb[NT];
-    load(xa, wa, 0);
-    for (uint32_t st = 0; st < nst; st += 2) {
-        if (st + 1 < nst) load(xb, wb, st + 1);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch above the use
-        mma(xa, wa);
-        if (st + 1 < nst) {
-            if (st + 2 < nst) load(xa, wa, st + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(xb, wb);
+    if constexpr (NT == 8u) {
+        // Eight column tiles (M <= 32): the weights come in whole 128-byte
+        // lines and go through the wave's LDS area into the operand layout.
+        // Per double step of 64 k and group of four tiles, each tile takes
+        // two loads of 8 rows x 128 bytes (lane l: row 8 h + l / 8, bytes
+        // 16 (l % 8)), written to LDS with rows WRS bytes apart and read
+        // back per step (lane l: row l % 16, bytes 16 (4 s + l / 16)).  The
+        // operand-layout loads took half of sixteen lines per instruction,
+        // and the small-matmul stream ran about 11% slower with them.
+        // The registers that staged a group take the next group's loads at
+        // once, so as many bytes are in flight as before; x comes per
+        // double step, the next one's loads issued with the last group.
+        constexpr uint32_t GT = 4u, NG = NT / GT, WRS = 144u;
+        static_assert(GT * 16u * WRS <= SDPA_VCHUNK_BYTES, "weight staging fits the wave's LDS area");
+        __attribute__((address_space(3))) uint8_t* wl =
+            (__attribute__((address_space(3))) uint8_t*)sdpa_vlds + (threadIdx.x >> 6) * SDPA_VCHUNK_BYTES;
+        const uint32_t nds = (nst + 1u) / 2u, nit = nds * NG;
+        // past the last step of an odd count the loads read the next k (or
+        // nothing, past the window) and their products are skipped
+        auto load_w = [&](u32x4* R, uint32_t it) {
+            const uint32_t k = kb + (it / NG) * 64u + (lane % 8u) * 8u;
+            const uint32_t t0 = (it % NG) * GT;
+#pragma unroll
+            for (uint32_t tt = 0; tt < GT; ++tt)
+#pragma unroll
+                for (uint32_t h = 0; h < 2; ++h)
+                    R[2u * tt + h] = rld16(rw, (((t0 + tt) * 16u + 8u * h + lane / 8u) * K + k) * 2u);
+        };
+        auto load_x = [&](u32x4* X, uint32_t d) {
+#pragma unroll
+            for (uint32_t s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (uint32_t t = 0; t < MTMAX; ++t)
+                    X[s2 * MTMAX + t] = rld16(rx, ((t * 16u + r16) * K + kb + d * 64u + s2 * 32u + kg * 8u) * 2u);
+        };
+        u32x4 R[2 * GT], O[2 * GT], xa[2 * MTMAX], xb[2 * MTMAX];
+        auto dstep = [&](uint32_t d, const u32x4* X, u32x4* Xn) {
+#pragma unroll
+            for (uint32_t g = 0; g < NG; ++g) {
+                const uint32_t it = d * NG + g;
+#pragma unroll
+                for (uint32_t tt = 0; tt < GT; ++tt)
+#pragma unroll
+                    for (uint32_t h = 0; h < 2; ++h)
+                        *(__attribute__((address_space(3))) u32x4*)(wl + (tt * 16u + 8u * h + lane / 8u) * WRS +
+                                                                    (lane % 8u) * 16u) = R[2u * tt + h];
+                if (it + 1 < nit) load_w(R, it + 1);
+                if (g == NG - 1 && d + 1 < nds) load_x(Xn, d + 1);
+                __builtin_amdgcn_sched_barrier(0);  // keep the prefetch above the use
+#pragma unroll
+                for (uint32_t tt = 0; tt < GT; ++tt)
+#pragma unroll
+                    for (uint32_t s2 = 0; s2 < 2; ++s2)
+                        O[2u * tt + s2] = *(const __attribute__((address_space(3))) u32x4*)(
+                            wl + (tt * 16u + r16) * WRS + (4u * s2 + kg) * 16u);
+#pragma unroll
+                for (uint32_t s2 = 0; s2 < 2; ++s2) {
+                    if (2u * d + s2 >= nst) break;
+#pragma unroll
+                    for (uint32_t mt = 0; mt < MTMAX; ++mt) {
+                        if (mt >= MT) break;
+#pragma unroll
+                        for (uint32_t tt = 0; tt < GT; ++tt)
+                            acc[mt][g * GT + tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, X[s2 * MTMAX + mt]), __builtin_bit_cast(bf16x8, O[2u * tt + s2]),
+                                acc[mt][g * GT + tt], 0, 0, 0);
+                    }
+                }
+            }
+        };
+        load_w(R, 0);
+        load_x(xa, 0);
+        for (uint32_t d = 0; d < nds; d += 2) {
+            dstep(d, xa, xb);
+            if (d + 1 < nds) dstep(d + 1, xb, xa);
+        }
+    } else {
+        u32x4 xa[MTMAX], wa[NT], xb[MTMAX], wb[NT];
+        load(xa, wa, 0);
+        for (uint32_t st = 0; st < nst; st += 2) {
+            if (st + 1 < nst) load(xb, wb, st + 1);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch above the use
+            mma(xa, wa);
+            if (st + 1 < nst) {
+                if (st + 2 < nst) load(xa, wa, st + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(xb, wb);
+            }
         }
     }
     uint8_t* Y = (uint8_t*)u.out;
