@@ -350,6 +350,8 @@ int main(int argc, char** argv) {
     const C cfgs[] = {{2, 1, 1, 8, 4096}, {3, 1, 1, 64, 4096}, {3, 1, 2, 8, 4096}, {9, 1, 2, 64, 4096},
                       {9, 1, 1, 512, 4096}, {5, 2, 1, 64, 8192}, {8, 1, 1, 64, 4096}, {8, 2, 2, 8, 4096},
                       {12, 4, 2, 64, 4096}, {16, 2, 2, 512, 4096}, {10, 1, 2, 128, 4096}, {4, 4, 1, 32, 4096},
+                      // more worker workgroups than claim shards: shards served by two workgroups
+                      {20, 1, 1, 64, 4096}, {24, 2, 2, 64, 256},
                       // small unit queues: the fetcher keeps waiting for capacity
                       {2, 1, 1, 64, 64}, {3, 1, 2, 64, 128}, {9, 1, 2, 128, 256}, {12, 4, 2, 64, 64}};
     int rc = 0;

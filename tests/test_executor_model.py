@@ -3,9 +3,9 @@ executor_model.cpp): one thread per wave over bounds-checked arrays, with
 the executor's own claim-shard, queue-position, queue-entry and capacity
 arithmetic (csrc/gpuos_internal.h).  Checks bounds, that every queue entry
 read is the one published for the claimed position, exactly-once units,
-dependency order, and that every wave leaves after the stop, for 1-16
+dependency order, and that every wave leaves after the stop, for 2-24
 workgroups, 1-4 waves per workgroup, one or two units per wave, 1-8 claim
-shards, rings of 8-512 entries, small and large unit queues, and stops with
+shards (also shards served by two or three workgroups), rings of 8-512 entries, small and large unit queues, and stops with
 work in flight."""
 import os
 import subprocess
@@ -21,4 +21,4 @@ def test_protocol_model_passes_every_configuration(tmp_path):
                     os.path.join(HERE, "native", "executor_model.cpp"), "-o", exe], check=True)
     r = subprocess.run([exe, "2000"], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert r.stdout.count("ok ") == 32, r.stdout
+    assert r.stdout.count("ok ") == 36, r.stdout
