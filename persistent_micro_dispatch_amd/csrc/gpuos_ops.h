@@ -1673,8 +1673,9 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
 // layout of v_mfma_f32_16x16x32_bf16, and issues one MFMA per (row tile,
 // column tile) pair into fp32 accumulators (lane l holds rows 4 (l / 16) +
 // i, column l % 16 of each 16x16 tile); the next step's loads are issued
-// before the current step's MFMAs.  Rows past M and columns past N read zero
-// through the bounded windows.  With several k-splits each unit writes fp32
+// before the current step's MFMAs.  At M <= 32 the weights instead come in
+// whole 128-byte lines and reach the operand layout through LDS (below).
+// Rows past M and columns past N read zero through the bounded windows.  With several k-splits each unit writes fp32
 // partial tiles and the last unit of a column block adds them in split
 // order.
 template <uint32_t DTO, uint32_t MTMAX, uint32_t NT>
