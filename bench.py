@@ -64,6 +64,9 @@ KERNEL_SOURCES = ["persistent_micro_dispatch_amd/csrc/gpuos_device.hip",
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gpuos_executor_hbm_traffic.md")
 
 
+CORUN_CAP_S = 120.0  # longest the co-run steps go on while GEMMs are queued
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -585,9 +588,17 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
             e1.record(gs)
         tc0 = time.perf_counter()
         k_co = 0
+        capped = False
         while not e1.query():
             one_step()
             k_co += 1
+            log(f"{name}: step {k_co} beside the GEMMs")
+            # with an executor wave on every CU no GEMM workgroup fits, and
+            # the GEMMs only advance between launches: stop after CORUN_CAP_S
+            if time.perf_counter() - tc0 > CORUN_CAP_S:
+                capped = True
+                log(f"{name}: GEMMs still queued after {CORUN_CAP_S:.0f} s of steps; stopping the steps")
+                break
         tc1 = time.perf_counter()
         gs.synchronize()
         gemm_co_ms = e0.elapsed_time(e1) / n_gemm
@@ -597,6 +608,7 @@ def run_workload(name, steps, warmup, waves=0, units_per_wave=0, ring=512, num_w
             "gemm_tflops_corun": flop / (gemm_co_ms * 1e-3) / 1e12,
             "gemm_retained": gemm_alone_ms / gemm_co_ms,
             "corun_steps": k_co,
+            "corun_capped": capped,  # the GEMMs outlasted the steps: their time includes a tail run alone
             "ops_per_s_with_gemm": nd * k_co / (tc1 - tc0) if k_co else None,
         })
         del a, b, c
