@@ -1667,15 +1667,14 @@ __device__ __forceinline__ void gemv_tile(const Unit& u, uint32_t lane) {
 // k-split of MM_KC = 1024), with NT = 8 column tiles and MT <= 2 row tiles
 // at M <= 32 and NT = 4, MT <= 4 above (the same 16 accumulator tiles;
 // every unit reads all of x beside its weight slice, so the wider units
-// read x half as often).  Per step of 32 k the wave loads, for each 16-row
-// tile of x and each 16-column tile of Wt, one 16-byte piece of a row per
-// lane (lane l: row l % 16, k offset 8 (l / 16)), which is the operand
-// layout of v_mfma_f32_16x16x32_bf16, and issues one MFMA per (row tile,
-// column tile) pair into fp32 accumulators (lane l holds rows 4 (l / 16) +
-// i, column l % 16 of each 16x16 tile); the next step's loads are issued
-// before the current step's MFMAs.  At M <= 32 the weights instead come in
-// whole 128-byte lines and reach the operand layout through LDS (below).
-// Rows past M and columns past N read zero through the bounded windows.  With several k-splits each unit writes fp32
+// read x half as often).  Per step of 32 k each MFMA takes, for one 16-row
+// tile of x and one 16-column tile of Wt, one 16-byte piece of a row per
+// lane (lane l: row l % 16, k offset 8 (l / 16)), the operand layout of
+// v_mfma_f32_16x16x32_bf16, into fp32 accumulators (lane l holds rows
+// 4 (l / 16) + i, column l % 16 of each 16x16 tile).  x is loaded in that
+// layout; the weights come in whole 128-byte lines and reach it through
+// LDS (below).  Rows past M and columns past N read zero through the
+// bounded windows.  With several k-splits each unit writes fp32
 // partial tiles and the last unit of a column block adds them in split
 // order.
 template <uint32_t DTO, uint32_t MTMAX, uint32_t NT>
@@ -1695,43 +1694,24 @@ __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
     for (uint32_t mt = 0; mt < MTMAX; ++mt)
 #pragma unroll
         for (uint32_t nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    auto load = [&](u32x4* xv, u32x4* wv, uint32_t st) {
-        const uint32_t k = kb + st * 32u + kg * 8u;
-#pragma unroll
-        for (uint32_t t = 0; t < MTMAX; ++t) xv[t] = rld16(rx, ((t * 16u + r16) * K + k) * 2u);   // rows past M: outside the window
-#pragma unroll
-        for (uint32_t t = 0; t < NT; ++t) wv[t] = rld16(rw, ((t * 16u + r16) * K + k) * 2u);  // columns past N: likewise
-        // (no non-temporal hint on the weights, unlike attention's keys: one
-        // load reads 64 bytes of each row and the next step the other half
-        // of the line, which the hint had evicted in between: 1.77x the
-        // weights' bytes from memory with it, 1.05x without)
-    };
-    auto mma = [&](const u32x4* xv, const u32x4* wv) {
-#pragma unroll
-        for (uint32_t mt = 0; mt < MTMAX; ++mt) {
-            if (mt >= MT) break;
-#pragma unroll
-            for (uint32_t nt = 0; nt < NT; ++nt)
-                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xv[mt]),
-                                                                      __builtin_bit_cast(bf16x8, wv[nt]),
-                                                                      acc[mt][nt], 0, 0, 0);
-        }
-    };
     const uint32_t nst = kn / 32u;
-    if constexpr (NT == 8u) {
-        // Eight column tiles (M <= 32): the weights come in whole 128-byte
-        // lines and go through the wave's LDS area into the operand layout.
+    {
+        // The weights come in whole 128-byte lines and go through the
+        // wave's LDS area into the operand layout.
         // Per double step of 64 k and group of four tiles, each tile takes
         // two loads of 8 rows x 128 bytes (lane l: row 8 h + l / 8, bytes
         // 16 (l % 8)), written to LDS with rows WRS bytes apart and read
         // back per step (lane l: row l % 16, bytes 16 (4 s + l / 16)).  The
         // operand-layout loads took half of sixteen lines per instruction,
-        // and the small-matmul stream ran about 11% slower with them.
+        // and the small-matmul stream ran about 11% slower with them (no
+        // non-temporal hint here: with those loads it had evicted the other
+        // half of each line before the next step read it, 1.77x the weight
+        // bytes from memory).
         // The registers that staged a group take the next group's loads at
         // once, so as many bytes are in flight as before; x comes per
         // double step, the next one's loads issued with the last group.
         constexpr uint32_t GT = 4u, NG = NT / GT, WRS = 144u;
-        static_assert(GT * 16u * WRS <= SDPA_VCHUNK_BYTES, "weight staging fits the wave's LDS area");
+        static_assert(NT % GT == 0 && GT * 16u * WRS <= SDPA_VCHUNK_BYTES, "weight staging fits the wave's LDS area");
         __attribute__((address_space(3))) uint8_t* wl =
             (__attribute__((address_space(3))) uint8_t*)sdpa_vlds + (threadIdx.x >> 6) * SDPA_VCHUNK_BYTES;
         const uint32_t nds = (nst + 1u) / 2u, nit = nds * NG;
@@ -1793,19 +1773,6 @@ __device__ __forceinline__ void matmul_tile(const Unit& u, uint32_t lane) {
         for (uint32_t d = 0; d < nds; d += 2) {
             dstep(d, xa, xb);
             if (d + 1 < nds) dstep(d + 1, xb, xa);
-        }
-    } else {
-        u32x4 xa[MTMAX], wa[NT], xb[MTMAX], wb[NT];
-        load(xa, wa, 0);
-        for (uint32_t st = 0; st < nst; st += 2) {
-            if (st + 1 < nst) load(xb, wb, st + 1);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch above the use
-            mma(xa, wa);
-            if (st + 1 < nst) {
-                if (st + 2 < nst) load(xa, wa, st + 2);
-                __builtin_amdgcn_sched_barrier(0);
-                mma(xb, wb);
-            }
         }
     }
     uint8_t* Y = (uint8_t*)u.out;
