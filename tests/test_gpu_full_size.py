@@ -1,7 +1,8 @@
-"""GPU parity at the full sizes of the element-wise and row-op streams, in
-the launch configuration bench.py times (512-entry ring; two waves per
-workgroup for the element-wise stream, four waves and two units per wave
-for the row ops), through the C ABI.
+"""GPU parity at the full sizes of the element-wise, row-op, decode and
+small-matmul streams, in the launch configuration bench.py times (512-entry
+ring; two waves per workgroup for the element-wise stream, four waves and
+two units per wave for the row ops and decode, four waves and one unit per
+wave for the small matmuls), through the C ABI.
 
 - Element-wise: all 100,000 descriptors with the op set restricted to the
   exactly rounded ones (add, mul, ReLU), free-running; the final pool must
@@ -10,7 +11,9 @@ for the row ops), through the C ABI.
   GPU).  The ops are independent (read-only inputs, outputs in a rotating
   arena), so outputs that no later descriptor overwrites -- those after the
   arena's last wrap -- are checked one by one: each sampled descriptor is
-  replayed by the oracle on its own input slice, downloaded from the GPU."""
+  replayed by the oracle on its own input slice, downloaded from the GPU.
+- Small matmuls: all 1,920 projections; sampled outputs of the last pass
+  are checked against the oracle on their own x and weights."""
 import numpy as np
 import pytest
 
@@ -160,3 +163,52 @@ def test_decode_full_stream_last_step_sampled():
         res = check_record(r[0], arrays, arrays[:3] + [g_out], p.arrays, hp)
         say(f"    worst {res['worst']:.3g}")
         assert res["ok"], res
+
+
+def test_matmul_full_stream_sampled_outputs():
+    """The small-matmul stream at its full size (1,920 projections of 32
+    token rows, 604 MB of weights) in the launch configuration bench.py
+    times (512-entry ring, four waves per workgroup, one unit per wave).
+    Every pass writes the same outputs from the same inputs, so sampled
+    output buffers are checked against the oracle run on that descriptor's
+    own x and weights (downloaded from the GPU), four of each projection
+    shape."""
+    import torch
+    s = W.make_matmul()
+    recs = s.recs
+    say(f"matmul full stream, {len(recs)} descriptors, ring 512, 4 waves, 1 unit per wave")
+    pool = DevicePool.from_stream(s, fill="device")
+    descs = to_descs(recs, pool.ptrs)
+    ctx = G.gpuos_init(ring_entries=512, waves_per_wg=4, units_per_wave=1)
+    try:
+        rc, _, n = G.gpuos_submit_bursts(ctx, descs, np.asarray(s.bursts, np.uint32), G.GPUOS_SUBMIT_BLOCK)
+        assert rc == 0 and n == len(descs)
+        rc, es, st = G.gpuos_sync(ctx, G.GPUOS_SEQ_ALL, 120_000_000_000)
+        assert rc == 0, (rc, es, st)
+    finally:
+        assert G.gpuos_shutdown(ctx) == 0
+    torch.cuda.current_stream().synchronize()
+    per_pass = int(s.bursts[0])
+    last = np.arange(len(recs) - per_pass, len(recs))
+    rng = np.random.default_rng(41)
+    pick = []
+    for K, N in {(int(r["dim"][0]), int(r["dim"][1])) for r in recs[last]}:
+        cand = last[(recs["dim"][last, 0] == K) & (recs["dim"][last, 1] == N)]
+        pick += [int(i) for i in rng.choice(cand, size=min(4, len(cand)), replace=False)]
+    say(f"  checking {len(pick)} projections of the last pass")
+    bad = []
+    for i in sorted(pick):
+        r = recs[i:i + 1].copy()
+        M, K, N = int(r["size"][0]), int(r["dim"][0, 0]), int(r["dim"][0, 1])
+        x = pool.tensors[int(r["buf"][0, W.A])][: M * K * 2].cpu().numpy()
+        wt = pool.tensors[int(r["buf"][0, W.B])][: N * K * 2].cpu().numpy()
+        g_out = pool.tensors[int(r["buf"][0, W.OUT])][: M * N * 2].cpu().numpy()
+        arrays = [x, wt, np.zeros(M * N * 2, np.uint8)]
+        r["buf"][0, W.A], r["buf"][0, W.B], r["buf"][0, W.OUT] = 0, 1, 2
+        r["off"][0, W.A] = r["off"][0, W.B] = r["off"][0, W.OUT] = 0
+        p = oracle.Pool([a.copy() for a in arrays])
+        hp = run_record_oracle(p, r[0], False)
+        res = check_record(r[0], arrays, [x, wt, g_out], p.arrays, hp)
+        if not res["ok"]:
+            bad.append((i, K, N, res))
+    assert not bad, bad[:3]
