@@ -110,19 +110,22 @@ def test_rows_full_stream_sampled_outputs():
     assert not bad, bad[:3]
 
 
-def test_decode_full_stream_last_step_sampled():
-    """The decode stream bench.py times (2,000 steps x 32 layers, caches of
-    [8, 32, 4096, 128] bf16 per layer, 16 GiB, drawn on the GPU), with four
-    waves and two units per wave.  The last step's attention outputs are
+@pytest.mark.parametrize("kv_heads", [None, 8], ids=["mha", "gqa"])
+def test_decode_full_stream_last_step_sampled(kv_heads):
+    """The decode streams bench.py times (2,000 steps x 32 layers, caches of
+    [8, Hkv, 4096, 128] bf16 per layer drawn on the GPU: 32 key/value heads,
+    16 GiB, or 8 shared by groups of four query heads on the matrix cores),
+    with four waves and two units per wave.  The last step's attention outputs are
     final (their output buffers are not written again), and so are the
     caches and the q/k buffers that step used (rotated in place by its RoPE,
     not used again): for sampled layers the oracle recomputes that step's
     SDPA from them, and the appended cache rows must equal k bit for bit."""
     import torch
-    s = W.make_decode(steps=2000)
+    s = W.make_decode(steps=2000) if kv_heads is None else W.make_decode(steps=2000, kv_heads=kv_heads)
     recs = s.recs
     L = s.meta["layers"]
-    say(f"decode full stream, {len(recs)} descriptors, 16 GiB of caches, ring 512, 4 waves, 2 units per wave")
+    say(f"decode full stream ({'32' if kv_heads is None else kv_heads} key/value heads), {len(recs)} descriptors, "
+        "ring 512, 4 waves, 2 units per wave")
     pool = DevicePool.from_stream(s, fill="device")
     descs = to_descs(recs, pool.ptrs)
     ctx = G.gpuos_init(ring_entries=512, waves_per_wg=4, units_per_wave=2)
@@ -138,18 +141,20 @@ def test_decode_full_stream_last_step_sampled():
     for layer in (0, L - 1):
         rope, app, sdpa = recs[last + 3 * layer: last + 3 * layer + 3]
         assert (int(rope["op"]), int(app["op"]), int(sdpa["op"])) == (W.OP_ROPE, W.OP_KV_APPEND, W.OP_SDPA)
-        B_, (H, D, C, _) = int(sdpa["size"]), [int(v) for v in sdpa["dim"]]
+        B_, (H, D, C, Hkv) = int(sdpa["size"]), [int(v) for v in sdpa["dim"]]
+        Hkv = Hkv or H
+        assert Hkv == (kv_heads or H)
         say(f"  layer {layer}: batch {B_}, lengths {[int(x) for x in sdpa['lens'][:B_]]}")
         q = pool.tensors[int(sdpa["buf"][W.A])][: B_ * H * D * 2].cpu().numpy()
-        kb = pool.tensors[int(app["buf"][W.A])][: B_ * H * D * 2].cpu().numpy()
-        Kc = pool.tensors[int(sdpa["buf"][W.AUX0])][: B_ * H * C * D * 2].cpu().numpy()
-        Vc = pool.tensors[int(sdpa["buf"][W.AUX1])][: B_ * H * C * D * 2].cpu().numpy()
+        kb = pool.tensors[int(app["buf"][W.A])][: B_ * Hkv * D * 2].cpu().numpy()
+        Kc = pool.tensors[int(sdpa["buf"][W.AUX0])][: B_ * Hkv * C * D * 2].cpu().numpy()
+        Vc = pool.tensors[int(sdpa["buf"][W.AUX1])][: B_ * Hkv * C * D * 2].cpu().numpy()
         o_buf = int(sdpa["buf"][W.OUT])
         es_o = W.DTYPE_BYTES[int(sdpa["out_dtype"])]
         g_out = pool.tensors[o_buf][: B_ * H * D * es_o].cpu().numpy()
         # the appended rows are k, bit for bit
-        kc = Kc.view(np.uint16).reshape(B_, H, C, D)
-        kk = kb.view(np.uint16).reshape(B_, H, D)
+        kc = Kc.view(np.uint16).reshape(B_, Hkv, C, D)
+        kk = kb.view(np.uint16).reshape(B_, Hkv, D)
         for b in range(B_):
             assert np.array_equal(kc[b, :, int(sdpa["lens"][b]) - 1, :], kk[b]), (layer, b)
         # attention against the oracle on the final q and caches
